@@ -13,7 +13,7 @@ Recipe (the pages publish no tensors, so every input is synthetic):
   * activations bf16: "iid" rows ~ N(0,1); "corr" rows are grouped in
     requests, row = base_request + 0.3 * noise with base and noise ~ N(0,1),
     which makes rows of one request share most of their picks (MTP-style
-    verify rows);
+    verify rows; row r belongs to request r // ceil(T / requests));
   * expert weights ~ N(0, 0.02) in fp32, then quantised:
       FP8 E4M3FN with one fp32 scale per 128x128 block, s = amax/448,
       q = RNE(w/s) (torch's cast) after clamping to +-448;
@@ -128,10 +128,11 @@ def make_case(spec: dict, T: int, seed: int, device="cpu", rows: str = "iid",
     if rows == "iid":
         x = torch.randn(T, H, generator=g, device=dev)
     elif rows == "corr":
-        assert T % requests == 0
+        # row r belongs to request r // ceil(T / requests)
+        per = -(-T // requests)
         base = torch.randn(requests, H, generator=g, device=dev)
         z = torch.randn(T, H, generator=g, device=dev)
-        x = base.repeat_interleave(T // requests, dim=0) + 0.3 * z
+        x = base.repeat_interleave(per, dim=0)[:T] + 0.3 * z
     else:
         raise ValueError(rows)
     x = x.to(torch.bfloat16)

@@ -1,0 +1,252 @@
+// moe_api.cpp -- host side of the C ABI in include/moe.h: argument
+// validation, workspace carving and the launch.  No allocation, no host
+// synchronisation (except moe_read_error, which is documented to wait).
+#include "moe.h"
+#include "moe_internal.h"
+
+#include <string.h>
+
+using namespace moe;
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+constexpr int kNoRows = -1;  // fill(): valid call with rows == 0
+
+struct DevInfo {
+  int ncu = 0;
+  size_t max_lds = 0;
+};
+
+// Device properties, cached per device id (read once; the library keeps no
+// other state).
+DevInfo dev_info() {
+  static DevInfo cache[64];
+  static bool have[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DevInfo{};
+  if (!have[dev]) {
+    hipDeviceProp_t pr;
+    if (hipGetDeviceProperties(&pr, dev) != hipSuccess) return DevInfo{};
+    cache[dev].ncu = pr.multiProcessorCount;
+    cache[dev].max_lds = pr.sharedMemPerBlock;
+    have[dev] = true;
+  }
+  return cache[dev];
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_cfg(const moe_config* c) {
+  if (!c) return MOE_ERR_NULL;
+  if (c->routed_fmt != MOE_FMT_FP8_B128 && c->routed_fmt != MOE_FMT_MXFP4) return MOE_ERR_FORMAT;
+  if (c->shared_fmt != MOE_FMT_FP8_B128) return MOE_ERR_FORMAT;
+  if (c->bias_dtype != MOE_BIAS_F32 && c->bias_dtype != MOE_BIAS_BF16) return MOE_ERR_FORMAT;
+  if (c->hidden < 128 || c->hidden > 8192 || c->hidden % 128) return MOE_ERR_SHAPE;
+  if (c->inter < 128 || c->inter > 4096 || c->inter % 128) return MOE_ERR_SHAPE;
+  if (c->n_shared != 0 && c->n_shared != 1) return MOE_ERR_SHAPE;
+  if (c->n_shared && (c->shared_inter < 128 || c->shared_inter > 4096 || c->shared_inter % 128))
+    return MOE_ERR_SHAPE;
+  if (c->n_experts < 1 || c->n_experts > kMaxExperts) return MOE_ERR_SHAPE;
+  if (c->top_k < 1 || c->top_k > kMaxTopK || c->top_k > c->n_experts) return MOE_ERR_SHAPE;
+  if (c->n_group < 1 || c->n_group > kMaxGroups || c->n_experts % c->n_group) return MOE_ERR_SHAPE;
+  if (c->topk_group < 1 || c->topk_group > c->n_group) return MOE_ERR_SHAPE;
+  if (c->n_group > 1) {
+    const int gsz = c->n_experts / c->n_group;
+    if (gsz < 2 || c->topk_group * gsz < c->top_k) return MOE_ERR_SHAPE;
+  }
+  if (!(c->routed_scale == c->routed_scale)) return MOE_ERR_SHAPE;
+  if (c->max_rows < 1 || c->max_rows > kMaxRows) return MOE_ERR_ROWS;
+  return MOE_OK;
+}
+
+int check_weights(const moe_config* c, const moe_weights* w, bool need_experts) {
+  if (!w) return MOE_ERR_NULL;
+  if (!w->router_w || !w->bias) return MOE_ERR_NULL;
+  if (need_experts) {
+    if (!w->w_gate_up || !w->s_gate_up || !w->w_down || !w->s_down) return MOE_ERR_NULL;
+    if (c->n_shared && (!w->sh_w_gate_up || !w->sh_s_gate_up || !w->sh_w_down || !w->sh_s_down))
+      return MOE_ERR_NULL;
+  }
+  const void* ps[] = {w->router_w, w->bias, w->w_gate_up, w->s_gate_up, w->w_down, w->s_down,
+                      w->sh_w_gate_up, w->sh_s_gate_up, w->sh_w_down, w->sh_s_down};
+  const int n = need_experts ? 10 : 2;
+  for (int i = 0; i < n; ++i)
+    if (ps[i] && !aligned16(ps[i])) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+int hs_for(int H, int ncu) { return (H + ncu - 1) / ncu; }
+
+int fill(const moe_config* c, const moe_weights* w, const uint16_t* x, int rows, void* ws,
+         size_t ws_bytes, Params& p, int mode) {
+  int rc = check_cfg(c);
+  if (rc) return rc;
+  rc = check_weights(c, w, mode == kModeForward);
+  if (rc) return rc;
+  if (rows < 0 || rows > c->max_rows) return MOE_ERR_ROWS;
+  if (rows == 0) return kNoRows;  // a no-op: x, out and ws may be NULL
+  if (!x || !ws) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(ws)) return MOE_ERR_ALIGN;
+  const WsLayout L = ws_layout(c->max_rows, c->n_experts, c->top_k, c->inter,
+                               c->n_shared ? c->shared_inter : 0);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  const DevInfo d = dev_info();
+  if (d.ncu <= 0) {
+    g_last_hip = (int)hipErrorNoDevice;
+    return MOE_ERR_HIP;
+  }
+  if (d.ncu > 1024) return MOE_ERR_SHAPE;
+  const int hs = hs_for(c->hidden, d.ncu);
+  if (hs > kMaxSlice) return MOE_ERR_SHAPE;
+  int ns = 0;
+  size_t lds = lds_plan(rows > 0 ? rows : 1, c->top_k, c->n_experts, hs, d.max_lds, &ns);
+  if (ns < 3) return MOE_ERR_SHAPE;
+  if (lds < (size_t)kMinLds) lds = kMinLds;
+  memset(&p, 0, sizeof p);
+  p.H = c->hidden;
+  p.I = c->inter;
+  p.Is = c->n_shared ? c->shared_inter : 0;
+  p.E = c->n_experts;
+  p.K = c->top_k;
+  p.ng = c->n_group;
+  p.kg = c->topk_group;
+  p.n_shared = c->n_shared;
+  p.T = rows;
+  p.routed_fmt = c->routed_fmt;
+  p.bias_bf16 = c->bias_dtype == MOE_BIAS_BF16;
+  p.routed_scale = (double)c->routed_scale;
+  p.hs = hs;
+  p.ncu = d.ncu;
+  p.mid_ld = L.mid_ld;
+  p.lds_bytes = (int)lds;
+  p.ns = ns;
+  p.x = x;
+  p.router_w = w->router_w;
+  p.bias = w->bias;
+  p.wgu = w->w_gate_up;
+  p.sgu = w->s_gate_up;
+  p.wd = w->w_down;
+  p.sd = w->s_down;
+  p.sh_wgu = w->sh_w_gate_up;
+  p.sh_sgu = w->sh_s_gate_up;
+  p.sh_wd = w->sh_w_down;
+  p.sh_sd = w->sh_s_down;
+  char* base = (char*)ws;
+  p.flags = (uint32_t*)(base + L.flags);
+  p.err = (uint32_t*)(base + L.err);
+  p.scores = (double*)(base + L.scores);
+  p.mid = (uint16_t*)(base + L.mid);
+  return MOE_OK;
+}
+
+int do_launch(const Params& p, int mode, void* stream) {
+  hipError_t e = launch(p, mode, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    g_last_hip = (int)e;
+    return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_workspace_size(const moe_config* cfg, size_t* bytes) {
+  if (!bytes) return MOE_ERR_NULL;
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  *bytes = ws_layout(cfg->max_rows, cfg->n_experts, cfg->top_k, cfg->inter,
+                     cfg->n_shared ? cfg->shared_inter : 0).total;
+  return MOE_OK;
+}
+
+int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws) return MOE_ERR_NULL;
+  if (!aligned16(ws)) return MOE_ERR_ALIGN;
+  const WsLayout L = ws_layout(1, 1, 1, 128, 0);
+  if (ws_bytes < L.scores) return MOE_ERR_WORKSPACE;
+  hipError_t e = hipMemsetAsync(ws, 0, L.scores, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    g_last_hip = (int)e;
+    return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+int moe_route(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
+              int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  Params p;
+  int rc = fill(cfg, w, x, rows, ws, ws_bytes, p, kModeRoute);
+  if (rc == kNoRows) return MOE_OK;
+  if (rc) return rc;
+  if (!topk_ids || !topk_w) return MOE_ERR_NULL;
+  if (rows == 0) return MOE_OK;
+  p.ids_out = topk_ids;
+  p.w_out = topk_w;
+  return do_launch(p, kModeRoute, stream);
+}
+
+int moe_groups(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
+               int32_t* groups_out, void* ws, size_t ws_bytes, void* stream) {
+  Params p;
+  int rc = fill(cfg, w, x, rows, ws, ws_bytes, p, kModeGroups);
+  if (rc == kNoRows) return MOE_OK;
+  if (rc) return rc;
+  if (!groups_out) return MOE_ERR_NULL;
+  if (rows == 0) return MOE_OK;
+  p.groups_out = groups_out;
+  return do_launch(p, kModeGroups, stream);
+}
+
+int moe_forward(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
+                uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  Params p;
+  int rc = fill(cfg, w, x, rows, ws, ws_bytes, p, kModeForward);
+  if (rc == kNoRows) return MOE_OK;
+  if (rc) return rc;
+  if (!out) return MOE_ERR_NULL;
+  if (!aligned16(out)) return MOE_ERR_ALIGN;
+  const size_t nb = (size_t)rows * cfg->hidden * 2;
+  const char *xo = (const char*)x, *oo = (const char*)out;
+  if (rows > 0 && xo < oo + nb && oo < xo + nb) return MOE_ERR_ALIAS;
+  if (rows == 0) return MOE_OK;
+  p.out = out;
+  return do_launch(p, kModeForward, stream);
+}
+
+int moe_read_error(void* ws, void* stream, uint32_t* bits) {
+  if (!ws || !bits) return MOE_ERR_NULL;
+  const WsLayout L = ws_layout(1, 1, 1, 128, 0);
+  uint32_t* err = (uint32_t*)((char*)ws + L.err);
+  hipError_t e = hipMemcpyAsync(bits, err, 4, hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e == hipSuccess) e = hipMemsetAsync(err, 0, 4, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) {
+    g_last_hip = (int)e;
+    return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+const char* moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "sizes outside what the kernels support";
+    case MOE_ERR_FORMAT: return "unknown weight format or bias dtype";
+    case MOE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case MOE_ERR_ROWS: return "rows out of range (0..max_rows, max_rows <= 64)";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_ALIAS: return "out overlaps x";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown error code";
+  }
+}
+
+int moe_last_hip_error(void) { return g_last_hip; }
+
+}  // extern "C"

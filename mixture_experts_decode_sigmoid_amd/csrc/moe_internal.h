@@ -1,0 +1,68 @@
+// moe_internal.h -- parameter block shared by the host API (moe_api.cpp) and
+// the device code (moe_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWaves = 8;                 // waves per workgroup (one workgroup per CU)
+constexpr int kThreads = kWaves * 64;
+constexpr int kMaxRows = 64;              // rows per call
+constexpr int kMaxExperts = 256;          // routed experts (4 per lane in the router)
+constexpr int kMaxTopK = 8;
+constexpr int kMaxGroups = 64;            // router groups
+constexpr int kMaxSlice = 64;             // output rows per CU in down
+constexpr int kMinLds = 84 * 1024;        // LDS per workgroup: more than half a CU's, so one per CU
+
+enum Mode { kModeForward = 0, kModeRoute = 1, kModeGroups = 2 };
+
+// Workspace layout (byte offsets from the workspace base).
+struct WsLayout {
+  size_t flags, err, scores, mid, total;
+  int mid_ld;  // bf16 elements per (row, slot) line of mid
+};
+
+struct Params {
+  // shape
+  int H, I, Is, E, K, ng, kg, n_shared, T;
+  int routed_fmt, bias_bf16;
+  double routed_scale;
+  int hs;          // output rows per CU in down
+  int ncu;         // workgroups launched (= CUs)
+  int mid_ld;
+  int lds_bytes;   // dynamic LDS size
+  int ns;          // weight stages in the LDS ring
+  // inputs
+  const uint16_t* x;
+  const uint16_t* router_w;
+  const void* bias;
+  const uint8_t* wgu;
+  const void* sgu;
+  const uint8_t* wd;
+  const void* sd;
+  const uint8_t* sh_wgu;
+  const float* sh_sgu;
+  const uint8_t* sh_wd;
+  const float* sh_sd;
+  // outputs
+  uint16_t* out;
+  int32_t* ids_out;
+  float* w_out;
+  int32_t* groups_out;
+  // workspace
+  uint32_t* flags;
+  uint32_t* err;
+  double* scores;  // [T][E][2]: s, b
+  uint16_t* mid;   // [T][K+1][mid_ld] bf16
+};
+
+WsLayout ws_layout(int max_rows, int E, int K, int I, int Is);
+// LDS bytes for a call and the number of weight stages that fit in max_lds
+// (*ns < 2: does not fit).
+size_t lds_plan(int T, int K, int E, int hs, size_t max_lds, int* ns);
+hipError_t launch(const Params& p, int mode, hipStream_t stream);
+
+}  // namespace moe

@@ -181,8 +181,11 @@ def forward(spec, case, rows=None, nthreads=0):
     pw = ptrs(case["w_gate_up"]); ps = ptrs(case["s_gate_up"])
     pd = ptrs(case["w_down"]); pds = ptrs(case["s_down"])
     rw = _c(case["router_w"], np.uint16); bias = np.ascontiguousarray(case["bias"])
-    shw = np.ascontiguousarray(case["sh_w_gate_up"]); shs = _c(case["sh_s_gate_up"], np.float32)
-    shd = np.ascontiguousarray(case["sh_w_down"]); shds = _c(case["sh_s_down"], np.float32)
+    if cfg.n_shared:
+        shw = np.ascontiguousarray(case["sh_w_gate_up"]); shs = _c(case["sh_s_gate_up"], np.float32)
+        shd = np.ascontiguousarray(case["sh_w_down"]); shds = _c(case["sh_s_down"], np.float32)
+    else:
+        shw = shs = shd = shds = None
     if rows is None:
         rows = list(range(T))
     rows_a = np.asarray(rows, np.int32)

@@ -1,0 +1,136 @@
+"""Bitwise properties of the GPU path that need no oracle: a row's output is
+identical alone or inside any batch (batch invariance), repeated calls are
+identical (determinism), unused experts are never read (poisoned with NaN
+codes, the output does not change), exact routing ties resolve by index,
+and a non-finite activation raises the device error word."""
+import numpy as np
+import pytest
+import torch
+
+import fixtures
+import mixture_experts_decode_sigmoid_amd as moe
+from _gpu import gpu_case, oracle_route, run_forward, say
+
+pytestmark = pytest.mark.gpu
+
+MID = dict(hidden=2048, inter=512, shared_inter=512, n_experts=64, top_k=6, n_group=8, topk_group=3)
+
+
+def _layer(spec, case, T):
+    return moe.Layer(spec, case, max_rows=T)
+
+
+@pytest.mark.parametrize("T", [1, 2, 5, 8, 16, 37, 64])
+def test_batch_invariance_mid(T):
+    say(f"batch invariance mid T={T}")
+    spec = fixtures.spec_with("tiny", **MID)
+    case = gpu_case(spec, 64, 21, rows="corr", requests=16)
+    layer = _layer(spec, case, 64)
+    full = run_forward(layer, case["x"])
+    g = torch.Generator().manual_seed(T)
+    perm = torch.randperm(64, generator=g)[:T]
+    sub = run_forward(layer, case["x"][perm.cuda()].contiguous())
+    assert np.array_equal(sub, full[perm.numpy()])
+    for r in perm[:3].tolist():
+        one = run_forward(layer, case["x"][r:r + 1].contiguous())
+        assert np.array_equal(one[0], full[r])
+
+
+def test_batch_invariance_v3_t8():
+    say("batch invariance v3 t8")
+    spec, case = fixtures.make_workload("v3_t8", device="cuda")
+    layer = _layer(spec, case, 8)
+    full = run_forward(layer, case["x"])
+    for r in range(8):
+        one = run_forward(layer, case["x"][r:r + 1].contiguous())
+        assert np.array_equal(one[0], full[r]), r
+    rev = run_forward(layer, case["x"].flip(0).contiguous())
+    assert np.array_equal(rev, full[::-1])
+
+
+def test_determinism_and_negative_control():
+    say("determinism")
+    spec = fixtures.spec_with("tiny", **MID)
+    case = gpu_case(spec, 16, 22, rows="corr", requests=4)
+    layer = _layer(spec, case, 16)
+    ref = run_forward(layer, case["x"])
+    for _ in range(20):
+        assert np.array_equal(run_forward(layer, case["x"]), ref)
+    x2 = case["x"].clone()
+    x2[3, 100] = -x2[3, 100]
+    alt = run_forward(layer, x2)
+    assert not np.array_equal(alt[3], ref[3])
+    assert np.array_equal(np.delete(alt, 3, 0), np.delete(ref, 3, 0))
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_poisoned_unused_experts(fmt):
+    say(f"poison unused fmt={fmt}")
+    over = dict(MID)
+    if fmt:
+        over.update(routed_fmt=1, bias_bf16=1, n_group=1, topk_group=1)
+    spec = fixtures.spec_with("tiny", **over)
+    case = gpu_case(spec, 8, 23, rows="corr", requests=2)
+    layer = _layer(spec, case, 8)
+    ref = run_forward(layer, case["x"])
+    ids, _, _, _ = oracle_route(spec, case)
+    unused = sorted(set(range(spec["n_experts"])) - set(ids.ravel().tolist()))
+    assert unused
+    for e in unused:
+        if fmt == 0:
+            case["w_gate_up"][e].fill_(0x7F)   # E4M3 NaN
+            case["w_down"][e].fill_(0x7F)
+        else:
+            case["s_gate_up"][e].fill_(0xFF)   # E8M0 NaN
+            case["s_down"][e].fill_(0xFF)
+    out = run_forward(layer, case["x"])
+    assert np.array_equal(out, ref)
+    assert layer.read_error() == 0
+
+
+def test_routing_exact_ties():
+    say("routing ties")
+    spec = fixtures.spec_with("tiny", **MID)
+    case = gpu_case(spec, 6, 24)
+    rw, bias = case["router_w"], case["bias"]
+    rw[40] = rw[9]
+    rw[50] = rw[9]
+    bias[9] = bias[40] = bias[50] = 3.0
+    layer = _layer(spec, case, 6)
+    ids, wts = layer.route(case["x"])
+    ids_o, w_o, _, _ = oracle_route(spec, case)
+    assert np.array_equal(ids.cpu().numpy(), ids_o)
+    # ties resolve to the lower index, in order
+    for r in range(6):
+        row = ids_o[r].tolist()
+        assert row.index(9) < row.index(40) < row.index(50)
+
+
+def test_error_word_on_nan_activation():
+    say("error word")
+    spec = fixtures.spec_with("tiny")
+    case = gpu_case(spec, 2, 25)
+    layer = _layer(spec, case, 2)
+    x = case["x"].clone()
+    x[1, 7] = float("nan")
+    run_forward(layer, x)
+    bits = layer.read_error()
+    assert bits & (moe.MOE_DEVERR_NONFINITE_SCORE | moe.MOE_DEVERR_NONFINITE_MID)
+    assert layer.read_error() == 0          # read clears
+    run_forward(layer, case["x"])
+    assert layer.read_error() == 0
+
+
+def test_rows_zero_and_limits():
+    spec = fixtures.spec_with("tiny")
+    case = gpu_case(spec, 4, 26)
+    layer = _layer(spec, case, 4)
+    empty = torch.empty(0, spec["hidden"], dtype=torch.bfloat16, device="cuda")
+    layer.forward(empty, out=torch.empty_like(empty))
+    with pytest.raises(moe.MoeError) as e:
+        big = torch.zeros(5, spec["hidden"], dtype=torch.bfloat16, device="cuda")
+        layer.forward(big)
+    assert e.value.code == moe.MOE_ERR_ROWS
+    with pytest.raises(moe.MoeError) as e:
+        layer.forward(case["x"], out=case["x"])
+    assert e.value.code == moe.MOE_ERR_ALIAS

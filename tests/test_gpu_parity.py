@@ -1,0 +1,120 @@
+"""GPU path against the fp64 oracle, through the C ABI.
+
+Small cases run the whole batch through the oracle; they are sized to span
+several weight chunks (1024-element K chunks, 16-row tiles) with ragged
+tails.  Full-size cases (DeepSeek-V3 shape at 1, 8 and 64 rows; the
+V4-style MXFP4 layer at 16 rows) are checked on sampled rows the oracle
+computes one by one.  Routing must match bit-exactly (ids and order),
+outputs within 2e-2 relative L2 and 1e-1 max-abs of the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import fixtures
+import mixture_experts_decode_sigmoid_amd as moe
+from _gpu import (MAX_ABS, REL_L2, gpu_case, oracle_route, oracle_rows, parity, run_forward, say)
+
+pytestmark = pytest.mark.gpu
+
+# (name, spec overrides, T, seed, row recipe)
+SMALL = [
+    ("tiny_t1", dict(), 1, 1, "iid"),
+    ("tiny_t8", dict(), 8, 11, "corr"),
+    ("tiny_t64", dict(), 64, 12, "iid"),
+    ("grouped_k6_bf16bias", dict(n_experts=32, top_k=6, n_group=4, topk_group=2, bias_bf16=1), 13, 13, "iid"),
+    ("multichunk_ragged", dict(hidden=1152, inter=640, shared_inter=384, n_experts=24, top_k=5), 9, 14, "corr"),
+    ("wide_h3072", dict(hidden=3072, inter=256, shared_inter=256, n_experts=16, top_k=4,
+                        n_group=4, topk_group=2), 20, 15, "iid"),
+    ("mxfp4_small", dict(hidden=1536, inter=1536, shared_inter=512, n_experts=16, top_k=6,
+                         routed_fmt=1, bias_bf16=1), 16, 16, "corr"),
+    ("no_shared", dict(n_shared=0, hidden=512, inter=256, n_experts=12, top_k=3), 7, 17, "iid"),
+    ("k_equals_e", dict(n_experts=8, top_k=8, hidden=256, inter=128), 3, 18, "iid"),
+]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib_loaded():
+    moe.lib()
+    assert torch.cuda.is_available()
+
+
+def _spec(over):
+    return fixtures.spec_with("tiny", **over)
+
+
+@pytest.mark.parametrize("name,over,T,seed,rows", SMALL, ids=[s[0] for s in SMALL])
+def test_small_parity(name, over, T, seed, rows):
+    say(f"case {name} T={T} seed={seed}")
+    spec = _spec(over)
+    case = gpu_case(spec, T, seed, rows=rows, requests=max(1, T // 4))
+    layer = moe.Layer(spec, case, max_rows=max(T, 1))
+    ids_o, w_o, ge, gg = oracle_route(spec, case)
+    assert np.min(ge) > 1e-9 and np.min(gg) > 1e-9
+    ids, wts = layer.route(case["x"])
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ids_o)
+    assert np.allclose(wts.cpu().numpy(), w_o, rtol=1e-6, atol=0)
+    out = run_forward(layer, case["x"])
+    assert layer.read_error() == 0
+    o64, _ = oracle_rows(spec, case, range(T), ids=ids_o)
+    rel, mx = parity(out, o64, list(range(T)))
+    say(f"  rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert rel <= REL_L2 and mx <= MAX_ABS
+
+
+@pytest.mark.parametrize("name,over,T,seed,rows", SMALL[:6], ids=[s[0] for s in SMALL[:6]])
+def test_small_groups_exact(name, over, T, seed, rows):
+    import oracle
+    say(f"groups {name} T={T}")
+    spec = _spec(over)
+    case = gpu_case(spec, T, seed, rows=rows, requests=max(1, T // 4))
+    layer = moe.Layer(spec, case, max_rows=T)
+    ids_o, _, _, _ = oracle_route(spec, case)
+    ge_o, gn_o, gs_o, cols_o, _ = oracle.groups(spec, ids_o)
+    ge, gn, gs, cols = layer.groups(case["x"])
+    assert ge == ge_o.tolist() and gn == gn_o.tolist() and gs == gs_o.tolist()
+    assert cols == cols_o.tolist()
+
+
+FULL = [
+    ("v3_t1", [0]),
+    ("v3_t8", [0, 3, 5, 7]),
+    ("v3_t64", [0, 17, 42, 63]),
+    ("v4_t16", [0, 6, 15]),
+]
+
+
+@pytest.fixture(scope="module")
+def full_cases():
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            cache.clear()
+            torch.cuda.empty_cache()
+            spec, case = fixtures.make_workload(name, device="cuda")
+            cache[name] = (spec, case)
+        return cache[name]
+    return get
+
+
+@pytest.mark.parametrize("name,rows", FULL, ids=[f[0] for f in FULL])
+def test_full_size_sampled(full_cases, name, rows):
+    say(f"full {name} rows={rows}")
+    spec, case = full_cases(name)
+    T = case["x"].shape[0]
+    layer = moe.Layer(spec, case, max_rows=T)
+    ids_o, w_o, ge, gg = oracle_route(spec, case)
+    assert np.min(ge) > 1e-9 and np.min(gg) > 1e-9
+    ids, wts = layer.route(case["x"])
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ids_o)
+    D = len(set(ids_o.ravel().tolist()))
+    say(f"  distinct routed experts D={D}")
+    out = run_forward(layer, case["x"])
+    assert layer.read_error() == 0
+    o64, _ = oracle_rows(spec, case, rows, ids=ids_o)
+    rel, mx = parity(out, o64, rows)
+    say(f"  rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert rel <= REL_L2 and mx <= MAX_ABS
+    assert np.all(np.isfinite(out.view(np.int16).astype(np.float64)))
