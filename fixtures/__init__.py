@@ -112,12 +112,13 @@ def _quant(w, fmt):
 
 
 def make_case(spec: dict, T: int, seed: int, device="cpu", rows: str = "iid",
-              requests: int = 1, expert_chunk: int = 16) -> dict:
+              requests: int = 1, expert_chunk: int = 16, experts: bool = True) -> dict:
     """Draws one seeded case.  Returns torch tensors on `device`:
     x [T,H] bf16, router_w [E,H] bf16, bias [E] fp32|bf16,
     w_gate_up [E,2I,H] u8 (or [E,2I,H/2] for MXFP4), s_gate_up,
     w_down [E,H,I] u8 (or [E,H,I/2]), s_down, and the shared expert's
-    sh_w_gate_up [2I_s,H] u8, sh_s_gate_up, sh_w_down [H,I_s] u8, sh_s_down."""
+    sh_w_gate_up [2I_s,H] u8, sh_s_gate_up, sh_w_down [H,I_s] u8, sh_s_down.
+    experts=False stops after the router weights, bias and activations."""
     H, I, Is, E = spec["hidden"], spec["inter"], spec["shared_inter"], spec["n_experts"]
     fmt = spec["routed_fmt"]
     g = _gen(device, seed)
@@ -137,6 +138,8 @@ def make_case(spec: dict, T: int, seed: int, device="cpu", rows: str = "iid",
         raise ValueError(rows)
     x = x.to(torch.bfloat16)
     case = dict(x=x, router_w=rw, bias=bias)
+    if not experts:
+        return case
     if spec["n_shared"]:
         wsh = torch.randn(2 * Is, H, generator=g, device=dev) * 0.02
         case["sh_w_gate_up"], case["sh_s_gate_up"] = quant_fp8_b128(wsh)
@@ -194,3 +197,24 @@ def host_case(case: dict, experts=None) -> dict:
     for k in ("w_gate_up", "s_gate_up", "w_down", "s_down"):
         out[k] = [case[k][e].cpu().numpy() if e in experts else None for e in range(E)]
     return out
+
+
+def weight_bytes(spec: dict) -> dict:
+    """Bytes of each weight tensor the layer reads (values + scales)."""
+    H, I, Is, E = spec["hidden"], spec["inter"], spec["shared_inter"], spec["n_experts"]
+    if spec["routed_fmt"] == FMT_FP8_B128:
+        routed = 3 * I * H + 4 * ((2 * I // 128) * (H // 128) + (H // 128) * (I // 128))
+    else:
+        routed = 3 * I * H // 2 + (2 * I * (H // 32) + H * (I // 32))
+    shared = (3 * Is * H + 4 * ((2 * Is // 128) * (H // 128) + (H // 128) * (Is // 128))) if spec["n_shared"] else 0
+    router = 2 * E * H + (2 if spec["bias_bf16"] else 4) * E
+    return dict(routed_expert=routed, shared_expert=shared, router=router)
+
+
+def algorithmic_bytes(spec: dict, distinct: int) -> int:
+    """Bytes the layer must move for one call: every used expert's weights and
+    scales once (the shared expert and `distinct` routed experts) plus the
+    router weights and bias.  Activations, mid values and outputs (<0.1%)
+    are not counted."""
+    b = weight_bytes(spec)
+    return b["shared_expert"] + distinct * b["routed_expert"] + b["router"]

@@ -138,6 +138,10 @@ int fill(const moe_config* c, const moe_weights* w, const uint16_t* x, int rows,
   p.err = (uint32_t*)(base + L.err);
   p.scores = (double*)(base + L.scores);
   p.mid = (uint16_t*)(base + L.mid);
+#ifdef MOE_TIMELINE
+  p.timeline = (uint64_t*)(base + L.total);  // callers of a timeline build add 1024*16*8 bytes
+  if (ws_bytes < L.total + 1024 * 16 * 8) return MOE_ERR_WORKSPACE;
+#endif
   return MOE_OK;
 }
 

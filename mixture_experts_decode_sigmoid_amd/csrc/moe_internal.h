@@ -8,8 +8,10 @@
 
 namespace moe {
 
-constexpr int kWaves = 8;                 // waves per workgroup (one workgroup per CU)
-constexpr int kThreads = kWaves * 64;
+constexpr int kWaves = 8;                 // compute waves per workgroup (one workgroup per CU)
+constexpr int kProducers = 2;             // waves that only stream weights into LDS
+constexpr int kAllWaves = kWaves + kProducers;
+constexpr int kThreads = kAllWaves * 64;
 constexpr int kMaxRows = 64;              // rows per call
 constexpr int kMaxExperts = 256;          // routed experts (4 per lane in the router)
 constexpr int kMaxTopK = 8;
@@ -57,6 +59,7 @@ struct Params {
   uint32_t* err;
   double* scores;  // [T][E][2]: s, b
   uint16_t* mid;   // [T][K+1][mid_ld] bf16
+  uint64_t* timeline;  // optional phase stamps ([ncu][16]); NULL unless built with MOE_TIMELINE
 };
 
 WsLayout ws_layout(int max_rows, int E, int K, int I, int Is);

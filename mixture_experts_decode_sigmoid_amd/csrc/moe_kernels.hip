@@ -110,6 +110,21 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
 
+// Optional per-CU phase stamps (build with -DMOE_TIMELINE): thread 0 of each
+// workgroup writes s_memrealtime (100 MHz) at phase boundaries into
+// p.timeline[blockIdx.x * 16 + i].
+#ifdef MOE_TIMELINE
+#define MOE_STAMP(p, i)                                                                  \
+  do {                                                                                   \
+    if (threadIdx.x == 0 && (p).timeline)                                                \
+      (p).timeline[blockIdx.x * 16 + (i)] = __builtin_amdgcn_s_memrealtime();            \
+  } while (0)
+#else
+#define MOE_STAMP(p, i) \
+  do {                  \
+  } while (0)
+#endif
+
 // ------------------------------------------------------------------ LDS map
 
 // Weight stages: a ring of `ns` stages, each 16 weight rows of one K chunk
@@ -119,7 +134,8 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; 
 // 16-byte pad puts the 16 rows an MFMA tile reads in one ds_read_b128 on
 // different LDS banks.
 constexpr int kPitch = 1040;
-constexpr int kStageBytes = 16 * kPitch;
+constexpr int kScaleOff = 16 * kPitch;          // the chunk's weight scales follow its rows
+constexpr int kStageBytes = kScaleOff + 512;
 constexpr int kChunkElems = 1024;
 
 struct Lds {
@@ -138,14 +154,13 @@ struct Lds {
   double* rgs;       // [kWaves][64] group scores
   int32_t* rkept;    // [kWaves][64]
   float* pbuf;       // [T*(K+1)][hs] down products
-  char* dummy;       // [1024] target of placeholder DMAs, never read
   char* stages;      // [ns][kStageBytes]
 };
 
 __host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct LdsOffsets {
-  size_t ids, w, first, egrp, rmask, gexp, gcnt, gstart, cols, misc, red, pbuf, dummy, stages;
+  size_t ids, w, first, egrp, rmask, gexp, gcnt, gstart, cols, misc, red, pbuf, stages;
 };
 
 __host__ __device__ inline LdsOffsets lds_offsets(int T, int K, int E, int hs) {
@@ -167,8 +182,6 @@ __host__ __device__ inline LdsOffsets lds_offsets(int T, int K, int E, int hs) {
   size_t pb = 4 * (size_t)T * (K + 1) * hs;
   size_t rs = 8 * (size_t)kWaves * E + 8 * (size_t)kWaves * 64 + 4 * (size_t)kWaves * 64;
   q = align_up(q + (pb > rs ? pb : rs), 16);
-  o.dummy = q;
-  q += 1024;
   o.stages = q;
   return o;
 }
@@ -203,7 +216,6 @@ __device__ inline Lds lds_map(char* base, const Params& p) {
   L.rb = (double*)(base + o.pbuf);
   L.rgs = L.rb + (size_t)kWaves * p.E;
   L.rkept = (int32_t*)(L.rgs + (size_t)kWaves * 64);
-  L.dummy = base + o.dummy;
   L.stages = base + o.stages;
   return L;
 }
@@ -211,11 +223,15 @@ __device__ inline Lds lds_map(char* base, const Params& p) {
 // ------------------------------------------------------------------ flags
 
 // Raise this CU's flag to `value` after all of the workgroup's prior global
-// stores.  Every wave waits for its own stores, the workgroup meets, then one
-// thread releases at agent scope and stores the flag.
+// stores.  Every compute wave waits for its own stores, the workgroup meets,
+// then one thread releases at agent scope and stores the flag.  The barrier
+// is the bare s_barrier: producer waves may have weight DMA in flight and
+// must not wait for it here.
 __device__ inline void publish(const Params& p, uint32_t value) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  if ((threadIdx.x >> 6) < kWaves) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   if (threadIdx.x == 0) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __hip_atomic_store(&p.flags[blockIdx.x], value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -223,7 +239,8 @@ __device__ inline void publish(const Params& p, uint32_t value) {
 }
 
 // Wait until every CU's flag has reached `target` (wrap-around safe), then
-// acquire.  Wave 0 polls; the workgroup barrier after it orders the rest.
+// acquire.  Wave 0 polls and acquires; the barrier after it orders the rest
+// of the workgroup (bare s_barrier, as in publish).
 __device__ inline void wait_all(const Params& p, uint32_t target) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
@@ -243,7 +260,9 @@ __device__ inline void wait_all(const Params& p, uint32_t target) {
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
-  __syncthreads();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // ------------------------------------------------------------------ S0 logits
@@ -257,6 +276,7 @@ __device__ inline double load_bias(const Params& p, int e) {
 // order, then a fixed xor butterfly; one wave per (row, expert).
 __device__ inline void router_logits(const Params& p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (wave >= kWaves) return;
   for (int e = blockIdx.x; e < p.E; e += p.ncu) {
     const uint16_t* wr = p.router_w + (size_t)e * p.H;
     const double bias = load_bias(p, e);
@@ -408,7 +428,7 @@ __device__ inline void build_groups(const Params& p, const Lds& L) {
     int wbase = base;
     for (int w = 0; w < wave; ++w) wbase += L.misc[8 + w];
     int total = 0;
-    for (int w = 0; w < kWaves; ++w) total += L.misc[8 + w];
+    for (int w = 0; w < kAllWaves; ++w) total += L.misc[8 + w];
     if (isf) {
       const int g = wbase + before;
       const int e = L.ids[u];
@@ -464,22 +484,39 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-__device__ __forceinline__ void dma16(const void* g, lds_char* l) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+// One row segment of up to 1 KB into LDS: 64 lanes x 16 B through a buffer
+// resource whose size is the segment's valid bytes, so lanes past the end
+// (a ragged tail, or a row with no valid bytes) read zeros without touching
+// memory.  The buffer form of the LDS DMA is the one the compiler counts
+// among outstanding vector memory operations.
+__device__ __forceinline__ const void* uniform_ptr(const void* q) {
+  const uint64_t v = (uint64_t)q;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
+
+// The descriptor's base and size are wave-uniform by construction; taking
+// them through readfirstlane keeps the descriptor in scalar registers (a
+// descriptor the compiler believes divergent costs a loop per instruction).
+__device__ __forceinline__ void dma_row(const uint8_t* base, int nbytes, lds_char* l) {
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(base), 0,
+                                                               __builtin_amdgcn_readfirstlane(nbytes), 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)l, 16,
+                                           (threadIdx.x & 63) * 16, 0, 0, 0);
 }
 
 // Waits until at most n of this wave's vector memory operations are
-// outstanding (n is one of the small even counts the stream uses).
+// outstanding (n is a multiple of 9: a producer issues 9 DMAs per chunk).
 __device__ __forceinline__ void wait_vm(int n) {
   switch (n) {
     case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-    case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
-    case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
+    case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+    case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
+    case 27: asm volatile("s_waitcnt vmcnt(27)" ::: "memory"); break;
+    case 36: asm volatile("s_waitcnt vmcnt(36)" ::: "memory"); break;
+    case 45: asm volatile("s_waitcnt vmcnt(45)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(54)" ::: "memory"); break;
   }
 }
 
@@ -500,12 +537,14 @@ __device__ __forceinline__ uint32_t lds_off(const void* p) {
   return (uint32_t)(size_t)(const lds_char*)p;
 }
 __device__ __forceinline__ uint32_t lds_off(const lds_char* p) { return (uint32_t)(size_t)p; }
-__device__ __forceinline__ uint32_t lds_ld32(const void* p) {
+template <class P>
+__device__ __forceinline__ uint32_t lds_ld32(P p) {
   uint32_t v;
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_off(p)) : "memory");
   return v;
 }
-__device__ __forceinline__ float lds_ldf(const void* p) { return __uint_as_float(lds_ld32(p)); }
+template <class P>
+__device__ __forceinline__ float lds_ldf(P p) { return __uint_as_float(lds_ld32(p)); }
 // For an address every lane of the wave shares.
 __device__ __forceinline__ int lds_ldi_uniform(const int32_t* p) {
   return __builtin_amdgcn_readfirstlane((int)lds_ld32(p));
@@ -516,29 +555,41 @@ __device__ __forceinline__ void lds_st32(void* p, uint32_t v) {
 __device__ __forceinline__ void lds_st128(void* p, u32x4 v) {
   asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(lds_off(p)), "v"(v) : "memory");
 }
+// A lane's part of one K-block of the stage with its scales, in one round
+// trip: FP8, 32 weight bytes and the two 128-row block scales (the second
+// one 32 bytes after the first); MXFP4, 16 weight bytes and a dword of the
+// row's E8M0 scales.
 template <class P>
-__device__ __forceinline__ u32x4 lds_ld128(P p) {
-  u32x4 v;
-  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_off(p)) : "memory");
-  return v;
+__device__ __forceinline__ void lds_ld_fp8_block(P w, P sc, u32x4& a, u32x4& b, uint32_t& s0, uint32_t& s1) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:16\n\t"
+      "ds_read_b32 %2, %5\n\tds_read_b32 %3, %5 offset:32\n\ts_waitcnt lgkmcnt(0)"
+      : "=&v"(a), "=&v"(b), "=&v"(s0), "=&v"(s1)
+      : "v"(lds_off(w)), "v"(lds_off(sc))
+      : "memory");
 }
 template <class P>
-__device__ __forceinline__ void lds_ld128x2(P p, u32x4& a, u32x4& b) {
-  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
-               : "=&v"(a), "=&v"(b)
-               : "v"(lds_off(p))
+__device__ __forceinline__ void lds_ld_fp4_block(P w, P sc, u32x4& a, uint32_t& s0) {
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b32 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(a), "=&v"(s0)
+               : "v"(lds_off(w)), "v"(lds_off(sc))
                : "memory");
 }
 
-// Per-lane prefetch of one chunk: activations, and the weight scales the
-// lane's MFMA outputs need.
+// Per-lane prefetch of one chunk: the activations of column tiles
+// 0..NPRE-1 (later tiles are loaded when used), and where the FP8 scale
+// changes inside the 16-row weight tile.  NPRE is 1 for batches of at most
+// 16 rows (no group has more than 16 columns) and 2 above.
+template <int NPRE>
 struct Pre {
-  u32x4 B[16];
-  float s_lo, s_hi;  // FP8: block scales of output rows below / from `split`
-  int split;
-  uint32_t bscale;   // MXFP4: E8M0 scale byte of this lane's weight row and K sub-block
+  u32x4 B[4 * NPRE];
+  int split;         // FP8: MFMA output rows (4*lg + q) below it take the first scale
   int nct;
 };
+
+// Column tiles a group can have: 1 when NPRE is 1, else up to 4 (64 rows).
+template <int NPRE>
+constexpr int max_tiles() { return NPRE == 1 ? 1 : kMaxRows / 16; }
 
 struct Pos {
   int phase;  // 0 shared up/gate, 1 routed up/gate, 2 down, 3 end
@@ -651,18 +702,19 @@ __device__ inline void group_weights(const Params& p, const Lds& L, int g, Chunk
   }
 }
 
+// Group of an up/gate position: the shared expert's jobs come first, then
+// rt_tiles jobs per routed group.
+__device__ __forceinline__ int chunk_group(const Params& p, const Sched& s, const Pos& c) {
+  return c.phase == 0 ? 0 : p.n_shared + (c.j - s.sh_tiles) / s.rt_tiles;
+}
+
 __device__ inline Chunk chunk_of(const Params& p, const Lds& L, const Sched& s, const Pos& c) {
   Chunk k;
   k.kc = c.kc;
   if (c.phase <= 1) {
     k.kind = 1;
-    if (c.phase == 0) {
-      k.g = 0;
-      k.tile = c.j;
-    } else {
-      k.g = p.n_shared + (c.j - s.sh_tiles) / s.rt_tiles;
-      k.tile = (c.j - s.sh_tiles) % s.rt_tiles;
-    }
+    k.g = chunk_group(p, s, c);
+    k.tile = c.phase == 0 ? c.j : (c.j - s.sh_tiles) % s.rt_tiles;
     k.rt = 0;
     group_weights(p, L, k.g, k, false);
     k.kdim = p.H;
@@ -686,38 +738,57 @@ __device__ __forceinline__ int weight_row_index(const Sched& s, const Chunk& k, 
   return s.h0 + 16 * k.rt + r;
 }
 
-// Two DMA instructions per wave per chunk (rows 2w, 2w+1), always issued so
-// every wave's vmcnt bookkeeping is the same: a row past the live rows
-// reloads the last live row into its own (unread for output) slot, and lanes
-// past the row's end reload its last 16 bytes.
+// Producer wave pw streams rows 8pw..8pw+7 of a chunk (8 DMA instructions,
+// always issued: a row past the live rows has no valid bytes) and one DMA of
+// scales, so its vmcnt bookkeeping is 9 per chunk.  Scales land at
+// kScaleOff: FP8, 16 floats from producer 0 (the 8 K-blocks' scales of the
+// tile's first and second 128-row block); MXFP4, 32 E8M0 bytes per row.
 __device__ inline void issue_chunk(const Params& p, const Lds& L, const Sched& s, const Pos& c,
-                                   lds_char* stage) {
+                                   lds_char* stage, int pw) {
   const Chunk k = chunk_of(p, L, s, c);
-  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int lane = threadIdx.x & 63;
   const int cbytes = k.fmt ? kChunkElems / 2 : kChunkElems;
-  const int rowbytes = k.fmt ? k.kdim / 2 : k.kdim;
+  const int rowbytes = __builtin_amdgcn_readfirstlane(k.fmt ? k.kdim / 2 : k.kdim);
   const int koff = k.kc * cbytes;
   const int left = rowbytes - koff;
-  const int nbytes = left < cbytes ? left : cbytes;
-  const int loff = koff + (lane * 16 < nbytes - 16 ? lane * 16 : nbytes - 16);
+  const int nbytes = __builtin_amdgcn_readfirstlane(left < cbytes ? left : cbytes);
+  // this wave's 8 chunk rows are consecutive weight rows (gate rows, up
+  // rows, or output rows), so one base and the row pitch address them all
+  const int nl = __builtin_amdgcn_readfirstlane(k.nlive - 8 * pw);
+  const uint8_t* b = (const uint8_t*)uniform_ptr(
+      k.w + (size_t)weight_row_index(s, k, nl > 0 ? 8 * pw : 0) * rowbytes + koff);
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int r = 2 * wave + q;
-    const int src = r < k.nlive ? r : k.nlive - 1;
-    const uint8_t* rp = k.w + (size_t)weight_row_index(s, k, src) * rowbytes;
-    dma16(rp + loff, stage + r * kPitch);
+  for (int q = 0; q < 8; ++q)
+    dma_row(q < nl ? b + q * rowbytes : b, q < nl ? nbytes : 0, stage + (8 * pw + q) * kPitch);
+  const uint32_t kOob = 0x7ffffff0u;
+  uint32_t voff = kOob, nrec;
+  if (k.fmt == 0) {
+    const int nkb = k.kdim / 128;
+    int nb_lo, nb_hi, nrows;
+    if (k.kind == 1) {
+      nb_lo = (8 * k.tile) / 128;
+      nb_hi = (k.iexp + 8 * k.tile) / 128;
+      nrows = 2 * k.iexp / 128;
+    } else {
+      const int hb = s.h0 + 16 * k.rt;
+      nb_lo = hb / 128;
+      nb_hi = (hb + k.nlive - 1) / 128;
+      nrows = p.H / 128;
+    }
+    const int kb = k.kc * 8 + (lane & 7);
+    if (pw == 0 && lane < 16 && kb < nkb) voff = (uint32_t)(((lane < 8 ? nb_lo : nb_hi) * nkb + kb) * 4);
+    nrec = (uint32_t)(nrows * nkb * 4);
+  } else {
+    const int spr = k.kdim / 32;                 // scale bytes per weight row
+    const int r = 8 * pw + (lane >> 3), d = lane & 7;
+    const int valid = spr - k.kc * 32 < 32 ? spr - k.kc * 32 : 32;
+    if (r < k.nlive && 4 * d < valid) voff = (uint32_t)(weight_row_index(s, k, r) * spr + k.kc * 32 + 4 * d);
+    nrec = (uint32_t)((k.kind == 1 ? 2 * k.iexp : p.H) * spr);
   }
-}
-
-// Two placeholder DMAs (1 KB of the router weights into an LDS slot nobody
-// reads) where the stream has no chunk left but the loop shape needs the
-// same two outstanding operations after a prefetch.
-__device__ inline void issue_dummy(const Params& p, lds_char* dummy) {
-  const int lane = threadIdx.x & 63;
-  const int bytes = p.E * p.H * 2;
-  const uint8_t* src = (const uint8_t*)p.router_w + (lane * 16 < bytes - 16 ? lane * 16 : bytes - 16);
-  dma16(src, dummy);
-  dma16(src, dummy);
+  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(k.s), 0,
+                                                                __builtin_amdgcn_readfirstlane((int)nrec), 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(stage + kScaleOff + 256 * pw),
+                                           4, voff, 0, 0, 0);
 }
 
 // Column c of group g as row*16 + slot.
@@ -731,61 +802,45 @@ __device__ __forceinline__ int group_ncols(const Params& p, const Lds& L, int g)
   return lds_ldi_uniform(L.gcnt + g);
 }
 
-// Activations of the next chunk for this lane: for each 16-column tile ct,
-// B[4ct+m] holds the 8 bf16 of column ct*16 + (lane & 15) at elements
-// kb*128 + 32*(lane >> 4) + 8m .. +7 (x rows for up/gate, mid lines for
-// down).  Also the chunk's weight scales:
-// FP8 block scales of this wave's K-block, or the lane's MXFP4 E8M0 byte.
-__device__ inline void load_pre(const Params& p, const Lds& L, const Sched& s, const Chunk& k, Pre& P) {
+// Activations of column tile ct at K-block kb for this lane: B[m] holds the
+// 8 bf16 of column ct*16 + (lane & 15) at elements kb*128 + 32*(lane >> 4) +
+// 8m .. +7 (x rows for up/gate, mid lines for down).  A lane past the
+// group's columns loads the last column again: MFMA columns are independent
+// and that output is never stored.
+__device__ __forceinline__ void load_tile(const Params& p, const Lds& L, const Chunk& k, int kb,
+                                          int ct, int ncols, u32x4* B) {
   const int lane = threadIdx.x & 63, lg = lane >> 4, row = lane & 15;
-  const int kb = k.kc * 8 + wave_id();
+  const int c = ct * 16 + row < ncols ? ct * 16 + row : ncols - 1;
+  const int code = col_code(p, L, k.g, c);
+  const uint16_t* src = k.kind == 1
+      ? p.x + (size_t)(code >> 4) * p.H
+      : p.mid + ((size_t)(code >> 4) * (p.K + 1) + (code & 15)) * p.mid_ld;
+  const uint16_t* ptr = src + kb * 128 + 32 * lg;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) B[m] = ld16(ptr + 8 * m);
+}
+
+// Activations of the next chunk for this lane: for each 16-column tile
+// ct < NPRE, B[4ct+m] holds the 8 bf16 of column ct*16 + (lane & 15) at
+// elements kb*128 + 32*(lane >> 4) + 8m .. +7 (x rows for up/gate, mid lines
+// for down), one chunk ahead of their use.  Every register is loaded on
+// every call (a wave past the chunk's K range loads the last block again, a
+// tile past the group's columns its last column): a register that is only
+// sometimes loaded makes the compiler wait for all loads before the merge.
+template <int NPRE>
+__device__ inline void load_pre(const Params& p, const Lds& L, const Sched& s, const Chunk& k, Pre<NPRE>& P) {
+  const int nkb = (k.kdim + 127) >> 7;
+  const int kb = k.kc * 8 + wave_id() < nkb ? k.kc * 8 + wave_id() : nkb - 1;
   const int ncols = group_ncols(p, L, k.g);
   P.nct = (ncols + 15) >> 4;
-  if (kb * 128 >= k.kdim) return;
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    if (ct < P.nct) {
-      // a lane past the group's columns loads the last column again: MFMA
-      // columns are independent and that output is never stored
-      const int c = ct * 16 + row < ncols ? ct * 16 + row : ncols - 1;
-      const int code = col_code(p, L, k.g, c);
-      const uint16_t* src = k.kind == 1
-          ? p.x + (size_t)(code >> 4) * p.H
-          : p.mid + ((size_t)(code >> 4) * (p.K + 1) + (code & 15)) * p.mid_ld;
-      const uint16_t* ptr = src + kb * 128 + 32 * lg;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) P.B[4 * ct + m] = ld16(ptr + 8 * m);
-    }
-  }
-  // Every scale register is written by a load on every path (the one the
-  // format does not use reads the scale array's first element): a constant
-  // written into a register whose previous load may be in flight would cost
-  // a vmcnt(0).
-  if (k.fmt == 0) {
-    const float* sp = (const float*)k.s;
-    if (k.kind == 1) {
-      // rows 0..7 of the MFMA tile are gate rows, 8..15 up rows
-      const int nkbH = p.H / 128;
-      P.s_lo = sp[(size_t)((8 * k.tile) / 128) * nkbH + kb];
-      P.s_hi = sp[(size_t)((k.iexp + 8 * k.tile) / 128) * nkbH + kb];
-      P.split = 8;
-    } else {
-      // a 16-row down tile spans at most two 128-row scale blocks
-      const int nkbI = k.iexp / 128;
-      const int hb = s.h0 + 16 * k.rt;
-      const int nb0 = hb / 128, nb1 = (hb + k.nlive - 1) / 128;
-      P.s_lo = sp[(size_t)nb0 * nkbI + kb];
-      P.s_hi = sp[(size_t)nb1 * nkbI + kb];
-      P.split = (nb0 + 1) * 128 - hb;
-    }
-    P.bscale = *(const uint8_t*)k.s;
+  for (int ct = 0; ct < NPRE; ++ct) load_tile(p, L, k, kb, ct, ncols, P.B + 4 * ct);
+  if (k.kind == 1) {
+    P.split = 8;  // rows 0..7 of the MFMA tile are gate rows, 8..15 up rows
   } else {
-    const int r = row < k.nlive ? row : k.nlive - 1;
-    const uint8_t* sp = (const uint8_t*)k.s;
-    P.bscale = sp[(size_t)weight_row_index(s, k, r) * (k.kdim / 32) + kb * 4 + lg];
-    P.s_lo = *(const float*)k.s;
-    P.s_hi = *(const float*)k.s;
-    P.split = 0;
+    // a 16-row down tile spans at most two 128-row scale blocks
+    const int hb = s.h0 + 16 * k.rt;
+    P.split = (hb / 128 + 1) * 128 - hb;
   }
 }
 
@@ -796,16 +851,15 @@ __device__ inline void load_pre(const Params& p, const Lds& L, const Sched& s, c
 // them then happens once, at this point (vmcnt(2) in the steady state), and
 // none of them is left with a load in flight that a later reuse of the
 // register would have to wait out with vmcnt(0).
-__device__ __forceinline__ void settle_pre(const Pre& P) {
-  asm volatile("" ::"v"(P.B[0]), "v"(P.B[1]), "v"(P.B[2]), "v"(P.B[3]), "v"(P.B[4]), "v"(P.B[5]),
-               "v"(P.B[6]), "v"(P.B[7]));
-  asm volatile("" ::"v"(P.B[8]), "v"(P.B[9]), "v"(P.B[10]), "v"(P.B[11]), "v"(P.B[12]),
-               "v"(P.B[13]), "v"(P.B[14]), "v"(P.B[15]));
-  asm volatile("" ::"v"(P.s_lo), "v"(P.s_hi), "v"(P.bscale));
+template <int NPRE>
+__device__ __forceinline__ void settle_pre(const Pre<NPRE>& P) {
+#pragma unroll
+  for (int i = 0; i < 4 * NPRE; ++i) asm volatile("" ::"v"(P.B[i]));
 }
 
-template <int F>
-__device__ inline void compute_chunk(const Chunk& k, const lds_char* stage, const Pre& P, f32x4* acc) {
+template <int F, int NPRE>
+__device__ inline void compute_chunk(const Params& p, const Lds& L, const Chunk& k,
+                                     const lds_char* stage, const Pre<NPRE>& P, f32x4* acc) {
   const int lane = threadIdx.x & 63, lg = lane >> 4, row = lane & 15;
   const int wave = wave_id();
   const int kb = k.kc * 8 + wave;
@@ -813,43 +867,63 @@ __device__ inline void compute_chunk(const Chunk& k, const lds_char* stage, cons
   bf16x8 A[4];
   if (F == 0) {
     u32x4 a0, a1;
-    lds_ld128x2(stage + row * kPitch + wave * 128 + 32 * lg, a0, a1);
+    uint32_t slo, shi;
+    lds_ld_fp8_block(stage + row * kPitch + wave * 128 + 32 * lg, stage + kScaleOff + 4 * wave, a0, a1, slo, shi);
     A[0] = e4m3x8_to_bf16(a0[0], a0[1]);
     A[1] = e4m3x8_to_bf16(a0[2], a0[3]);
     A[2] = e4m3x8_to_bf16(a1[0], a1[1]);
     A[3] = e4m3x8_to_bf16(a1[2], a1[3]);
+    const float s_lo = __uint_as_float(slo), s_hi = __uint_as_float(shi);
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
+    for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) {
       if (ct < P.nct) {
+        u32x4 Bl[4];
+        const u32x4* B = P.B + 4 * (ct < NPRE ? ct : 0);
+        if (ct >= NPRE) {
+          load_tile(p, L, k, kb, ct, group_ncols(p, L, k.g), Bl);
+          B = Bl;
+        }
         f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m = 0; m < 4; ++m) t = mfma16(A[m], __builtin_bit_cast(bf16x8, P.B[4 * ct + m]), t);
+        for (int m = 0; m < 4; ++m) t = mfma16(A[m], __builtin_bit_cast(bf16x8, B[m]), t);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[ct][q] = fmaf(t[q], 4 * lg + q < P.split ? P.s_lo : P.s_hi, acc[ct][q]);
+        for (int q = 0; q < 4; ++q) acc[ct][q] = fmaf(t[q], 4 * lg + q < P.split ? s_lo : s_hi, acc[ct][q]);
       }
     }
   } else {
-    const u32x4 a = lds_ld128(stage + row * kPitch + wave * 64 + 16 * lg);
-    const float sc = e8m0_to_f32(P.bscale);
+    u32x4 a;
+    uint32_t sw;
+    lds_ld_fp4_block(stage + row * kPitch + wave * 64 + 16 * lg, stage + kScaleOff + row * 32 + 4 * wave, a, sw);
+    const float sc = e8m0_to_f32((sw >> (8 * lg)) & 0xffu);
 #pragma unroll
     for (int m = 0; m < 4; ++m) A[m] = e2m1x8_to_bf16(a[m], sc);
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-      if (ct < P.nct)
+    for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) {
+      if (ct < P.nct) {
+        u32x4 Bl[4];
+        const u32x4* B = P.B + 4 * (ct < NPRE ? ct : 0);
+        if (ct >= NPRE) {
+          load_tile(p, L, k, kb, ct, group_ncols(p, L, k.g), Bl);
+          B = Bl;
+        }
 #pragma unroll
-        for (int m = 0; m < 4; ++m) acc[ct] = mfma16(A[m], __builtin_bit_cast(bf16x8, P.B[4 * ct + m]), acc[ct]);
+        for (int m = 0; m < 4; ++m) acc[ct] = mfma16(A[m], __builtin_bit_cast(bf16x8, B[m]), acc[ct]);
+      }
+    }
   }
 }
 
 // End of an up/gate job: sum the 8 waves' K-block partials in wave order,
 // mid = silu(gate) * up, rounded to bf16, stored at the column's (row, slot).
+// Two workgroup barriers per column tile (the producer waves replay them).
+template <int MAXCT>
 __device__ inline void reduce_up(const Params& p, const Lds& L, const Chunk& k, f32x4* acc, int nct) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ncols = group_ncols(p, L, k.g);
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
+  for (int ct = 0; ct < MAXCT; ++ct) {
     if (ct < nct) {
-      lds_st128(L.red + ((size_t)wave * 64 + lane) * 4, __builtin_bit_cast(u32x4, acc[ct]));
+      if (wave < kWaves) lds_st128(L.red + ((size_t)wave * 64 + lane) * 4, __builtin_bit_cast(u32x4, acc[ct]));
       bar_lds();
       if (tid < 128) {
         const int i = tid >> 4, cc = tid & 15, col = ct * 16 + cc;
@@ -875,13 +949,14 @@ __device__ inline void reduce_up(const Params& p, const Lds& L, const Chunk& k, 
 
 // End of a down row tile: sum the waves' partials in wave order into the
 // LDS products P[row][slot][h].
+template <int MAXCT>
 __device__ inline void reduce_down(const Params& p, const Lds& L, const Chunk& k, f32x4* acc, int nct) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ncols = group_ncols(p, L, k.g);
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
+  for (int ct = 0; ct < MAXCT; ++ct) {
     if (ct < nct) {
-      lds_st128(L.red + ((size_t)wave * 64 + lane) * 4, __builtin_bit_cast(u32x4, acc[ct]));
+      if (wave < kWaves) lds_st128(L.red + ((size_t)wave * 64 + lane) * 4, __builtin_bit_cast(u32x4, acc[ct]));
       bar_lds();
       if (tid < 256) {
         const int ln = tid >> 2, q = tid & 3;
@@ -915,22 +990,20 @@ __device__ inline void combine(const Params& p, const Lds& L, const Sched& s) {
 
 // ------------------------------------------------------------------ kernel
 
-template <int MODE, int FMT>
+template <int MODE, int FMT, int NPRE>
 __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const Lds L = lds_map(smem, p);
   lds_char* const st3 = (lds_char*)(smem + (L.stages - smem));
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x, wave = wave_id();
+  const bool producer = wave >= kWaves;
+  const int pw = wave - kWaves;
 
+  MOE_STAMP(p, 0);
   if (tid == 0)
     L.misc[1] = (int32_t)__hip_atomic_load(&p.flags[blockIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  const uint32_t epoch = (uint32_t)L.misc[1];
-
-  // S0: router logits of this CU's experts, published for every CU
-  router_logits(p);
-  publish(p, epoch + 1);
-  if (MODE != kModeForward && blockIdx.x != 0) return;
+  const uint32_t epoch = (uint32_t)__builtin_amdgcn_readfirstlane(L.misc[1]);
 
   Sched s;
   s.sh_tiles = (MODE == kModeForward && p.n_shared) ? p.Is / 8 : 0;
@@ -943,21 +1016,33 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   if (s.hc < 0) s.hc = 0;
   s.nrt = (s.hc + 15) / 16;
 
+  // Producer waves stream weight chunks into the LDS ring; they issue no
+  // other vector memory operation, so their in-order vmcnt tracks the ring
+  // exactly, and the compute waves' activation loads never queue behind a
+  // DMA.
   Pos ipos = {0, first_job(p, 0), 0, 0}, cpos;
   int n_i = 0, n_c = 0;
-  if (MODE == kModeForward) {
-    settle(p, s, ipos);
-    // S1: start streaming the shared expert's up/gate chunks before routing
-    while (n_i < p.ns - 2 && ipos.phase == 0 && !blocked(s, ipos)) {
-      issue_chunk(p, L, s, ipos, st3 + (n_i % p.ns) * kStageBytes);
+  settle(p, s, ipos);
+  // S1: the shared expert's up/gate chunks need no routing: start them now
+  if (MODE == kModeForward && producer) {
+    while (n_i < p.ns - 1 && ipos.phase == 0 && !blocked(s, ipos)) {
+      issue_chunk(p, L, s, ipos, st3 + (n_i % p.ns) * kStageBytes, pw);
       advance(p, s, ipos);
       ++n_i;
     }
   }
 
+  // S0: router logits of this CU's experts, published for every CU
+  router_logits(p);
+  publish(p, epoch + 1);
+  MOE_STAMP(p, 1);
+  if (MODE != kModeForward && blockIdx.x != 0) return;
+
   // S2: route every row, then group the step's distinct experts
   wait_all(p, epoch + 1);
-  for (int r = wave; r < p.T; r += kWaves) route_row(p, L, r);
+  MOE_STAMP(p, 2);
+  if (!producer)
+    for (int r = wave; r < p.T; r += kWaves) route_row(p, L, r);
   __syncthreads();
   if (MODE == kModeRoute) {
     for (int u = tid; u < p.T * p.K; u += kThreads) {
@@ -967,7 +1052,8 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
     return;
   }
   build_groups(p, L);
-  const int G = L.misc[0];
+  MOE_STAMP(p, 3);
+  const int G = __builtin_amdgcn_readfirstlane(L.misc[0]);
   if (MODE == kModeGroups) {
     int32_t* o = p.groups_out;
     if (tid == 0) {
@@ -996,78 +1082,109 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   bool passed2 = false;
   auto cross_to_down = [&](const Pos& c) {
     if (!passed2 && c.phase >= 2) {
+      MOE_STAMP(p, 4);
       publish(p, epoch + 2);
       if (c.phase == 2) wait_all(p, epoch + 2);
+      MOE_STAMP(p, 5);
       passed2 = true;
     }
   };
-  // The activations of chunk n+1 are loaded into the same registers right
-  // after chunk n's MFMAs have read them, one step ahead of their use.
-  Pre pre;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) pre.B[i] = u32x4{0u, 0u, 0u, 0u};
-  pre.s_lo = pre.s_hi = 1.f;
-  pre.split = 0;
-  pre.nct = 0;
-  pre.bscale = 127u;
-  f32x4 acc[4];
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#ifdef MOE_LAPS
+  uint64_t cyc[6] = {0, 0, 0, 0, 0, 0};
+  uint64_t tq = __builtin_amdgcn_s_memtime();
+#define MOE_LAP(i)                                    \
+  do {                                                \
+    const uint64_t t2 = __builtin_amdgcn_s_memtime(); \
+    cyc[i] += t2 - tq;                                \
+    tq = t2;                                          \
+  } while (0)
+#else
+#define MOE_LAP(i) \
+  do {             \
+  } while (0)
+#endif
 
-  // Fill the ring to ns - 2 chunks, prefetch the first chunk's activations,
-  // then issue exactly one more DMA pair (the next chunk, or placeholders):
-  // the loop is entered in the same state its back edge leaves it in.
-  lds_char* const dummy3 = (lds_char*)(smem + (L.dummy - smem));
-  while (ipos.phase < 3 && n_i < n_c + p.ns - 2) {
-    issue_chunk(p, L, s, ipos, st3 + (n_i % p.ns) * kStageBytes);
-    advance(p, s, ipos);
-    ++n_i;
-  }
-  cross_to_down(cpos);
-  if (cpos.phase < 3) load_pre(p, L, s, chunk_of(p, L, s, cpos), pre);
-  asm volatile("" ::: "memory");
-  if (ipos.phase < 3) {
-    issue_chunk(p, L, s, ipos, st3 + (n_i % p.ns) * kStageBytes);
-    advance(p, s, ipos);
-    ++n_i;
-  } else {
-    issue_dummy(p, dummy3);
-  }
-  int W = 2;
-
-  // One step: wait for this chunk's DMA and activations, multiply, close the
-  // job if it ends here, prefetch the next chunk's activations, then (main
-  // loop only) refill the stage freed by the previous chunk.  The main loop
-  // issues exactly two DMAs per wave after every prefetch, so a wait for the
-  // prefetched registers is vmcnt(2) and never drains the ring; the drain
-  // loop issues none.
-  auto step = [&](bool refill) {
-    wait_vm(W);
-    bar_lds();
-    const Chunk k = chunk_of(p, L, s, cpos);
-    const lds_char* stage = st3 + (n_c % p.ns) * kStageBytes;
-    settle_pre(pre);
-    if (k.fmt == 0) compute_chunk<0>(k, stage, pre, acc);
-    else compute_chunk<FMT>(k, stage, pre, acc);
-    if (cpos.kc == chunk_count(p, cpos) - 1) {
-      if (k.kind == 1) reduce_up(p, L, k, acc, pre.nct);
-      else reduce_down(p, L, k, acc, pre.nct);
-    }
-    advance(p, s, cpos);
-    ++n_c;
-    cross_to_down(cpos);
-    if (cpos.phase < 3) load_pre(p, L, s, chunk_of(p, L, s, cpos), pre);
-    asm volatile("" ::: "memory");
-    W = 0;
-    if (refill) {
-      issue_chunk(p, L, s, ipos, st3 + (n_i % p.ns) * kStageBytes);
+  // One step: the producers wait for chunk n to land (the chunks after it
+  // stay in flight), everyone meets, the compute waves multiply chunk n and
+  // prefetch the activations of chunk n+1, a job ending here is reduced, and
+  // the producers refill the stage chunk n-1 freed with chunk n+ns-1.
+  // Producer and compute waves run separate loops that meet at the same
+  // sequence of barriers: the top of each step, two per column tile of a
+  // reduction, and the flag hand-over.  Kept apart, the producers' code
+  // holds no load into a register, so nothing makes them drain the ring.
+  if (producer) {
+    while (ipos.phase < 3 && n_i < n_c + p.ns - 1) {
+      issue_chunk(p, L, s, ipos, st3 + (n_i % p.ns) * kStageBytes, pw);
       advance(p, s, ipos);
       ++n_i;
-      W = 2;
     }
-  };
-  while (ipos.phase < 3) step(true);
-  while (cpos.phase < 3) step(false);
+    cross_to_down(cpos);
+    while (cpos.phase < 3) {
+      wait_vm(9 * (n_i - 1 - n_c));
+      MOE_LAP(0);
+      bar_lds();
+      MOE_LAP(1);
+      if (cpos.kc == chunk_count(p, cpos) - 1) {
+        const int g = cpos.phase <= 1 ? chunk_group(p, s, cpos) : cpos.j;
+        const int nct = (group_ncols(p, L, g) + 15) >> 4;
+        for (int ct = 0; ct < nct; ++ct) {
+          bar_lds();
+          bar_lds();
+        }
+      }
+      MOE_LAP(3);
+      advance(p, s, cpos);
+      ++n_c;
+      cross_to_down(cpos);
+      MOE_LAP(4);
+      if (ipos.phase < 3 && n_i < n_c + p.ns - 1) {
+        issue_chunk(p, L, s, ipos, st3 + (n_i % p.ns) * kStageBytes, pw);
+        advance(p, s, ipos);
+        ++n_i;
+      }
+      MOE_LAP(5);
+    }
+  } else {
+    constexpr int MAXCT = max_tiles<NPRE>();
+    Pre<NPRE> pre;
+    f32x4 acc[MAXCT];
+#pragma unroll
+    for (int ct = 0; ct < MAXCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    cross_to_down(cpos);
+    if (cpos.phase < 3) load_pre(p, L, s, chunk_of(p, L, s, cpos), pre);
+    while (cpos.phase < 3) {
+      MOE_LAP(0);
+      bar_lds();
+      MOE_LAP(1);
+      const Chunk k = chunk_of(p, L, s, cpos);
+      const lds_char* stage = st3 + (n_c % p.ns) * kStageBytes;
+      settle_pre(pre);
+      if (k.fmt == 0) compute_chunk<0>(p, L, k, stage, pre, acc);
+      else compute_chunk<FMT>(p, L, k, stage, pre, acc);
+      MOE_LAP(2);
+      if (cpos.kc == chunk_count(p, cpos) - 1) {
+        if (k.kind == 1) reduce_up<MAXCT>(p, L, k, acc, pre.nct);
+        else reduce_down<MAXCT>(p, L, k, acc, pre.nct);
+      }
+      MOE_LAP(3);
+      advance(p, s, cpos);
+      ++n_c;
+      cross_to_down(cpos);
+      MOE_LAP(4);
+      if (cpos.phase >= 3) break;
+      load_pre(p, L, s, chunk_of(p, L, s, cpos), pre);
+      MOE_LAP(5);
+    }
+  }
+#ifdef MOE_LAPS
+  if (p.timeline && (threadIdx.x == 0 || threadIdx.x == 64 * kWaves)) {
+    if (threadIdx.x == 0)
+      for (int i = 0; i < 6; ++i) p.timeline[blockIdx.x * 16 + 10 + i] = cyc[i];
+    else
+      for (int i = 0; i < 6; ++i) p.timeline[1024 * 16 - 256 * 8 + blockIdx.x * 8 + i] = cyc[i];
+  }
+#endif
+  MOE_STAMP(p, 6);
   if (!passed2) {
     publish(p, epoch + 2);
     passed2 = true;
@@ -1076,6 +1193,11 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
 
   // S5: combine this CU's output rows
   combine(p, L, s);
+  MOE_STAMP(p, 7);
+  if (threadIdx.x == 0 && p.timeline) {
+    p.timeline[blockIdx.x * 16 + 8] = (uint64_t)n_c;
+    p.timeline[blockIdx.x * 16 + 9] = (uint64_t)p.ns;
+  }
 }
 
 // ------------------------------------------------------------------ host glue
@@ -1092,9 +1214,9 @@ WsLayout ws_layout(int max_rows, int E, int K, int I, int Is) {
   return w;
 }
 
-template <int MODE, int FMT>
+template <int MODE, int FMT, int NPRE = 1>
 static hipError_t launch_one(const Params& p, hipStream_t stream) {
-  auto kfn = moe_fused<MODE, FMT>;
+  auto kfn = moe_fused<MODE, FMT, NPRE>;
   hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kfn, dim3(p.ncu), dim3(kThreads), p.lds_bytes, stream, p);
@@ -1102,12 +1224,15 @@ static hipError_t launch_one(const Params& p, hipStream_t stream) {
 }
 
 hipError_t launch(const Params& p, int mode, hipStream_t stream) {
+  const bool wide = p.T > 16;  // some group may have more than one 16-column tile
   if (p.routed_fmt == 0) {
-    if (mode == kModeForward) return launch_one<kModeForward, 0>(p, stream);
+    if (mode == kModeForward)
+      return wide ? launch_one<kModeForward, 0, 2>(p, stream) : launch_one<kModeForward, 0, 1>(p, stream);
     if (mode == kModeRoute) return launch_one<kModeRoute, 0>(p, stream);
     return launch_one<kModeGroups, 0>(p, stream);
   }
-  if (mode == kModeForward) return launch_one<kModeForward, 1>(p, stream);
+  if (mode == kModeForward)
+    return wide ? launch_one<kModeForward, 1, 2>(p, stream) : launch_one<kModeForward, 1, 1>(p, stream);
   if (mode == kModeRoute) return launch_one<kModeRoute, 1>(p, stream);
   return launch_one<kModeGroups, 1>(p, stream);
 }
