@@ -89,7 +89,7 @@ int fill(const moe_config* c, const moe_weights* w, const uint16_t* x, int rows,
   if (rows == 0) return kNoRows;  // a no-op: x, out and ws may be NULL
   if (!x || !ws) return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(ws)) return MOE_ERR_ALIGN;
-  const WsLayout L = ws_layout(c->max_rows, c->n_experts, c->top_k, c->inter,
+  const WsLayout L = ws_layout(c->max_rows, c->n_experts, c->top_k, c->hidden, c->inter,
                                c->n_shared ? c->shared_inter : 0);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   const DevInfo d = dev_info();
@@ -138,6 +138,7 @@ int fill(const moe_config* c, const moe_weights* w, const uint16_t* x, int rows,
   p.err = (uint32_t*)(base + L.err);
   p.scores = (double*)(base + L.scores);
   p.mid = (uint16_t*)(base + L.mid);
+  p.prod = rows > kLdsProdRows ? (float*)(base + L.prod) : nullptr;
 #ifdef MOE_TIMELINE
   p.timeline = (uint64_t*)(base + L.total);  // callers of a timeline build add 1024*16*8 bytes
   if (ws_bytes < L.total + 1024 * 16 * 8) return MOE_ERR_WORKSPACE;
@@ -162,7 +163,7 @@ int moe_workspace_size(const moe_config* cfg, size_t* bytes) {
   if (!bytes) return MOE_ERR_NULL;
   int rc = check_cfg(cfg);
   if (rc) return rc;
-  *bytes = ws_layout(cfg->max_rows, cfg->n_experts, cfg->top_k, cfg->inter,
+  *bytes = ws_layout(cfg->max_rows, cfg->n_experts, cfg->top_k, cfg->hidden, cfg->inter,
                      cfg->n_shared ? cfg->shared_inter : 0).total;
   return MOE_OK;
 }
@@ -170,7 +171,7 @@ int moe_workspace_size(const moe_config* cfg, size_t* bytes) {
 int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   if (!ws) return MOE_ERR_NULL;
   if (!aligned16(ws)) return MOE_ERR_ALIGN;
-  const WsLayout L = ws_layout(1, 1, 1, 128, 0);
+  const WsLayout L = ws_layout(1, 1, 1, 128, 128, 0);
   if (ws_bytes < L.scores) return MOE_ERR_WORKSPACE;
   hipError_t e = hipMemsetAsync(ws, 0, L.scores, (hipStream_t)stream);
   if (e != hipSuccess) {
@@ -223,7 +224,7 @@ int moe_forward(const moe_config* cfg, const moe_weights* w, const uint16_t* x, 
 
 int moe_read_error(void* ws, void* stream, uint32_t* bits) {
   if (!ws || !bits) return MOE_ERR_NULL;
-  const WsLayout L = ws_layout(1, 1, 1, 128, 0);
+  const WsLayout L = ws_layout(1, 1, 1, 128, 128, 0);
   uint32_t* err = (uint32_t*)((char*)ws + L.err);
   hipError_t e = hipMemcpyAsync(bits, err, 4, hipMemcpyDeviceToHost, (hipStream_t)stream);
   if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);

@@ -23,9 +23,13 @@ enum Mode { kModeForward = 0, kModeRoute = 1, kModeGroups = 2 };
 
 // Workspace layout (byte offsets from the workspace base).
 struct WsLayout {
-  size_t flags, err, scores, mid, total;
+  size_t flags, err, scores, mid, prod, total;
   int mid_ld;  // bf16 elements per (row, slot) line of mid
 };
+
+// Batches above this many rows keep the down products in the workspace
+// instead of LDS (their LDS goes to the ring and the job-end partials).
+constexpr int kLdsProdRows = 16;
 
 struct Params {
   // shape
@@ -59,10 +63,11 @@ struct Params {
   uint32_t* err;
   double* scores;  // [T][E][2]: s, b
   uint16_t* mid;   // [T][K+1][mid_ld] bf16
+  float* prod;     // wide batches: [ncu][T][K+1][hs] fp32 down products (else NULL)
   uint64_t* timeline;  // optional phase stamps ([ncu][16]); NULL unless built with MOE_TIMELINE
 };
 
-WsLayout ws_layout(int max_rows, int E, int K, int I, int Is);
+WsLayout ws_layout(int max_rows, int E, int K, int H, int I, int Is);
 // LDS bytes for a call and the number of weight stages that fit in max_lds
 // (*ns < 2: does not fit).
 size_t lds_plan(int T, int K, int E, int hs, size_t max_lds, int* ns);

@@ -134,8 +134,7 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; 
 // 16-byte pad puts the 16 rows an MFMA tile reads in one ds_read_b128 on
 // different LDS banks.
 constexpr int kPitch = 1040;
-constexpr int kScaleOff = 16 * kPitch;          // the chunk's weight scales follow its rows
-constexpr int kStageBytes = kScaleOff + 512;
+constexpr int kStageBytes = 16 * kPitch;
 constexpr int kChunkElems = 1024;
 
 struct Lds {
@@ -149,18 +148,25 @@ struct Lds {
   int32_t* gstart;   // [1+T*K]
   int32_t* cols;     // [T*(K+1)] row*16 + slot
   int32_t* misc;     // [32]: 0 = G, 1 = epoch, 8.. = scan
-  float* red;        // [kWaves][64][4] cross-wave reduction
-  double* rb;        // [kWaves][E] router keys (aliases pbuf)
+  uint32_t* ctl;     // [64] chunk-stream counters (see kCtl*)
+  float* red;        // [red_slots][red_tiles][kWaves][64][4] job-end partials
+  double* rb;        // [kWaves][E] router keys (aliases red and pbuf)
   double* rgs;       // [kWaves][64] group scores
   int32_t* rkept;    // [kWaves][64]
-  float* pbuf;       // [T*(K+1)][hs] down products
+  float* pbuf;       // [T*(K+1)][hs] down products (batches of at most 16 rows)
   char* stages;      // [ns][kStageBytes]
 };
 
 __host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Job-end partials: up to 16 columns per tile when a batch has at most 16
+// rows (one tile, two slots), else 4 tiles in one slot.
+__host__ __device__ inline int red_tiles(int T) { return T > 16 ? kMaxRows / 16 : 1; }
+__host__ __device__ inline int red_slots(int T) { return T > 16 ? 1 : 2; }
+constexpr size_t kRedTileBytes = 16 * (size_t)kWaves * 64;  // one tile: [wave][lane] f32x4
+
 struct LdsOffsets {
-  size_t ids, w, first, egrp, rmask, gexp, gcnt, gstart, cols, misc, red, pbuf, stages;
+  size_t ids, w, first, egrp, rmask, gexp, gcnt, gstart, cols, misc, ctl, red, pbuf, stages;
 };
 
 __host__ __device__ inline LdsOffsets lds_offsets(int T, int K, int E, int hs) {
@@ -177,11 +183,15 @@ __host__ __device__ inline LdsOffsets lds_offsets(int T, int K, int E, int hs) {
   o.gstart = q; q = align_up(q + 4 * (size_t)gmax, 16);
   o.cols = q; q = align_up(q + 4 * (size_t)T * (K + 1), 16);
   o.misc = q; q = align_up(q + 4 * 32, 16);
-  o.red = q; q = align_up(q + 16 * (size_t)kWaves * 64, 16);
-  o.pbuf = q;
-  size_t pb = 4 * (size_t)T * (K + 1) * hs;
-  size_t rs = 8 * (size_t)kWaves * E + 8 * (size_t)kWaves * 64 + 4 * (size_t)kWaves * 64;
-  q = align_up(q + (pb > rs ? pb : rs), 16);
+  o.ctl = q; q = align_up(q + 4 * 64, 16);
+  // the routing scratch (used before the stream) overlaps the job-end
+  // partials and the down products (used in it)
+  o.red = q;
+  const size_t rd = (size_t)red_slots(T) * red_tiles(T) * kRedTileBytes;
+  o.pbuf = q + rd;
+  const size_t pb = T > kLdsProdRows ? 0 : 4 * (size_t)T * (K + 1) * hs;
+  const size_t rs = 8 * (size_t)kWaves * E + 8 * (size_t)kWaves * 64 + 4 * (size_t)kWaves * 64;
+  q = align_up(q + (rd + pb > rs ? rd + pb : rs), 16);
   o.stages = q;
   return o;
 }
@@ -211,9 +221,10 @@ __device__ inline Lds lds_map(char* base, const Params& p) {
   L.gstart = (int32_t*)(base + o.gstart);
   L.cols = (int32_t*)(base + o.cols);
   L.misc = (int32_t*)(base + o.misc);
+  L.ctl = (uint32_t*)(base + o.ctl);
   L.red = (float*)(base + o.red);
   L.pbuf = (float*)(base + o.pbuf);
-  L.rb = (double*)(base + o.pbuf);
+  L.rb = (double*)(base + o.red);
   L.rgs = L.rb + (size_t)kWaves * p.E;
   L.rkept = (int32_t*)(L.rgs + (size_t)kWaves * 64);
   L.stages = base + o.stages;
@@ -241,25 +252,29 @@ __device__ inline void publish(const Params& p, uint32_t value) {
 // Wait until every CU's flag has reached `target` (wrap-around safe), then
 // acquire.  Wave 0 polls and acquires; the barrier after it orders the rest
 // of the workgroup (bare s_barrier, as in publish).
-__device__ inline void wait_all(const Params& p, uint32_t target) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    int spins = 0;
-    for (;;) {
-      bool ok = true;
-      for (int i = lane; i < p.ncu; i += 64) {
-        uint32_t v = __hip_atomic_load(&p.flags[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ok = ok && ((int32_t)(v - target) >= 0);
-      }
-      if (__all(ok)) break;
-      if (++spins > kSpinLimit) {
-        if (lane == 0) set_err(p.err, kErrTimeout);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
+// One wave polls every CU's flag until all have reached `target`
+// (wrap-around safe), then acquires at agent scope.
+__device__ inline void poll_flags(const Params& p, uint32_t target) {
+  const int lane = threadIdx.x & 63;
+  int spins = 0;
+  for (;;) {
+    bool ok = true;
+    for (int i = lane; i < p.ncu; i += 64) {
+      uint32_t v = __hip_atomic_load(&p.flags[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ok = ok && ((int32_t)(v - target) >= 0);
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (__all(ok)) break;
+    if (++spins > kSpinLimit) {
+      if (lane == 0) set_err(p.err, kErrTimeout);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
   }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+__device__ inline void wait_all(const Params& p, uint32_t target) {
+  if (threadIdx.x < 64) poll_flags(p, target);
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -273,7 +288,8 @@ __device__ inline double load_bias(const Params& p, int e) {
 }
 
 // l[r][e] = sum_h x[r][h] * Wr[e][h]: lane l sums h = 8l + 512j + 0..7 in
-// order, then a fixed xor butterfly; one wave per (row, expert).
+// order, then a fixed xor butterfly; one wave per (row, expert).  The loads
+// of up to 8 j are issued before their products are summed.
 __device__ inline void router_logits(const Params& p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (wave >= kWaves) return;
@@ -283,13 +299,24 @@ __device__ inline void router_logits(const Params& p) {
     for (int r = wave; r < p.T; r += kWaves) {
       const uint16_t* xr = p.x + (size_t)r * p.H;
       double acc = 0.0;
-      for (int h = 8 * lane; h < p.H; h += 512) {
-        u32x4 xv = ld16(xr + h), wv = ld16(wr + h);
+      for (int h0 = 8 * lane; h0 < p.H; h0 += 512 * 8) {
+        u32x4 xv[8], wv[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t xa = xv[j], wa = wv[j];
-          acc = fma((double)bf16_bits_to_f32(xa & 0xffffu), (double)bf16_bits_to_f32(wa & 0xffffu), acc);
-          acc = fma((double)bf16_bits_to_f32(xa >> 16), (double)bf16_bits_to_f32(wa >> 16), acc);
+        for (int j = 0; j < 8; ++j) {
+          const int h = h0 + 512 * j < p.H ? h0 + 512 * j : h0;
+          xv[j] = ld16(xr + h);
+          wv[j] = ld16(wr + h);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (h0 + 512 * j < p.H) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t xa = xv[j][i], wa = wv[j][i];
+              acc = fma((double)bf16_bits_to_f32(xa & 0xffffu), (double)bf16_bits_to_f32(wa & 0xffffu), acc);
+              acc = fma((double)bf16_bits_to_f32(xa >> 16), (double)bf16_bits_to_f32(wa >> 16), acc);
+            }
+          }
         }
       }
 #pragma unroll
@@ -318,13 +345,14 @@ __device__ __forceinline__ bool key_before(double b1, int e1, double b2, int e2)
 __device__ inline void route_row(const Params& p, const Lds& L, int r) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const double* sc = p.scores + (size_t)r * p.E * 2;
-  double bv[4];
+  double bv[4], sv[4];
   bool alive[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
     alive[i] = e < p.E;
     double b = alive[i] ? sc[2 * e + 1] : -INFINITY;
+    sv[i] = alive[i] ? sc[2 * e] : 0.0;
     bv[i] = isnan(b) ? -INFINITY : b;
   }
   if (p.ng > 1) {
@@ -360,6 +388,7 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r) {
   }
   double ssum = 0.0;
   int picks[kMaxTopK];
+  double pick_s[kMaxTopK];
 #pragma unroll
   for (int k = 0; k < kMaxTopK; ++k) {
     if (k < p.K) {
@@ -380,17 +409,21 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (lane + 64 * i == be) alive[i] = false;
+      // the pick's score s, from the lane that holds it
+      const int slot = be >> 6;
+      const double mine = slot == 0 ? sv[0] : slot == 1 ? sv[1] : slot == 2 ? sv[2] : sv[3];
+      const double sp = __shfl(mine, be & 63, 64);
       picks[k] = be;
-      ssum += sc[2 * be];
+      pick_s[k] = sp;
+      ssum += sp;
     }
   }
   if (lane == 0) {
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k) {
       if (k < p.K) {
-        const int e = picks[k];
-        L.ids[r * p.K + k] = e;
-        L.w[r * p.K + k] = (float)(sc[2 * e] / ssum * p.routed_scale);
+        L.ids[r * p.K + k] = picks[k];
+        L.w[r * p.K + k] = (float)(pick_s[k] / ssum * p.routed_scale);
       }
     }
   }
@@ -484,6 +517,11 @@ typedef __attribute__((address_space(3))) char lds_char;
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// Wave-uniform loop state, re-asserted as uniform: the compiler's uniformity
+// analysis loses track of it across the stream loops (asm results, loop
+// exits), and then keeps it in vector registers behind masked branches.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 // One row segment of up to 1 KB into LDS: 64 lanes x 16 B through a buffer
 // resource whose size is the segment's valid bytes, so lanes past the end
 // (a ragged tail, or a row with no valid bytes) read zeros without touching
@@ -507,16 +545,18 @@ __device__ __forceinline__ void dma_row(const uint8_t* base, int nbytes, lds_cha
 }
 
 // Waits until at most n of this wave's vector memory operations are
-// outstanding (n is a multiple of 9: a producer issues 9 DMAs per chunk).
+// outstanding (n is a multiple of 8: a producer issues 8 DMAs per chunk and
+// keeps at most 7 chunks in flight, 56 operations, within the counter's 63).
 __device__ __forceinline__ void wait_vm(int n) {
   switch (n) {
     case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
-    case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
-    case 27: asm volatile("s_waitcnt vmcnt(27)" ::: "memory"); break;
-    case 36: asm volatile("s_waitcnt vmcnt(36)" ::: "memory"); break;
-    case 45: asm volatile("s_waitcnt vmcnt(45)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(54)" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    case 24: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+    case 32: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
+    case 40: asm volatile("s_waitcnt vmcnt(40)" ::: "memory"); break;
+    case 48: asm volatile("s_waitcnt vmcnt(48)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(56)" ::: "memory"); break;
   }
 }
 
@@ -549,53 +589,130 @@ __device__ __forceinline__ float lds_ldf(P p) { return __uint_as_float(lds_ld32(
 __device__ __forceinline__ int lds_ldi_uniform(const int32_t* p) {
   return __builtin_amdgcn_readfirstlane((int)lds_ld32(p));
 }
+// Stores are not waited for: a wave's LDS operations complete in order, so
+// a later flag store is seen after the data it publishes, and every reader
+// waits for its own reads.  (A compiler-placed lgkmcnt wait that follows
+// stays sufficient: an extra older operation completes first.)
 __device__ __forceinline__ void lds_st32(void* p, uint32_t v) {
-  asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(lds_off(p)), "v"(v) : "memory");
+  asm volatile("ds_write_b32 %0, %1" ::"v"(lds_off(p)), "v"(v) : "memory");
 }
 __device__ __forceinline__ void lds_st128(void* p, u32x4 v) {
-  asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(lds_off(p)), "v"(v) : "memory");
+  asm volatile("ds_write_b128 %0, %1" ::"v"(lds_off(p)), "v"(v) : "memory");
 }
-// A lane's part of one K-block of the stage with its scales, in one round
-// trip: FP8, 32 weight bytes and the two 128-row block scales (the second
-// one 32 bytes after the first); MXFP4, 16 weight bytes and a dword of the
-// row's E8M0 scales.
-template <class P>
-__device__ __forceinline__ void lds_ld_fp8_block(P w, P sc, u32x4& a, u32x4& b, uint32_t& s0, uint32_t& s1) {
-  asm volatile(
-      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:16\n\t"
-      "ds_read_b32 %2, %5\n\tds_read_b32 %3, %5 offset:32\n\ts_waitcnt lgkmcnt(0)"
-      : "=&v"(a), "=&v"(b), "=&v"(s0), "=&v"(s1)
-      : "v"(lds_off(w)), "v"(lds_off(sc))
-      : "memory");
+// Chunk-stream counters in LDS.  Every counter counts up from 0 within a
+// launch and is written by one wave only.
+constexpr int kCtlReady = 0;   // [2]  chunks producer pw has landed in LDS
+constexpr int kCtlDone = 8;    // [8]  chunks compute wave w has finished reading
+constexpr int kCtlPart = 16;   // [8]  jobs whose partials wave w has stored
+constexpr int kCtlSlot = 24;   // [2]  1 + the last job summed out of partial slot s
+constexpr int kCtlMidOut = 40; // [8]  1 once wave w's mid stores are complete
+constexpr int kCtlCrossed = 48;// [1]  1 once wave 0 has seen every CU's mid
+
+// Minimum of N consecutive LDS counters (N = 1, 2 or 8), one round trip.
+// Every lane reads the same words; the result is taken through
+// readfirstlane so the compiler knows it is uniform (an asm result is
+// otherwise assumed divergent, and every branch on it becomes a masked one).
+template <int N>
+__device__ __forceinline__ uint32_t lds_min(const uint32_t* a) {
+  if (N == 1) {
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_off(a)) : "memory");
+    return __builtin_amdgcn_readfirstlane(v);
+  } else if (N == 2) {
+    uint64_t v;
+    asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_off(a)) : "memory");
+    const uint32_t v0 = (uint32_t)v, v1 = (uint32_t)(v >> 32);
+    return __builtin_amdgcn_readfirstlane(v0 < v1 ? v0 : v1);
+  } else {
+    u32x4 a0, a1;
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(a0), "=&v"(a1) : "v"(lds_off(a)) : "memory");
+    uint32_t m = a0[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) m = a0[i] < m ? a0[i] : m;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = a1[i] < m ? a1[i] : m;
+    return __builtin_amdgcn_readfirstlane(m);
+  }
 }
+
+// Spins until the minimum of N counters reaches `target`.  Bounded: on
+// timeout the error bit is set and `ok` latches false, after which every
+// wait of this wave returns at once (the kernel then finishes with wrong
+// values, never hangs).
+template <int N>
+__device__ inline uint32_t lds_wait(const Params& p, const uint32_t* a, uint32_t target, bool& ok) {
+  if (!ok) return target;
+  int spins = 0;
+  uint32_t v;
+  while ((v = lds_min<N>(a)) < target) {
+    if (++spins > kSpinLimit) {
+      set_err(p.err, kErrTimeout);
+      ok = false;
+      return target;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return v;
+}
+
+// A lane's part of one K-block of the stage, in one round trip: FP8, 32
+// weight bytes; MXFP4, 16.
 template <class P>
-__device__ __forceinline__ void lds_ld_fp4_block(P w, P sc, u32x4& a, uint32_t& s0) {
-  asm volatile("ds_read_b128 %0, %2\n\tds_read_b32 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-               : "=&v"(a), "=&v"(s0)
-               : "v"(lds_off(w)), "v"(lds_off(sc))
+__device__ __forceinline__ void lds_ld_fp8_block(P w, u32x4& a, u32x4& b) {
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(a), "=&v"(b)
+               : "v"(lds_off(w))
                : "memory");
 }
+template <class P>
+__device__ __forceinline__ void lds_ld_fp4_block(P w, u32x4& a) {
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(a) : "v"(lds_off(w)) : "memory");
+}
 
-// Per-lane prefetch of one chunk: the activations of column tiles
-// 0..NPRE-1 (later tiles are loaded when used), and where the FP8 scale
-// changes inside the 16-row weight tile.  NPRE is 1 for batches of at most
-// 16 rows (no group has more than 16 columns) and 2 above.
-template <int NPRE>
-struct Pre {
-  u32x4 B[4 * NPRE];
-  int split;         // FP8: MFMA output rows (4*lg + q) below it take the first scale
-  int nct;
-};
+// LDS partials of a cross-wave reduction: wave w's f32x4 of lane l at
+// red[(w*64 + l)*4 ..], so one lane's eight partials sit 1 KB apart.  These
+// read a thread's 8 (down) or 2 x 8 (up/gate: gate at +0, up at +512 B)
+// partials in one round trip.
+__device__ __forceinline__ void lds_ld_partials8(const float* p, float (&a)[8]) {
+  asm volatile(
+      "ds_read_b32 %0, %8\n\tds_read_b32 %1, %8 offset:1024\n\t"
+      "ds_read_b32 %2, %8 offset:2048\n\tds_read_b32 %3, %8 offset:3072\n\t"
+      "ds_read_b32 %4, %8 offset:4096\n\tds_read_b32 %5, %8 offset:5120\n\t"
+      "ds_read_b32 %6, %8 offset:6144\n\tds_read_b32 %7, %8 offset:7168\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]), "=&v"(a[7])
+      : "v"(lds_off(p))
+      : "memory");
+}
+__device__ __forceinline__ void lds_ld_partials16(const float* p, float (&a)[8], float (&b)[8]) {
+  asm volatile(
+      "ds_read_b32 %0, %16\n\tds_read_b32 %1, %16 offset:1024\n\t"
+      "ds_read_b32 %2, %16 offset:2048\n\tds_read_b32 %3, %16 offset:3072\n\t"
+      "ds_read_b32 %4, %16 offset:4096\n\tds_read_b32 %5, %16 offset:5120\n\t"
+      "ds_read_b32 %6, %16 offset:6144\n\tds_read_b32 %7, %16 offset:7168\n\t"
+      "ds_read_b32 %8, %16 offset:512\n\tds_read_b32 %9, %16 offset:1536\n\t"
+      "ds_read_b32 %10, %16 offset:2560\n\tds_read_b32 %11, %16 offset:3584\n\t"
+      "ds_read_b32 %12, %16 offset:4608\n\tds_read_b32 %13, %16 offset:5632\n\t"
+      "ds_read_b32 %14, %16 offset:6656\n\tds_read_b32 %15, %16 offset:7680\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]), "=&v"(a[7]),
+        "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(b[4]), "=&v"(b[5]), "=&v"(b[6]), "=&v"(b[7])
+      : "v"(lds_off(p))
+      : "memory");
+}
 
-// Column tiles a group can have: 1 when NPRE is 1, else up to 4 (64 rows).
+// Column tiles a group can have: 1 when NPRE is 1 (batches of at most 16
+// rows), else up to 4 (64 rows).
 template <int NPRE>
 constexpr int max_tiles() { return NPRE == 1 ? 1 : kMaxRows / 16; }
 
-struct Pos {
-  int phase;  // 0 shared up/gate, 1 routed up/gate, 2 down, 3 end
-  int j;      // up/gate: global job index; down: group
-  int rt;     // down: 16-row tile of this CU's slice
-  int kc;     // chunk along the reduction axis
+// Per-lane prefetch of one chunk: the activations of column tiles
+// 0..NPRE-1; later tiles are loaded when used.
+template <int NPRE>
+struct Pre {
+  u32x4 B[4 * NPRE];
+  uint32_t sw;  // MXFP4: this lane's row's four E8M0 scales of its K-block
 };
 
 struct Sched {
@@ -608,13 +725,25 @@ struct Sched {
   int routed;
 };
 
-struct Chunk {
-  int kind;  // 1 up/gate, 2 down
-  int g, tile, rt, kc;
-  int fmt, iexp, kdim, nlive;
-  const uint8_t* w;
-  const void* s;
+// Position in this CU's job sequence.  A job is one up/gate tile of a group
+// (8 gate + 8 up rows of W_gate_up over all of H) or one 16-row tile of this
+// CU's down rows for a group (over the group's intermediate size); it is
+// streamed as nchunks(K) chunks.
+struct It {
+  int phase;  // 0 shared up/gate, 1 routed up/gate, 2 down, 3 end
+  int j;      // up/gate: global job index; down: group
+  int rt;     // down: 16-row tile of this CU's slice
+  int g;      // the job's group (kept current by settle / next_job)
+  int tile;   // up/gate: its 8-intermediate tile of that group
 };
+
+__device__ __forceinline__ void uni(It& c) {
+  c.phase = uni(c.phase);
+  c.j = uni(c.j);
+  c.rt = uni(c.rt);
+  c.g = uni(c.g);
+  c.tile = uni(c.tile);
+}
 
 __device__ __forceinline__ int nchunks(int kdim) { return (kdim + kChunkElems - 1) / kChunkElems; }
 
@@ -624,22 +753,23 @@ __device__ __forceinline__ int first_job(const Params& p, int begin) {
   return begin + (((int)blockIdx.x - r) % p.ncu + p.ncu) % p.ncu;
 }
 
-__device__ __forceinline__ int chunk_count(const Params& p, const Pos& c) {
-  if (c.phase <= 1) return nchunks(p.H);
-  return nchunks((p.n_shared && c.j == 0) ? p.Is : p.I);
-}
-
-__device__ __forceinline__ bool blocked(const Sched& s, const Pos& c) {
+__device__ __forceinline__ bool blocked(const Sched& s, const It& c) {
   return c.phase == 0 && c.j >= s.sh_tiles;  // routed work before routing is known
 }
 
-__device__ inline void settle(const Params& p, const Sched& s, Pos& c) {
+// Up/gate jobs: the shared expert's tiles come first, then rt_tiles tiles
+// per routed group; a down job names its group.  The group and tile are
+// derived once on entering a phase and then advanced incrementally.
+__device__ inline void settle(const Params& p, const Sched& s, It& c) {
   for (;;) {
     if (c.phase == 0) {
+      c.g = 0;
+      c.tile = c.j;
       if (c.j < s.sh_tiles || !s.routed) return;
       c.phase = 1;
       c.j = first_job(p, s.sh_tiles);
-      c.kc = 0;
+      c.g = p.n_shared + (c.j - s.sh_tiles) / s.rt_tiles;
+      c.tile = (c.j - s.sh_tiles) % s.rt_tiles;
       continue;
     }
     if (c.phase == 1) {
@@ -647,19 +777,25 @@ __device__ inline void settle(const Params& p, const Sched& s, Pos& c) {
       c.phase = 2;
       c.j = 0;
       c.rt = 0;
-      c.kc = 0;
+      c.tile = 0;
       continue;
     }
+    c.g = c.j;
     if (c.phase == 2 && (s.nrt <= 0 || c.j >= s.G)) c.phase = 3;
     return;
   }
 }
 
-__device__ inline void advance(const Params& p, const Sched& s, Pos& c) {
-  if (++c.kc < chunk_count(p, c)) return;
-  c.kc = 0;
-  if (c.phase <= 1) {
+__device__ inline void next_job(const Params& p, const Sched& s, It& c) {
+  if (c.phase == 0) {
     c.j += p.ncu;
+  } else if (c.phase == 1) {
+    c.j += p.ncu;
+    c.tile += p.ncu;
+    while (c.tile >= s.rt_tiles) {
+      c.tile -= s.rt_tiles;
+      ++c.g;
+    }
   } else if (++c.rt >= s.nrt) {
     c.rt = 0;
     ++c.j;
@@ -667,245 +803,289 @@ __device__ inline void advance(const Params& p, const Sched& s, Pos& c) {
   settle(p, s, c);
 }
 
-// Weights of group g: the shared expert (group 0 when present) or routed
-// expert gexp[g].
-__device__ inline void group_weights(const Params& p, const Lds& L, int g, Chunk& k, bool down) {
-  if (p.n_shared && g == 0) {
-    k.fmt = 0;
-    k.iexp = p.Is;
-    k.w = down ? p.sh_wd : p.sh_wgu;
-    k.s = down ? (const void*)p.sh_sd : (const void*)p.sh_sgu;
-    return;
-  }
-  const size_t e = (size_t)lds_ldi_uniform(L.gexp + g);
-  const size_t H = p.H, I = p.I;
-  k.fmt = p.routed_fmt;
-  k.iexp = p.I;
-  if (p.routed_fmt == 0) {
-    // W_gate_up [E][2I][H], W_down [E][H][I] bytes; fp32 scales per 128x128
-    if (down) {
-      k.w = p.wd + e * H * I;
-      k.s = (const float*)p.sd + e * (H / 128) * (I / 128);
-    } else {
-      k.w = p.wgu + e * 2 * I * H;
-      k.s = (const float*)p.sgu + e * (2 * I / 128) * (H / 128);
-    }
-  } else {
-    // W_gate_up [E][2I][H/2], W_down [E][H][I/2] bytes; E8M0 per 32 along K
-    if (down) {
-      k.w = p.wd + e * H * (I / 2);
-      k.s = (const uint8_t*)p.sd + e * H * (I / 32);
-    } else {
-      k.w = p.wgu + e * 2 * I * (H / 2);
-      k.s = (const uint8_t*)p.sgu + e * 2 * I * (H / 32);
-    }
-  }
+__device__ __forceinline__ int job_group(const Params&, const Sched&, const It& c) { return c.g; }
+__device__ __forceinline__ int job_tile(const Sched&, const It& c) { return c.phase <= 1 ? c.tile : 0; }
+__device__ __forceinline__ bool shared_group(const Params& p, int g) { return p.n_shared && g == 0; }
+__device__ __forceinline__ int job_kdim(const Params& p, const It& c, int g) {
+  return c.phase <= 1 ? p.H : (shared_group(p, g) ? p.Is : p.I);
 }
-
-// Group of an up/gate position: the shared expert's jobs come first, then
-// rt_tiles jobs per routed group.
-__device__ __forceinline__ int chunk_group(const Params& p, const Sched& s, const Pos& c) {
-  return c.phase == 0 ? 0 : p.n_shared + (c.j - s.sh_tiles) / s.rt_tiles;
+__device__ __forceinline__ int group_ncols(const Params& p, const Lds& L, int g) {
+  if (shared_group(p, g)) return p.T;
+  return lds_ldi_uniform(L.gcnt + g);
 }
-
-__device__ inline Chunk chunk_of(const Params& p, const Lds& L, const Sched& s, const Pos& c) {
-  Chunk k;
-  k.kc = c.kc;
-  if (c.phase <= 1) {
-    k.kind = 1;
-    k.g = chunk_group(p, s, c);
-    k.tile = c.phase == 0 ? c.j : (c.j - s.sh_tiles) % s.rt_tiles;
-    k.rt = 0;
-    group_weights(p, L, k.g, k, false);
-    k.kdim = p.H;
-    k.nlive = 16;
-  } else {
-    k.kind = 2;
-    k.g = c.j;
-    k.tile = 0;
-    k.rt = c.rt;
-    group_weights(p, L, k.g, k, true);
-    k.kdim = k.iexp;
-    k.nlive = s.hc - 16 * c.rt < 16 ? s.hc - 16 * c.rt : 16;
-  }
-  return k;
-}
-
-// Weight row n of chunk row r: up/gate rows 0..7 are gate rows 8t..8t+7 and
-// rows 8..15 the up rows I+8t..I+8t+7; down rows are output rows h0+16rt+r.
-__device__ __forceinline__ int weight_row_index(const Sched& s, const Chunk& k, int r) {
-  if (k.kind == 1) return r < 8 ? 8 * k.tile + r : k.iexp + 8 * k.tile + r - 8;
-  return s.h0 + 16 * k.rt + r;
-}
-
-// Producer wave pw streams rows 8pw..8pw+7 of a chunk (8 DMA instructions,
-// always issued: a row past the live rows has no valid bytes) and one DMA of
-// scales, so its vmcnt bookkeeping is 9 per chunk.  Scales land at
-// kScaleOff: FP8, 16 floats from producer 0 (the 8 K-blocks' scales of the
-// tile's first and second 128-row block); MXFP4, 32 E8M0 bytes per row.
-__device__ inline void issue_chunk(const Params& p, const Lds& L, const Sched& s, const Pos& c,
-                                   lds_char* stage, int pw) {
-  const Chunk k = chunk_of(p, L, s, c);
-  const int lane = threadIdx.x & 63;
-  const int cbytes = k.fmt ? kChunkElems / 2 : kChunkElems;
-  const int rowbytes = __builtin_amdgcn_readfirstlane(k.fmt ? k.kdim / 2 : k.kdim);
-  const int koff = k.kc * cbytes;
-  const int left = rowbytes - koff;
-  const int nbytes = __builtin_amdgcn_readfirstlane(left < cbytes ? left : cbytes);
-  // this wave's 8 chunk rows are consecutive weight rows (gate rows, up
-  // rows, or output rows), so one base and the row pitch address them all
-  const int nl = __builtin_amdgcn_readfirstlane(k.nlive - 8 * pw);
-  const uint8_t* b = (const uint8_t*)uniform_ptr(
-      k.w + (size_t)weight_row_index(s, k, nl > 0 ? 8 * pw : 0) * rowbytes + koff);
-#pragma unroll
-  for (int q = 0; q < 8; ++q)
-    dma_row(q < nl ? b + q * rowbytes : b, q < nl ? nbytes : 0, stage + (8 * pw + q) * kPitch);
-  const uint32_t kOob = 0x7ffffff0u;
-  uint32_t voff = kOob, nrec;
-  if (k.fmt == 0) {
-    const int nkb = k.kdim / 128;
-    int nb_lo, nb_hi, nrows;
-    if (k.kind == 1) {
-      nb_lo = (8 * k.tile) / 128;
-      nb_hi = (k.iexp + 8 * k.tile) / 128;
-      nrows = 2 * k.iexp / 128;
-    } else {
-      const int hb = s.h0 + 16 * k.rt;
-      nb_lo = hb / 128;
-      nb_hi = (hb + k.nlive - 1) / 128;
-      nrows = p.H / 128;
-    }
-    const int kb = k.kc * 8 + (lane & 7);
-    if (pw == 0 && lane < 16 && kb < nkb) voff = (uint32_t)(((lane < 8 ? nb_lo : nb_hi) * nkb + kb) * 4);
-    nrec = (uint32_t)(nrows * nkb * 4);
-  } else {
-    const int spr = k.kdim / 32;                 // scale bytes per weight row
-    const int r = 8 * pw + (lane >> 3), d = lane & 7;
-    const int valid = spr - k.kc * 32 < 32 ? spr - k.kc * 32 : 32;
-    if (r < k.nlive && 4 * d < valid) voff = (uint32_t)(weight_row_index(s, k, r) * spr + k.kc * 32 + 4 * d);
-    nrec = (uint32_t)((k.kind == 1 ? 2 * k.iexp : p.H) * spr);
-  }
-  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(k.s), 0,
-                                                                __builtin_amdgcn_readfirstlane((int)nrec), 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(stage + kScaleOff + 256 * pw),
-                                           4, voff, 0, 0, 0);
-}
-
 // Column c of group g as row*16 + slot.
 __device__ __forceinline__ int col_code(const Params& p, const Lds& L, int g, int c) {
-  if (p.n_shared && g == 0) return c * 16 + p.K;
+  if (shared_group(p, g)) return c * 16 + p.K;
   return (int)lds_ld32(L.cols + lds_ldi_uniform(L.gstart + g) + c);
 }
 
-__device__ __forceinline__ int group_ncols(const Params& p, const Lds& L, int g) {
-  if (p.n_shared && g == 0) return p.T;
-  return lds_ldi_uniform(L.gcnt + g);
+// ---------------------------------------------------------------- producers
+
+// A producer wave's view of the job it streams: its 8 chunk rows (rows
+// 8pw..8pw+7: gate rows 8t.., up rows I+8t.., or output rows) are
+// consecutive rows of the weight matrix, so one base pointer and the row
+// pitch address them; its lanes' part of the chunk's scale DMA is an offset
+// that moves by 32 bytes per chunk.  Computed once per job.
+struct Feed {
+  It it;
+  int kc, nck;
+  const uint8_t* w;    // first of this wave's rows at K offset 0
+  int rowbytes;        // bytes of one weight row
+  int cbytes;          // bytes of one row per chunk
+  int nl;              // live rows among this wave's 8 (may be <= 0)
+};
+
+__device__ inline void feed_job(const Params& p, const Lds& L, const Sched& s, Feed& f, int pw) {
+  const It& c = f.it;
+  const int g = job_group(p, s, c);
+  const bool sh = shared_group(p, g), down = c.phase == 2;
+  const int fmt = sh ? 0 : p.routed_fmt;
+  const int iexp = sh ? p.Is : p.I;
+  const int kdim = down ? iexp : p.H;
+  const int tile = job_tile(s, c);
+  const int hb = s.h0 + 16 * c.rt;
+  const int nlive = down ? (s.hc - 16 * c.rt < 16 ? s.hc - 16 * c.rt : 16) : 16;
+  const uint8_t* w;
+  if (sh) {
+    w = down ? p.sh_wd : p.sh_wgu;
+  } else {
+    // W_gate_up [E][2I][H], W_down [E][H][I] bytes (MXFP4: [E][2I][H/2], [E][H][I/2])
+    const size_t e = (size_t)lds_ldi_uniform(L.gexp + g);
+    const size_t H = p.H, I = p.I, div = fmt ? 2 : 1;
+    w = down ? p.wd + e * H * (I / div) : p.wgu + e * 2 * I * (H / div);
+  }
+  f.kc = 0;
+  f.nck = nchunks(kdim);
+  f.rowbytes = fmt ? kdim / 2 : kdim;
+  f.cbytes = fmt ? kChunkElems / 2 : kChunkElems;
+  f.nl = nlive - 8 * pw;
+  // a wave with no live rows keeps a valid base (it loads no bytes)
+  const int row0 = down ? hb + (f.nl > 0 ? 8 * pw : 0) : (pw == 0 ? 8 * tile : iexp + 8 * tile);
+  f.w = w + (size_t)row0 * f.rowbytes;
 }
 
-// Activations of column tile ct at K-block kb for this lane: B[m] holds the
-// 8 bf16 of column ct*16 + (lane & 15) at elements kb*128 + 32*(lane >> 4) +
-// 8m .. +7 (x rows for up/gate, mid lines for down).  A lane past the
-// group's columns loads the last column again: MFMA columns are independent
-// and that output is never stored.
-__device__ __forceinline__ void load_tile(const Params& p, const Lds& L, const Chunk& k, int kb,
-                                          int ct, int ncols, u32x4* B) {
-  const int lane = threadIdx.x & 63, lg = lane >> 4, row = lane & 15;
-  const int c = ct * 16 + row < ncols ? ct * 16 + row : ncols - 1;
-  const int code = col_code(p, L, k.g, c);
-  const uint16_t* src = k.kind == 1
-      ? p.x + (size_t)(code >> 4) * p.H
-      : p.mid + ((size_t)(code >> 4) * (p.K + 1) + (code & 15)) * p.mid_ld;
-  const uint16_t* ptr = src + kb * 128 + 32 * lg;
+// Issues chunk f.kc of the job into `stage`: this wave's 8 row DMAs, always
+// issued (a row past the live rows loads no bytes), so its vmcnt
+// bookkeeping is 8 per chunk.
+__device__ inline void feed_chunk(const Feed& f, lds_char* stage, int pw) {
+  const int rb = __builtin_amdgcn_readfirstlane(f.rowbytes);
+  const int cb = __builtin_amdgcn_readfirstlane(f.cbytes);
+  const int koff = __builtin_amdgcn_readfirstlane(f.kc) * cb;
+  const int nbytes = rb - koff < cb ? rb - koff : cb;
+  const int nl = __builtin_amdgcn_readfirstlane(f.nl);
+  const uint8_t* b = (const uint8_t*)uniform_ptr(f.w) + koff;
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    dma_row(q < nl ? b + q * rb : b, q < nl ? nbytes : 0, stage + (8 * pw + q) * kPitch);
+}
+
+// ---------------------------------------------------------------- compute
+
+// A compute wave's view of the job it multiplies, computed once per job.
+template <int NPRE>
+struct Eat {
+  It it;
+  int kc, nck;
+  int kind;     // 1 up/gate, 2 down
+  int g, tile, rt, fmt, kdim, nlive, ncols, nct;
+  int eid;      // routed expert of the group
+  int split;    // FP8: MFMA output rows (4*lg + q) below it take the first block scale
+  float sreg;   // FP8: lane i < 32 holds the first row block's scale of K-block 8i + wave,
+                // lane 32 + i the second block's (one load per job; read back by readlane)
+  const uint8_t* srow;  // MXFP4: this lane's weight row's E8M0 scales
+  const uint16_t* abase;              // x (up/gate) or mid (down)
+  uint32_t act[max_tiles<NPRE>()];    // this lane's column per tile: activation offset + 32*lg
+};
+
+template <int NPRE>
+__device__ inline void eat_job(const Params& p, const Lds& L, const Sched& s, Eat<NPRE>& e) {
+  const int lane = threadIdx.x & 63, lg = lane >> 4;
+  const It& c = e.it;
+  e.kc = 0;
+  // consecutive jobs of one group (the down tiles of a CU's slice) share
+  // the column lookups
+  const int g = job_group(p, s, c), kind = c.phase <= 1 ? 1 : 2;
+  const bool same = g == e.g && kind == e.kind;
+  e.g = g;
+  const bool sh = shared_group(p, e.g);
+  e.kind = kind;
+  e.fmt = sh ? 0 : p.routed_fmt;
+  e.kdim = job_kdim(p, c, e.g);
+  e.nck = nchunks(e.kdim);
+  e.tile = job_tile(s, c);
+  e.rt = c.phase == 2 ? c.rt : 0;
+  e.nlive = e.kind == 2 ? (s.hc - 16 * e.rt < 16 ? s.hc - 16 * e.rt : 16) : 16;
+  if (e.kind == 1) {
+    e.split = 8;  // rows 0..7 of the MFMA tile are gate rows, 8..15 up rows
+  } else {
+    // a 16-row down tile spans at most two 128-row scale blocks
+    const int hb = s.h0 + 16 * e.rt;
+    e.split = (hb / 128 + 1) * 128 - hb;
+  }
+  int gstart = 0;
+  if (same) {
+  } else if (sh) {
+    e.ncols = p.T;
+  } else {
+    uint32_t a, b, c;
+    asm volatile("ds_read_b32 %0, %3\n\tds_read_b32 %1, %4\n\tds_read_b32 %2, %5\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(a), "=&v"(b), "=&v"(c)
+                 : "v"(lds_off(L.gcnt + e.g)), "v"(lds_off(L.gstart + e.g)), "v"(lds_off(L.gexp + e.g))
+                 : "memory");
+    e.ncols = uni((int)a);
+    gstart = uni((int)b);
+    e.eid = uni((int)c);
+  }
+  const size_t eid = (size_t)e.eid;
+  // the job's weight scales
+  {
+    const size_t H = p.H, I = p.I;
+    const int iexp = sh ? p.Is : p.I;
+    const int hb = s.h0 + 16 * e.rt;
+    if (e.fmt == 0) {
+      const float* S;
+      if (sh) S = e.kind == 1 ? p.sh_sgu : p.sh_sd;
+      else S = e.kind == 1 ? (const float*)p.sgu + eid * (2 * I / 128) * (H / 128)
+                           : (const float*)p.sd + eid * (H / 128) * (I / 128);
+      const int nkb = e.kdim / 128;
+      const int nb_lo = e.kind == 1 ? (8 * e.tile) / 128 : hb / 128;
+      const int nb_hi = e.kind == 1 ? (iexp + 8 * e.tile) / 128 : (hb + e.nlive - 1) / 128;
+      const int kb = (lane & 31) * 8 + wave_id();
+      e.sreg = (lane & 31) < e.nck && kb < nkb ? S[(size_t)(lane < 32 ? nb_lo : nb_hi) * nkb + kb] : 0.f;
+    } else {
+      const uint8_t* S = e.kind == 1 ? (const uint8_t*)p.sgu + eid * 2 * I * (H / 32)
+                                     : (const uint8_t*)p.sd + eid * H * (I / 32);
+      const int row = lane & 15;
+      const int wr = e.kind == 1 ? (row < 8 ? 8 * e.tile + row : iexp + 8 * e.tile + row - 8)
+                                 : hb + (row < e.nlive ? row : e.nlive - 1);
+      e.srow = S + (size_t)wr * (e.kdim / 32);
+    }
+  }
+  if (same) return;
+  e.nct = (e.ncols + 15) >> 4;
+  e.abase = e.kind == 1 ? p.x : p.mid;
+  // a lane past the group's columns takes the last column: MFMA columns
+  // are independent and that output is never stored
+  int codes[max_tiles<NPRE>()];
+#pragma unroll
+  for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) {
+    const int cc = ct * 16 + (lane & 15) < e.ncols ? ct * 16 + (lane & 15) : e.ncols - 1;
+    codes[ct] = sh ? cc * 16 + p.K : gstart + cc;
+  }
+  if (!sh) {
+    // the routed group's column codes, all tiles in one round trip
+    if (max_tiles<NPRE>() == 1) {
+      asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                   : "=v"(codes[0]) : "v"(lds_off(L.cols + codes[0])) : "memory");
+    } else {
+      int c4[4];
+      asm volatile("ds_read_b32 %0, %4\n\tds_read_b32 %1, %5\n\tds_read_b32 %2, %6\n\tds_read_b32 %3, %7\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=&v"(c4[0]), "=&v"(c4[1]), "=&v"(c4[2]), "=&v"(c4[3])
+                   : "v"(lds_off(L.cols + codes[0])), "v"(lds_off(L.cols + codes[max_tiles<NPRE>() > 1 ? 1 : 0])),
+                     "v"(lds_off(L.cols + codes[max_tiles<NPRE>() > 2 ? 2 : 0])),
+                     "v"(lds_off(L.cols + codes[max_tiles<NPRE>() > 3 ? 3 : 0]))
+                   : "memory");
+#pragma unroll
+      for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) codes[ct] = c4[ct];
+    }
+  }
+#pragma unroll
+  for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) {
+    const int code = codes[ct];
+    e.act[ct] = (e.kind == 1 ? (uint32_t)(code >> 4) * (uint32_t)p.H
+                             : ((uint32_t)(code >> 4) * (uint32_t)(p.K + 1) + (uint32_t)(code & 15)) *
+                                   (uint32_t)p.mid_ld) +
+                32u * lg;
+  }
+}
+
+// Activations of column tile ct at K-block kb for this lane: the 8 bf16 at
+// elements kb*128 + 32*(lane >> 4) + 8m .. +7 of its column's row (x for
+// up/gate, the mid line for down).
+template <int NPRE>
+__device__ __forceinline__ void load_tile(const Eat<NPRE>& e, int kb, int ct, u32x4* B) {
+  const uint16_t* ptr = e.abase + e.act[ct] + kb * 128;
 #pragma unroll
   for (int m = 0; m < 4; ++m) B[m] = ld16(ptr + 8 * m);
 }
 
-// Activations of the next chunk for this lane: for each 16-column tile
-// ct < NPRE, B[4ct+m] holds the 8 bf16 of column ct*16 + (lane & 15) at
-// elements kb*128 + 32*(lane >> 4) + 8m .. +7 (x rows for up/gate, mid lines
-// for down), one chunk ahead of their use.  Every register is loaded on
-// every call (a wave past the chunk's K range loads the last block again, a
-// tile past the group's columns its last column): a register that is only
+// The activations of chunk e.kc for tiles 0..NPRE-1, one chunk ahead of
+// their use.  Every register is loaded on every call (a wave past the
+// chunk's K range loads the last block again): a register that is only
 // sometimes loaded makes the compiler wait for all loads before the merge.
 template <int NPRE>
-__device__ inline void load_pre(const Params& p, const Lds& L, const Sched& s, const Chunk& k, Pre<NPRE>& P) {
-  const int nkb = (k.kdim + 127) >> 7;
-  const int kb = k.kc * 8 + wave_id() < nkb ? k.kc * 8 + wave_id() : nkb - 1;
-  const int ncols = group_ncols(p, L, k.g);
-  P.nct = (ncols + 15) >> 4;
+__device__ inline void load_pre(const Eat<NPRE>& e, Pre<NPRE>& P) {
+  const int nkb = (e.kdim + 127) >> 7;
+  const int kb = e.kc * 8 + wave_id() < nkb ? e.kc * 8 + wave_id() : nkb - 1;
 #pragma unroll
-  for (int ct = 0; ct < NPRE; ++ct) load_tile(p, L, k, kb, ct, ncols, P.B + 4 * ct);
-  if (k.kind == 1) {
-    P.split = 8;  // rows 0..7 of the MFMA tile are gate rows, 8..15 up rows
-  } else {
-    // a 16-row down tile spans at most two 128-row scale blocks
-    const int hb = s.h0 + 16 * k.rt;
-    P.split = (hb / 128 + 1) * 128 - hb;
-  }
+  for (int ct = 0; ct < NPRE; ++ct) load_tile(e, kb, ct, P.B + 4 * ct);
+  if (e.fmt != 0) P.sw = *(const uint32_t*)(e.srow + 4 * kb);
+}
+
+// Marks every prefetched register as read here, on every path: the wait for
+// them then happens once, at this point.
+template <int NPRE>
+__device__ __forceinline__ void settle_pre(const Pre<NPRE>& P, int fmt) {
+#pragma unroll
+  for (int i = 0; i < 4 * NPRE; ++i) asm volatile("" ::"v"(P.B[i]));
+  if (fmt != 0) asm volatile("" ::"v"(P.sw));
 }
 
 // Multiplies this wave's K-block of the chunk in `stage` into acc[ct].
 // FP8: a 4-MFMA block sum per K-block, then times its 128x128 block scale.
 // MXFP4: the E8M0 scale is folded into the exact bf16 conversion.
-// Marks every prefetched register as read here, on every path: the wait for
-// them then happens once, at this point (vmcnt(2) in the steady state), and
-// none of them is left with a load in flight that a later reuse of the
-// register would have to wait out with vmcnt(0).
-template <int NPRE>
-__device__ __forceinline__ void settle_pre(const Pre<NPRE>& P) {
-#pragma unroll
-  for (int i = 0; i < 4 * NPRE; ++i) asm volatile("" ::"v"(P.B[i]));
+// This wave's weights of a chunk, copied out of the stage so the stage can
+// be released before the math: FP8 32 bytes per lane, MXFP4 16.
+struct Raw {
+  u32x4 a0, a1;
+};
+
+// False when the wave has no K-block in this chunk (a ragged last chunk).
+template <int F, int NPRE>
+__device__ __forceinline__ bool fetch_chunk(const Eat<NPRE>& e, const lds_char* stage, Raw& r) {
+  const int lane = threadIdx.x & 63, lg = lane >> 4, row = lane & 15;
+  const int wave = wave_id();
+  if ((e.kc * 8 + wave) * 128 >= e.kdim) return false;
+  if (F == 0) lds_ld_fp8_block(stage + row * kPitch + wave * 128 + 32 * lg, r.a0, r.a1);
+  else lds_ld_fp4_block(stage + row * kPitch + wave * 64 + 16 * lg, r.a0);
+  return true;
 }
 
 template <int F, int NPRE>
-__device__ inline void compute_chunk(const Params& p, const Lds& L, const Chunk& k,
-                                     const lds_char* stage, const Pre<NPRE>& P, f32x4* acc) {
-  const int lane = threadIdx.x & 63, lg = lane >> 4, row = lane & 15;
-  const int wave = wave_id();
-  const int kb = k.kc * 8 + wave;
-  if (kb * 128 >= k.kdim) return;
+__device__ inline void compute_chunk(const Eat<NPRE>& e, const Raw& r, const Pre<NPRE>& P, f32x4* acc) {
+  const int lane = threadIdx.x & 63, lg = lane >> 4;
+  const int kb = e.kc * 8 + wave_id();
   bf16x8 A[4];
+  float s_lo = 1.f, s_hi = 1.f;
   if (F == 0) {
-    u32x4 a0, a1;
-    uint32_t slo, shi;
-    lds_ld_fp8_block(stage + row * kPitch + wave * 128 + 32 * lg, stage + kScaleOff + 4 * wave, a0, a1, slo, shi);
-    A[0] = e4m3x8_to_bf16(a0[0], a0[1]);
-    A[1] = e4m3x8_to_bf16(a0[2], a0[3]);
-    A[2] = e4m3x8_to_bf16(a1[0], a1[1]);
-    A[3] = e4m3x8_to_bf16(a1[2], a1[3]);
-    const float s_lo = __uint_as_float(slo), s_hi = __uint_as_float(shi);
+    A[0] = e4m3x8_to_bf16(r.a0[0], r.a0[1]);
+    A[1] = e4m3x8_to_bf16(r.a0[2], r.a0[3]);
+    A[2] = e4m3x8_to_bf16(r.a1[0], r.a1[1]);
+    A[3] = e4m3x8_to_bf16(r.a1[2], r.a1[3]);
+    s_lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e.sreg), e.kc));
+    s_hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e.sreg), 32 + e.kc));
+  } else {
+    const float sc = e8m0_to_f32((P.sw >> (8 * lg)) & 0xffu);
 #pragma unroll
-    for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) {
-      if (ct < P.nct) {
-        u32x4 Bl[4];
-        const u32x4* B = P.B + 4 * (ct < NPRE ? ct : 0);
-        if (ct >= NPRE) {
-          load_tile(p, L, k, kb, ct, group_ncols(p, L, k.g), Bl);
-          B = Bl;
-        }
+    for (int m = 0; m < 4; ++m) A[m] = e2m1x8_to_bf16(r.a0[m], sc);
+  }
+#pragma unroll
+  for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) {
+    if (ct < e.nct) {
+      u32x4 Bl[4];
+      const u32x4* B = P.B + 4 * (ct < NPRE ? ct : 0);
+      if (ct >= NPRE) {
+        load_tile(e, kb, ct, Bl);
+        B = Bl;
+      }
+      if (F == 0) {
         f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < 4; ++m) t = mfma16(A[m], __builtin_bit_cast(bf16x8, B[m]), t);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[ct][q] = fmaf(t[q], 4 * lg + q < P.split ? s_lo : s_hi, acc[ct][q]);
-      }
-    }
-  } else {
-    u32x4 a;
-    uint32_t sw;
-    lds_ld_fp4_block(stage + row * kPitch + wave * 64 + 16 * lg, stage + kScaleOff + row * 32 + 4 * wave, a, sw);
-    const float sc = e8m0_to_f32((sw >> (8 * lg)) & 0xffu);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) A[m] = e2m1x8_to_bf16(a[m], sc);
-#pragma unroll
-    for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) {
-      if (ct < P.nct) {
-        u32x4 Bl[4];
-        const u32x4* B = P.B + 4 * (ct < NPRE ? ct : 0);
-        if (ct >= NPRE) {
-          load_tile(p, L, k, kb, ct, group_ncols(p, L, k.g), Bl);
-          B = Bl;
-        }
+        for (int q = 0; q < 4; ++q) acc[ct][q] = fmaf(t[q], 4 * lg + q < e.split ? s_lo : s_hi, acc[ct][q]);
+      } else {
 #pragma unroll
         for (int m = 0; m < 4; ++m) acc[ct] = mfma16(A[m], __builtin_bit_cast(bf16x8, B[m]), acc[ct]);
       }
@@ -913,75 +1093,170 @@ __device__ inline void compute_chunk(const Params& p, const Lds& L, const Chunk&
   }
 }
 
-// End of an up/gate job: sum the 8 waves' K-block partials in wave order,
-// mid = silu(gate) * up, rounded to bf16, stored at the column's (row, slot).
-// Two workgroup barriers per column tile (the producer waves replay them).
-template <int MAXCT>
-__device__ inline void reduce_up(const Params& p, const Lds& L, const Chunk& k, f32x4* acc, int nct) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ncols = group_ncols(p, L, k.g);
+// Job-end reductions.  At the end of a job every compute wave stores its
+// partial tiles into partial slot (job % slots) and raises its part count;
+// it never waits for the others there.  Job j is summed by its owner wave
+// (j mod 8) later: at the owner's next job end, at the up/gate -> down
+// hand-over, or while the owner waits for a slot.  The sum runs over the
+// waves in order 0..7, exactly as a workgroup-wide reduction would.  A slot
+// is reused for job j only after job j - slots was summed out of it.
+template <int NPRE>
+struct Owned {
+  int jc;       // the job's index in this CU's sequence, -1 when none
+  int kind, g, tile, rt, ncols, nct, nlive;
+};
+
+// Eight waves' partial f32x4 of one lane, 1 KB apart, in one round trip.
+__device__ __forceinline__ void lds_ld_wave_partials(const float* t, u32x4 (&v)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:1024\n\t"
+      "ds_read_b128 %2, %8 offset:2048\n\tds_read_b128 %3, %8 offset:3072\n\t"
+      "ds_read_b128 %4, %8 offset:4096\n\tds_read_b128 %5, %8 offset:5120\n\t"
+      "ds_read_b128 %6, %8 offset:6144\n\tds_read_b128 %7, %8 offset:7168\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(lds_off(t))
+      : "memory");
+}
+
+template <int NPRE>
+__device__ __forceinline__ const float* red_slot(const Lds& L, int T, int jc) {
+  return L.red + (size_t)(jc % red_slots(T)) * red_tiles(T) * (kRedTileBytes / 4);
+}
+
+// Sums the owned job out of its slot.  Lane l holds MFMA rows 4*(l>>4)+q of
+// column (l & 15) in every wave's partial.  Up/gate: rows 0..7 are gate
+// rows, 8..15 (32 lanes on) the matching up rows; lanes 0..31 each finish
+// four intermediates, mid = silu(gate) * up rounded to bf16.  Down: every
+// lane finishes its four rows into the LDS products.
+template <int NPRE>
+__device__ inline void sum_job(const Params& p, const Lds& L, const Owned<NPRE>& o) {
+  const int lane = threadIdx.x & 63;
+  const float* base = red_slot<NPRE>(L, p.T, o.jc);
 #pragma unroll
-  for (int ct = 0; ct < MAXCT; ++ct) {
-    if (ct < nct) {
-      if (wave < kWaves) lds_st128(L.red + ((size_t)wave * 64 + lane) * 4, __builtin_bit_cast(u32x4, acc[ct]));
-      bar_lds();
-      if (tid < 128) {
-        const int i = tid >> 4, cc = tid & 15, col = ct * 16 + cc;
-        const int gl = (i >> 2) * 16 + cc, ul = gl + 32, q = i & 3;
-        float g = 0.f, u = 0.f;
-        for (int w = 0; w < kWaves; ++w) {
-          g += lds_ldf(L.red + ((size_t)w * 64 + gl) * 4 + q);
-          u += lds_ldf(L.red + ((size_t)w * 64 + ul) * 4 + q);
+  for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) {
+    if (ct < o.nct) {
+      const float* t = base + (size_t)ct * (kRedTileBytes / 4);
+      const int col = ct * 16 + (lane & 15);
+      const int code = col_code(p, L, o.g, col < o.ncols ? col : o.ncols - 1);
+      if (o.kind == 1) {
+        if (lane < 32) {
+          u32x4 v[8];
+          float gs[4], us[4];
+          lds_ld_wave_partials(t + (size_t)lane * 4, v);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            gs[q] = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) gs[q] += __uint_as_float(v[w][q]);
+          }
+          lds_ld_wave_partials(t + (size_t)(lane + 32) * 4, v);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            us[q] = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) us[q] += __uint_as_float(v[w][q]);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float g = gs[q], u = us[q];
+            if (col < o.ncols) {
+              const float m = g / (1.0f + expf(-g)) * u;
+              if (!isfinite(m)) set_err(p.err, kErrMid);
+              const int i = 4 * (lane >> 4) + q;
+              p.mid[((size_t)(code >> 4) * (p.K + 1) + (code & 15)) * p.mid_ld + 8 * o.tile + i] =
+                  (uint16_t)f32_to_bf16_rne(m);
+            }
+          }
         }
-        if (col < ncols) {
-          const float m = g / (1.0f + expf(-g)) * u;
-          if (!isfinite(m)) set_err(p.err, kErrMid);
-          const int code = col_code(p, L, k.g, col);
-          p.mid[((size_t)(code >> 4) * (p.K + 1) + (code & 15)) * p.mid_ld + 8 * k.tile + i] =
-              (uint16_t)f32_to_bf16_rne(m);
+      } else {
+        u32x4 pv[8];
+        lds_ld_wave_partials(t + (size_t)lane * 4, pv);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float v = 0.f;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) v += __uint_as_float(pv[w][q]);
+          const int i = 4 * (lane >> 4) + q;
+          if (i < o.nlive && col < o.ncols) {
+            if (!isfinite(v)) set_err(p.err, kErrMid);
+            const size_t at = ((size_t)(code >> 4) * (p.K + 1) + (code & 15)) * p.hs + 16 * o.rt + i;
+            if (NPRE == 1) lds_st32(L.pbuf + at, __float_as_uint(v));
+            else p.prod[(size_t)blockIdx.x * p.T * (p.K + 1) * p.hs + at] = v;
+          }
         }
       }
-      bar_lds();
-      acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
 }
 
-// End of a down row tile: sum the waves' partials in wave order into the
-// LDS products P[row][slot][h].
-template <int MAXCT>
-__device__ inline void reduce_down(const Params& p, const Lds& L, const Chunk& k, f32x4* acc, int nct) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ncols = group_ncols(p, L, k.g);
-#pragma unroll
-  for (int ct = 0; ct < MAXCT; ++ct) {
-    if (ct < nct) {
-      if (wave < kWaves) lds_st128(L.red + ((size_t)wave * 64 + lane) * 4, __builtin_bit_cast(u32x4, acc[ct]));
-      bar_lds();
-      if (tid < 256) {
-        const int ln = tid >> 2, q = tid & 3;
-        const int i = 4 * (ln >> 4) + q, col = ct * 16 + (ln & 15);
-        if (i < k.nlive && col < ncols) {
-          float v = 0.f;
-          for (int w = 0; w < kWaves; ++w) v += lds_ldf(L.red + ((size_t)w * 64 + ln) * 4 + q);
-          if (!isfinite(v)) set_err(p.err, kErrMid);
-          const int code = col_code(p, L, k.g, col);
-          lds_st32(L.pbuf + ((size_t)(code >> 4) * (p.K + 1) + (code & 15)) * p.hs + 16 * k.rt + i,
-                   __float_as_uint(v));
-        }
+// Sums the owned job when every wave's partials are in (or waits for them
+// when `block`), then releases its slot.
+template <int NPRE>
+__device__ inline void service(const Params& p, const Lds& L, Owned<NPRE>& o, bool block, bool& ok) {
+  o.jc = uni(o.jc);
+  if (o.jc < 0) return;
+  if (block) lds_wait<8>(p, L.ctl + kCtlPart, (uint32_t)(o.jc + 1), ok);
+  else if (ok && (int)lds_min<8>(L.ctl + kCtlPart) < o.jc + 1) return;
+  sum_job(p, L, o);
+  lds_st32(L.ctl + kCtlSlot + o.jc % red_slots(p.T), (uint32_t)(o.jc + 1));
+  o.jc = -1;
+}
+
+// End of job jc for this wave: wait for its slot (summing an owned job
+// meanwhile), store the partial tiles, raise the part count, finish an older
+// owned job, and take ownership of jc when it is this wave's.
+template <int NPRE>
+__device__ inline void job_end(const Params& p, const Lds& L, const Eat<NPRE>& e, f32x4* acc, int jc,
+                               Owned<NPRE>& own, bool& ok) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int ns = red_slots(p.T);
+  if (jc >= ns) {
+    const uint32_t target = (uint32_t)(jc - ns + 1);
+    const uint32_t* sd = L.ctl + kCtlSlot + jc % ns;
+    int spins = 0;
+    while (ok && lds_min<1>(sd) < target) {
+      service(p, L, own, false, ok);
+      if (++spins > kSpinLimit) {
+        set_err(p.err, kErrTimeout);
+        ok = false;
+        break;
       }
-      bar_lds();
-      acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      __builtin_amdgcn_s_sleep(1);
     }
   }
+  float* base = (float*)red_slot<NPRE>(L, p.T, jc);
+#pragma unroll
+  for (int ct = 0; ct < max_tiles<NPRE>(); ++ct)
+    if (ct < e.nct)
+      lds_st128(base + (size_t)ct * (kRedTileBytes / 4) + ((size_t)wave * 64 + lane) * 4,
+                __builtin_bit_cast(u32x4, acc[ct]));
+  lds_st32(L.ctl + kCtlPart + wave, (uint32_t)(jc + 1));
+  service(p, L, own, true, ok);
+  if (jc % kWaves == wave) {
+    own.jc = jc;
+    own.kind = e.kind;
+    own.g = e.g;
+    own.tile = e.tile;
+    own.rt = e.rt;
+    own.ncols = e.ncols;
+    own.nct = e.nct;
+    own.nlive = e.nlive;
+  }
+#pragma unroll
+  for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // out[r][h] = P_shared + sum_p w[r][p] * P[r][p], fp32 FMA chain in slot
 // order, rounded to bf16 once.
+// The products are in LDS for batches of at most 16 rows, else in this
+// CU's part of the workspace.
+template <int NPRE>
 __device__ inline void combine(const Params& p, const Lds& L, const Sched& s) {
+  const float* P = NPRE == 1 ? L.pbuf : p.prod + (size_t)blockIdx.x * p.T * (p.K + 1) * p.hs;
   for (int t = threadIdx.x; t < p.T * s.hc; t += kThreads) {
     const int r = t / s.hc, hl = t - r * s.hc;
-    const float* pr = L.pbuf + (size_t)r * (p.K + 1) * p.hs + hl;
+    const float* pr = P + (size_t)r * (p.K + 1) * p.hs + hl;
     float acc = p.n_shared ? pr[(size_t)p.K * p.hs] : 0.f;
     for (int k = 0; k < p.K; ++k) acc = fmaf(L.w[r * p.K + k], pr[(size_t)k * p.hs], acc);
     p.out[(size_t)r * p.H + s.h0 + hl] = (uint16_t)f32_to_bf16_rne(acc);
@@ -1000,6 +1275,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   const int pw = wave - kWaves;
 
   MOE_STAMP(p, 0);
+  if (tid < 64) L.ctl[tid] = 0u;
   if (tid == 0)
     L.misc[1] = (int32_t)__hip_atomic_load(&p.flags[blockIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
@@ -1020,16 +1296,24 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   // other vector memory operation, so their in-order vmcnt tracks the ring
   // exactly, and the compute waves' activation loads never queue behind a
   // DMA.
-  Pos ipos = {0, first_job(p, 0), 0, 0}, cpos;
+  Feed feed;
+  feed.it = It{0, first_job(p, 0), 0, 0, 0};
+  feed.kc = 0;
   int n_i = 0, n_c = 0;
-  settle(p, s, ipos);
+  settle(p, s, feed.it);
   // S1: the shared expert's up/gate chunks need no routing: start them now
   if (MODE == kModeForward && producer) {
-    while (n_i < p.ns - 1 && ipos.phase == 0 && !blocked(s, ipos)) {
-      issue_chunk(p, L, s, ipos, st3 + (n_i % p.ns) * kStageBytes, pw);
-      advance(p, s, ipos);
+    __builtin_amdgcn_s_setprio(3);
+    while (n_i < p.ns - 1 && feed.it.phase < 3 && !blocked(s, feed.it)) {
+      if (feed.kc == 0) feed_job(p, L, s, feed, pw);
+      feed_chunk(feed, st3 + (n_i % p.ns) * kStageBytes, pw);
       ++n_i;
+      if (++feed.kc == feed.nck) {
+        feed.kc = 0;
+        next_job(p, s, feed.it);
+      }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // S0: router logits of this CU's experts, published for every CU
@@ -1072,23 +1356,13 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   s.G = G;
   s.n_jobs = s.sh_tiles + (G - p.n_shared) * s.rt_tiles;
   s.routed = 1;
-  settle(p, s, ipos);
-  cpos = {0, first_job(p, 0), 0, 0};
-  settle(p, s, cpos);
+  settle(p, s, feed.it);
+  It start = It{0, first_job(p, 0), 0, 0, 0};
+  settle(p, s, start);
 
   // S3 / S4: the chunk stream.  The second flag (every CU's mid is out) is
   // raised after this CU's last up/gate job and awaited before the first
-  // down chunk's activations are read.
-  bool passed2 = false;
-  auto cross_to_down = [&](const Pos& c) {
-    if (!passed2 && c.phase >= 2) {
-      MOE_STAMP(p, 4);
-      publish(p, epoch + 2);
-      if (c.phase == 2) wait_all(p, epoch + 2);
-      MOE_STAMP(p, 5);
-      passed2 = true;
-    }
-  };
+  // down chunk's activations are read; only the compute waves take part.
 #ifdef MOE_LAPS
   uint64_t cyc[6] = {0, 0, 0, 0, 0, 0};
   uint64_t tq = __builtin_amdgcn_s_memtime();
@@ -1103,78 +1377,143 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   do {             \
   } while (0)
 #endif
+  bool ok = true;
 
-  // One step: the producers wait for chunk n to land (the chunks after it
-  // stay in flight), everyone meets, the compute waves multiply chunk n and
-  // prefetch the activations of chunk n+1, a job ending here is reduced, and
-  // the producers refill the stage chunk n-1 freed with chunk n+ns-1.
-  // Producer and compute waves run separate loops that meet at the same
-  // sequence of barriers: the top of each step, two per column tile of a
-  // reduction, and the flag hand-over.  Kept apart, the producers' code
-  // holds no load into a register, so nothing makes them drain the ring.
+  // The producers and the compute waves never meet at a workgroup barrier
+  // inside the stream: they hand chunks over through LDS counters.  A
+  // producer keeps up to ns - 1 chunks in flight; when the oldest has
+  // landed (its in-order vmcnt says so) it raises its ready count, and it
+  // refills a stage once every compute wave's done count has passed the
+  // chunk that stage held.  A compute wave waits for both producers' ready
+  // counts, multiplies the chunk, raises its done count, and prefetches the
+  // next chunk's activations.  Per-job descriptors are computed when a job
+  // starts; a chunk only moves offsets.
   if (producer) {
-    while (ipos.phase < 3 && n_i < n_c + p.ns - 1) {
-      issue_chunk(p, L, s, ipos, st3 + (n_i % p.ns) * kStageBytes, pw);
-      advance(p, s, ipos);
-      ++n_i;
-    }
-    cross_to_down(cpos);
-    while (cpos.phase < 3) {
-      wait_vm(9 * (n_i - 1 - n_c));
-      MOE_LAP(0);
-      bar_lds();
-      MOE_LAP(1);
-      if (cpos.kc == chunk_count(p, cpos) - 1) {
-        const int g = cpos.phase <= 1 ? chunk_group(p, s, cpos) : cpos.j;
-        const int nct = (group_ncols(p, L, g) + 15) >> 4;
-        for (int ct = 0; ct < nct; ++ct) {
-          bar_lds();
-          bar_lds();
+    // The producers are the workgroup's youngest waves; the SIMD arbiter
+    // favours older waves, so without a raised priority the compute waves
+    // sharing their SIMDs starve the DMA issue.
+    __builtin_amdgcn_s_setprio(3);
+    int n_r = 0;       // chunks this wave has reported landed
+    uint32_t cdone = 0;  // last read minimum of the compute waves' done counts
+    for (;;) {
+      n_i = uni(n_i);
+      n_r = uni(n_r);
+      uni(feed.it);
+      feed.kc = uni(feed.kc);
+      if (feed.it.phase >= 3) break;
+      if (feed.kc == 0) feed_job(p, L, s, feed, pw);
+      // room for chunk n_i: fewer than ns - 1 chunks in flight, and its
+      // stage released by every compute wave; meanwhile report landings
+      while (n_i - n_r >= p.ns - 1 || (ok && n_i - (int)cdone >= p.ns)) {
+        if (n_i - (int)cdone >= p.ns) cdone = lds_min<8>(L.ctl + kCtlDone);
+        if (n_i - n_r >= p.ns - 1 || (n_r < n_i && n_i - (int)cdone >= p.ns)) {
+          wait_vm(8 * (n_i - 1 - n_r));
+          ++n_r;
+          lds_st32(L.ctl + kCtlReady + pw, (uint32_t)n_r);
+        } else if (n_i - (int)cdone >= p.ns) {
+          lds_wait<8>(p, L.ctl + kCtlDone, (uint32_t)(n_i - p.ns + 1), ok);
+          cdone = (uint32_t)(n_i - p.ns + 1);
         }
+        n_r = uni(n_r);
       }
-      MOE_LAP(3);
-      advance(p, s, cpos);
-      ++n_c;
-      cross_to_down(cpos);
-      MOE_LAP(4);
-      if (ipos.phase < 3 && n_i < n_c + p.ns - 1) {
-        issue_chunk(p, L, s, ipos, st3 + (n_i % p.ns) * kStageBytes, pw);
-        advance(p, s, ipos);
-        ++n_i;
+      MOE_LAP(0);
+      feed_chunk(feed, st3 + (n_i % p.ns) * kStageBytes, pw);
+      ++n_i;
+      if (++feed.kc == feed.nck) {
+        feed.kc = 0;
+        next_job(p, s, feed.it);
       }
-      MOE_LAP(5);
+      MOE_LAP(1);
     }
+    while (n_r < n_i) {
+      wait_vm(8 * (n_i - 1 - n_r));
+      ++n_r;
+      lds_st32(L.ctl + kCtlReady + pw, (uint32_t)n_r);
+    }
+    n_c = n_r;
+    __builtin_amdgcn_s_setprio(0);
   } else {
     constexpr int MAXCT = max_tiles<NPRE>();
+    const int wave_c = wave;
+    bool passed2 = false;
+    // every compute wave has completed its mid stores; wave 0 publishes and,
+    // when this CU has down work, waits for every CU and tells the others
+    int jc = 0;  // jobs ended
+    Owned<NPRE> own;
+    own.jc = -1;
+    auto cross_to_down = [&](const It& c) {
+      if (!passed2 && c.phase >= 2) {
+        MOE_STAMP(p, 4);
+        service(p, L, own, true, ok);  // this wave's last owned up/gate job
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_st32(L.ctl + kCtlMidOut + wave_c, 1u);
+        if (wave_c == 0) {
+          lds_wait<8>(p, L.ctl + kCtlMidOut, 1u, ok);
+          if (threadIdx.x == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __hip_atomic_store(&p.flags[blockIdx.x], epoch + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          if (c.phase == 2) poll_flags(p, epoch + 2);
+          lds_st32(L.ctl + kCtlCrossed, 1u);
+        }
+        if (c.phase == 2) lds_wait<1>(p, L.ctl + kCtlCrossed, 1u, ok);
+        MOE_STAMP(p, 5);
+        passed2 = true;
+      }
+    };
+    Eat<NPRE> e;
+    e.it = start;
+    e.g = -1;
+    e.kind = 0;
+    e.eid = 0;
     Pre<NPRE> pre;
     f32x4 acc[MAXCT];
 #pragma unroll
     for (int ct = 0; ct < MAXCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    cross_to_down(cpos);
-    if (cpos.phase < 3) load_pre(p, L, s, chunk_of(p, L, s, cpos), pre);
-    while (cpos.phase < 3) {
+    uint32_t rdy = 0;  // last seen minimum of the producers' ready counts
+    cross_to_down(e.it);
+    if (e.it.phase < 3) {
+      eat_job(p, L, s, e);
+      load_pre(e, pre);
+    }
+    while (e.it.phase < 3) {
+      n_c = uni(n_c);
+      rdy = (uint32_t)uni((int)rdy);
+      uni(e.it);
+      e.kc = uni(e.kc);
+      e.nck = uni(e.nck);
+      e.nct = uni(e.nct);
+      e.kind = uni(e.kind);
+      e.fmt = uni(e.fmt);
       MOE_LAP(0);
-      bar_lds();
+      if ((int)rdy <= n_c) rdy = lds_wait<2>(p, L.ctl + kCtlReady, (uint32_t)(n_c + 1), ok);
       MOE_LAP(1);
-      const Chunk k = chunk_of(p, L, s, cpos);
       const lds_char* stage = st3 + (n_c % p.ns) * kStageBytes;
-      settle_pre(pre);
-      if (k.fmt == 0) compute_chunk<0>(p, L, k, stage, pre, acc);
-      else compute_chunk<FMT>(p, L, k, stage, pre, acc);
-      MOE_LAP(2);
-      if (cpos.kc == chunk_count(p, cpos) - 1) {
-        if (k.kind == 1) reduce_up<MAXCT>(p, L, k, acc, pre.nct);
-        else reduce_down<MAXCT>(p, L, k, acc, pre.nct);
+      Raw raw;
+      const bool live = e.fmt == 0 ? fetch_chunk<0>(e, stage, raw) : fetch_chunk<FMT>(e, stage, raw);
+      lds_st32(L.ctl + kCtlDone + wave, (uint32_t)(n_c + 1));  // the stage is free for this wave
+      settle_pre(pre, e.fmt);
+      if (live) {
+        if (e.fmt == 0) compute_chunk<0>(e, raw, pre, acc);
+        else compute_chunk<FMT>(e, raw, pre, acc);
       }
+      MOE_LAP(2);
+      if (e.kc == e.nck - 1) job_end(p, L, e, acc, jc++, own, ok);
       MOE_LAP(3);
-      advance(p, s, cpos);
       ++n_c;
-      cross_to_down(cpos);
+      if (++e.kc == e.nck) {
+        next_job(p, s, e.it);
+        cross_to_down(e.it);
+        MOE_LAP(4);
+        if (e.it.phase < 3) eat_job(p, L, s, e);
+        MOE_LAP(0);
+      }
       MOE_LAP(4);
-      if (cpos.phase >= 3) break;
-      load_pre(p, L, s, chunk_of(p, L, s, cpos), pre);
+      if (e.it.phase >= 3) break;
+      load_pre(e, pre);
       MOE_LAP(5);
     }
+    service(p, L, own, true, ok);  // the last owned down job
   }
 #ifdef MOE_LAPS
   if (p.timeline && (threadIdx.x == 0 || threadIdx.x == 64 * kWaves)) {
@@ -1185,14 +1524,10 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   }
 #endif
   MOE_STAMP(p, 6);
-  if (!passed2) {
-    publish(p, epoch + 2);
-    passed2 = true;
-  }
   __syncthreads();
 
   // S5: combine this CU's output rows
-  combine(p, L, s);
+  combine<NPRE>(p, L, s);
   MOE_STAMP(p, 7);
   if (threadIdx.x == 0 && p.timeline) {
     p.timeline[blockIdx.x * 16 + 8] = (uint64_t)n_c;
@@ -1202,7 +1537,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
 
 // ------------------------------------------------------------------ host glue
 
-WsLayout ws_layout(int max_rows, int E, int K, int I, int Is) {
+WsLayout ws_layout(int max_rows, int E, int K, int H, int I, int Is) {
   WsLayout w;
   size_t q = 0;
   w.flags = q; q = align_up(q + 4 * 1024, 256);
@@ -1210,6 +1545,9 @@ WsLayout ws_layout(int max_rows, int E, int K, int I, int Is) {
   w.scores = q; q = align_up(q + 16 * (size_t)max_rows * E, 256);
   w.mid_ld = (I > Is ? I : Is);
   w.mid = q; q = align_up(q + 2 * (size_t)max_rows * (K + 1) * w.mid_ld, 256);
+  // ncu * hs <= H + ncu - 1 and ncu <= 1024, so H + 1024 rows of products cover every CU's slice
+  w.prod = q;
+  if (max_rows > kLdsProdRows) q = align_up(q + 4 * (size_t)max_rows * (K + 1) * (H + 1024), 256);
   w.total = q;
   return w;
 }
