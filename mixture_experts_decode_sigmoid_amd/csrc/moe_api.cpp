@@ -100,9 +100,8 @@ int fill(const moe_config* c, const moe_weights* w, const uint16_t* x, int rows,
   if (d.ncu > 1024) return MOE_ERR_SHAPE;
   const int hs = hs_for(c->hidden, d.ncu);
   if (hs > kMaxSlice) return MOE_ERR_SHAPE;
-  int ns = 0;
-  size_t lds = lds_plan(rows > 0 ? rows : 1, c->top_k, c->n_experts, hs, d.max_lds, &ns);
-  if (ns < 3) return MOE_ERR_SHAPE;
+  size_t lds = lds_bytes(rows > 0 ? rows : 1, c->top_k, c->n_experts, hs);
+  if (lds > d.max_lds) return MOE_ERR_SHAPE;
   if (lds < (size_t)kMinLds) lds = kMinLds;
   memset(&p, 0, sizeof p);
   p.H = c->hidden;
@@ -121,7 +120,6 @@ int fill(const moe_config* c, const moe_weights* w, const uint16_t* x, int rows,
   p.ncu = d.ncu;
   p.mid_ld = L.mid_ld;
   p.lds_bytes = (int)lds;
-  p.ns = ns;
   p.x = x;
   p.router_w = w->router_w;
   p.bias = w->bias;
@@ -138,7 +136,6 @@ int fill(const moe_config* c, const moe_weights* w, const uint16_t* x, int rows,
   p.err = (uint32_t*)(base + L.err);
   p.scores = (double*)(base + L.scores);
   p.mid = (uint16_t*)(base + L.mid);
-  p.prod = rows > kLdsProdRows ? (float*)(base + L.prod) : nullptr;
 #ifdef MOE_TIMELINE
   p.timeline = (uint64_t*)(base + L.total);  // callers of a timeline build add 1024*16*8 bytes
   if (ws_bytes < L.total + 1024 * 16 * 8) return MOE_ERR_WORKSPACE;

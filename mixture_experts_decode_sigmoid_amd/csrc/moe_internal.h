@@ -8,10 +8,9 @@
 
 namespace moe {
 
-constexpr int kWaves = 8;                 // compute waves per workgroup (one workgroup per CU)
-constexpr int kProducers = 2;             // waves that only stream weights into LDS
-constexpr int kAllWaves = kWaves + kProducers;
-constexpr int kThreads = kAllWaves * 64;
+constexpr int kWaves = 8;                 // waves per workgroup (one workgroup per CU)
+constexpr int kAllWaves = kWaves;
+constexpr int kThreads = kWaves * 64;
 constexpr int kMaxRows = 64;              // rows per call
 constexpr int kMaxExperts = 256;          // routed experts (4 per lane in the router)
 constexpr int kMaxTopK = 8;
@@ -23,13 +22,9 @@ enum Mode { kModeForward = 0, kModeRoute = 1, kModeGroups = 2 };
 
 // Workspace layout (byte offsets from the workspace base).
 struct WsLayout {
-  size_t flags, err, scores, mid, prod, total;
+  size_t flags, err, scores, mid, total;
   int mid_ld;  // bf16 elements per (row, slot) line of mid
 };
-
-// Batches above this many rows keep the down products in the workspace
-// instead of LDS (their LDS goes to the ring and the job-end partials).
-constexpr int kLdsProdRows = 16;
 
 struct Params {
   // shape
@@ -40,7 +35,6 @@ struct Params {
   int ncu;         // workgroups launched (= CUs)
   int mid_ld;
   int lds_bytes;   // dynamic LDS size
-  int ns;          // weight stages in the LDS ring
   // inputs
   const uint16_t* x;
   const uint16_t* router_w;
@@ -63,14 +57,12 @@ struct Params {
   uint32_t* err;
   double* scores;  // [T][E][2]: s, b
   uint16_t* mid;   // [T][K+1][mid_ld] bf16
-  float* prod;     // wide batches: [ncu][T][K+1][hs] fp32 down products (else NULL)
   uint64_t* timeline;  // optional phase stamps ([ncu][16]); NULL unless built with MOE_TIMELINE
 };
 
 WsLayout ws_layout(int max_rows, int E, int K, int H, int I, int Is);
-// LDS bytes for a call and the number of weight stages that fit in max_lds
-// (*ns < 2: does not fit).
-size_t lds_plan(int T, int K, int E, int hs, size_t max_lds, int* ns);
+// LDS bytes a call needs.
+size_t lds_bytes(int T, int K, int E, int hs);
 hipError_t launch(const Params& p, int mode, hipStream_t stream);
 
 }  // namespace moe

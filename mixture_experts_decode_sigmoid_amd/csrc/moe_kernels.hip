@@ -127,16 +127,6 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; 
 
 // ------------------------------------------------------------------ LDS map
 
-// Weight stages: a ring of `ns` stages, each 16 weight rows of one K chunk
-// (1024 elements: 1024 B of FP8 or 512 B of MXFP4) in slots of 1040 B.  A
-// DMA instruction always writes 64 lanes x 16 B = 1 KB, so each row owns a
-// full 1 KB slot (an MXFP4 row's second half holds filler nobody reads); the
-// 16-byte pad puts the 16 rows an MFMA tile reads in one ds_read_b128 on
-// different LDS banks.
-constexpr int kPitch = 1040;
-constexpr int kStageBytes = 16 * kPitch;
-constexpr int kChunkElems = 1024;
-
 struct Lds {
   int32_t* ids;      // [T*K]
   float* w;          // [T*K]
@@ -153,20 +143,26 @@ struct Lds {
   double* rb;        // [kWaves][E] router keys (aliases red and pbuf)
   double* rgs;       // [kWaves][64] group scores
   int32_t* rkept;    // [kWaves][64]
-  float* pbuf;       // [T*(K+1)][hs] down products (batches of at most 16 rows)
-  char* stages;      // [ns][kStageBytes]
+  float* pbuf;       // down products: [T*(K+1)][hs], or per wave [8][T*(K+1)][pitch] (see down_direct)
 };
 
 __host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Job-end partials: up to 16 columns per tile when a batch has at most 16
-// rows (one tile, two slots), else 4 tiles in one slot.
+// Job-end partials: one 16-column tile per job when a batch has at most 16
+// rows (four slots), else four tiles (two slots).
 __host__ __device__ inline int red_tiles(int T) { return T > 16 ? kMaxRows / 16 : 1; }
-__host__ __device__ inline int red_slots(int T) { return T > 16 ? 1 : 2; }
+__host__ __device__ inline int red_slots(int T) { return T > 16 ? 2 : 4; }
 constexpr size_t kRedTileBytes = 16 * (size_t)kWaves * 64;  // one tile: [wave][lane] f32x4
 
+// Batches of at most 8 rows keep every wave's down partials apart in LDS,
+// P[w][row][slot][h] with rows of the slice padded to whole 16-row tiles,
+// and the combine sums them over the waves; larger batches reduce each down
+// tile at its job end like the up/gate tiles.
+__host__ __device__ inline bool down_direct(int T) { return T <= 8; }
+__host__ __device__ inline int prod_pitch(int hs) { return (hs + 15) / 16 * 16; }
+
 struct LdsOffsets {
-  size_t ids, w, first, egrp, rmask, gexp, gcnt, gstart, cols, misc, ctl, red, pbuf, stages;
+  size_t ids, w, first, egrp, rmask, gexp, gcnt, gstart, cols, misc, ctl, red, pbuf, total;
 };
 
 __host__ __device__ inline LdsOffsets lds_offsets(int T, int K, int E, int hs) {
@@ -189,24 +185,15 @@ __host__ __device__ inline LdsOffsets lds_offsets(int T, int K, int E, int hs) {
   o.red = q;
   const size_t rd = (size_t)red_slots(T) * red_tiles(T) * kRedTileBytes;
   o.pbuf = q + rd;
-  const size_t pb = T > kLdsProdRows ? 0 : 4 * (size_t)T * (K + 1) * hs;
+  const size_t pb = down_direct(T) ? 4 * (size_t)kWaves * T * (K + 1) * prod_pitch(hs)
+                                   : 4 * (size_t)T * (K + 1) * hs;
   const size_t rs = 8 * (size_t)kWaves * E + 8 * (size_t)kWaves * 64 + 4 * (size_t)kWaves * 64;
   q = align_up(q + (rd + pb > rs ? rd + pb : rs), 16);
-  o.stages = q;
+  o.total = q;
   return o;
 }
 
-size_t lds_plan(int T, int K, int E, int hs, size_t max_lds, int* ns) {
-  const size_t fixed = lds_offsets(T, K, E, hs).stages;
-  if (fixed + 2 * (size_t)kStageBytes > max_lds) {
-    *ns = 0;
-    return fixed + 2 * (size_t)kStageBytes;
-  }
-  size_t n = (max_lds - fixed) / kStageBytes;
-  if (n > 8) n = 8;
-  *ns = (int)n;
-  return fixed + n * kStageBytes;
-}
+size_t lds_bytes(int T, int K, int E, int hs) { return lds_offsets(T, K, E, hs).total; }
 
 __device__ inline Lds lds_map(char* base, const Params& p) {
   LdsOffsets o = lds_offsets(p.T, p.K, p.E, p.hs);
@@ -227,31 +214,22 @@ __device__ inline Lds lds_map(char* base, const Params& p) {
   L.rb = (double*)(base + o.red);
   L.rgs = L.rb + (size_t)kWaves * p.E;
   L.rkept = (int32_t*)(L.rgs + (size_t)kWaves * 64);
-  L.stages = base + o.stages;
   return L;
 }
 
 // ------------------------------------------------------------------ flags
 
 // Raise this CU's flag to `value` after all of the workgroup's prior global
-// stores.  Every compute wave waits for its own stores, the workgroup meets,
-// then one thread releases at agent scope and stores the flag.  The barrier
-// is the bare s_barrier: producer waves may have weight DMA in flight and
-// must not wait for it here.
+// stores: the workgroup meets (each wave's stores complete first), then one
+// thread releases at agent scope and stores the flag.
 __device__ inline void publish(const Params& p, uint32_t value) {
-  if ((threadIdx.x >> 6) < kWaves) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+  __syncthreads();
   if (threadIdx.x == 0) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __hip_atomic_store(&p.flags[blockIdx.x], value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// Wait until every CU's flag has reached `target` (wrap-around safe), then
-// acquire.  Wave 0 polls and acquires; the barrier after it orders the rest
-// of the workgroup (bare s_barrier, as in publish).
 // One wave polls every CU's flag until all have reached `target`
 // (wrap-around safe), then acquires at agent scope.
 __device__ inline void poll_flags(const Params& p, uint32_t target) {
@@ -273,11 +251,11 @@ __device__ inline void poll_flags(const Params& p, uint32_t target) {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
+// Wait until every CU's flag has reached `target`: wave 0 polls and
+// acquires, the workgroup barrier orders the rest.
 __device__ inline void wait_all(const Params& p, uint32_t target) {
   if (threadIdx.x < 64) poll_flags(p, target);
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+  __syncthreads();
 }
 
 // ------------------------------------------------------------------ S0 logits
@@ -501,128 +479,80 @@ __device__ inline void build_groups(const Params& p, const Lds& L) {
   __syncthreads();
 }
 
-// ------------------------------------------------------------------ chunk stream
+// ------------------------------------------------------------------ weight stream
 //
-// Each CU streams a sequence of weight chunks: its shared-expert up/gate
-// jobs, its routed up/gate jobs, then its down units.  A chunk is 16 weight
-// rows x 1024 elements of the reduction axis.  Waves load chunks straight
-// into an LDS ring (global_load_lds, 1 KB of one row per instruction, two
-// rows per wave) `ns - 1` chunks ahead of the one being multiplied; wave w
-// multiplies the 128-element K-block w of each chunk.  The activations
-// (x for up/gate, mid for down) are loaded into registers one chunk ahead,
-// always before that step's DMA, so the in-order vmcnt wait for them never
-// waits for a newer DMA.
-
-typedef __attribute__((address_space(3))) char lds_char;
+// Each CU walks a sequence of jobs: its shared-expert up/gate tiles, its
+// routed up/gate tiles (16 weight rows, 8 gate + 8 up, over all of H), then
+// its 16-row down tiles of every used expert (over that expert's
+// intermediate size).  The 8 waves split every job along the reduction
+// axis: wave w owns the 128-element K-blocks w, w+8, w+16, ...  One such
+// K-block of one job is an item: the 16 rows' weights (FP8 32 bytes or
+// MXFP4 16 bytes per lane), the activations of the group's columns and the
+// block scale.  A wave loads its items straight from HBM into registers,
+// D items ahead of the one it multiplies; every item issues the same number
+// of loads, so the in-order wait for item n leaves items n+1..n+D-1 in
+// flight.  (An LDS ring fed by LDS-DMA reached a lower and less steady
+// share of HBM bandwidth.)
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Wave-uniform loop state, re-asserted as uniform: the compiler's uniformity
 // analysis loses track of it across the stream loops (asm results, loop
-// exits), and then keeps it in vector registers behind masked branches.
+// exits) and then keeps it in vector registers behind masked branches.
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// One row segment of up to 1 KB into LDS: 64 lanes x 16 B through a buffer
-// resource whose size is the segment's valid bytes, so lanes past the end
-// (a ragged tail, or a row with no valid bytes) read zeros without touching
-// memory.  The buffer form of the LDS DMA is the one the compiler counts
-// among outstanding vector memory operations.
-__device__ __forceinline__ const void* uniform_ptr(const void* q) {
+// A kernel-argument pointer taken through readfirstlane.  Choosing between
+// two fields of the argument block is otherwise folded into one load from a
+// chosen address, which forces the whole block into scratch memory.
+template <class T>
+__device__ __forceinline__ T* arg_ptr(T* q) {
   const uint64_t v = (uint64_t)q;
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (const void*)(((uint64_t)hi << 32) | lo);
+  return (T*)(((uint64_t)hi << 32) | lo);
 }
 
-// The descriptor's base and size are wave-uniform by construction; taking
-// them through readfirstlane keeps the descriptor in scalar registers (a
-// descriptor the compiler believes divergent costs a loop per instruction).
-__device__ __forceinline__ void dma_row(const uint8_t* base, int nbytes, lds_char* l) {
-  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(base), 0,
-                                                               __builtin_amdgcn_readfirstlane(nbytes), 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)l, 16,
-                                           (threadIdx.x & 63) * 16, 0, 0, 0);
-}
-
-// Waits until at most n of this wave's vector memory operations are
-// outstanding (n is a multiple of 8: a producer issues 8 DMAs per chunk and
-// keeps at most 7 chunks in flight, 56 operations, within the counter's 63).
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-    case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
-    case 24: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
-    case 32: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
-    case 40: asm volatile("s_waitcnt vmcnt(40)" ::: "memory"); break;
-    case 48: asm volatile("s_waitcnt vmcnt(48)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(56)" ::: "memory"); break;
-  }
-}
-
-// Workgroup barrier for LDS traffic only.  It does not wait for the weight
-// DMA still in flight (a __syncthreads() would: its workgroup fence covers
-// the DMA's LDS writes); DMA completion is awaited explicitly with wait_vm.
-__device__ __forceinline__ void bar_lds() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// LDS accesses inside the chunk stream go through these: the compiler cannot
-// tell them apart from the stage a DMA is still writing and would otherwise
-// wait for every outstanding DMA (vmcnt(0)) before each of them.  Every block
-// waits for its own LDS operation, so no asm load leaves a register in flight.
+// LDS accesses of the stream's synchronisation go through these.  Reads
+// wait for themselves; stores are not waited for (a wave's LDS operations
+// complete in order, so a later flag store is seen after the data it
+// publishes, and a compiler-placed lgkmcnt wait that follows stays
+// sufficient: an extra older operation completes first).
 __device__ __forceinline__ uint32_t lds_off(const void* p) {
-  return (uint32_t)(size_t)(const lds_char*)p;
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)p;
 }
-__device__ __forceinline__ uint32_t lds_off(const lds_char* p) { return (uint32_t)(size_t)p; }
 template <class P>
 __device__ __forceinline__ uint32_t lds_ld32(P p) {
   uint32_t v;
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_off(p)) : "memory");
   return v;
 }
-template <class P>
-__device__ __forceinline__ float lds_ldf(P p) { return __uint_as_float(lds_ld32(p)); }
 // For an address every lane of the wave shares.
 __device__ __forceinline__ int lds_ldi_uniform(const int32_t* p) {
   return __builtin_amdgcn_readfirstlane((int)lds_ld32(p));
 }
-// Stores are not waited for: a wave's LDS operations complete in order, so
-// a later flag store is seen after the data it publishes, and every reader
-// waits for its own reads.  (A compiler-placed lgkmcnt wait that follows
-// stays sufficient: an extra older operation completes first.)
 __device__ __forceinline__ void lds_st32(void* p, uint32_t v) {
   asm volatile("ds_write_b32 %0, %1" ::"v"(lds_off(p)), "v"(v) : "memory");
 }
 __device__ __forceinline__ void lds_st128(void* p, u32x4 v) {
   asm volatile("ds_write_b128 %0, %1" ::"v"(lds_off(p)), "v"(v) : "memory");
 }
-// Chunk-stream counters in LDS.  Every counter counts up from 0 within a
-// launch and is written by one wave only.
-constexpr int kCtlReady = 0;   // [2]  chunks producer pw has landed in LDS
-constexpr int kCtlDone = 8;    // [8]  chunks compute wave w has finished reading
+
+// Stream counters in LDS.  Every counter counts up from 0 within a launch
+// and is written by one wave only.
 constexpr int kCtlPart = 16;   // [8]  jobs whose partials wave w has stored
-constexpr int kCtlSlot = 24;   // [2]  1 + the last job summed out of partial slot s
+constexpr int kCtlSlot = 24;   // [4]  1 + the last job summed out of partial slot s
 constexpr int kCtlMidOut = 40; // [8]  1 once wave w's mid stores are complete
 constexpr int kCtlCrossed = 48;// [1]  1 once wave 0 has seen every CU's mid
 
-// Minimum of N consecutive LDS counters (N = 1, 2 or 8), one round trip.
-// Every lane reads the same words; the result is taken through
-// readfirstlane so the compiler knows it is uniform (an asm result is
-// otherwise assumed divergent, and every branch on it becomes a masked one).
+// Minimum of N consecutive LDS counters (N = 1 or 8), one round trip.  Every
+// lane reads the same words; the result goes through readfirstlane so the
+// compiler knows it is uniform.
 template <int N>
 __device__ __forceinline__ uint32_t lds_min(const uint32_t* a) {
   if (N == 1) {
     uint32_t v;
     asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_off(a)) : "memory");
     return __builtin_amdgcn_readfirstlane(v);
-  } else if (N == 2) {
-    uint64_t v;
-    asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_off(a)) : "memory");
-    const uint32_t v0 = (uint32_t)v, v1 = (uint32_t)(v >> 32);
-    return __builtin_amdgcn_readfirstlane(v0 < v1 ? v0 : v1);
   } else {
     u32x4 a0, a1;
     asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
@@ -656,64 +586,13 @@ __device__ inline uint32_t lds_wait(const Params& p, const uint32_t* a, uint32_t
   return v;
 }
 
-// A lane's part of one K-block of the stage, in one round trip: FP8, 32
-// weight bytes; MXFP4, 16.
-template <class P>
-__device__ __forceinline__ void lds_ld_fp8_block(P w, u32x4& a, u32x4& b) {
-  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
-               : "=&v"(a), "=&v"(b)
-               : "v"(lds_off(w))
-               : "memory");
-}
-template <class P>
-__device__ __forceinline__ void lds_ld_fp4_block(P w, u32x4& a) {
-  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(a) : "v"(lds_off(w)) : "memory");
-}
-
-// LDS partials of a cross-wave reduction: wave w's f32x4 of lane l at
-// red[(w*64 + l)*4 ..], so one lane's eight partials sit 1 KB apart.  These
-// read a thread's 8 (down) or 2 x 8 (up/gate: gate at +0, up at +512 B)
-// partials in one round trip.
-__device__ __forceinline__ void lds_ld_partials8(const float* p, float (&a)[8]) {
-  asm volatile(
-      "ds_read_b32 %0, %8\n\tds_read_b32 %1, %8 offset:1024\n\t"
-      "ds_read_b32 %2, %8 offset:2048\n\tds_read_b32 %3, %8 offset:3072\n\t"
-      "ds_read_b32 %4, %8 offset:4096\n\tds_read_b32 %5, %8 offset:5120\n\t"
-      "ds_read_b32 %6, %8 offset:6144\n\tds_read_b32 %7, %8 offset:7168\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]), "=&v"(a[7])
-      : "v"(lds_off(p))
-      : "memory");
-}
-__device__ __forceinline__ void lds_ld_partials16(const float* p, float (&a)[8], float (&b)[8]) {
-  asm volatile(
-      "ds_read_b32 %0, %16\n\tds_read_b32 %1, %16 offset:1024\n\t"
-      "ds_read_b32 %2, %16 offset:2048\n\tds_read_b32 %3, %16 offset:3072\n\t"
-      "ds_read_b32 %4, %16 offset:4096\n\tds_read_b32 %5, %16 offset:5120\n\t"
-      "ds_read_b32 %6, %16 offset:6144\n\tds_read_b32 %7, %16 offset:7168\n\t"
-      "ds_read_b32 %8, %16 offset:512\n\tds_read_b32 %9, %16 offset:1536\n\t"
-      "ds_read_b32 %10, %16 offset:2560\n\tds_read_b32 %11, %16 offset:3584\n\t"
-      "ds_read_b32 %12, %16 offset:4608\n\tds_read_b32 %13, %16 offset:5632\n\t"
-      "ds_read_b32 %14, %16 offset:6656\n\tds_read_b32 %15, %16 offset:7680\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]), "=&v"(a[7]),
-        "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(b[4]), "=&v"(b[5]), "=&v"(b[6]), "=&v"(b[7])
-      : "v"(lds_off(p))
-      : "memory");
-}
-
 // Column tiles a group can have: 1 when NPRE is 1 (batches of at most 16
 // rows), else up to 4 (64 rows).
 template <int NPRE>
 constexpr int max_tiles() { return NPRE == 1 ? 1 : kMaxRows / 16; }
-
-// Per-lane prefetch of one chunk: the activations of column tiles
-// 0..NPRE-1; later tiles are loaded when used.
+// Items in flight per wave.
 template <int NPRE>
-struct Pre {
-  u32x4 B[4 * NPRE];
-  uint32_t sw;  // MXFP4: this lane's row's four E8M0 scales of its K-block
-};
+constexpr int depth() { return NPRE == 1 ? 5 : 3; }
 
 struct Sched {
   int sh_tiles;  // shared up/gate jobs (I_s / 8)
@@ -725,10 +604,7 @@ struct Sched {
   int routed;
 };
 
-// Position in this CU's job sequence.  A job is one up/gate tile of a group
-// (8 gate + 8 up rows of W_gate_up over all of H) or one 16-row tile of this
-// CU's down rows for a group (over the group's intermediate size); it is
-// streamed as nchunks(K) chunks.
+// Position in this CU's job sequence.
 struct It {
   int phase;  // 0 shared up/gate, 1 routed up/gate, 2 down, 3 end
   int j;      // up/gate: global job index; down: group
@@ -745,16 +621,10 @@ __device__ __forceinline__ void uni(It& c) {
   c.tile = uni(c.tile);
 }
 
-__device__ __forceinline__ int nchunks(int kdim) { return (kdim + kChunkElems - 1) / kChunkElems; }
-
 // Smallest j >= begin with j = blockIdx.x (mod ncu): jobs are dealt round-robin.
 __device__ __forceinline__ int first_job(const Params& p, int begin) {
   const int r = begin % p.ncu;
   return begin + (((int)blockIdx.x - r) % p.ncu + p.ncu) % p.ncu;
-}
-
-__device__ __forceinline__ bool blocked(const Sched& s, const It& c) {
-  return c.phase == 0 && c.j >= s.sh_tiles;  // routed work before routing is known
 }
 
 // Up/gate jobs: the shared expert's tiles come first, then rt_tiles tiles
@@ -765,7 +635,7 @@ __device__ inline void settle(const Params& p, const Sched& s, It& c) {
     if (c.phase == 0) {
       c.g = 0;
       c.tile = c.j;
-      if (c.j < s.sh_tiles || !s.routed) return;
+      if (c.j < s.sh_tiles) return;
       c.phase = 1;
       c.j = first_job(p, s.sh_tiles);
       c.g = p.n_shared + (c.j - s.sh_tiles) / s.rt_tiles;
@@ -803,15 +673,19 @@ __device__ inline void next_job(const Params& p, const Sched& s, It& c) {
   settle(p, s, c);
 }
 
-__device__ __forceinline__ int job_group(const Params&, const Sched&, const It& c) { return c.g; }
-__device__ __forceinline__ int job_tile(const Sched&, const It& c) { return c.phase <= 1 ? c.tile : 0; }
 __device__ __forceinline__ bool shared_group(const Params& p, int g) { return p.n_shared && g == 0; }
-__device__ __forceinline__ int job_kdim(const Params& p, const It& c, int g) {
-  return c.phase <= 1 ? p.H : (shared_group(p, g) ? p.Is : p.I);
+__device__ __forceinline__ int job_kdim(const Params& p, const It& c) {
+  // (fields taken through uni(): see arg_ptr)
+  const int H = uni(p.H), I = uni(p.I), Is = uni(p.Is);
+  return c.phase <= 1 ? H : (shared_group(p, c.g) ? Is : I);
 }
-__device__ __forceinline__ int group_ncols(const Params& p, const Lds& L, int g) {
-  if (shared_group(p, g)) return p.T;
-  return lds_ldi_uniform(L.gcnt + g);
+// This wave's items in a job of reduction length kdim: K-blocks w + 8i.
+__device__ __forceinline__ int items_of(int kdim, int w) {
+  const int nkb = kdim >> 7;
+  return nkb > w ? (nkb - 1 - w) / 8 + 1 : 0;
+}
+__device__ __forceinline__ int job_nlive(const Sched& s, const It& c) {
+  return c.phase == 2 ? (s.hc - 16 * c.rt < 16 ? s.hc - 16 * c.rt : 16) : 16;
 }
 // Column c of group g as row*16 + slot.
 __device__ __forceinline__ int col_code(const Params& p, const Lds& L, int g, int c) {
@@ -819,102 +693,204 @@ __device__ __forceinline__ int col_code(const Params& p, const Lds& L, int g, in
   return (int)lds_ld32(L.cols + lds_ldi_uniform(L.gstart + g) + c);
 }
 
-// ---------------------------------------------------------------- producers
+// Column facts of a job's group: its column count and expert (LDS, one
+// round trip for a routed group), and this lane's column code in tiles
+// 0..NT-1 (a lane past the group's columns takes the last column: MFMA
+// columns are independent and that output is never stored).
+template <int NT>
+__device__ inline void group_cols(const Params& p, const Lds& L, int g, int& ncols, int& eid, int (&code)[NT]) {
+  const int lane = threadIdx.x & 63;
+  int gstart = 0;
+  const bool sh = shared_group(p, g);
+  if (sh) {
+    ncols = p.T;
+    eid = 0;
+  } else {
+    uint32_t a, b, c;
+    asm volatile("ds_read_b32 %0, %3\n\tds_read_b32 %1, %4\n\tds_read_b32 %2, %5\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(a), "=&v"(b), "=&v"(c)
+                 : "v"(lds_off(L.gcnt + g)), "v"(lds_off(L.gstart + g)), "v"(lds_off(L.gexp + g))
+                 : "memory");
+    ncols = uni((int)a);
+    gstart = uni((int)b);
+    eid = uni((int)c);
+  }
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) {
+    const int cc = ct * 16 + (lane & 15) < ncols ? ct * 16 + (lane & 15) : ncols - 1;
+    code[ct] = sh ? cc * 16 + p.K : (int)lds_ld32(L.cols + gstart + cc);
+  }
+}
 
-// A producer wave's view of the job it streams: its 8 chunk rows (rows
-// 8pw..8pw+7: gate rows 8t.., up rows I+8t.., or output rows) are
-// consecutive rows of the weight matrix, so one base pointer and the row
-// pitch address them; its lanes' part of the chunk's scale DMA is an offset
-// that moves by 32 bytes per chunk.  Computed once per job.
-struct Feed {
-  It it;
-  int kc, nck;
-  const uint8_t* w;    // first of this wave's rows at K offset 0
-  int rowbytes;        // bytes of one weight row
-  int cbytes;          // bytes of one row per chunk
-  int nl;              // live rows among this wave's 8 (may be <= 0)
+// Activation offset (elements) of column code `code` for lane group lg:
+// x rows for up/gate, mid lines for down.
+__device__ __forceinline__ uint32_t act_offset(const Params& p, int kind, int code, int lg) {
+  return (kind == 1 ? (uint32_t)(code >> 4) * (uint32_t)p.H
+                    : ((uint32_t)(code >> 4) * (uint32_t)(p.K + 1) + (uint32_t)(code & 15)) * (uint32_t)p.mid_ld) +
+         32u * (uint32_t)lg;
+}
+
+// One item in registers.
+template <int NPRE>
+struct Item {
+  u32x4 w0, w1;       // this lane's weights (row lane & 15): FP8 32 bytes, MXFP4 16 (w1 repeats w0)
+  u32x4 B[4 * NPRE];  // activations of column tiles 0..NPRE-1 (column lane & 15 of the tile)
+  uint32_t s;         // FP8: the K-block's scale of the tile's first (lanes 0-31) or second
+                      // (32-63) 128-row block; MXFP4: the lane's row's four E8M0 scales
 };
 
-__device__ inline void feed_job(const Params& p, const Lds& L, const Sched& s, Feed& f, int pw) {
+// The fetch side: where this wave's next items come from.
+template <int NPRE>
+struct Fetch {
+  It it;
+  int i, n;           // next item of the job, this wave's items in it
+  int fmt, live;      // live = 0 past the end of the phase (dummy items)
+  int g, eid;         // group of the last job set up, and its expert
+  const uint8_t* wrow;  // this lane's weight row at K offset 0
+  const uint8_t* srow;  // this lane's scale row (see Item::s)
+  const uint16_t* abase;
+  uint32_t act[NPRE];   // this lane's column per prefetched tile: activation offset
+};
+
+// Weight and scale rows of a job for this lane.  Up/gate: rows 0..7 are gate
+// rows 8t.., 8..15 up rows I+8t..; down: output rows h0+16rt.. (a row past
+// the live rows repeats the last live one).
+template <int NPRE>
+__device__ inline void fetch_job(const Params& p, const Lds& L, const Sched& s, Fetch<NPRE>& f) {
+  const int lane = threadIdx.x & 63, lg = lane >> 4, row = lane & 15;
   const It& c = f.it;
-  const int g = job_group(p, s, c);
-  const bool sh = shared_group(p, g), down = c.phase == 2;
-  const int fmt = sh ? 0 : p.routed_fmt;
-  const int iexp = sh ? p.Is : p.I;
-  const int kdim = down ? iexp : p.H;
-  const int tile = job_tile(s, c);
+  const bool down = c.phase == 2, sh = shared_group(p, c.g);
+  const int iexp = sh ? uni(p.Is) : uni(p.I), kdim = job_kdim(p, c), nlive = job_nlive(s, c);
   const int hb = s.h0 + 16 * c.rt;
-  const int nlive = down ? (s.hc - 16 * c.rt < 16 ? s.hc - 16 * c.rt : 16) : 16;
-  const uint8_t* w;
-  if (sh) {
-    w = down ? p.sh_wd : p.sh_wgu;
-  } else {
-    // W_gate_up [E][2I][H], W_down [E][H][I] bytes (MXFP4: [E][2I][H/2], [E][H][I/2])
-    const size_t e = (size_t)lds_ldi_uniform(L.gexp + g);
-    const size_t H = p.H, I = p.I, div = fmt ? 2 : 1;
-    w = down ? p.wd + e * H * (I / div) : p.wgu + e * 2 * I * (H / div);
-  }
-  f.kc = 0;
-  f.nck = nchunks(kdim);
-  f.rowbytes = fmt ? kdim / 2 : kdim;
-  f.cbytes = fmt ? kChunkElems / 2 : kChunkElems;
-  f.nl = nlive - 8 * pw;
-  // a wave with no live rows keeps a valid base (it loads no bytes)
-  const int row0 = down ? hb + (f.nl > 0 ? 8 * pw : 0) : (pw == 0 ? 8 * tile : iexp + 8 * tile);
-  f.w = w + (size_t)row0 * f.rowbytes;
-}
-
-// Issues chunk f.kc of the job into `stage`: this wave's 8 row DMAs, always
-// issued (a row past the live rows loads no bytes), so its vmcnt
-// bookkeeping is 8 per chunk.
-__device__ inline void feed_chunk(const Feed& f, lds_char* stage, int pw) {
-  const int rb = __builtin_amdgcn_readfirstlane(f.rowbytes);
-  const int cb = __builtin_amdgcn_readfirstlane(f.cbytes);
-  const int koff = __builtin_amdgcn_readfirstlane(f.kc) * cb;
-  const int nbytes = rb - koff < cb ? rb - koff : cb;
-  const int nl = __builtin_amdgcn_readfirstlane(f.nl);
-  const uint8_t* b = (const uint8_t*)uniform_ptr(f.w) + koff;
+  // consecutive jobs of one group (the down tiles of this CU's slice) share
+  // the column lookups
+  if (c.g != f.g) {
+    int ncols, code[NPRE];
+    group_cols<NPRE>(p, L, c.g, ncols, f.eid, code);
+    f.g = c.g;
+    f.abase = down ? arg_ptr(p.mid) : arg_ptr(p.x);
 #pragma unroll
-  for (int q = 0; q < 8; ++q)
-    dma_row(q < nl ? b + q * rb : b, q < nl ? nbytes : 0, stage + (8 * pw + q) * kPitch);
+    for (int ct = 0; ct < NPRE; ++ct) f.act[ct] = act_offset(p, down ? 2 : 1, code[ct], lg);
+  }
+  const int eid = f.eid;
+  f.fmt = sh ? 0 : uni(p.routed_fmt);
+  f.n = items_of(kdim, wave_id());
+  f.i = 0;
+  const int wr = down ? hb + (row < nlive ? row : nlive - 1) : (row < 8 ? 8 * c.tile + row : iexp + 8 * c.tile + row - 8);
+  const size_t H = p.H, I = p.I, e = (size_t)eid;
+  const uint8_t* w;
+  const uint8_t* sc;
+  if (f.fmt == 0) {
+    // FP8 weights [rows][kdim] bytes; fp32 scales [rows/128][kdim/128]
+    const float* S;
+    if (sh) {
+      w = down ? arg_ptr(p.sh_wd) : arg_ptr(p.sh_wgu);
+      S = down ? arg_ptr(p.sh_sd) : arg_ptr(p.sh_sgu);
+    } else {
+      w = down ? arg_ptr(p.wd) + e * H * I : arg_ptr(p.wgu) + e * 2 * I * H;
+      S = down ? (const float*)arg_ptr(p.sd) + e * (H / 128) * (I / 128)
+               : (const float*)arg_ptr(p.sgu) + e * (2 * I / 128) * (H / 128);
+    }
+    const int nkb = kdim / 128;
+    const int nb_lo = down ? hb / 128 : (8 * c.tile) / 128;
+    const int nb_hi = down ? (hb + nlive - 1) / 128 : (iexp + 8 * c.tile) / 128;
+    f.wrow = w + (size_t)wr * kdim;
+    sc = (const uint8_t*)(S + (size_t)(lane < 32 ? nb_lo : nb_hi) * nkb);
+  } else {
+    // MXFP4 weights [rows][kdim/2] bytes; E8M0 scales [rows][kdim/32]
+    w = down ? arg_ptr(p.wd) + e * H * (I / 2) : arg_ptr(p.wgu) + e * 2 * I * (H / 2);
+    const uint8_t* S = down ? (const uint8_t*)arg_ptr(p.sd) + e * H * (I / 32)
+                            : (const uint8_t*)arg_ptr(p.sgu) + e * 2 * I * (H / 32);
+    f.wrow = w + (size_t)wr * (kdim / 2);
+    sc = S + (size_t)wr * (kdim / 32);
+  }
+  f.srow = sc;
 }
 
-// ---------------------------------------------------------------- compute
+// Issues the loads of the fetch side's next item into `it`: always
+// 3 + 4*NPRE loads; a dead item (past the phase) loads from x instead.
+template <int NPRE>
+__device__ __forceinline__ void fetch_item(const Params& p, const Fetch<NPRE>& f, Item<NPRE>& it) {
+  const int lane = threadIdx.x & 63, lg = lane >> 4;
+  const int kb = f.live ? wave_id() + 8 * f.i : 0;
+  const int kbytes = f.fmt ? 64 : 128, lbytes = f.fmt ? 16 : 32;
+  const uint8_t* wp = f.live ? f.wrow + kb * kbytes + lg * lbytes : (const uint8_t*)p.x;
+  const uint8_t* sp = f.live ? f.srow + 4 * kb : (const uint8_t*)p.x;
+  const uint16_t* ab = f.live ? f.abase : arg_ptr(p.x);
+  it.w0 = ld16(wp);
+  it.w1 = ld16(wp + (f.fmt ? 0 : 16));
+  it.s = *(const uint32_t*)sp;
+#pragma unroll
+  for (int ct = 0; ct < NPRE; ++ct) {
+    const uint16_t* a = ab + (f.live ? f.act[ct] + kb * 128 : 0);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) it.B[4 * ct + m] = ld16(a + 8 * m);
+  }
+}
 
-// A compute wave's view of the job it multiplies, computed once per job.
+// Moves the fetch side one item on, over jobs this wave has no items in,
+// and stops (dead items) at phase `stop`.
+template <int NPRE>
+__device__ inline void fetch_next(const Params& p, const Lds& L, const Sched& s, Fetch<NPRE>& f, int stop) {
+  f.live = uni(f.live);
+  if (!f.live) return;
+  f.i = uni(f.i) + 1;
+  f.n = uni(f.n);
+  while (f.i >= f.n) {
+    next_job(p, s, f.it);
+    uni(f.it);
+    if (f.it.phase >= stop) {
+      f.live = 0;
+      return;
+    }
+    fetch_job(p, L, s, f);
+  }
+}
+
+template <int NPRE>
+__device__ inline void fetch_start(const Params& p, const Lds& L, const Sched& s, Fetch<NPRE>& f, It start, int stop) {
+  f.it = start;
+  f.live = start.phase < stop;
+  f.fmt = 0;
+  f.g = -1;
+  f.eid = 0;
+  if (!f.live) return;
+  fetch_job(p, L, s, f);
+  while (f.n == 0) {
+    next_job(p, s, f.it);
+    if (f.it.phase >= stop) {
+      f.live = 0;
+      return;
+    }
+    fetch_job(p, L, s, f);
+  }
+}
+
+// The multiplying side's view of its current job.
 template <int NPRE>
 struct Eat {
   It it;
-  int kc, nck;
+  int i, n;
   int kind;     // 1 up/gate, 2 down
-  int g, tile, rt, fmt, kdim, nlive, ncols, nct;
-  int eid;      // routed expert of the group
+  int g;        // group of the job
+  int fmt, tile, rt, ncols, nct, nlive;
   int split;    // FP8: MFMA output rows (4*lg + q) below it take the first block scale
-  float sreg;   // FP8: lane i < 32 holds the first row block's scale of K-block 8i + wave,
-                // lane 32 + i the second block's (one load per job; read back by readlane)
-  const uint8_t* srow;  // MXFP4: this lane's weight row's E8M0 scales
-  const uint16_t* abase;              // x (up/gate) or mid (down)
-  uint32_t act[max_tiles<NPRE>()];    // this lane's column per tile: activation offset + 32*lg
+  const uint16_t* abase;
+  uint32_t act[max_tiles<NPRE>()];  // this lane's column per tile (tiles >= NPRE are loaded when used)
+  uint32_t pidx[max_tiles<NPRE>()]; // its down products' offset (per-wave layout, see down_direct)
 };
 
 template <int NPRE>
 __device__ inline void eat_job(const Params& p, const Lds& L, const Sched& s, Eat<NPRE>& e) {
-  const int lane = threadIdx.x & 63, lg = lane >> 4;
+  const int lg = (threadIdx.x & 63) >> 4;
   const It& c = e.it;
-  e.kc = 0;
-  // consecutive jobs of one group (the down tiles of a CU's slice) share
-  // the column lookups
-  const int g = job_group(p, s, c), kind = c.phase <= 1 ? 1 : 2;
-  const bool same = g == e.g && kind == e.kind;
-  e.g = g;
-  const bool sh = shared_group(p, e.g);
-  e.kind = kind;
-  e.fmt = sh ? 0 : p.routed_fmt;
-  e.kdim = job_kdim(p, c, e.g);
-  e.nck = nchunks(e.kdim);
-  e.tile = job_tile(s, c);
+  e.kind = c.phase <= 1 ? 1 : 2;
+  e.fmt = shared_group(p, c.g) ? 0 : uni(p.routed_fmt);
+  e.tile = c.phase <= 1 ? c.tile : 0;
   e.rt = c.phase == 2 ? c.rt : 0;
-  e.nlive = e.kind == 2 ? (s.hc - 16 * e.rt < 16 ? s.hc - 16 * e.rt : 16) : 16;
+  e.nlive = job_nlive(s, c);
+  e.n = items_of(job_kdim(p, c), wave_id());
+  e.i = 0;
   if (e.kind == 1) {
     e.split = 8;  // rows 0..7 of the MFMA tile are gate rows, 8..15 up rows
   } else {
@@ -922,161 +898,52 @@ __device__ inline void eat_job(const Params& p, const Lds& L, const Sched& s, Ea
     const int hb = s.h0 + 16 * e.rt;
     e.split = (hb / 128 + 1) * 128 - hb;
   }
-  int gstart = 0;
-  if (same) {
-  } else if (sh) {
-    e.ncols = p.T;
-  } else {
-    uint32_t a, b, c;
-    asm volatile("ds_read_b32 %0, %3\n\tds_read_b32 %1, %4\n\tds_read_b32 %2, %5\n\ts_waitcnt lgkmcnt(0)"
-                 : "=&v"(a), "=&v"(b), "=&v"(c)
-                 : "v"(lds_off(L.gcnt + e.g)), "v"(lds_off(L.gstart + e.g)), "v"(lds_off(L.gexp + e.g))
-                 : "memory");
-    e.ncols = uni((int)a);
-    gstart = uni((int)b);
-    e.eid = uni((int)c);
-  }
-  const size_t eid = (size_t)e.eid;
-  // the job's weight scales
-  {
-    const size_t H = p.H, I = p.I;
-    const int iexp = sh ? p.Is : p.I;
-    const int hb = s.h0 + 16 * e.rt;
-    if (e.fmt == 0) {
-      const float* S;
-      if (sh) S = e.kind == 1 ? p.sh_sgu : p.sh_sd;
-      else S = e.kind == 1 ? (const float*)p.sgu + eid * (2 * I / 128) * (H / 128)
-                           : (const float*)p.sd + eid * (H / 128) * (I / 128);
-      const int nkb = e.kdim / 128;
-      const int nb_lo = e.kind == 1 ? (8 * e.tile) / 128 : hb / 128;
-      const int nb_hi = e.kind == 1 ? (iexp + 8 * e.tile) / 128 : (hb + e.nlive - 1) / 128;
-      const int kb = (lane & 31) * 8 + wave_id();
-      e.sreg = (lane & 31) < e.nck && kb < nkb ? S[(size_t)(lane < 32 ? nb_lo : nb_hi) * nkb + kb] : 0.f;
-    } else {
-      const uint8_t* S = e.kind == 1 ? (const uint8_t*)p.sgu + eid * 2 * I * (H / 32)
-                                     : (const uint8_t*)p.sd + eid * H * (I / 32);
-      const int row = lane & 15;
-      const int wr = e.kind == 1 ? (row < 8 ? 8 * e.tile + row : iexp + 8 * e.tile + row - 8)
-                                 : hb + (row < e.nlive ? row : e.nlive - 1);
-      e.srow = S + (size_t)wr * (e.kdim / 32);
-    }
-  }
-  if (same) return;
+  // consecutive jobs of one group (the down tiles of this CU's slice, within
+  // one phase) have the same columns
+  if (c.g == e.g) return;
+  e.g = c.g;
+  int eid, code[max_tiles<NPRE>()];
+  group_cols<max_tiles<NPRE>()>(p, L, c.g, e.ncols, eid, code);
   e.nct = (e.ncols + 15) >> 4;
-  e.abase = e.kind == 1 ? p.x : p.mid;
-  // a lane past the group's columns takes the last column: MFMA columns
-  // are independent and that output is never stored
-  int codes[max_tiles<NPRE>()];
+  e.abase = e.kind == 1 ? arg_ptr(p.x) : arg_ptr(p.mid);
 #pragma unroll
   for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) {
-    const int cc = ct * 16 + (lane & 15) < e.ncols ? ct * 16 + (lane & 15) : e.ncols - 1;
-    codes[ct] = sh ? cc * 16 + p.K : gstart + cc;
-  }
-  if (!sh) {
-    // the routed group's column codes, all tiles in one round trip
-    if (max_tiles<NPRE>() == 1) {
-      asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
-                   : "=v"(codes[0]) : "v"(lds_off(L.cols + codes[0])) : "memory");
-    } else {
-      int c4[4];
-      asm volatile("ds_read_b32 %0, %4\n\tds_read_b32 %1, %5\n\tds_read_b32 %2, %6\n\tds_read_b32 %3, %7\n\t"
-                   "s_waitcnt lgkmcnt(0)"
-                   : "=&v"(c4[0]), "=&v"(c4[1]), "=&v"(c4[2]), "=&v"(c4[3])
-                   : "v"(lds_off(L.cols + codes[0])), "v"(lds_off(L.cols + codes[max_tiles<NPRE>() > 1 ? 1 : 0])),
-                     "v"(lds_off(L.cols + codes[max_tiles<NPRE>() > 2 ? 2 : 0])),
-                     "v"(lds_off(L.cols + codes[max_tiles<NPRE>() > 3 ? 3 : 0]))
-                   : "memory");
-#pragma unroll
-      for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) codes[ct] = c4[ct];
-    }
-  }
-#pragma unroll
-  for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) {
-    const int code = codes[ct];
-    e.act[ct] = (e.kind == 1 ? (uint32_t)(code >> 4) * (uint32_t)p.H
-                             : ((uint32_t)(code >> 4) * (uint32_t)(p.K + 1) + (uint32_t)(code & 15)) *
-                                   (uint32_t)p.mid_ld) +
-                32u * lg;
+    e.act[ct] = act_offset(p, e.kind, code[ct], lg);
+    e.pidx[ct] = ((uint32_t)(code[ct] >> 4) * (uint32_t)(p.K + 1) + (uint32_t)(code[ct] & 15)) *
+                 (uint32_t)prod_pitch(p.hs);
   }
 }
 
-// Activations of column tile ct at K-block kb for this lane: the 8 bf16 at
-// elements kb*128 + 32*(lane >> 4) + 8m .. +7 of its column's row (x for
-// up/gate, the mid line for down).
-template <int NPRE>
-__device__ __forceinline__ void load_tile(const Eat<NPRE>& e, int kb, int ct, u32x4* B) {
-  const uint16_t* ptr = e.abase + e.act[ct] + kb * 128;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) B[m] = ld16(ptr + 8 * m);
-}
-
-// The activations of chunk e.kc for tiles 0..NPRE-1, one chunk ahead of
-// their use.  Every register is loaded on every call (a wave past the
-// chunk's K range loads the last block again): a register that is only
-// sometimes loaded makes the compiler wait for all loads before the merge.
-template <int NPRE>
-__device__ inline void load_pre(const Eat<NPRE>& e, Pre<NPRE>& P) {
-  const int nkb = (e.kdim + 127) >> 7;
-  const int kb = e.kc * 8 + wave_id() < nkb ? e.kc * 8 + wave_id() : nkb - 1;
-#pragma unroll
-  for (int ct = 0; ct < NPRE; ++ct) load_tile(e, kb, ct, P.B + 4 * ct);
-  if (e.fmt != 0) P.sw = *(const uint32_t*)(e.srow + 4 * kb);
-}
-
-// Marks every prefetched register as read here, on every path: the wait for
-// them then happens once, at this point.
-template <int NPRE>
-__device__ __forceinline__ void settle_pre(const Pre<NPRE>& P, int fmt) {
-#pragma unroll
-  for (int i = 0; i < 4 * NPRE; ++i) asm volatile("" ::"v"(P.B[i]));
-  if (fmt != 0) asm volatile("" ::"v"(P.sw));
-}
-
-// Multiplies this wave's K-block of the chunk in `stage` into acc[ct].
-// FP8: a 4-MFMA block sum per K-block, then times its 128x128 block scale.
-// MXFP4: the E8M0 scale is folded into the exact bf16 conversion.
-// This wave's weights of a chunk, copied out of the stage so the stage can
-// be released before the math: FP8 32 bytes per lane, MXFP4 16.
-struct Raw {
-  u32x4 a0, a1;
-};
-
-// False when the wave has no K-block in this chunk (a ragged last chunk).
+// Multiplies one item into acc[ct].  FP8: a 4-MFMA block sum, then times the
+// 128x128 block scale of the output row; MXFP4: the E8M0 scale is folded
+// into the exact bf16 conversion.
 template <int F, int NPRE>
-__device__ __forceinline__ bool fetch_chunk(const Eat<NPRE>& e, const lds_char* stage, Raw& r) {
-  const int lane = threadIdx.x & 63, lg = lane >> 4, row = lane & 15;
-  const int wave = wave_id();
-  if ((e.kc * 8 + wave) * 128 >= e.kdim) return false;
-  if (F == 0) lds_ld_fp8_block(stage + row * kPitch + wave * 128 + 32 * lg, r.a0, r.a1);
-  else lds_ld_fp4_block(stage + row * kPitch + wave * 64 + 16 * lg, r.a0);
-  return true;
-}
-
-template <int F, int NPRE>
-__device__ inline void compute_chunk(const Eat<NPRE>& e, const Raw& r, const Pre<NPRE>& P, f32x4* acc) {
-  const int lane = threadIdx.x & 63, lg = lane >> 4;
-  const int kb = e.kc * 8 + wave_id();
+__device__ inline void eat_item(const Eat<NPRE>& e, const Item<NPRE>& it, f32x4* acc) {
+  const int lg = (threadIdx.x & 63) >> 4;
+  const int kb = wave_id() + 8 * e.i;
   bf16x8 A[4];
   float s_lo = 1.f, s_hi = 1.f;
   if (F == 0) {
-    A[0] = e4m3x8_to_bf16(r.a0[0], r.a0[1]);
-    A[1] = e4m3x8_to_bf16(r.a0[2], r.a0[3]);
-    A[2] = e4m3x8_to_bf16(r.a1[0], r.a1[1]);
-    A[3] = e4m3x8_to_bf16(r.a1[2], r.a1[3]);
-    s_lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e.sreg), e.kc));
-    s_hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e.sreg), 32 + e.kc));
+    A[0] = e4m3x8_to_bf16(it.w0[0], it.w0[1]);
+    A[1] = e4m3x8_to_bf16(it.w0[2], it.w0[3]);
+    A[2] = e4m3x8_to_bf16(it.w1[0], it.w1[1]);
+    A[3] = e4m3x8_to_bf16(it.w1[2], it.w1[3]);
+    s_lo = __int_as_float(__builtin_amdgcn_readlane((int)it.s, 0));
+    s_hi = __int_as_float(__builtin_amdgcn_readlane((int)it.s, 32));
   } else {
-    const float sc = e8m0_to_f32((P.sw >> (8 * lg)) & 0xffu);
+    const float sc = e8m0_to_f32((it.s >> (8 * lg)) & 0xffu);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) A[m] = e2m1x8_to_bf16(r.a0[m], sc);
+    for (int m = 0; m < 4; ++m) A[m] = e2m1x8_to_bf16(it.w0[m], sc);
   }
 #pragma unroll
   for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) {
     if (ct < e.nct) {
       u32x4 Bl[4];
-      const u32x4* B = P.B + 4 * (ct < NPRE ? ct : 0);
+      const u32x4* B = it.B + 4 * (ct < NPRE ? ct : 0);
       if (ct >= NPRE) {
-        load_tile(e, kb, ct, Bl);
+        const uint16_t* a = e.abase + e.act[ct] + kb * 128;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) Bl[m] = ld16(a + 8 * m);
         B = Bl;
       }
       if (F == 0) {
@@ -1093,14 +960,13 @@ __device__ inline void compute_chunk(const Eat<NPRE>& e, const Raw& r, const Pre
   }
 }
 
-// Job-end reductions.  At the end of a job every compute wave stores its
-// partial tiles into partial slot (job % slots) and raises its part count;
-// it never waits for the others there.  Job j is summed by its owner wave
-// (j mod 8) later: at the owner's next job end, at the up/gate -> down
-// hand-over, or while the owner waits for a slot.  The sum runs over the
-// waves in order 0..7, exactly as a workgroup-wide reduction would.  A slot
-// is reused for job j only after job j - slots was summed out of it.
-template <int NPRE>
+// Job-end reductions.  At the end of a job every wave stores its partial
+// tiles into partial slot (job % slots) and raises its part count; it never
+// waits for the others there.  Job j is summed by its owner wave (j mod 8)
+// later: at the owner's next job end, at the up/gate -> down hand-over, or
+// while the owner waits for a slot.  The sum runs over the waves in order
+// 0..7, exactly as a workgroup-wide reduction would.  A slot is reused for
+// job j only after job j - slots was summed out of it.
 struct Owned {
   int jc;       // the job's index in this CU's sequence, -1 when none
   int kind, g, tile, rt, ncols, nct, nlive;
@@ -1119,7 +985,6 @@ __device__ __forceinline__ void lds_ld_wave_partials(const float* t, u32x4 (&v)[
       : "memory");
 }
 
-template <int NPRE>
 __device__ __forceinline__ const float* red_slot(const Lds& L, int T, int jc) {
   return L.red + (size_t)(jc % red_slots(T)) * red_tiles(T) * (kRedTileBytes / 4);
 }
@@ -1130,9 +995,9 @@ __device__ __forceinline__ const float* red_slot(const Lds& L, int T, int jc) {
 // four intermediates, mid = silu(gate) * up rounded to bf16.  Down: every
 // lane finishes its four rows into the LDS products.
 template <int NPRE>
-__device__ inline void sum_job(const Params& p, const Lds& L, const Owned<NPRE>& o) {
+__device__ inline void sum_job(const Params& p, const Lds& L, const Owned& o) {
   const int lane = threadIdx.x & 63;
-  const float* base = red_slot<NPRE>(L, p.T, o.jc);
+  const float* base = red_slot(L, p.T, o.jc);
 #pragma unroll
   for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) {
     if (ct < o.nct) {
@@ -1180,9 +1045,8 @@ __device__ inline void sum_job(const Params& p, const Lds& L, const Owned<NPRE>&
           const int i = 4 * (lane >> 4) + q;
           if (i < o.nlive && col < o.ncols) {
             if (!isfinite(v)) set_err(p.err, kErrMid);
-            const size_t at = ((size_t)(code >> 4) * (p.K + 1) + (code & 15)) * p.hs + 16 * o.rt + i;
-            if (NPRE == 1) lds_st32(L.pbuf + at, __float_as_uint(v));
-            else p.prod[(size_t)blockIdx.x * p.T * (p.K + 1) * p.hs + at] = v;
+            lds_st32(L.pbuf + ((size_t)(code >> 4) * (p.K + 1) + (code & 15)) * p.hs + 16 * o.rt + i,
+                     __float_as_uint(v));
           }
         }
       }
@@ -1193,30 +1057,42 @@ __device__ inline void sum_job(const Params& p, const Lds& L, const Owned<NPRE>&
 // Sums the owned job when every wave's partials are in (or waits for them
 // when `block`), then releases its slot.
 template <int NPRE>
-__device__ inline void service(const Params& p, const Lds& L, Owned<NPRE>& o, bool block, bool& ok) {
+__device__ inline void service(const Params& p, const Lds& L, Owned& o, bool block, bool& ok) {
   o.jc = uni(o.jc);
   if (o.jc < 0) return;
   if (block) lds_wait<8>(p, L.ctl + kCtlPart, (uint32_t)(o.jc + 1), ok);
   else if (ok && (int)lds_min<8>(L.ctl + kCtlPart) < o.jc + 1) return;
-  sum_job(p, L, o);
+  sum_job<NPRE>(p, L, o);
   lds_st32(L.ctl + kCtlSlot + o.jc % red_slots(p.T), (uint32_t)(o.jc + 1));
   o.jc = -1;
 }
 
 // End of job jc for this wave: wait for its slot (summing an owned job
-// meanwhile), store the partial tiles, raise the part count, finish an older
-// owned job, and take ownership of jc when it is this wave's.
+// meanwhile), store the partial tiles, raise the part count, sum an older
+// owned job if its partials are all in, and take ownership of jc when it is
+// this wave's.
 template <int NPRE>
-__device__ inline void job_end(const Params& p, const Lds& L, const Eat<NPRE>& e, f32x4* acc, int jc,
-                               Owned<NPRE>& own, bool& ok) {
+__device__ inline void job_end(const Params& p, const Lds& L, const Eat<NPRE>& e, f32x4* acc, int jc, Owned& own,
+                               bool& ok) {
   const int lane = threadIdx.x & 63, wave = wave_id();
+  if (NPRE == 1 && e.kind == 2 && down_direct(p.T)) {
+    // this wave's partial of the tile into its own products; the combine sums the waves
+    float* P = L.pbuf + (size_t)wave * p.T * (p.K + 1) * prod_pitch(p.hs);
+#pragma unroll
+    for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) {
+      if (ct < e.nct)
+        lds_st128(P + e.pidx[ct] + 16 * e.rt + 4 * (lane >> 4), __builtin_bit_cast(u32x4, acc[ct]));
+      acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    return;
+  }
   const int ns = red_slots(p.T);
   if (jc >= ns) {
     const uint32_t target = (uint32_t)(jc - ns + 1);
     const uint32_t* sd = L.ctl + kCtlSlot + jc % ns;
     int spins = 0;
     while (ok && lds_min<1>(sd) < target) {
-      service(p, L, own, false, ok);
+      service<NPRE>(p, L, own, false, ok);
       if (++spins > kSpinLimit) {
         set_err(p.err, kErrTimeout);
         ok = false;
@@ -1225,18 +1101,19 @@ __device__ inline void job_end(const Params& p, const Lds& L, const Eat<NPRE>& e
       __builtin_amdgcn_s_sleep(1);
     }
   }
-  float* base = (float*)red_slot<NPRE>(L, p.T, jc);
+  float* base = (float*)red_slot(L, p.T, jc);
 #pragma unroll
   for (int ct = 0; ct < max_tiles<NPRE>(); ++ct)
     if (ct < e.nct)
       lds_st128(base + (size_t)ct * (kRedTileBytes / 4) + ((size_t)wave * 64 + lane) * 4,
                 __builtin_bit_cast(u32x4, acc[ct]));
   lds_st32(L.ctl + kCtlPart + wave, (uint32_t)(jc + 1));
-  service(p, L, own, true, ok);
+  service<NPRE>(p, L, own, false, ok);
   if (jc % kWaves == wave) {
+    service<NPRE>(p, L, own, true, ok);  // the previous owned job, 8 jobs back
     own.jc = jc;
     own.kind = e.kind;
-    own.g = e.g;
+    own.g = e.it.g;
     own.tile = e.tile;
     own.rt = e.rt;
     own.ncols = e.ncols;
@@ -1247,18 +1124,87 @@ __device__ inline void job_end(const Params& p, const Lds& L, const Eat<NPRE>& e
   for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
+// Moves the multiplying side on after an item; at the end of a job (and for
+// every following job this wave has no items in) runs the job end.  Returns
+// false once the phase is done.
+template <int NPRE>
+__device__ inline bool eat_next(const Params& p, const Lds& L, const Sched& s, Eat<NPRE>& e, f32x4* acc, int& jc,
+                                Owned& own, bool& ok, int stop) {
+  e.i = uni(e.i) + 1;
+  e.n = uni(e.n);
+  while (e.i >= e.n) {
+    job_end<NPRE>(p, L, e, acc, jc++, own, ok);
+    next_job(p, s, e.it);
+    uni(e.it);
+    if (e.it.phase >= stop) return false;
+    eat_job(p, L, s, e);
+  }
+  return true;
+}
+
+// One phase (up/gate, or down) of the stream: a D-deep register pipeline.
+// Each step multiplies item n out of ring slot n % D and refills that slot
+// with item n + D.
+template <int NPRE, int FMT>
+__device__ __forceinline__ void run_phase(const Params& p, const Lds& L, const Sched& s, It start, int stop, f32x4* acc,
+                                 int& jc, Owned& own, bool& ok) {
+  constexpr int D = depth<NPRE>();
+  if (start.phase >= stop) return;
+  Fetch<NPRE> f;
+  fetch_start(p, L, s, f, start, stop);
+  Item<NPRE> ring[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    fetch_item(p, f, ring[d]);
+    fetch_next(p, L, s, f, stop);
+  }
+  Eat<NPRE> e;
+  e.it = start;
+  e.g = -1;
+  eat_job(p, L, s, e);
+  // jobs this wave has no items in still end (with zero partials)
+  bool more = true;
+  while (e.n == 0 && more) {
+    job_end<NPRE>(p, L, e, acc, jc++, own, ok);
+    next_job(p, s, e.it);
+    if (e.it.phase >= stop) more = false;
+    else eat_job(p, L, s, e);
+  }
+  while (more) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (more) {
+        if (e.fmt == 0) eat_item<0>(e, ring[d], acc);
+        else eat_item<FMT>(e, ring[d], acc);
+        fetch_item(p, f, ring[d]);
+        fetch_next(p, L, s, f, stop);
+        more = eat_next(p, L, s, e, acc, jc, own, ok, stop);
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the dead items' loads
+}
+
 // out[r][h] = P_shared + sum_p w[r][p] * P[r][p], fp32 FMA chain in slot
 // order, rounded to bf16 once.
-// The products are in LDS for batches of at most 16 rows, else in this
-// CU's part of the workspace.
-template <int NPRE>
+// With per-wave down products, each product is first summed over the waves
+// in order 0..7 (the same sum a job-end reduction forms).
+__device__ __forceinline__ float down_product(const Params& p, const Lds& L, int r, int slot, int hl) {
+  if (!down_direct(p.T)) return L.pbuf[((size_t)r * (p.K + 1) + slot) * p.hs + hl];
+  const size_t wstride = (size_t)p.T * (p.K + 1) * prod_pitch(p.hs);
+  const float* q = L.pbuf + ((size_t)r * (p.K + 1) + slot) * prod_pitch(p.hs) + hl;
+  float v = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) v += q[w * wstride];
+  if (!isfinite(v)) set_err(p.err, kErrMid);
+  return v;
+}
+
 __device__ inline void combine(const Params& p, const Lds& L, const Sched& s) {
-  const float* P = NPRE == 1 ? L.pbuf : p.prod + (size_t)blockIdx.x * p.T * (p.K + 1) * p.hs;
   for (int t = threadIdx.x; t < p.T * s.hc; t += kThreads) {
     const int r = t / s.hc, hl = t - r * s.hc;
-    const float* pr = P + (size_t)r * (p.K + 1) * p.hs + hl;
-    float acc = p.n_shared ? pr[(size_t)p.K * p.hs] : 0.f;
-    for (int k = 0; k < p.K; ++k) acc = fmaf(L.w[r * p.K + k], pr[(size_t)k * p.hs], acc);
+    float acc = p.n_shared ? down_product(p, L, r, p.K, hl) : 0.f;
+    for (int k = 0; k < p.K; ++k) acc = fmaf(L.w[r * p.K + k], down_product(p, L, r, k, hl), acc);
     p.out[(size_t)r * p.H + s.h0 + hl] = (uint16_t)f32_to_bf16_rne(acc);
   }
 }
@@ -1269,10 +1215,7 @@ template <int MODE, int FMT, int NPRE>
 __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const Lds L = lds_map(smem, p);
-  lds_char* const st3 = (lds_char*)(smem + (L.stages - smem));
   const int tid = threadIdx.x, wave = wave_id();
-  const bool producer = wave >= kWaves;
-  const int pw = wave - kWaves;
 
   MOE_STAMP(p, 0);
   if (tid < 64) L.ctl[tid] = 0u;
@@ -1280,41 +1223,6 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
     L.misc[1] = (int32_t)__hip_atomic_load(&p.flags[blockIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const uint32_t epoch = (uint32_t)__builtin_amdgcn_readfirstlane(L.misc[1]);
-
-  Sched s;
-  s.sh_tiles = (MODE == kModeForward && p.n_shared) ? p.Is / 8 : 0;
-  s.rt_tiles = p.I / 8;
-  s.n_jobs = 0;
-  s.G = 0;
-  s.routed = 0;
-  s.h0 = blockIdx.x * p.hs;
-  s.hc = p.H - s.h0 < p.hs ? p.H - s.h0 : p.hs;
-  if (s.hc < 0) s.hc = 0;
-  s.nrt = (s.hc + 15) / 16;
-
-  // Producer waves stream weight chunks into the LDS ring; they issue no
-  // other vector memory operation, so their in-order vmcnt tracks the ring
-  // exactly, and the compute waves' activation loads never queue behind a
-  // DMA.
-  Feed feed;
-  feed.it = It{0, first_job(p, 0), 0, 0, 0};
-  feed.kc = 0;
-  int n_i = 0, n_c = 0;
-  settle(p, s, feed.it);
-  // S1: the shared expert's up/gate chunks need no routing: start them now
-  if (MODE == kModeForward && producer) {
-    __builtin_amdgcn_s_setprio(3);
-    while (n_i < p.ns - 1 && feed.it.phase < 3 && !blocked(s, feed.it)) {
-      if (feed.kc == 0) feed_job(p, L, s, feed, pw);
-      feed_chunk(feed, st3 + (n_i % p.ns) * kStageBytes, pw);
-      ++n_i;
-      if (++feed.kc == feed.nck) {
-        feed.kc = 0;
-        next_job(p, s, feed.it);
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
-  }
 
   // S0: router logits of this CU's experts, published for every CU
   router_logits(p);
@@ -1325,8 +1233,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   // S2: route every row, then group the step's distinct experts
   wait_all(p, epoch + 1);
   MOE_STAMP(p, 2);
-  if (!producer)
-    for (int r = wave; r < p.T; r += kWaves) route_row(p, L, r);
+  for (int r = wave; r < p.T; r += kWaves) route_row(p, L, r);
   __syncthreads();
   if (MODE == kModeRoute) {
     for (int u = tid; u < p.T * p.K; u += kThreads) {
@@ -1343,7 +1250,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
     if (tid == 0) {
       o[0] = G; o[1] = p.T; o[2] = p.K; o[3] = p.n_shared;
     }
-    // g differs per thread here, so plain LDS reads (no DMA is in flight)
+    // g differs per thread here, so plain LDS reads
     for (int g = tid; g < G; g += kThreads) {
       o[4 + g] = p.n_shared && g == 0 ? -1 : L.gexp[g];
       o[4 + G + g] = p.n_shared && g == 0 ? p.T : L.gcnt[g];
@@ -1353,191 +1260,70 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
     for (int c = tid; c < ncol; c += kThreads) o[4 + 3 * G + c] = L.cols[c];
     return;
   }
+
+  Sched s;
+  s.sh_tiles = p.n_shared ? p.Is / 8 : 0;
+  s.rt_tiles = p.I / 8;
   s.G = G;
   s.n_jobs = s.sh_tiles + (G - p.n_shared) * s.rt_tiles;
   s.routed = 1;
-  settle(p, s, feed.it);
-  It start = It{0, first_job(p, 0), 0, 0, 0};
-  settle(p, s, start);
+  s.h0 = blockIdx.x * p.hs;
+  s.hc = uni(p.H) - s.h0 < uni(p.hs) ? uni(p.H) - s.h0 : uni(p.hs);
+  if (s.hc < 0) s.hc = 0;
+  s.nrt = (s.hc + 15) / 16;
 
-  // S3 / S4: the chunk stream.  The second flag (every CU's mid is out) is
-  // raised after this CU's last up/gate job and awaited before the first
-  // down chunk's activations are read; only the compute waves take part.
-#ifdef MOE_LAPS
-  uint64_t cyc[6] = {0, 0, 0, 0, 0, 0};
-  uint64_t tq = __builtin_amdgcn_s_memtime();
-#define MOE_LAP(i)                                    \
-  do {                                                \
-    const uint64_t t2 = __builtin_amdgcn_s_memtime(); \
-    cyc[i] += t2 - tq;                                \
-    tq = t2;                                          \
-  } while (0)
-#else
-#define MOE_LAP(i) \
-  do {             \
-  } while (0)
-#endif
+  // S3 / S4: the weight stream.  The second flag (every CU's mid is out) is
+  // raised after this CU's up/gate jobs and awaited before any down
+  // activation is loaded.
   bool ok = true;
-
-  // The producers and the compute waves never meet at a workgroup barrier
-  // inside the stream: they hand chunks over through LDS counters.  A
-  // producer keeps up to ns - 1 chunks in flight; when the oldest has
-  // landed (its in-order vmcnt says so) it raises its ready count, and it
-  // refills a stage once every compute wave's done count has passed the
-  // chunk that stage held.  A compute wave waits for both producers' ready
-  // counts, multiplies the chunk, raises its done count, and prefetches the
-  // next chunk's activations.  Per-job descriptors are computed when a job
-  // starts; a chunk only moves offsets.
-  if (producer) {
-    // The producers are the workgroup's youngest waves; the SIMD arbiter
-    // favours older waves, so without a raised priority the compute waves
-    // sharing their SIMDs starve the DMA issue.
-    __builtin_amdgcn_s_setprio(3);
-    int n_r = 0;       // chunks this wave has reported landed
-    uint32_t cdone = 0;  // last read minimum of the compute waves' done counts
-    for (;;) {
-      n_i = uni(n_i);
-      n_r = uni(n_r);
-      uni(feed.it);
-      feed.kc = uni(feed.kc);
-      if (feed.it.phase >= 3) break;
-      if (feed.kc == 0) feed_job(p, L, s, feed, pw);
-      // room for chunk n_i: fewer than ns - 1 chunks in flight, and its
-      // stage released by every compute wave; meanwhile report landings
-      while (n_i - n_r >= p.ns - 1 || (ok && n_i - (int)cdone >= p.ns)) {
-        if (n_i - (int)cdone >= p.ns) cdone = lds_min<8>(L.ctl + kCtlDone);
-        if (n_i - n_r >= p.ns - 1 || (n_r < n_i && n_i - (int)cdone >= p.ns)) {
-          wait_vm(8 * (n_i - 1 - n_r));
-          ++n_r;
-          lds_st32(L.ctl + kCtlReady + pw, (uint32_t)n_r);
-        } else if (n_i - (int)cdone >= p.ns) {
-          lds_wait<8>(p, L.ctl + kCtlDone, (uint32_t)(n_i - p.ns + 1), ok);
-          cdone = (uint32_t)(n_i - p.ns + 1);
-        }
-        n_r = uni(n_r);
-      }
-      MOE_LAP(0);
-      feed_chunk(feed, st3 + (n_i % p.ns) * kStageBytes, pw);
-      ++n_i;
-      if (++feed.kc == feed.nck) {
-        feed.kc = 0;
-        next_job(p, s, feed.it);
-      }
-      MOE_LAP(1);
-    }
-    while (n_r < n_i) {
-      wait_vm(8 * (n_i - 1 - n_r));
-      ++n_r;
-      lds_st32(L.ctl + kCtlReady + pw, (uint32_t)n_r);
-    }
-    n_c = n_r;
-    __builtin_amdgcn_s_setprio(0);
-  } else {
-    constexpr int MAXCT = max_tiles<NPRE>();
-    const int wave_c = wave;
-    bool passed2 = false;
-    // every compute wave has completed its mid stores; wave 0 publishes and,
-    // when this CU has down work, waits for every CU and tells the others
-    int jc = 0;  // jobs ended
-    Owned<NPRE> own;
-    own.jc = -1;
-    auto cross_to_down = [&](const It& c) {
-      if (!passed2 && c.phase >= 2) {
-        MOE_STAMP(p, 4);
-        service(p, L, own, true, ok);  // this wave's last owned up/gate job
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        lds_st32(L.ctl + kCtlMidOut + wave_c, 1u);
-        if (wave_c == 0) {
-          lds_wait<8>(p, L.ctl + kCtlMidOut, 1u, ok);
-          if (threadIdx.x == 0) {
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-            __hip_atomic_store(&p.flags[blockIdx.x], epoch + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-          if (c.phase == 2) poll_flags(p, epoch + 2);
-          lds_st32(L.ctl + kCtlCrossed, 1u);
-        }
-        if (c.phase == 2) lds_wait<1>(p, L.ctl + kCtlCrossed, 1u, ok);
-        MOE_STAMP(p, 5);
-        passed2 = true;
-      }
-    };
-    Eat<NPRE> e;
-    e.it = start;
-    e.g = -1;
-    e.kind = 0;
-    e.eid = 0;
-    Pre<NPRE> pre;
-    f32x4 acc[MAXCT];
+  int jc = 0;  // jobs ended
+  Owned own;
+  own.jc = -1;
+  constexpr int MAXCT = max_tiles<NPRE>();
+  f32x4 acc[MAXCT];
 #pragma unroll
-    for (int ct = 0; ct < MAXCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint32_t rdy = 0;  // last seen minimum of the producers' ready counts
-    cross_to_down(e.it);
-    if (e.it.phase < 3) {
-      eat_job(p, L, s, e);
-      load_pre(e, pre);
+  for (int ct = 0; ct < MAXCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  It up = It{0, first_job(p, 0), 0, 0, 0};
+  settle(p, s, up);
+  run_phase<NPRE, FMT>(p, L, s, up, 2, acc, jc, own, ok);
+
+  It down = It{2, 0, 0, 0, 0};
+  settle(p, s, down);
+  MOE_STAMP(p, 4);
+  service<NPRE>(p, L, own, true, ok);  // this wave's last owned up/gate job
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_st32(L.ctl + kCtlMidOut + wave, 1u);
+  if (wave == 0) {
+    lds_wait<8>(p, L.ctl + kCtlMidOut, 1u, ok);
+    if (tid == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_store(&p.flags[blockIdx.x], epoch + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    while (e.it.phase < 3) {
-      n_c = uni(n_c);
-      rdy = (uint32_t)uni((int)rdy);
-      uni(e.it);
-      e.kc = uni(e.kc);
-      e.nck = uni(e.nck);
-      e.nct = uni(e.nct);
-      e.kind = uni(e.kind);
-      e.fmt = uni(e.fmt);
-      MOE_LAP(0);
-      if ((int)rdy <= n_c) rdy = lds_wait<2>(p, L.ctl + kCtlReady, (uint32_t)(n_c + 1), ok);
-      MOE_LAP(1);
-      const lds_char* stage = st3 + (n_c % p.ns) * kStageBytes;
-      Raw raw;
-      const bool live = e.fmt == 0 ? fetch_chunk<0>(e, stage, raw) : fetch_chunk<FMT>(e, stage, raw);
-      lds_st32(L.ctl + kCtlDone + wave, (uint32_t)(n_c + 1));  // the stage is free for this wave
-      settle_pre(pre, e.fmt);
-      if (live) {
-        if (e.fmt == 0) compute_chunk<0>(e, raw, pre, acc);
-        else compute_chunk<FMT>(e, raw, pre, acc);
-      }
-      MOE_LAP(2);
-      if (e.kc == e.nck - 1) job_end(p, L, e, acc, jc++, own, ok);
-      MOE_LAP(3);
-      ++n_c;
-      if (++e.kc == e.nck) {
-        next_job(p, s, e.it);
-        cross_to_down(e.it);
-        MOE_LAP(4);
-        if (e.it.phase < 3) eat_job(p, L, s, e);
-        MOE_LAP(0);
-      }
-      MOE_LAP(4);
-      if (e.it.phase >= 3) break;
-      load_pre(e, pre);
-      MOE_LAP(5);
-    }
-    service(p, L, own, true, ok);  // the last owned down job
+    if (down.phase == 2) poll_flags(p, epoch + 2);
+    lds_st32(L.ctl + kCtlCrossed, 1u);
   }
-#ifdef MOE_LAPS
-  if (p.timeline && (threadIdx.x == 0 || threadIdx.x == 64 * kWaves)) {
-    if (threadIdx.x == 0)
-      for (int i = 0; i < 6; ++i) p.timeline[blockIdx.x * 16 + 10 + i] = cyc[i];
-    else
-      for (int i = 0; i < 6; ++i) p.timeline[1024 * 16 - 256 * 8 + blockIdx.x * 8 + i] = cyc[i];
-  }
-#endif
+  if (down.phase == 2) lds_wait<1>(p, L.ctl + kCtlCrossed, 1u, ok);
+  MOE_STAMP(p, 5);
+
+  run_phase<NPRE, FMT>(p, L, s, down, 3, acc, jc, own, ok);
+  service<NPRE>(p, L, own, true, ok);  // the last owned down job
   MOE_STAMP(p, 6);
   __syncthreads();
 
   // S5: combine this CU's output rows
-  combine<NPRE>(p, L, s);
+  combine(p, L, s);
   MOE_STAMP(p, 7);
   if (threadIdx.x == 0 && p.timeline) {
-    p.timeline[blockIdx.x * 16 + 8] = (uint64_t)n_c;
-    p.timeline[blockIdx.x * 16 + 9] = (uint64_t)p.ns;
+    p.timeline[blockIdx.x * 16 + 8] = (uint64_t)jc;
+    p.timeline[blockIdx.x * 16 + 9] = (uint64_t)depth<NPRE>();
   }
 }
 
 // ------------------------------------------------------------------ host glue
 
 WsLayout ws_layout(int max_rows, int E, int K, int H, int I, int Is) {
+  (void)H;
   WsLayout w;
   size_t q = 0;
   w.flags = q; q = align_up(q + 4 * 1024, 256);
@@ -1545,9 +1331,6 @@ WsLayout ws_layout(int max_rows, int E, int K, int H, int I, int Is) {
   w.scores = q; q = align_up(q + 16 * (size_t)max_rows * E, 256);
   w.mid_ld = (I > Is ? I : Is);
   w.mid = q; q = align_up(q + 2 * (size_t)max_rows * (K + 1) * w.mid_ld, 256);
-  // ncu * hs <= H + ncu - 1 and ncu <= 1024, so H + 1024 rows of products cover every CU's slice
-  w.prod = q;
-  if (max_rows > kLdsProdRows) q = align_up(q + 4 * (size_t)max_rows * (K + 1) * (H + 1024), 256);
   w.total = q;
   return w;
 }
