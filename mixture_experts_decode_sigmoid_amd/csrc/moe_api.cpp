@@ -100,9 +100,6 @@ int fill(const moe_config* c, const moe_weights* w, const uint16_t* x, int rows,
   if (d.ncu > 1024) return MOE_ERR_SHAPE;
   const int hs = hs_for(c->hidden, d.ncu);
   if (hs > kMaxSlice) return MOE_ERR_SHAPE;
-  size_t lds = lds_bytes(rows > 0 ? rows : 1, c->top_k, c->n_experts, hs);
-  if (lds > d.max_lds) return MOE_ERR_SHAPE;
-  if (lds < (size_t)kMinLds) lds = kMinLds;
   memset(&p, 0, sizeof p);
   p.H = c->hidden;
   p.I = c->inter;
@@ -119,6 +116,11 @@ int fill(const moe_config* c, const moe_weights* w, const uint16_t* x, int rows,
   p.hs = hs;
   p.ncu = d.ncu;
   p.mid_ld = L.mid_ld;
+  // the narrow stream for batches of at most 16 rows when its partials fit
+  size_t lds = rows <= 16 ? stream_geometry(p, 1) : (size_t)-1;
+  if (lds > d.max_lds) lds = stream_geometry(p, 0);
+  if (lds > d.max_lds) return MOE_ERR_SHAPE;
+  if (lds < (size_t)kMinLds) lds = kMinLds;
   p.lds_bytes = (int)lds;
   p.x = x;
   p.router_w = w->router_w;

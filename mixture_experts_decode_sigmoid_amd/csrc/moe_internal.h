@@ -35,6 +35,12 @@ struct Params {
   int ncu;         // workgroups launched (= CUs)
   int mid_ld;
   int lds_bytes;   // dynamic LDS size
+  // stream geometry (see lds_offsets): narrow = per-wave partials in LDS
+  int narrow;      // 1: batches of at most 16 rows whose partials fit in LDS
+  int nrt_p;       // 16-row down tiles of a CU's slice, rounded up to 1, 2 or 4
+  int wpt;         // waves per down tile (8 / nrt_p); they split its K-blocks
+  int pitch;       // floats per (row, slot) line of the down products (16 * tiles)
+  int tpc;         // up/gate tiles of one group a CU can hold
   // inputs
   const uint16_t* x;
   const uint16_t* router_w;
@@ -57,12 +63,13 @@ struct Params {
   uint32_t* err;
   double* scores;  // [T][E][2]: s, b
   uint16_t* mid;   // [T][K+1][mid_ld] bf16
-  uint64_t* timeline;  // optional phase stamps ([ncu][16]); NULL unless built with MOE_TIMELINE
+  uint64_t* timeline;  // optional phase stamps ([ncu][64]); NULL unless built with MOE_TIMELINE
 };
 
 WsLayout ws_layout(int max_rows, int E, int K, int H, int I, int Is);
-// LDS bytes a call needs.
-size_t lds_bytes(int T, int K, int E, int hs);
+// Fills the stream geometry of p (T, K, E, I, Is, hs, ncu set) for the
+// narrow (narrow = 1) or wide layout and returns the LDS bytes it needs.
+size_t stream_geometry(Params& p, int narrow);
 hipError_t launch(const Params& p, int mode, hipStream_t stream);
 
 }  // namespace moe

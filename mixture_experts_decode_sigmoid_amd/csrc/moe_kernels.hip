@@ -108,20 +108,44 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+// Loads through global-address-space pointers.  A generic (flat) load also
+// counts in the LDS/scalar counter, so every LDS wait would drain it too.
+template <class T>
+__device__ __forceinline__ T ldg(const void* p) {
+  return *(const __attribute__((address_space(1))) T*)p;
+}
+__device__ __forceinline__ u32x4 ld16(const void* p) { return ldg<u32x4>(p); }
 
 // Optional per-CU phase stamps (build with -DMOE_TIMELINE): thread 0 of each
 // workgroup writes s_memrealtime (100 MHz) at phase boundaries into
-// p.timeline[blockIdx.x * 16 + i].
+// p.timeline[blockIdx.x * 64 + i]; MOE_WSTAMP(p, k) has lane 0 of every wave
+// write slot 16 + 8k + wave.
 #ifdef MOE_TIMELINE
 #define MOE_STAMP(p, i)                                                                  \
   do {                                                                                   \
     if (threadIdx.x == 0 && (p).timeline)                                                \
-      (p).timeline[blockIdx.x * 16 + (i)] = __builtin_amdgcn_s_memrealtime();            \
+      (p).timeline[blockIdx.x * 64 + (i)] = __builtin_amdgcn_s_memrealtime();            \
+  } while (0)
+#define MOE_WSTAMP(p, k)                                                                 \
+  do {                                                                                   \
+    if ((threadIdx.x & 63) == 0 && (p).timeline)                                         \
+      (p).timeline[blockIdx.x * 64 + 16 + 8 * (k) + (threadIdx.x >> 6)] =                \
+          __builtin_amdgcn_s_memrealtime();                                              \
+  } while (0)
+#define MOE_JSTAMP(p, jc)                                                                \
+  do {                                                                                   \
+    if (threadIdx.x == 0 && (p).timeline && (jc) < 24)                                   \
+      (p).timeline[blockIdx.x * 64 + 40 + (jc)] = __builtin_amdgcn_s_memrealtime();     \
   } while (0)
 #else
+#define MOE_JSTAMP(p, jc) \
+  do {                    \
+  } while (0)
 #define MOE_STAMP(p, i) \
   do {                  \
+  } while (0)
+#define MOE_WSTAMP(p, k) \
+  do {                   \
   } while (0)
 #endif
 
@@ -137,13 +161,14 @@ struct Lds {
   int32_t* gcnt;     // [1+T*K]
   int32_t* gstart;   // [1+T*K]
   int32_t* cols;     // [T*(K+1)] row*16 + slot
+  int32_t* cgrp;     // [T*(K+1)] group of each column
   int32_t* misc;     // [32]: 0 = G, 1 = epoch, 8.. = scan
   uint32_t* ctl;     // [64] chunk-stream counters (see kCtl*)
   float* red;        // [red_slots][red_tiles][kWaves][64][4] job-end partials
   double* rb;        // [kWaves][E] router keys (aliases red and pbuf)
   double* rgs;       // [kWaves][64] group scores
   int32_t* rkept;    // [kWaves][64]
-  float* pbuf;       // down products: [T*(K+1)][hs], or per wave [8][T*(K+1)][pitch] (see down_direct)
+  float* pbuf;       // wide: down products [T*(K+1)][hs]; narrow: the per-wave partials (see lds_offsets)
 };
 
 __host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -154,18 +179,26 @@ __host__ __device__ inline int red_tiles(int T) { return T > 16 ? kMaxRows / 16 
 __host__ __device__ inline int red_slots(int T) { return T > 16 ? 2 : 4; }
 constexpr size_t kRedTileBytes = 16 * (size_t)kWaves * 64;  // one tile: [wave][lane] f32x4
 
-// Batches of at most 8 rows keep every wave's down partials apart in LDS,
-// P[w][row][slot][h] with rows of the slice padded to whole 16-row tiles,
-// and the combine sums them over the waves; larger batches reduce each down
-// tile at its job end like the up/gate tiles.
-__host__ __device__ inline bool down_direct(int T) { return T <= 8; }
-__host__ __device__ inline int prod_pitch(int hs) { return (hs + 15) / 16 * 16; }
-
+// Narrow layout (batches of at most 16 rows): no reduction runs inside the
+// weight stream.  Every wave keeps its partial tiles apart in LDS and they
+// are summed over the waves, in wave order, after the phase:
+//   up/gate  Pu[w][col * tpc + t][16]  (w = 0..7; col = the group's column
+//            index in the column table, t = the tile's index among the CU's
+//            tiles of that group; 16 rows: 8 gate then 8 up)
+//   down     Pd[kp][row][slot][pitch]  (kp = 0..wpt-1, the K-phase of the
+//            waves that share a 16-row down tile; h along the slice)
+// Pu and Pd share one region (Pu is consumed before Pd is written), which
+// also holds the routing scratch before the stream.  The wide layout keeps
+// job-end partial slots summed by an owner wave, and one copy of the down
+// products [row][slot][hs].
 struct LdsOffsets {
-  size_t ids, w, first, egrp, rmask, gexp, gcnt, gstart, cols, misc, ctl, red, pbuf, total;
+  size_t ids, w, first, egrp, rmask, gexp, gcnt, gstart, cols, cgrp, misc, ctl, red, pbuf, total;
 };
 
-__host__ __device__ inline LdsOffsets lds_offsets(int T, int K, int E, int hs) {
+__host__ __device__ inline size_t pu_floats(int T, int K, int tpc) { return (size_t)kWaves * T * (K + 1) * tpc * 16; }
+
+__host__ __device__ inline LdsOffsets lds_offsets(int T, int K, int E, int hs, int narrow, int tpc, int wpt,
+                                                  int pitch) {
   LdsOffsets o;
   size_t q = 0;
   const int uses = T * K, gmax = 1 + T * K;
@@ -178,25 +211,42 @@ __host__ __device__ inline LdsOffsets lds_offsets(int T, int K, int E, int hs) {
   o.gcnt = q; q = align_up(q + 4 * (size_t)gmax, 16);
   o.gstart = q; q = align_up(q + 4 * (size_t)gmax, 16);
   o.cols = q; q = align_up(q + 4 * (size_t)T * (K + 1), 16);
+  o.cgrp = q; q = align_up(q + 4 * (size_t)T * (K + 1), 16);
   o.misc = q; q = align_up(q + 4 * 32, 16);
   o.ctl = q; q = align_up(q + 4 * 64, 16);
   // the routing scratch (used before the stream) overlaps the job-end
   // partials and the down products (used in it)
   o.red = q;
-  const size_t rd = (size_t)red_slots(T) * red_tiles(T) * kRedTileBytes;
-  o.pbuf = q + rd;
-  const size_t pb = down_direct(T) ? 4 * (size_t)kWaves * T * (K + 1) * prod_pitch(hs)
-                                   : 4 * (size_t)T * (K + 1) * hs;
   const size_t rs = 8 * (size_t)kWaves * E + 8 * (size_t)kWaves * 64 + 4 * (size_t)kWaves * 64;
-  q = align_up(q + (rd + pb > rs ? rd + pb : rs), 16);
+  size_t need;
+  if (narrow) {
+    o.pbuf = q;
+    const size_t pu = 4 * pu_floats(T, K, tpc);
+    const size_t pd = 4 * (size_t)wpt * T * (K + 1) * pitch;
+    need = pu > pd ? pu : pd;
+  } else {
+    const size_t rd = (size_t)red_slots(T) * red_tiles(T) * kRedTileBytes;
+    o.pbuf = q + rd;
+    need = rd + 4 * (size_t)T * (K + 1) * hs;
+  }
+  q = align_up(q + (need > rs ? need : rs), 16);
   o.total = q;
   return o;
 }
 
-size_t lds_bytes(int T, int K, int E, int hs) { return lds_offsets(T, K, E, hs).total; }
+size_t stream_geometry(Params& p, int narrow) {
+  const int nrt = (p.hs + 15) / 16;
+  p.nrt_p = nrt <= 1 ? 1 : nrt <= 2 ? 2 : 4;
+  p.wpt = kWaves / p.nrt_p;
+  p.pitch = 16 * nrt;
+  const int tiles = (p.I > p.Is ? p.I : p.Is) / 8;
+  p.tpc = (tiles + p.ncu - 1) / p.ncu;
+  p.narrow = narrow;
+  return lds_offsets(p.T, p.K, p.E, p.hs, p.narrow, p.tpc, p.wpt, p.pitch).total;
+}
 
 __device__ inline Lds lds_map(char* base, const Params& p) {
-  LdsOffsets o = lds_offsets(p.T, p.K, p.E, p.hs);
+  LdsOffsets o = lds_offsets(p.T, p.K, p.E, p.hs, p.narrow, p.tpc, p.wpt, p.pitch);
   Lds L;
   L.ids = (int32_t*)(base + o.ids);
   L.w = (float*)(base + o.w);
@@ -207,6 +257,7 @@ __device__ inline Lds lds_map(char* base, const Params& p) {
   L.gcnt = (int32_t*)(base + o.gcnt);
   L.gstart = (int32_t*)(base + o.gstart);
   L.cols = (int32_t*)(base + o.cols);
+  L.cgrp = (int32_t*)(base + o.cgrp);
   L.misc = (int32_t*)(base + o.misc);
   L.ctl = (uint32_t*)(base + o.ctl);
   L.red = (float*)(base + o.red);
@@ -364,6 +415,7 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r) {
     for (int i = 0; i < 4; ++i)
       if (alive[i]) alive[i] = L.rkept[wave * 64 + (lane + 64 * i) / gsz] != 0;
   }
+  MOE_STAMP(p, 14);
   double ssum = 0.0;
   int picks[kMaxTopK];
   double pick_s[kMaxTopK];
@@ -396,6 +448,7 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r) {
       ssum += sp;
     }
   }
+  MOE_STAMP(p, 15);
   if (lane == 0) {
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k) {
@@ -467,7 +520,10 @@ __device__ inline void build_groups(const Params& p, const Lds& L) {
   }
   __syncthreads();
   if (p.n_shared)
-    for (int r = tid; r < p.T; r += kThreads) L.cols[r] = r * 16 + p.K;
+    for (int r = tid; r < p.T; r += kThreads) {
+      L.cols[r] = r * 16 + p.K;
+      L.cgrp[r] = 0;
+    }
   for (int u = tid; u < U; u += kThreads) {
     const int e = L.ids[u], r = u / p.K, slot = u - r * p.K;
     const uint32_t lo = L.rmask[2 * e], hi = L.rmask[2 * e + 1];
@@ -475,6 +531,7 @@ __device__ inline void build_groups(const Params& p, const Lds& L) {
                               : __popc(lo) + __popc(hi & ((1u << (r - 32)) - 1u));
     const int g = L.egrp[e];
     L.cols[L.gstart[g] + rank] = r * 16 + slot;
+    L.cgrp[L.gstart[g] + rank] = g;
   }
   __syncthreads();
 }
@@ -539,6 +596,7 @@ __device__ __forceinline__ void lds_st128(void* p, u32x4 v) {
 
 // Stream counters in LDS.  Every counter counts up from 0 within a launch
 // and is written by one wave only.
+constexpr int kCtlProg = 0;    // [8]  jobs wave w has ended
 constexpr int kCtlPart = 16;   // [8]  jobs whose partials wave w has stored
 constexpr int kCtlSlot = 24;   // [4]  1 + the last job summed out of partial slot s
 constexpr int kCtlMidOut = 40; // [8]  1 once wave w's mid stores are complete
@@ -601,7 +659,8 @@ struct Sched {
   int G;         // groups, known after routing
   int h0, hc;    // this CU's down rows
   int nrt;       // 16-row tiles of them
-  int routed;
+  int nrt_p, wpt;  // tiles rounded up to 1, 2 or 4; waves per tile
+  int narrow;    // each wave walks only its own down tile's jobs
 };
 
 // Position in this CU's job sequence.
@@ -646,12 +705,12 @@ __device__ inline void settle(const Params& p, const Sched& s, It& c) {
       if (c.j < s.n_jobs) return;
       c.phase = 2;
       c.j = 0;
-      c.rt = 0;
+      c.rt = s.narrow ? wave_id() % s.nrt_p : 0;
       c.tile = 0;
       continue;
     }
     c.g = c.j;
-    if (c.phase == 2 && (s.nrt <= 0 || c.j >= s.G)) c.phase = 3;
+    if (c.phase == 2 && (c.rt >= s.nrt || c.j >= s.G)) c.phase = 3;
     return;
   }
 }
@@ -666,6 +725,8 @@ __device__ inline void next_job(const Params& p, const Sched& s, It& c) {
       c.tile -= s.rt_tiles;
       ++c.g;
     }
+  } else if (s.narrow) {
+    ++c.j;
   } else if (++c.rt >= s.nrt) {
     c.rt = 0;
     ++c.j;
@@ -679,10 +740,27 @@ __device__ __forceinline__ int job_kdim(const Params& p, const It& c) {
   const int H = uni(p.H), I = uni(p.I), Is = uni(p.Is);
   return c.phase <= 1 ? H : (shared_group(p, c.g) ? Is : I);
 }
-// This wave's items in a job of reduction length kdim: K-blocks w + 8i.
-__device__ __forceinline__ int items_of(int kdim, int w) {
-  const int nkb = kdim >> 7;
-  return nkb > w ? (nkb - 1 - w) / 8 + 1 : 0;
+// This wave's K-blocks of a job: k0 + step*i, i < n.  Up/gate jobs split
+// their K-blocks over all 8 waves (k0 = w, step 8).  A down tile belongs to
+// the wpt waves w with w % nrt_p == tile, which split its K-blocks
+// (k0 = w / nrt_p, step wpt); the other waves have no items in it.
+struct KRange {
+  int k0, step, n;
+};
+__device__ __forceinline__ KRange job_krange(const Params& p, const Sched& s, const It& c) {
+  const int w = wave_id(), nkb = job_kdim(p, c) >> 7;
+  KRange r;
+  if (c.phase <= 1) {
+    r.k0 = w;
+    r.step = kWaves;
+  } else {
+    r.k0 = w % s.nrt_p == c.rt ? w / s.nrt_p : nkb;
+    r.step = s.wpt;
+  }
+  r.n = uni(nkb > r.k0 ? (nkb - 1 - r.k0) / r.step + 1 : 0);
+  r.k0 = uni(r.k0);
+  r.step = uni(r.step);
+  return r;
 }
 __device__ __forceinline__ int job_nlive(const Sched& s, const It& c) {
   return c.phase == 2 ? (s.hc - 16 * c.rt < 16 ? s.hc - 16 * c.rt : 16) : 16;
@@ -745,6 +823,7 @@ struct Fetch {
   It it;
   int i, n;           // next item of the job, this wave's items in it
   int fmt, live;      // live = 0 past the end of the phase (dummy items)
+  int k0, step;       // K-blocks of the job's items: k0 + step*i
   int g, eid;         // group of the last job set up, and its expert
   const uint8_t* wrow;  // this lane's weight row at K offset 0
   const uint8_t* srow;  // this lane's scale row (see Item::s)
@@ -774,7 +853,10 @@ __device__ inline void fetch_job(const Params& p, const Lds& L, const Sched& s, 
   }
   const int eid = f.eid;
   f.fmt = sh ? 0 : uni(p.routed_fmt);
-  f.n = items_of(kdim, wave_id());
+  const KRange kr = job_krange(p, s, c);
+  f.n = kr.n;
+  f.k0 = kr.k0;
+  f.step = kr.step;
   f.i = 0;
   const int wr = down ? hb + (row < nlive ? row : nlive - 1) : (row < 8 ? 8 * c.tile + row : iexp + 8 * c.tile + row - 8);
   const size_t H = p.H, I = p.I, e = (size_t)eid;
@@ -812,14 +894,14 @@ __device__ inline void fetch_job(const Params& p, const Lds& L, const Sched& s, 
 template <int NPRE>
 __device__ __forceinline__ void fetch_item(const Params& p, const Fetch<NPRE>& f, Item<NPRE>& it) {
   const int lane = threadIdx.x & 63, lg = lane >> 4;
-  const int kb = f.live ? wave_id() + 8 * f.i : 0;
+  const int kb = f.live ? f.k0 + f.step * f.i : 0;
   const int kbytes = f.fmt ? 64 : 128, lbytes = f.fmt ? 16 : 32;
   const uint8_t* wp = f.live ? f.wrow + kb * kbytes + lg * lbytes : (const uint8_t*)p.x;
   const uint8_t* sp = f.live ? f.srow + 4 * kb : (const uint8_t*)p.x;
   const uint16_t* ab = f.live ? f.abase : arg_ptr(p.x);
   it.w0 = ld16(wp);
   it.w1 = ld16(wp + (f.fmt ? 0 : 16));
-  it.s = *(const uint32_t*)sp;
+  it.s = ldg<uint32_t>(sp);
 #pragma unroll
   for (int ct = 0; ct < NPRE; ++ct) {
     const uint16_t* a = ab + (f.live ? f.act[ct] + kb * 128 : 0);
@@ -875,9 +957,9 @@ struct Eat {
   int g;        // group of the job
   int fmt, tile, rt, ncols, nct, nlive;
   int split;    // FP8: MFMA output rows (4*lg + q) below it take the first block scale
+  int k0, step; // K-blocks of the items
   const uint16_t* abase;
   uint32_t act[max_tiles<NPRE>()];  // this lane's column per tile (tiles >= NPRE are loaded when used)
-  uint32_t pidx[max_tiles<NPRE>()]; // its down products' offset (per-wave layout, see down_direct)
 };
 
 template <int NPRE>
@@ -889,7 +971,10 @@ __device__ inline void eat_job(const Params& p, const Lds& L, const Sched& s, Ea
   e.tile = c.phase <= 1 ? c.tile : 0;
   e.rt = c.phase == 2 ? c.rt : 0;
   e.nlive = job_nlive(s, c);
-  e.n = items_of(job_kdim(p, c), wave_id());
+  const KRange kr = job_krange(p, s, c);
+  e.n = kr.n;
+  e.k0 = kr.k0;
+  e.step = kr.step;
   e.i = 0;
   if (e.kind == 1) {
     e.split = 8;  // rows 0..7 of the MFMA tile are gate rows, 8..15 up rows
@@ -907,11 +992,7 @@ __device__ inline void eat_job(const Params& p, const Lds& L, const Sched& s, Ea
   e.nct = (e.ncols + 15) >> 4;
   e.abase = e.kind == 1 ? arg_ptr(p.x) : arg_ptr(p.mid);
 #pragma unroll
-  for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) {
-    e.act[ct] = act_offset(p, e.kind, code[ct], lg);
-    e.pidx[ct] = ((uint32_t)(code[ct] >> 4) * (uint32_t)(p.K + 1) + (uint32_t)(code[ct] & 15)) *
-                 (uint32_t)prod_pitch(p.hs);
-  }
+  for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) e.act[ct] = act_offset(p, e.kind, code[ct], lg);
 }
 
 // Multiplies one item into acc[ct].  FP8: a 4-MFMA block sum, then times the
@@ -920,7 +1001,7 @@ __device__ inline void eat_job(const Params& p, const Lds& L, const Sched& s, Ea
 template <int F, int NPRE>
 __device__ inline void eat_item(const Eat<NPRE>& e, const Item<NPRE>& it, f32x4* acc) {
   const int lg = (threadIdx.x & 63) >> 4;
-  const int kb = wave_id() + 8 * e.i;
+  const int kb = e.k0 + e.step * e.i;
   bf16x8 A[4];
   float s_lo = 1.f, s_hi = 1.f;
   if (F == 0) {
@@ -959,6 +1040,9 @@ __device__ inline void eat_item(const Eat<NPRE>& e, const Item<NPRE>& it, f32x4*
     }
   }
 }
+
+// mid = silu(gate) * up in fp32 (one expression for both layouts).
+__device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 // Job-end reductions.  At the end of a job every wave stores its partial
 // tiles into partial slot (job % slots) and raises its part count; it never
@@ -1026,7 +1110,7 @@ __device__ inline void sum_job(const Params& p, const Lds& L, const Owned& o) {
           for (int q = 0; q < 4; ++q) {
             const float g = gs[q], u = us[q];
             if (col < o.ncols) {
-              const float m = g / (1.0f + expf(-g)) * u;
+              const float m = swiglu(g, u);
               if (!isfinite(m)) set_err(p.err, kErrMid);
               const int i = 4 * (lane >> 4) + q;
               p.mid[((size_t)(code >> 4) * (p.K + 1) + (code & 15)) * p.mid_ld + 8 * o.tile + i] =
@@ -1075,17 +1159,6 @@ template <int NPRE>
 __device__ inline void job_end(const Params& p, const Lds& L, const Eat<NPRE>& e, f32x4* acc, int jc, Owned& own,
                                bool& ok) {
   const int lane = threadIdx.x & 63, wave = wave_id();
-  if (NPRE == 1 && e.kind == 2 && down_direct(p.T)) {
-    // this wave's partial of the tile into its own products; the combine sums the waves
-    float* P = L.pbuf + (size_t)wave * p.T * (p.K + 1) * prod_pitch(p.hs);
-#pragma unroll
-    for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) {
-      if (ct < e.nct)
-        lds_st128(P + e.pidx[ct] + 16 * e.rt + 4 * (lane >> 4), __builtin_bit_cast(u32x4, acc[ct]));
-      acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    return;
-  }
   const int ns = red_slots(p.T);
   if (jc >= ns) {
     const uint32_t target = (uint32_t)(jc - ns + 1);
@@ -1124,6 +1197,18 @@ __device__ inline void job_end(const Params& p, const Lds& L, const Eat<NPRE>& e
   for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
+// The two waves of a SIMD (w and w ^ 4) have the same work, but the issue
+// arbiter favours the older one, which would then finish its phase early and
+// leave the newer one streaming alone.  At every job end the wave that is
+// ahead of its partner lowers its priority.
+__device__ __forceinline__ void balance(const Lds& L, int jc) {
+  const int wave = wave_id();
+  lds_st32(L.ctl + kCtlProg + wave, (uint32_t)jc);
+  const int other = (int)lds_min<1>(L.ctl + kCtlProg + (wave ^ 4));
+  if (jc > other) __builtin_amdgcn_s_setprio(0);
+  else __builtin_amdgcn_s_setprio(2);
+}
+
 // Moves the multiplying side on after an item; at the end of a job (and for
 // every following job this wave has no items in) runs the job end.  Returns
 // false once the phase is done.
@@ -1134,6 +1219,8 @@ __device__ inline bool eat_next(const Params& p, const Lds& L, const Sched& s, E
   e.n = uni(e.n);
   while (e.i >= e.n) {
     job_end<NPRE>(p, L, e, acc, jc++, own, ok);
+    MOE_JSTAMP(p, jc - 1);
+    balance(L, jc);
     next_job(p, s, e.it);
     uni(e.it);
     if (e.it.phase >= stop) return false;
@@ -1170,32 +1257,314 @@ __device__ __forceinline__ void run_phase(const Params& p, const Lds& L, const S
     if (e.it.phase >= stop) more = false;
     else eat_job(p, L, s, e);
   }
-  while (more) {
+  // The loop is left by a jump, so that every path into an item's wait has
+  // issued the same loads since that item's (a guarded body would let the
+  // compiler's wait counting assume skipped refills and wait for more).
+  if (more) {
+    for (;;) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-      if (more) {
+      for (int d = 0; d < D; ++d) {
         if (e.fmt == 0) eat_item<0>(e, ring[d], acc);
         else eat_item<FMT>(e, ring[d], acc);
         fetch_item(p, f, ring[d]);
         fetch_next(p, L, s, f, stop);
-        more = eat_next(p, L, s, e, acc, jc, own, ok, stop);
+        if (!eat_next(p, L, s, e, acc, jc, own, ok, stop)) goto drained;
       }
     }
   }
+drained:
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the dead items' loads
+  __builtin_amdgcn_s_setprio(0);
+}
+
+// ------------------------------------------------------------------ narrow stream
+//
+// Batches of at most 16 rows (one 16-column MFMA tile per group).  A wave's
+// items run through a D-deep register ring: each step multiplies the oldest
+// item, refills its slot with the item D later and counts; only a job
+// change on either side does more.  At a job end the wave stores its
+// partial tile into its own part of LDS and never waits for another wave.
+
+// The fetch side: byte offsets of this lane's next item from uniform bases.
+struct FetchN {
+  It it;
+  int left;                      // items left in the job (large once past the phase)
+  const uint8_t* wb;             // weights
+  const uint8_t* sb;             // block scales
+  const uint8_t* ab;             // activations: x or mid
+  uint32_t wo, so, ao;           // this lane's offsets of the next item
+  uint32_t winc, sinc, ainc;     // per item
+  uint32_t w1o;                  // second weight load: +16 (FP8) or +0 (MXFP4)
+};
+
+struct ItemN {
+  u32x4 w0, w1, B[4];
+  uint32_t s;
+};
+
+// The job's weight, scale and activation offsets for this lane; its first
+// item is K-block kr.k0.
+__device__ inline void fetch_setup_n(const Params& p, const Lds& L, const Sched& s, FetchN& f, const KRange& kr) {
+  const int lane = threadIdx.x & 63, lg = lane >> 4, row = lane & 15;
+  const It& c = f.it;
+  const bool down = c.phase == 2, sh = shared_group(p, c.g);
+  const int kdim = job_kdim(p, c), nlive = job_nlive(s, c);
+  int ncols, eid, code[1];
+  group_cols<1>(p, L, c.g, ncols, eid, code);
+  f.left = kr.n;
+  f.ab = (const uint8_t*)(down ? arg_ptr(p.mid) : arg_ptr(p.x));
+  f.ao = 2 * act_offset(p, down ? 2 : 1, code[0], lg) + 256u * (uint32_t)kr.k0;
+  f.ainc = 256u * (uint32_t)kr.step;
+  const int iexp = sh ? uni(p.Is) : uni(p.I);
+  const int hb = s.h0 + 16 * c.rt;
+  const int wr = down ? hb + (row < nlive ? row : nlive - 1) : (row < 8 ? 8 * c.tile + row : iexp + 8 * c.tile + row - 8);
+  const size_t H = uni(p.H), I = uni(p.I), e = (size_t)eid;
+  const int fmt = sh ? 0 : uni(p.routed_fmt);
+  if (fmt == 0) {
+    // FP8 weights [rows][kdim] bytes; fp32 scales [rows/128][kdim/128]
+    const uint8_t* w;
+    const float* S;
+    if (sh) {
+      w = down ? arg_ptr(p.sh_wd) : arg_ptr(p.sh_wgu);
+      S = down ? arg_ptr(p.sh_sd) : arg_ptr(p.sh_sgu);
+    } else {
+      w = down ? arg_ptr(p.wd) + e * H * I : arg_ptr(p.wgu) + e * 2 * I * H;
+      S = down ? (const float*)arg_ptr(p.sd) + e * (H / 128) * (I / 128)
+               : (const float*)arg_ptr(p.sgu) + e * (2 * I / 128) * (H / 128);
+    }
+    const int nkb = kdim / 128;
+    const int nb_lo = down ? hb / 128 : (8 * c.tile) / 128;
+    const int nb_hi = down ? (hb + nlive - 1) / 128 : (iexp + 8 * c.tile) / 128;
+    f.wb = w;
+    f.wo = (uint32_t)wr * (uint32_t)kdim + 128u * (uint32_t)kr.k0 + 32u * (uint32_t)lg;
+    f.winc = 128u * (uint32_t)kr.step;
+    f.w1o = 16;
+    f.sb = (const uint8_t*)S;
+    f.so = 4u * ((uint32_t)(lane < 32 ? nb_lo : nb_hi) * (uint32_t)nkb + (uint32_t)kr.k0);
+  } else {
+    // MXFP4 weights [rows][kdim/2] bytes; E8M0 scales [rows][kdim/32]
+    f.wb = down ? arg_ptr(p.wd) + e * H * (I / 2) : arg_ptr(p.wgu) + e * 2 * I * (H / 2);
+    f.sb = down ? (const uint8_t*)arg_ptr(p.sd) + e * H * (I / 32) : (const uint8_t*)arg_ptr(p.sgu) + e * 2 * I * (H / 32);
+    f.wo = (uint32_t)wr * (uint32_t)(kdim / 2) + 64u * (uint32_t)kr.k0 + 16u * (uint32_t)lg;
+    f.winc = 64u * (uint32_t)kr.step;
+    f.w1o = 0;
+    f.so = (uint32_t)wr * (uint32_t)(kdim / 32) + 4u * (uint32_t)kr.k0;
+  }
+  f.sinc = 4u * (uint32_t)kr.step;
+}
+
+// Past the phase: items load 16 bytes of x and are never multiplied.
+__device__ inline void fetch_dead_n(const Params& p, FetchN& f) {
+  f.left = 1 << 30;
+  f.wb = f.sb = f.ab = (const uint8_t*)arg_ptr(p.x);
+  f.wo = f.so = f.ao = 0;
+  f.winc = f.sinc = f.ainc = 0;
+  f.w1o = 0;
+}
+
+// Moves the fetch side to the next job (from f.it, which is `first` or the
+// job just finished) in which this wave has items.
+__device__ inline void fetch_next_n(const Params& p, const Lds& L, const Sched& s, FetchN& f, int stop, bool first) {
+  if (!first) {
+    next_job(p, s, f.it);
+    uni(f.it);
+  }
+  for (;;) {
+    if (f.it.phase >= stop) {
+      fetch_dead_n(p, f);
+      return;
+    }
+    const KRange kr = job_krange(p, s, f.it);
+    if (kr.n > 0) {
+      fetch_setup_n(p, L, s, f, kr);
+      return;
+    }
+    next_job(p, s, f.it);
+    uni(f.it);
+  }
+}
+
+__device__ __forceinline__ void fetch_item_n(const FetchN& f, ItemN& it) {
+  const uint8_t* w = f.wb + f.wo;
+  it.w0 = ldg<u32x4>(w);
+  it.w1 = ldg<u32x4>(w + f.w1o);
+  it.s = ldg<uint32_t>(f.sb + f.so);
+  const uint8_t* a = f.ab + f.ao;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) it.B[m] = ldg<u32x4>(a + 16 * m);
+}
+
+__device__ __forceinline__ void fetch_adv_n(FetchN& f) {
+  f.wo += f.winc;
+  f.so += f.sinc;
+  f.ao += f.ainc;
+  f.left = uni(f.left) - 1;
+}
+
+// The multiplying side.
+struct EatN {
+  It it;
+  int left;        // items left in the job
+  int fmt;         // 0 FP8, 1 MXFP4
+  int split;       // FP8: MFMA output rows (4*lg + q) below it take the first block scale
+  uint32_t pidx;   // this lane's partial (floats from L.pbuf); only stored when pst
+  bool pst;        // this lane's column is one of the group's
+};
+
+__device__ inline void eat_setup_n(const Params& p, const Lds& L, const Sched& s, EatN& e, const KRange& kr) {
+  const int lane = threadIdx.x & 63, lg = lane >> 4, wave = wave_id();
+  const It& c = e.it;
+  const bool sh = shared_group(p, c.g);
+  int ncols, eid, code[1], gstart = 0;
+  group_cols<1>(p, L, c.g, ncols, eid, code);
+  if (!sh) gstart = lds_ldi_uniform(L.gstart + c.g);
+  e.left = kr.n;
+  e.fmt = sh ? 0 : uni(p.routed_fmt);
+  e.pst = (lane & 15) < ncols;
+  const int col = lane & 15;
+  if (c.phase <= 1) {
+    e.split = 8;  // rows 0..7 of the tile are gate rows, 8..15 up rows
+    const uint32_t slot = (uint32_t)(gstart + col) * (uint32_t)p.tpc + (uint32_t)(c.tile / p.ncu);
+    e.pidx = ((uint32_t)wave * (uint32_t)(p.T * (p.K + 1) * p.tpc) + slot) * 16u + 4u * (uint32_t)lg;
+  } else {
+    const int hb = s.h0 + 16 * c.rt;
+    e.split = (hb / 128 + 1) * 128 - hb;  // a 16-row tile spans at most two scale blocks
+    e.pidx = (((uint32_t)kr.k0 * (uint32_t)p.T + (uint32_t)(code[0] >> 4)) * (uint32_t)(p.K + 1) +
+              (uint32_t)(code[0] & 15)) * (uint32_t)p.pitch +
+             16u * (uint32_t)c.rt + 4u * (uint32_t)lg;
+  }
+}
+
+// Moves the multiplying side to its next job with items; false at the end
+// of the phase.
+__device__ inline bool eat_next_n(const Params& p, const Lds& L, const Sched& s, EatN& e, int stop, bool first) {
+  if (!first) {
+    next_job(p, s, e.it);
+    uni(e.it);
+  }
+  for (;;) {
+    if (e.it.phase >= stop) return false;
+    const KRange kr = job_krange(p, s, e.it);
+    if (kr.n > 0) {
+      eat_setup_n(p, L, s, e, kr);
+      return true;
+    }
+    next_job(p, s, e.it);
+    uni(e.it);
+  }
+}
+
+template <int F>
+__device__ __forceinline__ void eat_item_n(const EatN& e, const ItemN& it, f32x4& acc) {
+  const int lg = (threadIdx.x & 63) >> 4;
+  bf16x8 A[4];
+  if (F == 0) {
+    A[0] = e4m3x8_to_bf16(it.w0[0], it.w0[1]);
+    A[1] = e4m3x8_to_bf16(it.w0[2], it.w0[3]);
+    A[2] = e4m3x8_to_bf16(it.w1[0], it.w1[1]);
+    A[3] = e4m3x8_to_bf16(it.w1[2], it.w1[3]);
+    const float s_lo = __int_as_float(__builtin_amdgcn_readlane((int)it.s, 0));
+    const float s_hi = __int_as_float(__builtin_amdgcn_readlane((int)it.s, 32));
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) t = mfma16(A[m], __builtin_bit_cast(bf16x8, it.B[m]), t);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = fmaf(t[q], 4 * lg + q < e.split ? s_lo : s_hi, acc[q]);
+  } else {
+    const float sc = e8m0_to_f32((it.s >> (8 * lg)) & 0xffu);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) A[m] = e2m1x8_to_bf16(it.w0[m], sc);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc = mfma16(A[m], __builtin_bit_cast(bf16x8, it.B[m]), acc);
+  }
+}
+
+// One phase of the narrow stream.  Partials go to LDS, which must be zero
+// where this wave has no items.
+template <int FMT>
+__device__ __forceinline__ void run_narrow(const Params& p, const Lds& L, const Sched& s, It start, int stop) {
+  constexpr int D = 5;
+  if (start.phase >= stop) return;
+  FetchN f;
+  f.it = start;
+  fetch_next_n(p, L, s, f, stop, true);
+  ItemN ring[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    fetch_item_n(f, ring[d]);
+    fetch_adv_n(f);
+    if (f.left == 0) fetch_next_n(p, L, s, f, stop, false);
+  }
+  EatN e;
+  e.it = start;
+  if (eat_next_n(p, L, s, e, stop, true)) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // Left only by the jump below, so that every path into an item's wait
+    // has issued the same loads since that item's.
+    for (;;) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        if (FMT == 0 || e.fmt == 0) eat_item_n<0>(e, ring[d], acc);
+        else eat_item_n<1>(e, ring[d], acc);
+        fetch_item_n(f, ring[d]);
+        fetch_adv_n(f);
+        if (f.left == 0) fetch_next_n(p, L, s, f, stop, false);
+        e.left = uni(e.left) - 1;
+        if (e.left == 0) {
+          if (e.pst) lds_st128(L.pbuf + e.pidx, __builtin_bit_cast(u32x4, acc));
+          acc = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (!eat_next_n(p, L, s, e, stop, false)) goto drained;
+        }
+      }
+    }
+  }
+drained:
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the dead items' loads
 }
 
-// out[r][h] = P_shared + sum_p w[r][p] * P[r][p], fp32 FMA chain in slot
-// order, rounded to bf16 once.
-// With per-wave down products, each product is first summed over the waves
-// in order 0..7 (the same sum a job-end reduction forms).
-__device__ __forceinline__ float down_product(const Params& p, const Lds& L, int r, int slot, int hl) {
-  if (!down_direct(p.T)) return L.pbuf[((size_t)r * (p.K + 1) + slot) * p.hs + hl];
-  const size_t wstride = (size_t)p.T * (p.K + 1) * prod_pitch(p.hs);
-  const float* q = L.pbuf + ((size_t)r * (p.K + 1) + slot) * prod_pitch(p.hs) + hl;
-  float v = 0.f;
+// Zeroes the narrow partial region (n floats).
+__device__ inline void zero_partials(const Lds& L, size_t n) {
+  for (size_t i = 4 * (size_t)threadIdx.x; i < n; i += 4 * kThreads) *(u32x4*)(L.pbuf + i) = u32x4{0u, 0u, 0u, 0u};
+}
+
+// After the narrow up/gate phase: every (column, intermediate) of this CU's
+// tiles is summed over the 8 waves in order, gate and up, and its SwiGLU
+// value goes to mid as bf16.  Whole workgroup.
+__device__ inline void up_reduce_n(const Params& p, const Lds& L, const Sched& s) {
+  const int ncol = p.T * (p.K + p.n_shared);
+  const int nslot = ncol * p.tpc;
+  const size_t wstride = (size_t)p.T * (p.K + 1) * p.tpc * 16;
+  for (int q = threadIdx.x; q < nslot * 8; q += kThreads) {
+    const int slot = q >> 3, i = q & 7;
+    const int ci = slot / p.tpc, tl = slot - ci * p.tpc;
+    const int g = L.cgrp[ci];
+    const bool sh = shared_group(p, g);
+    const int base = sh ? 0 : s.sh_tiles + (g - p.n_shared) * s.rt_tiles;
+    const int tiles = sh ? s.sh_tiles : s.rt_tiles;
+    const int t = (((int)blockIdx.x - base) % p.ncu + p.ncu) % p.ncu + tl * p.ncu;
+    if (t >= tiles) continue;
+    const float* pu = L.pbuf + (size_t)slot * 16;
+    float gs = 0.f, us = 0.f;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) v += q[w * wstride];
+    for (int w = 0; w < kWaves; ++w) gs += pu[w * wstride + i];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) us += pu[w * wstride + 8 + i];
+    const float m = swiglu(gs, us);
+    if (!isfinite(m)) set_err(p.err, kErrMid);
+    const int code = L.cols[ci];
+    p.mid[((size_t)(code >> 4) * (p.K + 1) + (code & 15)) * p.mid_ld + 8 * t + i] = (uint16_t)f32_to_bf16_rne(m);
+  }
+}
+
+// out[r][h] = P_shared + sum_p w[r][p] * P[r][p], fp32 FMA chain in slot
+// order, rounded to bf16 once.  Narrow: each product is first summed over
+// the K-phases of its tile in order (the sum a wide job-end reduction forms).
+__device__ __forceinline__ float down_product(const Params& p, const Lds& L, int r, int slot, int hl) {
+  if (!p.narrow) return L.pbuf[((size_t)r * (p.K + 1) + slot) * p.hs + hl];
+  const size_t kstride = (size_t)p.T * (p.K + 1) * p.pitch;
+  const float* q = L.pbuf + ((size_t)r * (p.K + 1) + slot) * p.pitch + hl;
+  float v = 0.f;
+  for (int kp = 0; kp < p.wpt; ++kp) v += q[kp * kstride];
   if (!isfinite(v)) set_err(p.err, kErrMid);
   return v;
 }
@@ -1211,8 +1580,11 @@ __device__ inline void combine(const Params& p, const Lds& L, const Sched& s) {
 
 // ------------------------------------------------------------------ kernel
 
-template <int MODE, int FMT, int NPRE>
+// NARROW = 1: the narrow stream (per-wave partials); 0: the wide stream
+// (up to four 16-column tiles per group, owner reductions).
+template <int MODE, int FMT, int NARROW>
 __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
+  constexpr int NPRE = NARROW ? 1 : 2;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const Lds L = lds_map(smem, p);
   const int tid = threadIdx.x, wave = wave_id();
@@ -1235,6 +1607,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   MOE_STAMP(p, 2);
   for (int r = wave; r < p.T; r += kWaves) route_row(p, L, r);
   __syncthreads();
+  MOE_STAMP(p, 10);
   if (MODE == kModeRoute) {
     for (int u = tid; u < p.T * p.K; u += kThreads) {
       p.ids_out[u] = L.ids[u];
@@ -1266,15 +1639,43 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   s.rt_tiles = p.I / 8;
   s.G = G;
   s.n_jobs = s.sh_tiles + (G - p.n_shared) * s.rt_tiles;
-  s.routed = 1;
   s.h0 = blockIdx.x * p.hs;
   s.hc = uni(p.H) - s.h0 < uni(p.hs) ? uni(p.H) - s.h0 : uni(p.hs);
   if (s.hc < 0) s.hc = 0;
   s.nrt = (s.hc + 15) / 16;
+  s.nrt_p = uni(p.nrt_p);
+  s.wpt = uni(p.wpt);
+  s.narrow = NARROW;
 
   // S3 / S4: the weight stream.  The second flag (every CU's mid is out) is
   // raised after this CU's up/gate jobs and awaited before any down
   // activation is loaded.
+  if (NARROW) {
+    zero_partials(L, pu_floats(p.T, p.K, p.tpc));
+    __syncthreads();
+    It up = It{0, first_job(p, 0), 0, 0, 0};
+    settle(p, s, up);
+    run_narrow<FMT>(p, L, s, up, 2);
+    MOE_WSTAMP(p, 0);
+    __syncthreads();
+    MOE_STAMP(p, 4);
+    up_reduce_n(p, L, s);
+    publish(p, epoch + 2);
+    MOE_STAMP(p, 12);
+    zero_partials(L, (size_t)p.wpt * p.T * (p.K + 1) * p.pitch);
+    It down = It{2, 0, wave % s.nrt_p, 0, 0};  // this wave's down tile
+    settle(p, s, down);
+    wait_all(p, epoch + 2);
+    MOE_STAMP(p, 5);
+    MOE_WSTAMP(p, 1);
+    run_narrow<FMT>(p, L, s, down, 3);
+    MOE_WSTAMP(p, 2);
+    MOE_STAMP(p, 6);
+    __syncthreads();
+    combine(p, L, s);
+    MOE_STAMP(p, 7);
+    return;
+  }
   bool ok = true;
   int jc = 0;  // jobs ended
   Owned own;
@@ -1287,6 +1688,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   It up = It{0, first_job(p, 0), 0, 0, 0};
   settle(p, s, up);
   run_phase<NPRE, FMT>(p, L, s, up, 2, acc, jc, own, ok);
+  MOE_WSTAMP(p, 0);
 
   It down = It{2, 0, 0, 0, 0};
   settle(p, s, down);
@@ -1296,17 +1698,22 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   lds_st32(L.ctl + kCtlMidOut + wave, 1u);
   if (wave == 0) {
     lds_wait<8>(p, L.ctl + kCtlMidOut, 1u, ok);
+    MOE_STAMP(p, 11);
     if (tid == 0) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       __hip_atomic_store(&p.flags[blockIdx.x], epoch + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    MOE_STAMP(p, 12);
     if (down.phase == 2) poll_flags(p, epoch + 2);
+    MOE_STAMP(p, 13);
     lds_st32(L.ctl + kCtlCrossed, 1u);
   }
   if (down.phase == 2) lds_wait<1>(p, L.ctl + kCtlCrossed, 1u, ok);
   MOE_STAMP(p, 5);
+  MOE_WSTAMP(p, 1);
 
   run_phase<NPRE, FMT>(p, L, s, down, 3, acc, jc, own, ok);
+  MOE_WSTAMP(p, 2);
   service<NPRE>(p, L, own, true, ok);  // the last owned down job
   MOE_STAMP(p, 6);
   __syncthreads();
@@ -1314,10 +1721,6 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   // S5: combine this CU's output rows
   combine(p, L, s);
   MOE_STAMP(p, 7);
-  if (threadIdx.x == 0 && p.timeline) {
-    p.timeline[blockIdx.x * 16 + 8] = (uint64_t)jc;
-    p.timeline[blockIdx.x * 16 + 9] = (uint64_t)depth<NPRE>();
-  }
 }
 
 // ------------------------------------------------------------------ host glue
@@ -1335,9 +1738,9 @@ WsLayout ws_layout(int max_rows, int E, int K, int H, int I, int Is) {
   return w;
 }
 
-template <int MODE, int FMT, int NPRE = 1>
+template <int MODE, int FMT, int NARROW = 1>
 static hipError_t launch_one(const Params& p, hipStream_t stream) {
-  auto kfn = moe_fused<MODE, FMT, NPRE>;
+  auto kfn = moe_fused<MODE, FMT, NARROW>;
   hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kfn, dim3(p.ncu), dim3(kThreads), p.lds_bytes, stream, p);
@@ -1345,15 +1748,15 @@ static hipError_t launch_one(const Params& p, hipStream_t stream) {
 }
 
 hipError_t launch(const Params& p, int mode, hipStream_t stream) {
-  const bool wide = p.T > 16;  // some group may have more than one 16-column tile
+  const bool wide = !p.narrow;
   if (p.routed_fmt == 0) {
     if (mode == kModeForward)
-      return wide ? launch_one<kModeForward, 0, 2>(p, stream) : launch_one<kModeForward, 0, 1>(p, stream);
+      return wide ? launch_one<kModeForward, 0, 0>(p, stream) : launch_one<kModeForward, 0, 1>(p, stream);
     if (mode == kModeRoute) return launch_one<kModeRoute, 0>(p, stream);
     return launch_one<kModeGroups, 0>(p, stream);
   }
   if (mode == kModeForward)
-    return wide ? launch_one<kModeForward, 1, 2>(p, stream) : launch_one<kModeForward, 1, 1>(p, stream);
+    return wide ? launch_one<kModeForward, 1, 0>(p, stream) : launch_one<kModeForward, 1, 1>(p, stream);
   if (mode == kModeRoute) return launch_one<kModeRoute, 1>(p, stream);
   return launch_one<kModeGroups, 1>(p, stream);
 }

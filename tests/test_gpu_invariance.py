@@ -14,16 +14,19 @@ from _gpu import gpu_case, oracle_route, run_forward, say
 pytestmark = pytest.mark.gpu
 
 MID = dict(hidden=2048, inter=512, shared_inter=512, n_experts=64, top_k=6, n_group=8, topk_group=3)
+# hidden > 16 * 256: two 16-row down tiles per CU, split over the waves
+MID2 = dict(hidden=4352, inter=256, shared_inter=256, n_experts=32, top_k=4, n_group=4, topk_group=2)
 
 
 def _layer(spec, case, T):
     return moe.Layer(spec, case, max_rows=T)
 
 
-@pytest.mark.parametrize("T", [1, 2, 5, 8, 16, 37, 64])
-def test_batch_invariance_mid(T):
-    say(f"batch invariance mid T={T}")
-    spec = fixtures.spec_with("tiny", **MID)
+@pytest.mark.parametrize("mid,T", [(1, 1), (1, 2), (1, 5), (1, 8), (1, 16), (1, 37), (1, 64),
+                                   (2, 1), (2, 9), (2, 16), (2, 17)])
+def test_batch_invariance_mid(mid, T):
+    say(f"batch invariance mid{mid} T={T}")
+    spec = fixtures.spec_with("tiny", **(MID if mid == 1 else MID2))
     case = gpu_case(spec, 64, 21, rows="corr", requests=16)
     layer = _layer(spec, case, 64)
     full = run_forward(layer, case["x"])

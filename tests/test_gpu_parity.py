@@ -29,6 +29,11 @@ SMALL = [
                          routed_fmt=1, bias_bf16=1), 16, 16, "corr"),
     ("no_shared", dict(n_shared=0, hidden=512, inter=256, n_experts=12, top_k=3), 7, 17, "iid"),
     ("k_equals_e", dict(n_experts=8, top_k=8, hidden=256, inter=128), 3, 18, "iid"),
+    # hidden > 16 * 256: a CU's down slice spans two 16-row tiles (the second ragged)
+    ("two_down_tiles", dict(hidden=4352, inter=256, shared_inter=256, n_experts=16, top_k=4), 5, 19, "corr"),
+    ("two_down_tiles_wide", dict(hidden=4352, inter=256, shared_inter=256, n_experts=16, top_k=4), 24, 20, "iid"),
+    ("mxfp4_two_tiles", dict(hidden=4608, inter=512, shared_inter=256, n_experts=16, top_k=6,
+                             routed_fmt=1, bias_bf16=1), 12, 21, "corr"),
 ]
 
 
