@@ -368,9 +368,75 @@ __device__ __forceinline__ bool key_before(double b1, int e1, double b2, int e2)
   return b1 > b2 || (b1 == b2 && e1 < e2);
 }
 
+// Cross-lane moves that need no LDS round trip: DPP within 16-lane rows
+// (xor 1, xor 2, half-row mirror, row mirror) and a swizzle (xor 16 within
+// 32 lanes).  After the four DPP steps of an all-reduce every lane holds its
+// row's result; after the swizzle, its 32-lane half's.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+constexpr int kSwizzleXor16 = 0x401F;
+
+template <int CTRL>
+__device__ __forceinline__ int xlane(int v) {
+  if (CTRL == kSwizzleXor16) return __builtin_amdgcn_ds_swizzle(v, kSwizzleXor16);
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double xlane_d(double v) {
+  const long long u = __double_as_longlong(v);
+  const int lo = xlane<CTRL>((int)(u & 0xffffffffll)), hi = xlane<CTRL>((int)(u >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  const long long u = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(u & 0xffffffffll), l);
+  const int hi = __builtin_amdgcn_readlane((int)(u >> 32), l);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+// (key, index) maximum under key_before, one exchange step.
+template <int CTRL>
+__device__ __forceinline__ void best_step(double& b, int& e) {
+  const double ob = xlane_d<CTRL>(b);
+  const int oe = xlane<CTRL>(e);
+  if (key_before(ob, oe, b, e)) {
+    b = ob;
+    e = oe;
+  }
+}
+// The wave's best (key, index); the result is the same in every lane.
+__device__ __forceinline__ void wave_best(double& b, int& e) {
+  best_step<kDppXor1>(b, e);
+  best_step<kDppXor2>(b, e);
+  best_step<kDppHalfMirror>(b, e);
+  best_step<kDppMirror>(b, e);
+  best_step<kSwizzleXor16>(b, e);
+  const double b0 = readlane_d(b, 0), b1 = readlane_d(b, 32);
+  const int e0 = __builtin_amdgcn_readlane(e, 0), e1 = __builtin_amdgcn_readlane(e, 32);
+  const bool second = key_before(b1, e1, b0, e0);
+  b = second ? b1 : b0;
+  e = second ? e1 : e0;
+}
+
+// Two largest values (t1 >= t2) of an aligned lane group, one exchange step.
+template <int CTRL>
+__device__ __forceinline__ void top2_step(double (&t1)[4], double (&t2)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const double o1 = xlane_d<CTRL>(t1[i]), o2 = xlane_d<CTRL>(t2[i]);
+    const double hi = fmax(t1[i], o1), lo = fmin(t1[i], o1);
+    t2[i] = fmax(lo, fmax(t2[i], o2));
+    t1[i] = hi;
+  }
+}
+
+__device__ __forceinline__ double pick4(const double (&v)[4], int i) {
+  return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
+}
+
 // Routes row r with one wave: group stage (sum of the two best keys per
 // group, keep k_g groups by (score desc, index asc)), then K rounds of wave
 // argmax over (key desc, index asc); weights s/sum(s)*scale in fp64.
+// Lane l holds experts l, l+64, l+128, l+192.
 __device__ inline void route_row(const Params& p, const Lds& L, int r) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const double* sc = p.scores + (size_t)r * p.E * 2;
@@ -385,35 +451,72 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r) {
     bv[i] = isnan(b) ? -INFINITY : b;
   }
   if (p.ng > 1) {
-    double* rb = L.rb + (size_t)wave * p.E;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (alive[i]) rb[lane + 64 * i] = bv[i];
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     const int gsz = p.E / p.ng;
-    if (lane < p.ng) {
-      double t1 = -INFINITY, t2 = -INFINITY;
-      for (int e = lane * gsz; e < (lane + 1) * gsz; ++e) {
-        double v = rb[e];
-        if (v > t1) { t2 = t1; t1 = v; }
-        else if (v > t2) { t2 = v; }
-      }
-      L.rgs[wave * 64 + lane] = t1 + t2;
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    if (lane < p.ng) {
-      const double mine = L.rgs[wave * 64 + lane];
-      int rank = 0;
-      for (int j = 0; j < p.ng; ++j) rank += key_before(L.rgs[wave * 64 + j], j, mine, lane) ? 1 : 0;
-      L.rkept[wave * 64 + lane] = rank < p.kg;
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    if (gsz <= 64 && (gsz & (gsz - 1)) == 0) {
+      // each group is an aligned run of gsz lanes of one slot: butterfly
+      double t1[4], t2[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (alive[i]) alive[i] = L.rkept[wave * 64 + (lane + 64 * i) / gsz] != 0;
+      for (int i = 0; i < 4; ++i) {
+        t1[i] = bv[i];
+        t2[i] = -INFINITY;
+      }
+      if (gsz > 1) top2_step<kDppXor1>(t1, t2);
+      if (gsz > 2) top2_step<kDppXor2>(t1, t2);
+      if (gsz > 4) top2_step<kDppHalfMirror>(t1, t2);
+      if (gsz > 8) top2_step<kDppMirror>(t1, t2);
+      if (gsz > 16) top2_step<kSwizzleXor16>(t1, t2);
+      if (gsz > 32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const double o1 = __shfl_xor(t1[i], 32, 64), o2 = __shfl_xor(t2[i], 32, 64);
+          const double hi = fmax(t1[i], o1), lo = fmin(t1[i], o1);
+          t2[i] = fmax(lo, fmax(t2[i], o2));
+          t1[i] = hi;
+        }
+      }
+      double gs[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gs[i] = t1[i] + t2[i];
+      // rank of this lane's group j_i = (lane + 64 i) / gsz among all groups
+      int rank[4] = {0, 0, 0, 0};
+      for (int j = 0; j < p.ng; ++j) {
+        const int first = j * gsz;
+        const double gj = readlane_d(pick4(gs, first >> 6), first & 63);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rank[i] += key_before(gj, j, gs[i], (lane + 64 * i) / gsz) ? 1 : 0;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) alive[i] = alive[i] && rank[i] < p.kg;
+    } else {
+      double* rb = L.rb + (size_t)wave * p.E;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (alive[i]) rb[lane + 64 * i] = bv[i];
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      if (lane < p.ng) {
+        double t1 = -INFINITY, t2 = -INFINITY;
+        for (int e = lane * gsz; e < (lane + 1) * gsz; ++e) {
+          double v = rb[e];
+          if (v > t1) { t2 = t1; t1 = v; }
+          else if (v > t2) { t2 = v; }
+        }
+        L.rgs[wave * 64 + lane] = t1 + t2;
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      if (lane < p.ng) {
+        const double mine = L.rgs[wave * 64 + lane];
+        int rank = 0;
+        for (int j = 0; j < p.ng; ++j) rank += key_before(L.rgs[wave * 64 + j], j, mine, lane) ? 1 : 0;
+        L.rkept[wave * 64 + lane] = rank < p.kg;
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (alive[i]) alive[i] = L.rkept[wave * 64 + (lane + 64 * i) / gsz] != 0;
+    }
   }
   MOE_STAMP(p, 14);
   double ssum = 0.0;
@@ -429,20 +532,12 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r) {
         const int e = lane + 64 * i;
         if (alive[i] && key_before(bv[i], e, bb, be)) { bb = bv[i]; be = e; }
       }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        double ob = __shfl_xor(bb, off, 64);
-        int oe = __shfl_xor(be, off, 64);
-        if (key_before(ob, oe, bb, be)) { bb = ob; be = oe; }
-      }
-      // be is now the same in every lane; its owner retires it
+      wave_best(bb, be);
+      // be is now uniform; its owner retires it
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (lane + 64 * i == be) alive[i] = false;
-      // the pick's score s, from the lane that holds it
-      const int slot = be >> 6;
-      const double mine = slot == 0 ? sv[0] : slot == 1 ? sv[1] : slot == 2 ? sv[2] : sv[3];
-      const double sp = __shfl(mine, be & 63, 64);
+      const double sp = readlane_d(pick4(sv, be >> 6), be & 63);
       picks[k] = be;
       pick_s[k] = sp;
       ssum += sp;
@@ -1482,7 +1577,7 @@ __device__ __forceinline__ void eat_item_n(const EatN& e, const ItemN& it, f32x4
 // One phase of the narrow stream.  Partials go to LDS, which must be zero
 // where this wave has no items.
 template <int FMT>
-__device__ __forceinline__ void run_narrow(const Params& p, const Lds& L, const Sched& s, It start, int stop) {
+__device__ __forceinline__ void run_narrow(const Params& p, const Lds& L, const Sched& s, It start, int stop, int& jc) {
   constexpr int D = 5;
   if (start.phase >= stop) return;
   FetchN f;
@@ -1513,6 +1608,8 @@ __device__ __forceinline__ void run_narrow(const Params& p, const Lds& L, const 
         if (e.left == 0) {
           if (e.pst) lds_st128(L.pbuf + e.pidx, __builtin_bit_cast(u32x4, acc));
           acc = f32x4{0.f, 0.f, 0.f, 0.f};
+          MOE_JSTAMP(p, jc);
+          balance(L, ++jc);
           if (!eat_next_n(p, L, s, e, stop, false)) goto drained;
         }
       }
@@ -1520,6 +1617,7 @@ __device__ __forceinline__ void run_narrow(const Params& p, const Lds& L, const 
   }
 drained:
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the dead items' loads
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // Zeroes the narrow partial region (n floats).
@@ -1655,7 +1753,8 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
     __syncthreads();
     It up = It{0, first_job(p, 0), 0, 0, 0};
     settle(p, s, up);
-    run_narrow<FMT>(p, L, s, up, 2);
+    int jn = 0;  // jobs this wave has ended (for balance)
+    run_narrow<FMT>(p, L, s, up, 2, jn);
     MOE_WSTAMP(p, 0);
     __syncthreads();
     MOE_STAMP(p, 4);
@@ -1668,7 +1767,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
     wait_all(p, epoch + 2);
     MOE_STAMP(p, 5);
     MOE_WSTAMP(p, 1);
-    run_narrow<FMT>(p, L, s, down, 3);
+    run_narrow<FMT>(p, L, s, down, 3, jn);
     MOE_WSTAMP(p, 2);
     MOE_STAMP(p, 6);
     __syncthreads();

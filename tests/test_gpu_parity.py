@@ -67,6 +67,25 @@ def test_small_parity(name, over, T, seed, rows):
     assert rel <= REL_L2 and mx <= MAX_ABS
 
 
+# (E, n_group, topk_group, K, T): group sizes 2..128, powers of two and not
+ROUTING = [(48, 4, 2, 6, 9), (256, 2, 1, 8, 5), (256, 4, 2, 8, 7), (256, 8, 4, 8, 16),
+           (128, 64, 8, 8, 3), (64, 16, 5, 7, 4), (200, 8, 3, 5, 11)]
+
+
+@pytest.mark.parametrize("E,ng,kg,K,T", ROUTING, ids=[f"e{r[0]}_g{r[1]}_k{r[3]}" for r in ROUTING])
+def test_routing_groupings(E, ng, kg, K, T):
+    say(f"routing E={E} ng={ng} kg={kg} K={K} T={T}")
+    spec = _spec(dict(n_experts=E, n_group=ng, topk_group=kg, top_k=K))
+    case = gpu_case(spec, T, 100 + E + ng, rows="iid")
+    layer = moe.Layer(spec, case, max_rows=T)
+    ids_o, w_o, ge, gg = oracle_route(spec, case)
+    assert np.min(ge) > 1e-9 and np.min(gg) > 1e-9
+    ids, wts = layer.route(case["x"])
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ids_o)
+    assert np.allclose(wts.cpu().numpy(), w_o, rtol=1e-6, atol=0)
+
+
 @pytest.mark.parametrize("name,over,T,seed,rows", SMALL[:6], ids=[s[0] for s in SMALL[:6]])
 def test_small_groups_exact(name, over, T, seed, rows):
     import oracle
