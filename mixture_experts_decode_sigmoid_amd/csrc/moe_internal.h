@@ -41,6 +41,7 @@ struct Params {
   int wpt;         // waves per down tile (8 / nrt_p); they split its K-blocks
   int pitch;       // floats per (row, slot) line of the down products (16 * tiles)
   int tpc;         // up/gate tiles of one group a CU can hold
+  int njd;         // narrow: job table entries
   // inputs
   const uint16_t* x;
   const uint16_t* router_w;

@@ -169,6 +169,7 @@ struct Lds {
   double* rgs;       // [kWaves][64] group scores
   int32_t* rkept;    // [kWaves][64]
   float* pbuf;       // wide: down products [T*(K+1)][hs]; narrow: the per-wave partials (see lds_offsets)
+  struct JobDesc* jd;  // narrow: job tables (see build_jobs)
 };
 
 __host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -192,13 +193,14 @@ constexpr size_t kRedTileBytes = 16 * (size_t)kWaves * 64;  // one tile: [wave][
 // job-end partial slots summed by an owner wave, and one copy of the down
 // products [row][slot][hs].
 struct LdsOffsets {
-  size_t ids, w, first, egrp, rmask, gexp, gcnt, gstart, cols, cgrp, misc, ctl, red, pbuf, total;
+  size_t ids, w, first, egrp, rmask, gexp, gcnt, gstart, cols, cgrp, misc, ctl, jd, red, pbuf, total;
 };
+constexpr size_t kJobDescBytes = 48;
 
 __host__ __device__ inline size_t pu_floats(int T, int K, int tpc) { return (size_t)kWaves * T * (K + 1) * tpc * 16; }
 
 __host__ __device__ inline LdsOffsets lds_offsets(int T, int K, int E, int hs, int narrow, int tpc, int wpt,
-                                                  int pitch) {
+                                                  int pitch, int njd) {
   LdsOffsets o;
   size_t q = 0;
   const int uses = T * K, gmax = 1 + T * K;
@@ -214,6 +216,7 @@ __host__ __device__ inline LdsOffsets lds_offsets(int T, int K, int E, int hs, i
   o.cgrp = q; q = align_up(q + 4 * (size_t)T * (K + 1), 16);
   o.misc = q; q = align_up(q + 4 * 32, 16);
   o.ctl = q; q = align_up(q + 4 * 64, 16);
+  o.jd = q; q = align_up(q + (narrow ? kJobDescBytes * (size_t)njd : 0), 16);
   // the routing scratch (used before the stream) overlaps the job-end
   // partials and the down products (used in it)
   o.red = q;
@@ -242,11 +245,17 @@ size_t stream_geometry(Params& p, int narrow) {
   const int tiles = (p.I > p.Is ? p.I : p.Is) / 8;
   p.tpc = (tiles + p.ncu - 1) / p.ncu;
   p.narrow = narrow;
-  return lds_offsets(p.T, p.K, p.E, p.hs, p.narrow, p.tpc, p.wpt, p.pitch).total;
+  // job tables: this CU's up/gate jobs (at most a share of the largest job
+  // count the batch can have) and one down job per group
+  const int gmax = 1 + (p.E < p.T * p.K ? p.E : p.T * p.K);
+  const int sh_tiles = p.n_shared ? p.Is / 8 : 0;
+  const long jobs = sh_tiles + (long)(gmax - 1) * (p.I / 8);
+  p.njd = (int)((jobs + p.ncu - 1) / p.ncu) + gmax;
+  return lds_offsets(p.T, p.K, p.E, p.hs, p.narrow, p.tpc, p.wpt, p.pitch, p.njd).total;
 }
 
 __device__ inline Lds lds_map(char* base, const Params& p) {
-  LdsOffsets o = lds_offsets(p.T, p.K, p.E, p.hs, p.narrow, p.tpc, p.wpt, p.pitch);
+  LdsOffsets o = lds_offsets(p.T, p.K, p.E, p.hs, p.narrow, p.tpc, p.wpt, p.pitch, p.njd);
   Lds L;
   L.ids = (int32_t*)(base + o.ids);
   L.w = (float*)(base + o.w);
@@ -260,6 +269,7 @@ __device__ inline Lds lds_map(char* base, const Params& p) {
   L.cgrp = (int32_t*)(base + o.cgrp);
   L.misc = (int32_t*)(base + o.misc);
   L.ctl = (uint32_t*)(base + o.ctl);
+  L.jd = (JobDesc*)(base + o.jd);
   L.red = (float*)(base + o.red);
   L.pbuf = (float*)(base + o.pbuf);
   L.rb = (double*)(base + o.red);
@@ -1380,16 +1390,145 @@ drained:
 // change on either side does more.  At a job end the wave stores its
 // partial tile into its own part of LDS and never waits for another wave.
 
+// A job as the narrow stream sees it, built once per call for every job of
+// this CU (see build_jobs).  Lanes add their row, K-block and column.
+struct JobDesc {
+  uint64_t wb;        // weights of the job's row 0 (up/gate: gate row 8t; down: the expert's W_down)
+  uint64_t sb;        // block scales of that row (FP8 up/gate: its 128-row block row; MXFP4: its row)
+  uint32_t rowbytes;  // weight bytes per row
+  uint32_t jump;      // up/gate: rows between lane row 7 (gate) and lane row 8 (up), minus one
+  uint32_t shi;       // FP8 up/gate: scale bytes from the gate rows' block row to the up rows'; MXFP4: scale bytes per row
+  int32_t nkb;        // K-blocks
+  int32_t fmt;        // 0 FP8, 1 MXFP4
+  int32_t ncols;      // the group's columns
+  int32_t cbase;      // its first column in the column table
+  int32_t pslot;      // up/gate: partial slot of its column 0
+};
+static_assert(sizeof(JobDesc) == 48, "three 16-byte LDS reads");
+
+__device__ inline JobDesc read_desc(const Lds& L, int k) {
+  u32x4 a, b, c;
+  asm volatile("ds_read_b128 %0, %3\n\tds_read_b128 %1, %3 offset:16\n\tds_read_b128 %2, %3 offset:32\n\t"
+               "s_waitcnt lgkmcnt(0)"
+               : "=&v"(a), "=&v"(b), "=&v"(c)
+               : "v"(lds_off(L.jd + k))
+               : "memory");
+  JobDesc d;
+  d.wb = ((uint64_t)(uint32_t)uni((int)a[1]) << 32) | (uint32_t)uni((int)a[0]);
+  d.sb = ((uint64_t)(uint32_t)uni((int)a[3]) << 32) | (uint32_t)uni((int)a[2]);
+  d.rowbytes = (uint32_t)uni((int)b[0]);
+  d.jump = (uint32_t)uni((int)b[1]);
+  d.shi = (uint32_t)uni((int)b[2]);
+  d.nkb = uni((int)b[3]);
+  d.fmt = uni((int)c[0]);
+  d.ncols = uni((int)c[1]);
+  d.cbase = uni((int)c[2]);
+  d.pslot = uni((int)c[3]);
+  return d;
+}
+
+// Job tables of this CU: its up/gate jobs (shared tiles, then routed tiles,
+// dealt round-robin over CUs) at 0..nU-1, then one down job per group at
+// nU + g.  Whole workgroup; ends synchronised.
+__device__ inline void build_jobs(const Params& p, const Lds& L, const Sched& s, int nU) {
+  const size_t H = p.H, I = p.I;
+  for (int k = threadIdx.x; k < nU + s.G; k += kThreads) {
+    JobDesc d;
+    const bool up = k < nU;
+    int g, tile = 0;
+    if (up) {
+      const int j = (int)blockIdx.x + k * p.ncu;
+      if (j < s.sh_tiles) {
+        g = 0;
+        tile = j;
+      } else {
+        g = p.n_shared + (j - s.sh_tiles) / s.rt_tiles;
+        tile = (j - s.sh_tiles) % s.rt_tiles;
+      }
+    } else {
+      g = k - nU;
+    }
+    const bool sh = shared_group(p, g);
+    const int e = sh ? 0 : L.gexp[g];
+    const int iexp = sh ? p.Is : p.I;
+    const int kdim = up ? p.H : iexp;
+    d.fmt = sh ? 0 : p.routed_fmt;
+    d.nkb = kdim / 128;
+    d.ncols = sh ? p.T : L.gcnt[g];
+    d.cbase = sh ? 0 : L.gstart[g];
+    d.pslot = up ? d.cbase * p.tpc + tile / p.ncu : 0;
+    d.jump = up ? iexp - 8 : 0;
+    const uint8_t* w;
+    const uint8_t* S;
+    if (d.fmt == 0) {
+      d.rowbytes = kdim;
+      if (sh) {
+        w = up ? p.sh_wgu : p.sh_wd;
+        S = (const uint8_t*)(up ? p.sh_sgu : p.sh_sd);
+      } else {
+        w = up ? p.wgu + (size_t)e * 2 * I * H : p.wd + (size_t)e * H * I;
+        S = up ? (const uint8_t*)p.sgu + 4 * (size_t)e * (2 * I / 128) * (H / 128)
+               : (const uint8_t*)p.sd + 4 * (size_t)e * (H / 128) * (I / 128);
+      }
+      if (up) {
+        const int nb_lo = (8 * tile) / 128, nb_hi = (iexp + 8 * tile) / 128;
+        w += (size_t)8 * tile * kdim;
+        S += 4 * (size_t)nb_lo * d.nkb;
+        d.shi = 4u * (uint32_t)((nb_hi - nb_lo) * d.nkb);
+      } else {
+        d.shi = 0;
+      }
+    } else {
+      d.rowbytes = kdim / 2;
+      d.shi = kdim / 32;
+      w = up ? p.wgu + (size_t)e * 2 * I * (H / 2) : p.wd + (size_t)e * H * (I / 2);
+      S = up ? (const uint8_t*)p.sgu + (size_t)e * 2 * I * (H / 32) : (const uint8_t*)p.sd + (size_t)e * H * (I / 32);
+      if (up) {
+        w += (size_t)8 * tile * d.rowbytes;
+        S += (size_t)8 * tile * d.shi;
+      }
+    }
+    d.wb = (uint64_t)w;
+    d.sb = (uint64_t)S;
+    L.jd[k] = d;
+  }
+  __syncthreads();
+}
+
+// Per-wave constants of a phase (KIND 1 up/gate, 2 down).  Up/gate: every
+// wave takes K-blocks w + 8i of each job, rows 0..7 of a tile are gate rows
+// and 8..15 up rows.  Down: wave w takes tile rt = w % nrt_p of the CU's
+// slice, rows hb.. (nlive live), and K-blocks w / nrt_p + wpt*i.
+struct PhaseN {
+  int k0, lstep;  // this wave's K-blocks: k0 + (i << lstep)
+  int hb, nlive;  // down: first row of this wave's tile and its live rows
+  int split;      // FP8: MFMA output rows (4*lg + q) below it take the first scale block row
+  int dnb;        // FP8 down: block rows between the tile's first and last live row (0 or 1)
+  int rt;         // down: this wave's tile
+};
+template <int KIND>
+__device__ __forceinline__ int ph_k0(const PhaseN& ph) { return KIND == 1 ? wave_id() : ph.k0; }
+template <int KIND>
+__device__ __forceinline__ int ph_lstep(const PhaseN& ph) { return KIND == 1 ? 3 : ph.lstep; }
+template <int KIND>
+__device__ __forceinline__ int ph_split(const PhaseN& ph) { return KIND == 1 ? 8 : ph.split; }
+
+template <int KIND>
+__device__ __forceinline__ int job_items(const PhaseN& ph, int nkb) {
+  const int k0 = ph_k0<KIND>(ph);
+  return nkb > k0 ? ((nkb - 1 - k0) >> ph_lstep<KIND>(ph)) + 1 : 0;
+}
+
 // The fetch side: byte offsets of this lane's next item from uniform bases.
 struct FetchN {
-  It it;
+  int k;                         // next job to set up
   int left;                      // items left in the job (large once past the phase)
+  int nstep;                     // K-blocks per item step (0 once past the phase)
+  int fmt;                       // 0 FP8, 1 MXFP4
   const uint8_t* wb;             // weights
   const uint8_t* sb;             // block scales
   const uint8_t* ab;             // activations: x or mid
   uint32_t wo, so, ao;           // this lane's offsets of the next item
-  uint32_t winc, sinc, ainc;     // per item
-  uint32_t w1o;                  // second weight load: +16 (FP8) or +0 (MXFP4)
 };
 
 struct ItemN {
@@ -1397,161 +1536,114 @@ struct ItemN {
   uint32_t s;
 };
 
-// The job's weight, scale and activation offsets for this lane; its first
-// item is K-block kr.k0.
-__device__ inline void fetch_setup_n(const Params& p, const Lds& L, const Sched& s, FetchN& f, const KRange& kr) {
-  const int lane = threadIdx.x & 63, lg = lane >> 4, row = lane & 15;
-  const It& c = f.it;
-  const bool down = c.phase == 2, sh = shared_group(p, c.g);
-  const int kdim = job_kdim(p, c), nlive = job_nlive(s, c);
-  int ncols, eid, code[1];
-  group_cols<1>(p, L, c.g, ncols, eid, code);
-  f.left = kr.n;
-  f.ab = (const uint8_t*)(down ? arg_ptr(p.mid) : arg_ptr(p.x));
-  f.ao = 2 * act_offset(p, down ? 2 : 1, code[0], lg) + 256u * (uint32_t)kr.k0;
-  f.ainc = 256u * (uint32_t)kr.step;
-  const int iexp = sh ? uni(p.Is) : uni(p.I);
-  const int hb = s.h0 + 16 * c.rt;
-  const int wr = down ? hb + (row < nlive ? row : nlive - 1) : (row < 8 ? 8 * c.tile + row : iexp + 8 * c.tile + row - 8);
-  const size_t H = uni(p.H), I = uni(p.I), e = (size_t)eid;
-  const int fmt = sh ? 0 : uni(p.routed_fmt);
-  if (fmt == 0) {
-    // FP8 weights [rows][kdim] bytes; fp32 scales [rows/128][kdim/128]
-    const uint8_t* w;
-    const float* S;
-    if (sh) {
-      w = down ? arg_ptr(p.sh_wd) : arg_ptr(p.sh_wgu);
-      S = down ? arg_ptr(p.sh_sd) : arg_ptr(p.sh_sgu);
-    } else {
-      w = down ? arg_ptr(p.wd) + e * H * I : arg_ptr(p.wgu) + e * 2 * I * H;
-      S = down ? (const float*)arg_ptr(p.sd) + e * (H / 128) * (I / 128)
-               : (const float*)arg_ptr(p.sgu) + e * (2 * I / 128) * (H / 128);
-    }
-    const int nkb = kdim / 128;
-    const int nb_lo = down ? hb / 128 : (8 * c.tile) / 128;
-    const int nb_hi = down ? (hb + nlive - 1) / 128 : (iexp + 8 * c.tile) / 128;
-    f.wb = w;
-    f.wo = (uint32_t)wr * (uint32_t)kdim + 128u * (uint32_t)kr.k0 + 32u * (uint32_t)lg;
-    f.winc = 128u * (uint32_t)kr.step;
-    f.w1o = 16;
-    f.sb = (const uint8_t*)S;
-    f.so = 4u * ((uint32_t)(lane < 32 ? nb_lo : nb_hi) * (uint32_t)nkb + (uint32_t)kr.k0);
-  } else {
-    // MXFP4 weights [rows][kdim/2] bytes; E8M0 scales [rows][kdim/32]
-    f.wb = down ? arg_ptr(p.wd) + e * H * (I / 2) : arg_ptr(p.wgu) + e * 2 * I * (H / 2);
-    f.sb = down ? (const uint8_t*)arg_ptr(p.sd) + e * H * (I / 32) : (const uint8_t*)arg_ptr(p.sgu) + e * 2 * I * (H / 32);
-    f.wo = (uint32_t)wr * (uint32_t)(kdim / 2) + 64u * (uint32_t)kr.k0 + 16u * (uint32_t)lg;
-    f.winc = 64u * (uint32_t)kr.step;
-    f.w1o = 0;
-    f.so = (uint32_t)wr * (uint32_t)(kdim / 32) + 4u * (uint32_t)kr.k0;
-  }
-  f.sinc = 4u * (uint32_t)kr.step;
+// Column code (row*16 + slot) of this lane's column in a job (a lane past
+// the group's columns takes its last one: MFMA columns are independent and
+// that output is never stored).
+__device__ __forceinline__ int lane_code(const Lds& L, const JobDesc& d) {
+  const int col = threadIdx.x & 15;
+  return (int)lds_ld32(L.cols + d.cbase + (col < d.ncols ? col : d.ncols - 1));
 }
 
-// Past the phase: items load 16 bytes of x and are never multiplied.
-__device__ inline void fetch_dead_n(const Params& p, FetchN& f) {
+// Moves the fetch side to the next job of [f.k, kend) with items for this
+// wave, or past the end (dead items: 16 bytes of x, never multiplied).
+template <int FMT, int KIND>
+__device__ inline void fetch_next_n(const Params& p, const Lds& L, const PhaseN& ph, FetchN& f, int kend) {
+  const int lane = threadIdx.x & 63, lg = lane >> 4, row = lane & 15;
+  const int k0 = ph_k0<KIND>(ph);
+  for (; f.k < kend; ++f.k) {
+    const JobDesc d = read_desc(L, f.k);
+    const int n = job_items<KIND>(ph, d.nkb);
+    if (n == 0) continue;
+    ++f.k;
+    const int fmt = FMT == 0 ? 0 : d.fmt;
+    const int code = lane_code(L, d);
+    const uint32_t kb = fmt ? 64u : 128u, lb = fmt ? 16u : 32u;
+    const uint32_t lrow = KIND == 1 ? (row < 8 ? row : row + d.jump) : ph.hb + (row < ph.nlive ? row : ph.nlive - 1);
+    f.wb = (const uint8_t*)d.wb;
+    f.wo = lrow * d.rowbytes + (uint32_t)k0 * kb + (uint32_t)lg * lb;
+    if (fmt == 0) {
+      if (KIND == 1) {
+        f.sb = (const uint8_t*)d.sb;
+        f.so = (lane < 32 ? 0u : d.shi) + 4u * (uint32_t)k0;
+      } else {
+        f.sb = (const uint8_t*)d.sb + 4 * (size_t)(ph.hb >> 7) * d.nkb;
+        f.so = (lane < 32 ? 0u : 4u * (uint32_t)(ph.dnb * d.nkb)) + 4u * (uint32_t)k0;
+      }
+    } else {
+      f.sb = (const uint8_t*)d.sb;
+      f.so = lrow * d.shi + 4u * (uint32_t)k0;
+    }
+    f.ao = 2 * act_offset(p, KIND, code, lg) + 256u * (uint32_t)k0;
+    f.fmt = fmt;
+    f.nstep = 1 << ph_lstep<KIND>(ph);
+    f.left = n;
+    return;
+  }
   f.left = 1 << 30;
+  f.nstep = 0;
+  f.fmt = 0;
   f.wb = f.sb = f.ab = (const uint8_t*)arg_ptr(p.x);
   f.wo = f.so = f.ao = 0;
-  f.winc = f.sinc = f.ainc = 0;
-  f.w1o = 0;
 }
 
-// Moves the fetch side to the next job (from f.it, which is `first` or the
-// job just finished) in which this wave has items.
-__device__ inline void fetch_next_n(const Params& p, const Lds& L, const Sched& s, FetchN& f, int stop, bool first) {
-  if (!first) {
-    next_job(p, s, f.it);
-    uni(f.it);
-  }
-  for (;;) {
-    if (f.it.phase >= stop) {
-      fetch_dead_n(p, f);
-      return;
-    }
-    const KRange kr = job_krange(p, s, f.it);
-    if (kr.n > 0) {
-      fetch_setup_n(p, L, s, f, kr);
-      return;
-    }
-    next_job(p, s, f.it);
-    uni(f.it);
-  }
-}
-
+template <int FMT>
 __device__ __forceinline__ void fetch_item_n(const FetchN& f, ItemN& it) {
   const uint8_t* w = f.wb + f.wo;
   it.w0 = ldg<u32x4>(w);
-  it.w1 = ldg<u32x4>(w + f.w1o);
+  it.w1 = ldg<u32x4>(w + (FMT == 0 || f.fmt == 0 ? 16 : 0));
   it.s = ldg<uint32_t>(f.sb + f.so);
   const uint8_t* a = f.ab + f.ao;
 #pragma unroll
   for (int m = 0; m < 4; ++m) it.B[m] = ldg<u32x4>(a + 16 * m);
 }
 
+template <int FMT>
 __device__ __forceinline__ void fetch_adv_n(FetchN& f) {
-  f.wo += f.winc;
-  f.so += f.sinc;
-  f.ao += f.ainc;
+  const uint32_t n = (uint32_t)uni(f.nstep);
+  f.wo += n * (FMT == 0 || f.fmt == 0 ? 128u : 64u);
+  f.so += 4u * n;
+  f.ao += 256u * n;
   f.left = uni(f.left) - 1;
 }
 
 // The multiplying side.
 struct EatN {
-  It it;
+  int k;
   int left;        // items left in the job
   int fmt;         // 0 FP8, 1 MXFP4
-  int split;       // FP8: MFMA output rows (4*lg + q) below it take the first block scale
   uint32_t pidx;   // this lane's partial (floats from L.pbuf); only stored when pst
   bool pst;        // this lane's column is one of the group's
 };
 
-__device__ inline void eat_setup_n(const Params& p, const Lds& L, const Sched& s, EatN& e, const KRange& kr) {
-  const int lane = threadIdx.x & 63, lg = lane >> 4, wave = wave_id();
-  const It& c = e.it;
-  const bool sh = shared_group(p, c.g);
-  int ncols, eid, code[1], gstart = 0;
-  group_cols<1>(p, L, c.g, ncols, eid, code);
-  if (!sh) gstart = lds_ldi_uniform(L.gstart + c.g);
-  e.left = kr.n;
-  e.fmt = sh ? 0 : uni(p.routed_fmt);
-  e.pst = (lane & 15) < ncols;
-  const int col = lane & 15;
-  if (c.phase <= 1) {
-    e.split = 8;  // rows 0..7 of the tile are gate rows, 8..15 up rows
-    const uint32_t slot = (uint32_t)(gstart + col) * (uint32_t)p.tpc + (uint32_t)(c.tile / p.ncu);
-    e.pidx = ((uint32_t)wave * (uint32_t)(p.T * (p.K + 1) * p.tpc) + slot) * 16u + 4u * (uint32_t)lg;
-  } else {
-    const int hb = s.h0 + 16 * c.rt;
-    e.split = (hb / 128 + 1) * 128 - hb;  // a 16-row tile spans at most two scale blocks
-    e.pidx = (((uint32_t)kr.k0 * (uint32_t)p.T + (uint32_t)(code[0] >> 4)) * (uint32_t)(p.K + 1) +
-              (uint32_t)(code[0] & 15)) * (uint32_t)p.pitch +
-             16u * (uint32_t)c.rt + 4u * (uint32_t)lg;
-  }
-}
-
-// Moves the multiplying side to its next job with items; false at the end
-// of the phase.
-__device__ inline bool eat_next_n(const Params& p, const Lds& L, const Sched& s, EatN& e, int stop, bool first) {
-  if (!first) {
-    next_job(p, s, e.it);
-    uni(e.it);
-  }
-  for (;;) {
-    if (e.it.phase >= stop) return false;
-    const KRange kr = job_krange(p, s, e.it);
-    if (kr.n > 0) {
-      eat_setup_n(p, L, s, e, kr);
-      return true;
+// Moves the multiplying side to its next job of [e.k, kend) with items;
+// false at the end.
+template <int FMT, int KIND>
+__device__ inline bool eat_next_n(const Params& p, const Lds& L, const PhaseN& ph, EatN& e, int kend) {
+  const int lane = threadIdx.x & 63, lg = lane >> 4, col = lane & 15;
+  for (; e.k < kend; ++e.k) {
+    const JobDesc d = read_desc(L, e.k);
+    const int n = job_items<KIND>(ph, d.nkb);
+    if (n == 0) continue;
+    ++e.k;
+    e.left = n;
+    e.fmt = FMT == 0 ? 0 : d.fmt;
+    e.pst = col < d.ncols;
+    if (KIND == 1) {
+      const uint32_t slot = (uint32_t)d.pslot + (uint32_t)col * (uint32_t)p.tpc;
+      e.pidx = ((uint32_t)wave_id() * (uint32_t)(p.T * (p.K + 1) * p.tpc) + slot) * 16u + 4u * (uint32_t)lg;
+    } else {
+      const int code = lane_code(L, d);
+      e.pidx = (((uint32_t)ph.k0 * (uint32_t)p.T + (uint32_t)(code >> 4)) * (uint32_t)(p.K + 1) +
+                (uint32_t)(code & 15)) * (uint32_t)p.pitch +
+               16u * (uint32_t)ph.rt + 4u * (uint32_t)lg;
     }
-    next_job(p, s, e.it);
-    uni(e.it);
+    return true;
   }
+  return false;
 }
 
 template <int F>
-__device__ __forceinline__ void eat_item_n(const EatN& e, const ItemN& it, f32x4& acc) {
-  const int lg = (threadIdx.x & 63) >> 4;
+__device__ __forceinline__ void eat_item_n(int split, int lg, const ItemN& it, f32x4& acc) {
   bf16x8 A[4];
   if (F == 0) {
     A[0] = e4m3x8_to_bf16(it.w0[0], it.w0[1]);
@@ -1564,7 +1656,7 @@ __device__ __forceinline__ void eat_item_n(const EatN& e, const ItemN& it, f32x4
 #pragma unroll
     for (int m = 0; m < 4; ++m) t = mfma16(A[m], __builtin_bit_cast(bf16x8, it.B[m]), t);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[q] = fmaf(t[q], 4 * lg + q < e.split ? s_lo : s_hi, acc[q]);
+    for (int q = 0; q < 4; ++q) acc[q] = fmaf(t[q], 4 * lg + q < split ? s_lo : s_hi, acc[q]);
   } else {
     const float sc = e8m0_to_f32((it.s >> (8 * lg)) & 0xffu);
 #pragma unroll
@@ -1574,48 +1666,56 @@ __device__ __forceinline__ void eat_item_n(const EatN& e, const ItemN& it, f32x4
   }
 }
 
-// One phase of the narrow stream.  Partials go to LDS, which must be zero
-// where this wave has no items.
-template <int FMT>
-__device__ __forceinline__ void run_narrow(const Params& p, const Lds& L, const Sched& s, It start, int stop, int& jc) {
+// One phase of the narrow stream over jobs [k, kend) of the job tables.
+// Partials go to LDS, which must be zero where this wave has no items.
+template <int FMT, int KIND>
+__device__ __forceinline__ void run_narrow(const Params& p, const Lds& L, const PhaseN& ph, int k, int kend, int& jc) {
   constexpr int D = 5;
-  if (start.phase >= stop) return;
   FetchN f;
-  f.it = start;
-  fetch_next_n(p, L, s, f, stop, true);
+  f.k = k;
+  f.ab = (const uint8_t*)(KIND == 1 ? arg_ptr(p.x) : arg_ptr(p.mid));
+  fetch_next_n<FMT, KIND>(p, L, ph, f, kend);
   ItemN ring[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    fetch_item_n(f, ring[d]);
-    fetch_adv_n(f);
-    if (f.left == 0) fetch_next_n(p, L, s, f, stop, false);
+    fetch_item_n<FMT>(f, ring[d]);
+    fetch_adv_n<FMT>(f);
+    if (f.left == 0) fetch_next_n<FMT, KIND>(p, L, ph, f, kend);
   }
   EatN e;
-  e.it = start;
-  if (eat_next_n(p, L, s, e, stop, true)) {
+  e.k = k;
+  if (eat_next_n<FMT, KIND>(p, L, ph, e, kend)) {
+    const int lg = (threadIdx.x & 63) >> 4;
+    const int split = ph_split<KIND>(ph);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    // Left only by the jump below, so that every path into an item's wait
-    // has issued the same loads since that item's.
+    // The loop is left only after a whole round of D slots: once the last
+    // job has ended, the rest of the round multiplies dead items and
+    // refills with dead loads.  So every path to an item's wait has issued
+    // the same D-1 items since (an exit in mid-round would make the
+    // compiler's wait counting assume fewer and drain the ring).
+    bool done = false;
     for (;;) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
-        if (FMT == 0 || e.fmt == 0) eat_item_n<0>(e, ring[d], acc);
-        else eat_item_n<1>(e, ring[d], acc);
-        fetch_item_n(f, ring[d]);
-        fetch_adv_n(f);
-        if (f.left == 0) fetch_next_n(p, L, s, f, stop, false);
-        e.left = uni(e.left) - 1;
-        if (e.left == 0) {
-          if (e.pst) lds_st128(L.pbuf + e.pidx, __builtin_bit_cast(u32x4, acc));
-          acc = f32x4{0.f, 0.f, 0.f, 0.f};
-          MOE_JSTAMP(p, jc);
-          balance(L, ++jc);
-          if (!eat_next_n(p, L, s, e, stop, false)) goto drained;
+        if (FMT == 0 || e.fmt == 0) eat_item_n<0>(split, lg, ring[d], acc);
+        else eat_item_n<1>(split, lg, ring[d], acc);
+        fetch_item_n<FMT>(f, ring[d]);
+        fetch_adv_n<FMT>(f);
+        if (f.left == 0) fetch_next_n<FMT, KIND>(p, L, ph, f, kend);
+        if (!done) {
+          e.left = uni(e.left) - 1;
+          if (e.left == 0) {
+            if (e.pst) lds_st128(L.pbuf + e.pidx, __builtin_bit_cast(u32x4, acc));
+            acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            MOE_JSTAMP(p, jc);
+            balance(L, ++jc);
+            done = !eat_next_n<FMT, KIND>(p, L, ph, e, kend);
+          }
         }
       }
+      if (done) break;
     }
   }
-drained:
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the dead items' loads
   __builtin_amdgcn_s_setprio(0);
 }
@@ -1678,6 +1778,91 @@ __device__ inline void combine(const Params& p, const Lds& L, const Sched& s) {
 
 // ------------------------------------------------------------------ kernel
 
+__device__ __forceinline__ Sched make_sched(const Params& p, int G, int narrow) {
+  Sched s;
+  s.sh_tiles = p.n_shared ? p.Is / 8 : 0;
+  s.rt_tiles = p.I / 8;
+  s.G = G;
+  s.n_jobs = s.sh_tiles + (G - p.n_shared) * s.rt_tiles;
+  s.h0 = blockIdx.x * p.hs;
+  s.hc = uni(p.H) - s.h0 < uni(p.hs) ? uni(p.H) - s.h0 : uni(p.hs);
+  if (s.hc < 0) s.hc = 0;
+  s.nrt = (s.hc + 15) / 16;
+  s.nrt_p = uni(p.nrt_p);
+  s.wpt = uni(p.wpt);
+  s.narrow = narrow;
+  return s;
+}
+
+// The kernel-argument block (the kernel's one argument, at offset 0 of the
+// argument segment), through an opaque copy of its address: loads through
+// it are not merged with loads before this point.  Used between the stages
+// of the narrow path, so that argument values are loaded again where needed
+// instead of being held in scalar registers across the weight stream.
+typedef const __attribute__((address_space(4))) Params KArgs;
+__device__ __forceinline__ const Params& fresh_args() {
+  KArgs* q = (KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(q));
+  return *(const Params*)q;
+}
+
+// The narrow path after routing: up/gate stream, its reduction and the
+// second flag barrier, the down stream, the combine.
+template <int FMT>
+__device__ __forceinline__ void narrow_path(char* smem, int G, uint32_t epoch) {
+  const int wave = wave_id();
+  int jn = 0;  // jobs this wave has ended (for balance)
+  int nU;
+  {
+    const Params& p = fresh_args();
+    const Lds L = lds_map(smem, p);
+    const Sched s = make_sched(p, G, 1);
+    zero_partials(L, pu_floats(p.T, p.K, p.tpc));
+    nU = (int)blockIdx.x < s.n_jobs ? (s.n_jobs - 1 - (int)blockIdx.x) / p.ncu + 1 : 0;
+    build_jobs(p, L, s, nU);
+    PhaseN ph = {};
+    run_narrow<FMT, 1>(p, L, ph, 0, nU, jn);
+    MOE_WSTAMP(p, 0);
+  }
+  nU = uni(nU);
+  {
+    const Params& p = fresh_args();
+    const Lds L = lds_map(smem, p);
+    const Sched s = make_sched(p, G, 1);
+    __syncthreads();
+    MOE_STAMP(p, 4);
+    up_reduce_n(p, L, s);
+    publish(p, epoch + 2);
+    MOE_STAMP(p, 12);
+    zero_partials(L, (size_t)p.wpt * p.T * (p.K + 1) * p.pitch);
+    // down: wave w takes tile w % nrt_p of this CU's slice and K-blocks
+    // w / nrt_p + wpt*i of it
+    PhaseN ph;
+    ph.rt = wave % s.nrt_p;
+    ph.k0 = wave / s.nrt_p;
+    ph.lstep = 31 - __builtin_clz(s.wpt);
+    ph.hb = s.h0 + 16 * ph.rt;
+    ph.nlive = s.hc - 16 * ph.rt < 16 ? s.hc - 16 * ph.rt : 16;
+    ph.split = (ph.hb / 128 + 1) * 128 - ph.hb;  // a 16-row tile spans at most two scale block rows
+    ph.dnb = ph.nlive > 0 ? ((ph.hb + ph.nlive - 1) >> 7) - (ph.hb >> 7) : 0;
+    wait_all(p, epoch + 2);
+    MOE_STAMP(p, 5);
+    MOE_WSTAMP(p, 1);
+    run_narrow<FMT, 2>(p, L, ph, nU, ph.nlive > 0 ? nU + s.G : nU, jn);
+    MOE_WSTAMP(p, 2);
+    MOE_STAMP(p, 6);
+  }
+  {
+    const Params& p = fresh_args();
+    const Lds L = lds_map(smem, p);
+    const Sched s = make_sched(p, G, 1);
+    __syncthreads();
+    combine(p, L, s);
+    MOE_STAMP(p, 7);
+  }
+}
+
+
 // NARROW = 1: the narrow stream (per-wave partials); 0: the wide stream
 // (up to four 16-column tiles per group, owner reductions).
 template <int MODE, int FMT, int NARROW>
@@ -1732,49 +1917,11 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
     return;
   }
 
-  Sched s;
-  s.sh_tiles = p.n_shared ? p.Is / 8 : 0;
-  s.rt_tiles = p.I / 8;
-  s.G = G;
-  s.n_jobs = s.sh_tiles + (G - p.n_shared) * s.rt_tiles;
-  s.h0 = blockIdx.x * p.hs;
-  s.hc = uni(p.H) - s.h0 < uni(p.hs) ? uni(p.H) - s.h0 : uni(p.hs);
-  if (s.hc < 0) s.hc = 0;
-  s.nrt = (s.hc + 15) / 16;
-  s.nrt_p = uni(p.nrt_p);
-  s.wpt = uni(p.wpt);
-  s.narrow = NARROW;
-
-  // S3 / S4: the weight stream.  The second flag (every CU's mid is out) is
-  // raised after this CU's up/gate jobs and awaited before any down
-  // activation is loaded.
   if (NARROW) {
-    zero_partials(L, pu_floats(p.T, p.K, p.tpc));
-    __syncthreads();
-    It up = It{0, first_job(p, 0), 0, 0, 0};
-    settle(p, s, up);
-    int jn = 0;  // jobs this wave has ended (for balance)
-    run_narrow<FMT>(p, L, s, up, 2, jn);
-    MOE_WSTAMP(p, 0);
-    __syncthreads();
-    MOE_STAMP(p, 4);
-    up_reduce_n(p, L, s);
-    publish(p, epoch + 2);
-    MOE_STAMP(p, 12);
-    zero_partials(L, (size_t)p.wpt * p.T * (p.K + 1) * p.pitch);
-    It down = It{2, 0, wave % s.nrt_p, 0, 0};  // this wave's down tile
-    settle(p, s, down);
-    wait_all(p, epoch + 2);
-    MOE_STAMP(p, 5);
-    MOE_WSTAMP(p, 1);
-    run_narrow<FMT>(p, L, s, down, 3, jn);
-    MOE_WSTAMP(p, 2);
-    MOE_STAMP(p, 6);
-    __syncthreads();
-    combine(p, L, s);
-    MOE_STAMP(p, 7);
+    narrow_path<FMT>(smem, G, epoch);
     return;
   }
+  const Sched s = make_sched(p, G, 0);
   bool ok = true;
   int jc = 0;  // jobs ended
   Owned own;
