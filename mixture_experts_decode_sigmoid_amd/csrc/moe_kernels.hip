@@ -168,6 +168,9 @@ struct Lds {
   double* rb;        // [kWaves][E] router keys (aliases red and pbuf)
   double* rgs;       // [kWaves][64] group scores
   int32_t* rkept;    // [kWaves][64]
+  double* rcb;       // [kWaves][E] top-k candidates: key b
+  double* rcs;       // [kWaves][E] and score s
+  int32_t* rce;      // [kWaves][E] and expert
   float* pbuf;       // wide: down products [T*(K+1)][hs]; narrow: the per-wave partials (see lds_offsets)
   struct JobDesc* jd;  // narrow: job tables (see build_jobs)
 };
@@ -220,7 +223,9 @@ __host__ __device__ inline LdsOffsets lds_offsets(int T, int K, int E, int hs, i
   // the routing scratch (used before the stream) overlaps the job-end
   // partials and the down products (used in it)
   o.red = q;
-  const size_t rs = 8 * (size_t)kWaves * E + 8 * (size_t)kWaves * 64 + 4 * (size_t)kWaves * 64;
+  // routing scratch: rb, rgs, rkept, then the top-k candidates (b, s, e) per wave
+  const size_t rs = 8 * (size_t)kWaves * E + 8 * (size_t)kWaves * 64 + 4 * (size_t)kWaves * 64 +
+                    20 * (size_t)kWaves * E;
   size_t need;
   if (narrow) {
     o.pbuf = q;
@@ -275,6 +280,9 @@ __device__ inline Lds lds_map(char* base, const Params& p) {
   L.rb = (double*)(base + o.red);
   L.rgs = L.rb + (size_t)kWaves * p.E;
   L.rkept = (int32_t*)(L.rgs + (size_t)kWaves * 64);
+  L.rcb = (double*)(L.rkept + (size_t)kWaves * 64);
+  L.rcs = L.rcb + (size_t)kWaves * p.E;
+  L.rce = (int32_t*)(L.rcs + (size_t)kWaves * p.E);
   return L;
 }
 
@@ -427,6 +435,29 @@ __device__ __forceinline__ void wave_best(double& b, int& e) {
   e = second ? e1 : e0;
 }
 
+// Unsigned maximum over the wave (every lane gets it).
+template <int CTRL>
+__device__ __forceinline__ uint32_t umax_step(uint32_t v) {
+  const uint32_t o = (uint32_t)xlane<CTRL>((int)v);
+  return o > v ? o : v;
+}
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = umax_step<kDppXor1>(v);
+  v = umax_step<kDppXor2>(v);
+  v = umax_step<kDppHalfMirror>(v);
+  v = umax_step<kDppMirror>(v);
+  v = umax_step<kSwizzleXor16>(v);
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  return a > b ? a : b;
+}
+
+// Order-preserving 32-bit code of a float (larger float, larger code);
+// every code of a float is above 0, which marks "no candidate".
+__device__ __forceinline__ uint32_t ord32(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // Two largest values (t1 >= t2) of an aligned lane group, one exchange step.
 template <int CTRL>
 __device__ __forceinline__ void top2_step(double (&t1)[4], double (&t2)[4]) {
@@ -529,39 +560,66 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r) {
     }
   }
   MOE_STAMP(p, 14);
-  double ssum = 0.0;
-  int picks[kMaxTopK];
-  double pick_s[kMaxTopK];
+  // Top-k among the alive experts by (b desc, e asc), in two steps.
+  // (1) Rounded to fp32, keys keep their order (ties aside), so the k-th
+  // largest rounded key t is the rounding of the k-th largest exact key,
+  // and every expert whose rounded key is >= t holds all k winners.  t is
+  // found by rounds of wave maximum, each retiring every key equal to it.
+  uint32_t key[4];
 #pragma unroll
-  for (int k = 0; k < kMaxTopK; ++k) {
-    if (k < p.K) {
-      double bb = -INFINITY;
-      int be = 0x7fffffff;
+  for (int i = 0; i < 4; ++i) key[i] = alive[i] ? ord32((float)bv[i]) : 0u;
+  uint32_t t = 0u;
+  for (int cnt = 0; cnt < p.K;) {
+    uint32_t m = key[0] > key[1] ? key[0] : key[1];
+    m = m > key[2] ? m : key[2];
+    m = m > key[3] ? m : key[3];
+    t = wave_umax(m);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = lane + 64 * i;
-        if (alive[i] && key_before(bv[i], e, bb, be)) { bb = bv[i]; be = e; }
-      }
-      wave_best(bb, be);
-      // be is now uniform; its owner retires it
+    for (int i = 0; i < 4; ++i) {
+      const bool eq = key[i] == t;
+      cnt += __popcll(__ballot(eq));
+      if (eq) key[i] = 0u;
+    }
+    if (t == 0u) break;  // fewer alive experts than k (not reachable with validated shapes)
+  }
+  // (2) The candidates go to LDS in expert order; each is ranked exactly
+  // by (b desc, e asc) against all of them.
+  double* cb = L.rcb + (size_t)wave * p.E;
+  double* cs = L.rcs + (size_t)wave * p.E;
+  int32_t* ce = L.rce + (size_t)wave * p.E;
+  int nc = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (lane + 64 * i == be) alive[i] = false;
-      const double sp = readlane_d(pick4(sv, be >> 6), be & 63);
-      picks[k] = be;
-      pick_s[k] = sp;
-      ssum += sp;
+  for (int i = 0; i < 4; ++i) {
+    const bool c = alive[i] && ord32((float)bv[i]) >= t;
+    const unsigned long long bal = __ballot(c);
+    if (c) {
+      const int pos = nc + __popcll(bal & ((1ull << lane) - 1ull));
+      cb[pos] = bv[i];
+      cs[pos] = sv[i];
+      ce[pos] = lane + 64 * i;
+    }
+    nc += __popcll(bal);
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  double* ps = L.rgs + (size_t)wave * 64;  // the winners' s in pick order
+  for (int j = lane; j < nc; j += 64) {
+    const double bj = cb[j];
+    const int ej = ce[j];
+    int rank = 0;
+    for (int q = 0; q < nc; ++q) rank += key_before(cb[q], ce[q], bj, ej) ? 1 : 0;
+    if (rank < p.K) {
+      L.ids[r * p.K + rank] = ej;
+      ps[rank] = cs[j];
     }
   }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   MOE_STAMP(p, 15);
   if (lane == 0) {
-#pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k) {
-      if (k < p.K) {
-        L.ids[r * p.K + k] = picks[k];
-        L.w[r * p.K + k] = (float)(pick_s[k] / ssum * p.routed_scale);
-      }
-    }
+    double ssum = 0.0;
+    for (int k = 0; k < p.K; ++k) ssum += ps[k];
+    for (int k = 0; k < p.K; ++k) L.w[r * p.K + k] = (float)(ps[k] / ssum * p.routed_scale);
   }
 }
 
