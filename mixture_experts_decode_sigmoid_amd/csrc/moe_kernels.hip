@@ -1420,22 +1420,26 @@ __device__ __forceinline__ void run_phase(const Params& p, const Lds& L, const S
     if (e.it.phase >= stop) more = false;
     else eat_job(p, L, s, e);
   }
-  // The loop is left by a jump, so that every path into an item's wait has
-  // issued the same loads since that item's (a guarded body would let the
-  // compiler's wait counting assume skipped refills and wait for more).
-  if (more) {
+  // The loop is left only after a whole round of D slots (the rest of the
+  // round refills with dead loads), so every path to an item's wait has
+  // issued the same D-1 items since; an exit in mid-round would make the
+  // compiler's wait counting assume fewer and drain the ring.
+  bool done = !more;
+  if (!done) {
     for (;;) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
-        if (e.fmt == 0) eat_item<0>(e, ring[d], acc);
-        else eat_item<FMT>(e, ring[d], acc);
+        if (!done) {
+          if (e.fmt == 0) eat_item<0>(e, ring[d], acc);
+          else eat_item<FMT>(e, ring[d], acc);
+        }
         fetch_item(p, f, ring[d]);
         fetch_next(p, L, s, f, stop);
-        if (!eat_next(p, L, s, e, acc, jc, own, ok, stop)) goto drained;
+        if (!done) done = !eat_next(p, L, s, e, acc, jc, own, ok, stop);
       }
+      if (done) break;
     }
   }
-drained:
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the dead items' loads
   __builtin_amdgcn_s_setprio(0);
 }
