@@ -104,6 +104,9 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
   return __uint_as_float(c << 23);
 }
 
+// This thread's wave in the workgroup, as a scalar.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -334,52 +337,6 @@ __device__ inline double load_bias(const Params& p, int e) {
   return (double)((const float*)p.bias)[e];
 }
 
-// l[r][e] = sum_h x[r][h] * Wr[e][h]: lane l sums h = 8l + 512j + 0..7 in
-// order, then a fixed xor butterfly; one wave per (row, expert).  The loads
-// of up to 8 j are issued before their products are summed.
-__device__ inline void router_logits(const Params& p) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (wave >= kWaves) return;
-  for (int e = blockIdx.x; e < p.E; e += p.ncu) {
-    const uint16_t* wr = p.router_w + (size_t)e * p.H;
-    const double bias = load_bias(p, e);
-    for (int r = wave; r < p.T; r += kWaves) {
-      const uint16_t* xr = p.x + (size_t)r * p.H;
-      double acc = 0.0;
-      for (int h0 = 8 * lane; h0 < p.H; h0 += 512 * 8) {
-        u32x4 xv[8], wv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int h = h0 + 512 * j < p.H ? h0 + 512 * j : h0;
-          xv[j] = ld16(xr + h);
-          wv[j] = ld16(wr + h);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (h0 + 512 * j < p.H) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const uint32_t xa = xv[j][i], wa = wv[j][i];
-              acc = fma((double)bf16_bits_to_f32(xa & 0xffffu), (double)bf16_bits_to_f32(wa & 0xffffu), acc);
-              acc = fma((double)bf16_bits_to_f32(xa >> 16), (double)bf16_bits_to_f32(wa >> 16), acc);
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-      if (lane == 0) {
-        double s = 1.0 / (1.0 + exp(-acc));
-        double b = s + bias;
-        if (!isfinite(acc) || !isfinite(b)) set_err(p.err, kErrScore);
-        double* dst = p.scores + ((size_t)r * p.E + e) * 2;
-        dst[0] = s;
-        dst[1] = b;
-      }
-    }
-  }
-}
-
 // ------------------------------------------------------------------ S2 routing
 
 __device__ __forceinline__ bool key_before(double b1, int e1, double b2, int e2) {
@@ -456,6 +413,127 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
 __device__ __forceinline__ uint32_t ord32(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Sum over the wave in a fixed tree (the result is the same in every lane:
+// each step adds two equal-shaped partial sums, and fp addition commutes).
+__device__ __forceinline__ double wave_sum_d(double v) {
+  v += xlane_d<kDppXor1>(v);
+  v += xlane_d<kDppXor2>(v);
+  v += xlane_d<kDppHalfMirror>(v);
+  v += xlane_d<kDppMirror>(v);
+  v += xlane_d<kSwizzleXor16>(v);
+  return readlane_d(v, 0) + readlane_d(v, 32);
+}
+
+// l[r][e] = sum_h x[r][h] * Wr[e][h] for this CU's experts e = c, c+ncu, ..
+// and every row, in fp64 (bf16 products are exact).  Each dot is split into
+// 8 contiguous chunks of H/8, one per wave; lane l sums the 16-byte groups l
+// and l+64 of its chunk in order, the lanes are summed by a fixed tree and
+// the chunk sums in wave order.  Up to 4 dots' loads are issued before any
+// is summed.  Then s = sigmoid(l) and b = s + bias go to the workspace.
+__device__ inline void router_logits(const Params& p, const Lds& L) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int ch = p.H / kWaves, ngrp = ch >> 3;
+  const int g0 = lane < ngrp ? lane : ngrp - 1, g1 = lane + 64 < ngrp ? lane + 64 : g0;
+  const int nexp = p.E > (int)blockIdx.x ? (p.E - 1 - (int)blockIdx.x) / p.ncu + 1 : 0;
+  const int nd = nexp * p.T;
+  double* part = L.rb;  // [dot][wave]
+  for (int d0 = 0; d0 < nd; d0 += 4) {
+    u32x4 xv[4][2], wv[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d = d0 + j < nd ? d0 + j : nd - 1;
+      const int e = (int)blockIdx.x + (d / p.T) * p.ncu, r = d % p.T;
+      const uint16_t* xr = p.x + (size_t)r * p.H + (size_t)wave * ch;
+      const uint16_t* wr = p.router_w + (size_t)e * p.H + (size_t)wave * ch;
+      xv[j][0] = ld16(xr + 8 * g0);
+      wv[j][0] = ld16(wr + 8 * g0);
+      xv[j][1] = ld16(xr + 8 * g1);
+      wv[j][1] = ld16(wr + 8 * g1);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (d0 + j < nd) {
+        double acc = 0.0;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          if (q == 0 ? lane < ngrp : lane + 64 < ngrp) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t xa = xv[j][q][i], wa = wv[j][q][i];
+              acc = fma((double)bf16_bits_to_f32(xa & 0xffffu), (double)bf16_bits_to_f32(wa & 0xffffu), acc);
+              acc = fma((double)bf16_bits_to_f32(xa >> 16), (double)bf16_bits_to_f32(wa >> 16), acc);
+            }
+          }
+        }
+        acc = wave_sum_d(acc);
+        if (lane == 0) part[(d0 + j) * kWaves + wave] = acc;
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one dot's conversions at a time
+    }
+  }
+  __syncthreads();
+  for (int d = threadIdx.x; d < nd; d += kThreads) {
+    double l = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) l += part[d * kWaves + w];
+    const int e = (int)blockIdx.x + (d / p.T) * p.ncu, r = d % p.T;
+    const double s = 1.0 / (1.0 + exp(-l));
+    const double b = s + load_bias(p, e);
+    if (!isfinite(l) || !isfinite(b)) set_err(p.err, kErrScore);
+    double* dst = p.scores + ((size_t)r * p.E + e) * 2;
+    dst[0] = s;
+    dst[1] = b;
+  }
+}
+
+// The same logits with one wave per (row, expert): lane l sums h = 8l +
+// 512j + 0..7 in order, then a fixed xor butterfly.  The loads of up to 8 j
+// are issued before their products are summed.  Used from 8 rows up, where
+// every wave has rows of its own (and by the wide stream, whose register
+// budget has no room for the chunked form).
+__device__ inline void router_logits_rows(const Params& p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (wave >= kWaves) return;
+  for (int e = blockIdx.x; e < p.E; e += p.ncu) {
+    const uint16_t* wr = p.router_w + (size_t)e * p.H;
+    const double bias = load_bias(p, e);
+    for (int r = wave; r < p.T; r += kWaves) {
+      const uint16_t* xr = p.x + (size_t)r * p.H;
+      double acc = 0.0;
+      for (int h0 = 8 * lane; h0 < p.H; h0 += 512 * 8) {
+        u32x4 xv[8], wv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int h = h0 + 512 * j < p.H ? h0 + 512 * j : h0;
+          xv[j] = ld16(xr + h);
+          wv[j] = ld16(wr + h);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (h0 + 512 * j < p.H) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t xa = xv[j][i], wa = wv[j][i];
+              acc = fma((double)bf16_bits_to_f32(xa & 0xffffu), (double)bf16_bits_to_f32(wa & 0xffffu), acc);
+              acc = fma((double)bf16_bits_to_f32(xa >> 16), (double)bf16_bits_to_f32(wa >> 16), acc);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+      if (lane == 0) {
+        double s = 1.0 / (1.0 + exp(-acc));
+        double b = s + bias;
+        if (!isfinite(acc) || !isfinite(b)) set_err(p.err, kErrScore);
+        double* dst = p.scores + ((size_t)r * p.E + e) * 2;
+        dst[0] = s;
+        dst[1] = b;
+      }
+    }
+  }
 }
 
 // Two largest values (t1 >= t2) of an aligned lane group, one exchange step.
@@ -628,9 +706,89 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r) {
 // Distinct experts of the step in order of first use over u = r*K + slot
 // (group 0 = shared expert when present), each group's columns in ascending
 // u.  Needs L.ids; whole workgroup; ends synchronised.
+// Orders this wave's earlier LDS writes before its later LDS reads.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
+// gstart[g] = base + sum of gcnt over groups g0..g-1, for g0 <= g < G, by
+// one wave (64 groups per pass).
+__device__ inline void scan_gstart(const Lds& L, int g0, int G, int base) {
+  const int lane = threadIdx.x & 63;
+  for (int c0 = g0; c0 < G; c0 += 64) {
+    const int g = c0 + lane;
+    const int c = g < G ? L.gcnt[g] : 0;
+    int v = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(v, off, 64);
+      if (lane >= off) v += t;
+    }
+    if (g < G) L.gstart[g] = base + v - c;
+    base += __shfl(v, 63, 64);
+  }
+}
+
+// Column of use u = r*K + slot within its group: the rows using an expert,
+// in ascending order (a row picks an expert at most once).
+__device__ __forceinline__ int use_rank(const Lds& L, int e, int r) {
+  const uint32_t lo = L.rmask[2 * e], hi = L.rmask[2 * e + 1];
+  return r < 32 ? __popc(lo & ((1u << r) - 1u)) : __popc(lo) + __popc(hi & ((1u << (r - 32)) - 1u));
+}
+
 __device__ inline void build_groups(const Params& p, const Lds& L) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int U = p.T * p.K;
+  if (U <= 64) {
+    // one wave, one use per lane, no workgroup barriers
+    if (wave == 0) {
+      const bool valid = lane < U;
+      const int e = valid ? L.ids[lane] : 0, r = lane / p.K;
+      if (valid) {
+        L.first[e] = 0xffffffffu;
+        L.rmask[2 * e] = 0u;
+        L.rmask[2 * e + 1] = 0u;
+      }
+      wave_sync();
+      if (valid) {
+        atomicMin(&L.first[e], (uint32_t)lane);
+        atomicOr(&L.rmask[2 * e + (r >> 5)], 1u << (r & 31));
+      }
+      wave_sync();
+      const bool isf = valid && L.first[e] == (uint32_t)lane;
+      const unsigned long long m = __ballot(isf);
+      const int G = p.n_shared + __popcll(m);
+      if (isf) {
+        const int g = p.n_shared + __popcll(m & ((1ull << lane) - 1ull));
+        L.egrp[e] = g;
+        L.gexp[g] = e;
+        L.gcnt[g] = __popc(L.rmask[2 * e]) + __popc(L.rmask[2 * e + 1]);
+      }
+      if (lane == 0) {
+        L.misc[0] = G;
+        if (p.n_shared) {
+          L.gexp[0] = -1;
+          L.gcnt[0] = p.T;
+          L.gstart[0] = 0;
+        }
+      }
+      wave_sync();
+      scan_gstart(L, p.n_shared, G, p.n_shared ? p.T : 0);
+      wave_sync();
+      if (p.n_shared && lane < p.T) {
+        L.cols[lane] = lane * 16 + p.K;
+        L.cgrp[lane] = 0;
+      }
+      if (valid) {
+        const int g = L.egrp[e], c = L.gstart[g] + use_rank(L, e, r);
+        L.cols[c] = r * 16 + (lane - r * p.K);
+        L.cgrp[c] = g;
+      }
+    }
+    __syncthreads();
+    return;
+  }
   for (int e = tid; e < p.E; e += kThreads) {
     L.first[e] = 0xffffffffu;
     L.rmask[2 * e] = 0u;
@@ -667,19 +825,16 @@ __device__ inline void build_groups(const Params& p, const Lds& L) {
     __syncthreads();
   }
   const int G = base;
-  if (tid == 0) {
-    L.misc[0] = G;
-    int s = 0;
-    if (p.n_shared) {
-      L.gexp[0] = -1;
-      L.gcnt[0] = p.T;
-      L.gstart[0] = 0;
-      s = p.T;
+  if (wave == 0) {
+    if (lane == 0) {
+      L.misc[0] = G;
+      if (p.n_shared) {
+        L.gexp[0] = -1;
+        L.gcnt[0] = p.T;
+        L.gstart[0] = 0;
+      }
     }
-    for (int g = p.n_shared; g < G; ++g) {
-      L.gstart[g] = s;
-      s += L.gcnt[g];
-    }
+    scan_gstart(L, p.n_shared, G, p.n_shared ? p.T : 0);
   }
   __syncthreads();
   if (p.n_shared)
@@ -689,12 +844,9 @@ __device__ inline void build_groups(const Params& p, const Lds& L) {
     }
   for (int u = tid; u < U; u += kThreads) {
     const int e = L.ids[u], r = u / p.K, slot = u - r * p.K;
-    const uint32_t lo = L.rmask[2 * e], hi = L.rmask[2 * e + 1];
-    const int rank = (r < 32) ? __popc(lo & ((1u << r) - 1u))
-                              : __popc(lo) + __popc(hi & ((1u << (r - 32)) - 1u));
-    const int g = L.egrp[e];
-    L.cols[L.gstart[g] + rank] = r * 16 + slot;
-    L.cgrp[L.gstart[g] + rank] = g;
+    const int g = L.egrp[e], c = L.gstart[g] + use_rank(L, e, r);
+    L.cols[c] = r * 16 + slot;
+    L.cgrp[c] = g;
   }
   __syncthreads();
 }
@@ -714,7 +866,6 @@ __device__ inline void build_groups(const Params& p, const Lds& L) {
 // flight.  (An LDS ring fed by LDS-DMA reached a lower and less steady
 // share of HBM bandwidth.)
 
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Wave-uniform loop state, re-asserted as uniform: the compiler's uniformity
 // analysis loses track of it across the stream loops (asm results, loop
@@ -1942,7 +2093,8 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   const uint32_t epoch = (uint32_t)__builtin_amdgcn_readfirstlane(L.misc[1]);
 
   // S0: router logits of this CU's experts, published for every CU
-  router_logits(p);
+  if (NARROW && p.T < kWaves) router_logits(p, L);
+  else router_logits_rows(p);
   publish(p, epoch + 1);
   MOE_STAMP(p, 1);
   if (MODE != kModeForward && blockIdx.x != 0) return;
