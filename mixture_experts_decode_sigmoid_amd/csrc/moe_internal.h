@@ -40,8 +40,7 @@ struct Params {
   int nrt_p;       // 16-row down tiles of a CU's slice, rounded up to 1, 2 or 4
   int wpt;         // waves per down tile (8 / nrt_p); they split its K-blocks
   int pitch;       // floats per (row, slot) line of the down products (16 * tiles)
-  int tpc;         // up/gate tiles of one group a CU can hold
-  int njd;         // narrow: job table entries
+  int qcap;        // narrow: up/gate job entries of a CU (its share of the most jobs a batch can have)
   // inputs
   const uint16_t* x;
   const uint16_t* router_w;

@@ -119,28 +119,54 @@ __device__ __forceinline__ T ldg(const void* p) {
 }
 __device__ __forceinline__ u32x4 ld16(const void* p) { return ldg<u32x4>(p); }
 
+// A store other CUs read after a flag barrier: agent scope, written through
+// to the device's point of coherence, so that raising the flag needs no
+// writeback of this XCD's L2 (see publish).
+template <class T>
+__device__ __forceinline__ void st_agent(void* a, T v) {
+  __hip_atomic_store((__attribute__((address_space(1))) T*)a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// a * b for per-lane index arithmetic in the streams, kept apart from a
+// following add: fused, the product becomes a 64-bit multiply-add whose
+// unused high addend half may share a register with an item in flight, and
+// reading it would wait for that load.
+__device__ __forceinline__ uint32_t lmul(uint32_t a, uint32_t b) {
+  uint32_t t = a * b;
+  asm("" : "+v"(t));
+  return t;
+}
+
 // Optional per-CU phase stamps (build with -DMOE_TIMELINE): thread 0 of each
 // workgroup writes s_memrealtime (100 MHz) at phase boundaries into
 // p.timeline[blockIdx.x * 64 + i]; MOE_WSTAMP(p, k) has lane 0 of every wave
 // write slot 16 + 8k + wave.
 #ifdef MOE_TIMELINE
+// (global-address-space stores: a generic store would also count on the
+// LDS counter, and the next LDS wait would wait for it)
+#define MOE_TL(p, i) (*(__attribute__((address_space(1))) uint64_t*)((p).timeline + blockIdx.x * 64 + (i)))
 #define MOE_STAMP(p, i)                                                                  \
   do {                                                                                   \
-    if (threadIdx.x == 0 && (p).timeline)                                                \
-      (p).timeline[blockIdx.x * 64 + (i)] = __builtin_amdgcn_s_memrealtime();            \
+    if (threadIdx.x == 0 && (p).timeline) MOE_TL(p, i) = __builtin_amdgcn_s_memrealtime(); \
   } while (0)
 #define MOE_WSTAMP(p, k)                                                                 \
   do {                                                                                   \
     if ((threadIdx.x & 63) == 0 && (p).timeline)                                         \
-      (p).timeline[blockIdx.x * 64 + 16 + 8 * (k) + (threadIdx.x >> 6)] =                \
-          __builtin_amdgcn_s_memrealtime();                                              \
+      MOE_TL(p, 16 + 8 * (k) + (threadIdx.x >> 6)) = __builtin_amdgcn_s_memrealtime();  \
   } while (0)
 #define MOE_JSTAMP(p, jc)                                                                \
   do {                                                                                   \
     if (threadIdx.x == 0 && (p).timeline && (jc) < 24)                                   \
-      (p).timeline[blockIdx.x * 64 + 40 + (jc)] = __builtin_amdgcn_s_memrealtime();     \
+      MOE_TL(p, 40 + (jc)) = __builtin_amdgcn_s_memrealtime();                           \
+  } while (0)
+#define MOE_TVAL(p, i, v)                                                                \
+  do {                                                                                   \
+    if (threadIdx.x == 0 && (p).timeline) MOE_TL(p, i) = (v);                            \
   } while (0)
 #else
+#define MOE_TVAL(p, i, v) \
+  do {                    \
+  } while (0)
 #define MOE_JSTAMP(p, jc) \
   do {                    \
   } while (0)
@@ -175,7 +201,11 @@ struct Lds {
   double* rcs;       // [kWaves][E] and score s
   int32_t* rce;      // [kWaves][E] and expert
   float* pbuf;       // wide: down products [T*(K+1)][hs]; narrow: the per-wave partials (see lds_offsets)
-  struct JobDesc* jd;  // narrow: job tables (see build_jobs)
+  struct JobDesc* jd;  // narrow: job descriptors (this CU's up/gate jobs, then down jobs)
+  uint32_t* wcnt;    // narrow: [kPuWin] chunks of the job in each partial window that have ended
+  uint32_t* wgen;    // narrow: [kPuWin] jobs summed out of each window
+  uint32_t* ccnt;    // narrow: up/gate chunks claimed by this CU's waves
+  uint32_t* cfifo;   // narrow: [kWaves][8] each wave's claimed chunks, fetch side to multiplying side
 };
 
 __host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -186,27 +216,29 @@ __host__ __device__ inline int red_tiles(int T) { return T > 16 ? kMaxRows / 16 
 __host__ __device__ inline int red_slots(int T) { return T > 16 ? 2 : 4; }
 constexpr size_t kRedTileBytes = 16 * (size_t)kWaves * 64;  // one tile: [wave][lane] f32x4
 
-// Narrow layout (batches of at most 16 rows): no reduction runs inside the
-// weight stream.  Every wave keeps its partial tiles apart in LDS and they
-// are summed over the waves, in wave order, after the phase:
-//   up/gate  Pu[w][col * tpc + t][16]  (w = 0..7; col = the group's column
-//            index in the column table, t = the tile's index among the CU's
-//            tiles of that group; 16 rows: 8 gate then 8 up)
+// Narrow layout (batches of at most 16 rows): every wave keeps its partial
+// tiles apart in LDS, and they are summed over the waves in wave order:
+//   up/gate  Pu[win][w][col][16], win = local job mod kPuWin (w = 0..7, the
+//            job's K-phase; col < T, the job's column; 16 rows: 8 gate then
+//            8 up), summed by the wave that ends the job's last chunk
 //   down     Pd[kp][row][slot][pitch]  (kp = 0..wpt-1, the K-phase of the
-//            waves that share a 16-row down tile; h along the slice)
-// Pu and Pd share one region (Pu is consumed before Pd is written), which
-// also holds the routing scratch before the stream.  The wide layout keeps
+//            waves that share a 16-row down tile; h along the slice),
+//            summed in the combine
+// Pu and Pd share one region (Pu is done with before Pd is written), which
+// also holds the routing scratch before the stream.  The job descriptors
+// (qcap up/gate entries, then one down job per group) sit before it.  The wide layout keeps
 // job-end partial slots summed by an owner wave, and one copy of the down
 // products [row][slot][hs].
+constexpr int kPuWin = 8;
 struct LdsOffsets {
-  size_t ids, w, first, egrp, rmask, gexp, gcnt, gstart, cols, cgrp, misc, ctl, jd, red, pbuf, total;
+  size_t ids, w, first, egrp, rmask, gexp, gcnt, gstart, cols, cgrp, misc, ctl, wst, jd, red, pbuf, total;
 };
 constexpr size_t kJobDescBytes = 48;
 
-__host__ __device__ inline size_t pu_floats(int T, int K, int tpc) { return (size_t)kWaves * T * (K + 1) * tpc * 16; }
+__host__ __device__ inline size_t pu_floats(int T) { return (size_t)kPuWin * kWaves * T * 16; }
 
-__host__ __device__ inline LdsOffsets lds_offsets(int T, int K, int E, int hs, int narrow, int tpc, int wpt,
-                                                  int pitch, int njd) {
+__host__ __device__ inline LdsOffsets lds_offsets(int T, int K, int E, int hs, int narrow, int wpt, int pitch,
+                                                  int qcap) {
   LdsOffsets o;
   size_t q = 0;
   const int uses = T * K, gmax = 1 + T * K;
@@ -222,7 +254,8 @@ __host__ __device__ inline LdsOffsets lds_offsets(int T, int K, int E, int hs, i
   o.cgrp = q; q = align_up(q + 4 * (size_t)T * (K + 1), 16);
   o.misc = q; q = align_up(q + 4 * 32, 16);
   o.ctl = q; q = align_up(q + 4 * 64, 16);
-  o.jd = q; q = align_up(q + (narrow ? kJobDescBytes * (size_t)njd : 0), 16);
+  o.wst = q; q = align_up(q + 8 * kPuWin + 16 + 4 * kWaves * 8, 16);
+  o.jd = q; q = align_up(q + (narrow ? kJobDescBytes * (size_t)(qcap + gmax) : 0), 16);
   // the routing scratch (used before the stream) overlaps the job-end
   // partials and the down products (used in it)
   o.red = q;
@@ -232,7 +265,7 @@ __host__ __device__ inline LdsOffsets lds_offsets(int T, int K, int E, int hs, i
   size_t need;
   if (narrow) {
     o.pbuf = q;
-    const size_t pu = 4 * pu_floats(T, K, tpc);
+    const size_t pu = 4 * pu_floats(T);
     const size_t pd = 4 * (size_t)wpt * T * (K + 1) * pitch;
     need = pu > pd ? pu : pd;
   } else {
@@ -250,20 +283,18 @@ size_t stream_geometry(Params& p, int narrow) {
   p.nrt_p = nrt <= 1 ? 1 : nrt <= 2 ? 2 : 4;
   p.wpt = kWaves / p.nrt_p;
   p.pitch = 16 * nrt;
-  const int tiles = (p.I > p.Is ? p.I : p.Is) / 8;
-  p.tpc = (tiles + p.ncu - 1) / p.ncu;
   p.narrow = narrow;
-  // job tables: this CU's up/gate jobs (at most a share of the largest job
-  // count the batch can have) and one down job per group
+  // up/gate job entries: a CU's share of the largest job count the batch
+  // can have
   const int gmax = 1 + (p.E < p.T * p.K ? p.E : p.T * p.K);
   const int sh_tiles = p.n_shared ? p.Is / 8 : 0;
   const long jobs = sh_tiles + (long)(gmax - 1) * (p.I / 8);
-  p.njd = (int)((jobs + p.ncu - 1) / p.ncu) + gmax;
-  return lds_offsets(p.T, p.K, p.E, p.hs, p.narrow, p.tpc, p.wpt, p.pitch, p.njd).total;
+  p.qcap = (int)((jobs + p.ncu - 1) / p.ncu);
+  return lds_offsets(p.T, p.K, p.E, p.hs, p.narrow, p.wpt, p.pitch, p.qcap).total;
 }
 
 __device__ inline Lds lds_map(char* base, const Params& p) {
-  LdsOffsets o = lds_offsets(p.T, p.K, p.E, p.hs, p.narrow, p.tpc, p.wpt, p.pitch, p.njd);
+  LdsOffsets o = lds_offsets(p.T, p.K, p.E, p.hs, p.narrow, p.wpt, p.pitch, p.qcap);
   Lds L;
   L.ids = (int32_t*)(base + o.ids);
   L.w = (float*)(base + o.w);
@@ -278,6 +309,10 @@ __device__ inline Lds lds_map(char* base, const Params& p) {
   L.misc = (int32_t*)(base + o.misc);
   L.ctl = (uint32_t*)(base + o.ctl);
   L.jd = (JobDesc*)(base + o.jd);
+  L.wcnt = (uint32_t*)(base + o.wst);
+  L.wgen = L.wcnt + kPuWin;
+  L.ccnt = L.wgen + kPuWin;
+  L.cfifo = L.ccnt + 4;
   L.red = (float*)(base + o.red);
   L.pbuf = (float*)(base + o.pbuf);
   L.rb = (double*)(base + o.red);
@@ -291,15 +326,17 @@ __device__ inline Lds lds_map(char* base, const Params& p) {
 
 // ------------------------------------------------------------------ flags
 
-// Raise this CU's flag to `value` after all of the workgroup's prior global
-// stores: the workgroup meets (each wave's stores complete first), then one
-// thread releases at agent scope and stores the flag.
+// Raise this CU's flag to `value` after the workgroup's prior stores that
+// other CUs read.  Those stores are agent-scope (st_agent), so once each
+// wave has waited for its own stores to complete they are visible device
+// wide: the workgroup meets and one thread stores the flag, with no
+// writeback of the L2 (an agent-scope release fence would write back the
+// whole XCD's L2, and with every CU of an XCD doing so at once that costs
+// microseconds).
 __device__ inline void publish(const Params& p, uint32_t value) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __hip_atomic_store(&p.flags[blockIdx.x], value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (threadIdx.x == 0) __hip_atomic_store(&p.flags[blockIdx.x], value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // One wave polls every CU's flag until all have reached `target`
@@ -483,8 +520,8 @@ __device__ inline void router_logits(const Params& p, const Lds& L) {
     const double b = s + load_bias(p, e);
     if (!isfinite(l) || !isfinite(b)) set_err(p.err, kErrScore);
     double* dst = p.scores + ((size_t)r * p.E + e) * 2;
-    dst[0] = s;
-    dst[1] = b;
+    st_agent<uint64_t>(dst, __builtin_bit_cast(uint64_t, s));
+    st_agent<uint64_t>(dst + 1, __builtin_bit_cast(uint64_t, b));
   }
 }
 
@@ -529,8 +566,8 @@ __device__ inline void router_logits_rows(const Params& p) {
         double b = s + bias;
         if (!isfinite(acc) || !isfinite(b)) set_err(p.err, kErrScore);
         double* dst = p.scores + ((size_t)r * p.E + e) * 2;
-        dst[0] = s;
-        dst[1] = b;
+        st_agent<uint64_t>(dst, __builtin_bit_cast(uint64_t, s));
+        st_agent<uint64_t>(dst + 1, __builtin_bit_cast(uint64_t, b));
       }
     }
   }
@@ -1117,9 +1154,10 @@ __device__ inline void group_cols(const Params& p, const Lds& L, int g, int& nco
 // Activation offset (elements) of column code `code` for lane group lg:
 // x rows for up/gate, mid lines for down.
 __device__ __forceinline__ uint32_t act_offset(const Params& p, int kind, int code, int lg) {
-  return (kind == 1 ? (uint32_t)(code >> 4) * (uint32_t)p.H
-                    : ((uint32_t)(code >> 4) * (uint32_t)(p.K + 1) + (uint32_t)(code & 15)) * (uint32_t)p.mid_ld) +
-         32u * (uint32_t)lg;
+  const uint32_t t = kind == 1 ? lmul((uint32_t)(code >> 4), (uint32_t)p.H)
+                               : lmul(lmul((uint32_t)(code >> 4), (uint32_t)(p.K + 1)) + (uint32_t)(code & 15),
+                                      (uint32_t)p.mid_ld);
+  return t + 32u * (uint32_t)lg;
 }
 
 // One item in registers.
@@ -1608,14 +1646,14 @@ __device__ __forceinline__ void run_phase(const Params& p, const Lds& L, const S
 struct JobDesc {
   uint64_t wb;        // weights of the job's row 0 (up/gate: gate row 8t; down: the expert's W_down)
   uint64_t sb;        // block scales of that row (FP8 up/gate: its 128-row block row; MXFP4: its row)
-  uint32_t rowbytes;  // weight bytes per row
+  uint32_t tile;      // up/gate: the 8-intermediate tile
   uint32_t jump;      // up/gate: rows between lane row 7 (gate) and lane row 8 (up), minus one
   uint32_t shi;       // FP8 up/gate: scale bytes from the gate rows' block row to the up rows'; MXFP4: scale bytes per row
   int32_t nkb;        // K-blocks
   int32_t fmt;        // 0 FP8, 1 MXFP4
   int32_t ncols;      // the group's columns
   int32_t cbase;      // its first column in the column table
-  int32_t pslot;      // up/gate: partial slot of its column 0
+  int32_t spare;
 };
 static_assert(sizeof(JobDesc) == 48, "three 16-byte LDS reads");
 
@@ -1629,82 +1667,105 @@ __device__ inline JobDesc read_desc(const Lds& L, int k) {
   JobDesc d;
   d.wb = ((uint64_t)(uint32_t)uni((int)a[1]) << 32) | (uint32_t)uni((int)a[0]);
   d.sb = ((uint64_t)(uint32_t)uni((int)a[3]) << 32) | (uint32_t)uni((int)a[2]);
-  d.rowbytes = (uint32_t)uni((int)b[0]);
+  d.tile = (uint32_t)uni((int)b[0]);
   d.jump = (uint32_t)uni((int)b[1]);
   d.shi = (uint32_t)uni((int)b[2]);
   d.nkb = uni((int)b[3]);
   d.fmt = uni((int)c[0]);
   d.ncols = uni((int)c[1]);
   d.cbase = uni((int)c[2]);
-  d.pslot = uni((int)c[3]);
+  d.spare = 0;
   return d;
 }
 
-// Job tables of this CU: its up/gate jobs (shared tiles, then routed tiles,
-// dealt round-robin over CUs) at 0..nU-1, then one down job per group at
-// nU + g.  Whole workgroup; ends synchronised.
-__device__ inline void build_jobs(const Params& p, const Lds& L, const Sched& s, int nU) {
+// The descriptor of an up/gate job (tile `tile` of the expert's 8-row gate
+// and up tiles) or of a down job (the expert's whole W_down).
+__device__ inline JobDesc make_desc(const Params& p, bool up, bool sh, int e, int tile, int ncols, int cbase) {
   const size_t H = p.H, I = p.I;
-  for (int k = threadIdx.x; k < nU + s.G; k += kThreads) {
-    JobDesc d;
-    const bool up = k < nU;
-    int g, tile = 0;
+  JobDesc d;
+  const int iexp = sh ? p.Is : p.I;
+  const int kdim = up ? p.H : iexp;
+  d.fmt = sh ? 0 : p.routed_fmt;
+  d.nkb = kdim / 128;
+  d.ncols = ncols;
+  d.cbase = cbase;
+  d.spare = 0;
+  d.jump = up ? iexp - 8 : 0;
+  d.tile = (uint32_t)tile;
+  const uint8_t* w;
+  const uint8_t* S;
+  if (d.fmt == 0) {
+    if (sh) {
+      w = up ? p.sh_wgu : p.sh_wd;
+      S = (const uint8_t*)(up ? p.sh_sgu : p.sh_sd);
+    } else {
+      w = up ? p.wgu + (size_t)e * 2 * I * H : p.wd + (size_t)e * H * I;
+      S = up ? (const uint8_t*)p.sgu + 4 * (size_t)e * (2 * I / 128) * (H / 128)
+             : (const uint8_t*)p.sd + 4 * (size_t)e * (H / 128) * (I / 128);
+    }
     if (up) {
-      const int j = (int)blockIdx.x + k * p.ncu;
-      if (j < s.sh_tiles) {
-        g = 0;
-        tile = j;
-      } else {
-        g = p.n_shared + (j - s.sh_tiles) / s.rt_tiles;
-        tile = (j - s.sh_tiles) % s.rt_tiles;
-      }
+      const int nb_lo = (8 * tile) / 128, nb_hi = (iexp + 8 * tile) / 128;
+      w += (size_t)8 * tile * kdim;
+      S += 4 * (size_t)nb_lo * d.nkb;
+      d.shi = 4u * (uint32_t)((nb_hi - nb_lo) * d.nkb);
     } else {
-      g = k - nU;
+      d.shi = 0;
     }
-    const bool sh = shared_group(p, g);
-    const int e = sh ? 0 : L.gexp[g];
-    const int iexp = sh ? p.Is : p.I;
-    const int kdim = up ? p.H : iexp;
-    d.fmt = sh ? 0 : p.routed_fmt;
-    d.nkb = kdim / 128;
-    d.ncols = sh ? p.T : L.gcnt[g];
-    d.cbase = sh ? 0 : L.gstart[g];
-    d.pslot = up ? d.cbase * p.tpc + tile / p.ncu : 0;
-    d.jump = up ? iexp - 8 : 0;
-    const uint8_t* w;
-    const uint8_t* S;
-    if (d.fmt == 0) {
-      d.rowbytes = kdim;
-      if (sh) {
-        w = up ? p.sh_wgu : p.sh_wd;
-        S = (const uint8_t*)(up ? p.sh_sgu : p.sh_sd);
-      } else {
-        w = up ? p.wgu + (size_t)e * 2 * I * H : p.wd + (size_t)e * H * I;
-        S = up ? (const uint8_t*)p.sgu + 4 * (size_t)e * (2 * I / 128) * (H / 128)
-               : (const uint8_t*)p.sd + 4 * (size_t)e * (H / 128) * (I / 128);
-      }
-      if (up) {
-        const int nb_lo = (8 * tile) / 128, nb_hi = (iexp + 8 * tile) / 128;
-        w += (size_t)8 * tile * kdim;
-        S += 4 * (size_t)nb_lo * d.nkb;
-        d.shi = 4u * (uint32_t)((nb_hi - nb_lo) * d.nkb);
-      } else {
-        d.shi = 0;
-      }
-    } else {
-      d.rowbytes = kdim / 2;
-      d.shi = kdim / 32;
-      w = up ? p.wgu + (size_t)e * 2 * I * (H / 2) : p.wd + (size_t)e * H * (I / 2);
-      S = up ? (const uint8_t*)p.sgu + (size_t)e * 2 * I * (H / 32) : (const uint8_t*)p.sd + (size_t)e * H * (I / 32);
-      if (up) {
-        w += (size_t)8 * tile * d.rowbytes;
-        S += (size_t)8 * tile * d.shi;
-      }
+  } else {
+    d.shi = kdim / 32;
+    w = up ? p.wgu + (size_t)e * 2 * I * (H / 2) : p.wd + (size_t)e * H * (I / 2);
+    S = up ? (const uint8_t*)p.sgu + (size_t)e * 2 * I * (H / 32) : (const uint8_t*)p.sd + (size_t)e * H * (I / 32);
+    if (up) {
+      w += (size_t)8 * tile * (kdim / 2);
+      S += (size_t)8 * tile * d.shi;
     }
-    d.wb = (uint64_t)w;
-    d.sb = (uint64_t)S;
-    L.jd[k] = d;
   }
+  d.wb = (uint64_t)w;
+  d.sb = (uint64_t)S;
+  return d;
+}
+
+// Up/gate job j of the step: the shared tiles, then rt_tiles tiles per
+// routed group.  Sets its group and tile.
+__device__ __forceinline__ void up_job(const Params& p, const Sched& s, int j, int& g, int& tile) {
+  if (j < s.sh_tiles) {
+    g = 0;
+    tile = j;
+  } else {
+    g = p.n_shared + (j - s.sh_tiles) / s.rt_tiles;
+    tile = (j - s.sh_tiles) % s.rt_tiles;
+  }
+}
+
+// Up/gate jobs of a narrow call: CU c takes jobs c + q*ncu (local job q),
+// as in the wide stream.  Inside the CU a job is cut into chunks, one per
+// K-phase w (K-blocks w + 8i, the blocks wave w takes in the wide stream),
+// and the waves claim chunks in order from an LDS counter.  A chunk's
+// partial is the same sum whichever wave forms it, so the job's sum over its
+// K-phases in order does not depend on which wave did what, and waves that
+// stream faster take more chunks.
+
+// The job tables of a narrow call: this CU's up/gate jobs at 0..nU-1 and
+// one down job per group at qcap + g.  Whole workgroup (plain per-thread
+// LDS accesses); ends synchronised.
+__device__ inline void build_jobs(const Params& p, const Lds& L, const Sched& s, int nU) {
+  for (int k = threadIdx.x; k < p.qcap + s.G; k += kThreads) {
+    if (k < nU) {
+      int g, tile;
+      up_job(p, s, (int)blockIdx.x + k * p.ncu, g, tile);
+      const bool sh = shared_group(p, g);
+      L.jd[k] = make_desc(p, true, sh, sh ? 0 : L.gexp[g], tile, sh ? p.T : L.gcnt[g], sh ? 0 : L.gstart[g]);
+    } else if (k >= p.qcap) {
+      const int g = k - p.qcap;
+      const bool sh = shared_group(p, g);
+      L.jd[k] = make_desc(p, false, sh, sh ? 0 : L.gexp[g], 0, sh ? p.T : L.gcnt[g], sh ? 0 : L.gstart[g]);
+    }
+  }
+  if (threadIdx.x < kPuWin) {
+    L.wcnt[threadIdx.x] = 0u;
+    L.wgen[threadIdx.x] = 0u;
+  }
+  if (threadIdx.x == 0) *L.ccnt = 0u;
   __syncthreads();
 }
 
@@ -1718,6 +1779,7 @@ struct PhaseN {
   int split;      // FP8: MFMA output rows (4*lg + q) below it take the first scale block row
   int dnb;        // FP8 down: block rows between the tile's first and last live row (0 or 1)
   int rt;         // down: this wave's tile
+  int nw;         // up/gate: waves with items (min(K-blocks, 8))
 };
 template <int KIND>
 __device__ __forceinline__ int ph_k0(const PhaseN& ph) { return KIND == 1 ? wave_id() : ph.k0; }
@@ -1734,7 +1796,9 @@ __device__ __forceinline__ int job_items(const PhaseN& ph, int nkb) {
 
 // The fetch side: byte offsets of this lane's next item from uniform bases.
 struct FetchN {
-  int k;                         // next job to set up
+  int k;                         // next job to set up (down)
+  int nch;                       // up/gate: chunks claimed by this wave
+  int cnt;                       // items fetched so far
   int left;                      // items left in the job (large once past the phase)
   int nstep;                     // K-blocks per item step (0 once past the phase)
   int fmt;                       // 0 FP8, 1 MXFP4
@@ -1757,57 +1821,131 @@ __device__ __forceinline__ int lane_code(const Lds& L, const JobDesc& d) {
   return (int)lds_ld32(L.cols + d.cbase + (col < d.ncols ? col : d.ncols - 1));
 }
 
-// Moves the fetch side to the next job of [f.k, kend) with items for this
-// wave, or past the end (dead items: 16 bytes of x, never multiplied).
+// Sets the fetch side to job descriptor d, whose first item is this wave's
+// K-block k0; `code` is this lane's column (row*16 + slot), n its items.
+template <int FMT, int KIND>
+__device__ __forceinline__ void fetch_from_desc(const Params& p, const PhaseN& ph, FetchN& f, const JobDesc& d, int k0,
+                                                int n, int code) {
+  const int lane = threadIdx.x & 63, lg = lane >> 4, row = lane & 15;
+  const int fmt = FMT == 0 ? 0 : d.fmt;
+  const uint32_t kb = fmt ? 64u : 128u, lb = fmt ? 16u : 32u;
+  const uint32_t lrow = KIND == 1 ? (row < 8 ? row : row + d.jump) : ph.hb + (row < ph.nlive ? row : ph.nlive - 1);
+  f.wb = (const uint8_t*)d.wb;
+  f.wo = lmul(lrow, (uint32_t)(d.nkb * (fmt ? 64 : 128))) + (uint32_t)k0 * kb + (uint32_t)lg * lb;
+  if (fmt == 0) {
+    if (KIND == 1) {
+      f.sb = (const uint8_t*)d.sb;
+      f.so = (lane < 32 ? 0u : d.shi) + 4u * (uint32_t)k0;
+    } else {
+      f.sb = (const uint8_t*)d.sb + 4 * (size_t)(ph.hb >> 7) * d.nkb;
+      f.so = (lane < 32 ? 0u : 4u * (uint32_t)(ph.dnb * d.nkb)) + 4u * (uint32_t)k0;
+    }
+  } else {
+    f.sb = (const uint8_t*)d.sb;
+    f.so = lmul(lrow, d.shi) + 4u * (uint32_t)k0;
+  }
+  f.ao = 2 * act_offset(p, KIND, code, lg) + 256u * (uint32_t)k0;
+  f.fmt = fmt;
+  f.nstep = 1 << ph_lstep<KIND>(ph);
+  f.left = n;
+}
+
+// Past the last job: dead items load from the start of x (weights and
+// scales) and of the phase's own activations, and are never multiplied (f.ab
+// stays: a split fill's items still take their activations from it).
+// (The fields are stored in the order fetch_from_desc stores them: the
+// compiler merges the two paths' stores pairwise, and pairs of different
+// fields would leave the fetch side in scratch memory.)
+__device__ __forceinline__ void fetch_dead(const Params& p, FetchN& f) {
+  f.wb = (const uint8_t*)arg_ptr(p.x);
+  f.wo = 0;
+  f.sb = (const uint8_t*)arg_ptr(p.x);
+  f.so = 0;
+  f.ao = 0;
+  f.fmt = 0;
+  f.nstep = 0;
+  f.left = 1 << 30;
+}
+
+// Down: moves the fetch side to the next job of [f.k, kend) with items for
+// this wave, or past the end.
 template <int FMT, int KIND>
 __device__ inline void fetch_next_n(const Params& p, const Lds& L, const PhaseN& ph, FetchN& f, int kend) {
-  const int lane = threadIdx.x & 63, lg = lane >> 4, row = lane & 15;
-  const int k0 = ph_k0<KIND>(ph);
   for (; f.k < kend; ++f.k) {
     const JobDesc d = read_desc(L, f.k);
     const int n = job_items<KIND>(ph, d.nkb);
     if (n == 0) continue;
     ++f.k;
-    const int fmt = FMT == 0 ? 0 : d.fmt;
-    const int code = lane_code(L, d);
-    const uint32_t kb = fmt ? 64u : 128u, lb = fmt ? 16u : 32u;
-    const uint32_t lrow = KIND == 1 ? (row < 8 ? row : row + d.jump) : ph.hb + (row < ph.nlive ? row : ph.nlive - 1);
-    f.wb = (const uint8_t*)d.wb;
-    f.wo = lrow * d.rowbytes + (uint32_t)k0 * kb + (uint32_t)lg * lb;
-    if (fmt == 0) {
-      if (KIND == 1) {
-        f.sb = (const uint8_t*)d.sb;
-        f.so = (lane < 32 ? 0u : d.shi) + 4u * (uint32_t)k0;
-      } else {
-        f.sb = (const uint8_t*)d.sb + 4 * (size_t)(ph.hb >> 7) * d.nkb;
-        f.so = (lane < 32 ? 0u : 4u * (uint32_t)(ph.dnb * d.nkb)) + 4u * (uint32_t)k0;
-      }
-    } else {
-      f.sb = (const uint8_t*)d.sb;
-      f.so = lrow * d.shi + 4u * (uint32_t)k0;
-    }
-    f.ao = 2 * act_offset(p, KIND, code, lg) + 256u * (uint32_t)k0;
-    f.fmt = fmt;
-    f.nstep = 1 << ph_lstep<KIND>(ph);
-    f.left = n;
+    fetch_from_desc<FMT, KIND>(p, ph, f, d, ph_k0<KIND>(ph), n, lane_code(L, d));
     return;
   }
-  f.left = 1 << 30;
-  f.nstep = 0;
-  f.fmt = 0;
-  f.wb = f.sb = f.ab = (const uint8_t*)arg_ptr(p.x);
-  f.wo = f.so = f.ao = 0;
+  fetch_dead(p, f);
+}
+
+// LDS reads through address-space pointers, so that the compiler counts
+// them on the right counter (see ldg).
+template <class T>
+__device__ __forceinline__ T lds_get(const void* a) {
+  return *(const __attribute__((address_space(3))) T*)a;
+}
+
+// Adds 1 to an LDS word from lane 0 and returns the old value to all lanes.
+__device__ __forceinline__ uint32_t lds_inc_lane0(uint32_t* a) {
+  uint32_t v = 0;
+  if ((threadIdx.x & 63) == 0)
+    asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_off(a)), "v"(1u) : "memory");
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+__device__ __forceinline__ void write_desc(const Lds& L, int k, const JobDesc& d) {
+  char* a = (char*)(L.jd + k);
+  lds_st128(a, u32x4{(uint32_t)d.wb, (uint32_t)(d.wb >> 32), (uint32_t)d.sb, (uint32_t)(d.sb >> 32)});
+  lds_st128(a + 16, u32x4{d.tile, d.jump, d.shi, (uint32_t)d.nkb});
+  lds_st128(a + 32, u32x4{(uint32_t)d.fmt, (uint32_t)d.ncols, (uint32_t)d.cbase, 0u});
+}
+
+// Up/gate: claims this CU's next chunk c (local job c / nw, K-phase
+// c mod nw) and moves the fetch side to it, handing c on to the multiplying
+// side; past the end once c / nw reaches the CU's nU jobs (the wave then
+// claims no more).
+__device__ __forceinline__ int chunk_job(uint32_t c, int nw) { return nw == kWaves ? (int)(c >> 3) : (int)c / nw; }
+template <int FMT>
+__device__ inline void fetch_next_up(const Params& p, const Lds& L, const PhaseN& ph, FetchN& f, int nU) {
+  const uint32_t c = lds_inc_lane0(L.ccnt);
+  const int q = chunk_job(c, ph.nw), kp = (int)c - q * ph.nw;
+  if (q < nU) {
+    const JobDesc d = read_desc(L, q);
+    lds_st32(L.cfifo + wave_id() * 8 + (f.nch & 7), c);
+    f.nch = f.nch + 1;
+    fetch_from_desc<FMT, 1>(p, ph, f, d, kp, ((d.nkb - 1 - kp) >> 3) + 1, lane_code(L, d));
+    return;
+  }
+  fetch_dead(p, f);
+}
+
+// kend: up/gate, the CU's job count; down, the end of its job range.
+template <int FMT, int KIND>
+__device__ __forceinline__ void fetch_next_any(const Params& p, const Lds& L, const PhaseN& ph, FetchN& f, int kend) {
+  if (KIND == 1) fetch_next_up<FMT>(p, L, ph, f, kend);
+  else fetch_next_n<FMT, KIND>(p, L, ph, f, kend);
 }
 
 template <int FMT>
-__device__ __forceinline__ void fetch_item_n(const FetchN& f, ItemN& it) {
+__device__ __forceinline__ void fetch_weights_n(const FetchN& f, ItemN& it) {
   const uint8_t* w = f.wb + f.wo;
   it.w0 = ldg<u32x4>(w);
   it.w1 = ldg<u32x4>(w + (FMT == 0 || f.fmt == 0 ? 16 : 0));
   it.s = ldg<uint32_t>(f.sb + f.so);
-  const uint8_t* a = f.ab + f.ao;
+}
+__device__ __forceinline__ void fetch_acts_n(const uint8_t* ab, uint32_t ao, ItemN& it) {
+  const uint8_t* a = ab + ao;
 #pragma unroll
   for (int m = 0; m < 4; ++m) it.B[m] = ldg<u32x4>(a + 16 * m);
+}
+template <int FMT>
+__device__ __forceinline__ void fetch_item_n(const FetchN& f, ItemN& it) {
+  fetch_weights_n<FMT>(f, it);
+  fetch_acts_n(f.ab, f.ao, it);
 }
 
 template <int FMT>
@@ -1817,19 +1955,22 @@ __device__ __forceinline__ void fetch_adv_n(FetchN& f) {
   f.so += 4u * n;
   f.ao += 256u * n;
   f.left = uni(f.left) - 1;
+  f.cnt = uni(f.cnt) + 1;
 }
 
 // The multiplying side.
 struct EatN {
   int k;
+  int nch;         // up/gate: chunks taken from the fetch side
+  int q;           // up/gate: the local job being multiplied
   int left;        // items left in the job
   int fmt;         // 0 FP8, 1 MXFP4
   uint32_t pidx;   // this lane's partial (floats from L.pbuf); only stored when pst
   bool pst;        // this lane's column is one of the group's
 };
 
-// Moves the multiplying side to its next job of [e.k, kend) with items;
-// false at the end.
+// Down: moves the multiplying side to its next job of [e.k, kend) with
+// items; false at the end.
 template <int FMT, int KIND>
 __device__ inline bool eat_next_n(const Params& p, const Lds& L, const PhaseN& ph, EatN& e, int kend) {
   const int lane = threadIdx.x & 63, lg = lane >> 4, col = lane & 15;
@@ -1841,18 +1982,80 @@ __device__ inline bool eat_next_n(const Params& p, const Lds& L, const PhaseN& p
     e.left = n;
     e.fmt = FMT == 0 ? 0 : d.fmt;
     e.pst = col < d.ncols;
-    if (KIND == 1) {
-      const uint32_t slot = (uint32_t)d.pslot + (uint32_t)col * (uint32_t)p.tpc;
-      e.pidx = ((uint32_t)wave_id() * (uint32_t)(p.T * (p.K + 1) * p.tpc) + slot) * 16u + 4u * (uint32_t)lg;
-    } else {
-      const int code = lane_code(L, d);
-      e.pidx = (((uint32_t)ph.k0 * (uint32_t)p.T + (uint32_t)(code >> 4)) * (uint32_t)(p.K + 1) +
-                (uint32_t)(code & 15)) * (uint32_t)p.pitch +
-               16u * (uint32_t)ph.rt + 4u * (uint32_t)lg;
-    }
+    const int code = lane_code(L, d);
+    e.pidx = lmul(lmul((uint32_t)ph.k0 * (uint32_t)p.T + (uint32_t)(code >> 4), (uint32_t)(p.K + 1)) +
+                      (uint32_t)(code & 15),
+                  (uint32_t)p.pitch) +
+             16u * (uint32_t)ph.rt + 4u * (uint32_t)lg;
     return true;
   }
   return false;
+}
+
+// Up/gate: moves the multiplying side to the next chunk the fetch side has
+// set up (fnch: chunks it has claimed); false at the end.  The partial goes
+// to window q mod kPuWin, K-phase row kp, the lane's column.
+template <int FMT>
+__device__ inline bool eat_next_up(const Params& p, const Lds& L, const PhaseN& ph, EatN& e, int fnch) {
+  if (e.nch >= fnch) return false;
+  const int lane = threadIdx.x & 63, lg = lane >> 4, col = lane & 15;
+  const uint32_t c = (uint32_t)lds_ldi_uniform((const int32_t*)L.cfifo + wave_id() * 8 + (e.nch & 7));
+  e.nch = e.nch + 1;
+  const int q = chunk_job(c, ph.nw), kp = (int)c - q * ph.nw;
+  const JobDesc d = read_desc(L, q);
+  e.q = q;
+  e.left = ((d.nkb - 1 - kp) >> 3) + 1;
+  e.fmt = FMT == 0 ? 0 : d.fmt;
+  e.pst = col < d.ncols;
+  e.pidx = ((((uint32_t)q & (kPuWin - 1)) * kWaves + (uint32_t)kp) * (uint32_t)p.T + (uint32_t)col) * 16u +
+           4u * (uint32_t)lg;
+  return true;
+}
+
+// Up/gate job q is complete in partial window win (waves 0..nw-1 stored):
+// every (column, intermediate) is summed over the 8 waves in order (a wave
+// without items adds zero), gate and up, and its SwiGLU value goes to mid as
+// bf16.  One wave; lane = (column, pair of intermediates).
+__device__ inline void up_reduce_job(const Params& p, const Lds& L, int q, int win, int nw) {
+  const JobDesc d = read_desc(L, q);
+  const int lane = threadIdx.x & 63, col = lane >> 2, i2 = 2 * (lane & 3);
+  if (col < d.ncols) {
+    const size_t wstride = (size_t)p.T * 16;
+    const float* pu = L.pbuf + ((size_t)win * kWaves * p.T + col) * 16 + i2;
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      f32x2 gv = {0.f, 0.f}, uv = {0.f, 0.f};
+      if (w < nw) {
+        gv = lds_get<f32x2>(pu + w * wstride);
+        uv = lds_get<f32x2>(pu + w * wstride + 8);
+      }
+      g0 += gv[0];
+      g1 += gv[1];
+      u0 += uv[0];
+      u1 += uv[1];
+    }
+    const float m0 = swiglu(g0, u0), m1 = swiglu(g1, u1);
+    if (!isfinite(m0) || !isfinite(m1)) set_err(p.err, kErrMid);
+    const int code = lds_get<int32_t>(L.cols + d.cbase + col);
+    st_agent<uint32_t>(p.mid + ((size_t)(code >> 4) * (p.K + 1) + (code & 15)) * p.mid_ld + 8 * d.tile + i2,
+                       f32_to_bf16_rne(m0) | (f32_to_bf16_rne(m1) << 16));
+  }
+}
+
+// The end of a chunk of up/gate job e.q: once the window's previous job is
+// summed, store the chunk's partial tile and arrive; the wave that ends the
+// job's last (nw-th) chunk sums the job and frees the window.
+__device__ inline void up_job_end(const Params& p, const Lds& L, const EatN& e, const f32x4& acc, int nw, bool& ok) {
+  const int win = e.q & (kPuWin - 1);
+  lds_wait<1>(p, L.wgen + win, (uint32_t)(e.q / kPuWin), ok);
+  if (e.pst) lds_st128(L.pbuf + e.pidx, __builtin_bit_cast(u32x4, acc));
+  if (lds_inc_lane0(L.wcnt + win) == (uint32_t)nw - 1) {
+    up_reduce_job(p, L, e.q, win, nw);
+    lds_st32(L.wcnt + win, 0u);
+    lds_st32(L.wgen + win, (uint32_t)(e.q / kPuWin + 1));
+  }
 }
 
 template <int F>
@@ -1879,25 +2082,61 @@ __device__ __forceinline__ void eat_item_n(int split, int lg, const ItemN& it, f
   }
 }
 
-// One phase of the narrow stream over jobs [k, kend) of the job tables.
-// Partials go to LDS, which must be zero where this wave has no items.
-template <int FMT, int KIND>
-__device__ __forceinline__ void run_narrow(const Params& p, const Lds& L, const PhaseN& ph, int k, int kend, int& jc) {
-  constexpr int D = 5;
+// One phase of the narrow stream over jobs [k, kend) of the job tables, in
+// pieces: ring_open sets the fetch side to the first job, ring_fill issues
+// the first D items (all loads, or weights and scales only, the
+// activations following in ring_fill_acts), and ring_run multiplies and
+// refills until the last job has ended.  Partials go to LDS, which must be
+// zero where this wave has no items.
+constexpr int kRingD = 5;
+struct RingN {
   FetchN f;
-  f.k = k;
-  f.ab = (const uint8_t*)(KIND == 1 ? arg_ptr(p.x) : arg_ptr(p.mid));
-  fetch_next_n<FMT, KIND>(p, L, ph, f, kend);
-  ItemN ring[D];
+  ItemN r[kRingD];
+  uint32_t aop[kRingD];  // activation offsets of the filled items (split fill)
+};
+
+template <int FMT, int KIND>
+__device__ __forceinline__ void ring_open(const Params& p, const Lds& L, const PhaseN& ph, RingN& R, int k, int kend) {
+  R.f.k = k;
+  R.f.nch = 0;
+  R.f.cnt = 0;
+  R.f.ab = (const uint8_t*)(KIND == 1 ? arg_ptr(p.x) : arg_ptr(p.mid));
+  fetch_next_any<FMT, KIND>(p, L, ph, R.f, kend);
+}
+
+// WONLY: weights and scales only (the activation offsets are kept).
+template <int FMT, int KIND, bool WONLY>
+__device__ __forceinline__ void ring_fill(const Params& p, const Lds& L, const PhaseN& ph, RingN& R, int kend) {
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    fetch_item_n<FMT>(f, ring[d]);
-    fetch_adv_n<FMT>(f);
-    if (f.left == 0) fetch_next_n<FMT, KIND>(p, L, ph, f, kend);
+  for (int d = 0; d < kRingD; ++d) {
+    if (WONLY) {
+      fetch_weights_n<FMT>(R.f, R.r[d]);
+      R.aop[d] = R.f.ao;
+    } else {
+      fetch_item_n<FMT>(R.f, R.r[d]);
+    }
+    fetch_adv_n<FMT>(R.f);
+    if (R.f.left == 0) fetch_next_any<FMT, KIND>(p, L, ph, R.f, kend);
   }
+}
+
+__device__ __forceinline__ void ring_fill_acts(RingN& R) {
+#pragma unroll
+  for (int d = 0; d < kRingD; ++d) fetch_acts_n(R.f.ab, R.aop[d], R.r[d]);
+}
+
+// PEEL: the first round is its own copy, so that the loop's waits are
+// counted from the steady load order (a split fill issues them in another).
+// Up/gate (KIND 1): chunks are claimed from the CU's counter and chunk ends
+// go through the partial windows.
+template <int FMT, int KIND, bool PEEL>
+__device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const PhaseN& ph, RingN& R, int k, int kend,
+                                         int& jc, bool& ok) {
   EatN e;
   e.k = k;
-  if (eat_next_n<FMT, KIND>(p, L, ph, e, kend)) {
+  e.nch = 0;
+  const bool any = KIND == 1 ? eat_next_up<FMT>(p, L, ph, e, R.f.nch) : eat_next_n<FMT, KIND>(p, L, ph, e, kend);
+  if (any) {
     const int lg = (threadIdx.x & 63) >> 4;
     const int split = ph_split<KIND>(ph);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1907,64 +2146,43 @@ __device__ __forceinline__ void run_narrow(const Params& p, const Lds& L, const 
     // the same D-1 items since (an exit in mid-round would make the
     // compiler's wait counting assume fewer and drain the ring).
     bool done = false;
-    for (;;) {
+    auto round = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int d = 0; d < D; ++d) {
-        if (FMT == 0 || e.fmt == 0) eat_item_n<0>(split, lg, ring[d], acc);
-        else eat_item_n<1>(split, lg, ring[d], acc);
-        fetch_item_n<FMT>(f, ring[d]);
-        fetch_adv_n<FMT>(f);
-        if (f.left == 0) fetch_next_n<FMT, KIND>(p, L, ph, f, kend);
+      for (int d = 0; d < kRingD; ++d) {
+        if (FMT == 0 || e.fmt == 0) eat_item_n<0>(split, lg, R.r[d], acc);
+        else eat_item_n<1>(split, lg, R.r[d], acc);
+        fetch_item_n<FMT>(R.f, R.r[d]);
+        fetch_adv_n<FMT>(R.f);
+        if (R.f.left == 0) fetch_next_any<FMT, KIND>(p, L, ph, R.f, kend);
         if (!done) {
           e.left = uni(e.left) - 1;
           if (e.left == 0) {
-            if (e.pst) lds_st128(L.pbuf + e.pidx, __builtin_bit_cast(u32x4, acc));
+            if (KIND == 1) up_job_end(p, L, e, acc, ph.nw, ok);
+            else if (e.pst) lds_st128(L.pbuf + e.pidx, __builtin_bit_cast(u32x4, acc));
             acc = f32x4{0.f, 0.f, 0.f, 0.f};
             MOE_JSTAMP(p, jc);
             balance(L, ++jc);
-            done = !eat_next_n<FMT, KIND>(p, L, ph, e, kend);
+            done = KIND == 1 ? !eat_next_up<FMT>(p, L, ph, e, R.f.nch) : !eat_next_n<FMT, KIND>(p, L, ph, e, kend);
           }
         }
       }
-      if (done) break;
+    };
+    if (PEEL) round();
+    if (!done) {
+      for (;;) {
+        round();
+        if (done) break;
+      }
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the dead items' loads
   __builtin_amdgcn_s_setprio(0);
 }
 
+
 // Zeroes the narrow partial region (n floats).
 __device__ inline void zero_partials(const Lds& L, size_t n) {
   for (size_t i = 4 * (size_t)threadIdx.x; i < n; i += 4 * kThreads) *(u32x4*)(L.pbuf + i) = u32x4{0u, 0u, 0u, 0u};
-}
-
-// After the narrow up/gate phase: every (column, intermediate) of this CU's
-// tiles is summed over the 8 waves in order, gate and up, and its SwiGLU
-// value goes to mid as bf16.  Whole workgroup.
-__device__ inline void up_reduce_n(const Params& p, const Lds& L, const Sched& s) {
-  const int ncol = p.T * (p.K + p.n_shared);
-  const int nslot = ncol * p.tpc;
-  const size_t wstride = (size_t)p.T * (p.K + 1) * p.tpc * 16;
-  for (int q = threadIdx.x; q < nslot * 8; q += kThreads) {
-    const int slot = q >> 3, i = q & 7;
-    const int ci = slot / p.tpc, tl = slot - ci * p.tpc;
-    const int g = L.cgrp[ci];
-    const bool sh = shared_group(p, g);
-    const int base = sh ? 0 : s.sh_tiles + (g - p.n_shared) * s.rt_tiles;
-    const int tiles = sh ? s.sh_tiles : s.rt_tiles;
-    const int t = (((int)blockIdx.x - base) % p.ncu + p.ncu) % p.ncu + tl * p.ncu;
-    if (t >= tiles) continue;
-    const float* pu = L.pbuf + (size_t)slot * 16;
-    float gs = 0.f, us = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) gs += pu[w * wstride + i];
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) us += pu[w * wstride + 8 + i];
-    const float m = swiglu(gs, us);
-    if (!isfinite(m)) set_err(p.err, kErrMid);
-    const int code = L.cols[ci];
-    p.mid[((size_t)(code >> 4) * (p.K + 1) + (code & 15)) * p.mid_ld + 8 * t + i] = (uint16_t)f32_to_bf16_rne(m);
-  }
 }
 
 // out[r][h] = P_shared + sum_p w[r][p] * P[r][p], fp32 FMA chain in slot
@@ -2019,32 +2237,36 @@ __device__ __forceinline__ const Params& fresh_args() {
   return *(const Params*)q;
 }
 
-// The narrow path after routing: up/gate stream, its reduction and the
-// second flag barrier, the down stream, the combine.
+// The narrow path after routing: the up/gate stream (its sums formed at job
+// ends), the second flag barrier, the down stream, the combine.
 template <int FMT>
 __device__ __forceinline__ void narrow_path(char* smem, int G, uint32_t epoch) {
   const int wave = wave_id();
   int jn = 0;  // jobs this wave has ended (for balance)
-  int nU;
+  bool ok = true;
+  RingN R;
   {
     const Params& p = fresh_args();
     const Lds L = lds_map(smem, p);
     const Sched s = make_sched(p, G, 1);
-    zero_partials(L, pu_floats(p.T, p.K, p.tpc));
-    nU = (int)blockIdx.x < s.n_jobs ? (s.n_jobs - 1 - (int)blockIdx.x) / p.ncu + 1 : 0;
-    build_jobs(p, L, s, nU);
+    const int nkb = p.H / 128;
     PhaseN ph = {};
-    run_narrow<FMT, 1>(p, L, ph, 0, nU, jn);
+    ph.nw = nkb < kWaves ? nkb : kWaves;
+    const int nU = (int)blockIdx.x < s.n_jobs ? (s.n_jobs - 1 - (int)blockIdx.x) / p.ncu + 1 : 0;
+    build_jobs(p, L, s, nU);
+    MOE_STAMP(p, 11);
+    ring_open<FMT, 1>(p, L, ph, R, 0, nU);
+    ring_fill<FMT, 1, false>(p, L, ph, R, nU);
+    MOE_STAMP(p, 13);
+    ring_run<FMT, 1, false>(p, L, ph, R, 0, nU, jn, ok);
     MOE_WSTAMP(p, 0);
+    MOE_TVAL(p, 8, jn);
   }
-  nU = uni(nU);
   {
     const Params& p = fresh_args();
     const Lds L = lds_map(smem, p);
     const Sched s = make_sched(p, G, 1);
-    __syncthreads();
     MOE_STAMP(p, 4);
-    up_reduce_n(p, L, s);
     publish(p, epoch + 2);
     MOE_STAMP(p, 12);
     zero_partials(L, (size_t)p.wpt * p.T * (p.K + 1) * p.pitch);
@@ -2058,10 +2280,17 @@ __device__ __forceinline__ void narrow_path(char* smem, int G, uint32_t epoch) {
     ph.nlive = s.hc - 16 * ph.rt < 16 ? s.hc - 16 * ph.rt : 16;
     ph.split = (ph.hb / 128 + 1) * 128 - ph.hb;  // a 16-row tile spans at most two scale block rows
     ph.dnb = ph.nlive > 0 ? ((ph.hb + ph.nlive - 1) >> 7) - (ph.hb >> 7) : 0;
+    ph.nw = 0;
+    const int kend = ph.nlive > 0 ? p.qcap + s.G : p.qcap;
+    // the first D items' weights do not depend on mid: issue them before the
+    // wait, their activations after it
+    ring_open<FMT, 2>(p, L, ph, R, p.qcap, kend);
+    ring_fill<FMT, 2, true>(p, L, ph, R, kend);
     wait_all(p, epoch + 2);
     MOE_STAMP(p, 5);
     MOE_WSTAMP(p, 1);
-    run_narrow<FMT, 2>(p, L, ph, nU, ph.nlive > 0 ? nU + s.G : nU, jn);
+    ring_fill_acts(R);
+    ring_run<FMT, 2, true>(p, L, ph, R, p.qcap, kend, jn, ok);
     MOE_WSTAMP(p, 2);
     MOE_STAMP(p, 6);
   }

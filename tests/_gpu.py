@@ -56,7 +56,12 @@ def parity(gpu_bits: np.ndarray, o64: np.ndarray, rows):
     return rel, mx
 
 
-def run_forward(layer: moe.Layer, x: torch.Tensor) -> np.ndarray:
+def run_forward(layer: moe.Layer, x: torch.Tensor, check: bool = True) -> np.ndarray:
+    """One forward; with `check`, also asserts that the call raised no device
+    error bit (a timed-out wait, a non-finite score or sum)."""
     out = layer.forward(x)
     torch.cuda.synchronize()
+    if check:
+        bits = layer.read_error()
+        assert bits == 0, f"device error bits {bits:#x}"
     return fixtures.bits16(out)

@@ -116,7 +116,7 @@ def test_error_word_on_nan_activation():
     layer = _layer(spec, case, 2)
     x = case["x"].clone()
     x[1, 7] = float("nan")
-    run_forward(layer, x)
+    run_forward(layer, x, check=False)
     bits = layer.read_error()
     assert bits & (moe.MOE_DEVERR_NONFINITE_SCORE | moe.MOE_DEVERR_NONFINITE_MID)
     assert layer.read_error() == 0          # read clears
