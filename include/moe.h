@@ -113,8 +113,9 @@ typedef struct {
  * Returns MOE_OK, MOE_ERR_NULL or a validation code. */
 int moe_workspace_size(const moe_config* cfg, size_t* bytes);
 
-/* Initialises a workspace: clears its cross-workgroup flags and its error
- * word.  Call once after allocating it (stream-ordered, asynchronous). */
+/* Initialises a workspace: clears all ws_bytes of it (the cross-workgroup
+ * flags, the error word and the epoch-tagged score slots).  Call once after
+ * allocating it (stream-ordered, asynchronous). */
 int moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Routing only: writes topk_ids[rows, K] (int32, in selection order: key

@@ -172,7 +172,8 @@ int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   if (!aligned16(ws)) return MOE_ERR_ALIGN;
   const WsLayout L = ws_layout(1, 1, 1, 128, 128, 0);
   if (ws_bytes < L.scores) return MOE_ERR_WORKSPACE;
-  hipError_t e = hipMemsetAsync(ws, 0, L.scores, (hipStream_t)stream);
+  // the whole workspace: flags, error word and the tagged score slots
+  hipError_t e = hipMemsetAsync(ws, 0, ws_bytes, (hipStream_t)stream);
   if (e != hipSuccess) {
     g_last_hip = (int)e;
     return MOE_ERR_HIP;

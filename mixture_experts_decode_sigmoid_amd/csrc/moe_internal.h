@@ -61,7 +61,7 @@ struct Params {
   // workspace
   uint32_t* flags;
   uint32_t* err;
-  double* scores;  // [T][E][2]: s, b
+  double* scores;  // [T][E] score slots: two 64-bit words (tag, high half of s), (tag, low half)
   uint16_t* mid;   // [T][K+1][mid_ld] bf16
   uint64_t* timeline;  // optional phase stamps ([ncu][64]); NULL unless built with MOE_TIMELINE
 };

@@ -3,12 +3,14 @@
 // One persistent launch: one workgroup of 8 waves per CU, all resident.
 //
 //   S0  router logits   CU c computes l[r][e] for its experts e = c, c+ncu..
-//                       (fp64 sums of exact bf16 products), sigmoid, bias;
-//                       publishes them, then raises its flag (epoch + 1).
+//                       (fp64 sums of exact bf16 products) and sigmoid, and
+//                       publishes each score in a slot tagged with the call's
+//                       epoch; then raises its flag (epoch + 1).
 //   S1  shared up/gate  the shared expert does not depend on routing, so its
 //                       8-intermediate tiles are streamed while the other CUs
 //                       finish S0.
-//   S2  route + group   every CU waits for all flags, routes every row itself
+//   S2  route + group   every CU polls the score slots of every row until
+//                       they carry the call's tag, routes every row itself
 //                       (no hand-off) and builds the step's group table in
 //                       LDS: distinct experts in order of first use, found by
 //                       ballot / prefix count, each with its using rows.
@@ -369,6 +371,18 @@ __device__ inline void wait_all(const Params& p, uint32_t target) {
 
 // ------------------------------------------------------------------ S0 logits
 
+// Score slots: s[r][e] as two 64-bit words (tag, high half of s) and (tag,
+// low half of s), each stored at agent scope; tag = the call's epoch + 1,
+// so a reader polls the slots themselves and needs no flag barrier (a slot
+// is current once both its words carry the call's tag).  The key
+// b = s + bias is recomputed by the reader in the same fp64 operation.
+__device__ __forceinline__ void publish_score(const Params& p, int r, int e, double s, uint32_t tag) {
+  uint64_t* dst = (uint64_t*)p.scores + ((size_t)r * p.E + e) * 2;
+  const uint64_t sb = __builtin_bit_cast(uint64_t, s);
+  st_agent<uint64_t>(dst, ((uint64_t)tag << 32) | (sb >> 32));
+  st_agent<uint64_t>(dst + 1, ((uint64_t)tag << 32) | (sb & 0xffffffffull));
+}
+
 __device__ inline double load_bias(const Params& p, int e) {
   if (p.bias_bf16) return (double)bf16_bits_to_f32(((const uint16_t*)p.bias)[e]);
   return (double)((const float*)p.bias)[e];
@@ -469,7 +483,7 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 // and l+64 of its chunk in order, the lanes are summed by a fixed tree and
 // the chunk sums in wave order.  Up to 4 dots' loads are issued before any
 // is summed.  Then s = sigmoid(l) and b = s + bias go to the workspace.
-__device__ inline void router_logits(const Params& p, const Lds& L) {
+__device__ inline void router_logits(const Params& p, const Lds& L, uint32_t tag) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int ch = p.H / kWaves, ngrp = ch >> 3;
   const int g0 = lane < ngrp ? lane : ngrp - 1, g1 = lane + 64 < ngrp ? lane + 64 : g0;
@@ -519,9 +533,7 @@ __device__ inline void router_logits(const Params& p, const Lds& L) {
     const double s = 1.0 / (1.0 + exp(-l));
     const double b = s + load_bias(p, e);
     if (!isfinite(l) || !isfinite(b)) set_err(p.err, kErrScore);
-    double* dst = p.scores + ((size_t)r * p.E + e) * 2;
-    st_agent<uint64_t>(dst, __builtin_bit_cast(uint64_t, s));
-    st_agent<uint64_t>(dst + 1, __builtin_bit_cast(uint64_t, b));
+    publish_score(p, r, e, s, tag);
   }
 }
 
@@ -530,7 +542,7 @@ __device__ inline void router_logits(const Params& p, const Lds& L) {
 // are issued before their products are summed.  Used from 8 rows up, where
 // every wave has rows of its own (and by the wide stream, whose register
 // budget has no room for the chunked form).
-__device__ inline void router_logits_rows(const Params& p) {
+__device__ inline void router_logits_rows(const Params& p, uint32_t tag) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (wave >= kWaves) return;
   for (int e = blockIdx.x; e < p.E; e += p.ncu) {
@@ -565,9 +577,7 @@ __device__ inline void router_logits_rows(const Params& p) {
         double s = 1.0 / (1.0 + exp(-acc));
         double b = s + bias;
         if (!isfinite(acc) || !isfinite(b)) set_err(p.err, kErrScore);
-        double* dst = p.scores + ((size_t)r * p.E + e) * 2;
-        st_agent<uint64_t>(dst, __builtin_bit_cast(uint64_t, s));
-        st_agent<uint64_t>(dst + 1, __builtin_bit_cast(uint64_t, b));
+        publish_score(p, r, e, s, tag);
       }
     }
   }
@@ -593,17 +603,54 @@ __device__ __forceinline__ double pick4(const double (&v)[4], int i) {
 // group, keep k_g groups by (score desc, index asc)), then K rounds of wave
 // argmax over (key desc, index asc); weights s/sum(s)*scale in fp64.
 // Lane l holds experts l, l+64, l+128, l+192.
-__device__ inline void route_row(const Params& p, const Lds& L, int r) {
+// POLL: poll row r's score slots (agent-scope loads) until every one
+// carries this call's tag (bounded: on timeout the error bit is set and
+// routing runs on).  Otherwise the flags have been waited for and the slots
+// are read once with plain loads (many rows per wave: they hit in L2).
+template <bool POLL>
+__device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t tag) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const double* sc = p.scores + (size_t)r * p.E * 2;
+  typedef __attribute__((address_space(1))) uint64_t G64;
+  const G64* sc = (const G64*)p.scores + (size_t)r * p.E * 2;
+  uint64_t w0[4] = {0, 0, 0, 0}, w1[4] = {0, 0, 0, 0};
+  if (!POLL) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + 64 * i;
+      if (e < p.E) {
+        w0[i] = sc[2 * e];
+        w1[i] = sc[2 * e + 1];
+      }
+    }
+  }
+  for (int spins = 0; POLL;) {
+    bool ready = true;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + 64 * i;
+      if (e < p.E) {
+        w0[i] = __hip_atomic_load(sc + 2 * e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        w1[i] = __hip_atomic_load(sc + 2 * e + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ready = ready && (uint32_t)(w0[i] >> 32) == tag && (uint32_t)(w1[i] >> 32) == tag;
+      }
+    }
+    if (__all(ready)) break;
+    if (++spins > kSpinLimit) {
+      if (lane == 0) set_err(p.err, kErrTimeout);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  MOE_STAMP(p, 9);
   double bv[4], sv[4];
   bool alive[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
     alive[i] = e < p.E;
-    double b = alive[i] ? sc[2 * e + 1] : -INFINITY;
-    sv[i] = alive[i] ? sc[2 * e] : 0.0;
+    const double s = __builtin_bit_cast(double, (w0[i] << 32) | (w1[i] & 0xffffffffull));
+    const double b = alive[i] ? s + load_bias(p, e) : -INFINITY;
+    sv[i] = alive[i] ? s : 0.0;
     bv[i] = isnan(b) ? -INFINITY : b;
   }
   if (p.ng > 1) {
@@ -2322,16 +2369,18 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   const uint32_t epoch = (uint32_t)__builtin_amdgcn_readfirstlane(L.misc[1]);
 
   // S0: router logits of this CU's experts, published for every CU
-  if (NARROW && p.T < kWaves) router_logits(p, L);
-  else router_logits_rows(p);
+  if (NARROW && p.T < kWaves) router_logits(p, L, epoch + 1);
+  else router_logits_rows(p, epoch + 1);
   publish(p, epoch + 1);
   MOE_STAMP(p, 1);
   if (MODE != kModeForward && blockIdx.x != 0) return;
 
-  // S2: route every row, then group the step's distinct experts
-  wait_all(p, epoch + 1);
+  // S2: route every row, then group the step's distinct experts.  A wave
+  // of the narrow path has at most two rows and polls their score slots; the
+  // wide path waits for every CU's flag first and reads them from L2.
+  if (!NARROW) wait_all(p, epoch + 1);
   MOE_STAMP(p, 2);
-  for (int r = wave; r < p.T; r += kWaves) route_row(p, L, r);
+  for (int r = wave; r < p.T; r += kWaves) route_row<NARROW>(p, L, r, epoch + 1);
   __syncthreads();
   MOE_STAMP(p, 10);
   if (MODE == kModeRoute) {
