@@ -158,7 +158,7 @@ __device__ __forceinline__ uint32_t lmul(uint32_t a, uint32_t b) {
   } while (0)
 #define MOE_JSTAMP(p, jc)                                                                \
   do {                                                                                   \
-    if (threadIdx.x == 0 && (p).timeline && (jc) < 24)                                   \
+    if (threadIdx.x == 0 && (p).timeline && (jc) < 20)                                   \
       MOE_TL(p, 40 + (jc)) = __builtin_amdgcn_s_memrealtime();                           \
   } while (0)
 #define MOE_TVAL(p, i, v)                                                                \
@@ -212,6 +212,12 @@ struct Lds {
 
 __host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// LDS words of the narrow stream's start (misc[]).
+constexpr int kMiscNU = 2;      // this CU's up/gate jobs, once routed
+constexpr int kMiscReady = 3;   // 1 once the routed jobs' tables are written
+constexpr int kMiscRouted = 4;  // rows routed so far (early start)
+constexpr int kMiscPolled = 5;  // rows whose scores are in (early start)
+
 // Job-end partials: one 16-column tile per job when a batch has at most 16
 // rows (four slots), else four tiles (two slots).
 __host__ __device__ inline int red_tiles(int T) { return T > 16 ? kMaxRows / 16 : 1; }
@@ -259,24 +265,31 @@ __host__ __device__ inline LdsOffsets lds_offsets(int T, int K, int E, int hs, i
   o.wst = q; q = align_up(q + 8 * kPuWin + 16 + 4 * kWaves * 8, 16);
   o.jd = q; q = align_up(q + (narrow ? kJobDescBytes * (size_t)(qcap + gmax) : 0), 16);
   // the routing scratch (used before the stream) overlaps the job-end
-  // partials and the down products (used in it)
+  // partials and the down products (used in it), except in a narrow call of
+  // fewer rows than waves, whose free waves stream while rows are routed
   o.red = q;
   // routing scratch: rb, rgs, rkept, then the top-k candidates (b, s, e) per wave
   const size_t rs = 8 * (size_t)kWaves * E + 8 * (size_t)kWaves * 64 + 4 * (size_t)kWaves * 64 +
                     20 * (size_t)kWaves * E;
-  size_t need;
+  size_t end;
   if (narrow) {
-    o.pbuf = q;
     const size_t pu = 4 * pu_floats(T);
     const size_t pd = 4 * (size_t)wpt * T * (K + 1) * pitch;
-    need = pu > pd ? pu : pd;
+    const size_t need = pu > pd ? pu : pd;
+    if (T < kWaves) {
+      o.pbuf = align_up(q + rs, 16);
+      end = o.pbuf + need;
+    } else {
+      o.pbuf = q;
+      end = q + (need > rs ? need : rs);
+    }
   } else {
     const size_t rd = (size_t)red_slots(T) * red_tiles(T) * kRedTileBytes;
+    const size_t need = rd + 4 * (size_t)T * (K + 1) * hs;
     o.pbuf = q + rd;
-    need = rd + 4 * (size_t)T * (K + 1) * hs;
+    end = q + (need > rs ? need : rs);
   }
-  q = align_up(q + (need > rs ? need : rs), 16);
-  o.total = q;
+  o.total = align_up(end, 16);
   return o;
 }
 
@@ -613,6 +626,9 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
   typedef __attribute__((address_space(1))) uint64_t G64;
   const G64* sc = (const G64*)p.scores + (size_t)r * p.E * 2;
   uint64_t w0[4] = {0, 0, 0, 0}, w1[4] = {0, 0, 0, 0};
+  double bias[4];  // loaded first: they do not depend on the scores
+#pragma unroll
+  for (int i = 0; i < 4; ++i) bias[i] = lane + 64 * i < p.E ? load_bias(p, lane + 64 * i) : 0.0;
   if (!POLL) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -642,6 +658,9 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
     __builtin_amdgcn_s_sleep(1);
   }
   MOE_STAMP(p, 9);
+  if (POLL && lane == 0)  // rows whose scores are in (see narrow_forward)
+    __hip_atomic_fetch_add((__attribute__((address_space(3))) uint32_t*)(L.misc + kMiscPolled), 1u,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   double bv[4], sv[4];
   bool alive[4];
 #pragma unroll
@@ -649,10 +668,11 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
     const int e = lane + 64 * i;
     alive[i] = e < p.E;
     const double s = __builtin_bit_cast(double, (w0[i] << 32) | (w1[i] & 0xffffffffull));
-    const double b = alive[i] ? s + load_bias(p, e) : -INFINITY;
+    const double b = alive[i] ? s + bias[i] : -INFINITY;
     sv[i] = alive[i] ? s : 0.0;
     bv[i] = isnan(b) ? -INFINITY : b;
   }
+  MOE_STAMP(p, 60);
   if (p.ng > 1) {
     const int gsz = p.E / p.ng;
     if (gsz <= 64 && (gsz & (gsz - 1)) == 0) {
@@ -821,12 +841,13 @@ __device__ __forceinline__ int use_rank(const Lds& L, int e, int r) {
   return r < 32 ? __popc(lo & ((1u << r) - 1u)) : __popc(lo) + __popc(hi & ((1u << (r - 32)) - 1u));
 }
 
-__device__ inline void build_groups(const Params& p, const Lds& L) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// The grouping of up to 64 uses by one wave (wave 0), one use per lane, no
+// workgroup barriers.
+__device__ inline void groups_one_wave(const Params& p, const Lds& L) {
+  const int lane = threadIdx.x & 63;
   const int U = p.T * p.K;
-  if (U <= 64) {
-    // one wave, one use per lane, no workgroup barriers
-    if (wave == 0) {
+  {
+    {
       const bool valid = lane < U;
       const int e = valid ? L.ids[lane] : 0, r = lane / p.K;
       if (valid) {
@@ -870,6 +891,14 @@ __device__ inline void build_groups(const Params& p, const Lds& L) {
         L.cgrp[c] = g;
       }
     }
+  }
+}
+
+__device__ inline void build_groups(const Params& p, const Lds& L) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int U = p.T * p.K;
+  if (U <= 64) {
+    if (wave == 0) groups_one_wave(p, L);
     __syncthreads();
     return;
   }
@@ -1792,28 +1821,46 @@ __device__ __forceinline__ void up_job(const Params& p, const Sched& s, int j, i
 // K-phases in order does not depend on which wave did what, and waves that
 // stream faster take more chunks.
 
-// The job tables of a narrow call: this CU's up/gate jobs at 0..nU-1 and
-// one down job per group at qcap + g.  Whole workgroup (plain per-thread
-// LDS accesses); ends synchronised.
-__device__ inline void build_jobs(const Params& p, const Lds& L, const Sched& s, int nU) {
-  for (int k = threadIdx.x; k < p.qcap + s.G; k += kThreads) {
-    if (k < nU) {
-      int g, tile;
-      up_job(p, s, (int)blockIdx.x + k * p.ncu, g, tile);
-      const bool sh = shared_group(p, g);
-      L.jd[k] = make_desc(p, true, sh, sh ? 0 : L.gexp[g], tile, sh ? p.T : L.gcnt[g], sh ? 0 : L.gstart[g]);
-    } else if (k >= p.qcap) {
-      const int g = k - p.qcap;
-      const bool sh = shared_group(p, g);
-      L.jd[k] = make_desc(p, false, sh, sh ? 0 : L.gexp[g], 0, sh ? p.T : L.gcnt[g], sh ? 0 : L.gstart[g]);
-    }
+
+// The narrow stream's state and the tables of this CU's shared-expert jobs
+// (local jobs 0..nS-1; they need no routing).  Whole workgroup, plain
+// per-thread LDS accesses; the caller synchronises.
+__device__ inline void stream_init(const Params& p, const Lds& L, int nS) {
+  const int tid = threadIdx.x;
+  for (int k = tid; k < nS; k += kThreads)
+    L.jd[k] = make_desc(p, true, true, 0, (int)blockIdx.x + k * p.ncu, p.T, 0);
+  if (p.n_shared && tid < p.T) {
+    L.cols[tid] = tid * 16 + p.K;
+    L.cgrp[tid] = 0;
   }
-  if (threadIdx.x < kPuWin) {
-    L.wcnt[threadIdx.x] = 0u;
-    L.wgen[threadIdx.x] = 0u;
+  if (tid < kPuWin) {
+    L.wcnt[tid] = 0u;
+    L.wgen[tid] = 0u;
   }
-  if (threadIdx.x == 0) *L.ccnt = 0u;
-  __syncthreads();
+  if (tid == 0) {
+    *L.ccnt = 0u;
+    L.misc[kMiscReady] = 0;
+    L.misc[kMiscRouted] = 0;
+    L.misc[kMiscPolled] = 0;
+  }
+}
+
+// The tables that need the routing: the routed up/gate jobs (local jobs
+// nS..nU-1) and one down job per group at qcap + g, written by threads
+// first, first + stride, ...; then nU.
+__device__ inline void routed_tables(const Params& p, const Lds& L, const Sched& s, int nS, int nU, int first,
+                                     int stride) {
+  for (int k = nS + first; k < nU; k += stride) {
+    int g, tile;
+    up_job(p, s, (int)blockIdx.x + k * p.ncu, g, tile);
+    const bool sh = shared_group(p, g);
+    L.jd[k] = make_desc(p, true, sh, sh ? 0 : L.gexp[g], tile, sh ? p.T : L.gcnt[g], sh ? 0 : L.gstart[g]);
+  }
+  for (int g = first; g < s.G; g += stride) {
+    const bool sh = shared_group(p, g);
+    L.jd[p.qcap + g] = make_desc(p, false, sh, sh ? 0 : L.gexp[g], 0, sh ? p.T : L.gcnt[g], sh ? 0 : L.gstart[g]);
+  }
+  if (first == 0) L.misc[kMiscNU] = nU;
 }
 
 // Per-wave constants of a phase (KIND 1 up/gate, 2 down).  Up/gate: every
@@ -1845,6 +1892,7 @@ __device__ __forceinline__ int job_items(const PhaseN& ph, int nkb) {
 struct FetchN {
   int k;                         // next job to set up (down)
   int nch;                       // up/gate: chunks claimed by this wave
+  int nu;                        // up/gate: the CU's job count once the routed tables are in (else -1)
   int cnt;                       // items fetched so far
   int left;                      // items left in the job (large once past the phase)
   int nstep;                     // K-blocks per item step (0 once past the phase)
@@ -1944,23 +1992,20 @@ __device__ __forceinline__ uint32_t lds_inc_lane0(uint32_t* a) {
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
 }
 
-__device__ __forceinline__ void write_desc(const Lds& L, int k, const JobDesc& d) {
-  char* a = (char*)(L.jd + k);
-  lds_st128(a, u32x4{(uint32_t)d.wb, (uint32_t)(d.wb >> 32), (uint32_t)d.sb, (uint32_t)(d.sb >> 32)});
-  lds_st128(a + 16, u32x4{d.tile, d.jump, d.shi, (uint32_t)d.nkb});
-  lds_st128(a + 32, u32x4{(uint32_t)d.fmt, (uint32_t)d.ncols, (uint32_t)d.cbase, 0u});
-}
-
 // Up/gate: claims this CU's next chunk c (local job c / nw, K-phase
 // c mod nw) and moves the fetch side to it, handing c on to the multiplying
-// side; past the end once c / nw reaches the CU's nU jobs (the wave then
-// claims no more).
+// side; past the end once c / nw reaches the CU's job count (the wave then
+// claims no more).  Jobs from nS on wait for the routed tables (bounded).
 __device__ __forceinline__ int chunk_job(uint32_t c, int nw) { return nw == kWaves ? (int)(c >> 3) : (int)c / nw; }
 template <int FMT>
-__device__ inline void fetch_next_up(const Params& p, const Lds& L, const PhaseN& ph, FetchN& f, int nU) {
+__device__ inline void fetch_next_up(const Params& p, const Lds& L, const PhaseN& ph, FetchN& f, int nS, bool& ok) {
   const uint32_t c = lds_inc_lane0(L.ccnt);
   const int q = chunk_job(c, ph.nw), kp = (int)c - q * ph.nw;
-  if (q < nU) {
+  if (q >= nS && f.nu < 0) {
+    lds_wait<1>(p, (const uint32_t*)L.misc + kMiscReady, 1u, ok);
+    f.nu = ok ? lds_ldi_uniform(L.misc + kMiscNU) : 0;
+  }
+  if (q < (q < nS ? nS : f.nu)) {
     const JobDesc d = read_desc(L, q);
     lds_st32(L.cfifo + wave_id() * 8 + (f.nch & 7), c);
     f.nch = f.nch + 1;
@@ -1970,10 +2015,12 @@ __device__ inline void fetch_next_up(const Params& p, const Lds& L, const PhaseN
   fetch_dead(p, f);
 }
 
-// kend: up/gate, the CU's job count; down, the end of its job range.
+// kend: up/gate, the CU's shared-expert job count; down, the end of its
+// job range.
 template <int FMT, int KIND>
-__device__ __forceinline__ void fetch_next_any(const Params& p, const Lds& L, const PhaseN& ph, FetchN& f, int kend) {
-  if (KIND == 1) fetch_next_up<FMT>(p, L, ph, f, kend);
+__device__ __forceinline__ void fetch_next_any(const Params& p, const Lds& L, const PhaseN& ph, FetchN& f, int kend,
+                                               bool& ok) {
+  if (KIND == 1) fetch_next_up<FMT>(p, L, ph, f, kend, ok);
   else fetch_next_n<FMT, KIND>(p, L, ph, f, kend);
 }
 
@@ -2143,17 +2190,20 @@ struct RingN {
 };
 
 template <int FMT, int KIND>
-__device__ __forceinline__ void ring_open(const Params& p, const Lds& L, const PhaseN& ph, RingN& R, int k, int kend) {
+__device__ __forceinline__ void ring_open(const Params& p, const Lds& L, const PhaseN& ph, RingN& R, int k, int kend,
+                                          bool& ok) {
   R.f.k = k;
   R.f.nch = 0;
+  R.f.nu = -1;
   R.f.cnt = 0;
   R.f.ab = (const uint8_t*)(KIND == 1 ? arg_ptr(p.x) : arg_ptr(p.mid));
-  fetch_next_any<FMT, KIND>(p, L, ph, R.f, kend);
+  fetch_next_any<FMT, KIND>(p, L, ph, R.f, kend, ok);
 }
 
 // WONLY: weights and scales only (the activation offsets are kept).
 template <int FMT, int KIND, bool WONLY>
-__device__ __forceinline__ void ring_fill(const Params& p, const Lds& L, const PhaseN& ph, RingN& R, int kend) {
+__device__ __forceinline__ void ring_fill(const Params& p, const Lds& L, const PhaseN& ph, RingN& R, int kend,
+                                          bool& ok) {
 #pragma unroll
   for (int d = 0; d < kRingD; ++d) {
     if (WONLY) {
@@ -2163,7 +2213,7 @@ __device__ __forceinline__ void ring_fill(const Params& p, const Lds& L, const P
       fetch_item_n<FMT>(R.f, R.r[d]);
     }
     fetch_adv_n<FMT>(R.f);
-    if (R.f.left == 0) fetch_next_any<FMT, KIND>(p, L, ph, R.f, kend);
+    if (R.f.left == 0) fetch_next_any<FMT, KIND>(p, L, ph, R.f, kend, ok);
   }
 }
 
@@ -2200,7 +2250,7 @@ __device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const Ph
         else eat_item_n<1>(split, lg, R.r[d], acc);
         fetch_item_n<FMT>(R.f, R.r[d]);
         fetch_adv_n<FMT>(R.f);
-        if (R.f.left == 0) fetch_next_any<FMT, KIND>(p, L, ph, R.f, kend);
+        if (R.f.left == 0) fetch_next_any<FMT, KIND>(p, L, ph, R.f, kend, ok);
         if (!done) {
           e.left = uni(e.left) - 1;
           if (e.left == 0) {
@@ -2284,10 +2334,13 @@ __device__ __forceinline__ const Params& fresh_args() {
   return *(const Params*)q;
 }
 
-// The narrow path after routing: the up/gate stream (its sums formed at job
-// ends), the second flag barrier, the down stream, the combine.
+// The narrow forward after the logits: routing and grouping, the up/gate
+// stream (its sums formed at job ends), the second flag barrier, the down
+// stream, the combine.  With fewer rows than waves, the waves that route no
+// row start on this CU's shared-expert jobs at once, and the others join
+// once the routed tables are written.
 template <int FMT>
-__device__ __forceinline__ void narrow_path(char* smem, int G, uint32_t epoch) {
+__device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
   const int wave = wave_id();
   int jn = 0;  // jobs this wave has ended (for balance)
   bool ok = true;
@@ -2295,27 +2348,72 @@ __device__ __forceinline__ void narrow_path(char* smem, int G, uint32_t epoch) {
   {
     const Params& p = fresh_args();
     const Lds L = lds_map(smem, p);
-    const Sched s = make_sched(p, G, 1);
     const int nkb = p.H / 128;
     PhaseN ph = {};
     ph.nw = nkb < kWaves ? nkb : kWaves;
-    const int nU = (int)blockIdx.x < s.n_jobs ? (s.n_jobs - 1 - (int)blockIdx.x) / p.ncu + 1 : 0;
-    build_jobs(p, L, s, nU);
-    MOE_STAMP(p, 11);
-    ring_open<FMT, 1>(p, L, ph, R, 0, nU);
-    ring_fill<FMT, 1, false>(p, L, ph, R, nU);
+    const int sh_tiles = p.n_shared ? p.Is / 8 : 0;
+    const int nS = (int)blockIdx.x < sh_tiles ? (sh_tiles - 1 - (int)blockIdx.x) / p.ncu + 1 : 0;
+    const bool early = p.T < kWaves && p.T * p.K <= 64 && nS > 0;
+    stream_init(p, L, nS);
+    __syncthreads();
+    MOE_STAMP(p, 2);
+    if (early) {
+      // The streaming waves start once every row's scores are in: their
+      // loads would otherwise queue ahead of the polls.  The routing waves
+      // run at raised priority until their rows are routed.
+      if (wave < p.T) {
+        __builtin_amdgcn_s_setprio(3);
+        route_row<true>(p, L, wave, epoch + 1);
+        if (wave != 0) __builtin_amdgcn_s_setprio(0);
+        lds_inc_lane0((uint32_t*)(L.misc + kMiscRouted));  // after this wave's ids / w writes (LDS order)
+      }
+      if (wave == 0) {
+        lds_wait<1>(p, (const uint32_t*)L.misc + kMiscRouted, (uint32_t)p.T, ok);
+        MOE_STAMP(p, 10);
+        groups_one_wave(p, L);
+        wave_sync();
+        MOE_STAMP(p, 3);
+        const int G = lds_ldi_uniform(L.misc);
+        const Sched s = make_sched(p, G, 1);
+        const int nU = (int)blockIdx.x < s.n_jobs ? (s.n_jobs - 1 - (int)blockIdx.x) / p.ncu + 1 : 0;
+        routed_tables(p, L, s, nS, nU, threadIdx.x & 63, 64);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tables, before the flag
+        lds_st32(L.misc + kMiscReady, 1u);
+        __builtin_amdgcn_s_setprio(0);
+        MOE_STAMP(p, 11);
+      }
+      if (wave >= p.T) lds_wait<1>(p, (const uint32_t*)L.misc + kMiscPolled, (uint32_t)p.T, ok);
+    } else {
+      for (int r = wave; r < p.T; r += kWaves) route_row<true>(p, L, r, epoch + 1);
+      __syncthreads();
+      MOE_STAMP(p, 10);
+      build_groups(p, L);
+      MOE_STAMP(p, 3);
+      const int G = lds_ldi_uniform(L.misc);
+      const Sched s = make_sched(p, G, 1);
+      const int nU = (int)blockIdx.x < s.n_jobs ? (s.n_jobs - 1 - (int)blockIdx.x) / p.ncu + 1 : 0;
+      routed_tables(p, L, s, nS, nU, threadIdx.x, kThreads);
+      if (threadIdx.x == 0) L.misc[kMiscReady] = 1;
+      __syncthreads();
+      MOE_STAMP(p, 11);
+    }
+    ring_open<FMT, 1>(p, L, ph, R, 0, nS, ok);
+    MOE_STAMP(p, 62);
+    ring_fill<FMT, 1, false>(p, L, ph, R, nS, ok);
     MOE_STAMP(p, 13);
-    ring_run<FMT, 1, false>(p, L, ph, R, 0, nU, jn, ok);
+    ring_run<FMT, 1, false>(p, L, ph, R, 0, nS, jn, ok);
     MOE_WSTAMP(p, 0);
     MOE_TVAL(p, 8, jn);
   }
+  int G;
   {
     const Params& p = fresh_args();
     const Lds L = lds_map(smem, p);
-    const Sched s = make_sched(p, G, 1);
     MOE_STAMP(p, 4);
     publish(p, epoch + 2);
     MOE_STAMP(p, 12);
+    G = lds_ldi_uniform(L.misc);
+    const Sched s = make_sched(p, G, 1);
     zero_partials(L, (size_t)p.wpt * p.T * (p.K + 1) * p.pitch);
     // down: wave w takes tile w % nrt_p of this CU's slice and K-blocks
     // w / nrt_p + wpt*i of it
@@ -2331,8 +2429,8 @@ __device__ __forceinline__ void narrow_path(char* smem, int G, uint32_t epoch) {
     const int kend = ph.nlive > 0 ? p.qcap + s.G : p.qcap;
     // the first D items' weights do not depend on mid: issue them before the
     // wait, their activations after it
-    ring_open<FMT, 2>(p, L, ph, R, p.qcap, kend);
-    ring_fill<FMT, 2, true>(p, L, ph, R, kend);
+    ring_open<FMT, 2>(p, L, ph, R, p.qcap, kend, ok);
+    ring_fill<FMT, 2, true>(p, L, ph, R, kend, ok);
     wait_all(p, epoch + 2);
     MOE_STAMP(p, 5);
     MOE_WSTAMP(p, 1);
@@ -2374,10 +2472,15 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   publish(p, epoch + 1);
   MOE_STAMP(p, 1);
   if (MODE != kModeForward && blockIdx.x != 0) return;
+  if (NARROW && MODE == kModeForward) {
+    narrow_forward<FMT>(smem, epoch);
+    return;
+  }
 
-  // S2: route every row, then group the step's distinct experts.  A wave
-  // of the narrow path has at most two rows and polls their score slots; the
-  // wide path waits for every CU's flag first and reads them from L2.
+  // S2 (wide stream, and the routing-only calls): route every row, then
+  // group the step's distinct experts.  A wave of a narrow call has at most
+  // two rows and polls their score slots; the wide stream waits for every
+  // CU's flag first and reads them from L2.
   if (!NARROW) wait_all(p, epoch + 1);
   MOE_STAMP(p, 2);
   for (int r = wave; r < p.T; r += kWaves) route_row<NARROW>(p, L, r, epoch + 1);
@@ -2409,10 +2512,6 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
     return;
   }
 
-  if (NARROW) {
-    narrow_path<FMT>(smem, G, epoch);
-    return;
-  }
   const Sched s = make_sched(p, G, 0);
   bool ok = true;
   int jc = 0;  // jobs ended
