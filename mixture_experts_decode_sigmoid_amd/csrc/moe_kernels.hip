@@ -2182,15 +2182,17 @@ __device__ __forceinline__ void eat_item_n(int split, int lg, const ItemN& it, f
 // activations following in ring_fill_acts), and ring_run multiplies and
 // refills until the last job has ended.  Partials go to LDS, which must be
 // zero where this wave has no items.
-constexpr int kRingD = 5;
+constexpr int kRingD = 5;   // up/gate
+constexpr int kRingDD = 6;  // down: its second tile has fewer live rows, so items carry fewer bytes
+template <int D = kRingD>
 struct RingN {
   FetchN f;
-  ItemN r[kRingD];
-  uint32_t aop[kRingD];  // activation offsets of the filled items (split fill)
+  ItemN r[D];
+  uint32_t aop[D];  // activation offsets of the filled items (split fill)
 };
 
-template <int FMT, int KIND>
-__device__ __forceinline__ void ring_open(const Params& p, const Lds& L, const PhaseN& ph, RingN& R, int k, int kend,
+template <int FMT, int KIND, int D>
+__device__ __forceinline__ void ring_open(const Params& p, const Lds& L, const PhaseN& ph, RingN<D>& R, int k, int kend,
                                           bool& ok) {
   R.f.k = k;
   R.f.nch = 0;
@@ -2201,11 +2203,11 @@ __device__ __forceinline__ void ring_open(const Params& p, const Lds& L, const P
 }
 
 // WONLY: weights and scales only (the activation offsets are kept).
-template <int FMT, int KIND, bool WONLY>
-__device__ __forceinline__ void ring_fill(const Params& p, const Lds& L, const PhaseN& ph, RingN& R, int kend,
+template <int FMT, int KIND, bool WONLY, int D>
+__device__ __forceinline__ void ring_fill(const Params& p, const Lds& L, const PhaseN& ph, RingN<D>& R, int kend,
                                           bool& ok) {
 #pragma unroll
-  for (int d = 0; d < kRingD; ++d) {
+  for (int d = 0; d < D; ++d) {
     if (WONLY) {
       fetch_weights_n<FMT>(R.f, R.r[d]);
       R.aop[d] = R.f.ao;
@@ -2217,17 +2219,18 @@ __device__ __forceinline__ void ring_fill(const Params& p, const Lds& L, const P
   }
 }
 
-__device__ __forceinline__ void ring_fill_acts(RingN& R) {
+template <int D>
+__device__ __forceinline__ void ring_fill_acts(RingN<D>& R) {
 #pragma unroll
-  for (int d = 0; d < kRingD; ++d) fetch_acts_n(R.f.ab, R.aop[d], R.r[d]);
+  for (int d = 0; d < D; ++d) fetch_acts_n(R.f.ab, R.aop[d], R.r[d]);
 }
 
 // PEEL: the first round is its own copy, so that the loop's waits are
 // counted from the steady load order (a split fill issues them in another).
 // Up/gate (KIND 1): chunks are claimed from the CU's counter and chunk ends
 // go through the partial windows.
-template <int FMT, int KIND, bool PEEL>
-__device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const PhaseN& ph, RingN& R, int k, int kend,
+template <int FMT, int KIND, bool PEEL, int D>
+__device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const PhaseN& ph, RingN<D>& R, int k, int kend,
                                          int& jc, bool& ok) {
   EatN e;
   e.k = k;
@@ -2245,7 +2248,7 @@ __device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const Ph
     bool done = false;
     auto round = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int d = 0; d < kRingD; ++d) {
+      for (int d = 0; d < D; ++d) {
         if (FMT == 0 || e.fmt == 0) eat_item_n<0>(split, lg, R.r[d], acc);
         else eat_item_n<1>(split, lg, R.r[d], acc);
         fetch_item_n<FMT>(R.f, R.r[d]);
@@ -2344,8 +2347,8 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
   const int wave = wave_id();
   int jn = 0;  // jobs this wave has ended (for balance)
   bool ok = true;
-  RingN R;
   {
+    RingN<kRingD> R;
     const Params& p = fresh_args();
     const Lds L = lds_map(smem, p);
     const int nkb = p.H / 128;
@@ -2397,11 +2400,11 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
       __syncthreads();
       MOE_STAMP(p, 11);
     }
-    ring_open<FMT, 1>(p, L, ph, R, 0, nS, ok);
+    ring_open<FMT, 1, kRingD>(p, L, ph, R, 0, nS, ok);
     MOE_STAMP(p, 62);
-    ring_fill<FMT, 1, false>(p, L, ph, R, nS, ok);
+    ring_fill<FMT, 1, false, kRingD>(p, L, ph, R, nS, ok);
     MOE_STAMP(p, 13);
-    ring_run<FMT, 1, false>(p, L, ph, R, 0, nS, jn, ok);
+    ring_run<FMT, 1, false, kRingD>(p, L, ph, R, 0, nS, jn, ok);
     MOE_WSTAMP(p, 0);
     MOE_TVAL(p, 8, jn);
   }
@@ -2429,13 +2432,14 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
     const int kend = ph.nlive > 0 ? p.qcap + s.G : p.qcap;
     // the first D items' weights do not depend on mid: issue them before the
     // wait, their activations after it
-    ring_open<FMT, 2>(p, L, ph, R, p.qcap, kend, ok);
-    ring_fill<FMT, 2, true>(p, L, ph, R, kend, ok);
+    RingN<kRingDD> R;
+    ring_open<FMT, 2, kRingDD>(p, L, ph, R, p.qcap, kend, ok);
+    ring_fill<FMT, 2, true, kRingDD>(p, L, ph, R, kend, ok);
     wait_all(p, epoch + 2);
     MOE_STAMP(p, 5);
     MOE_WSTAMP(p, 1);
     ring_fill_acts(R);
-    ring_run<FMT, 2, true>(p, L, ph, R, p.qcap, kend, jn, ok);
+    ring_run<FMT, 2, true, kRingDD>(p, L, ph, R, p.qcap, kend, jn, ok);
     MOE_WSTAMP(p, 2);
     MOE_STAMP(p, 6);
   }
