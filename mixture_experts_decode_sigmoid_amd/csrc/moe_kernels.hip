@@ -1911,17 +1911,23 @@ struct ItemN {
 // Column code (row*16 + slot) of this lane's column in a job (a lane past
 // the group's columns takes its last one: MFMA columns are independent and
 // that output is never stored).
-// C4 (jobs of at most 4 columns): group column c sits at MFMA columns
-// 4c..4c+3, one per lane of a quad (see eat_item_n).
-template <int C4>
+// Activation loads per item, AL = 1, 2 or 4: a job of at most 4*AL columns
+// places group column c at MFMA columns G*c..G*c+G-1 (G = 4/AL lanes per
+// column), and lane G*c+j loads the 16-B pieces j, j+G, .. of its K-block
+// (see act_operand).
+template <int AL>
+__device__ __forceinline__ int lane_col(int lane) {
+  return (lane & 15) >> (AL == 1 ? 2 : AL == 2 ? 1 : 0);
+}
+template <int AL>
 __device__ __forceinline__ int lane_code(const Lds& L, const JobDesc& d) {
-  const int col = C4 ? (threadIdx.x & 15) >> 2 : threadIdx.x & 15;
+  const int col = lane_col<AL>(threadIdx.x);
   return (int)lds_ld32(L.cols + d.cbase + (col < d.ncols ? col : d.ncols - 1));
 }
 
 // Sets the fetch side to job descriptor d, whose first item is this wave's
 // K-block k0; `code` is this lane's column (row*16 + slot), n its items.
-template <int FMT, int KIND, int C4>
+template <int FMT, int KIND, int AL>
 __device__ __forceinline__ void fetch_from_desc(const Params& p, const PhaseN& ph, FetchN& f, const JobDesc& d, int k0,
                                                 int n, int code) {
   const int lane = threadIdx.x & 63, lg = lane >> 4, row = lane & 15;
@@ -1942,8 +1948,8 @@ __device__ __forceinline__ void fetch_from_desc(const Params& p, const PhaseN& p
     f.sb = (const uint8_t*)d.sb;
     f.so = lmul(lrow, d.shi) + 4u * (uint32_t)k0;
   }
-  // C4: a lane loads only the 16 B of MFMA m = lane mod 4 (its quad shares them)
-  f.ao = 2 * act_offset(p, KIND, code, lg) + 256u * (uint32_t)k0 + (C4 ? 16u * (uint32_t)(lane & 3) : 0u);
+  // a lane's first piece: j = lane mod G
+  f.ao = 2 * act_offset(p, KIND, code, lg) + 256u * (uint32_t)k0 + 16u * (uint32_t)(lane & (4 / AL - 1));
   f.fmt = fmt;
   f.nstep = 1 << ph_lstep<KIND>(ph);
   f.left = n;
@@ -1968,14 +1974,14 @@ __device__ __forceinline__ void fetch_dead(const Params& p, FetchN& f) {
 
 // Down: moves the fetch side to the next job of [f.k, kend) with items for
 // this wave, or past the end.
-template <int FMT, int KIND, int C4>
+template <int FMT, int KIND, int AL>
 __device__ inline void fetch_next_n(const Params& p, const Lds& L, const PhaseN& ph, FetchN& f, int kend) {
   for (; f.k < kend; ++f.k) {
     const JobDesc d = read_desc(L, f.k);
     const int n = job_items<KIND>(ph, d.nkb);
     if (n == 0) continue;
     ++f.k;
-    fetch_from_desc<FMT, KIND, C4>(p, ph, f, d, ph_k0<KIND>(ph), n, lane_code<C4>(L, d));
+    fetch_from_desc<FMT, KIND, AL>(p, ph, f, d, ph_k0<KIND>(ph), n, lane_code<AL>(L, d));
     return;
   }
   fetch_dead(p, f);
@@ -2001,7 +2007,7 @@ __device__ __forceinline__ uint32_t lds_inc_lane0(uint32_t* a) {
 // side; past the end once c / nw reaches the CU's job count (the wave then
 // claims no more).  Jobs from nS on wait for the routed tables (bounded).
 __device__ __forceinline__ int chunk_job(uint32_t c, int nw) { return nw == kWaves ? (int)(c >> 3) : (int)c / nw; }
-template <int FMT, int C4>
+template <int FMT, int AL>
 __device__ inline void fetch_next_up(const Params& p, const Lds& L, const PhaseN& ph, FetchN& f, int nS, bool& ok) {
   const uint32_t c = lds_inc_lane0(L.ccnt);
   const int q = chunk_job(c, ph.nw), kp = (int)c - q * ph.nw;
@@ -2013,7 +2019,7 @@ __device__ inline void fetch_next_up(const Params& p, const Lds& L, const PhaseN
     const JobDesc d = read_desc(L, q);
     lds_st32(L.cfifo + wave_id() * 8 + (f.nch & 7), c);
     f.nch = f.nch + 1;
-    fetch_from_desc<FMT, 1, C4>(p, ph, f, d, kp, ((d.nkb - 1 - kp) >> 3) + 1, lane_code<C4>(L, d));
+    fetch_from_desc<FMT, 1, AL>(p, ph, f, d, kp, ((d.nkb - 1 - kp) >> 3) + 1, lane_code<AL>(L, d));
     return;
   }
   fetch_dead(p, f);
@@ -2021,11 +2027,11 @@ __device__ inline void fetch_next_up(const Params& p, const Lds& L, const PhaseN
 
 // kend: up/gate, the CU's shared-expert job count; down, the end of its
 // job range.
-template <int FMT, int KIND, int C4>
+template <int FMT, int KIND, int AL>
 __device__ __forceinline__ void fetch_next_any(const Params& p, const Lds& L, const PhaseN& ph, FetchN& f, int kend,
                                                bool& ok) {
-  if (KIND == 1) fetch_next_up<FMT, C4>(p, L, ph, f, kend, ok);
-  else fetch_next_n<FMT, KIND, C4>(p, L, ph, f, kend);
+  if (KIND == 1) fetch_next_up<FMT, AL>(p, L, ph, f, kend, ok);
+  else fetch_next_n<FMT, KIND, AL>(p, L, ph, f, kend);
 }
 
 template <int FMT>
@@ -2035,18 +2041,18 @@ __device__ __forceinline__ void fetch_weights_n(const FetchN& f, ItemN& it) {
   it.w1 = ldg<u32x4>(w + (FMT == 0 || f.fmt == 0 ? 16 : 0));
   it.s = ldg<uint32_t>(f.sb + f.so);
 }
-// Activations: 4 x 16 B per lane, or with C4 one 16 B load (the load
+// Activations: AL loads of 16 B per lane, pieces j + G*i (the load
 // instructions, not the bytes, are what the vector memory path pays for).
-template <int C4>
+template <int AL>
 __device__ __forceinline__ void fetch_acts_n(const uint8_t* ab, uint32_t ao, ItemN& it) {
   const uint8_t* a = ab + ao;
 #pragma unroll
-  for (int m = 0; m < (C4 ? 1 : 4); ++m) it.B[m] = ldg<u32x4>(a + 16 * m);
+  for (int i = 0; i < AL; ++i) it.B[i] = ldg<u32x4>(a + 16 * (4 / AL) * i);
 }
-template <int FMT, int C4>
+template <int FMT, int AL>
 __device__ __forceinline__ void fetch_item_n(const FetchN& f, ItemN& it) {
   fetch_weights_n<FMT>(f, it);
-  fetch_acts_n<C4>(f.ab, f.ao, it);
+  fetch_acts_n<AL>(f.ab, f.ao, it);
 }
 
 template <int FMT>
@@ -2072,9 +2078,9 @@ struct EatN {
 
 // Down: moves the multiplying side to its next job of [e.k, kend) with
 // items; false at the end.
-template <int FMT, int KIND, int C4>
+template <int FMT, int KIND, int AL>
 __device__ inline bool eat_next_n(const Params& p, const Lds& L, const PhaseN& ph, EatN& e, int kend) {
-  const int lane = threadIdx.x & 63, lg = lane >> 4, col = C4 ? (lane & 15) >> 2 : lane & 15;
+  const int lane = threadIdx.x & 63, lg = lane >> 4, col = lane_col<AL>(lane);
   for (; e.k < kend; ++e.k) {
     const JobDesc d = read_desc(L, e.k);
     const int n = job_items<KIND>(ph, d.nkb);
@@ -2082,8 +2088,8 @@ __device__ inline bool eat_next_n(const Params& p, const Lds& L, const PhaseN& p
     ++e.k;
     e.left = n;
     e.fmt = FMT == 0 ? 0 : d.fmt;
-    e.pst = col < d.ncols && (!C4 || (lane & 3) == 0);
-    const int code = lane_code<C4>(L, d);
+    e.pst = col < d.ncols && (lane & (4 / AL - 1)) == 0;
+    const int code = lane_code<AL>(L, d);
     e.pidx = lmul(lmul((uint32_t)ph.k0 * (uint32_t)p.T + (uint32_t)(code >> 4), (uint32_t)(p.K + 1)) +
                       (uint32_t)(code & 15),
                   (uint32_t)p.pitch) +
@@ -2096,10 +2102,10 @@ __device__ inline bool eat_next_n(const Params& p, const Lds& L, const PhaseN& p
 // Up/gate: moves the multiplying side to the next chunk the fetch side has
 // set up (fnch: chunks it has claimed); false at the end.  The partial goes
 // to window q mod kPuWin, K-phase row kp, the lane's column.
-template <int FMT, int C4>
+template <int FMT, int AL>
 __device__ inline bool eat_next_up(const Params& p, const Lds& L, const PhaseN& ph, EatN& e, int fnch) {
   if (e.nch >= fnch) return false;
-  const int lane = threadIdx.x & 63, lg = lane >> 4, col = C4 ? (lane & 15) >> 2 : lane & 15;
+  const int lane = threadIdx.x & 63, lg = lane >> 4, col = lane_col<AL>(lane);
   const uint32_t c = (uint32_t)lds_ldi_uniform((const int32_t*)L.cfifo + wave_id() * 8 + (e.nch & 7));
   e.nch = e.nch + 1;
   const int q = chunk_job(c, ph.nw), kp = (int)c - q * ph.nw;
@@ -2107,7 +2113,7 @@ __device__ inline bool eat_next_up(const Params& p, const Lds& L, const PhaseN& 
   e.q = q;
   e.left = ((d.nkb - 1 - kp) >> 3) + 1;
   e.fmt = FMT == 0 ? 0 : d.fmt;
-  e.pst = col < d.ncols && (!C4 || (lane & 3) == 0);
+  e.pst = col < d.ncols && (lane & (4 / AL - 1)) == 0;
   e.pidx = ((((uint32_t)q & (kPuWin - 1)) * kWaves + (uint32_t)kp) * (uint32_t)p.T + (uint32_t)col) * 16u +
            4u * (uint32_t)lg;
   return true;
@@ -2159,26 +2165,36 @@ __device__ inline void up_job_end(const Params& p, const Lds& L, const EatN& e, 
   }
 }
 
-// C4: MFMA m's activations are the 16 B lane m of each quad loaded,
-// broadcast over the quad (DPP quad permutation).
-template <int C4>
+// MFMA m's activations: piece m is load m / G of the column's lane m mod G,
+// broadcast over the column's G lanes by a DPP quad permutation (G = 4:
+// quad_perm(m,m,m,m); G = 2: (0,0,2,2) or (1,1,3,3)).
+template <int AL>
 __device__ __forceinline__ bf16x8 act_operand(const ItemN& it, int m) {
-  if (!C4) return __builtin_bit_cast(bf16x8, it.B[m]);
-  u32x4 b;  // quad_perm(m, m, m, m): 0x00, 0x55, 0xAA, 0xFF
+  if (AL == 4) return __builtin_bit_cast(bf16x8, it.B[m]);
+  constexpr int G = 4 / AL;
+  u32x4 b;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int v = (int)it.B[0][i];
-    switch (m) {
-      case 0: b[i] = (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x00, 0xF, 0xF, false); break;
-      case 1: b[i] = (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x55, 0xF, 0xF, false); break;
-      case 2: b[i] = (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0xAA, 0xF, 0xF, false); break;
-      default: b[i] = (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0xFF, 0xF, 0xF, false); break;
+    const int v = (int)it.B[m / G][i];
+    int r;
+    if (G == 4) {
+      switch (m) {
+        case 0: r = __builtin_amdgcn_update_dpp(0, v, 0x00, 0xF, 0xF, false); break;
+        case 1: r = __builtin_amdgcn_update_dpp(0, v, 0x55, 0xF, 0xF, false); break;
+        case 2: r = __builtin_amdgcn_update_dpp(0, v, 0xAA, 0xF, 0xF, false); break;
+        default: r = __builtin_amdgcn_update_dpp(0, v, 0xFF, 0xF, 0xF, false); break;
+      }
+    } else if ((m & 1) == 0) {
+      r = __builtin_amdgcn_update_dpp(0, v, 0xA0, 0xF, 0xF, false);
+    } else {
+      r = __builtin_amdgcn_update_dpp(0, v, 0xF5, 0xF, 0xF, false);
     }
+    b[i] = (uint32_t)r;
   }
   return __builtin_bit_cast(bf16x8, b);
 }
 
-template <int F, int C4>
+template <int F, int AL>
 __device__ __forceinline__ void eat_item_n(int split, int lg, const ItemN& it, f32x4& acc) {
   bf16x8 A[4];
   if (F == 0) {
@@ -2190,7 +2206,7 @@ __device__ __forceinline__ void eat_item_n(int split, int lg, const ItemN& it, f
     const float s_hi = __int_as_float(__builtin_amdgcn_readlane((int)it.s, 32));
     f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int m = 0; m < 4; ++m) t = mfma16(A[m], act_operand<C4>(it, m), t);
+    for (int m = 0; m < 4; ++m) t = mfma16(A[m], act_operand<AL>(it, m), t);
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = fmaf(t[q], 4 * lg + q < split ? s_lo : s_hi, acc[q]);
   } else {
@@ -2198,7 +2214,7 @@ __device__ __forceinline__ void eat_item_n(int split, int lg, const ItemN& it, f
 #pragma unroll
     for (int m = 0; m < 4; ++m) A[m] = e2m1x8_to_bf16(it.w0[m], sc);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) acc = mfma16(A[m], act_operand<C4>(it, m), acc);
+    for (int m = 0; m < 4; ++m) acc = mfma16(A[m], act_operand<AL>(it, m), acc);
   }
 }
 
@@ -2217,7 +2233,7 @@ struct RingN {
   uint32_t aop[D];  // activation offsets of the filled items (split fill)
 };
 
-template <int FMT, int KIND, int D, int C4>
+template <int FMT, int KIND, int D, int AL>
 __device__ __forceinline__ void ring_open(const Params& p, const Lds& L, const PhaseN& ph, RingN<D>& R, int k, int kend,
                                           bool& ok) {
   R.f.k = k;
@@ -2225,11 +2241,11 @@ __device__ __forceinline__ void ring_open(const Params& p, const Lds& L, const P
   R.f.nu = -1;
   R.f.cnt = 0;
   R.f.ab = (const uint8_t*)(KIND == 1 ? arg_ptr(p.x) : arg_ptr(p.mid));
-  fetch_next_any<FMT, KIND, C4>(p, L, ph, R.f, kend, ok);
+  fetch_next_any<FMT, KIND, AL>(p, L, ph, R.f, kend, ok);
 }
 
 // WONLY: weights and scales only (the activation offsets are kept).
-template <int FMT, int KIND, bool WONLY, int D, int C4>
+template <int FMT, int KIND, bool WONLY, int D, int AL>
 __device__ __forceinline__ void ring_fill(const Params& p, const Lds& L, const PhaseN& ph, RingN<D>& R, int kend,
                                           bool& ok) {
 #pragma unroll
@@ -2238,31 +2254,31 @@ __device__ __forceinline__ void ring_fill(const Params& p, const Lds& L, const P
       fetch_weights_n<FMT>(R.f, R.r[d]);
       R.aop[d] = R.f.ao;
     } else {
-      fetch_item_n<FMT, C4>(R.f, R.r[d]);
+      fetch_item_n<FMT, AL>(R.f, R.r[d]);
     }
     fetch_adv_n<FMT>(R.f);
-    if (R.f.left == 0) fetch_next_any<FMT, KIND, C4>(p, L, ph, R.f, kend, ok);
+    if (R.f.left == 0) fetch_next_any<FMT, KIND, AL>(p, L, ph, R.f, kend, ok);
   }
 }
 
-template <int D, int C4>
+template <int D, int AL>
 __device__ __forceinline__ void ring_fill_acts(RingN<D>& R) {
 #pragma unroll
-  for (int d = 0; d < D; ++d) fetch_acts_n<C4>(R.f.ab, R.aop[d], R.r[d]);
+  for (int d = 0; d < D; ++d) fetch_acts_n<AL>(R.f.ab, R.aop[d], R.r[d]);
 }
 
 // PEEL: the first round is its own copy, so that the loop's waits are
 // counted from the steady load order (a split fill issues them in another).
 // Up/gate (KIND 1): chunks are claimed from the CU's counter and chunk ends
 // go through the partial windows.
-template <int FMT, int KIND, bool PEEL, int D, int C4>
+template <int FMT, int KIND, bool PEEL, int D, int AL>
 __device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const PhaseN& ph, RingN<D>& R, int k, int kend,
                                          int& jc, bool& ok) {
   EatN e;
   e.k = k;
   e.nch = 0;
   const bool any =
-      KIND == 1 ? eat_next_up<FMT, C4>(p, L, ph, e, R.f.nch) : eat_next_n<FMT, KIND, C4>(p, L, ph, e, kend);
+      KIND == 1 ? eat_next_up<FMT, AL>(p, L, ph, e, R.f.nch) : eat_next_n<FMT, KIND, AL>(p, L, ph, e, kend);
   if (any) {
     const int lg = (threadIdx.x & 63) >> 4;
     const int split = ph_split<KIND>(ph);
@@ -2276,11 +2292,11 @@ __device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const Ph
     auto round = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
-        if (FMT == 0 || e.fmt == 0) eat_item_n<0, C4>(split, lg, R.r[d], acc);
-        else eat_item_n<1, C4>(split, lg, R.r[d], acc);
-        fetch_item_n<FMT, C4>(R.f, R.r[d]);
+        if (FMT == 0 || e.fmt == 0) eat_item_n<0, AL>(split, lg, R.r[d], acc);
+        else eat_item_n<1, AL>(split, lg, R.r[d], acc);
+        fetch_item_n<FMT, AL>(R.f, R.r[d]);
         fetch_adv_n<FMT>(R.f);
-        if (R.f.left == 0) fetch_next_any<FMT, KIND, C4>(p, L, ph, R.f, kend, ok);
+        if (R.f.left == 0) fetch_next_any<FMT, KIND, AL>(p, L, ph, R.f, kend, ok);
         if (!done) {
           e.left = uni(e.left) - 1;
           if (e.left == 0) {
@@ -2289,8 +2305,8 @@ __device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const Ph
             acc = f32x4{0.f, 0.f, 0.f, 0.f};
             MOE_JSTAMP(p, jc);
             balance(L, ++jc);
-            done = KIND == 1 ? !eat_next_up<FMT, C4>(p, L, ph, e, R.f.nch)
-                             : !eat_next_n<FMT, KIND, C4>(p, L, ph, e, kend);
+            done = KIND == 1 ? !eat_next_up<FMT, AL>(p, L, ph, e, R.f.nch)
+                             : !eat_next_n<FMT, KIND, AL>(p, L, ph, e, kend);
           }
         }
       }
@@ -2370,7 +2386,7 @@ __device__ __forceinline__ const Params& fresh_args() {
 // stream, the combine.  With fewer rows than waves, the waves that route no
 // row start on this CU's shared-expert jobs at once, and the others join
 // once the routed tables are written.
-template <int FMT, int C4>
+template <int FMT, int AL>
 __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
   const int wave = wave_id();
   int jn = 0;  // jobs this wave has ended (for balance)
@@ -2428,11 +2444,11 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
       __syncthreads();
       MOE_STAMP(p, 11);
     }
-    ring_open<FMT, 1, kRingD, C4>(p, L, ph, R, 0, nS, ok);
+    ring_open<FMT, 1, kRingD, AL>(p, L, ph, R, 0, nS, ok);
     MOE_STAMP(p, 62);
-    ring_fill<FMT, 1, false, kRingD, C4>(p, L, ph, R, nS, ok);
+    ring_fill<FMT, 1, false, kRingD, AL>(p, L, ph, R, nS, ok);
     MOE_STAMP(p, 13);
-    ring_run<FMT, 1, false, kRingD, C4>(p, L, ph, R, 0, nS, jn, ok);
+    ring_run<FMT, 1, false, kRingD, AL>(p, L, ph, R, 0, nS, jn, ok);
     MOE_WSTAMP(p, 0);
     MOE_TVAL(p, 8, jn);
   }
@@ -2461,13 +2477,13 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
     // the first D items' weights do not depend on mid: issue them before the
     // wait, their activations after it
     RingN<kRingDD> R;
-    ring_open<FMT, 2, kRingDD, C4>(p, L, ph, R, p.qcap, kend, ok);
-    ring_fill<FMT, 2, true, kRingDD, C4>(p, L, ph, R, kend, ok);
+    ring_open<FMT, 2, kRingDD, AL>(p, L, ph, R, p.qcap, kend, ok);
+    ring_fill<FMT, 2, true, kRingDD, AL>(p, L, ph, R, kend, ok);
     wait_all(p, epoch + 2);
     MOE_STAMP(p, 5);
     MOE_WSTAMP(p, 1);
-    ring_fill_acts<kRingDD, C4>(R);
-    ring_run<FMT, 2, true, kRingDD, C4>(p, L, ph, R, p.qcap, kend, jn, ok);
+    ring_fill_acts<kRingDD, AL>(R);
+    ring_run<FMT, 2, true, kRingDD, AL>(p, L, ph, R, p.qcap, kend, jn, ok);
     MOE_WSTAMP(p, 2);
     MOE_STAMP(p, 6);
   }
@@ -2482,9 +2498,9 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
 }
 
 
-// NARROW = 1: the narrow stream (per-wave partials), 2: the same with jobs
-// of at most 4 columns (batches of up to 4 rows: one activation load per
-// item); 0: the wide stream
+// NARROW = 1: the narrow stream (per-wave partials, 4 activation loads per
+// item); 2 and 3: the same for batches of up to 4 and 8 rows (1 and 2
+// loads per item, see lane_col); 0: the wide stream
 // (up to four 16-column tiles per group, owner reductions).
 template <int MODE, int FMT, int NARROW>
 __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
@@ -2507,7 +2523,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   MOE_STAMP(p, 1);
   if (MODE != kModeForward && blockIdx.x != 0) return;
   if (NARROW && MODE == kModeForward) {
-    narrow_forward<FMT, NARROW == 2>(smem, epoch);
+    narrow_forward<FMT, NARROW == 2 ? 1 : NARROW == 3 ? 2 : 4>(smem, epoch);
     return;
   }
 
@@ -2619,17 +2635,22 @@ static hipError_t launch_one(const Params& p, hipStream_t stream) {
 }
 
 hipError_t launch(const Params& p, int mode, hipStream_t stream) {
-  const bool wide = !p.narrow, c4 = p.narrow && p.T <= 4;
+  const bool wide = !p.narrow;
+  const int nk = p.T <= 4 ? 2 : p.T <= 8 ? 3 : 1;  // narrow kernel by batch size
   if (p.routed_fmt == 0) {
     if (mode == kModeForward)
-      return wide ? launch_one<kModeForward, 0, 0>(p, stream)
-                  : c4 ? launch_one<kModeForward, 0, 2>(p, stream) : launch_one<kModeForward, 0, 1>(p, stream);
+      return wide      ? launch_one<kModeForward, 0, 0>(p, stream)
+             : nk == 2 ? launch_one<kModeForward, 0, 2>(p, stream)
+             : nk == 3 ? launch_one<kModeForward, 0, 3>(p, stream)
+                       : launch_one<kModeForward, 0, 1>(p, stream);
     if (mode == kModeRoute) return launch_one<kModeRoute, 0>(p, stream);
     return launch_one<kModeGroups, 0>(p, stream);
   }
   if (mode == kModeForward)
-    return wide ? launch_one<kModeForward, 1, 0>(p, stream)
-                : c4 ? launch_one<kModeForward, 1, 2>(p, stream) : launch_one<kModeForward, 1, 1>(p, stream);
+    return wide      ? launch_one<kModeForward, 1, 0>(p, stream)
+           : nk == 2 ? launch_one<kModeForward, 1, 2>(p, stream)
+           : nk == 3 ? launch_one<kModeForward, 1, 3>(p, stream)
+                     : launch_one<kModeForward, 1, 1>(p, stream);
   if (mode == kModeRoute) return launch_one<kModeRoute, 1>(p, stream);
   return launch_one<kModeGroups, 1>(p, stream);
 }
