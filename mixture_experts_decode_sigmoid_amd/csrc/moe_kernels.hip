@@ -2331,15 +2331,29 @@ __device__ inline void zero_partials(const Lds& L, size_t n) {
 
 // out[r][h] = P_shared + sum_p w[r][p] * P[r][p], fp32 FMA chain in slot
 // order, rounded to bf16 once.  Narrow: each product is first summed over
-// the K-phases of its tile in order (the sum a wide job-end reduction forms).
+// the K-phases of its tile in order (sum_kphases: the sum a wide job-end
+// reduction forms).
 __device__ __forceinline__ float down_product(const Params& p, const Lds& L, int r, int slot, int hl) {
   if (!p.narrow) return L.pbuf[((size_t)r * (p.K + 1) + slot) * p.hs + hl];
+  return L.pbuf[((size_t)r * (p.K + 1) + slot) * p.pitch + hl];  // summed by sum_kphases
+}
+
+// Narrow: each (row, slot, h) product is first summed over its K-phases
+// (in order, into the K-phase 0 copy) by one thread per product, so the
+// row's chain below reads one value per slot.  Whole workgroup; ends
+// synchronised.
+__device__ inline void sum_kphases(const Params& p, const Lds& L, const Sched& s) {
   const size_t kstride = (size_t)p.T * (p.K + 1) * p.pitch;
-  const float* q = L.pbuf + ((size_t)r * (p.K + 1) + slot) * p.pitch + hl;
-  float v = 0.f;
-  for (int kp = 0; kp < p.wpt; ++kp) v += q[kp * kstride];
-  if (!isfinite(v)) set_err(p.err, kErrMid);
-  return v;
+  const int n = p.T * (p.K + 1) * s.hc;
+  for (int t = threadIdx.x; t < n; t += kThreads) {
+    const int rs = t / s.hc, hl = t - rs * s.hc;  // rs = row * (K+1) + slot
+    float* q = L.pbuf + (size_t)rs * p.pitch + hl;
+    float v = 0.f;
+    for (int kp = 0; kp < p.wpt; ++kp) v += q[kp * kstride];
+    if (!isfinite(v)) set_err(p.err, kErrMid);
+    q[0] = v;
+  }
+  __syncthreads();
 }
 
 __device__ inline void combine(const Params& p, const Lds& L, const Sched& s) {
@@ -2492,6 +2506,7 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
     const Lds L = lds_map(smem, p);
     const Sched s = make_sched(p, G, 1);
     __syncthreads();
+    sum_kphases(p, L, s);
     combine(p, L, s);
     MOE_STAMP(p, 7);
   }
