@@ -266,7 +266,8 @@ __host__ __device__ inline LdsOffsets lds_offsets(int T, int K, int E, int hs, i
   o.jd = q; q = align_up(q + (narrow ? kJobDescBytes * (size_t)(qcap + gmax) : 0), 16);
   // the routing scratch (used before the stream) overlaps the job-end
   // partials and the down products (used in it), except in a narrow call of
-  // fewer rows than waves, whose free waves stream while rows are routed
+  // at most as many rows as waves, whose waves stream while other rows are
+  // routed
   o.red = q;
   // routing scratch: rb, rgs, rkept, then the top-k candidates (b, s, e) per wave
   const size_t rs = 8 * (size_t)kWaves * E + 8 * (size_t)kWaves * 64 + 4 * (size_t)kWaves * 64 +
@@ -276,7 +277,7 @@ __host__ __device__ inline LdsOffsets lds_offsets(int T, int K, int E, int hs, i
     const size_t pu = 4 * pu_floats(T);
     const size_t pd = 4 * (size_t)wpt * T * (K + 1) * pitch;
     const size_t need = pu > pd ? pu : pd;
-    if (T < kWaves) {
+    if (T <= kWaves) {
       o.pbuf = align_up(q + rs, 16);
       end = o.pbuf + need;
     } else {
@@ -2397,9 +2398,10 @@ __device__ __forceinline__ const Params& fresh_args() {
 
 // The narrow forward after the logits: routing and grouping, the up/gate
 // stream (its sums formed at job ends), the second flag barrier, the down
-// stream, the combine.  With fewer rows than waves, the waves that route no
-// row start on this CU's shared-expert jobs at once, and the others join
-// once the routed tables are written.
+// stream, the combine.  With at most as many rows as waves, the waves that
+// route no row start on this CU's shared-expert jobs at once, the other
+// waves but wave 0 as soon as their row is routed, and wave 0 once it has
+// grouped the uses and written the routed tables.
 template <int FMT, int AL>
 __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
   const int wave = wave_id();
@@ -2414,7 +2416,7 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
     ph.nw = nkb < kWaves ? nkb : kWaves;
     const int sh_tiles = p.n_shared ? p.Is / 8 : 0;
     const int nS = (int)blockIdx.x < sh_tiles ? (sh_tiles - 1 - (int)blockIdx.x) / p.ncu + 1 : 0;
-    const bool early = p.T < kWaves && p.T * p.K <= 64 && nS > 0;
+    const bool early = p.T <= kWaves && p.T * p.K <= 64 && nS > 0;
     stream_init(p, L, nS);
     __syncthreads();
     MOE_STAMP(p, 2);
