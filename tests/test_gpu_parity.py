@@ -34,6 +34,16 @@ SMALL = [
     ("two_down_tiles_wide", dict(hidden=4352, inter=256, shared_inter=256, n_experts=16, top_k=4), 24, 20, "iid"),
     ("mxfp4_two_tiles", dict(hidden=4608, inter=512, shared_inter=256, n_experts=16, top_k=6,
                              routed_fmt=1, bias_bf16=1), 12, 21, "corr"),
+    # up to 4 rows (one activation load per item, 4 lanes per column) and up
+    # to 8 (two loads, 2 lanes per column), with MXFP4 experts, with every
+    # row of one request sharing experts (jobs at full column capacity), and
+    # with two down tiles
+    ("mxfp4_t3", dict(hidden=1536, inter=1536, shared_inter=512, n_experts=16, top_k=6,
+                      routed_fmt=1, bias_bf16=1), 3, 22, "corr"),
+    ("mxfp4_t6", dict(hidden=1536, inter=1536, shared_inter=512, n_experts=16, top_k=6,
+                      routed_fmt=1, bias_bf16=1), 6, 23, "corr"),
+    ("four_rows_one_request", dict(hidden=1024, inter=512, shared_inter=256, n_experts=12, top_k=4), 4, 24, "corr"),
+    ("two_down_tiles_t2", dict(hidden=4352, inter=256, shared_inter=256, n_experts=16, top_k=4), 2, 25, "corr"),
 ]
 
 
