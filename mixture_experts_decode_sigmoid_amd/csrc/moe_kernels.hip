@@ -799,7 +799,12 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   MOE_STAMP(p, 15);
-  if (lane == 0) {
+  if (POLL) {
+    // every lane forms the same sum in pick order; lane k writes weight k
+    double ssum = 0.0;
+    for (int k = 0; k < p.K; ++k) ssum += ps[k];
+    if (lane < p.K) L.w[r * p.K + lane] = (float)(ps[lane] / ssum * p.routed_scale);
+  } else if (lane == 0) {  // (the same values; this form keeps the wide stream's code as measured)
     double ssum = 0.0;
     for (int k = 0; k < p.K; ++k) ssum += ps[k];
     for (int k = 0; k < p.K; ++k) L.w[r * p.K + k] = (float)(ps[k] / ssum * p.routed_scale);
@@ -2225,8 +2230,12 @@ __device__ __forceinline__ void eat_item_n(int split, int lg, const ItemN& it, f
 // activations following in ring_fill_acts), and ring_run multiplies and
 // refills until the last job has ended.  Partials go to LDS, which must be
 // zero where this wave has no items.
-constexpr int kRingD = 5;   // up/gate
+constexpr int kRingD = 5;   // up/gate (and the default)
 constexpr int kRingDD = 6;  // down: its second tile has fewer live rows, so items carry fewer bytes
+// up/gate ring depth by activation loads per item (2 loads: 7 measured
+// best at 8 rows)
+template <int AL>
+constexpr int ring_up() { return AL == 2 ? 7 : kRingD; }
 template <int D = kRingD>
 struct RingN {
   FetchN f;
@@ -2408,7 +2417,7 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
   int jn = 0;  // jobs this wave has ended (for balance)
   bool ok = true;
   {
-    RingN<kRingD> R;
+    RingN<ring_up<AL>()> R;
     const Params& p = fresh_args();
     const Lds L = lds_map(smem, p);
     const int nkb = p.H / 128;
@@ -2460,11 +2469,11 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
       __syncthreads();
       MOE_STAMP(p, 11);
     }
-    ring_open<FMT, 1, kRingD, AL>(p, L, ph, R, 0, nS, ok);
+    ring_open<FMT, 1, ring_up<AL>(), AL>(p, L, ph, R, 0, nS, ok);
     MOE_STAMP(p, 62);
-    ring_fill<FMT, 1, false, kRingD, AL>(p, L, ph, R, nS, ok);
+    ring_fill<FMT, 1, false, ring_up<AL>(), AL>(p, L, ph, R, nS, ok);
     MOE_STAMP(p, 13);
-    ring_run<FMT, 1, false, kRingD, AL>(p, L, ph, R, 0, nS, jn, ok);
+    ring_run<FMT, 1, false, ring_up<AL>(), AL>(p, L, ph, R, 0, nS, jn, ok);
     MOE_WSTAMP(p, 0);
     MOE_TVAL(p, 8, jn);
   }
