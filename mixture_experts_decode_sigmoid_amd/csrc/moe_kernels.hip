@@ -144,12 +144,19 @@ __device__ __forceinline__ uint32_t lmul(uint32_t a, uint32_t b) {
 // p.timeline[blockIdx.x * 64 + i]; MOE_WSTAMP(p, k) has lane 0 of every wave
 // write slot 16 + 8k + wave.
 #ifdef MOE_TIMELINE
-// (global-address-space stores: a generic store would also count on the
-// LDS counter, and the next LDS wait would wait for it)
-#define MOE_TL(p, i) (*(__attribute__((address_space(1))) uint64_t*)((p).timeline + blockIdx.x * 64 + (i)))
+// The stamps are kept in the first 64 LDS words (the layout starts after
+// them in such a build) and copied out at the end of the call: a global
+// store per stamp would make the compiler wait for it before reusing its
+// registers.
+extern __shared__ __attribute__((aligned(16))) char moe_tl_smem[];
+#define MOE_TL(p, i) (((__attribute__((address_space(3))) uint64_t*)(moe_tl_smem))[i])
 #define MOE_STAMP(p, i)                                                                  \
   do {                                                                                   \
     if (threadIdx.x == 0 && (p).timeline) MOE_TL(p, i) = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#define MOE_LSTAMP(p, i)                                                                 \
+  do {                                                                                   \
+    if ((threadIdx.x & 63) == 0 && (p).timeline) MOE_TL(p, i) = __builtin_amdgcn_s_memrealtime(); \
   } while (0)
 #define MOE_WSTAMP(p, k)                                                                 \
   do {                                                                                   \
@@ -174,6 +181,9 @@ __device__ __forceinline__ uint32_t lmul(uint32_t a, uint32_t b) {
   } while (0)
 #define MOE_STAMP(p, i) \
   do {                  \
+  } while (0)
+#define MOE_LSTAMP(p, i) \
+  do {                   \
   } while (0)
 #define MOE_WSTAMP(p, k) \
   do {                   \
@@ -248,7 +258,11 @@ __host__ __device__ inline size_t pu_floats(int T) { return (size_t)kPuWin * kWa
 __host__ __device__ inline LdsOffsets lds_offsets(int T, int K, int E, int hs, int narrow, int wpt, int pitch,
                                                   int qcap) {
   LdsOffsets o;
+#ifdef MOE_TIMELINE
+  size_t q = 64 * 8;  // the stamps first (see MOE_TL)
+#else
   size_t q = 0;
+#endif
   const int uses = T * K, gmax = 1 + T * K;
   o.ids = q; q = align_up(q + 4 * (size_t)uses, 16);
   o.w = q; q = align_up(q + 4 * (size_t)uses, 16);
@@ -402,6 +416,14 @@ __device__ inline double load_bias(const Params& p, int e) {
   return (double)((const float*)p.bias)[e];
 }
 
+// The same in two steps: the bits (bf16 or f32), then the value.
+__device__ __forceinline__ uint32_t load_bias_raw(const Params& p, int e) {
+  return p.bias_bf16 ? (uint32_t)((const uint16_t*)p.bias)[e] : ((const uint32_t*)p.bias)[e];
+}
+__device__ __forceinline__ double bias_from_raw(const Params& p, uint32_t raw) {
+  return (double)(p.bias_bf16 ? bf16_bits_to_f32(raw) : __builtin_bit_cast(float, raw));
+}
+
 // ------------------------------------------------------------------ S2 routing
 
 __device__ __forceinline__ bool key_before(double b1, int e1, double b2, int e2) {
@@ -497,14 +519,19 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 // and l+64 of its chunk in order, the lanes are summed by a fixed tree and
 // the chunk sums in wave order.  Up to 4 dots' loads are issued before any
 // is summed.  Then s = sigmoid(l) and b = s + bias go to the workspace.
-__device__ inline void router_logits(const Params& p, const Lds& L, uint32_t tag) {
+__device__ inline void router_logits(const Params& p, const Lds& L, uint32_t epoch, uint32_t dtag) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int ch = p.H / kWaves, ngrp = ch >> 3;
   const int g0 = lane < ngrp ? lane : ngrp - 1, g1 = lane + 64 < ngrp ? lane + 64 : g0;
   const int nexp = p.E > (int)blockIdx.x ? (p.E - 1 - (int)blockIdx.x) / p.ncu + 1 : 0;
   const int nd = nexp * p.T;
   double* part = L.rb;  // [dot][wave]
-  for (int d0 = 0; d0 < nd; d0 += 4) {
+  // the bias bits of this thread's first dot, loaded ahead of the sums
+  const int d_first = threadIdx.x;
+  uint32_t braw = d_first < nd ? load_bias_raw(p, (int)blockIdx.x + (d_first / p.T) * p.ncu) : 0u;
+  // four dots per pass; the first pass is peeled so that no loop-entry
+  // wait (for the previous pass's unused loads) holds its loads back
+  auto pass = [&](int d0) {
     u32x4 xv[4][2], wv[4][2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -537,44 +564,55 @@ __device__ inline void router_logits(const Params& p, const Lds& L, uint32_t tag
       }
       __builtin_amdgcn_sched_barrier(0);  // one dot's conversions at a time
     }
-  }
+  };
+  if (nd > 0) pass(0);
+  for (int d0 = 4; d0 < nd; d0 += 4) pass(d0);
   __syncthreads();
+  asm volatile("" : "+v"(epoch), "+v"(braw));  // first read here, after the router loads
   for (int d = threadIdx.x; d < nd; d += kThreads) {
     double l = 0.0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) l += part[d * kWaves + w];
     const int e = (int)blockIdx.x + (d / p.T) * p.ncu, r = d % p.T;
     const double s = 1.0 / (1.0 + exp(-l));
-    const double b = s + load_bias(p, e);
+    const double b = s + (d == d_first ? bias_from_raw(p, braw) : load_bias(p, e));
     if (!isfinite(l) || !isfinite(b)) set_err(p.err, kErrScore);
-    publish_score(p, r, e, s, tag);
+    publish_score(p, r, e, s, epoch + dtag);
   }
 }
 
 // The same logits with one wave per (row, expert): lane l sums h = 8l +
 // 512j + 0..7 in order, then a fixed xor butterfly.  The loads of up to 8 j
-// are issued before their products are summed.  Used from 8 rows up, where
+// (16 with LATE) are issued before their products are summed.  Used from 8 rows up, where
 // every wave has rows of its own (and by the wide stream, whose register
 // budget has no room for the chunked form).
-__device__ inline void router_logits_rows(const Params& p, uint32_t tag) {
+// LATE: `v` is the epoch, a load still in flight, first read once the sums
+// are formed (tag = epoch + 1); otherwise `v` is the tag.
+template <bool LATE>
+__device__ inline void router_logits_rows(const Params& p, uint32_t v) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (wave >= kWaves) return;
   for (int e = blockIdx.x; e < p.E; e += p.ncu) {
     const uint16_t* wr = p.router_w + (size_t)e * p.H;
-    const double bias = load_bias(p, e);
+    // LATE: the bias bits are converted once the sums are formed
+    const uint32_t braw = LATE ? load_bias_raw(p, e) : 0u;
+    const double bias = LATE ? 0.0 : load_bias(p, e);
     for (int r = wave; r < p.T; r += kWaves) {
       const uint16_t* xr = p.x + (size_t)r * p.H;
       double acc = 0.0;
-      for (int h0 = 8 * lane; h0 < p.H; h0 += 512 * 8) {
-        u32x4 xv[8], wv[8];
+      // LATE: up to 16 j per pass (one pass at H <= 8192), so the loads
+      // make one round trip
+      constexpr int NJ = LATE ? 16 : 8;
+      for (int h0 = 8 * lane; h0 < p.H; h0 += 512 * NJ) {
+        u32x4 xv[NJ], wv[NJ];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           const int h = h0 + 512 * j < p.H ? h0 + 512 * j : h0;
           xv[j] = ld16(xr + h);
           wv[j] = ld16(wr + h);
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           if (h0 + 512 * j < p.H) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -587,11 +625,13 @@ __device__ inline void router_logits_rows(const Params& p, uint32_t tag) {
       }
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+      uint32_t ep = v, br = braw;
+      if (LATE) asm volatile("" : "+v"(ep), "+v"(br));
       if (lane == 0) {
         double s = 1.0 / (1.0 + exp(-acc));
-        double b = s + bias;
+        double b = s + (LATE ? bias_from_raw(p, br) : bias);
         if (!isfinite(acc) || !isfinite(b)) set_err(p.err, kErrScore);
-        publish_score(p, r, e, s, tag);
+        publish_score(p, r, e, s, LATE ? ep + 1 : v);
       }
     }
   }
@@ -658,7 +698,7 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
     }
     __builtin_amdgcn_s_sleep(1);
   }
-  MOE_STAMP(p, 9);
+  if (r == 0) MOE_LSTAMP(p, 9);
   if (POLL && lane == 0)  // rows whose scores are in (see narrow_forward)
     __hip_atomic_fetch_add((__attribute__((address_space(3))) uint32_t*)(L.misc + kMiscPolled), 1u,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -673,7 +713,7 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
     sv[i] = alive[i] ? s : 0.0;
     bv[i] = isnan(b) ? -INFINITY : b;
   }
-  MOE_STAMP(p, 60);
+  if (r == 0) MOE_LSTAMP(p, 60);
   if (p.ng > 1) {
     const int gsz = p.E / p.ng;
     if (gsz <= 64 && (gsz & (gsz - 1)) == 0) {
@@ -702,15 +742,38 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
 #pragma unroll
       for (int i = 0; i < 4; ++i) gs[i] = t1[i] + t2[i];
       // rank of this lane's group j_i = (lane + 64 i) / gsz among all groups
-      int rank[4] = {0, 0, 0, 0};
-      for (int j = 0; j < p.ng; ++j) {
-        const int first = j * gsz;
-        const double gj = readlane_d(pick4(gs, first >> 6), first & 63);
+      if (POLL && gsz == 32) {
+        // groups 2i and 2i+1 are the halves of slot i: a swap of halves
+        // gives every lane both scores, so every lane holds all groups
+        double glo[4], ghi[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rank[i] += key_before(gj, j, gs[i], (lane + 64 * i) / gsz) ? 1 : 0;
+        for (int i = 0; i < 4; ++i) {
+          const long long u = __double_as_longlong(gs[i]);
+          const auto lo = __builtin_amdgcn_permlane32_swap((unsigned)u, (unsigned)u, false, false);
+          const auto hi = __builtin_amdgcn_permlane32_swap((unsigned)(u >> 32), (unsigned)(u >> 32), false, false);
+          glo[i] = __longlong_as_double(((long long)hi[0] << 32) | lo[0]);
+          ghi[i] = __longlong_as_double(((long long)hi[1] << 32) | lo[1]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int own = 2 * i + (lane >> 5);
+          int rank = 0;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (j < p.ng) rank += key_before((j & 1) ? ghi[j >> 1] : glo[j >> 1], j, gs[i], own) ? 1 : 0;
+          alive[i] = alive[i] && rank < p.kg;
+        }
+      } else {
+        int rank[4] = {0, 0, 0, 0};
+        for (int j = 0; j < p.ng; ++j) {
+          const int first = j * gsz;
+          const double gj = readlane_d(pick4(gs, first >> 6), first & 63);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) rank[i] += key_before(gj, j, gs[i], (lane + 64 * i) / gsz) ? 1 : 0;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) alive[i] = alive[i] && rank[i] < p.kg;
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) alive[i] = alive[i] && rank[i] < p.kg;
     } else {
       double* rb = L.rb + (size_t)wave * p.E;
 #pragma unroll
@@ -742,7 +805,7 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
         if (alive[i]) alive[i] = L.rkept[wave * 64 + (lane + 64 * i) / gsz] != 0;
     }
   }
-  MOE_STAMP(p, 14);
+  if (r == 0) MOE_LSTAMP(p, 14);
   // Top-k among the alive experts by (b desc, e asc), in two steps.
   // (1) Rounded to fp32, keys keep their order (ties aside), so the k-th
   // largest rounded key t is the rounding of the k-th largest exact key,
@@ -786,19 +849,36 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   double* ps = L.rgs + (size_t)wave * 64;  // the winners' s in pick order
-  for (int j = lane; j < nc; j += 64) {
-    const double bj = cb[j];
-    const int ej = ce[j];
-    int rank = 0;
-    for (int q = 0; q < nc; ++q) rank += key_before(cb[q], ce[q], bj, ej) ? 1 : 0;
-    if (rank < p.K) {
-      L.ids[r * p.K + rank] = ej;
-      ps[rank] = cs[j];
+  if (POLL && nc <= 8) {
+    // lane 8a + c compares candidate c with candidate a; a's rank is the
+    // count of its lane group's bits
+    const int a = lane >> 3, c = lane & 7;
+    const bool in = a < nc && c < nc;
+    const int ia = in ? a : 0, ic = in ? c : 0;
+    const double ba = cb[ia], bc = cb[ic];
+    const int ea = ce[ia], ec = ce[ic];
+    const double sa = cs[ia];
+    const unsigned long long before = __ballot(in && key_before(bc, ec, ba, ea));
+    const int rank = __popc((uint32_t)(before >> (8 * a)) & 0xffu);
+    if (in && c == 0 && rank < p.K) {
+      L.ids[r * p.K + rank] = ea;
+      ps[rank] = sa;
+    }
+  } else {
+    for (int j = lane; j < nc; j += 64) {
+      const double bj = cb[j];
+      const int ej = ce[j];
+      int rank = 0;
+      for (int q = 0; q < nc; ++q) rank += key_before(cb[q], ce[q], bj, ej) ? 1 : 0;
+      if (rank < p.K) {
+        L.ids[r * p.K + rank] = ej;
+        ps[rank] = cs[j];
+      }
     }
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  MOE_STAMP(p, 15);
+  if (r == 0) MOE_LSTAMP(p, 15);
   if (POLL) {
     // every lane forms the same sum in pick order; lane k writes weight k
     double ssum = 0.0;
@@ -1831,6 +1911,12 @@ __device__ __forceinline__ void up_job(const Params& p, const Sched& s, int j, i
 // The narrow stream's state and the tables of this CU's shared-expert jobs
 // (local jobs 0..nS-1; they need no routing).  Whole workgroup, plain
 // per-thread LDS accesses; the caller synchronises.
+// This CU's shared-expert up/gate jobs (dealt c, c + ncu, ...).
+__device__ __forceinline__ int shared_jobs_here(const Params& p) {
+  const int sh_tiles = p.n_shared ? p.Is / 8 : 0;
+  return (int)blockIdx.x < sh_tiles ? (sh_tiles - 1 - (int)blockIdx.x) / p.ncu + 1 : 0;
+}
+
 __device__ inline void stream_init(const Params& p, const Lds& L, int nS) {
   const int tid = threadIdx.x;
   for (int k = tid; k < nS; k += kThreads)
@@ -1854,19 +1940,25 @@ __device__ inline void stream_init(const Params& p, const Lds& L, int nS) {
 // The tables that need the routing: the routed up/gate jobs (local jobs
 // nS..nU-1) and one down job per group at qcap + g, written by threads
 // first, first + stride, ...; then nU.
+// PART: 1 the up/gate jobs and nU, 2 the down jobs, 3 both.
+template <int PART = 3>
 __device__ inline void routed_tables(const Params& p, const Lds& L, const Sched& s, int nS, int nU, int first,
                                      int stride) {
-  for (int k = nS + first; k < nU; k += stride) {
-    int g, tile;
-    up_job(p, s, (int)blockIdx.x + k * p.ncu, g, tile);
-    const bool sh = shared_group(p, g);
-    L.jd[k] = make_desc(p, true, sh, sh ? 0 : L.gexp[g], tile, sh ? p.T : L.gcnt[g], sh ? 0 : L.gstart[g]);
+  if (PART & 1) {
+    for (int k = nS + first; k < nU; k += stride) {
+      int g, tile;
+      up_job(p, s, (int)blockIdx.x + k * p.ncu, g, tile);
+      const bool sh = shared_group(p, g);
+      L.jd[k] = make_desc(p, true, sh, sh ? 0 : L.gexp[g], tile, sh ? p.T : L.gcnt[g], sh ? 0 : L.gstart[g]);
+    }
   }
-  for (int g = first; g < s.G; g += stride) {
-    const bool sh = shared_group(p, g);
-    L.jd[p.qcap + g] = make_desc(p, false, sh, sh ? 0 : L.gexp[g], 0, sh ? p.T : L.gcnt[g], sh ? 0 : L.gstart[g]);
+  if (PART & 2) {
+    for (int g = first; g < s.G; g += stride) {
+      const bool sh = shared_group(p, g);
+      L.jd[p.qcap + g] = make_desc(p, false, sh, sh ? 0 : L.gexp[g], 0, sh ? p.T : L.gcnt[g], sh ? 0 : L.gstart[g]);
+    }
   }
-  if (first == 0) L.misc[kMiscNU] = nU;
+  if ((PART & 1) && first == 0) L.misc[kMiscNU] = nU;
 }
 
 // Per-wave constants of a phase (KIND 1 up/gate, 2 down).  Up/gate: every
@@ -2423,38 +2515,40 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
     const int nkb = p.H / 128;
     PhaseN ph = {};
     ph.nw = nkb < kWaves ? nkb : kWaves;
-    const int sh_tiles = p.n_shared ? p.Is / 8 : 0;
-    const int nS = (int)blockIdx.x < sh_tiles ? (sh_tiles - 1 - (int)blockIdx.x) / p.ncu + 1 : 0;
+    const int nS = shared_jobs_here(p);
     const bool early = p.T <= kWaves && p.T * p.K <= 64 && nS > 0;
-    stream_init(p, L, nS);
-    __syncthreads();
     MOE_STAMP(p, 2);
     if (early) {
-      // The streaming waves start once every row's scores are in: their
-      // loads would otherwise queue ahead of the polls.  The routing waves
-      // run at raised priority until their rows are routed.
-      if (wave < p.T) {
+      // The top T waves route (row r by wave 7 - r; the scores of a batch
+      // under 8 rows are published by wave 0), wave 7 then groups.  The
+      // streaming waves start once every row's scores are in: their loads
+      // would otherwise queue ahead of the polls.  The routing waves run at
+      // raised priority until their rows are routed.
+      const int r = kWaves - 1 - wave;
+      if (r < p.T) {
         __builtin_amdgcn_s_setprio(3);
-        route_row<true>(p, L, wave, epoch + 1);
-        if (wave != 0) __builtin_amdgcn_s_setprio(0);
+        route_row<true>(p, L, r, epoch + 1);
+        if (r != 0) __builtin_amdgcn_s_setprio(0);
         lds_inc_lane0((uint32_t*)(L.misc + kMiscRouted));  // after this wave's ids / w writes (LDS order)
       }
-      if (wave == 0) {
+      if (r == 0) {
         lds_wait<1>(p, (const uint32_t*)L.misc + kMiscRouted, (uint32_t)p.T, ok);
-        MOE_STAMP(p, 10);
+        MOE_LSTAMP(p, 10);
         groups_one_wave(p, L);
         wave_sync();
-        MOE_STAMP(p, 3);
+        MOE_LSTAMP(p, 3);
         const int G = lds_ldi_uniform(L.misc);
         const Sched s = make_sched(p, G, 1);
         const int nU = (int)blockIdx.x < s.n_jobs ? (s.n_jobs - 1 - (int)blockIdx.x) / p.ncu + 1 : 0;
-        routed_tables(p, L, s, nS, nU, threadIdx.x & 63, 64);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tables, before the flag
+        routed_tables<1>(p, L, s, nS, nU, threadIdx.x & 63, 64);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the up/gate tables, before the flag
         lds_st32(L.misc + kMiscReady, 1u);
+        // the down tables are read after the phase barrier
+        routed_tables<2>(p, L, s, nS, nU, threadIdx.x & 63, 64);
         __builtin_amdgcn_s_setprio(0);
-        MOE_STAMP(p, 11);
+        MOE_LSTAMP(p, 11);
       }
-      if (wave >= p.T) lds_wait<1>(p, (const uint32_t*)L.misc + kMiscPolled, (uint32_t)p.T, ok);
+      if (r >= p.T) lds_wait<1>(p, (const uint32_t*)L.misc + kMiscPolled, (uint32_t)p.T, ok);
     } else {
       for (int r = wave; r < p.T; r += kWaves) route_row<true>(p, L, r, epoch + 1);
       __syncthreads();
@@ -2520,6 +2614,10 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
     sum_kphases(p, L, s);
     combine(p, L, s);
     MOE_STAMP(p, 7);
+#ifdef MOE_TIMELINE
+    __syncthreads();
+    if (threadIdx.x < 64 && p.timeline) p.timeline[blockIdx.x * 64 + threadIdx.x] = MOE_TL(p, threadIdx.x);
+#endif
   }
 }
 
@@ -2536,6 +2634,29 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   const int tid = threadIdx.x, wave = wave_id();
 
   MOE_STAMP(p, 0);
+  if (NARROW && MODE == kModeForward) {
+    // Every wave reads the epoch for itself and first needs it to tag its
+    // scores, after the router loads have come in.  The stream's LDS words
+    // are set before the first meeting.  The scores are read through their
+    // tags, so no flag is raised after them (waiting for the score stores
+    // to reach memory would hold the workgroup for a store round trip).
+    const uint32_t ep = __hip_atomic_load(&p.flags[blockIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < 64) L.ctl[tid] = 0u;
+    stream_init(p, L, shared_jobs_here(p));
+    __syncthreads();
+    if (NARROW == 2 || p.T < kWaves) {  // (NARROW 2 runs at most 4 rows)
+      router_logits(p, L, ep, 1u);
+      // the logit partials lie in wave 0's routing scratch (wave 0 reads
+      // them) unless the experts are few
+      const int nd = (p.E > (int)blockIdx.x ? (p.E - 1 - (int)blockIdx.x) / p.ncu + 1 : 0) * p.T;
+      if (kWaves * nd > p.E) __syncthreads();
+    } else {
+      router_logits_rows<true>(p, ep);
+    }
+    MOE_STAMP(p, 1);
+    narrow_forward<FMT, NARROW == 2 ? 1 : NARROW == 3 ? 2 : 4>(smem, __builtin_amdgcn_readfirstlane(ep));
+    return;
+  }
   if (tid < 64) L.ctl[tid] = 0u;
   if (tid == 0)
     L.misc[1] = (int32_t)__hip_atomic_load(&p.flags[blockIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -2543,15 +2664,11 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   const uint32_t epoch = (uint32_t)__builtin_amdgcn_readfirstlane(L.misc[1]);
 
   // S0: router logits of this CU's experts, published for every CU
-  if (NARROW && p.T < kWaves) router_logits(p, L, epoch + 1);
-  else router_logits_rows(p, epoch + 1);
+  if (NARROW && p.T < kWaves) router_logits(p, L, epoch, 1u);
+  else router_logits_rows<false>(p, epoch + 1);
   publish(p, epoch + 1);
   MOE_STAMP(p, 1);
   if (MODE != kModeForward && blockIdx.x != 0) return;
-  if (NARROW && MODE == kModeForward) {
-    narrow_forward<FMT, NARROW == 2 ? 1 : NARROW == 3 ? 2 : 4>(smem, epoch);
-    return;
-  }
 
   // S2 (wide stream, and the routing-only calls): route every row, then
   // group the step's distinct experts.  A wave of a narrow call has at most
@@ -2634,6 +2751,10 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   // S5: combine this CU's output rows
   combine(p, L, s);
   MOE_STAMP(p, 7);
+#ifdef MOE_TIMELINE
+  __syncthreads();
+  if (tid < 64 && p.timeline) p.timeline[blockIdx.x * 64 + tid] = MOE_TL(p, tid);
+#endif
 }
 
 // ------------------------------------------------------------------ host glue
