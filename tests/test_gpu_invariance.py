@@ -137,3 +137,61 @@ def test_rows_zero_and_limits():
     with pytest.raises(moe.MoeError) as e:
         layer.forward(case["x"], out=case["x"])
     assert e.value.code == moe.MOE_ERR_ALIAS
+
+
+# DeepSeek-V3 routing geometry (256 experts in 8 groups of 32, keep 4,
+# top-8) on a small layer: the paths that hold for 32-lane groups and for
+# ties at the top-k threshold.
+V3R = dict(hidden=1024, inter=256, shared_inter=256, n_experts=256, top_k=8, n_group=8, topk_group=4)
+
+
+def _route_both(spec, case, T):
+    layer = _layer(spec, case, T)
+    ids, wts = layer.route(case["x"])
+    ids_o, w_o, _, _ = oracle_route(spec, case)
+    ids = ids.cpu().numpy()
+    assert np.array_equal(ids, ids_o)
+    assert np.allclose(wts.cpu().numpy(), w_o, rtol=1e-6, atol=0)
+    return ids
+
+
+@pytest.mark.parametrize("T", [1, 3, 8])
+def test_routing_group_tie_at_the_kept_boundary(T):
+    """Groups 2 and 5 are copies of each other and tie for the last kept
+    group: the lower group (2) is kept, so its experts are picked and group
+    5's identical ones are not."""
+    say(f"group tie T={T}")
+    spec = fixtures.spec_with("tiny", **V3R)
+    case = gpu_case(spec, T, 31)
+    rw, bias = case["router_w"], case["bias"]
+    bias.zero_()
+    for g in (0, 1, 3):
+        bias[32 * g + 1] = 5.0
+        bias[32 * g + 7] = 5.0
+    bias[64 + 2] = 3.0
+    bias[64 + 9] = 3.0
+    rw[160:192] = rw[64:96]
+    bias[160:192] = bias[64:96]
+    ids = _route_both(spec, case, T)
+    for r in range(T):
+        row = set(ids[r].tolist())
+        assert {66, 73} <= row and not row & set(range(160, 192))
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_routing_ties_past_k(T):
+    """Ten experts (five in each of groups 0 and 1) share one router row and
+    one bias, so the top-k threshold is a ten-way exact tie: the eight lowest
+    indices win, in index order."""
+    say(f"ties past k T={T}")
+    spec = fixtures.spec_with("tiny", **V3R)
+    case = gpu_case(spec, T, 32)
+    rw, bias = case["router_w"], case["bias"]
+    bias.zero_()
+    tied = [0, 1, 2, 3, 4, 32, 33, 34, 35, 36]
+    for e in tied:
+        rw[e] = rw[0]
+        bias[e] = 3.0
+    ids = _route_both(spec, case, T)
+    for r in range(T):
+        assert ids[r].tolist() == tied[:8]
