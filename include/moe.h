@@ -63,7 +63,7 @@ extern "C" {
 #define MOE_ERR_ALIGN 4     /* a pointer is not 16-byte aligned */
 #define MOE_ERR_ROWS 5      /* rows < 0, rows > max_rows, or max_rows > 64 */
 #define MOE_ERR_WORKSPACE 6 /* workspace too small or not initialised */
-#define MOE_ERR_ALIAS 7     /* out overlaps x */
+#define MOE_ERR_ALIAS 7     /* out overlaps x, or a residual overlaps out without being it */
 #define MOE_ERR_HIP 8       /* a HIP runtime call failed; see moe_last_hip_error() */
 
 /* ---- device error bits (moe_read_error) ---- */
@@ -141,6 +141,21 @@ int moe_groups(const moe_config* cfg, const moe_weights* w, const uint16_t* x, i
  * writes each row once.  rows == 0 is a no-op.  out must not overlap x. */
 int moe_forward(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
                 uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/* The fused layer with the residual add folded into its combine:
+ * out[r, h] = bf16_RNE(P_shared + sum_p w[r,p] * P[r,p,h] + residual[r, h]),
+ * the residual (bf16, [rows, H], row-major) added in fp32 after the same
+ * fixed-order chain moe_forward forms, then rounded once.  This is the
+ * fourth launch of the unfused layout (the "add" after the routed and the
+ * shared expert paths) that the fused kernel absorbs, as described in
+ * "Daily AI Hotspot 2026-08-21: Shared-Expert Fusion Lands on NVIDIA and AMD
+ * the Same Day", section "Most Worth Your Attention Today".
+ * residual is device memory the caller owns; it may be out itself (in-place
+ * add: each element is read before it is written, by the same thread) but
+ * may not overlap out otherwise (MOE_ERR_ALIAS); NULL with rows > 0 gives
+ * MOE_ERR_NULL.  Everything else is as for moe_forward. */
+int moe_forward_residual(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
+                         const uint16_t* residual, uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
 /* Waits for `stream`, then returns the workspace's device error bits in
  * *bits (host) and clears them. */

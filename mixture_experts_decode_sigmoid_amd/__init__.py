@@ -74,19 +74,20 @@ def lib() -> C.CDLL:
         L.moe_route.argtypes = [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, P, Z, P]
         L.moe_groups.argtypes = [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, Z, P]
         L.moe_forward.argtypes = [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, Z, P]
+        L.moe_forward_residual.argtypes = [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, P, Z, P]
         L.moe_read_error.argtypes = [P, P, C.POINTER(C.c_uint32)]
         L.moe_strerror.argtypes = [I]
         L.moe_strerror.restype = C.c_char_p
         L.moe_last_hip_error.argtypes = []
         for f in ("moe_workspace_size", "moe_workspace_init", "moe_route", "moe_groups",
-                  "moe_forward", "moe_read_error", "moe_last_hip_error"):
+                  "moe_forward", "moe_forward_residual", "moe_read_error", "moe_last_hip_error"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
 
 
 EXPORTS = ("moe_workspace_size", "moe_workspace_init", "moe_route", "moe_groups",
-           "moe_forward", "moe_read_error", "moe_strerror", "moe_last_hip_error")
+           "moe_forward", "moe_forward_residual", "moe_read_error", "moe_strerror", "moe_last_hip_error")
 
 
 def strerror(code: int) -> str:
@@ -161,6 +162,12 @@ def moe_forward(cfg, w, x, out, ws, stream=None):
                              _ptr(ws), ws.numel(), _stream(stream)), "moe_forward")
 
 
+def moe_forward_residual(cfg, w, x, residual, out, ws, stream=None):
+    """x, residual, out: [rows, H] bf16 (device); residual may be out."""
+    _check(lib().moe_forward_residual(C.byref(cfg), C.byref(w), _ptr(x), int(x.shape[0]), _ptr(residual),
+                                      _ptr(out), _ptr(ws), ws.numel(), _stream(stream)), "moe_forward_residual")
+
+
 def moe_read_error(ws, stream=None) -> int:
     bits = C.c_uint32(0)
     _check(lib().moe_read_error(_ptr(ws), _stream(stream), C.byref(bits)), "moe_read_error")
@@ -183,10 +190,14 @@ class Layer:
         self.w = make_weights(case)
         self.ws = new_workspace(self.cfg, device)
 
-    def forward(self, x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    def forward(self, x: torch.Tensor, out: torch.Tensor | None = None, stream=None,
+                residual: torch.Tensor | None = None) -> torch.Tensor:
         if out is None:
             out = torch.empty_like(x)
-        moe_forward(self.cfg, self.w, x, out, self.ws, stream)
+        if residual is None:
+            moe_forward(self.cfg, self.w, x, out, self.ws, stream)
+        else:
+            moe_forward_residual(self.cfg, self.w, x, residual, out, self.ws, stream)
         return out
 
     def route(self, x: torch.Tensor, stream=None):

@@ -206,8 +206,8 @@ int moe_groups(const moe_config* cfg, const moe_weights* w, const uint16_t* x, i
   return do_launch(p, kModeGroups, stream);
 }
 
-int moe_forward(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
-                uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+static int forward(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
+                   const uint16_t* residual, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
   Params p;
   int rc = fill(cfg, w, x, rows, ws, ws_bytes, p, kModeForward);
   if (rc == kNoRows) return MOE_OK;
@@ -217,9 +217,27 @@ int moe_forward(const moe_config* cfg, const moe_weights* w, const uint16_t* x, 
   const size_t nb = (size_t)rows * cfg->hidden * 2;
   const char *xo = (const char*)x, *oo = (const char*)out;
   if (rows > 0 && xo < oo + nb && oo < xo + nb) return MOE_ERR_ALIAS;
+  if (residual) {
+    // the residual may be out itself (each element is read, then written,
+    // by one thread) but may not overlap it otherwise
+    const char* ro = (const char*)residual;
+    if (ro != oo && ro < oo + nb && oo < ro + nb) return MOE_ERR_ALIAS;
+  }
   if (rows == 0) return MOE_OK;
   p.out = out;
+  p.residual = residual;
   return do_launch(p, kModeForward, stream);
+}
+
+int moe_forward(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
+                uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  return forward(cfg, w, x, rows, nullptr, out, ws, ws_bytes, stream);
+}
+
+int moe_forward_residual(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
+                         const uint16_t* residual, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  if (rows > 0 && !residual) return MOE_ERR_NULL;
+  return forward(cfg, w, x, rows, residual, out, ws, ws_bytes, stream);
 }
 
 int moe_read_error(void* ws, void* stream, uint32_t* bits) {
@@ -246,7 +264,7 @@ const char* moe_strerror(int code) {
     case MOE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case MOE_ERR_ROWS: return "rows out of range (0..max_rows, max_rows <= 64)";
     case MOE_ERR_WORKSPACE: return "workspace too small";
-    case MOE_ERR_ALIAS: return "out overlaps x";
+    case MOE_ERR_ALIAS: return "out overlaps x, or the residual overlaps out without being it";
     case MOE_ERR_HIP: return "HIP runtime error";
     default: return "unknown error code";
   }

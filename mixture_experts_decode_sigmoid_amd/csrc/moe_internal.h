@@ -18,7 +18,7 @@ constexpr int kMaxGroups = 64;            // router groups
 constexpr int kMaxSlice = 64;             // output rows per CU in down
 constexpr int kMinLds = 84 * 1024;        // LDS per workgroup: more than half a CU's, so one per CU
 
-enum Mode { kModeForward = 0, kModeRoute = 1, kModeGroups = 2 };
+enum Mode { kModeForward = 0, kModeRoute = 1, kModeGroups = 2, kModeForwardRes = 3 };  // 3: kernel only (wide stream with a residual)
 
 // Workspace layout (byte offsets from the workspace base).
 struct WsLayout {
@@ -57,7 +57,10 @@ struct Params {
   uint16_t* out;
   int32_t* ids_out;
   float* w_out;
-  int32_t* groups_out;
+  union {
+    int32_t* groups_out;       // groups mode
+    const uint16_t* residual;  // forward: optional [T, H] bf16 added in the combine (NULL: none)
+  };
   // workspace
   uint32_t* flags;
   uint32_t* err;
@@ -71,5 +74,7 @@ WsLayout ws_layout(int max_rows, int E, int K, int H, int I, int Is);
 // narrow (narrow = 1) or wide layout and returns the LDS bytes it needs.
 size_t stream_geometry(Params& p, int narrow);
 hipError_t launch(const Params& p, int mode, hipStream_t stream);
+// The forward of the wide stream with a residual (moe_kernels_res.hip).
+hipError_t launch_res_wide(const Params& p, hipStream_t stream);
 
 }  // namespace moe

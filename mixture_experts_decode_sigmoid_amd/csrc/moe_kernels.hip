@@ -308,6 +308,7 @@ __host__ __device__ inline LdsOffsets lds_offsets(int T, int K, int E, int hs, i
   return o;
 }
 
+#ifndef MOE_RES_WIDE_TU
 size_t stream_geometry(Params& p, int narrow) {
   const int nrt = (p.hs + 15) / 16;
   p.nrt_p = nrt <= 1 ? 1 : nrt <= 2 ? 2 : 4;
@@ -322,6 +323,7 @@ size_t stream_geometry(Params& p, int narrow) {
   p.qcap = (int)((jobs + p.ncu - 1) / p.ncu);
   return lds_offsets(p.T, p.K, p.E, p.hs, p.narrow, p.wpt, p.pitch, p.qcap).total;
 }
+#endif
 
 __device__ inline Lds lds_map(char* base, const Params& p) {
   LdsOffsets o = lds_offsets(p.T, p.K, p.E, p.hs, p.narrow, p.wpt, p.pitch, p.qcap);
@@ -2458,12 +2460,20 @@ __device__ inline void sum_kphases(const Params& p, const Lds& L, const Sched& s
   __syncthreads();
 }
 
+// RES: a residual, when given, is added in fp32 after the chain, then
+// rounded once (the residual add of the unfused layout, folded in).  The
+// wide stream has a kernel of its own for it (kModeForwardRes), so that its
+// residual-free kernel keeps its code.
+template <bool RES>
 __device__ inline void combine(const Params& p, const Lds& L, const Sched& s) {
   for (int t = threadIdx.x; t < p.T * s.hc; t += kThreads) {
     const int r = t / s.hc, hl = t - r * s.hc;
+    const size_t o = (size_t)r * p.H + s.h0 + hl;
+    const uint32_t res = RES && p.residual ? p.residual[o] : 0u;  // issued ahead of the chain
     float acc = p.n_shared ? down_product(p, L, r, p.K, hl) : 0.f;
     for (int k = 0; k < p.K; ++k) acc = fmaf(L.w[r * p.K + k], down_product(p, L, r, k, hl), acc);
-    p.out[(size_t)r * p.H + s.h0 + hl] = (uint16_t)f32_to_bf16_rne(acc);
+    if (RES && p.residual) acc += bf16_bits_to_f32(res);
+    p.out[o] = (uint16_t)f32_to_bf16_rne(acc);
   }
 }
 
@@ -2612,7 +2622,7 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
     const Sched s = make_sched(p, G, 1);
     __syncthreads();
     sum_kphases(p, L, s);
-    combine(p, L, s);
+    combine<true>(p, L, s);
     MOE_STAMP(p, 7);
 #ifdef MOE_TIMELINE
     __syncthreads();
@@ -2634,7 +2644,8 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   const int tid = threadIdx.x, wave = wave_id();
 
   MOE_STAMP(p, 0);
-  if (NARROW && MODE == kModeForward) {
+  constexpr bool kFwd = MODE == kModeForward || MODE == kModeForwardRes;
+  if (NARROW && kFwd) {
     // Every wave reads the epoch for itself and first needs it to tag its
     // scores, after the router loads have come in.  The stream's LDS words
     // are set before the first meeting.  The scores are read through their
@@ -2668,7 +2679,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   else router_logits_rows<false>(p, epoch + 1);
   publish(p, epoch + 1);
   MOE_STAMP(p, 1);
-  if (MODE != kModeForward && blockIdx.x != 0) return;
+  if (!kFwd && blockIdx.x != 0) return;
 
   // S2 (wide stream, and the routing-only calls): route every row, then
   // group the step's distinct experts.  A wave of a narrow call has at most
@@ -2749,7 +2760,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   __syncthreads();
 
   // S5: combine this CU's output rows
-  combine(p, L, s);
+  combine<MODE == kModeForwardRes>(p, L, s);
   MOE_STAMP(p, 7);
 #ifdef MOE_TIMELINE
   __syncthreads();
@@ -2759,6 +2770,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
 
 // ------------------------------------------------------------------ host glue
 
+#ifndef MOE_RES_WIDE_TU
 WsLayout ws_layout(int max_rows, int E, int K, int H, int I, int Is) {
   (void)H;
   WsLayout w;
@@ -2772,6 +2784,8 @@ WsLayout ws_layout(int max_rows, int E, int K, int H, int I, int Is) {
   return w;
 }
 
+#endif
+
 template <int MODE, int FMT, int NARROW = 1>
 static hipError_t launch_one(const Params& p, hipStream_t stream) {
   auto kfn = moe_fused<MODE, FMT, NARROW>;
@@ -2781,10 +2795,12 @@ static hipError_t launch_one(const Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+#ifndef MOE_RES_WIDE_TU
 hipError_t launch(const Params& p, int mode, hipStream_t stream) {
   const bool wide = !p.narrow;
   const int nk = p.T <= 4 ? 2 : p.T <= 8 ? 3 : 1;  // narrow kernel by batch size
-  if (p.routed_fmt == 0) {
+  const bool wide_res = mode == kModeForward && wide && p.residual;
+  if (p.routed_fmt == 0 && !wide_res) {
     if (mode == kModeForward)
       return wide      ? launch_one<kModeForward, 0, 0>(p, stream)
              : nk == 2 ? launch_one<kModeForward, 0, 2>(p, stream)
@@ -2793,13 +2809,25 @@ hipError_t launch(const Params& p, int mode, hipStream_t stream) {
     if (mode == kModeRoute) return launch_one<kModeRoute, 0>(p, stream);
     return launch_one<kModeGroups, 0>(p, stream);
   }
-  if (mode == kModeForward)
-    return wide      ? launch_one<kModeForward, 1, 0>(p, stream)
-           : nk == 2 ? launch_one<kModeForward, 1, 2>(p, stream)
-           : nk == 3 ? launch_one<kModeForward, 1, 3>(p, stream)
-                     : launch_one<kModeForward, 1, 1>(p, stream);
-  if (mode == kModeRoute) return launch_one<kModeRoute, 1>(p, stream);
-  return launch_one<kModeGroups, 1>(p, stream);
+  if (!wide_res) {
+    if (mode == kModeForward)
+      return wide      ? launch_one<kModeForward, 1, 0>(p, stream)
+             : nk == 2 ? launch_one<kModeForward, 1, 2>(p, stream)
+             : nk == 3 ? launch_one<kModeForward, 1, 3>(p, stream)
+                       : launch_one<kModeForward, 1, 1>(p, stream);
+    if (mode == kModeRoute) return launch_one<kModeRoute, 1>(p, stream);
+    return launch_one<kModeGroups, 1>(p, stream);
+  }
+  return launch_res_wide(p, stream);
 }
+#else
+// The wide stream with a residual: its kernels are built in a translation
+// unit of their own (moe_kernels_res.hip), so that the code object of the
+// other kernels is the same with or without them.
+hipError_t launch_res_wide(const Params& p, hipStream_t stream) {
+  return p.routed_fmt == 0 ? launch_one<kModeForwardRes, 0, 0>(p, stream)
+                           : launch_one<kModeForwardRes, 1, 0>(p, stream);
+}
+#endif
 
 }  // namespace moe

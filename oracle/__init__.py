@@ -200,5 +200,26 @@ def forward(spec, case, rows=None, nthreads=0):
     return out64, outb
 
 
+def forward_residual(spec, case, residual, rows=None, nthreads=0):
+    """The layer with the residual add folded in: the add that follows the
+    routed and shared expert paths as the fourth launch of the unfused layout
+    ("Daily AI Hotspot 2026-08-21: Shared-Expert Fusion Lands on NVIDIA and
+    AMD the Same Day", section "Most Worth Your Attention Today").  Reading:
+    out = bf16_RNE(layer + residual), the sum in fp64, rounded once.
+    residual: [T,H] bf16 bits (u16).  Returns (out64, out_bf16) as forward
+    does, for the listed rows."""
+    out64, _ = forward(spec, case, rows=rows, nthreads=nthreads)
+    res = _c(residual, np.uint16)
+    T, H = res.shape
+    o64 = np.full((T, H), np.nan)
+    ob = np.zeros((T, H), np.uint16)
+    for r in (range(T) if rows is None else rows):
+        for h in range(H):
+            v = float(out64[r, h]) + dec_bf16(res[r, h])
+            o64[r, h] = v
+            ob[r, h] = bf16_rne(v)
+    return o64, ob
+
+
 def max_threads() -> int:
     return int(lib().oracle_max_threads())

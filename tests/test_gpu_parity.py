@@ -152,3 +152,46 @@ def test_full_size_sampled(full_cases, name, rows):
     say(f"  rel_l2={rel:.3e} max_abs={mx:.3e}")
     assert rel <= REL_L2 and mx <= MAX_ABS
     assert np.all(np.isfinite(out.view(np.int16).astype(np.float64)))
+
+
+# The residual add folded into the combine (moe_forward_residual): parity with
+# the oracle's one-rounding reading, in place (residual is out) equal to out
+# of place bit for bit, in the 1-row, 8-row narrow and the wide stream.
+RESID = [
+    ("tiny_t1", dict(), 1, 41, "iid"),
+    ("tiny_t8", dict(), 8, 42, "corr"),
+    ("multichunk_ragged_t9", dict(hidden=1152, inter=640, shared_inter=384, n_experts=24, top_k=5), 9, 43, "corr"),
+    ("wide_t37", dict(hidden=512, inter=256, shared_inter=256, n_experts=16, top_k=4), 37, 44, "iid"),
+]
+
+
+@pytest.mark.parametrize("name,over,T,seed,rows", RESID, ids=[s[0] for s in RESID])
+def test_residual_parity(name, over, T, seed, rows):
+    import oracle
+    say(f"residual {name} T={T}")
+    spec = _spec(over)
+    case = gpu_case(spec, T, seed, rows=rows, requests=max(1, T // 4))
+    layer = moe.Layer(spec, case, max_rows=T)
+    H = spec["hidden"]
+    res = torch.randn(T, H, generator=torch.Generator().manual_seed(seed)).bfloat16().cuda()
+    out = layer.forward(case["x"], residual=res)
+    torch.cuda.synchronize()
+    assert layer.read_error() == 0
+    got = fixtures.bits16(out)
+    ids, _, _, _ = oracle_route(spec, case)
+    used = sorted(set(int(e) for r in range(T) for e in ids[r]))
+    h = fixtures.host_case(case, experts=used)
+    o64, _ = oracle.forward_residual(spec, h, fixtures.bits16(res))
+    rel, mx = parity(got, o64, list(range(T)))
+    assert rel <= REL_L2 and mx <= MAX_ABS, (rel, mx)
+    # in place: the residual buffer receives the output
+    inplace = res.clone()
+    layer.forward(case["x"], out=inplace, residual=inplace)
+    torch.cuda.synchronize()
+    assert np.array_equal(fixtures.bits16(inplace), got)
+    # a zero residual gives moe_forward's output bit for bit (no negative zeros
+    # in a random layer's output)
+    plain = run_forward(layer, case["x"])
+    zero = layer.forward(case["x"], residual=torch.zeros_like(res))
+    torch.cuda.synchronize()
+    assert np.array_equal(fixtures.bits16(zero), plain)

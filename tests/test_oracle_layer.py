@@ -204,3 +204,30 @@ def test_missing_used_expert_is_an_error(orc):
     h2 = dict(h); h2["w_gate_up"] = list(h["w_gate_up"]); h2["w_gate_up"][int(ids[0, 0])] = None
     with pytest.raises(ValueError):
         orc.forward(spec, h2)
+
+
+# ---------------------------------------------------------------- residual
+def test_residual_zero_is_the_layer(orc):
+    """A zero residual (either sign) leaves the layer's output as it is."""
+    spec, h = _tiny(T=3)
+    out64, outb = orc.forward(spec, h)
+    zero = np.zeros_like(h["x"])
+    o64, ob = orc.forward_residual(spec, h, zero)
+    assert np.array_equal(o64, out64) and np.array_equal(ob, outb)
+    o64n, obn = orc.forward_residual(spec, h, zero | np.uint16(0x8000))
+    assert np.array_equal(o64n, out64 + 0.0) and np.array_equal(obn, outb)
+
+
+def test_residual_alone_with_zero_weights(orc):
+    """With every expert weight zero the layer is exactly 0, so the output is
+    the residual itself, bit for bit (it is already bf16)."""
+    spec, h = _tiny(T=2)
+    hz = dict(h)
+    for k in ("w_gate_up", "w_down"):
+        hz[k] = [np.zeros_like(a) for a in h[k]]
+    hz["sh_w_gate_up"] = np.zeros_like(h["sh_w_gate_up"])
+    hz["sh_w_down"] = np.zeros_like(h["sh_w_down"])
+    res = fixtures.bits16(torch.randn(2, 256, generator=torch.Generator().manual_seed(5)).bfloat16())
+    o64, ob = orc.forward_residual(spec, hz, res)
+    assert np.array_equal(ob, res)
+    assert np.array_equal(o64, _bf(res))
