@@ -36,7 +36,7 @@ EXTRA = ("v3_t8", "v3_t64")
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("moe_kernels.hip", "moe_api.cpp", "moe_internal.h"):
+    for f in ("moe_kernels.hip", "moe_kernels_res.hip", "moe_api.cpp", "moe_internal.h"):
         with open(os.path.join(ROOT, "mixture_experts_decode_sigmoid_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
