@@ -32,6 +32,8 @@ PEAK_HBM_GBS = 8000.0
 N_COPIES = 4
 HEADLINE = "v3_t1"
 EXTRA = ("v3_t8", "v3_t64")
+# one GPU's share of the layer under 8-way tensor parallelism (own weights)
+EXTRA_SHARD = ("v3tp8_t1", "v3tp8_t8")
 
 
 def kernel_source_hash() -> str:
@@ -181,6 +183,20 @@ def main():
             extra[name] = dict(rows=T, distinct_experts=d_t, us_per_call=round(us_t, 2),
                                algorithmic_bytes=b_t, gbs=round(b_t / (us_t * 1e-6) / 1e9, 1),
                                frac_of_peak=round(b_t / (us_t * 1e-6) / 1e9 / PEAK_HBM_GBS, 4))
+
+        del copies
+        torch.cuda.empty_cache()
+        for name in EXTRA_SHARD:
+            spec_s, case_s = fixtures.make_workload(name, device="cuda")
+            cps = build_copies(spec_s, case_s, N_COPIES)
+            T = case_s["x"].shape[0]
+            us_t, d_t = time_layer(spec_s, cps, case_s["x"], max(20, args.steps // 2), max(5, args.warmup // 2))
+            b_t = fixtures.algorithmic_bytes(spec_s, d_t)
+            extra[name] = dict(rows=T, distinct_experts=d_t, us_per_call=round(us_t, 2),
+                               algorithmic_bytes=b_t, gbs=round(b_t / (us_t * 1e-6) / 1e9, 1),
+                               frac_of_peak=round(b_t / (us_t * 1e-6) / 1e9 / PEAK_HBM_GBS, 4))
+            del cps, case_s
+            torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:

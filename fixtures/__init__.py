@@ -48,15 +48,22 @@ SPECS = {
     "v4": dict(hidden=7168, inter=2048, shared_inter=2048, n_experts=256, top_k=6,
                n_group=1, topk_group=1, n_shared=1, routed_scale=2.5,
                routed_fmt=FMT_MXFP4, bias_bf16=1),
+    # one GPU's share of the V3 layer under 8-way tensor parallelism: the
+    # intermediate dimension split 8 ways (2048 / 8), the router whole
+    "v3tp8": dict(hidden=7168, inter=256, shared_inter=256, n_experts=256, top_k=8,
+                  n_group=8, topk_group=4, n_shared=1, routed_scale=2.5,
+                  routed_fmt=FMT_FP8_B128, bias_bf16=0),
 }
 
-# The five workloads: (spec, rows, row recipe, seed, requests).
+# The workloads: (spec, rows, row recipe, seed, requests).
 WORKLOADS = {
     "tiny_t1": ("tiny", 1, "iid", 1, 1),
     "v3_t1": ("v3", 1, "iid", 2, 1),
     "v3_t8": ("v3", 8, "corr", 3, 2),
     "v3_t64": ("v3", 64, "iid", 4, 64),
     "v4_t16": ("v4", 16, "corr", 5, 4),
+    "v3tp8_t1": ("v3tp8", 1, "iid", 6, 1),
+    "v3tp8_t8": ("v3tp8", 8, "corr", 7, 2),
 }
 
 

@@ -115,6 +115,9 @@ FULL = [
     ("v3_t8", [0, 3, 5, 7]),
     ("v3_t64", [0, 17, 42, 63]),
     ("v4_t16", [0, 6, 15]),
+    # the 8-way tensor-parallel share of the V3 layer (intermediate 256)
+    ("v3tp8_t1", [0]),
+    ("v3tp8_t8", [0, 4, 7]),
 ]
 
 
