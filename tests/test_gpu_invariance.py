@@ -195,3 +195,35 @@ def test_routing_ties_past_k(T):
     ids = _route_both(spec, case, T)
     for r in range(T):
         assert ids[r].tolist() == tied[:8]
+
+
+@pytest.mark.parametrize("T", [1, 8, 37])
+def test_graph_replay_matches_eager(T):
+    """moe_forward captured in a HIP graph (the launch-cost removal of the
+    upstream-overlap item): every replay, with eager work and eager calls of
+    the layer between replays, gives the eager output bit for bit.  The call
+    records one kernel launch and no memory set."""
+    say(f"graph replay T={T}")
+    spec = fixtures.spec_with("tiny", **MID)
+    case = gpu_case(spec, T, 50 + T, rows="corr", requests=max(1, T // 4))
+    layer = _layer(spec, case, T)
+    x = case["x"]
+    eager = run_forward(layer, x)
+    out = torch.empty_like(x)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.forward(x, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(x, out=out)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(fixtures.bits16(out), eager)
+        assert np.array_equal(run_forward(layer, x), eager)
+    assert layer.read_error() == 0
