@@ -929,8 +929,8 @@ __device__ __forceinline__ int use_rank(const Lds& L, int e, int r) {
   return r < 32 ? __popc(lo & ((1u << r) - 1u)) : __popc(lo) + __popc(hi & ((1u << (r - 32)) - 1u));
 }
 
-// The grouping of up to 64 uses by one wave (wave 0), one use per lane, no
-// workgroup barriers.
+// The grouping of up to 64 uses by one wave (the narrow stream's wave 7),
+// one use per lane, no workgroup barriers.
 __device__ inline void groups_one_wave(const Params& p, const Lds& L) {
   const int lane = threadIdx.x & 63;
   const int U = p.T * p.K;
@@ -2510,9 +2510,10 @@ __device__ __forceinline__ const Params& fresh_args() {
 // The narrow forward after the logits: routing and grouping, the up/gate
 // stream (its sums formed at job ends), the second flag barrier, the down
 // stream, the combine.  With at most as many rows as waves, the waves that
-// route no row start on this CU's shared-expert jobs at once, the other
-// waves but wave 0 as soon as their row is routed, and wave 0 once it has
-// grouped the uses and written the routed tables.
+// route no row start on this CU's shared-expert jobs once every row's
+// scores are in, the routing waves but wave 7 as soon as their row is
+// routed, and wave 7 once it has grouped the uses and written the routed
+// tables.
 template <int FMT, int AL>
 __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
   const int wave = wave_id();
