@@ -11,10 +11,15 @@ between steps so that a repeat cannot be served from the 256 MB last-level
 cache; inputs are resident in HBM before timing starts.
 
 value = achieved HBM GB/s on the algorithmic bytes (every used expert's
-weights and scales once, plus the router weights), B_alg / mean call time.
-The same figures at 8 rows (2 requests x 4 MTP rows) and 64 independent rows
-are reported under "extra".  cpu_baseline times the fp64 oracle on the
-host's cores on the one-row layer.
+weights and scales once, plus the router weights), B_alg / mean call time;
+median and p90 of the per-call times are reported beside the mean.  The same
+figures at 8 rows (2 requests x 4 MTP rows) and 64 independent rows, for the
+tiny layer, the DeepSeek-V4-style MXFP4 top-6 layer at 16 rows and the
+tensor-parallel shares are reported under "extra".  stream_read_gbs is what
+a plain streaming-read kernel reaches on this GPU; every fraction of the
+8 TB/s peak is also given as a fraction of it.  cpu_baseline times the fp64
+oracle on the host's cores on the one-row layer; cpu_extra adds one-core
+figures.
 """
 from __future__ import annotations
 
@@ -32,8 +37,10 @@ PEAK_HBM_GBS = 8000.0
 N_COPIES = 4
 HEADLINE = "v3_t1"
 EXTRA = ("v3_t8", "v3_t64")
-# one GPU's share of the layer under 8-way tensor parallelism (own weights)
-EXTRA_SHARD = ("v3tp8_t1", "v3tp8_t8")
+# workloads with weights of their own: the tiny layer, the V4-style MXFP4
+# layer, and one GPU's share of the V3 layer under 8-way tensor parallelism
+EXTRA_OWN = ("tiny_t1", "v4_t16", "v3tp8_t1", "v3tp8_t8")
+STREAM_BYTES = 4 << 30
 
 
 def kernel_source_hash() -> str:
@@ -74,10 +81,15 @@ def build_copies(spec, case, n_copies):
     return copies
 
 
+def note(msg):
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
 def time_layer(spec, copies, x, steps, warmup):
-    """Mean µs per fused call over `steps` calls rotating weight copies,
-    timed with HIP events on the launch stream, plus the distinct expert
-    count of the step."""
+    """Per-call times (µs) of `steps` fused calls rotating weight copies,
+    timed with HIP events on the launch stream (one event between calls),
+    plus the distinct expert count of the step."""
+    import numpy as np
     import torch
     import mixture_experts_decode_sigmoid_amd as moe
     T = x.shape[0]
@@ -87,46 +99,128 @@ def time_layer(spec, copies, x, steps, warmup):
     for i in range(warmup):
         layers[i % len(layers)].forward(x, out)
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
     for i in range(steps):
         layers[i % len(layers)].forward(x, out)
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) * 1000.0 for i in range(steps)])
     errs = [l.read_error() for l in layers]
     if any(errs):
         raise RuntimeError(f"device error bits {errs}")
     ids, _ = layers[0].route(x)
     distinct = len(set(ids.cpu().view(-1).tolist()))
-    return ms * 1000.0 / steps, distinct
+    return per, distinct
 
 
-def cpu_baseline(spec, case, budget_s=12.0):
-    """The fp64 oracle on host cores, whole one-row layer, repeated up to
-    about budget_s seconds."""
+def summary(per, b_alg, stream_gbs):
+    import numpy as np
+    us = float(per.mean())
+    gbs = b_alg / (us * 1e-6) / 1e9
+    d = dict(us_per_call=round(us, 2), us_median=round(float(np.median(per)), 2),
+             us_p90=round(float(np.percentile(per, 90)), 2), algorithmic_bytes=b_alg,
+             gbs=round(gbs, 1), frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
+    if stream_gbs:
+        d["frac_of_stream_read"] = round(gbs / stream_gbs, 4)
+    return d
+
+
+def stream_read_gbs(reps=10):
+    """GB/s of a plain streaming read of a 4 GiB buffer (the library's probe
+    kernel), best grid of a small sweep, median of `reps` timed reads."""
+    import numpy as np
+    import torch
+    import mixture_experts_decode_sigmoid_amd as moe
+    buf = torch.ones(STREAM_BYTES // 4, dtype=torch.int32, device="cuda")
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    best = 0.0
+    for mult in (4, 8, 16):
+        blocks = ncu * mult
+        sink = torch.empty(blocks, dtype=torch.int32, device="cuda")
+        for _ in range(2):
+            moe.moe_probe_stream_read(buf, sink, blocks)
+        times = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            moe.moe_probe_stream_read(buf, sink, blocks)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e-3)
+        best = max(best, STREAM_BYTES / float(np.median(times)) / 1e9)
+    del buf
+    torch.cuda.empty_cache()
+    return round(best, 1)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_time(spec, case, rows, threads, budget_s, max_runs=5):
+    """Median seconds of the oracle over `rows` (host copies of only the
+    experts they use), and how many runs it took."""
     import numpy as np
     import fixtures
     import oracle
     h0 = fixtures.host_case(case, experts=[])
     ids, _, _, _ = oracle.route(spec, h0["x"], h0["router_w"], h0["bias"])
-    used = sorted(set(ids.ravel().tolist()))
+    used = sorted(set(int(e) for r in rows for e in ids[r]))
     h = fixtures.host_case(case, experts=used)
-    threads = oracle.max_threads()
     times = []
     t_start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        oracle.forward(spec, h, nthreads=threads)
+        oracle.forward(spec, h, rows=list(rows), nthreads=threads)
         times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > budget_s or len(times) >= 5:
+        if time.perf_counter() - t_start > budget_s or len(times) >= max_runs:
             break
-    t = float(np.median(times))
-    b_alg = fixtures.algorithmic_bytes(spec, len(used))
+    d_all = len(set(ids.ravel().tolist()))
+    return float(np.median(times)), len(times), d_all
+
+
+def cpu_baseline(spec, case, budget_s=12.0):
+    """The fp64 oracle on host cores, whole one-row layer, repeated up to
+    about budget_s seconds."""
+    import fixtures
+    import oracle
+    threads = oracle.max_threads()
+    t, n, d = _oracle_time(spec, case, [0], threads, budget_s)
+    b_alg = fixtures.algorithmic_bytes(spec, d)
     return dict(value=round(b_alg / t / 1e9, 4), unit="GB/s", cores=threads, kind="oracle",
-                sample=f"{HEADLINE}: whole one-row layer ({len(used)} routed + 1 shared expert), "
-                       f"median of {len(times)} calls, {t:.3f} s per call")
+                sample=f"{HEADLINE}: whole one-row layer ({d} routed + 1 shared expert), "
+                       f"median of {n} calls, {t:.3f} s per call", cpu_model=cpu_model())
+
+
+def cpu_extra(spec, case, device):
+    """One-core oracle figures: the tiny layer (1 row), the V3 layer at 1 row
+    and at 8 rows (2 of the 8 rows timed, scaled to the call)."""
+    import fixtures
+    res = {}
+    spec_t, case_t = fixtures.make_workload("tiny_t1", device=device)
+    t, n, d = _oracle_time(spec_t, case_t, [0], 1, 2.0)
+    res["tiny_t1"] = dict(cores=1, s_per_call=round(t, 6), runs=n,
+                          gbs=round(fixtures.algorithmic_bytes(spec_t, d) / t / 1e9, 4))
+    t, n, d = _oracle_time(spec, case, [0], 1, 4.0, max_runs=1)
+    res["v3_t1"] = dict(cores=1, s_per_call=round(t, 3), runs=n,
+                        gbs=round(fixtures.algorithmic_bytes(spec, d) / t / 1e9, 4))
+    sname, T, rows, seed, req = fixtures.WORKLOADS["v3_t8"]
+    head = fixtures.make_case(spec, T, seed, device=device, rows=rows, requests=req, experts=False)
+    c8 = dict(case, x=head["x"], router_w=head["router_w"], bias=head["bias"])
+    t, n, d = _oracle_time(spec, c8, [0, 5], 1, 8.0, max_runs=1)
+    t_call = t * T / 2
+    res["v3_t8"] = dict(cores=1, s_per_call=round(t_call, 3), runs=n, sample="rows 0 and 5 timed, scaled by 8/2",
+                        gbs=round(fixtures.algorithmic_bytes(spec, d) / t_call / 1e9, 4))
+    return res
 
 
 def main():
@@ -158,11 +252,17 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    stream_gbs = stream_read_gbs()
+    note(f"stream read {stream_gbs} GB/s")
+
     spec, case = fixtures.make_workload(HEADLINE, device="cuda")
     copies = build_copies(spec, case, N_COPIES)
-    us, distinct = time_layer(spec, copies, case["x"], args.steps, args.warmup)
+    per, distinct = time_layer(spec, copies, case["x"], args.steps, args.warmup)
+    us = float(per.mean())
     b_alg = fixtures.algorithmic_bytes(spec, distinct)
     gbs = b_alg / (us * 1e-6) / 1e9
+    head = summary(per, b_alg, stream_gbs)
+    note(f"{HEADLINE}: {us:.2f} us")
 
     extra = {}
     if not args.no_extra:
@@ -170,37 +270,39 @@ def main():
             sname, T, rows, seed, req = fixtures.WORKLOADS[name]
             # this workload's activations and router; expert weights are the
             # rotating copies above (same shapes and distribution)
-            head = fixtures.make_case(spec, T, seed, device="cuda", rows=rows, requests=req, experts=False)
+            hd = fixtures.make_case(spec, T, seed, device="cuda", rows=rows, requests=req, experts=False)
             cps = []
             for c in copies:
                 c2 = dict(c)
-                c2["router_w"] = head["router_w"]
-                c2["bias"] = head["bias"]
+                c2["router_w"] = hd["router_w"]
+                c2["bias"] = hd["bias"]
                 cps.append(c2)
             steps = max(20, args.steps // (4 if T > 8 else 2))
-            us_t, d_t = time_layer(spec, cps, head["x"], steps, max(5, args.warmup // 2))
-            b_t = fixtures.algorithmic_bytes(spec, d_t)
-            extra[name] = dict(rows=T, distinct_experts=d_t, us_per_call=round(us_t, 2),
-                               algorithmic_bytes=b_t, gbs=round(b_t / (us_t * 1e-6) / 1e9, 1),
-                               frac_of_peak=round(b_t / (us_t * 1e-6) / 1e9 / PEAK_HBM_GBS, 4))
+            per_t, d_t = time_layer(spec, cps, hd["x"], steps, max(5, args.warmup // 2))
+            extra[name] = dict(rows=T, distinct_experts=d_t,
+                               **summary(per_t, fixtures.algorithmic_bytes(spec, d_t), stream_gbs))
+            note(f"{name}: {extra[name]['us_per_call']} us")
 
         del copies
         torch.cuda.empty_cache()
-        for name in EXTRA_SHARD:
+        for name in EXTRA_OWN:
             spec_s, case_s = fixtures.make_workload(name, device="cuda")
             cps = build_copies(spec_s, case_s, N_COPIES)
             T = case_s["x"].shape[0]
-            us_t, d_t = time_layer(spec_s, cps, case_s["x"], max(20, args.steps // 2), max(5, args.warmup // 2))
-            b_t = fixtures.algorithmic_bytes(spec_s, d_t)
-            extra[name] = dict(rows=T, distinct_experts=d_t, us_per_call=round(us_t, 2),
-                               algorithmic_bytes=b_t, gbs=round(b_t / (us_t * 1e-6) / 1e9, 1),
-                               frac_of_peak=round(b_t / (us_t * 1e-6) / 1e9 / PEAK_HBM_GBS, 4))
+            per_t, d_t = time_layer(spec_s, cps, case_s["x"], max(20, args.steps // 2), max(5, args.warmup // 2))
+            extra[name] = dict(rows=T, distinct_experts=d_t,
+                               **summary(per_t, fixtures.algorithmic_bytes(spec_s, d_t), stream_gbs))
+            note(f"{name}: {extra[name]['us_per_call']} us")
             del cps, case_s
             torch.cuda.empty_cache()
 
     cpu = None
+    cpu_x = None
     if not args.no_cpu:
         cpu = cpu_baseline(spec, case)
+        note("cpu baseline done")
+        if not args.no_extra:
+            cpu_x = cpu_extra(spec, case, "cuda")
 
     line = {
         "metric": "µs per fused MoE layer call & achieved HBM GB/s at 1/8/64 decode rows",
@@ -211,6 +313,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(us / 1000.0, 5),
         "us_per_call": round(us, 2),
+        "us_median": head["us_median"],
+        "us_p90": head["us_p90"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -223,6 +327,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic_from_profiles(HEADLINE)},
         "cpu_baseline": cpu,
+        "cpu_extra": cpu_x,
+        "stream_read_gbs": stream_gbs,
+        "frac_of_stream_read": round(gbs / stream_gbs, 4),
         "extra": extra,
     }
     print(json.dumps(line), flush=True)

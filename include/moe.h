@@ -44,6 +44,20 @@
  *     gate, rows Iexp..2*Iexp-1 to the up half.  W_down is [H, Iexp].
  *   - A workspace belongs to one stream at a time: calls that overlap on the
  *     device must use different workspaces.
+ *   - Residency.  The forward, route and groups calls launch one persistent
+ *     kernel with exactly one workgroup per compute unit (grid = CU count,
+ *     512 threads, more than half a CU's LDS), and its workgroups wait on
+ *     each other (epoch flags and tagged score slots in the workspace).  It
+ *     is an ordinary launch, not a cooperative one: the cooperative launch
+ *     path was measured to cost several times the kernel-launch latency of
+ *     a decode step.  The library checks once per kernel instance, device
+ *     and LDS size that one such workgroup fits on a CU (occupancy query) and
+ *     returns MOE_ERR_LAUNCH otherwise.  What it cannot check is that no
+ *     other kernel holds CUs while the call runs: the call then waits for
+ *     those CUs (a kernel on another stream delays it); if a wait exceeds its
+ *     bound (hundreds of milliseconds of polling) the call sets MOE_DEVERR_WAIT_TIMEOUT and
+ *     its output is undefined.  The intended use is an exclusive device, as
+ *     in a decode loop where the layer's calls are stream-ordered.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -65,6 +79,8 @@ extern "C" {
 #define MOE_ERR_WORKSPACE 6 /* workspace too small or not initialised */
 #define MOE_ERR_ALIAS 7     /* out overlaps x, or a residual overlaps out without being it */
 #define MOE_ERR_HIP 8       /* a HIP runtime call failed; see moe_last_hip_error() */
+#define MOE_ERR_LAUNCH 9    /* the kernel's grid (one workgroup per CU, at the LDS size this
+                               call needs) cannot be resident all at once on this device */
 
 /* ---- device error bits (moe_read_error) ---- */
 #define MOE_DEVERR_NONFINITE_SCORE 0x1u /* a router logit/score was not finite */
@@ -160,6 +176,14 @@ int moe_forward_residual(const moe_config* cfg, const moe_weights* w, const uint
 /* Waits for `stream`, then returns the workspace's device error bits in
  * *bits (host) and clears them. */
 int moe_read_error(void* ws, void* stream, uint32_t* bits);
+
+/* Measurement helper (not part of the layer): reads `bytes` (a multiple of
+ * 16) of device memory at buf (16-byte aligned) once, as a plain streaming
+ * read with `blocks` workgroups of 256 threads, and writes one xor digest
+ * per workgroup to sink[blocks] (device).  Timing it gives the read
+ * bandwidth this GPU reaches without the layer's structure, the yardstick
+ * beside the published HBM peak.  Asynchronous on `stream`. */
+int moe_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, void* stream);
 
 /* Text of a return code (static string). */
 const char* moe_strerror(int code);

@@ -24,6 +24,7 @@ MOE_ERR_ROWS = 5
 MOE_ERR_WORKSPACE = 6
 MOE_ERR_ALIAS = 7
 MOE_ERR_HIP = 8
+MOE_ERR_LAUNCH = 9
 
 MOE_DEVERR_NONFINITE_SCORE = 0x1
 MOE_DEVERR_NONFINITE_MID = 0x2
@@ -58,16 +59,26 @@ class MoeError(RuntimeError):
 
 
 _lib = None
+_lib_path = LIB_PATH
+
+
+def use_library(path: str) -> None:
+    """Load another build of the same library (e.g. the phase-stamp build)
+    instead of libmoe.so; must be called before the first call."""
+    global _lib_path
+    if _lib is not None:
+        raise RuntimeError("the library is already loaded")
+    _lib_path = path
 
 
 def lib() -> C.CDLL:
     """The loaded libmoe.so (raises if it is missing: no fallback)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+        if not os.path.exists(_lib_path):
+            raise RuntimeError(f"{_lib_path} is missing: build it with "
                                "`python -m mixture_experts_decode_sigmoid_amd.build`")
-        L = C.CDLL(LIB_PATH)
+        L = C.CDLL(_lib_path)
         P, I, Z = C.c_void_p, C.c_int, C.c_size_t
         L.moe_workspace_size.argtypes = [C.POINTER(MoeConfig), C.POINTER(C.c_size_t)]
         L.moe_workspace_init.argtypes = [P, Z, P]
@@ -79,15 +90,18 @@ def lib() -> C.CDLL:
         L.moe_strerror.argtypes = [I]
         L.moe_strerror.restype = C.c_char_p
         L.moe_last_hip_error.argtypes = []
+        L.moe_probe_stream_read.argtypes = [P, Z, P, I, P]
         for f in ("moe_workspace_size", "moe_workspace_init", "moe_route", "moe_groups",
-                  "moe_forward", "moe_forward_residual", "moe_read_error", "moe_last_hip_error"):
+                  "moe_forward", "moe_forward_residual", "moe_read_error", "moe_last_hip_error",
+                  "moe_probe_stream_read"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
 
 
 EXPORTS = ("moe_workspace_size", "moe_workspace_init", "moe_route", "moe_groups",
-           "moe_forward", "moe_forward_residual", "moe_read_error", "moe_strerror", "moe_last_hip_error")
+           "moe_forward", "moe_forward_residual", "moe_read_error", "moe_strerror", "moe_last_hip_error",
+           "moe_probe_stream_read")
 
 
 def strerror(code: int) -> str:
@@ -178,17 +192,26 @@ def moe_last_hip_error() -> int:
     return int(lib().moe_last_hip_error())
 
 
+def moe_probe_stream_read(buf, sink, blocks: int, stream=None):
+    """buf: device tensor read once (bytes a multiple of 16); sink: int32
+    device tensor of at least `blocks` entries (written)."""
+    _check(lib().moe_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), int(blocks),
+                                       _stream(stream)), "moe_probe_stream_read")
+
+
 # ---------------------------------------------------------------- convenience
 
 class Layer:
     """Holds a config, weight pointers and a workspace for one device."""
 
-    def __init__(self, spec: dict, case: dict, max_rows: int, device="cuda"):
+    def __init__(self, spec: dict, case: dict, max_rows: int, device="cuda", ws_extra: int = 0):
         self.spec = spec
         self.case = case
         self.cfg = make_config(spec, max_rows)
         self.w = make_weights(case)
-        self.ws = new_workspace(self.cfg, device)
+        self.ws_bytes = moe_workspace_size(self.cfg)
+        self.ws = torch.empty(self.ws_bytes + ws_extra, dtype=torch.uint8, device=device)
+        moe_workspace_init(self.ws)
 
     def forward(self, x: torch.Tensor, out: torch.Tensor | None = None, stream=None,
                 residual: torch.Tensor | None = None) -> torch.Tensor:

@@ -6,6 +6,9 @@
 
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 using namespace moe;
 
 namespace {
@@ -19,19 +22,22 @@ struct DevInfo {
   size_t max_lds = 0;
 };
 
-// Device properties, cached per device id (read once; the library keeps no
-// other state).
-DevInfo dev_info() {
-  static DevInfo cache[64];
-  static bool have[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DevInfo{};
-  if (!have[dev]) {
-    hipDeviceProp_t pr;
-    if (hipGetDeviceProperties(&pr, dev) != hipSuccess) return DevInfo{};
-    cache[dev].ncu = pr.multiProcessorCount;
-    cache[dev].max_lds = pr.sharedMemPerBlock;
-    have[dev] = true;
+// Device properties, cached per device id (read once under a lock; later
+// reads see the published entry through the acquire load of `have`).
+DevInfo dev_info(int dev) {
+  static DevInfo cache[kMaxDevices];
+  static std::atomic<bool> have[kMaxDevices];
+  static std::mutex fill_lock;
+  if (dev < 0 || dev >= kMaxDevices) return DevInfo{};
+  if (!have[dev].load(std::memory_order_acquire)) {
+    std::lock_guard<std::mutex> g(fill_lock);
+    if (!have[dev].load(std::memory_order_relaxed)) {
+      hipDeviceProp_t pr;
+      if (hipGetDeviceProperties(&pr, dev) != hipSuccess) return DevInfo{};
+      cache[dev].ncu = pr.multiProcessorCount;
+      cache[dev].max_lds = pr.sharedMemPerBlock;
+      have[dev].store(true, std::memory_order_release);
+    }
   }
   return cache[dev];
 }
@@ -80,7 +86,7 @@ int check_weights(const moe_config* c, const moe_weights* w, bool need_experts) 
 int hs_for(int H, int ncu) { return (H + ncu - 1) / ncu; }
 
 int fill(const moe_config* c, const moe_weights* w, const uint16_t* x, int rows, void* ws,
-         size_t ws_bytes, Params& p, int mode) {
+         size_t ws_bytes, Params& p, int mode, int& dev) {
   int rc = check_cfg(c);
   if (rc) return rc;
   rc = check_weights(c, w, mode == kModeForward);
@@ -92,7 +98,8 @@ int fill(const moe_config* c, const moe_weights* w, const uint16_t* x, int rows,
   const WsLayout L = ws_layout(c->max_rows, c->n_experts, c->top_k, c->hidden, c->inter,
                                c->n_shared ? c->shared_inter : 0);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
-  const DevInfo d = dev_info();
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  const DevInfo d = dev_info(dev);
   if (d.ncu <= 0) {
     g_last_hip = (int)hipErrorNoDevice;
     return MOE_ERR_HIP;
@@ -145,8 +152,9 @@ int fill(const moe_config* c, const moe_weights* w, const uint16_t* x, int rows,
   return MOE_OK;
 }
 
-int do_launch(const Params& p, int mode, void* stream) {
-  hipError_t e = launch(p, mode, (hipStream_t)stream);
+int do_launch(const Params& p, int mode, void* stream, int dev) {
+  hipError_t e = launch(p, mode, (hipStream_t)stream, dev);
+  if (e == hipErrorCooperativeLaunchTooLarge) return MOE_ERR_LAUNCH;
   if (e != hipSuccess) {
     g_last_hip = (int)e;
     return MOE_ERR_HIP;
@@ -155,6 +163,32 @@ int do_launch(const Params& p, int mode, void* stream) {
 }
 
 }  // namespace
+
+void moe::set_last_hip(int e) { g_last_hip = e; }
+
+int moe::forward_checked(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
+                         const uint16_t* residual, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  Params p;
+  int dev = 0;
+  int rc = fill(cfg, w, x, rows, ws, ws_bytes, p, kModeForward, dev);
+  if (rc == kNoRows) return MOE_OK;
+  if (rc) return rc;
+  if (!out) return MOE_ERR_NULL;
+  if (!aligned16(out)) return MOE_ERR_ALIGN;
+  const size_t nb = (size_t)rows * cfg->hidden * 2;
+  const char *xo = (const char*)x, *oo = (const char*)out;
+  if (rows > 0 && xo < oo + nb && oo < xo + nb) return MOE_ERR_ALIAS;
+  if (residual) {
+    // the residual may be out itself (each element is read, then written,
+    // by one thread) but may not overlap it otherwise
+    const char* ro = (const char*)residual;
+    if (ro != oo && ro < oo + nb && oo < ro + nb) return MOE_ERR_ALIAS;
+  }
+  if (rows == 0) return MOE_OK;
+  p.out = out;
+  p.residual = residual;
+  return do_launch(p, kModeForward, stream, dev);
+}
 
 extern "C" {
 
@@ -184,60 +218,39 @@ int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
 int moe_route(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
               int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
   Params p;
-  int rc = fill(cfg, w, x, rows, ws, ws_bytes, p, kModeRoute);
+  int dev = 0;
+  int rc = fill(cfg, w, x, rows, ws, ws_bytes, p, kModeRoute, dev);
   if (rc == kNoRows) return MOE_OK;
   if (rc) return rc;
   if (!topk_ids || !topk_w) return MOE_ERR_NULL;
   if (rows == 0) return MOE_OK;
   p.ids_out = topk_ids;
   p.w_out = topk_w;
-  return do_launch(p, kModeRoute, stream);
+  return do_launch(p, kModeRoute, stream, dev);
 }
 
 int moe_groups(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
                int32_t* groups_out, void* ws, size_t ws_bytes, void* stream) {
   Params p;
-  int rc = fill(cfg, w, x, rows, ws, ws_bytes, p, kModeGroups);
+  int dev = 0;
+  int rc = fill(cfg, w, x, rows, ws, ws_bytes, p, kModeGroups, dev);
   if (rc == kNoRows) return MOE_OK;
   if (rc) return rc;
   if (!groups_out) return MOE_ERR_NULL;
   if (rows == 0) return MOE_OK;
   p.groups_out = groups_out;
-  return do_launch(p, kModeGroups, stream);
-}
-
-static int forward(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
-                   const uint16_t* residual, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
-  Params p;
-  int rc = fill(cfg, w, x, rows, ws, ws_bytes, p, kModeForward);
-  if (rc == kNoRows) return MOE_OK;
-  if (rc) return rc;
-  if (!out) return MOE_ERR_NULL;
-  if (!aligned16(out)) return MOE_ERR_ALIGN;
-  const size_t nb = (size_t)rows * cfg->hidden * 2;
-  const char *xo = (const char*)x, *oo = (const char*)out;
-  if (rows > 0 && xo < oo + nb && oo < xo + nb) return MOE_ERR_ALIAS;
-  if (residual) {
-    // the residual may be out itself (each element is read, then written,
-    // by one thread) but may not overlap it otherwise
-    const char* ro = (const char*)residual;
-    if (ro != oo && ro < oo + nb && oo < ro + nb) return MOE_ERR_ALIAS;
-  }
-  if (rows == 0) return MOE_OK;
-  p.out = out;
-  p.residual = residual;
-  return do_launch(p, kModeForward, stream);
+  return do_launch(p, kModeGroups, stream, dev);
 }
 
 int moe_forward(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
                 uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
-  return forward(cfg, w, x, rows, nullptr, out, ws, ws_bytes, stream);
+  return forward_checked(cfg, w, x, rows, nullptr, out, ws, ws_bytes, stream);
 }
 
 int moe_forward_residual(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
                          const uint16_t* residual, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
   if (rows > 0 && !residual) return MOE_ERR_NULL;
-  return forward(cfg, w, x, rows, residual, out, ws, ws_bytes, stream);
+  return forward_checked(cfg, w, x, rows, residual, out, ws, ws_bytes, stream);
 }
 
 int moe_read_error(void* ws, void* stream, uint32_t* bits) {
@@ -266,6 +279,7 @@ const char* moe_strerror(int code) {
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_ALIAS: return "out overlaps x, or the residual overlaps out without being it";
     case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_LAUNCH: return "one workgroup per CU at this LDS size cannot be resident on this device";
     default: return "unknown error code";
   }
 }

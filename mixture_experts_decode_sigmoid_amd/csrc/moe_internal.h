@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "moe.h"
+
 namespace moe {
 
 constexpr int kWaves = 8;                 // waves per workgroup (one workgroup per CU)
@@ -73,8 +75,19 @@ WsLayout ws_layout(int max_rows, int E, int K, int H, int I, int Is);
 // Fills the stream geometry of p (T, K, E, I, Is, hs, ncu set) for the
 // narrow (narrow = 1) or wide layout and returns the LDS bytes it needs.
 size_t stream_geometry(Params& p, int narrow);
-hipError_t launch(const Params& p, int mode, hipStream_t stream);
+// Launches the fused kernel instance for p and mode on device `dev` (the
+// current device).  Returns hipErrorCooperativeLaunchTooLarge when one
+// workgroup per CU with p's LDS size cannot be resident on this device.
+hipError_t launch(const Params& p, int mode, hipStream_t stream, int dev);
 // The forward of the wide stream with a residual (moe_kernels_res.hip).
-hipError_t launch_res_wide(const Params& p, hipStream_t stream);
+hipError_t launch_res_wide(const Params& p, hipStream_t stream, int dev);
+// moe_forward / moe_forward_residual after their own argument checks:
+// validates, carves the workspace ws (ws_bytes) and launches.
+int forward_checked(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
+                    const uint16_t* residual, uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
+// Records the HIP error behind a MOE_ERR_HIP return (moe_last_hip_error).
+void set_last_hip(int e);
+constexpr int kMaxDevices = 64;
 
 }  // namespace moe

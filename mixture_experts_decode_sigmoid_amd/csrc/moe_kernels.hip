@@ -40,12 +40,18 @@
 // the same fixed-order reduction over the 8 waves' K ranges; the combine is
 // row-local.  Only which CU does the work depends on the batch.
 //
-// Cross-CU data (scores, mid) is published with an agent-scope release fence
-// before a flag store and read after polling the flags and an agent-scope
-// acquire fence.  Each CU owns one flag and raises it by one per phase; a
-// call advances every flag by two, so the workspace needs no reset.  Waits
-// are bounded: on timeout an error bit is set and the kernel runs on.
+// Cross-CU data (scores, mid) is stored at agent scope (written through to
+// the device's point of coherence), so raising a flag after it needs only
+// the workgroup's own store completion, not an L2 writeback; the one
+// exception is the wide stream's mid, stored plainly and published with an
+// agent-scope release fence.  Readers poll the flags (or, for scores, the
+// epoch tags in the slots themselves) and then acquire at agent scope.
+// Each CU owns one flag and raises it by one per phase; a call advances
+// every flag by two, so the workspace needs no reset.  Waits are bounded:
+// on timeout an error bit is set and the kernel runs on.
 #include "moe_internal.h"
+
+#include <atomic>
 
 namespace moe {
 
@@ -583,17 +589,23 @@ __device__ inline void router_logits(const Params& p, const Lds& L, uint32_t epo
   }
 }
 
-// The same logits with one wave per (row, expert): lane l sums h = 8l +
-// 512j + 0..7 in order, then a fixed xor butterfly.  The loads of up to 8 j
-// (16 with LATE) are issued before their products are summed.  Used from 8 rows up, where
-// every wave has rows of its own (and by the wide stream, whose register
-// budget has no room for the chunked form).
+// The same logits with one wave per (row, expert), in the same summation
+// order as router_logits, so that a logit has the same bits whatever the
+// batch size (the two forms are chosen by batch size): the wave walks the 8
+// chunks of H/8 in order, lane l sums the 16-byte groups l and l+64 of a
+// chunk (8 elements each, in order), the lanes are summed by the same fixed
+// tree (wave_sum_d), and the chunk sums are added in chunk order.  The
+// loads of NC chunks are issued before their products are summed (all 8
+// with LATE).  Used from 8 rows up, where every wave has rows of its own.
 // LATE: `v` is the epoch, a load still in flight, first read once the sums
 // are formed (tag = epoch + 1); otherwise `v` is the tag.
 template <bool LATE>
 __device__ inline void router_logits_rows(const Params& p, uint32_t v) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (wave >= kWaves) return;
+  const int ch = p.H / kWaves, ngrp = ch >> 3;
+  const int g0 = lane < ngrp ? lane : ngrp - 1, g1 = lane + 64 < ngrp ? lane + 64 : g0;
+  constexpr int NC = LATE ? kWaves : kWaves / 2;
   for (int e = blockIdx.x; e < p.E; e += p.ncu) {
     const uint16_t* wr = p.router_w + (size_t)e * p.H;
     // LATE: the bias bits are converted once the sums are formed
@@ -601,38 +613,40 @@ __device__ inline void router_logits_rows(const Params& p, uint32_t v) {
     const double bias = LATE ? 0.0 : load_bias(p, e);
     for (int r = wave; r < p.T; r += kWaves) {
       const uint16_t* xr = p.x + (size_t)r * p.H;
-      double acc = 0.0;
-      // LATE: up to 16 j per pass (one pass at H <= 8192), so the loads
-      // make one round trip
-      constexpr int NJ = LATE ? 16 : 8;
-      for (int h0 = 8 * lane; h0 < p.H; h0 += 512 * NJ) {
-        u32x4 xv[NJ], wv[NJ];
+      double l = 0.0;
+      for (int c0 = 0; c0 < kWaves; c0 += NC) {
+        u32x4 xv[NC][2], wv[NC][2];
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int h = h0 + 512 * j < p.H ? h0 + 512 * j : h0;
-          xv[j] = ld16(xr + h);
-          wv[j] = ld16(wr + h);
+        for (int c = 0; c < NC; ++c) {
+          const size_t o = (size_t)(c0 + c) * ch;
+          xv[c][0] = ld16(xr + o + 8 * g0);
+          wv[c][0] = ld16(wr + o + 8 * g0);
+          xv[c][1] = ld16(xr + o + 8 * g1);
+          wv[c][1] = ld16(wr + o + 8 * g1);
         }
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          if (h0 + 512 * j < p.H) {
+        for (int c = 0; c < NC; ++c) {
+          double acc = 0.0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const uint32_t xa = xv[j][i], wa = wv[j][i];
-              acc = fma((double)bf16_bits_to_f32(xa & 0xffffu), (double)bf16_bits_to_f32(wa & 0xffffu), acc);
-              acc = fma((double)bf16_bits_to_f32(xa >> 16), (double)bf16_bits_to_f32(wa >> 16), acc);
+          for (int q = 0; q < 2; ++q) {
+            if (q == 0 ? lane < ngrp : lane + 64 < ngrp) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const uint32_t xa = xv[c][q][i], wa = wv[c][q][i];
+                acc = fma((double)bf16_bits_to_f32(xa & 0xffffu), (double)bf16_bits_to_f32(wa & 0xffffu), acc);
+                acc = fma((double)bf16_bits_to_f32(xa >> 16), (double)bf16_bits_to_f32(wa >> 16), acc);
+              }
             }
           }
+          l += wave_sum_d(acc);
         }
       }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
       uint32_t ep = v, br = braw;
       if (LATE) asm volatile("" : "+v"(ep), "+v"(br));
       if (lane == 0) {
-        double s = 1.0 / (1.0 + exp(-acc));
+        double s = 1.0 / (1.0 + exp(-l));
         double b = s + (LATE ? bias_from_raw(p, br) : bias);
-        if (!isfinite(acc) || !isfinite(b)) set_err(p.err, kErrScore);
+        if (!isfinite(l) || !isfinite(b)) set_err(p.err, kErrScore);
         publish_score(p, r, e, s, LATE ? ep + 1 : v);
       }
     }
@@ -2787,47 +2801,72 @@ WsLayout ws_layout(int max_rows, int E, int K, int H, int I, int Is) {
 
 #endif
 
+// Per kernel instance and device: the largest LDS size for which the
+// instance's dynamic LDS limit has been raised and one workgroup of kThreads
+// was found to fit on a CU (so the grid of one workgroup per CU can be
+// resident at once on an otherwise idle device).  Checked once per size
+// increase; later calls launch at once.
+static bool resident_ok(const void* kfn, std::atomic<int>& ok_lds, int lds, hipError_t& e) {
+  e = hipSuccess;
+  int have = ok_lds.load(std::memory_order_acquire);
+  if (lds <= have) return true;
+  e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return false;
+  int nb = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kfn, kThreads, (size_t)lds);
+  if (e != hipSuccess) return false;
+  if (nb < 1) {
+    e = hipErrorCooperativeLaunchTooLarge;
+    return false;
+  }
+  while (have < lds && !ok_lds.compare_exchange_weak(have, lds, std::memory_order_acq_rel)) {
+  }
+  return true;
+}
+
 template <int MODE, int FMT, int NARROW = 1>
-static hipError_t launch_one(const Params& p, hipStream_t stream) {
+static hipError_t launch_one(const Params& p, hipStream_t stream, int dev) {
+  static std::atomic<int> ok_lds[kMaxDevices];
   auto kfn = moe_fused<MODE, FMT, NARROW>;
-  hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
-  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  hipError_t e;
+  if (!resident_ok((const void*)kfn, ok_lds[dev], p.lds_bytes, e)) return e;
   hipLaunchKernelGGL(kfn, dim3(p.ncu), dim3(kThreads), p.lds_bytes, stream, p);
   return hipGetLastError();
 }
 
 #ifndef MOE_RES_WIDE_TU
-hipError_t launch(const Params& p, int mode, hipStream_t stream) {
+hipError_t launch(const Params& p, int mode, hipStream_t stream, int dev) {
   const bool wide = !p.narrow;
   const int nk = p.T <= 4 ? 2 : p.T <= 8 ? 3 : 1;  // narrow kernel by batch size
   const bool wide_res = mode == kModeForward && wide && p.residual;
   if (p.routed_fmt == 0 && !wide_res) {
     if (mode == kModeForward)
-      return wide      ? launch_one<kModeForward, 0, 0>(p, stream)
-             : nk == 2 ? launch_one<kModeForward, 0, 2>(p, stream)
-             : nk == 3 ? launch_one<kModeForward, 0, 3>(p, stream)
-                       : launch_one<kModeForward, 0, 1>(p, stream);
-    if (mode == kModeRoute) return launch_one<kModeRoute, 0>(p, stream);
-    return launch_one<kModeGroups, 0>(p, stream);
+      return wide      ? launch_one<kModeForward, 0, 0>(p, stream, dev)
+             : nk == 2 ? launch_one<kModeForward, 0, 2>(p, stream, dev)
+             : nk == 3 ? launch_one<kModeForward, 0, 3>(p, stream, dev)
+                       : launch_one<kModeForward, 0, 1>(p, stream, dev);
+    if (mode == kModeRoute) return launch_one<kModeRoute, 0>(p, stream, dev);
+    return launch_one<kModeGroups, 0>(p, stream, dev);
   }
   if (!wide_res) {
     if (mode == kModeForward)
-      return wide      ? launch_one<kModeForward, 1, 0>(p, stream)
-             : nk == 2 ? launch_one<kModeForward, 1, 2>(p, stream)
-             : nk == 3 ? launch_one<kModeForward, 1, 3>(p, stream)
-                       : launch_one<kModeForward, 1, 1>(p, stream);
-    if (mode == kModeRoute) return launch_one<kModeRoute, 1>(p, stream);
-    return launch_one<kModeGroups, 1>(p, stream);
+      return wide      ? launch_one<kModeForward, 1, 0>(p, stream, dev)
+             : nk == 2 ? launch_one<kModeForward, 1, 2>(p, stream, dev)
+             : nk == 3 ? launch_one<kModeForward, 1, 3>(p, stream, dev)
+                       : launch_one<kModeForward, 1, 1>(p, stream, dev);
+    if (mode == kModeRoute) return launch_one<kModeRoute, 1>(p, stream, dev);
+    return launch_one<kModeGroups, 1>(p, stream, dev);
   }
-  return launch_res_wide(p, stream);
+  return launch_res_wide(p, stream, dev);
 }
 #else
 // The wide stream with a residual: its kernels are built in a translation
 // unit of their own (moe_kernels_res.hip), so that the code object of the
 // other kernels is the same with or without them.
-hipError_t launch_res_wide(const Params& p, hipStream_t stream) {
-  return p.routed_fmt == 0 ? launch_one<kModeForwardRes, 0, 0>(p, stream)
-                           : launch_one<kModeForwardRes, 1, 0>(p, stream);
+hipError_t launch_res_wide(const Params& p, hipStream_t stream, int dev) {
+  return p.routed_fmt == 0 ? launch_one<kModeForwardRes, 0, 0>(p, stream, dev)
+                           : launch_one<kModeForwardRes, 1, 0>(p, stream, dev);
 }
 #endif
 

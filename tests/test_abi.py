@@ -77,3 +77,14 @@ def test_forward_argument_errors_without_launch():
     assert L.moe_route(C.byref(cfg), C.byref(w), x, 1, None, None, C.c_void_p(0x4000), 16, None) == moe.MOE_ERR_WORKSPACE
     for code in range(0, 10):
         assert isinstance(moe.strerror(code), str)
+
+
+def test_launch_error_code_and_probe_argument_errors():
+    assert "resident" in moe.strerror(moe.MOE_ERR_LAUNCH)
+    L = moe.lib()
+    sink = C.c_void_p(0x2000)
+    assert L.moe_probe_stream_read(None, 1 << 20, sink, 4, None) == moe.MOE_ERR_NULL
+    assert L.moe_probe_stream_read(C.c_void_p(0x1000), 1 << 20, None, 4, None) == moe.MOE_ERR_NULL
+    assert L.moe_probe_stream_read(C.c_void_p(0x1008), 1 << 20, sink, 4, None) == moe.MOE_ERR_ALIGN
+    assert L.moe_probe_stream_read(C.c_void_p(0x1000), 1000, sink, 4, None) == moe.MOE_ERR_ALIGN
+    assert L.moe_probe_stream_read(C.c_void_p(0x1000), 1 << 20, sink, 0, None) == moe.MOE_ERR_SHAPE

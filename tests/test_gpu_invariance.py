@@ -18,6 +18,11 @@ MID = dict(hidden=2048, inter=512, shared_inter=512, n_experts=64, top_k=6, n_gr
 MID2 = dict(hidden=4352, inter=256, shared_inter=256, n_experts=32, top_k=4, n_group=4, topk_group=2)
 
 
+# DeepSeek-V3 routing geometry (256 experts in 8 groups of 32, keep 4,
+# top-8) on a small layer.
+V3R = dict(hidden=1024, inter=256, shared_inter=256, n_experts=256, top_k=8, n_group=8, topk_group=4)
+
+
 def _layer(spec, case, T):
     return moe.Layer(spec, case, max_rows=T)
 
@@ -49,6 +54,69 @@ def test_batch_invariance_v3_t8():
         assert np.array_equal(one[0], full[r]), r
     rev = run_forward(layer, case["x"].flip(0).contiguous())
     assert np.array_equal(rev, full[::-1])
+
+
+@pytest.mark.parametrize("name", ["v3_t64", "v4_t16"])
+def test_batch_invariance_full_size(name):
+    """Every row of the 64-row DeepSeek-V3 batch (wide stream) and of the
+    16-row MXFP4 top-6 batch (narrow stream) alone, through the one-row
+    kernel, equals its row in the batch bit for bit; so does the batch in
+    reverse order."""
+    say(f"batch invariance {name}")
+    spec, case = fixtures.make_workload(name, device="cuda")
+    T = case["x"].shape[0]
+    layer = _layer(spec, case, T)
+    full = run_forward(layer, case["x"])
+    for r in range(T):
+        one = run_forward(layer, case["x"][r:r + 1].contiguous())
+        assert np.array_equal(one[0], full[r]), r
+    rev = run_forward(layer, case["x"].flip(0).contiguous())
+    assert np.array_equal(rev, full[::-1])
+    del layer, case
+    torch.cuda.empty_cache()
+
+
+def _score_slots(layer, T, E):
+    """The fp64 scores s[r][e] the last call left in its workspace's tagged
+    slots (two 64-bit words each: tag and high half, tag and low half)."""
+    torch.cuda.synchronize()
+    off = 4096 + 256  # after the per-CU flags and the error word
+    w = layer.ws[off:off + 16 * T * E].cpu().numpy().view(np.uint64).reshape(T, E, 2)
+    return ((w[..., 0] & np.uint64(0xFFFFFFFF)) << np.uint64(32)) | (w[..., 1] & np.uint64(0xFFFFFFFF))
+
+
+def test_router_logits_same_bits_at_every_batch_size():
+    """Activations spread over five decades make the fp64 logit sums inexact,
+    so their bits depend on the summation order: a row's scores must still
+    be the same bits whether it is routed alone or in a batch of 8 or 37
+    rows (the logit kernels differ by batch size), in moe_route and in
+    moe_forward."""
+    say("router logits order")
+    spec = fixtures.spec_with("tiny", **V3R)
+    T, E = 37, spec["n_experts"]
+    g = torch.Generator().manual_seed(77)
+    mag = torch.pow(10.0, torch.rand(T, spec["hidden"], generator=g) * 5 - 4)
+    sign = torch.where(torch.rand(T, spec["hidden"], generator=g) < 0.5, -1.0, 1.0)
+    case = gpu_case(spec, T, 78)
+    case["x"] = (mag * sign).bfloat16().cuda()
+    layer = _layer(spec, case, T)
+    ref = {}
+    for call in ("route", "forward"):
+        for n in (37, 8, 1):
+            x = case["x"][:n].contiguous()
+            if call == "route":
+                layer.route(x)
+            else:
+                run_forward(layer, x)
+            s = _score_slots(layer, n, E)
+            for r in range(n):
+                if r in ref:
+                    assert np.array_equal(s[r], ref[r]), (call, n, r)
+                else:
+                    ref[r] = s[r]
+    # the slots hold probabilities: the reading of the layout is right
+    sv = ref[0].view(np.float64)
+    assert np.all((sv > 0) & (sv < 1))
 
 
 def test_determinism_and_negative_control():
@@ -124,6 +192,30 @@ def test_error_word_on_nan_activation():
     assert layer.read_error() == 0
 
 
+@pytest.mark.parametrize("fmt,T", [(0, 2), (0, 20), (1, 3), (1, 20)])
+def test_error_word_on_nan_weight_code_in_a_used_expert(fmt, T):
+    """A NaN weight code (E4M3 0x7F) or a NaN block scale (E8M0 0xFF) in an
+    expert a row uses sets MOE_DEVERR_NONFINITE_MID (narrow and wide stream);
+    the same bytes in an unused expert set nothing (see the poison test)."""
+    say(f"error word used expert fmt={fmt} T={T}")
+    over = dict(MID)
+    if fmt:
+        over.update(routed_fmt=1, bias_bf16=1, n_group=1, topk_group=1)
+    spec = fixtures.spec_with("tiny", **over)
+    case = gpu_case(spec, T, 27 + T)
+    layer = _layer(spec, case, T)
+    ids, _, _, _ = oracle_route(spec, case)
+    e = int(ids[0, 0])
+    if fmt == 0:
+        case["w_gate_up"][e, 3, 17] = 0x7F      # one weight of one gate row
+    else:
+        case["s_down"][e, 5, 2] = 0xFF          # one block scale of one down row
+    run_forward(layer, case["x"], check=False)
+    bits = layer.read_error()
+    assert bits & moe.MOE_DEVERR_NONFINITE_MID, bits
+    assert not bits & moe.MOE_DEVERR_WAIT_TIMEOUT
+
+
 def test_rows_zero_and_limits():
     spec = fixtures.spec_with("tiny")
     case = gpu_case(spec, 4, 26)
@@ -139,10 +231,8 @@ def test_rows_zero_and_limits():
     assert e.value.code == moe.MOE_ERR_ALIAS
 
 
-# DeepSeek-V3 routing geometry (256 experts in 8 groups of 32, keep 4,
-# top-8) on a small layer: the paths that hold for 32-lane groups and for
+# The V3 routing geometry: the paths that hold for 32-lane groups and for
 # ties at the top-k threshold.
-V3R = dict(hidden=1024, inter=256, shared_inter=256, n_experts=256, top_k=8, n_group=8, topk_group=4)
 
 
 def _route_both(spec, case, T):

@@ -12,7 +12,7 @@ import torch
 
 import fixtures
 import mixture_experts_decode_sigmoid_amd as moe
-from _gpu import (MAX_ABS, REL_L2, gpu_case, oracle_route, oracle_rows, parity, run_forward, say)
+from _gpu import (MAX_ABS, REL_L2, bf16_to_f64, gpu_case, oracle_route, oracle_rows, parity, run_forward, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -112,9 +112,9 @@ def test_small_groups_exact(name, over, T, seed, rows):
 
 FULL = [
     ("v3_t1", [0]),
-    ("v3_t8", [0, 3, 5, 7]),
-    ("v3_t64", [0, 17, 42, 63]),
-    ("v4_t16", [0, 6, 15]),
+    ("v3_t8", list(range(8))),
+    ("v3_t64", list(range(64))),
+    ("v4_t16", list(range(16))),
     # the 8-way tensor-parallel share of the V3 layer (intermediate 256)
     ("v3tp8_t1", [0]),
     ("v3tp8_t8", [0, 4, 7]),
@@ -154,6 +154,10 @@ def test_full_size_sampled(full_cases, name, rows):
     rel, mx = parity(out, o64, rows)
     say(f"  rel_l2={rel:.3e} max_abs={mx:.3e}")
     assert rel <= REL_L2 and mx <= MAX_ABS
+    # every row on its own, too
+    for r in rows:
+        rel_r, mx_r = parity(out, o64, [r])
+        assert rel_r <= REL_L2 and mx_r <= MAX_ABS, (r, rel_r, mx_r)
     assert np.all(np.isfinite(out.view(np.int16).astype(np.float64)))
 
 
@@ -198,3 +202,54 @@ def test_residual_parity(name, over, T, seed, rows):
     zero = layer.forward(case["x"], residual=torch.zeros_like(res))
     torch.cuda.synchronize()
     assert np.array_equal(fixtures.bits16(zero), plain)
+
+
+# The DeepSeek-V3 routing geometry (256 experts in 8 groups of 32, keep 4,
+# top-8) on a small layer, at batch sizes the wide stream serves (its
+# routing is its own code: many rows per wave, read after a flag barrier):
+# routing and every row's output against the oracle for the whole batch.
+V3R = dict(hidden=1024, inter=256, shared_inter=256, n_experts=256, top_k=8, n_group=8, topk_group=4)
+
+
+@pytest.mark.parametrize("T,seed,rows", [(17, 61, "iid"), (37, 62, "corr"), (64, 63, "iid")])
+def test_v3_routing_wide_whole_batch(T, seed, rows):
+    say(f"v3 routing wide T={T}")
+    spec = _spec(V3R)
+    case = gpu_case(spec, T, seed, rows=rows, requests=max(1, T // 4))
+    layer = moe.Layer(spec, case, max_rows=T)
+    ids_o, w_o, ge, gg = oracle_route(spec, case)
+    assert np.min(ge) > 1e-9 and np.min(gg) > 1e-9
+    ids, wts = layer.route(case["x"])
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ids_o)
+    assert np.allclose(wts.cpu().numpy(), w_o, rtol=1e-6, atol=0)
+    out = run_forward(layer, case["x"])
+    o64, _ = oracle_rows(spec, case, range(T), ids=ids_o)
+    rel, mx = parity(out, o64, list(range(T)))
+    say(f"  rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert rel <= REL_L2 and mx <= MAX_ABS
+
+
+# The residual is added before the single rounding: with the residual set to
+# minus moe_forward's own bf16 output, the kernel's fp32 chain plus the
+# residual is the chain's rounding error, whose bf16 value is nonzero almost
+# everywhere and at most half a bf16 ulp of the output; a kernel that rounded
+# the layer to bf16 before adding would return exactly zero.
+@pytest.mark.parametrize("name,over,T,seed,rows", RESID, ids=[s[0] for s in RESID])
+def test_residual_single_rounding_bits(name, over, T, seed, rows):
+    say(f"residual rounding {name} T={T}")
+    spec = _spec(over)
+    case = gpu_case(spec, T, seed, rows=rows, requests=max(1, T // 4))
+    layer = moe.Layer(spec, case, max_rows=T)
+    plain = run_forward(layer, case["x"])
+    neg = torch.from_numpy((plain ^ np.uint16(0x8000)).view(np.int16)).view(torch.bfloat16).cuda()
+    got = fixtures.bits16(layer.forward(case["x"], residual=neg))
+    torch.cuda.synchronize()
+    assert layer.read_error() == 0
+    nz = (got & np.uint16(0x7FFF)) != 0
+    say(f"  nonzero {nz.mean():.4f}")
+    assert nz.mean() > 0.9
+    p = np.abs(bf16_to_f64(plain))
+    r = np.abs(bf16_to_f64(got))
+    ulp = np.where(p > 0, np.exp2(np.floor(np.log2(np.where(p > 0, p, 1.0))) - 7), 2.0 ** -133)
+    assert np.all(r <= ulp / 2)

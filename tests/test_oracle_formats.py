@@ -11,6 +11,8 @@ import numpy as np
 import pytest
 import torch
 
+import _bf16
+
 
 def test_e4m3_all_codes(orc):
     ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
@@ -64,31 +66,10 @@ def test_bf16_decode_all_codes(orc):
 @pytest.fixture(scope="module")
 def bf16_table():
     """All finite non-negative bf16 values, ascending, with their codes."""
-    codes = np.arange(0, 0x7F80, dtype=np.uint16)
-    vals = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
-    return codes, vals
+    return _bf16.table()
 
 
-def _brute_rne(v, codes, vals):
-    if v != v:
-        return None
-    sign = 0x8000 if math.copysign(1.0, v) < 0 else 0
-    a = abs(v)
-    top = vals[-1]
-    half_over = top + (top - vals[-2]) / 2  # halfway to 2^128
-    if a >= half_over:
-        return sign | 0x7F80
-    i = int(np.searchsorted(vals, a, side="right")) - 1  # vals[i] <= a
-    if i == len(vals) - 1:
-        return sign | int(codes[i])
-    lo, hi = vals[i], vals[i + 1]
-    if a - lo < hi - a:
-        c = codes[i]
-    elif a - lo > hi - a:
-        c = codes[i + 1]
-    else:
-        c = codes[i] if codes[i] % 2 == 0 else codes[i + 1]
-    return sign | int(c)
+_brute_rne = _bf16.brute_rne
 
 
 def test_bf16_rne_brute_force(orc, bf16_table):

@@ -17,6 +17,7 @@ import pytest
 import scipy.special
 import torch
 
+import _bf16
 import fixtures
 
 
@@ -231,3 +232,23 @@ def test_residual_alone_with_zero_weights(orc):
     o64, ob = orc.forward_residual(spec, hz, res)
     assert np.array_equal(ob, res)
     assert np.array_equal(o64, _bf(res))
+
+
+def test_residual_is_rounded_once(orc):
+    """With the residual set to minus the layer's own bf16 output, one
+    rounding of (layer + residual) leaves the layer's rounding error as a
+    bf16 value, RNE(layer64 - RNE(layer64)), nonzero wherever the layer is
+    not already a bf16 value; rounding the layer to bf16 first and then
+    adding would give exactly zero everywhere.  The expected codes come from
+    an exact fp64 difference and a brute-force bf16 rounding over the table
+    of every bf16 value, not from the oracle's own rounding."""
+    spec, h = _tiny(T=3)
+    out64, outb = orc.forward(spec, h)
+    res = outb ^ np.uint16(0x8000)
+    o64, ob = orc.forward_residual(spec, h, res)
+    codes, vals = _bf16.table()
+    err = out64 - _bf(outb)                 # exact (the operands are within a bf16 ulp)
+    assert np.array_equal(o64, err)
+    want = np.array([_bf16.brute_rne(float(v), codes, vals) for v in err.ravel()], np.uint16).reshape(ob.shape)
+    assert np.array_equal(ob, want)
+    assert np.count_nonzero(ob & np.uint16(0x7FFF)) > 0.95 * ob.size
