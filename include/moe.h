@@ -173,6 +173,26 @@ int moe_forward(const moe_config* cfg, const moe_weights* w, const uint16_t* x, 
 int moe_forward_residual(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
                          const uint16_t* residual, uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate or pass a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * layer as moe_forward (same kernel, same result bit for bit), with the
+ * workspace held in a static device array of the library, one per GPU, of
+ * 5 MiB (5,242,880 bytes), kept until the process ends.  Every configuration
+ * moe_workspace_size accepts fits (the largest needs 4,985,088 bytes); one
+ * that did not would give MOE_ERR_WORKSPACE.  Nothing is allocated.
+ *   - The first call on a device sets the array up (its address, and a
+ *     clearing kernel on `stream` for the words that must start at zero); that
+ *     first call must not be under stream capture (MOE_ERR_WORKSPACE if it
+ *     is).  Later calls may be captured.
+ *   - All calls on one device share the array and it keeps the last call's
+ *     contents: calls that overlap on one device race (they must be ordered,
+ *     e.g. on one stream).
+ *   - The device error bits of these calls stay in the array; there is no
+ *     moe_read_error for them.
+ * Arguments and return codes are as for moe_forward. */
+int moe_forward_noalloc(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
+                        uint16_t* out, void* stream);
+
 /* Waits for `stream`, then returns the workspace's device error bits in
  * *bits (host) and clears them. */
 int moe_read_error(void* ws, void* stream, uint32_t* bits);

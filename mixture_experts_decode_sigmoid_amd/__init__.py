@@ -91,9 +91,10 @@ def lib() -> C.CDLL:
         L.moe_strerror.restype = C.c_char_p
         L.moe_last_hip_error.argtypes = []
         L.moe_probe_stream_read.argtypes = [P, Z, P, I, P]
+        L.moe_forward_noalloc.argtypes = [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P]
         for f in ("moe_workspace_size", "moe_workspace_init", "moe_route", "moe_groups",
                   "moe_forward", "moe_forward_residual", "moe_read_error", "moe_last_hip_error",
-                  "moe_probe_stream_read"):
+                  "moe_probe_stream_read", "moe_forward_noalloc"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -101,7 +102,7 @@ def lib() -> C.CDLL:
 
 EXPORTS = ("moe_workspace_size", "moe_workspace_init", "moe_route", "moe_groups",
            "moe_forward", "moe_forward_residual", "moe_read_error", "moe_strerror", "moe_last_hip_error",
-           "moe_probe_stream_read")
+           "moe_probe_stream_read", "moe_forward_noalloc")
 
 
 def strerror(code: int) -> str:
@@ -180,6 +181,13 @@ def moe_forward_residual(cfg, w, x, residual, out, ws, stream=None):
     """x, residual, out: [rows, H] bf16 (device); residual may be out."""
     _check(lib().moe_forward_residual(C.byref(cfg), C.byref(w), _ptr(x), int(x.shape[0]), _ptr(residual),
                                       _ptr(out), _ptr(ws), ws.numel(), _stream(stream)), "moe_forward_residual")
+
+
+def moe_forward_noalloc(cfg, w, x, out, stream=None):
+    """moe_forward with the library's static per-device workspace (no
+    workspace argument, nothing allocated)."""
+    _check(lib().moe_forward_noalloc(C.byref(cfg), C.byref(w), _ptr(x), int(x.shape[0]), _ptr(out),
+                                     _stream(stream)), "moe_forward_noalloc")
 
 
 def moe_read_error(ws, stream=None) -> int:
