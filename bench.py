@@ -230,6 +230,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--workload", default=HEADLINE,
+                    help="time this workload only (for profiling runs; implies --no-extra --no-cpu)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (for PMC byte-counter calibration)")
     args = ap.parse_args()
@@ -251,6 +253,15 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+
+    if args.workload != HEADLINE:
+        spec, case = fixtures.make_workload(args.workload, device="cuda")
+        copies = build_copies(spec, case, N_COPIES)
+        per, distinct = time_layer(spec, copies, case["x"], args.steps, args.warmup)
+        d = summary(per, fixtures.algorithmic_bytes(spec, distinct), None)
+        print(json.dumps(dict(workload=args.workload, rows=case["x"].shape[0], distinct_experts=distinct, **d)),
+              flush=True)
+        return
 
     stream_gbs = stream_read_gbs()
     note(f"stream read {stream_gbs} GB/s")

@@ -98,6 +98,16 @@ def run(workload: str, calls: int, copies: int = 4):
         rows.append((med, f"waves: {name}", mx))
     for med, name, mx in sorted(rows):
         print(f"  {name:40s} {med:8.2f} {mx:8.2f}")
+    # spread over CUs of the phase ends (median over calls of each percentile),
+    # and by XCD (workgroup i runs on XCD i mod 8)
+    print("  spread over CUs: p10 / p50 / p90 / max; then the median per XCD 0..7")
+    for i in (11, 4, 12, 5, 6, 7):
+        if not valid[:, :, i].all():
+            continue
+        q = np.median(np.percentile(us[:, :, i], [10, 50, 90, 100], axis=1), axis=1)
+        xcd = [np.median(us[:, x::8, i]) for x in range(8)]
+        print(f"  {NAMES[i]:28s} " + " ".join(f"{v:7.2f}" for v in q) + "  |" +
+              " ".join(f"{v:6.1f}" for v in xcd))
     return rows
 
 
