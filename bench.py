@@ -45,7 +45,7 @@ STREAM_BYTES = 4 << 30
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("moe_kernels.hip", "moe_kernels_res.hip", "moe_api.cpp", "moe_internal.h"):
+    for f in ("moe_kernels.hip", "moe_api.cpp", "moe_internal.h"):
         with open(os.path.join(ROOT, "mixture_experts_decode_sigmoid_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

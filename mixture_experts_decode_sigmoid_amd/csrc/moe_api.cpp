@@ -123,9 +123,7 @@ int fill(const moe_config* c, const moe_weights* w, const uint16_t* x, int rows,
   p.hs = hs;
   p.ncu = d.ncu;
   p.mid_ld = L.mid_ld;
-  // the narrow stream for batches of at most 16 rows when its partials fit
-  size_t lds = rows <= 16 ? stream_geometry(p, 1) : (size_t)-1;
-  if (lds > d.max_lds) lds = stream_geometry(p, 0);
+  size_t lds = stream_geometry(p);
   if (lds > d.max_lds) return MOE_ERR_SHAPE;
   if (lds < (size_t)kMinLds) lds = kMinLds;
   p.lds_bytes = (int)lds;

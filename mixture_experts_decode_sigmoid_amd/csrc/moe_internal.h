@@ -20,7 +20,15 @@ constexpr int kMaxGroups = 64;            // router groups
 constexpr int kMaxSlice = 64;             // output rows per CU in down
 constexpr int kMinLds = 84 * 1024;        // LDS per workgroup: more than half a CU's, so one per CU
 
-enum Mode { kModeForward = 0, kModeRoute = 1, kModeGroups = 2, kModeForwardRes = 3 };  // 3: kernel only (wide stream with a residual)
+enum Mode { kModeForward = 0, kModeRoute = 1, kModeGroups = 2 };
+
+// Activation loads per weight item (AL) by batch size: a job takes at most
+// 4 * AL columns (a group with more columns is split into column tiles, each
+// a job of its own), and every item of a kernel issues the same loads.
+__host__ __device__ inline int stream_al(int T) { return T <= 4 ? 1 : T <= 8 ? 2 : T <= 16 ? 4 : 2; }
+// Down jobs are split over waves by K-phase up to this many rows; above it
+// every wave claims whole down jobs (the K-phase partials would not fit LDS).
+constexpr int kKsplitRows = 16;
 
 // Workspace layout (byte offsets from the workspace base).
 struct WsLayout {
@@ -37,12 +45,18 @@ struct Params {
   int ncu;         // workgroups launched (= CUs)
   int mid_ld;
   int lds_bytes;   // dynamic LDS size
-  // stream geometry (see lds_offsets): narrow = per-wave partials in LDS
-  int narrow;      // 1: batches of at most 16 rows whose partials fit in LDS
+  // stream geometry (see lds_offsets)
   int nrt_p;       // 16-row down tiles of a CU's slice, rounded up to 1, 2 or 4
-  int wpt;         // waves per down tile (8 / nrt_p); they split its K-blocks
+  int kph;         // K-phases of a down sum: waves per down tile (8 / nrt_p); every
+                   // down product is the sum of its K-phase partials in phase order
+  int wpt;         // copies of the down products in LDS: kph up to kKsplitRows rows
+                   // (one per K-phase), else 1 (each wave claims whole down jobs
+                   // and adds their K-phase partials itself)
   int pitch;       // floats per (row, slot) line of the down products (16 * tiles)
-  int qcap;        // narrow: up/gate job entries of a CU (its share of the most jobs a batch can have)
+  int cpj;         // columns per job (4 * AL); groups with more are split
+  int pcols;       // columns of an up/gate partial tile (min(T, cpj))
+  int qcap;        // up/gate job entries of a CU (its share of the most jobs a batch can have)
+  int dcap;        // down job entries (one per group and column tile, most a batch can have)
   // inputs
   const uint16_t* x;
   const uint16_t* router_w;
@@ -72,15 +86,13 @@ struct Params {
 };
 
 WsLayout ws_layout(int max_rows, int E, int K, int H, int I, int Is);
-// Fills the stream geometry of p (T, K, E, I, Is, hs, ncu set) for the
-// narrow (narrow = 1) or wide layout and returns the LDS bytes it needs.
-size_t stream_geometry(Params& p, int narrow);
+// Fills the stream geometry of p (T, K, E, I, Is, hs, ncu, n_shared set)
+// and returns the LDS bytes it needs.
+size_t stream_geometry(Params& p);
 // Launches the fused kernel instance for p and mode on device `dev` (the
 // current device).  Returns hipErrorCooperativeLaunchTooLarge when one
 // workgroup per CU with p's LDS size cannot be resident on this device.
 hipError_t launch(const Params& p, int mode, hipStream_t stream, int dev);
-// The forward of the wide stream with a residual (moe_kernels_res.hip).
-hipError_t launch_res_wide(const Params& p, hipStream_t stream, int dev);
 // moe_forward / moe_forward_residual after their own argument checks:
 // validates, carves the workspace ws (ws_bytes) and launches.
 int forward_checked(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,

@@ -209,66 +209,59 @@ struct Lds {
   int32_t* gstart;   // [1+T*K]
   int32_t* cols;     // [T*(K+1)] row*16 + slot
   int32_t* cgrp;     // [T*(K+1)] group of each column
-  int32_t* misc;     // [32]: 0 = G, 1 = epoch, 8.. = scan
-  uint32_t* ctl;     // [64] chunk-stream counters (see kCtl*)
-  float* red;        // [red_slots][red_tiles][kWaves][64][4] job-end partials
-  double* rb;        // [kWaves][E] router keys (aliases red and pbuf)
+  int32_t* misc;     // [32]: 0 = G, 1 = epoch, 8.. = scan, kMisc* words
+  uint32_t* ctl;     // [64] stream counters (see kCtl*)
+  double* rb;        // [kWaves][E] router keys (routing scratch, see lds_offsets)
   double* rgs;       // [kWaves][64] group scores
   int32_t* rkept;    // [kWaves][64]
   double* rcb;       // [kWaves][E] top-k candidates: key b
   double* rcs;       // [kWaves][E] and score s
   int32_t* rce;      // [kWaves][E] and expert
-  float* pbuf;       // wide: down products [T*(K+1)][hs]; narrow: the per-wave partials (see lds_offsets)
-  struct JobDesc* jd;  // narrow: job descriptors (this CU's up/gate jobs, then down jobs)
-  uint32_t* wcnt;    // narrow: [kPuWin] chunks of the job in each partial window that have ended
-  uint32_t* wgen;    // narrow: [kPuWin] jobs summed out of each window
-  uint32_t* ccnt;    // narrow: up/gate chunks claimed by this CU's waves
-  uint32_t* cfifo;   // narrow: [kWaves][8] each wave's claimed chunks, fetch side to multiplying side
+  float* pbuf;       // the per-wave partials (see lds_offsets)
+  struct JobDesc* jd;  // job descriptors (this CU's up/gate jobs, then the down jobs)
+  uint32_t* wcnt;    // [kPuWin] chunks of the job in each partial window that have ended
+  uint32_t* wgen;    // [kPuWin] jobs summed out of each window
+  uint32_t* ccnt;    // up/gate chunks claimed by this CU's waves ([1]: down jobs claimed)
+  uint32_t* cfifo;   // [kWaves][8] each wave's claimed chunks, fetch side to multiplying side
 };
 
 __host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// LDS words of the narrow stream's start (misc[]).
+// LDS words of the stream's start (misc[]).
 constexpr int kMiscNU = 2;      // this CU's up/gate jobs, once routed
 constexpr int kMiscReady = 3;   // 1 once the routed jobs' tables are written
 constexpr int kMiscRouted = 4;  // rows routed so far (early start)
 constexpr int kMiscPolled = 5;  // rows whose scores are in (early start)
+constexpr int kMiscND = 6;      // down job entries (groups x column tiles), once routed
 
-// Job-end partials: one 16-column tile per job when a batch has at most 16
-// rows (four slots), else four tiles (two slots).
-__host__ __device__ inline int red_tiles(int T) { return T > 16 ? kMaxRows / 16 : 1; }
-__host__ __device__ inline int red_slots(int T) { return T > 16 ? 2 : 4; }
-constexpr size_t kRedTileBytes = 16 * (size_t)kWaves * 64;  // one tile: [wave][lane] f32x4
-
-// Narrow layout (batches of at most 16 rows): every wave keeps its partial
-// tiles apart in LDS, and they are summed over the waves in wave order:
+// Every wave keeps its partial tiles apart in LDS, and they are summed over
+// the waves in wave order:
 //   up/gate  Pu[win][w][col][16], win = local job mod kPuWin (w = 0..7, the
-//            job's K-phase; col < T, the job's column; 16 rows: 8 gate then
-//            8 up), summed by the wave that ends the job's last chunk
+//            job's K-phase; col < pcols, the job's column; 16 rows: 8 gate
+//            then 8 up), summed by the wave that ends the job's last chunk
 //   down     Pd[kp][row][slot][pitch]  (kp = 0..wpt-1, the K-phase of the
 //            waves that share a 16-row down tile; h along the slice),
-//            summed in the combine
+//            summed in the combine; with wpt = 1 (above kKsplitRows rows)
+//            each down job is one wave's whole sum
 // Pu and Pd share one region (Pu is done with before Pd is written), which
-// also holds the routing scratch before the stream.  The job descriptors
-// (qcap up/gate entries, then one down job per group) sit before it.  The wide layout keeps
-// job-end partial slots summed by an owner wave, and one copy of the down
-// products [row][slot][hs].
+// also holds the routing scratch before the stream, except in a call of at
+// most as many rows as waves, whose waves stream while other rows are
+// routed.  The job descriptors (qcap up/gate entries, then dcap down
+// entries) sit before it.
 constexpr int kPuWin = 8;
 struct LdsOffsets {
-  size_t ids, w, first, egrp, rmask, gexp, gcnt, gstart, cols, cgrp, misc, ctl, wst, jd, red, pbuf, total;
+  size_t ids, w, first, egrp, rmask, gexp, gcnt, gstart, cols, cgrp, misc, ctl, wst, jd, rs, pbuf, total;
 };
 constexpr size_t kJobDescBytes = 48;
 
-__host__ __device__ inline size_t pu_floats(int T) { return (size_t)kPuWin * kWaves * T * 16; }
-
-__host__ __device__ inline LdsOffsets lds_offsets(int T, int K, int E, int hs, int narrow, int wpt, int pitch,
-                                                  int qcap) {
+__host__ __device__ inline LdsOffsets lds_offsets(const Params& p) {
   LdsOffsets o;
 #ifdef MOE_TIMELINE
   size_t q = 64 * 8;  // the stamps first (see MOE_TL)
 #else
   size_t q = 0;
 #endif
+  const int T = p.T, K = p.K, E = p.E;
   const int uses = T * K, gmax = 1 + T * K;
   o.ids = q; q = align_up(q + 4 * (size_t)uses, 16);
   o.w = q; q = align_up(q + 4 * (size_t)uses, 16);
@@ -283,56 +276,50 @@ __host__ __device__ inline LdsOffsets lds_offsets(int T, int K, int E, int hs, i
   o.misc = q; q = align_up(q + 4 * 32, 16);
   o.ctl = q; q = align_up(q + 4 * 64, 16);
   o.wst = q; q = align_up(q + 8 * kPuWin + 16 + 4 * kWaves * 8, 16);
-  o.jd = q; q = align_up(q + (narrow ? kJobDescBytes * (size_t)(qcap + gmax) : 0), 16);
-  // the routing scratch (used before the stream) overlaps the job-end
-  // partials and the down products (used in it), except in a narrow call of
-  // at most as many rows as waves, whose waves stream while other rows are
-  // routed
-  o.red = q;
+  o.jd = q; q = align_up(q + kJobDescBytes * (size_t)(p.qcap + p.dcap), 16);
   // routing scratch: rb, rgs, rkept, then the top-k candidates (b, s, e) per wave
+  o.rs = q;
   const size_t rs = 8 * (size_t)kWaves * E + 8 * (size_t)kWaves * 64 + 4 * (size_t)kWaves * 64 +
                     20 * (size_t)kWaves * E;
+  const size_t pu = 4 * (size_t)kPuWin * kWaves * p.pcols * 16;
+  const size_t pd = 4 * (size_t)p.wpt * T * (K + 1) * p.pitch;
+  const size_t need = pu > pd ? pu : pd;
   size_t end;
-  if (narrow) {
-    const size_t pu = 4 * pu_floats(T);
-    const size_t pd = 4 * (size_t)wpt * T * (K + 1) * pitch;
-    const size_t need = pu > pd ? pu : pd;
-    if (T <= kWaves) {
-      o.pbuf = align_up(q + rs, 16);
-      end = o.pbuf + need;
-    } else {
-      o.pbuf = q;
-      end = q + (need > rs ? need : rs);
-    }
+  if (T <= kWaves) {
+    o.pbuf = align_up(q + rs, 16);
+    end = o.pbuf + need;
   } else {
-    const size_t rd = (size_t)red_slots(T) * red_tiles(T) * kRedTileBytes;
-    const size_t need = rd + 4 * (size_t)T * (K + 1) * hs;
-    o.pbuf = q + rd;
+    o.pbuf = q;
     end = q + (need > rs ? need : rs);
   }
   o.total = align_up(end, 16);
   return o;
 }
 
-#ifndef MOE_RES_WIDE_TU
-size_t stream_geometry(Params& p, int narrow) {
+// Bounds of the job tables.  Up/gate: a CU gets at most ceil(tiles/ncu)
+// tiles of each group, and a group of c columns is ceil(c/cpj) jobs per tile;
+// over a batch the routed groups number at most min(E, T*K) with T*K
+// columns, so their column tiles number at most min(E, T*K) + T*K/cpj.
+size_t stream_geometry(Params& p) {
   const int nrt = (p.hs + 15) / 16;
   p.nrt_p = nrt <= 1 ? 1 : nrt <= 2 ? 2 : 4;
-  p.wpt = kWaves / p.nrt_p;
+  p.kph = kWaves / p.nrt_p;
+  p.wpt = p.T <= kKsplitRows ? p.kph : 1;
   p.pitch = 16 * nrt;
-  p.narrow = narrow;
-  // up/gate job entries: a CU's share of the largest job count the batch
-  // can have
-  const int gmax = 1 + (p.E < p.T * p.K ? p.E : p.T * p.K);
-  const int sh_tiles = p.n_shared ? p.Is / 8 : 0;
-  const long jobs = sh_tiles + (long)(gmax - 1) * (p.I / 8);
-  p.qcap = (int)((jobs + p.ncu - 1) / p.ncu);
-  return lds_offsets(p.T, p.K, p.E, p.hs, p.narrow, p.wpt, p.pitch, p.qcap).total;
+  p.cpj = 4 * stream_al(p.T);
+  p.pcols = p.T < p.cpj ? p.T : p.cpj;
+  const int tk = p.T * p.K;
+  const int nct_sh = p.n_shared ? (p.T + p.cpj - 1) / p.cpj : 0;
+  const int ct_routed = (p.E < tk ? p.E : tk) + (tk + p.cpj - 1) / p.cpj;
+  const int sh_tiles = p.n_shared ? p.Is / 8 : 0, rt_tiles = p.I / 8;
+  const int per_sh = (sh_tiles + p.ncu - 1) / p.ncu, per_rt = (rt_tiles + p.ncu - 1) / p.ncu;
+  p.qcap = per_sh * nct_sh + per_rt * ct_routed;
+  p.dcap = nct_sh + ct_routed;
+  return lds_offsets(p).total;
 }
-#endif
 
 __device__ inline Lds lds_map(char* base, const Params& p) {
-  LdsOffsets o = lds_offsets(p.T, p.K, p.E, p.hs, p.narrow, p.wpt, p.pitch, p.qcap);
+  LdsOffsets o = lds_offsets(p);
   Lds L;
   L.ids = (int32_t*)(base + o.ids);
   L.w = (float*)(base + o.w);
@@ -351,9 +338,8 @@ __device__ inline Lds lds_map(char* base, const Params& p) {
   L.wgen = L.wcnt + kPuWin;
   L.ccnt = L.wgen + kPuWin;
   L.cfifo = L.ccnt + 4;
-  L.red = (float*)(base + o.red);
   L.pbuf = (float*)(base + o.pbuf);
-  L.rb = (double*)(base + o.red);
+  L.rb = (double*)(base + o.rs);
   L.rgs = L.rb + (size_t)kWaves * p.E;
   L.rkept = (int32_t*)(L.rgs + (size_t)kWaves * 64);
   L.rcb = (double*)(L.rkept + (size_t)kWaves * 64);
@@ -1126,10 +1112,6 @@ __device__ __forceinline__ void lds_st128(void* p, u32x4 v) {
 // Stream counters in LDS.  Every counter counts up from 0 within a launch
 // and is written by one wave only.
 constexpr int kCtlProg = 0;    // [8]  jobs wave w has ended
-constexpr int kCtlPart = 16;   // [8]  jobs whose partials wave w has stored
-constexpr int kCtlSlot = 24;   // [4]  1 + the last job summed out of partial slot s
-constexpr int kCtlMidOut = 40; // [8]  1 once wave w's mid stores are complete
-constexpr int kCtlCrossed = 48;// [1]  1 once wave 0 has seen every CU's mid
 
 // Minimum of N consecutive LDS counters (N = 1 or 8), one round trip.  Every
 // lane reads the same words; the result goes through readfirstlane so the
@@ -1173,161 +1155,18 @@ __device__ inline uint32_t lds_wait(const Params& p, const uint32_t* a, uint32_t
   return v;
 }
 
-// Column tiles a group can have: 1 when NPRE is 1 (batches of at most 16
-// rows), else up to 4 (64 rows).
-template <int NPRE>
-constexpr int max_tiles() { return NPRE == 1 ? 1 : kMaxRows / 16; }
-// Items in flight per wave.
-template <int NPRE>
-constexpr int depth() { return NPRE == 1 ? 5 : 3; }
-
 struct Sched {
-  int sh_tiles;  // shared up/gate jobs (I_s / 8)
-  int rt_tiles;  // routed up/gate jobs per group (I / 8)
-  int n_jobs;    // all up/gate jobs, known after routing
+  int sh_tiles;  // shared up/gate tiles (I_s / 8)
+  int rt_tiles;  // routed up/gate tiles per group (I / 8)
+  int n_pairs;   // all (group, tile) pairs, known after routing
   int G;         // groups, known after routing
   int h0, hc;    // this CU's down rows
   int nrt;       // 16-row tiles of them
-  int nrt_p, wpt;  // tiles rounded up to 1, 2 or 4; waves per tile
-  int narrow;    // each wave walks only its own down tile's jobs
+  int nrt_p, wpt;  // tiles rounded up to 1, 2 or 4; copies of the down products
+  int kph;         // K-phases of a down sum
 };
-
-// Position in this CU's job sequence.
-struct It {
-  int phase;  // 0 shared up/gate, 1 routed up/gate, 2 down, 3 end
-  int j;      // up/gate: global job index; down: group
-  int rt;     // down: 16-row tile of this CU's slice
-  int g;      // the job's group (kept current by settle / next_job)
-  int tile;   // up/gate: its 8-intermediate tile of that group
-};
-
-__device__ __forceinline__ void uni(It& c) {
-  c.phase = uni(c.phase);
-  c.j = uni(c.j);
-  c.rt = uni(c.rt);
-  c.g = uni(c.g);
-  c.tile = uni(c.tile);
-}
-
-// Smallest j >= begin with j = blockIdx.x (mod ncu): jobs are dealt round-robin.
-__device__ __forceinline__ int first_job(const Params& p, int begin) {
-  const int r = begin % p.ncu;
-  return begin + (((int)blockIdx.x - r) % p.ncu + p.ncu) % p.ncu;
-}
-
-// Up/gate jobs: the shared expert's tiles come first, then rt_tiles tiles
-// per routed group; a down job names its group.  The group and tile are
-// derived once on entering a phase and then advanced incrementally.
-__device__ inline void settle(const Params& p, const Sched& s, It& c) {
-  for (;;) {
-    if (c.phase == 0) {
-      c.g = 0;
-      c.tile = c.j;
-      if (c.j < s.sh_tiles) return;
-      c.phase = 1;
-      c.j = first_job(p, s.sh_tiles);
-      c.g = p.n_shared + (c.j - s.sh_tiles) / s.rt_tiles;
-      c.tile = (c.j - s.sh_tiles) % s.rt_tiles;
-      continue;
-    }
-    if (c.phase == 1) {
-      if (c.j < s.n_jobs) return;
-      c.phase = 2;
-      c.j = 0;
-      c.rt = s.narrow ? wave_id() % s.nrt_p : 0;
-      c.tile = 0;
-      continue;
-    }
-    c.g = c.j;
-    if (c.phase == 2 && (c.rt >= s.nrt || c.j >= s.G)) c.phase = 3;
-    return;
-  }
-}
-
-__device__ inline void next_job(const Params& p, const Sched& s, It& c) {
-  if (c.phase == 0) {
-    c.j += p.ncu;
-  } else if (c.phase == 1) {
-    c.j += p.ncu;
-    c.tile += p.ncu;
-    while (c.tile >= s.rt_tiles) {
-      c.tile -= s.rt_tiles;
-      ++c.g;
-    }
-  } else if (s.narrow) {
-    ++c.j;
-  } else if (++c.rt >= s.nrt) {
-    c.rt = 0;
-    ++c.j;
-  }
-  settle(p, s, c);
-}
 
 __device__ __forceinline__ bool shared_group(const Params& p, int g) { return p.n_shared && g == 0; }
-__device__ __forceinline__ int job_kdim(const Params& p, const It& c) {
-  // (fields taken through uni(): see arg_ptr)
-  const int H = uni(p.H), I = uni(p.I), Is = uni(p.Is);
-  return c.phase <= 1 ? H : (shared_group(p, c.g) ? Is : I);
-}
-// This wave's K-blocks of a job: k0 + step*i, i < n.  Up/gate jobs split
-// their K-blocks over all 8 waves (k0 = w, step 8).  A down tile belongs to
-// the wpt waves w with w % nrt_p == tile, which split its K-blocks
-// (k0 = w / nrt_p, step wpt); the other waves have no items in it.
-struct KRange {
-  int k0, step, n;
-};
-__device__ __forceinline__ KRange job_krange(const Params& p, const Sched& s, const It& c) {
-  const int w = wave_id(), nkb = job_kdim(p, c) >> 7;
-  KRange r;
-  if (c.phase <= 1) {
-    r.k0 = w;
-    r.step = kWaves;
-  } else {
-    r.k0 = w % s.nrt_p == c.rt ? w / s.nrt_p : nkb;
-    r.step = s.wpt;
-  }
-  r.n = uni(nkb > r.k0 ? (nkb - 1 - r.k0) / r.step + 1 : 0);
-  r.k0 = uni(r.k0);
-  r.step = uni(r.step);
-  return r;
-}
-__device__ __forceinline__ int job_nlive(const Sched& s, const It& c) {
-  return c.phase == 2 ? (s.hc - 16 * c.rt < 16 ? s.hc - 16 * c.rt : 16) : 16;
-}
-// Column c of group g as row*16 + slot.
-__device__ __forceinline__ int col_code(const Params& p, const Lds& L, int g, int c) {
-  if (shared_group(p, g)) return c * 16 + p.K;
-  return (int)lds_ld32(L.cols + lds_ldi_uniform(L.gstart + g) + c);
-}
-
-// Column facts of a job's group: its column count and expert (LDS, one
-// round trip for a routed group), and this lane's column code in tiles
-// 0..NT-1 (a lane past the group's columns takes the last column: MFMA
-// columns are independent and that output is never stored).
-template <int NT>
-__device__ inline void group_cols(const Params& p, const Lds& L, int g, int& ncols, int& eid, int (&code)[NT]) {
-  const int lane = threadIdx.x & 63;
-  int gstart = 0;
-  const bool sh = shared_group(p, g);
-  if (sh) {
-    ncols = p.T;
-    eid = 0;
-  } else {
-    uint32_t a, b, c;
-    asm volatile("ds_read_b32 %0, %3\n\tds_read_b32 %1, %4\n\tds_read_b32 %2, %5\n\ts_waitcnt lgkmcnt(0)"
-                 : "=&v"(a), "=&v"(b), "=&v"(c)
-                 : "v"(lds_off(L.gcnt + g)), "v"(lds_off(L.gstart + g)), "v"(lds_off(L.gexp + g))
-                 : "memory");
-    ncols = uni((int)a);
-    gstart = uni((int)b);
-    eid = uni((int)c);
-  }
-#pragma unroll
-  for (int ct = 0; ct < NT; ++ct) {
-    const int cc = ct * 16 + (lane & 15) < ncols ? ct * 16 + (lane & 15) : ncols - 1;
-    code[ct] = sh ? cc * 16 + p.K : (int)lds_ld32(L.cols + gstart + cc);
-  }
-}
 
 // Activation offset (elements) of column code `code` for lane group lg:
 // x rows for up/gate, mid lines for down.
@@ -1338,394 +1177,8 @@ __device__ __forceinline__ uint32_t act_offset(const Params& p, int kind, int co
   return t + 32u * (uint32_t)lg;
 }
 
-// One item in registers.
-template <int NPRE>
-struct Item {
-  u32x4 w0, w1;       // this lane's weights (row lane & 15): FP8 32 bytes, MXFP4 16 (w1 repeats w0)
-  u32x4 B[4 * NPRE];  // activations of column tiles 0..NPRE-1 (column lane & 15 of the tile)
-  uint32_t s;         // FP8: the K-block's scale of the tile's first (lanes 0-31) or second
-                      // (32-63) 128-row block; MXFP4: the lane's row's four E8M0 scales
-};
-
-// The fetch side: where this wave's next items come from.
-template <int NPRE>
-struct Fetch {
-  It it;
-  int i, n;           // next item of the job, this wave's items in it
-  int fmt, live;      // live = 0 past the end of the phase (dummy items)
-  int k0, step;       // K-blocks of the job's items: k0 + step*i
-  int g, eid;         // group of the last job set up, and its expert
-  const uint8_t* wrow;  // this lane's weight row at K offset 0
-  const uint8_t* srow;  // this lane's scale row (see Item::s)
-  const uint16_t* abase;
-  uint32_t act[NPRE];   // this lane's column per prefetched tile: activation offset
-};
-
-// Weight and scale rows of a job for this lane.  Up/gate: rows 0..7 are gate
-// rows 8t.., 8..15 up rows I+8t..; down: output rows h0+16rt.. (a row past
-// the live rows repeats the last live one).
-template <int NPRE>
-__device__ inline void fetch_job(const Params& p, const Lds& L, const Sched& s, Fetch<NPRE>& f) {
-  const int lane = threadIdx.x & 63, lg = lane >> 4, row = lane & 15;
-  const It& c = f.it;
-  const bool down = c.phase == 2, sh = shared_group(p, c.g);
-  const int iexp = sh ? uni(p.Is) : uni(p.I), kdim = job_kdim(p, c), nlive = job_nlive(s, c);
-  const int hb = s.h0 + 16 * c.rt;
-  // consecutive jobs of one group (the down tiles of this CU's slice) share
-  // the column lookups
-  if (c.g != f.g) {
-    int ncols, code[NPRE];
-    group_cols<NPRE>(p, L, c.g, ncols, f.eid, code);
-    f.g = c.g;
-    f.abase = down ? arg_ptr(p.mid) : arg_ptr(p.x);
-#pragma unroll
-    for (int ct = 0; ct < NPRE; ++ct) f.act[ct] = act_offset(p, down ? 2 : 1, code[ct], lg);
-  }
-  const int eid = f.eid;
-  f.fmt = sh ? 0 : uni(p.routed_fmt);
-  const KRange kr = job_krange(p, s, c);
-  f.n = kr.n;
-  f.k0 = kr.k0;
-  f.step = kr.step;
-  f.i = 0;
-  const int wr = down ? hb + (row < nlive ? row : nlive - 1) : (row < 8 ? 8 * c.tile + row : iexp + 8 * c.tile + row - 8);
-  const size_t H = p.H, I = p.I, e = (size_t)eid;
-  const uint8_t* w;
-  const uint8_t* sc;
-  if (f.fmt == 0) {
-    // FP8 weights [rows][kdim] bytes; fp32 scales [rows/128][kdim/128]
-    const float* S;
-    if (sh) {
-      w = down ? arg_ptr(p.sh_wd) : arg_ptr(p.sh_wgu);
-      S = down ? arg_ptr(p.sh_sd) : arg_ptr(p.sh_sgu);
-    } else {
-      w = down ? arg_ptr(p.wd) + e * H * I : arg_ptr(p.wgu) + e * 2 * I * H;
-      S = down ? (const float*)arg_ptr(p.sd) + e * (H / 128) * (I / 128)
-               : (const float*)arg_ptr(p.sgu) + e * (2 * I / 128) * (H / 128);
-    }
-    const int nkb = kdim / 128;
-    const int nb_lo = down ? hb / 128 : (8 * c.tile) / 128;
-    const int nb_hi = down ? (hb + nlive - 1) / 128 : (iexp + 8 * c.tile) / 128;
-    f.wrow = w + (size_t)wr * kdim;
-    sc = (const uint8_t*)(S + (size_t)(lane < 32 ? nb_lo : nb_hi) * nkb);
-  } else {
-    // MXFP4 weights [rows][kdim/2] bytes; E8M0 scales [rows][kdim/32]
-    w = down ? arg_ptr(p.wd) + e * H * (I / 2) : arg_ptr(p.wgu) + e * 2 * I * (H / 2);
-    const uint8_t* S = down ? (const uint8_t*)arg_ptr(p.sd) + e * H * (I / 32)
-                            : (const uint8_t*)arg_ptr(p.sgu) + e * 2 * I * (H / 32);
-    f.wrow = w + (size_t)wr * (kdim / 2);
-    sc = S + (size_t)wr * (kdim / 32);
-  }
-  f.srow = sc;
-}
-
-// Issues the loads of the fetch side's next item into `it`: always
-// 3 + 4*NPRE loads; a dead item (past the phase) loads from x instead.
-template <int NPRE>
-__device__ __forceinline__ void fetch_item(const Params& p, const Fetch<NPRE>& f, Item<NPRE>& it) {
-  const int lane = threadIdx.x & 63, lg = lane >> 4;
-  const int kb = f.live ? f.k0 + f.step * f.i : 0;
-  const int kbytes = f.fmt ? 64 : 128, lbytes = f.fmt ? 16 : 32;
-  const uint8_t* wp = f.live ? f.wrow + kb * kbytes + lg * lbytes : (const uint8_t*)p.x;
-  const uint8_t* sp = f.live ? f.srow + 4 * kb : (const uint8_t*)p.x;
-  const uint16_t* ab = f.live ? f.abase : arg_ptr(p.x);
-  it.w0 = ld16(wp);
-  it.w1 = ld16(wp + (f.fmt ? 0 : 16));
-  it.s = ldg<uint32_t>(sp);
-#pragma unroll
-  for (int ct = 0; ct < NPRE; ++ct) {
-    const uint16_t* a = ab + (f.live ? f.act[ct] + kb * 128 : 0);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) it.B[4 * ct + m] = ld16(a + 8 * m);
-  }
-}
-
-// Moves the fetch side one item on, over jobs this wave has no items in,
-// and stops (dead items) at phase `stop`.
-template <int NPRE>
-__device__ inline void fetch_next(const Params& p, const Lds& L, const Sched& s, Fetch<NPRE>& f, int stop) {
-  f.live = uni(f.live);
-  if (!f.live) return;
-  f.i = uni(f.i) + 1;
-  f.n = uni(f.n);
-  while (f.i >= f.n) {
-    next_job(p, s, f.it);
-    uni(f.it);
-    if (f.it.phase >= stop) {
-      f.live = 0;
-      return;
-    }
-    fetch_job(p, L, s, f);
-  }
-}
-
-template <int NPRE>
-__device__ inline void fetch_start(const Params& p, const Lds& L, const Sched& s, Fetch<NPRE>& f, It start, int stop) {
-  f.it = start;
-  f.live = start.phase < stop;
-  f.fmt = 0;
-  f.g = -1;
-  f.eid = 0;
-  if (!f.live) return;
-  fetch_job(p, L, s, f);
-  while (f.n == 0) {
-    next_job(p, s, f.it);
-    if (f.it.phase >= stop) {
-      f.live = 0;
-      return;
-    }
-    fetch_job(p, L, s, f);
-  }
-}
-
-// The multiplying side's view of its current job.
-template <int NPRE>
-struct Eat {
-  It it;
-  int i, n;
-  int kind;     // 1 up/gate, 2 down
-  int g;        // group of the job
-  int fmt, tile, rt, ncols, nct, nlive;
-  int split;    // FP8: MFMA output rows (4*lg + q) below it take the first block scale
-  int k0, step; // K-blocks of the items
-  const uint16_t* abase;
-  uint32_t act[max_tiles<NPRE>()];  // this lane's column per tile (tiles >= NPRE are loaded when used)
-};
-
-template <int NPRE>
-__device__ inline void eat_job(const Params& p, const Lds& L, const Sched& s, Eat<NPRE>& e) {
-  const int lg = (threadIdx.x & 63) >> 4;
-  const It& c = e.it;
-  e.kind = c.phase <= 1 ? 1 : 2;
-  e.fmt = shared_group(p, c.g) ? 0 : uni(p.routed_fmt);
-  e.tile = c.phase <= 1 ? c.tile : 0;
-  e.rt = c.phase == 2 ? c.rt : 0;
-  e.nlive = job_nlive(s, c);
-  const KRange kr = job_krange(p, s, c);
-  e.n = kr.n;
-  e.k0 = kr.k0;
-  e.step = kr.step;
-  e.i = 0;
-  if (e.kind == 1) {
-    e.split = 8;  // rows 0..7 of the MFMA tile are gate rows, 8..15 up rows
-  } else {
-    // a 16-row down tile spans at most two 128-row scale blocks
-    const int hb = s.h0 + 16 * e.rt;
-    e.split = (hb / 128 + 1) * 128 - hb;
-  }
-  // consecutive jobs of one group (the down tiles of this CU's slice, within
-  // one phase) have the same columns
-  if (c.g == e.g) return;
-  e.g = c.g;
-  int eid, code[max_tiles<NPRE>()];
-  group_cols<max_tiles<NPRE>()>(p, L, c.g, e.ncols, eid, code);
-  e.nct = (e.ncols + 15) >> 4;
-  e.abase = e.kind == 1 ? arg_ptr(p.x) : arg_ptr(p.mid);
-#pragma unroll
-  for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) e.act[ct] = act_offset(p, e.kind, code[ct], lg);
-}
-
-// Multiplies one item into acc[ct].  FP8: a 4-MFMA block sum, then times the
-// 128x128 block scale of the output row; MXFP4: the E8M0 scale is folded
-// into the exact bf16 conversion.
-template <int F, int NPRE>
-__device__ inline void eat_item(const Eat<NPRE>& e, const Item<NPRE>& it, f32x4* acc) {
-  const int lg = (threadIdx.x & 63) >> 4;
-  const int kb = e.k0 + e.step * e.i;
-  bf16x8 A[4];
-  float s_lo = 1.f, s_hi = 1.f;
-  if (F == 0) {
-    A[0] = e4m3x8_to_bf16(it.w0[0], it.w0[1]);
-    A[1] = e4m3x8_to_bf16(it.w0[2], it.w0[3]);
-    A[2] = e4m3x8_to_bf16(it.w1[0], it.w1[1]);
-    A[3] = e4m3x8_to_bf16(it.w1[2], it.w1[3]);
-    s_lo = __int_as_float(__builtin_amdgcn_readlane((int)it.s, 0));
-    s_hi = __int_as_float(__builtin_amdgcn_readlane((int)it.s, 32));
-  } else {
-    const float sc = e8m0_to_f32((it.s >> (8 * lg)) & 0xffu);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) A[m] = e2m1x8_to_bf16(it.w0[m], sc);
-  }
-#pragma unroll
-  for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) {
-    if (ct < e.nct) {
-      u32x4 Bl[4];
-      const u32x4* B = it.B + 4 * (ct < NPRE ? ct : 0);
-      if (ct >= NPRE) {
-        const uint16_t* a = e.abase + e.act[ct] + kb * 128;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) Bl[m] = ld16(a + 8 * m);
-        B = Bl;
-      }
-      if (F == 0) {
-        f32x4 t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) t = mfma16(A[m], __builtin_bit_cast(bf16x8, B[m]), t);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[ct][q] = fmaf(t[q], 4 * lg + q < e.split ? s_lo : s_hi, acc[ct][q]);
-      } else {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) acc[ct] = mfma16(A[m], __builtin_bit_cast(bf16x8, B[m]), acc[ct]);
-      }
-    }
-  }
-}
-
 // mid = silu(gate) * up in fp32 (one expression for both layouts).
 __device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + expf(-g)) * u; }
-
-// Job-end reductions.  At the end of a job every wave stores its partial
-// tiles into partial slot (job % slots) and raises its part count; it never
-// waits for the others there.  Job j is summed by its owner wave (j mod 8)
-// later: at the owner's next job end, at the up/gate -> down hand-over, or
-// while the owner waits for a slot.  The sum runs over the waves in order
-// 0..7, exactly as a workgroup-wide reduction would.  A slot is reused for
-// job j only after job j - slots was summed out of it.
-struct Owned {
-  int jc;       // the job's index in this CU's sequence, -1 when none
-  int kind, g, tile, rt, ncols, nct, nlive;
-};
-
-// Eight waves' partial f32x4 of one lane, 1 KB apart, in one round trip.
-__device__ __forceinline__ void lds_ld_wave_partials(const float* t, u32x4 (&v)[8]) {
-  asm volatile(
-      "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:1024\n\t"
-      "ds_read_b128 %2, %8 offset:2048\n\tds_read_b128 %3, %8 offset:3072\n\t"
-      "ds_read_b128 %4, %8 offset:4096\n\tds_read_b128 %5, %8 offset:5120\n\t"
-      "ds_read_b128 %6, %8 offset:6144\n\tds_read_b128 %7, %8 offset:7168\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
-      : "v"(lds_off(t))
-      : "memory");
-}
-
-__device__ __forceinline__ const float* red_slot(const Lds& L, int T, int jc) {
-  return L.red + (size_t)(jc % red_slots(T)) * red_tiles(T) * (kRedTileBytes / 4);
-}
-
-// Sums the owned job out of its slot.  Lane l holds MFMA rows 4*(l>>4)+q of
-// column (l & 15) in every wave's partial.  Up/gate: rows 0..7 are gate
-// rows, 8..15 (32 lanes on) the matching up rows; lanes 0..31 each finish
-// four intermediates, mid = silu(gate) * up rounded to bf16.  Down: every
-// lane finishes its four rows into the LDS products.
-template <int NPRE>
-__device__ inline void sum_job(const Params& p, const Lds& L, const Owned& o) {
-  const int lane = threadIdx.x & 63;
-  const float* base = red_slot(L, p.T, o.jc);
-#pragma unroll
-  for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) {
-    if (ct < o.nct) {
-      const float* t = base + (size_t)ct * (kRedTileBytes / 4);
-      const int col = ct * 16 + (lane & 15);
-      const int code = col_code(p, L, o.g, col < o.ncols ? col : o.ncols - 1);
-      if (o.kind == 1) {
-        if (lane < 32) {
-          u32x4 v[8];
-          float gs[4], us[4];
-          lds_ld_wave_partials(t + (size_t)lane * 4, v);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            gs[q] = 0.f;
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) gs[q] += __uint_as_float(v[w][q]);
-          }
-          lds_ld_wave_partials(t + (size_t)(lane + 32) * 4, v);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            us[q] = 0.f;
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) us[q] += __uint_as_float(v[w][q]);
-          }
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float g = gs[q], u = us[q];
-            if (col < o.ncols) {
-              const float m = swiglu(g, u);
-              if (!isfinite(m)) set_err(p.err, kErrMid);
-              const int i = 4 * (lane >> 4) + q;
-              p.mid[((size_t)(code >> 4) * (p.K + 1) + (code & 15)) * p.mid_ld + 8 * o.tile + i] =
-                  (uint16_t)f32_to_bf16_rne(m);
-            }
-          }
-        }
-      } else {
-        u32x4 pv[8];
-        lds_ld_wave_partials(t + (size_t)lane * 4, pv);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float v = 0.f;
-#pragma unroll
-          for (int w = 0; w < kWaves; ++w) v += __uint_as_float(pv[w][q]);
-          const int i = 4 * (lane >> 4) + q;
-          if (i < o.nlive && col < o.ncols) {
-            if (!isfinite(v)) set_err(p.err, kErrMid);
-            lds_st32(L.pbuf + ((size_t)(code >> 4) * (p.K + 1) + (code & 15)) * p.hs + 16 * o.rt + i,
-                     __float_as_uint(v));
-          }
-        }
-      }
-    }
-  }
-}
-
-// Sums the owned job when every wave's partials are in (or waits for them
-// when `block`), then releases its slot.
-template <int NPRE>
-__device__ inline void service(const Params& p, const Lds& L, Owned& o, bool block, bool& ok) {
-  o.jc = uni(o.jc);
-  if (o.jc < 0) return;
-  if (block) lds_wait<8>(p, L.ctl + kCtlPart, (uint32_t)(o.jc + 1), ok);
-  else if (ok && (int)lds_min<8>(L.ctl + kCtlPart) < o.jc + 1) return;
-  sum_job<NPRE>(p, L, o);
-  lds_st32(L.ctl + kCtlSlot + o.jc % red_slots(p.T), (uint32_t)(o.jc + 1));
-  o.jc = -1;
-}
-
-// End of job jc for this wave: wait for its slot (summing an owned job
-// meanwhile), store the partial tiles, raise the part count, sum an older
-// owned job if its partials are all in, and take ownership of jc when it is
-// this wave's.
-template <int NPRE>
-__device__ inline void job_end(const Params& p, const Lds& L, const Eat<NPRE>& e, f32x4* acc, int jc, Owned& own,
-                               bool& ok) {
-  const int lane = threadIdx.x & 63, wave = wave_id();
-  const int ns = red_slots(p.T);
-  if (jc >= ns) {
-    const uint32_t target = (uint32_t)(jc - ns + 1);
-    const uint32_t* sd = L.ctl + kCtlSlot + jc % ns;
-    int spins = 0;
-    while (ok && lds_min<1>(sd) < target) {
-      service<NPRE>(p, L, own, false, ok);
-      if (++spins > kSpinLimit) {
-        set_err(p.err, kErrTimeout);
-        ok = false;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-  }
-  float* base = (float*)red_slot(L, p.T, jc);
-#pragma unroll
-  for (int ct = 0; ct < max_tiles<NPRE>(); ++ct)
-    if (ct < e.nct)
-      lds_st128(base + (size_t)ct * (kRedTileBytes / 4) + ((size_t)wave * 64 + lane) * 4,
-                __builtin_bit_cast(u32x4, acc[ct]));
-  lds_st32(L.ctl + kCtlPart + wave, (uint32_t)(jc + 1));
-  service<NPRE>(p, L, own, false, ok);
-  if (jc % kWaves == wave) {
-    service<NPRE>(p, L, own, true, ok);  // the previous owned job, 8 jobs back
-    own.jc = jc;
-    own.kind = e.kind;
-    own.g = e.it.g;
-    own.tile = e.tile;
-    own.rt = e.rt;
-    own.ncols = e.ncols;
-    own.nct = e.nct;
-    own.nlive = e.nlive;
-  }
-#pragma unroll
-  for (int ct = 0; ct < max_tiles<NPRE>(); ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-}
 
 // The two waves of a SIMD (w and w ^ 4) have the same work, but the issue
 // arbiter favours the older one, which would then finish its phase early and
@@ -1737,78 +1190,6 @@ __device__ __forceinline__ void balance(const Lds& L, int jc) {
   const int other = (int)lds_min<1>(L.ctl + kCtlProg + (wave ^ 4));
   if (jc > other) __builtin_amdgcn_s_setprio(0);
   else __builtin_amdgcn_s_setprio(2);
-}
-
-// Moves the multiplying side on after an item; at the end of a job (and for
-// every following job this wave has no items in) runs the job end.  Returns
-// false once the phase is done.
-template <int NPRE>
-__device__ inline bool eat_next(const Params& p, const Lds& L, const Sched& s, Eat<NPRE>& e, f32x4* acc, int& jc,
-                                Owned& own, bool& ok, int stop) {
-  e.i = uni(e.i) + 1;
-  e.n = uni(e.n);
-  while (e.i >= e.n) {
-    job_end<NPRE>(p, L, e, acc, jc++, own, ok);
-    MOE_JSTAMP(p, jc - 1);
-    balance(L, jc);
-    next_job(p, s, e.it);
-    uni(e.it);
-    if (e.it.phase >= stop) return false;
-    eat_job(p, L, s, e);
-  }
-  return true;
-}
-
-// One phase (up/gate, or down) of the stream: a D-deep register pipeline.
-// Each step multiplies item n out of ring slot n % D and refills that slot
-// with item n + D.
-template <int NPRE, int FMT>
-__device__ __forceinline__ void run_phase(const Params& p, const Lds& L, const Sched& s, It start, int stop, f32x4* acc,
-                                 int& jc, Owned& own, bool& ok) {
-  constexpr int D = depth<NPRE>();
-  if (start.phase >= stop) return;
-  Fetch<NPRE> f;
-  fetch_start(p, L, s, f, start, stop);
-  Item<NPRE> ring[D];
-#pragma unroll
-  for (int d = 0; d < D; ++d) {
-    fetch_item(p, f, ring[d]);
-    fetch_next(p, L, s, f, stop);
-  }
-  Eat<NPRE> e;
-  e.it = start;
-  e.g = -1;
-  eat_job(p, L, s, e);
-  // jobs this wave has no items in still end (with zero partials)
-  bool more = true;
-  while (e.n == 0 && more) {
-    job_end<NPRE>(p, L, e, acc, jc++, own, ok);
-    next_job(p, s, e.it);
-    if (e.it.phase >= stop) more = false;
-    else eat_job(p, L, s, e);
-  }
-  // The loop is left only after a whole round of D slots (the rest of the
-  // round refills with dead loads), so every path to an item's wait has
-  // issued the same D-1 items since; an exit in mid-round would make the
-  // compiler's wait counting assume fewer and drain the ring.
-  bool done = !more;
-  if (!done) {
-    for (;;) {
-#pragma unroll
-      for (int d = 0; d < D; ++d) {
-        if (!done) {
-          if (e.fmt == 0) eat_item<0>(e, ring[d], acc);
-          else eat_item<FMT>(e, ring[d], acc);
-        }
-        fetch_item(p, f, ring[d]);
-        fetch_next(p, L, s, f, stop);
-        if (!done) done = !eat_next(p, L, s, e, acc, jc, own, ok, stop);
-      }
-      if (done) break;
-    }
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the dead items' loads
-  __builtin_amdgcn_s_setprio(0);
 }
 
 // ------------------------------------------------------------------ narrow stream
@@ -1903,9 +1284,9 @@ __device__ inline JobDesc make_desc(const Params& p, bool up, bool sh, int e, in
   return d;
 }
 
-// Up/gate job j of the step: the shared tiles, then rt_tiles tiles per
-// routed group.  Sets its group and tile.
-__device__ __forceinline__ void up_job(const Params& p, const Sched& s, int j, int& g, int& tile) {
+// Up/gate (group, 8-intermediate tile) pair j of the step: the shared tiles,
+// then rt_tiles tiles per routed group.  Sets its group and tile.
+__device__ __forceinline__ void up_pair(const Params& p, const Sched& s, int j, int& g, int& tile) {
   if (j < s.sh_tiles) {
     g = 0;
     tile = j;
@@ -1915,28 +1296,36 @@ __device__ __forceinline__ void up_job(const Params& p, const Sched& s, int j, i
   }
 }
 
-// Up/gate jobs of a narrow call: CU c takes jobs c + q*ncu (local job q),
-// as in the wide stream.  Inside the CU a job is cut into chunks, one per
-// K-phase w (K-blocks w + 8i, the blocks wave w takes in the wide stream),
-// and the waves claim chunks in order from an LDS counter.  A chunk's
-// partial is the same sum whichever wave forms it, so the job's sum over its
-// K-phases in order does not depend on which wave did what, and waves that
-// stream faster take more chunks.
+// Column tiles of a group of c columns: jobs of at most cpj columns each.
+__device__ __forceinline__ int n_ctiles(const Params& p, int c) { return (c + p.cpj - 1) / p.cpj; }
 
+// Up/gate jobs of a call: CU c takes the (group, tile) pairs c + q*ncu in
+// order, and a pair is one job per column tile of its group (its weight rows
+// are streamed once per column tile, back to back, the repeats mostly from
+// the caches).  Inside the CU a job is cut into chunks, one per K-phase w
+// (K-blocks w + 8i), and the waves claim chunks in order from an LDS
+// counter.  A chunk's partial is the same sum whichever wave forms it, so
+// the job's sum over its K-phases in order does not depend on which wave did
+// what, and waves that stream faster take more chunks.
 
-// The narrow stream's state and the tables of this CU's shared-expert jobs
-// (local jobs 0..nS-1; they need no routing).  Whole workgroup, plain
-// per-thread LDS accesses; the caller synchronises.
-// This CU's shared-expert up/gate jobs (dealt c, c + ncu, ...).
-__device__ __forceinline__ int shared_jobs_here(const Params& p) {
+// This CU's shared-expert pairs (dealt c, c + ncu, ...) and their jobs.
+__device__ __forceinline__ int shared_pairs_here(const Params& p) {
   const int sh_tiles = p.n_shared ? p.Is / 8 : 0;
   return (int)blockIdx.x < sh_tiles ? (sh_tiles - 1 - (int)blockIdx.x) / p.ncu + 1 : 0;
 }
+__device__ __forceinline__ int shared_jobs_here(const Params& p) { return shared_pairs_here(p) * n_ctiles(p, p.T); }
 
+// The stream's state and the tables of this CU's shared-expert jobs (local
+// jobs 0..nS-1; they need no routing).  Whole workgroup, plain per-thread
+// LDS accesses; the caller synchronises.
 __device__ inline void stream_init(const Params& p, const Lds& L, int nS) {
   const int tid = threadIdx.x;
-  for (int k = tid; k < nS; k += kThreads)
-    L.jd[k] = make_desc(p, true, true, 0, (int)blockIdx.x + k * p.ncu, p.T, 0);
+  const int nct = n_ctiles(p, p.T);
+  for (int k = tid; k < nS; k += kThreads) {
+    const int q = k / nct, ct = k - q * nct;
+    const int nc = p.T - ct * p.cpj < p.cpj ? p.T - ct * p.cpj : p.cpj;
+    L.jd[k] = make_desc(p, true, true, 0, (int)blockIdx.x + q * p.ncu, nc, ct * p.cpj);
+  }
   if (p.n_shared && tid < p.T) {
     L.cols[tid] = tid * 16 + p.K;
     L.cgrp[tid] = 0;
@@ -1946,41 +1335,83 @@ __device__ inline void stream_init(const Params& p, const Lds& L, int nS) {
     L.wgen[tid] = 0u;
   }
   if (tid == 0) {
-    *L.ccnt = 0u;
+    L.ccnt[0] = 0u;
+    L.ccnt[1] = 0u;
     L.misc[kMiscReady] = 0;
     L.misc[kMiscRouted] = 0;
     L.misc[kMiscPolled] = 0;
   }
 }
 
-// The tables that need the routing: the routed up/gate jobs (local jobs
-// nS..nU-1) and one down job per group at qcap + g, written by threads
-// first, first + stride, ...; then nU.
-// PART: 1 the up/gate jobs and nU, 2 the down jobs, 3 both.
-template <int PART = 3>
-__device__ inline void routed_tables(const Params& p, const Lds& L, const Sched& s, int nS, int nU, int first,
-                                     int stride) {
-  if (PART & 1) {
-    for (int k = nS + first; k < nU; k += stride) {
-      int g, tile;
-      up_job(p, s, (int)blockIdx.x + k * p.ncu, g, tile);
-      const bool sh = shared_group(p, g);
-      L.jd[k] = make_desc(p, true, sh, sh ? 0 : L.gexp[g], tile, sh ? p.T : L.gcnt[g], sh ? 0 : L.gstart[g]);
-    }
+// Exclusive offsets of per-lane counts n over the wave, added to `base`
+// (which moves on by the wave's total).
+__device__ __forceinline__ int wave_offset(int n, int& base) {
+  const int lane = threadIdx.x & 63;
+  int v = n;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
   }
-  if (PART & 2) {
-    for (int g = first; g < s.G; g += stride) {
-      const bool sh = shared_group(p, g);
-      L.jd[p.qcap + g] = make_desc(p, false, sh, sh ? 0 : L.gexp[g], 0, sh ? p.T : L.gcnt[g], sh ? 0 : L.gstart[g]);
-    }
-  }
-  if ((PART & 1) && first == 0) L.misc[kMiscNU] = nU;
+  const int o = base + v - n;
+  base += __shfl(v, 63, 64);
+  return o;
 }
 
-// Per-wave constants of a phase (KIND 1 up/gate, 2 down).  Up/gate: every
-// wave takes K-blocks w + 8i of each job, rows 0..7 of a tile are gate rows
-// and 8..15 up rows.  Down: wave w takes tile rt = w % nrt_p of the CU's
-// slice, rows hb.. (nlive live), and K-blocks w / nrt_p + wpt*i.
+// The tables that need the routing, written by one wave:
+//   PART 1: the routed up/gate jobs (local jobs nS.., this CU's routed pairs
+//           in order, each pair's column tiles in order), then nU;
+//   PART 2: the down jobs at qcap + i (each group's column tiles, groups in
+//           order), then nD.
+template <int PART>
+__device__ inline void routed_tables(const Params& p, const Lds& L, const Sched& s, int nS) {
+  const int lane = threadIdx.x & 63;
+  if (PART & 1) {
+    // this CU's first routed pair: the smallest j >= sh_tiles with
+    // j = blockIdx.x (mod ncu)
+    const int r = s.sh_tiles % p.ncu;
+    const int first = s.sh_tiles + (((int)blockIdx.x - r) % p.ncu + p.ncu) % p.ncu;
+    int base = nS;
+    for (int j0 = first; j0 < s.n_pairs; j0 += 64 * p.ncu) {
+      const int j = j0 + lane * p.ncu;
+      int g = 0, tile = 0, c = 0, nct = 0;
+      if (j < s.n_pairs) {
+        up_pair(p, s, j, g, tile);
+        c = L.gcnt[g];
+        nct = n_ctiles(p, c);
+      }
+      const int off = wave_offset(nct, base);
+      for (int ct = 0; ct < nct; ++ct) {
+        const int nc = c - ct * p.cpj < p.cpj ? c - ct * p.cpj : p.cpj;
+        L.jd[off + ct] = make_desc(p, true, false, L.gexp[g], tile, nc, L.gstart[g] + ct * p.cpj);
+      }
+    }
+    if (lane == 0) L.misc[kMiscNU] = base;
+  }
+  if (PART & 2) {
+    int base = 0;
+    for (int g0 = 0; g0 < s.G; g0 += 64) {
+      const int g = g0 + lane;
+      const bool sh = shared_group(p, g);
+      const int c = g < s.G ? (sh ? p.T : L.gcnt[g]) : 0;
+      const int nct = n_ctiles(p, c);
+      const int off = wave_offset(nct, base);
+      for (int ct = 0; ct < nct; ++ct) {
+        const int nc = c - ct * p.cpj < p.cpj ? c - ct * p.cpj : p.cpj;
+        L.jd[p.qcap + off + ct] =
+            make_desc(p, false, sh, sh ? 0 : L.gexp[g], 0, nc, (sh ? 0 : L.gstart[g]) + ct * p.cpj);
+      }
+    }
+    if (lane == 0) L.misc[kMiscND] = base;
+  }
+}
+
+// Per-wave constants of a phase (KIND 1 up/gate, 2 down split by K-phase,
+// 3 down by claimed whole jobs).  Up/gate: every wave takes K-blocks w + 8i
+// of each job, rows 0..7 of a tile are gate rows and 8..15 up rows.  Down
+// (KIND 2): wave w takes tile rt = w % nrt_p of the CU's slice, rows hb..
+// (nlive live), and K-blocks w / nrt_p + wpt*i.  KIND 3: a claimed job's
+// tile and all its K-blocks (the constants are set per job).
 struct PhaseN {
   int k0, lstep;  // this wave's K-blocks: k0 + (i << lstep)
   int hb, nlive;  // down: first row of this wave's tile and its live rows
@@ -1988,6 +1419,7 @@ struct PhaseN {
   int dnb;        // FP8 down: block rows between the tile's first and last live row (0 or 1)
   int rt;         // down: this wave's tile
   int nw;         // up/gate: waves with items (min(K-blocks, 8))
+  int h0, hc, nrt;  // KIND 3: this CU's slice and its 16-row tiles
 };
 template <int KIND>
 __device__ __forceinline__ int ph_k0(const PhaseN& ph) { return KIND == 1 ? wave_id() : ph.k0; }
@@ -1995,6 +1427,24 @@ template <int KIND>
 __device__ __forceinline__ int ph_lstep(const PhaseN& ph) { return KIND == 1 ? 3 : ph.lstep; }
 template <int KIND>
 __device__ __forceinline__ int ph_split(const PhaseN& ph) { return KIND == 1 ? 8 : ph.split; }
+
+// The down constants of tile rt of the slice [h0, h0 + hc), K-blocks
+// k0 + (i << lstep).
+__device__ __forceinline__ PhaseN down_phase(int h0, int hc, int nrt, int rt, int k0, int lstep) {
+  PhaseN ph;
+  ph.rt = rt;
+  ph.k0 = k0;
+  ph.lstep = lstep;
+  ph.hb = h0 + 16 * rt;
+  ph.nlive = hc - 16 * rt < 16 ? hc - 16 * rt : 16;
+  ph.split = (ph.hb / 128 + 1) * 128 - ph.hb;  // a 16-row tile spans at most two scale block rows
+  ph.dnb = ph.nlive > 0 ? ((ph.hb + ph.nlive - 1) >> 7) - (ph.hb >> 7) : 0;
+  ph.nw = 0;
+  ph.h0 = h0;
+  ph.hc = hc;
+  ph.nrt = nrt;
+  return ph;
+}
 
 template <int KIND>
 __device__ __forceinline__ int job_items(const PhaseN& ph, int nkb) {
@@ -2004,7 +1454,8 @@ __device__ __forceinline__ int job_items(const PhaseN& ph, int nkb) {
 
 // The fetch side: byte offsets of this lane's next item from uniform bases.
 struct FetchN {
-  int k;                         // next job to set up (down)
+  int k;                         // next job to set up (down); KIND 3: the claimed unit, -1 before the first
+  int kp, nkb;                   // KIND 3: the unit's K-phase being fetched, and its K-blocks
   int nch;                       // up/gate: chunks claimed by this wave
   int nu;                        // up/gate: the CU's job count once the routed tables are in (else -1)
   int cnt;                       // items fetched so far
@@ -2139,12 +1590,56 @@ __device__ inline void fetch_next_up(const Params& p, const Lds& L, const PhaseN
   fetch_dead(p, f);
 }
 
-// kend: up/gate, the CU's shared-expert job count; down, the end of its
-// job range.
+// Items of K-phase kp of a down job of nkb K-blocks split into 1 << lkph
+// phases (K-blocks kp + (i << lkph)).
+__device__ __forceinline__ int phase_items(int nkb, int kp, int lkph) {
+  return nkb > kp ? ((nkb - 1 - kp) >> lkph) + 1 : 0;
+}
+
+// Claimed down (KIND 3): moves the fetch side to the next K-phase with
+// items of the wave's unit, or claims this CU's next down unit u (down entry
+// u / nrt, 16-row tile u mod nrt of the slice) and hands u on to the
+// multiplying side; past the end once u reaches nunits.  A unit's K-blocks
+// are fetched phase by phase (kp + kph*i for kp = 0, 1, ..), the order in
+// which its sum is formed (see dc_phase_end).
+template <int FMT, int AL>
+__device__ inline void fetch_next_dc(const Params& p, const Lds& L, const PhaseN& ph, FetchN& f, int nunits) {
+  const int kph = 1 << ph.lstep;
+  for (;;) {
+    if (f.k >= 0) {
+      for (int kp = f.kp + 1; kp < kph; ++kp) {
+        const int n = phase_items(f.nkb, kp, ph.lstep);
+        if (n > 0) {
+          f.kp = kp;
+          const int ent = f.k / ph.nrt, rt = f.k - ent * ph.nrt;
+          const JobDesc d = read_desc(L, p.qcap + ent);
+          const PhaseN q = down_phase(ph.h0, ph.hc, ph.nrt, rt, kp, ph.lstep);
+          fetch_from_desc<FMT, 2, AL>(p, q, f, d, kp, n, lane_code<AL>(L, d));
+          return;
+        }
+      }
+    }
+    const uint32_t u = lds_inc_lane0(L.ccnt + 1);
+    if ((int)u >= nunits) {
+      f.k = -1;
+      fetch_dead(p, f);
+      return;
+    }
+    lds_st32(L.cfifo + wave_id() * 8 + (f.nch & 7), u);
+    f.nch = f.nch + 1;
+    f.k = (int)u;
+    f.kp = -1;
+    f.nkb = read_desc(L, p.qcap + (int)u / ph.nrt).nkb;
+  }
+}
+
+// kend: up/gate, the CU's shared-expert job count; down (KIND 2), the end of
+// its job range; KIND 3, its unit count.
 template <int FMT, int KIND, int AL>
 __device__ __forceinline__ void fetch_next_any(const Params& p, const Lds& L, const PhaseN& ph, FetchN& f, int kend,
                                                bool& ok) {
   if (KIND == 1) fetch_next_up<FMT, AL>(p, L, ph, f, kend, ok);
+  else if (KIND == 3) fetch_next_dc<FMT, AL>(p, L, ph, f, kend);
   else fetch_next_n<FMT, KIND, AL>(p, L, ph, f, kend);
 }
 
@@ -2188,6 +1683,8 @@ struct EatN {
   int fmt;         // 0 FP8, 1 MXFP4
   uint32_t pidx;   // this lane's partial (floats from L.pbuf); only stored when pst
   bool pst;        // this lane's column is one of the group's
+  int split;       // KIND 3: the job's FP8 scale split (see PhaseN)
+  int kp, nkb;     // KIND 3: the K-phase being multiplied, and the unit's K-blocks
 };
 
 // Down: moves the multiplying side to its next job of [e.k, kend) with
@@ -2228,9 +1725,63 @@ __device__ inline bool eat_next_up(const Params& p, const Lds& L, const PhaseN& 
   e.left = ((d.nkb - 1 - kp) >> 3) + 1;
   e.fmt = FMT == 0 ? 0 : d.fmt;
   e.pst = col < d.ncols && (lane & (4 / AL - 1)) == 0;
-  e.pidx = ((((uint32_t)q & (kPuWin - 1)) * kWaves + (uint32_t)kp) * (uint32_t)p.T + (uint32_t)col) * 16u +
+  e.pidx = ((((uint32_t)q & (kPuWin - 1)) * kWaves + (uint32_t)kp) * (uint32_t)p.pcols + (uint32_t)col) * 16u +
            4u * (uint32_t)lg;
   return true;
+}
+
+// Claimed down (KIND 3): moves the multiplying side to the next unit the
+// fetch side has claimed, at its first K-phase; false at the end.  The
+// unit's sum goes to Pd[0][row][slot] at its tile.
+template <int FMT, int AL>
+__device__ inline bool eat_next_dc(const Params& p, const Lds& L, const PhaseN& ph, EatN& e, int fnch) {
+  if (e.nch >= fnch) return false;
+  const int lane = threadIdx.x & 63, lg = lane >> 4, col = lane_col<AL>(lane);
+  const uint32_t u = (uint32_t)lds_ldi_uniform((const int32_t*)L.cfifo + wave_id() * 8 + (e.nch & 7));
+  e.nch = e.nch + 1;
+  const int ent = (int)u / ph.nrt, rt = (int)u - ent * ph.nrt;
+  const JobDesc d = read_desc(L, p.qcap + ent);
+  e.nkb = d.nkb;
+  e.kp = 0;
+  e.left = phase_items(d.nkb, 0, ph.lstep);
+  e.fmt = FMT == 0 ? 0 : d.fmt;
+  e.pst = col < d.ncols && (lane & (4 / AL - 1)) == 0;
+  const int code = lane_code<AL>(L, d);
+  e.pidx = lmul(lmul((uint32_t)(code >> 4), (uint32_t)(p.K + 1)) + (uint32_t)(code & 15), (uint32_t)p.pitch) +
+           16u * (uint32_t)rt + 4u * (uint32_t)lg;
+  e.split = down_phase(ph.h0, ph.hc, ph.nrt, rt, 0, 0).split;
+  return true;
+}
+
+// Claimed down: the end of a K-phase's items.  The phase's partial (an FMA
+// chain over its K-blocks, as one wave forms it when the phases are split
+// over waves) is added to the unit's sum, which starts at +0 and takes the
+// phases in order, a phase without items adding +0: the sum a split down
+// job's products get in the combine.  Moves to the next phase with items,
+// or at the unit's end stores the sum (unit_end) and starts the next unit;
+// false once no unit is left.
+template <int FMT, int AL>
+__device__ inline bool dc_phase_end(const Params& p, const Lds& L, const PhaseN& ph, EatN& e, f32x4& acc, f32x4& tot,
+                                    int fnch, bool& unit_end) {
+  const int kph = 1 << ph.lstep;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) tot[q] += acc[q];
+  acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  unit_end = false;
+  for (int kp = e.kp + 1; kp < kph; ++kp) {
+    const int n = phase_items(e.nkb, kp, ph.lstep);
+    if (n > 0) {
+      e.kp = kp;
+      e.left = n;
+      return true;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tot[q] += 0.f;
+  }
+  unit_end = true;
+  if (e.pst) lds_st128(L.pbuf + e.pidx, __builtin_bit_cast(u32x4, tot));
+  tot = f32x4{0.f, 0.f, 0.f, 0.f};
+  return eat_next_dc<FMT, AL>(p, L, ph, e, fnch);
 }
 
 // Up/gate job q is complete in partial window win (waves 0..nw-1 stored):
@@ -2241,8 +1792,8 @@ __device__ inline void up_reduce_job(const Params& p, const Lds& L, int q, int w
   const JobDesc d = read_desc(L, q);
   const int lane = threadIdx.x & 63, col = lane >> 2, i2 = 2 * (lane & 3);
   if (col < d.ncols) {
-    const size_t wstride = (size_t)p.T * 16;
-    const float* pu = L.pbuf + ((size_t)win * kWaves * p.T + col) * 16 + i2;
+    const size_t wstride = (size_t)p.pcols * 16;
+    const float* pu = L.pbuf + ((size_t)win * kWaves * p.pcols + col) * 16 + i2;
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f;
 #pragma unroll
@@ -2395,12 +1946,14 @@ __device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const Ph
   EatN e;
   e.k = k;
   e.nch = 0;
-  const bool any =
-      KIND == 1 ? eat_next_up<FMT, AL>(p, L, ph, e, R.f.nch) : eat_next_n<FMT, KIND, AL>(p, L, ph, e, kend);
+  const bool any = KIND == 1   ? eat_next_up<FMT, AL>(p, L, ph, e, R.f.nch)
+                   : KIND == 3 ? eat_next_dc<FMT, AL>(p, L, ph, e, R.f.nch)
+                               : eat_next_n<FMT, KIND, AL>(p, L, ph, e, kend);
   if (any) {
     const int lg = (threadIdx.x & 63) >> 4;
-    const int split = ph_split<KIND>(ph);
+    const int split_c = KIND == 3 ? 0 : ph_split<KIND>(ph);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 tot = {0.f, 0.f, 0.f, 0.f};  // KIND 3: the unit's sum over its K-phases
     // The loop is left only after a whole round of D slots: once the last
     // job has ended, the rest of the round multiplies dead items and
     // refills with dead loads.  So every path to an item's wait has issued
@@ -2410,6 +1963,7 @@ __device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const Ph
     auto round = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
+        const int split = KIND == 3 ? e.split : split_c;
         if (FMT == 0 || e.fmt == 0) eat_item_n<0, AL>(split, lg, R.r[d], acc);
         else eat_item_n<1, AL>(split, lg, R.r[d], acc);
         fetch_item_n<FMT, AL>(R.f, R.r[d]);
@@ -2417,7 +1971,14 @@ __device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const Ph
         if (R.f.left == 0) fetch_next_any<FMT, KIND, AL>(p, L, ph, R.f, kend, ok);
         if (!done) {
           e.left = uni(e.left) - 1;
-          if (e.left == 0) {
+          if (KIND == 3 && e.left == 0) {
+            bool unit_end;
+            done = !dc_phase_end<FMT, AL>(p, L, ph, e, acc, tot, R.f.nch, unit_end);
+            if (unit_end) {
+              MOE_JSTAMP(p, jc);
+              balance(L, ++jc);
+            }
+          } else if (e.left == 0) {
             if (KIND == 1) up_job_end(p, L, e, acc, ph.nw, ok);
             else if (e.pst) lds_st128(L.pbuf + e.pidx, __builtin_bit_cast(u32x4, acc));
             acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -2448,18 +2009,16 @@ __device__ inline void zero_partials(const Lds& L, size_t n) {
 }
 
 // out[r][h] = P_shared + sum_p w[r][p] * P[r][p], fp32 FMA chain in slot
-// order, rounded to bf16 once.  Narrow: each product is first summed over
-// the K-phases of its tile in order (sum_kphases: the sum a wide job-end
-// reduction forms).
+// order, rounded to bf16 once.  Each product is first summed over the
+// K-phases of its tile in order (sum_kphases).
 __device__ __forceinline__ float down_product(const Params& p, const Lds& L, int r, int slot, int hl) {
-  if (!p.narrow) return L.pbuf[((size_t)r * (p.K + 1) + slot) * p.hs + hl];
   return L.pbuf[((size_t)r * (p.K + 1) + slot) * p.pitch + hl];  // summed by sum_kphases
 }
 
-// Narrow: each (row, slot, h) product is first summed over its K-phases
-// (in order, into the K-phase 0 copy) by one thread per product, so the
-// row's chain below reads one value per slot.  Whole workgroup; ends
-// synchronised.
+// Each (row, slot, h) product is first summed over its K-phases (in order,
+// into the K-phase 0 copy) by one thread per product, so the row's chain
+// below reads one value per slot.  With one K-phase (claimed down jobs) the
+// products are checked only.  Whole workgroup; ends synchronised.
 __device__ inline void sum_kphases(const Params& p, const Lds& L, const Sched& s) {
   const size_t kstride = (size_t)p.T * (p.K + 1) * p.pitch;
   const int n = p.T * (p.K + 1) * s.hc;
@@ -2475,9 +2034,7 @@ __device__ inline void sum_kphases(const Params& p, const Lds& L, const Sched& s
 }
 
 // RES: a residual, when given, is added in fp32 after the chain, then
-// rounded once (the residual add of the unfused layout, folded in).  The
-// wide stream has a kernel of its own for it (kModeForwardRes), so that its
-// residual-free kernel keeps its code.
+// rounded once (the residual add of the unfused layout, folded in).
 template <bool RES>
 __device__ inline void combine(const Params& p, const Lds& L, const Sched& s) {
   for (int t = threadIdx.x; t < p.T * s.hc; t += kThreads) {
@@ -2493,19 +2050,19 @@ __device__ inline void combine(const Params& p, const Lds& L, const Sched& s) {
 
 // ------------------------------------------------------------------ kernel
 
-__device__ __forceinline__ Sched make_sched(const Params& p, int G, int narrow) {
+__device__ __forceinline__ Sched make_sched(const Params& p, int G) {
   Sched s;
   s.sh_tiles = p.n_shared ? p.Is / 8 : 0;
   s.rt_tiles = p.I / 8;
   s.G = G;
-  s.n_jobs = s.sh_tiles + (G - p.n_shared) * s.rt_tiles;
+  s.n_pairs = s.sh_tiles + (G - p.n_shared) * s.rt_tiles;
   s.h0 = blockIdx.x * p.hs;
   s.hc = uni(p.H) - s.h0 < uni(p.hs) ? uni(p.H) - s.h0 : uni(p.hs);
   if (s.hc < 0) s.hc = 0;
   s.nrt = (s.hc + 15) / 16;
   s.nrt_p = uni(p.nrt_p);
   s.wpt = uni(p.wpt);
-  s.narrow = narrow;
+  s.kph = uni(p.kph);
   return s;
 }
 
@@ -2521,14 +2078,15 @@ __device__ __forceinline__ const Params& fresh_args() {
   return *(const Params*)q;
 }
 
-// The narrow forward after the logits: routing and grouping, the up/gate
-// stream (its sums formed at job ends), the second flag barrier, the down
-// stream, the combine.  With at most as many rows as waves, the waves that
-// route no row start on this CU's shared-expert jobs once every row's
-// scores are in, the routing waves but wave 7 as soon as their row is
-// routed, and wave 7 once it has grouped the uses and written the routed
-// tables.
-template <int FMT, int AL>
+// The forward after the logits: routing and grouping, the up/gate stream
+// (its sums formed at job ends), the second flag barrier, the down stream,
+// the combine.  With at most as many rows as waves, the waves that route no
+// row start on this CU's shared-expert jobs once every row's scores are in,
+// the routing waves but wave 7 as soon as their row is routed, and wave 7
+// once it has grouped the uses and written the routed tables.
+// DCLAIM: down jobs claimed whole by the waves (above kKsplitRows rows),
+// else split over the waves by K-phase.
+template <int FMT, int AL, bool DCLAIM>
 __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
   const int wave = wave_id();
   int jn = 0;  // jobs this wave has ended (for balance)
@@ -2563,13 +2121,12 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
         wave_sync();
         MOE_LSTAMP(p, 3);
         const int G = lds_ldi_uniform(L.misc);
-        const Sched s = make_sched(p, G, 1);
-        const int nU = (int)blockIdx.x < s.n_jobs ? (s.n_jobs - 1 - (int)blockIdx.x) / p.ncu + 1 : 0;
-        routed_tables<1>(p, L, s, nS, nU, threadIdx.x & 63, 64);
+        const Sched s = make_sched(p, G);
+        routed_tables<1>(p, L, s, nS);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the up/gate tables, before the flag
         lds_st32(L.misc + kMiscReady, 1u);
         // the down tables are read after the phase barrier
-        routed_tables<2>(p, L, s, nS, nU, threadIdx.x & 63, 64);
+        routed_tables<2>(p, L, s, nS);
         __builtin_amdgcn_s_setprio(0);
         MOE_LSTAMP(p, 11);
       }
@@ -2581,9 +2138,8 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
       build_groups(p, L);
       MOE_STAMP(p, 3);
       const int G = lds_ldi_uniform(L.misc);
-      const Sched s = make_sched(p, G, 1);
-      const int nU = (int)blockIdx.x < s.n_jobs ? (s.n_jobs - 1 - (int)blockIdx.x) / p.ncu + 1 : 0;
-      routed_tables(p, L, s, nS, nU, threadIdx.x, kThreads);
+      const Sched s = make_sched(p, G);
+      if (wave == 0) routed_tables<3>(p, L, s, nS);
       if (threadIdx.x == 0) L.misc[kMiscReady] = 1;
       __syncthreads();
       MOE_STAMP(p, 11);
@@ -2604,37 +2160,44 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
     publish(p, epoch + 2);
     MOE_STAMP(p, 12);
     G = lds_ldi_uniform(L.misc);
-    const Sched s = make_sched(p, G, 1);
+    const int nD = lds_ldi_uniform(L.misc + kMiscND);
+    const Sched s = make_sched(p, G);
     zero_partials(L, (size_t)p.wpt * p.T * (p.K + 1) * p.pitch);
-    // down: wave w takes tile w % nrt_p of this CU's slice and K-blocks
-    // w / nrt_p + wpt*i of it
-    PhaseN ph;
-    ph.rt = wave % s.nrt_p;
-    ph.k0 = wave / s.nrt_p;
-    ph.lstep = 31 - __builtin_clz(s.wpt);
-    ph.hb = s.h0 + 16 * ph.rt;
-    ph.nlive = s.hc - 16 * ph.rt < 16 ? s.hc - 16 * ph.rt : 16;
-    ph.split = (ph.hb / 128 + 1) * 128 - ph.hb;  // a 16-row tile spans at most two scale block rows
-    ph.dnb = ph.nlive > 0 ? ((ph.hb + ph.nlive - 1) >> 7) - (ph.hb >> 7) : 0;
-    ph.nw = 0;
-    const int kend = ph.nlive > 0 ? p.qcap + s.G : p.qcap;
     // the first D items' weights do not depend on mid: issue them before the
     // wait, their activations after it
     RingN<kRingDD> R;
-    ring_open<FMT, 2, kRingDD, AL>(p, L, ph, R, p.qcap, kend, ok);
-    ring_fill<FMT, 2, true, kRingDD, AL>(p, L, ph, R, kend, ok);
-    wait_all(p, epoch + 2);
-    MOE_STAMP(p, 5);
-    MOE_WSTAMP(p, 1);
-    ring_fill_acts<kRingDD, AL>(R);
-    ring_run<FMT, 2, true, kRingDD, AL>(p, L, ph, R, p.qcap, kend, jn, ok);
+    if (!DCLAIM) {
+      // wave w takes tile w % nrt_p of this CU's slice and K-blocks
+      // w / nrt_p + wpt*i of every down job
+      const PhaseN ph = down_phase(s.h0, s.hc, s.nrt, wave % s.nrt_p, wave / s.nrt_p, 31 - __builtin_clz(s.kph));
+      const int kend = ph.nlive > 0 ? p.qcap + nD : p.qcap;
+      ring_open<FMT, 2, kRingDD, AL>(p, L, ph, R, p.qcap, kend, ok);
+      ring_fill<FMT, 2, true, kRingDD, AL>(p, L, ph, R, kend, ok);
+      wait_all(p, epoch + 2);
+      MOE_STAMP(p, 5);
+      MOE_WSTAMP(p, 1);
+      ring_fill_acts<kRingDD, AL>(R);
+      ring_run<FMT, 2, true, kRingDD, AL>(p, L, ph, R, p.qcap, kend, jn, ok);
+    } else {
+      // the waves claim (down job, 16-row tile) units and stream all their
+      // K-blocks, K-phase by K-phase
+      const PhaseN ph = down_phase(s.h0, s.hc, s.nrt, 0, 0, 31 - __builtin_clz(s.kph));
+      const int nunits = s.hc > 0 ? nD * s.nrt : 0;
+      ring_open<FMT, 3, kRingDD, AL>(p, L, ph, R, -1, nunits, ok);
+      ring_fill<FMT, 3, true, kRingDD, AL>(p, L, ph, R, nunits, ok);
+      wait_all(p, epoch + 2);
+      MOE_STAMP(p, 5);
+      MOE_WSTAMP(p, 1);
+      ring_fill_acts<kRingDD, AL>(R);
+      ring_run<FMT, 3, true, kRingDD, AL>(p, L, ph, R, 0, nunits, jn, ok);
+    }
     MOE_WSTAMP(p, 2);
     MOE_STAMP(p, 6);
   }
   {
     const Params& p = fresh_args();
     const Lds L = lds_map(smem, p);
-    const Sched s = make_sched(p, G, 1);
+    const Sched s = make_sched(p, G);
     __syncthreads();
     sum_kphases(p, L, s);
     combine<true>(p, L, s);
@@ -2647,20 +2210,18 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
 }
 
 
-// NARROW = 1: the narrow stream (per-wave partials, 4 activation loads per
-// item); 2 and 3: the same for batches of up to 4 and 8 rows (1 and 2
-// loads per item, see lane_col); 0: the wide stream
-// (up to four 16-column tiles per group, owner reductions).
+// NARROW picks the stream by batch size (see stream_al): 2 for up to 4 rows
+// (one activation load per item), 3 up to 8 (two), 1 up to kKsplitRows
+// (four), 4 above (two, down jobs claimed whole).  The routing-only modes
+// are instantiated with 1.
 template <int MODE, int FMT, int NARROW>
 __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
-  constexpr int NPRE = NARROW ? 1 : 2;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const Lds L = lds_map(smem, p);
   const int tid = threadIdx.x, wave = wave_id();
 
   MOE_STAMP(p, 0);
-  constexpr bool kFwd = MODE == kModeForward || MODE == kModeForwardRes;
-  if (NARROW && kFwd) {
+  if (MODE == kModeForward) {
     // Every wave reads the epoch for itself and first needs it to tag its
     // scores, after the router loads have come in.  The stream's LDS words
     // are set before the first meeting.  The scores are read through their
@@ -2680,29 +2241,26 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
       router_logits_rows<true>(p, ep);
     }
     MOE_STAMP(p, 1);
-    narrow_forward<FMT, NARROW == 2 ? 1 : NARROW == 3 ? 2 : 4>(smem, __builtin_amdgcn_readfirstlane(ep));
+    constexpr int AL = NARROW == 2 ? 1 : NARROW == 3 || NARROW == 4 ? 2 : 4;
+    narrow_forward<FMT, AL, NARROW == 4>(smem, __builtin_amdgcn_readfirstlane(ep));
     return;
   }
+
+  // The routing-only calls: logits of this CU's experts published for
+  // every CU, then workgroup 0 routes every row (polling the tagged score
+  // slots) and groups the step's distinct experts.
   if (tid < 64) L.ctl[tid] = 0u;
   if (tid == 0)
     L.misc[1] = (int32_t)__hip_atomic_load(&p.flags[blockIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const uint32_t epoch = (uint32_t)__builtin_amdgcn_readfirstlane(L.misc[1]);
-
-  // S0: router logits of this CU's experts, published for every CU
-  if (NARROW && p.T < kWaves) router_logits(p, L, epoch, 1u);
+  if (p.T < kWaves) router_logits(p, L, epoch, 1u);
   else router_logits_rows<false>(p, epoch + 1);
   publish(p, epoch + 1);
   MOE_STAMP(p, 1);
-  if (!kFwd && blockIdx.x != 0) return;
-
-  // S2 (wide stream, and the routing-only calls): route every row, then
-  // group the step's distinct experts.  A wave of a narrow call has at most
-  // two rows and polls their score slots; the wide stream waits for every
-  // CU's flag first and reads them from L2.
-  if (NARROW == 0) wait_all(p, epoch + 1);
+  if (blockIdx.x != 0) return;
   MOE_STAMP(p, 2);
-  for (int r = wave; r < p.T; r += kWaves) route_row<NARROW != 0>(p, L, r, epoch + 1);
+  for (int r = wave; r < p.T; r += kWaves) route_row<true>(p, L, r, epoch + 1);
   __syncthreads();
   MOE_STAMP(p, 10);
   if (MODE == kModeRoute) {
@@ -2715,77 +2273,22 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   build_groups(p, L);
   MOE_STAMP(p, 3);
   const int G = __builtin_amdgcn_readfirstlane(L.misc[0]);
-  if (MODE == kModeGroups) {
-    int32_t* o = p.groups_out;
-    if (tid == 0) {
-      o[0] = G; o[1] = p.T; o[2] = p.K; o[3] = p.n_shared;
-    }
-    // g differs per thread here, so plain LDS reads
-    for (int g = tid; g < G; g += kThreads) {
-      o[4 + g] = p.n_shared && g == 0 ? -1 : L.gexp[g];
-      o[4 + G + g] = p.n_shared && g == 0 ? p.T : L.gcnt[g];
-      o[4 + 2 * G + g] = p.n_shared && g == 0 ? 0 : L.gstart[g];
-    }
-    const int ncol = p.T * (p.K + p.n_shared);
-    for (int c = tid; c < ncol; c += kThreads) o[4 + 3 * G + c] = L.cols[c];
-    return;
+  int32_t* o = p.groups_out;
+  if (tid == 0) {
+    o[0] = G; o[1] = p.T; o[2] = p.K; o[3] = p.n_shared;
   }
-
-  const Sched s = make_sched(p, G, 0);
-  bool ok = true;
-  int jc = 0;  // jobs ended
-  Owned own;
-  own.jc = -1;
-  constexpr int MAXCT = max_tiles<NPRE>();
-  f32x4 acc[MAXCT];
-#pragma unroll
-  for (int ct = 0; ct < MAXCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  It up = It{0, first_job(p, 0), 0, 0, 0};
-  settle(p, s, up);
-  run_phase<NPRE, FMT>(p, L, s, up, 2, acc, jc, own, ok);
-  MOE_WSTAMP(p, 0);
-
-  It down = It{2, 0, 0, 0, 0};
-  settle(p, s, down);
-  MOE_STAMP(p, 4);
-  service<NPRE>(p, L, own, true, ok);  // this wave's last owned up/gate job
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  lds_st32(L.ctl + kCtlMidOut + wave, 1u);
-  if (wave == 0) {
-    lds_wait<8>(p, L.ctl + kCtlMidOut, 1u, ok);
-    MOE_STAMP(p, 11);
-    if (tid == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __hip_atomic_store(&p.flags[blockIdx.x], epoch + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    MOE_STAMP(p, 12);
-    if (down.phase == 2) poll_flags(p, epoch + 2);
-    MOE_STAMP(p, 13);
-    lds_st32(L.ctl + kCtlCrossed, 1u);
+  // g differs per thread here, so plain LDS reads
+  for (int g = tid; g < G; g += kThreads) {
+    o[4 + g] = p.n_shared && g == 0 ? -1 : L.gexp[g];
+    o[4 + G + g] = p.n_shared && g == 0 ? p.T : L.gcnt[g];
+    o[4 + 2 * G + g] = p.n_shared && g == 0 ? 0 : L.gstart[g];
   }
-  if (down.phase == 2) lds_wait<1>(p, L.ctl + kCtlCrossed, 1u, ok);
-  MOE_STAMP(p, 5);
-  MOE_WSTAMP(p, 1);
-
-  run_phase<NPRE, FMT>(p, L, s, down, 3, acc, jc, own, ok);
-  MOE_WSTAMP(p, 2);
-  service<NPRE>(p, L, own, true, ok);  // the last owned down job
-  MOE_STAMP(p, 6);
-  __syncthreads();
-
-  // S5: combine this CU's output rows
-  combine<MODE == kModeForwardRes>(p, L, s);
-  MOE_STAMP(p, 7);
-#ifdef MOE_TIMELINE
-  __syncthreads();
-  if (tid < 64 && p.timeline) p.timeline[blockIdx.x * 64 + tid] = MOE_TL(p, tid);
-#endif
+  const int ncol = p.T * (p.K + p.n_shared);
+  for (int c = tid; c < ncol; c += kThreads) o[4 + 3 * G + c] = L.cols[c];
 }
 
 // ------------------------------------------------------------------ host glue
 
-#ifndef MOE_RES_WIDE_TU
 WsLayout ws_layout(int max_rows, int E, int K, int H, int I, int Is) {
   (void)H;
   WsLayout w;
@@ -2798,8 +2301,6 @@ WsLayout ws_layout(int max_rows, int E, int K, int H, int I, int Is) {
   w.total = q;
   return w;
 }
-
-#endif
 
 // Per kernel instance and device: the largest LDS size for which the
 // instance's dynamic LDS limit has been raised and one workgroup of kThreads
@@ -2835,39 +2336,19 @@ static hipError_t launch_one(const Params& p, hipStream_t stream, int dev) {
   return hipGetLastError();
 }
 
-#ifndef MOE_RES_WIDE_TU
+template <int FMT>
+static hipError_t launch_forward(const Params& p, hipStream_t stream, int dev) {
+  if (p.T <= 4) return launch_one<kModeForward, FMT, 2>(p, stream, dev);
+  if (p.T <= 8) return launch_one<kModeForward, FMT, 3>(p, stream, dev);
+  if (p.T <= kKsplitRows) return launch_one<kModeForward, FMT, 1>(p, stream, dev);
+  return launch_one<kModeForward, FMT, 4>(p, stream, dev);
+}
+
 hipError_t launch(const Params& p, int mode, hipStream_t stream, int dev) {
-  const bool wide = !p.narrow;
-  const int nk = p.T <= 4 ? 2 : p.T <= 8 ? 3 : 1;  // narrow kernel by batch size
-  const bool wide_res = mode == kModeForward && wide && p.residual;
-  if (p.routed_fmt == 0 && !wide_res) {
-    if (mode == kModeForward)
-      return wide      ? launch_one<kModeForward, 0, 0>(p, stream, dev)
-             : nk == 2 ? launch_one<kModeForward, 0, 2>(p, stream, dev)
-             : nk == 3 ? launch_one<kModeForward, 0, 3>(p, stream, dev)
-                       : launch_one<kModeForward, 0, 1>(p, stream, dev);
-    if (mode == kModeRoute) return launch_one<kModeRoute, 0>(p, stream, dev);
-    return launch_one<kModeGroups, 0>(p, stream, dev);
-  }
-  if (!wide_res) {
-    if (mode == kModeForward)
-      return wide      ? launch_one<kModeForward, 1, 0>(p, stream, dev)
-             : nk == 2 ? launch_one<kModeForward, 1, 2>(p, stream, dev)
-             : nk == 3 ? launch_one<kModeForward, 1, 3>(p, stream, dev)
-                       : launch_one<kModeForward, 1, 1>(p, stream, dev);
-    if (mode == kModeRoute) return launch_one<kModeRoute, 1>(p, stream, dev);
-    return launch_one<kModeGroups, 1>(p, stream, dev);
-  }
-  return launch_res_wide(p, stream, dev);
+  if (mode == kModeForward)
+    return p.routed_fmt == 0 ? launch_forward<0>(p, stream, dev) : launch_forward<1>(p, stream, dev);
+  if (mode == kModeRoute) return launch_one<kModeRoute, 0>(p, stream, dev);
+  return launch_one<kModeGroups, 0>(p, stream, dev);
 }
-#else
-// The wide stream with a residual: its kernels are built in a translation
-// unit of their own (moe_kernels_res.hip), so that the code object of the
-// other kernels is the same with or without them.
-hipError_t launch_res_wide(const Params& p, hipStream_t stream, int dev) {
-  return p.routed_fmt == 0 ? launch_one<kModeForwardRes, 0, 0>(p, stream, dev)
-                           : launch_one<kModeForwardRes, 1, 0>(p, stream, dev);
-}
-#endif
 
 }  // namespace moe
