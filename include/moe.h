@@ -96,8 +96,8 @@ typedef enum { MOE_BIAS_F32 = 0, MOE_BIAS_BF16 = 1 } moe_bias_dtype;
 
 /* Layer description (host struct). */
 typedef struct {
-  int hidden;        /* H: multiple of 128, 128..8192 */
-  int inter;         /* I: routed expert intermediate, multiple of 128, <= 4096 */
+  int hidden;        /* H: multiple of 128, 128..8192 (MXFP4 experts: multiple of 256, >= 2048) */
+  int inter;         /* I: routed expert intermediate, multiple of 128, <= 4096 (MXFP4: of 256) */
   int shared_inter;  /* I_s: shared expert intermediate, multiple of 128, <= 4096 */
   int n_experts;     /* E: 1..256 */
   int top_k;         /* K: 1..8 and <= E (any K, not only powers of two) */

@@ -51,6 +51,10 @@ int check_cfg(const moe_config* c) {
   if (c->bias_dtype != MOE_BIAS_F32 && c->bias_dtype != MOE_BIAS_BF16) return MOE_ERR_FORMAT;
   if (c->hidden < 128 || c->hidden > 8192 || c->hidden % 128) return MOE_ERR_SHAPE;
   if (c->inter < 128 || c->inter > 4096 || c->inter % 128) return MOE_ERR_SHAPE;
+  // MXFP4 experts stream 256 values of a row per item, and an up/gate job
+  // needs at least one item for each of its 8 K-phases
+  if (c->routed_fmt == MOE_FMT_MXFP4 && (c->hidden % 256 || c->hidden < 2048 || c->inter % 256))
+    return MOE_ERR_SHAPE;
   if (c->n_shared != 0 && c->n_shared != 1) return MOE_ERR_SHAPE;
   if (c->n_shared && (c->shared_inter < 128 || c->shared_inter > 4096 || c->shared_inter % 128))
     return MOE_ERR_SHAPE;

@@ -1245,7 +1245,7 @@ __device__ inline JobDesc make_desc(const Params& p, bool up, bool sh, int e, in
   const int iexp = sh ? p.Is : p.I;
   const int kdim = up ? p.H : iexp;
   d.fmt = sh ? 0 : p.routed_fmt;
-  d.nkb = kdim / 128;
+  d.nkb = kdim / (d.fmt ? 256 : 128);  // K-blocks: 128 bytes of every row (128 FP8 or 256 MXFP4 values)
   d.ncols = ncols;
   d.cbase = cbase;
   d.spare = 0;
@@ -1466,10 +1466,16 @@ struct FetchN {
   const uint8_t* sb;             // block scales
   const uint8_t* ab;             // activations: x or mid
   uint32_t wo, so, ao;           // this lane's offsets of the next item
+  uint32_t h2;                   // MXFP4 items: the second half's activation offset (FP8 items: 0)
 };
 
+// One item: a K-block of a 16-row tile, 128 bytes of each row (FP8: 128
+// values, one fp32 block scale per 128-row block; MXFP4: 256 values, the
+// lane's two E8M0 scales in s).  B: the activations, AL loads per 128
+// values (2*AL in a kernel with MXFP4 experts, whose FP8 items repeat the
+// first AL as the second).
 struct ItemN {
-  u32x4 w0, w1, B[4];
+  u32x4 w0, w1, B[8];
   uint32_t s;
 };
 
@@ -1497,10 +1503,10 @@ __device__ __forceinline__ void fetch_from_desc(const Params& p, const PhaseN& p
                                                 int n, int code) {
   const int lane = threadIdx.x & 63, lg = lane >> 4, row = lane & 15;
   const int fmt = FMT == 0 ? 0 : d.fmt;
-  const uint32_t kb = fmt ? 64u : 128u, lb = fmt ? 16u : 32u;
   const uint32_t lrow = KIND == 1 ? (row < 8 ? row : row + d.jump) : ph.hb + (row < ph.nlive ? row : ph.nlive - 1);
   f.wb = (const uint8_t*)d.wb;
-  f.wo = lmul(lrow, (uint32_t)(d.nkb * (fmt ? 64 : 128))) + (uint32_t)k0 * kb + (uint32_t)lg * lb;
+  // 128 bytes of each row per K-block, 32 per lane group
+  f.wo = lmul(lrow, (uint32_t)(d.nkb * 128)) + (uint32_t)k0 * 128u + (uint32_t)lg * 32u;
   if (fmt == 0) {
     if (KIND == 1) {
       f.sb = (const uint8_t*)d.sb;
@@ -1510,11 +1516,16 @@ __device__ __forceinline__ void fetch_from_desc(const Params& p, const PhaseN& p
       f.so = (lane < 32 ? 0u : 4u * (uint32_t)(ph.dnb * d.nkb)) + 4u * (uint32_t)k0;
     }
   } else {
+    // the K-block's 8 scale bytes of the row: lane group lg takes bytes
+    // 2lg and 2lg+1, from the aligned word 4*(lg >> 1)
     f.sb = (const uint8_t*)d.sb;
-    f.so = lmul(lrow, d.shi) + 4u * (uint32_t)k0;
+    f.so = lmul(lrow, d.shi) + 8u * (uint32_t)k0 + 4u * (uint32_t)(lg >> 1);
   }
-  // a lane's first piece: j = lane mod G
-  f.ao = 2 * act_offset(p, KIND, code, lg) + 256u * (uint32_t)k0 + 16u * (uint32_t)(lane & (4 / AL - 1));
+  // a lane's first piece: j = lane mod G; an MXFP4 K-block is 256 values,
+  // 64 per lane group
+  f.ao = 2 * act_offset(p, KIND, code, lg) + (fmt ? 64u * (uint32_t)lg : 0u) + (fmt ? 512u : 256u) * (uint32_t)k0 +
+         16u * (uint32_t)(lane & (4 / AL - 1));
+  f.h2 = fmt ? 64u : 0u;
   f.fmt = fmt;
   f.nstep = 1 << ph_lstep<KIND>(ph);
   f.left = n;
@@ -1532,6 +1543,7 @@ __device__ __forceinline__ void fetch_dead(const Params& p, FetchN& f) {
   f.sb = (const uint8_t*)arg_ptr(p.x);
   f.so = 0;
   f.ao = 0;
+  f.h2 = 0;
   f.fmt = 0;
   f.nstep = 0;
   f.left = 1 << 30;
@@ -1647,29 +1659,37 @@ template <int FMT>
 __device__ __forceinline__ void fetch_weights_n(const FetchN& f, ItemN& it) {
   const uint8_t* w = f.wb + f.wo;
   it.w0 = ldg<u32x4>(w);
-  it.w1 = ldg<u32x4>(w + (FMT == 0 || f.fmt == 0 ? 16 : 0));
+  it.w1 = ldg<u32x4>(w + 16);
   it.s = ldg<uint32_t>(f.sb + f.so);
 }
-// Activations: AL loads of 16 B per lane, pieces j + G*i (the load
-// instructions, not the bytes, are what the vector memory path pays for).
-template <int AL>
-__device__ __forceinline__ void fetch_acts_n(const uint8_t* ab, uint32_t ao, ItemN& it) {
+// Activations: AL loads of 16 B per lane per 128 values, pieces j + G*i
+// (the load instructions, not the bytes, are what the vector memory path
+// pays for).  A kernel with MXFP4 experts issues 2*AL: the second half at
+// h2 (64 B on: pieces 4.. of the lane group's 8), or again the first half
+// for an FP8 item (h2 = 0), so that every item issues the same loads.
+template <int FMT, int AL>
+__device__ __forceinline__ void fetch_acts_n(const uint8_t* ab, uint32_t ao, uint32_t h2, ItemN& it) {
   const uint8_t* a = ab + ao;
 #pragma unroll
   for (int i = 0; i < AL; ++i) it.B[i] = ldg<u32x4>(a + 16 * (4 / AL) * i);
+  if (FMT != 0) {
+#pragma unroll
+    for (int i = 0; i < AL; ++i) it.B[AL + i] = ldg<u32x4>(a + h2 + 16 * (4 / AL) * i);
+  }
 }
 template <int FMT, int AL>
 __device__ __forceinline__ void fetch_item_n(const FetchN& f, ItemN& it) {
   fetch_weights_n<FMT>(f, it);
-  fetch_acts_n<AL>(f.ab, f.ao, it);
+  fetch_acts_n<FMT, AL>(f.ab, f.ao, f.h2, it);
 }
 
 template <int FMT>
 __device__ __forceinline__ void fetch_adv_n(FetchN& f) {
   const uint32_t n = (uint32_t)uni(f.nstep);
-  f.wo += n * (FMT == 0 || f.fmt == 0 ? 128u : 64u);
-  f.so += 4u * n;
-  f.ao += 256u * n;
+  const bool mx = FMT != 0 && f.fmt != 0;
+  f.wo += n * 128u;
+  f.so += (mx ? 8u : 4u) * n;
+  f.ao += (mx ? 512u : 256u) * n;
   f.left = uni(f.left) - 1;
   f.cnt = uni(f.cnt) + 1;
 }
@@ -1843,7 +1863,7 @@ __device__ __forceinline__ bf16x8 act_operand(const ItemN& it, int m) {
     const int v = (int)it.B[m / G][i];
     int r;
     if (G == 4) {
-      switch (m) {
+      switch (m & 3) {
         case 0: r = __builtin_amdgcn_update_dpp(0, v, 0x00, 0xF, 0xF, false); break;
         case 1: r = __builtin_amdgcn_update_dpp(0, v, 0x55, 0xF, 0xF, false); break;
         case 2: r = __builtin_amdgcn_update_dpp(0, v, 0xAA, 0xF, 0xF, false); break;
@@ -1875,11 +1895,19 @@ __device__ __forceinline__ void eat_item_n(int split, int lg, const ItemN& it, f
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = fmaf(t[q], 4 * lg + q < split ? s_lo : s_hi, acc[q]);
   } else {
-    const float sc = e8m0_to_f32((it.s >> (8 * lg)) & 0xffu);
+    // 256 values: lane group lg holds values 64lg.. (w0: the first 32 with
+    // scale byte 2lg, w1: the next 32 with byte 2lg+1); MFMA m takes
+    // values 64lg + 8m.. of every lane group
+    const uint32_t sh = 16u * (uint32_t)(lg & 1);
+    const float sc0 = e8m0_to_f32((it.s >> sh) & 0xffu), sc1 = e8m0_to_f32((it.s >> (sh + 8)) & 0xffu);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) A[m] = e2m1x8_to_bf16(it.w0[m], sc);
+    for (int m = 0; m < 4; ++m) A[m] = e2m1x8_to_bf16(it.w0[m], sc0);
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc = mfma16(A[m], act_operand<AL>(it, m), acc);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) A[m] = e2m1x8_to_bf16(it.w1[m], sc1);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc = mfma16(A[m], act_operand<AL>(it, 4 + m), acc);
   }
 }
 
@@ -1891,15 +1919,15 @@ __device__ __forceinline__ void eat_item_n(int split, int lg, const ItemN& it, f
 // zero where this wave has no items.
 constexpr int kRingD = 5;   // up/gate (and the default)
 constexpr int kRingDD = 6;  // down: its second tile has fewer live rows, so items carry fewer bytes
-// up/gate ring depth by activation loads per item (2 loads: 7 measured
-// best at 8 rows)
-template <int AL>
-constexpr int ring_up() { return AL == 2 ? 7 : kRingD; }
+// up/gate ring depth by activation loads per item (FP8 with 2 loads: 7
+// measured best at 8 rows)
+template <int FMT, int AL>
+constexpr int ring_up() { return FMT == 0 && AL == 2 ? 7 : kRingD; }
 template <int D = kRingD>
 struct RingN {
   FetchN f;
   ItemN r[D];
-  uint32_t aop[D];  // activation offsets of the filled items (split fill)
+  uint32_t aop[D], h2p[D];  // activation offsets of the filled items (split fill)
 };
 
 template <int FMT, int KIND, int D, int AL>
@@ -1922,6 +1950,7 @@ __device__ __forceinline__ void ring_fill(const Params& p, const Lds& L, const P
     if (WONLY) {
       fetch_weights_n<FMT>(R.f, R.r[d]);
       R.aop[d] = R.f.ao;
+      R.h2p[d] = R.f.h2;
     } else {
       fetch_item_n<FMT, AL>(R.f, R.r[d]);
     }
@@ -1930,10 +1959,10 @@ __device__ __forceinline__ void ring_fill(const Params& p, const Lds& L, const P
   }
 }
 
-template <int D, int AL>
+template <int FMT, int D, int AL>
 __device__ __forceinline__ void ring_fill_acts(RingN<D>& R) {
 #pragma unroll
-  for (int d = 0; d < D; ++d) fetch_acts_n<AL>(R.f.ab, R.aop[d], R.r[d]);
+  for (int d = 0; d < D; ++d) fetch_acts_n<FMT, AL>(R.f.ab, R.aop[d], R.h2p[d], R.r[d]);
 }
 
 // PEEL: the first round is its own copy, so that the loop's waits are
@@ -2092,7 +2121,7 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
   int jn = 0;  // jobs this wave has ended (for balance)
   bool ok = true;
   {
-    RingN<ring_up<AL>()> R;
+    RingN<ring_up<FMT, AL>()> R;
     const Params& p = fresh_args();
     const Lds L = lds_map(smem, p);
     const int nkb = p.H / 128;
@@ -2144,11 +2173,11 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
       __syncthreads();
       MOE_STAMP(p, 11);
     }
-    ring_open<FMT, 1, ring_up<AL>(), AL>(p, L, ph, R, 0, nS, ok);
+    ring_open<FMT, 1, ring_up<FMT, AL>(), AL>(p, L, ph, R, 0, nS, ok);
     MOE_STAMP(p, 62);
-    ring_fill<FMT, 1, false, ring_up<AL>(), AL>(p, L, ph, R, nS, ok);
+    ring_fill<FMT, 1, false, ring_up<FMT, AL>(), AL>(p, L, ph, R, nS, ok);
     MOE_STAMP(p, 13);
-    ring_run<FMT, 1, false, ring_up<AL>(), AL>(p, L, ph, R, 0, nS, jn, ok);
+    ring_run<FMT, 1, false, ring_up<FMT, AL>(), AL>(p, L, ph, R, 0, nS, jn, ok);
     MOE_WSTAMP(p, 0);
     MOE_TVAL(p, 8, jn);
   }
@@ -2176,7 +2205,7 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
       wait_all(p, epoch + 2);
       MOE_STAMP(p, 5);
       MOE_WSTAMP(p, 1);
-      ring_fill_acts<kRingDD, AL>(R);
+      ring_fill_acts<FMT, kRingDD, AL>(R);
       ring_run<FMT, 2, true, kRingDD, AL>(p, L, ph, R, p.qcap, kend, jn, ok);
     } else {
       // the waves claim (down job, 16-row tile) units and stream all their
@@ -2188,7 +2217,7 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
       wait_all(p, epoch + 2);
       MOE_STAMP(p, 5);
       MOE_WSTAMP(p, 1);
-      ring_fill_acts<kRingDD, AL>(R);
+      ring_fill_acts<FMT, kRingDD, AL>(R);
       ring_run<FMT, 3, true, kRingDD, AL>(p, L, ph, R, 0, nunits, jn, ok);
     }
     MOE_WSTAMP(p, 2);
@@ -2210,10 +2239,10 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
 }
 
 
-// NARROW picks the stream by batch size (see stream_al): 2 for up to 4 rows
-// (one activation load per item), 3 up to 8 (two), 1 up to kKsplitRows
-// (four), 4 above (two, down jobs claimed whole).  The routing-only modes
-// are instantiated with 1.
+// NARROW picks the stream by batch size (see stream_al): 2 for one
+// activation load per item, 3 for two (down jobs split over the waves by
+// K-phase), 4 above kKsplitRows rows (two loads, down jobs claimed whole).
+// The routing-only modes are instantiated with 1.
 template <int MODE, int FMT, int NARROW>
 __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -2231,7 +2260,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
     if (tid < 64) L.ctl[tid] = 0u;
     stream_init(p, L, shared_jobs_here(p));
     __syncthreads();
-    if (NARROW == 2 || p.T < kWaves) {  // (NARROW 2 runs at most 4 rows)
+    if (p.T < kWaves) {
       router_logits(p, L, ep, 1u);
       // the logit partials lie in wave 0's routing scratch (wave 0 reads
       // them) unless the experts are few
@@ -2241,7 +2270,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
       router_logits_rows<true>(p, ep);
     }
     MOE_STAMP(p, 1);
-    constexpr int AL = NARROW == 2 ? 1 : NARROW == 3 || NARROW == 4 ? 2 : 4;
+    constexpr int AL = NARROW == 2 ? 1 : 2;
     narrow_forward<FMT, AL, NARROW == 4>(smem, __builtin_amdgcn_readfirstlane(ep));
     return;
   }
@@ -2338,10 +2367,9 @@ static hipError_t launch_one(const Params& p, hipStream_t stream, int dev) {
 
 template <int FMT>
 static hipError_t launch_forward(const Params& p, hipStream_t stream, int dev) {
-  if (p.T <= 4) return launch_one<kModeForward, FMT, 2>(p, stream, dev);
-  if (p.T <= 8) return launch_one<kModeForward, FMT, 3>(p, stream, dev);
-  if (p.T <= kKsplitRows) return launch_one<kModeForward, FMT, 1>(p, stream, dev);
-  return launch_one<kModeForward, FMT, 4>(p, stream, dev);
+  if (p.T > kKsplitRows) return launch_one<kModeForward, FMT, 4>(p, stream, dev);  // (stream_al: 2)
+  return stream_al(p.T) == 1 ? launch_one<kModeForward, FMT, 2>(p, stream, dev)
+                             : launch_one<kModeForward, FMT, 3>(p, stream, dev);
 }
 
 hipError_t launch(const Params& p, int mode, hipStream_t stream, int dev) {

@@ -43,6 +43,11 @@ def test_workspace_size_and_config_checks():
         (dict(n_group=7), moe.MOE_ERR_SHAPE),          # 256 % 7 != 0
         (dict(topk_group=9), moe.MOE_ERR_SHAPE),
         (dict(routed_fmt=5), moe.MOE_ERR_FORMAT),
+        # MXFP4 experts: 256 values per item, at least 8 items per row
+        (dict(routed_fmt=1, hidden=1536), moe.MOE_ERR_SHAPE),
+        (dict(routed_fmt=1, hidden=2176), moe.MOE_ERR_SHAPE),
+        (dict(routed_fmt=1, inter=1152), moe.MOE_ERR_SHAPE),
+        (dict(routed_fmt=1, hidden=2048, inter=1280), None),
         (dict(bias_bf16=0, n_group=1, topk_group=1, top_k=8), None),
     ]
     for over, code in bad:

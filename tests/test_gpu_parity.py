@@ -25,7 +25,7 @@ SMALL = [
     ("multichunk_ragged", dict(hidden=1152, inter=640, shared_inter=384, n_experts=24, top_k=5), 9, 14, "corr"),
     ("wide_h3072", dict(hidden=3072, inter=256, shared_inter=256, n_experts=16, top_k=4,
                         n_group=4, topk_group=2), 20, 15, "iid"),
-    ("mxfp4_small", dict(hidden=1536, inter=1536, shared_inter=512, n_experts=16, top_k=6,
+    ("mxfp4_small", dict(hidden=2048, inter=1536, shared_inter=512, n_experts=16, top_k=6,
                          routed_fmt=1, bias_bf16=1), 16, 16, "corr"),
     ("no_shared", dict(n_shared=0, hidden=512, inter=256, n_experts=12, top_k=3), 7, 17, "iid"),
     ("k_equals_e", dict(n_experts=8, top_k=8, hidden=256, inter=128), 3, 18, "iid"),
@@ -38,9 +38,9 @@ SMALL = [
     # to 8 (two loads, 2 lanes per column), with MXFP4 experts, with every
     # row of one request sharing experts (jobs at full column capacity), and
     # with two down tiles
-    ("mxfp4_t3", dict(hidden=1536, inter=1536, shared_inter=512, n_experts=16, top_k=6,
+    ("mxfp4_t3", dict(hidden=2048, inter=1536, shared_inter=512, n_experts=16, top_k=6,
                       routed_fmt=1, bias_bf16=1), 3, 22, "corr"),
-    ("mxfp4_t6", dict(hidden=1536, inter=1536, shared_inter=512, n_experts=16, top_k=6,
+    ("mxfp4_t6", dict(hidden=2048, inter=1536, shared_inter=512, n_experts=16, top_k=6,
                       routed_fmt=1, bias_bf16=1), 6, 23, "corr"),
     ("four_rows_one_request", dict(hidden=1024, inter=512, shared_inter=256, n_experts=12, top_k=4), 4, 24, "corr"),
     ("two_down_tiles_t2", dict(hidden=4352, inter=256, shared_inter=256, n_experts=16, top_k=4), 2, 25, "corr"),

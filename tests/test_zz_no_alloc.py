@@ -14,7 +14,7 @@ from _gpu import gpu_case, say
 pytestmark = pytest.mark.gpu
 
 V3R = dict(hidden=1024, inter=256, shared_inter=256, n_experts=256, top_k=8, n_group=8, topk_group=4)
-MX = dict(hidden=1536, inter=1536, shared_inter=512, n_experts=16, top_k=6, routed_fmt=1, bias_bf16=1)
+MX = dict(hidden=2048, inter=1536, shared_inter=512, n_experts=16, top_k=6, routed_fmt=1, bias_bf16=1)
 
 
 def _both(layer, x):
