@@ -398,8 +398,17 @@ __device__ inline void wait_all(const Params& p, uint32_t target) {
 // so a reader polls the slots themselves and needs no flag barrier (a slot
 // is current once both its words carry the call's tag).  The key
 // b = s + bias is recomputed by the reader in the same fp64 operation.
+// A row's slots are stored transposed by fours: expert e at
+// (e mod 4) * E4 + e / 4 (E4 = E rounded up to 4, over 4), so the routing
+// wave, whose lane l holds experts 4l..4l+3, reads one contiguous run of
+// slots per load instruction.
+__device__ __forceinline__ int slot_e4(int E) { return (E + 3) >> 2; }
+__device__ __forceinline__ size_t score_slot(const Params& p, int r, int e) {
+  const int e4 = slot_e4(p.E);
+  return (size_t)r * 4 * e4 + (size_t)(e & 3) * e4 + (e >> 2);
+}
 __device__ __forceinline__ void publish_score(const Params& p, int r, int e, double s, uint32_t tag) {
-  uint64_t* dst = (uint64_t*)p.scores + ((size_t)r * p.E + e) * 2;
+  uint64_t* dst = (uint64_t*)p.scores + score_slot(p, r, e) * 2;
   const uint64_t sb = __builtin_bit_cast(uint64_t, s);
   st_agent<uint64_t>(dst, ((uint64_t)tag << 32) | (sb >> 32));
   st_agent<uint64_t>(dst + 1, ((uint64_t)tag << 32) | (sb & 0xffffffffull));
@@ -639,57 +648,42 @@ __device__ inline void router_logits_rows(const Params& p, uint32_t v) {
   }
 }
 
-// Two largest values (t1 >= t2) of an aligned lane group, one exchange step.
+// Two largest values (t1 >= t2) over an aligned lane group, one exchange
+// step: the larger of the two firsts, and the larger of the smaller first
+// and the two seconds.
 template <int CTRL>
-__device__ __forceinline__ void top2_step(double (&t1)[4], double (&t2)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const double o1 = xlane_d<CTRL>(t1[i]), o2 = xlane_d<CTRL>(t2[i]);
-    const double hi = fmax(t1[i], o1), lo = fmin(t1[i], o1);
-    t2[i] = fmax(lo, fmax(t2[i], o2));
-    t1[i] = hi;
-  }
-}
-
-__device__ __forceinline__ double pick4(const double (&v)[4], int i) {
-  return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
+__device__ __forceinline__ void top2_step(double& t1, double& t2) {
+  const double o1 = xlane_d<CTRL>(t1), o2 = xlane_d<CTRL>(t2);
+  const double hi = fmax(t1, o1), lo = fmin(t1, o1);
+  t2 = fmax(lo, fmax(t2, o2));
+  t1 = hi;
 }
 
 // Routes row r with one wave: group stage (sum of the two best keys per
-// group, keep k_g groups by (score desc, index asc)), then K rounds of wave
-// argmax over (key desc, index asc); weights s/sum(s)*scale in fp64.
-// Lane l holds experts l, l+64, l+128, l+192.
-// POLL: poll row r's score slots (agent-scope loads) until every one
-// carries this call's tag (bounded: on timeout the error bit is set and
-// routing runs on).  Otherwise the flags have been waited for and the slots
-// are read once with plain loads (many rows per wave: they hit in L2).
-template <bool POLL>
+// group, keep k_g groups by (score desc, index asc)), then the top K by
+// (key desc, index asc); weights s/sum(s)*scale in fp64.
+// Lane l holds experts 4l .. 4l+3, so a group of 4m experts (m a power of
+// two) is an aligned run of m lanes.
+// Polls row r's score slots (agent-scope loads) until every one carries
+// this call's tag (bounded: on timeout the error bit is set and routing
+// runs on).
 __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t tag) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   typedef __attribute__((address_space(1))) uint64_t G64;
-  const G64* sc = (const G64*)p.scores + (size_t)r * p.E * 2;
+  const G64* sc = (const G64*)p.scores + score_slot(p, r, 0) * 2;  // the row's first slot
+  const int e4 = slot_e4(p.E);
   uint64_t w0[4] = {0, 0, 0, 0}, w1[4] = {0, 0, 0, 0};
   double bias[4];  // loaded first: they do not depend on the scores
 #pragma unroll
-  for (int i = 0; i < 4; ++i) bias[i] = lane + 64 * i < p.E ? load_bias(p, lane + 64 * i) : 0.0;
-  if (!POLL) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      if (e < p.E) {
-        w0[i] = sc[2 * e];
-        w1[i] = sc[2 * e + 1];
-      }
-    }
-  }
-  for (int spins = 0; POLL;) {
+  for (int i = 0; i < 4; ++i) bias[i] = 4 * lane + i < p.E ? load_bias(p, 4 * lane + i) : 0.0;
+  for (int spins = 0;;) {
     bool ready = true;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
+      const int e = 4 * lane + i, q = i * e4 + lane;  // q: expert e's slot in the row
       if (e < p.E) {
-        w0[i] = __hip_atomic_load(sc + 2 * e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        w1[i] = __hip_atomic_load(sc + 2 * e + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        w0[i] = __hip_atomic_load(sc + 2 * q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        w1[i] = __hip_atomic_load(sc + 2 * q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         ready = ready && (uint32_t)(w0[i] >> 32) == tag && (uint32_t)(w1[i] >> 32) == tag;
       }
     }
@@ -701,14 +695,14 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
     __builtin_amdgcn_s_sleep(1);
   }
   if (r == 0) MOE_LSTAMP(p, 9);
-  if (POLL && lane == 0)  // rows whose scores are in (see narrow_forward)
+  if (lane == 0)  // rows whose scores are in (see narrow_forward)
     __hip_atomic_fetch_add((__attribute__((address_space(3))) uint32_t*)(L.misc + kMiscPolled), 1u,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   double bv[4], sv[4];
   bool alive[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
+    const int e = 4 * lane + i;
     alive[i] = e < p.E;
     const double s = __builtin_bit_cast(double, (w0[i] << 32) | (w1[i] & 0xffffffffull));
     const double b = alive[i] ? s + bias[i] : -INFINITY;
@@ -717,70 +711,39 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
   }
   if (r == 0) MOE_LSTAMP(p, 60);
   if (p.ng > 1) {
-    const int gsz = p.E / p.ng;
-    if (gsz <= 64 && (gsz & (gsz - 1)) == 0) {
-      // each group is an aligned run of gsz lanes of one slot: butterfly
-      double t1[4], t2[4];
+    const int gsz = p.E / p.ng, lpg = gsz >> 2;
+    if ((gsz & 3) == 0 && lpg <= 64 && (lpg & (lpg - 1)) == 0) {
+      // the lane's own two best keys, then a butterfly over the group's lanes
+      double t1 = fmax(bv[0], bv[1]), t2 = fmin(bv[0], bv[1]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        t1[i] = bv[i];
-        t2[i] = -INFINITY;
+      for (int i = 2; i < 4; ++i) {
+        t2 = fmax(t2, fmin(t1, bv[i]));
+        t1 = fmax(t1, bv[i]);
       }
-      if (gsz > 1) top2_step<kDppXor1>(t1, t2);
-      if (gsz > 2) top2_step<kDppXor2>(t1, t2);
-      if (gsz > 4) top2_step<kDppHalfMirror>(t1, t2);
-      if (gsz > 8) top2_step<kDppMirror>(t1, t2);
-      if (gsz > 16) top2_step<kSwizzleXor16>(t1, t2);
-      if (gsz > 32) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const double o1 = __shfl_xor(t1[i], 32, 64), o2 = __shfl_xor(t2[i], 32, 64);
-          const double hi = fmax(t1[i], o1), lo = fmin(t1[i], o1);
-          t2[i] = fmax(lo, fmax(t2[i], o2));
-          t1[i] = hi;
-        }
+      if (lpg > 1) top2_step<kDppXor1>(t1, t2);
+      if (lpg > 2) top2_step<kDppXor2>(t1, t2);
+      if (lpg > 4) top2_step<kDppHalfMirror>(t1, t2);
+      if (lpg > 8) top2_step<kDppMirror>(t1, t2);
+      if (lpg > 16) top2_step<kSwizzleXor16>(t1, t2);
+      if (lpg > 32) {
+        const double o1 = __shfl_xor(t1, 32, 64), o2 = __shfl_xor(t2, 32, 64);
+        const double hi = fmax(t1, o1), lo = fmin(t1, o1);
+        t2 = fmax(lo, fmax(t2, o2));
+        t1 = hi;
       }
-      double gs[4];
+      // rank of this lane's group (lane / lpg) among all groups, from each
+      // group's score in its first lane
+      const double gs = t1 + t2;
+      const int own = lane / lpg;
+      int rank = 0;
+      for (int j = 0; j < p.ng; ++j) rank += key_before(readlane_d(gs, j * lpg), j, gs, own) ? 1 : 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) gs[i] = t1[i] + t2[i];
-      // rank of this lane's group j_i = (lane + 64 i) / gsz among all groups
-      if (POLL && gsz == 32) {
-        // groups 2i and 2i+1 are the halves of slot i: a swap of halves
-        // gives every lane both scores, so every lane holds all groups
-        double glo[4], ghi[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const long long u = __double_as_longlong(gs[i]);
-          const auto lo = __builtin_amdgcn_permlane32_swap((unsigned)u, (unsigned)u, false, false);
-          const auto hi = __builtin_amdgcn_permlane32_swap((unsigned)(u >> 32), (unsigned)(u >> 32), false, false);
-          glo[i] = __longlong_as_double(((long long)hi[0] << 32) | lo[0]);
-          ghi[i] = __longlong_as_double(((long long)hi[1] << 32) | lo[1]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int own = 2 * i + (lane >> 5);
-          int rank = 0;
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (j < p.ng) rank += key_before((j & 1) ? ghi[j >> 1] : glo[j >> 1], j, gs[i], own) ? 1 : 0;
-          alive[i] = alive[i] && rank < p.kg;
-        }
-      } else {
-        int rank[4] = {0, 0, 0, 0};
-        for (int j = 0; j < p.ng; ++j) {
-          const int first = j * gsz;
-          const double gj = readlane_d(pick4(gs, first >> 6), first & 63);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) rank[i] += key_before(gj, j, gs[i], (lane + 64 * i) / gsz) ? 1 : 0;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) alive[i] = alive[i] && rank[i] < p.kg;
-      }
+      for (int i = 0; i < 4; ++i) alive[i] = alive[i] && rank < p.kg;
     } else {
       double* rb = L.rb + (size_t)wave * p.E;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (alive[i]) rb[lane + 64 * i] = bv[i];
+        if (alive[i]) rb[4 * lane + i] = bv[i];
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       if (lane < p.ng) {
@@ -804,7 +767,7 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (alive[i]) alive[i] = L.rkept[wave * 64 + (lane + 64 * i) / gsz] != 0;
+        if (alive[i]) alive[i] = L.rkept[wave * 64 + (4 * lane + i) / gsz] != 0;
     }
   }
   if (r == 0) MOE_LSTAMP(p, 14);
@@ -844,14 +807,14 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
       const int pos = nc + __popcll(bal & ((1ull << lane) - 1ull));
       cb[pos] = bv[i];
       cs[pos] = sv[i];
-      ce[pos] = lane + 64 * i;
+      ce[pos] = 4 * lane + i;
     }
     nc += __popcll(bal);
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   double* ps = L.rgs + (size_t)wave * 64;  // the winners' s in pick order
-  if (POLL && nc <= 8) {
+  if (nc <= 8) {
     // lane 8a + c compares candidate c with candidate a; a's rank is the
     // count of its lane group's bits
     const int a = lane >> 3, c = lane & 7;
@@ -881,16 +844,10 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   if (r == 0) MOE_LSTAMP(p, 15);
-  if (POLL) {
-    // every lane forms the same sum in pick order; lane k writes weight k
-    double ssum = 0.0;
-    for (int k = 0; k < p.K; ++k) ssum += ps[k];
-    if (lane < p.K) L.w[r * p.K + lane] = (float)(ps[lane] / ssum * p.routed_scale);
-  } else if (lane == 0) {  // (the same values; this form keeps the wide stream's code as measured)
-    double ssum = 0.0;
-    for (int k = 0; k < p.K; ++k) ssum += ps[k];
-    for (int k = 0; k < p.K; ++k) L.w[r * p.K + k] = (float)(ps[k] / ssum * p.routed_scale);
-  }
+  // every lane forms the same sum in pick order; lane k writes weight k
+  double ssum = 0.0;
+  for (int k = 0; k < p.K; ++k) ssum += ps[k];
+  if (lane < p.K) L.w[r * p.K + lane] = (float)(ps[lane] / ssum * p.routed_scale);
 }
 
 // ------------------------------------------------------------------ S2 grouping
@@ -904,6 +861,20 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 }
 
+// Inclusive prefix sum over the wave by DPP: running sums within each row
+// of 16 lanes (shifts 1, 2, 4, 8, lanes shifted in from outside the row
+// adding 0), then the row totals carried on by the row broadcasts of lanes
+// 15 and 31.  No LDS round trip (a shuffle would be one per step).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false); // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false); // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 // gstart[g] = base + sum of gcnt over groups g0..g-1, for g0 <= g < G, by
 // one wave (64 groups per pass).
 __device__ inline void scan_gstart(const Lds& L, int g0, int G, int base) {
@@ -911,14 +882,9 @@ __device__ inline void scan_gstart(const Lds& L, int g0, int G, int base) {
   for (int c0 = g0; c0 < G; c0 += 64) {
     const int g = c0 + lane;
     const int c = g < G ? L.gcnt[g] : 0;
-    int v = c;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int t = __shfl_up(v, off, 64);
-      if (lane >= off) v += t;
-    }
+    const int v = wave_incl_scan(c);
     if (g < G) L.gstart[g] = base + v - c;
-    base += __shfl(v, 63, 64);
+    base += __builtin_amdgcn_readlane(v, 63);
   }
 }
 
@@ -1346,15 +1312,9 @@ __device__ inline void stream_init(const Params& p, const Lds& L, int nS) {
 // Exclusive offsets of per-lane counts n over the wave, added to `base`
 // (which moves on by the wave's total).
 __device__ __forceinline__ int wave_offset(int n, int& base) {
-  const int lane = threadIdx.x & 63;
-  int v = n;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(v, off, 64);
-    if (lane >= off) v += t;
-  }
+  const int v = wave_incl_scan(n);
   const int o = base + v - n;
-  base += __shfl(v, 63, 64);
+  base += __builtin_amdgcn_readlane(v, 63);
   return o;
 }
 
@@ -2139,7 +2099,7 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
       const int r = kWaves - 1 - wave;
       if (r < p.T) {
         __builtin_amdgcn_s_setprio(3);
-        route_row<true>(p, L, r, epoch + 1);
+        route_row(p, L, r, epoch + 1);
         if (r != 0) __builtin_amdgcn_s_setprio(0);
         lds_inc_lane0((uint32_t*)(L.misc + kMiscRouted));  // after this wave's ids / w writes (LDS order)
       }
@@ -2161,7 +2121,7 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
       }
       if (r >= p.T) lds_wait<1>(p, (const uint32_t*)L.misc + kMiscPolled, (uint32_t)p.T, ok);
     } else {
-      for (int r = wave; r < p.T; r += kWaves) route_row<true>(p, L, r, epoch + 1);
+      for (int r = wave; r < p.T; r += kWaves) route_row(p, L, r, epoch + 1);
       __syncthreads();
       MOE_STAMP(p, 10);
       build_groups(p, L);
@@ -2289,7 +2249,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   MOE_STAMP(p, 1);
   if (blockIdx.x != 0) return;
   MOE_STAMP(p, 2);
-  for (int r = wave; r < p.T; r += kWaves) route_row<true>(p, L, r, epoch + 1);
+  for (int r = wave; r < p.T; r += kWaves) route_row(p, L, r, epoch + 1);
   __syncthreads();
   MOE_STAMP(p, 10);
   if (MODE == kModeRoute) {
@@ -2324,7 +2284,7 @@ WsLayout ws_layout(int max_rows, int E, int K, int H, int I, int Is) {
   size_t q = 0;
   w.flags = q; q = align_up(q + 4 * 1024, 256);
   w.err = q; q = align_up(q + 256, 256);
-  w.scores = q; q = align_up(q + 16 * (size_t)max_rows * E, 256);
+  w.scores = q; q = align_up(q + 16 * (size_t)max_rows * 4 * ((E + 3) / 4), 256);
   w.mid_ld = (I > Is ? I : Is);
   w.mid = q; q = align_up(q + 2 * (size_t)max_rows * (K + 1) * w.mid_ld, 256);
   w.total = q;

@@ -77,11 +77,13 @@ def test_batch_invariance_full_size(name):
 
 
 def _score_slots(layer, T, E):
-    """The fp64 scores s[r][e] the last call left in its workspace's tagged
-    slots (two 64-bit words each: tag and high half, tag and low half)."""
+    """The fp64 scores of the last call, as left in its workspace's tagged
+    slots (two 64-bit words each: tag and high half, tag and low half; a
+    row's slots in the kernel's own order), one row of slots per row."""
     torch.cuda.synchronize()
     off = 4096 + 256  # after the per-CU flags and the error word
-    w = layer.ws[off:off + 16 * T * E].cpu().numpy().view(np.uint64).reshape(T, E, 2)
+    n = 4 * ((E + 3) // 4)
+    w = layer.ws[off:off + 16 * T * n].cpu().numpy().view(np.uint64).reshape(T, n, 2)
     return ((w[..., 0] & np.uint64(0xFFFFFFFF)) << np.uint64(32)) | (w[..., 1] & np.uint64(0xFFFFFFFF))
 
 
