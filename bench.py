@@ -85,24 +85,32 @@ def note(msg):
     print(f"bench: {msg}", file=sys.stderr, flush=True)
 
 
-def time_layer(spec, copies, x, steps, warmup):
-    """Per-call times (µs) of `steps` fused calls rotating weight copies,
-    timed with HIP events on the launch stream (one event between calls),
-    plus the distinct expert count of the step."""
+def time_layer(spec, copies, x, steps, warmup, unfused=False):
+    """Per-call times (µs) of `steps` fused calls (or calls of the unfused
+    four-launch layout) rotating weight copies, timed with HIP events on the
+    launch stream (one event between calls), plus the distinct expert count
+    of the step."""
     import numpy as np
     import torch
     import mixture_experts_decode_sigmoid_amd as moe
     T = x.shape[0]
     layers = [moe.Layer(spec, dict(c, x=x), max_rows=T) for c in copies]
     out = torch.empty_like(x)
+    t_r, t_s = torch.empty_like(x), torch.empty_like(x)
+
+    def call(l):
+        if unfused:
+            moe.moe_forward_unfused(l.cfg, l.w, x, out, t_r, t_s, l.ws)
+        else:
+            l.forward(x, out)
     stream = torch.cuda.current_stream()
     for i in range(warmup):
-        layers[i % len(layers)].forward(x, out)
+        call(layers[i % len(layers)])
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ev[0].record(stream)
     for i in range(steps):
-        layers[i % len(layers)].forward(x, out)
+        call(layers[i % len(layers)])
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     per = np.array([ev[i].elapsed_time(ev[i + 1]) * 1000.0 for i in range(steps)])
@@ -293,6 +301,26 @@ def main():
             extra[name] = dict(rows=T, distinct_experts=d_t,
                                **summary(per_t, fixtures.algorithmic_bytes(spec, d_t), stream_gbs))
             note(f"{name}: {extra[name]['us_per_call']} us")
+
+        # fusion A/B: the fused pass against the unfused four-launch layout
+        # (routed MoE, shared gate/up, shared down, add), alternating rounds
+        ab = {}
+        for name in (HEADLINE,) + EXTRA:
+            sname, T, rows, seed, req = fixtures.WORKLOADS[name]
+            hd = fixtures.make_case(spec, T, seed, device="cuda", rows=rows, requests=req, experts=False)
+            cps = [dict(c, router_w=hd["router_w"], bias=hd["bias"]) for c in copies]
+            steps = max(20, args.steps // (4 if T > 8 else 2))
+            f_us, u_us = [], []
+            for _ in range(3):
+                per_f, _ = time_layer(spec, cps, hd["x"], steps, 5)
+                per_u, _ = time_layer(spec, cps, hd["x"], steps, 5, unfused=True)
+                f_us.append(float(per_f.mean()))
+                u_us.append(float(per_u.mean()))
+            f, u = min(f_us), min(u_us)
+            ab[name] = dict(rows=T, fused_us=round(f, 2), unfused_us=round(u, 2),
+                            fusion_gain_pct=round(100.0 * (u - f) / u, 2), rounds=3, statistic="best of 3 means")
+            note(f"fusion A/B {name}: fused {f:.2f} us, unfused {u:.2f} us")
+        extra["fusion_ab"] = ab
 
         del copies
         torch.cuda.empty_cache()

@@ -193,6 +193,47 @@ int moe_forward_residual(const moe_config* cfg, const moe_weights* w, const uint
 int moe_forward_noalloc(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
                         uint16_t* out, void* stream);
 
+/* The same layer in the unfused layout, for measuring what fusion gains on
+ * this GPU: four launches, as before shared-expert fusion ("Daily AI
+ * Hotspot 2026-08-21: Shared-Expert Fusion Lands on NVIDIA and AMD the Same
+ * Day", "Most Worth Your Attention Today"): (1) the routed experts (routing,
+ * distinct experts, gate/up and down, the weighted sum) into tmp_routed,
+ * bf16; (2) the shared expert's gate/up, its SwiGLU values left in the
+ * workspace; (3) its down into tmp_shared, bf16; (4) out = bf16_RNE(
+ * tmp_routed + tmp_shared) in fp32.  Each launch is the fused kernel's own
+ * stream code with the other parts left out, so the difference to
+ * moe_forward is the layout (intermediates through HBM, three more launches,
+ * the shared expert no longer overlapping routing), not the kernels.  The
+ * two roundings make it differ from moe_forward in the last bf16 bit at
+ * times.  tmp_routed and tmp_shared are [rows, H] bf16 device buffers the
+ * caller owns; out, tmp_routed, tmp_shared and x must not overlap
+ * (MOE_ERR_ALIAS).  Needs a shared expert (n_shared = 1, else
+ * MOE_ERR_SHAPE).  Everything else is as for moe_forward. */
+int moe_forward_unfused(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows, uint16_t* out,
+                        uint16_t* tmp_routed, uint16_t* tmp_shared, void* ws, size_t ws_bytes, void* stream);
+
+/* The fused layer (with an optional residual, as moe_forward_residual, or
+ * NULL) for an input x that an upstream kernel is still producing: the call
+ * may be launched before x is written.  Every CU first issues loads of
+ * weights that do not depend on x (its router rows and the first item of its
+ * first shared-expert job), then waits until the device word *x_ready
+ * reaches x_ready_value (compared as (int32_t)(*x_ready - x_ready_value) >= 0,
+ * so a counter may wrap), then acquires at device scope and only then reads
+ * x.  The producer must make x visible at device scope before it raises the
+ * word (a kernel boundary, or a release store).  The wait is bounded by
+ * max_polls polls of the word (0: the default, several hundred
+ * milliseconds); when it gives up it sets MOE_DEVERR_WAIT_TIMEOUT and the
+ * call's output is undefined.  The producer must be able to run while this
+ * call waits: the call holds every CU (see Residency), so a producer on
+ * another stream that has not started yet cannot, and the wait then times
+ * out.  This is the prior art's poll on the activations issued after the
+ * first job's weights ("sgl-amd-mono-upstream PR #27", Modifications).
+ * x_ready is device memory (4-byte aligned); NULL with rows > 0 gives
+ * MOE_ERR_NULL.  Everything else is as for moe_forward_residual. */
+int moe_forward_after(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
+                      const uint16_t* residual, uint16_t* out, void* ws, size_t ws_bytes,
+                      const uint32_t* x_ready, uint32_t x_ready_value, uint32_t max_polls, void* stream);
+
 /* Waits for `stream`, then returns the workspace's device error bits in
  * *bits (host) and clears them. */
 int moe_read_error(void* ws, void* stream, uint32_t* bits);

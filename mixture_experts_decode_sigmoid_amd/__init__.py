@@ -92,9 +92,12 @@ def lib() -> C.CDLL:
         L.moe_last_hip_error.argtypes = []
         L.moe_probe_stream_read.argtypes = [P, Z, P, I, P]
         L.moe_forward_noalloc.argtypes = [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P]
+        L.moe_forward_unfused.argtypes = [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, P, P, Z, P]
+        L.moe_forward_after.argtypes = [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, P, Z, P,
+                                         C.c_uint32, C.c_uint32, P]
         for f in ("moe_workspace_size", "moe_workspace_init", "moe_route", "moe_groups",
                   "moe_forward", "moe_forward_residual", "moe_read_error", "moe_last_hip_error",
-                  "moe_probe_stream_read", "moe_forward_noalloc"):
+                  "moe_probe_stream_read", "moe_forward_noalloc", "moe_forward_after", "moe_forward_unfused"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -102,7 +105,7 @@ def lib() -> C.CDLL:
 
 EXPORTS = ("moe_workspace_size", "moe_workspace_init", "moe_route", "moe_groups",
            "moe_forward", "moe_forward_residual", "moe_read_error", "moe_strerror", "moe_last_hip_error",
-           "moe_probe_stream_read", "moe_forward_noalloc")
+           "moe_probe_stream_read", "moe_forward_noalloc", "moe_forward_after", "moe_forward_unfused")
 
 
 def strerror(code: int) -> str:
@@ -188,6 +191,22 @@ def moe_forward_noalloc(cfg, w, x, out, stream=None):
     workspace argument, nothing allocated)."""
     _check(lib().moe_forward_noalloc(C.byref(cfg), C.byref(w), _ptr(x), int(x.shape[0]), _ptr(out),
                                      _stream(stream)), "moe_forward_noalloc")
+
+
+def moe_forward_unfused(cfg, w, x, out, tmp_routed, tmp_shared, ws, stream=None):
+    """The four-launch unfused layout of the same layer (routed MoE, shared
+    gate/up, shared down, add); tmp_routed and tmp_shared: [rows, H] bf16."""
+    _check(lib().moe_forward_unfused(C.byref(cfg), C.byref(w), _ptr(x), int(x.shape[0]), _ptr(out), _ptr(tmp_routed),
+                                     _ptr(tmp_shared), _ptr(ws), ws.numel(), _stream(stream)), "moe_forward_unfused")
+
+
+def moe_forward_after(cfg, w, x, out, ws, x_ready, x_ready_value: int, residual=None, max_polls: int = 0,
+                      stream=None):
+    """moe_forward (or with a residual) reading x only once the device word
+    x_ready (int32/uint32 tensor, element 0) reaches x_ready_value."""
+    _check(lib().moe_forward_after(C.byref(cfg), C.byref(w), _ptr(x), int(x.shape[0]), _ptr(residual), _ptr(out),
+                                   _ptr(ws), ws.numel(), _ptr(x_ready), C.c_uint32(x_ready_value & 0xFFFFFFFF),
+                                   C.c_uint32(max_polls), _stream(stream)), "moe_forward_after")
 
 
 def moe_read_error(ws, stream=None) -> int:

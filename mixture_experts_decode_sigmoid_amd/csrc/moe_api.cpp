@@ -169,7 +169,8 @@ int do_launch(const Params& p, int mode, void* stream, int dev) {
 void moe::set_last_hip(int e) { g_last_hip = e; }
 
 int moe::forward_checked(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
-                         const uint16_t* residual, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+                         const uint16_t* residual, uint16_t* out, void* ws, size_t ws_bytes, void* stream,
+                         const uint32_t* x_ready, uint32_t x_ready_value, uint32_t x_spins) {
   Params p;
   int dev = 0;
   int rc = fill(cfg, w, x, rows, ws, ws_bytes, p, kModeForward, dev);
@@ -189,6 +190,9 @@ int moe::forward_checked(const moe_config* cfg, const moe_weights* w, const uint
   if (rows == 0) return MOE_OK;
   p.out = out;
   p.residual = residual;
+  p.x_ready = x_ready;
+  p.x_ready_value = x_ready_value;
+  p.x_spins = x_spins ? x_spins : 400000u;
   return do_launch(p, kModeForward, stream, dev);
 }
 
@@ -253,6 +257,54 @@ int moe_forward_residual(const moe_config* cfg, const moe_weights* w, const uint
                          const uint16_t* residual, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
   if (rows > 0 && !residual) return MOE_ERR_NULL;
   return forward_checked(cfg, w, x, rows, residual, out, ws, ws_bytes, stream);
+}
+
+int moe_forward_unfused(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows, uint16_t* out,
+                        uint16_t* tmp_routed, uint16_t* tmp_shared, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (!cfg->n_shared) return MOE_ERR_SHAPE;
+  if (rows == 0) return rows <= cfg->max_rows ? MOE_OK : MOE_ERR_ROWS;
+  if (!out || !tmp_routed || !tmp_shared) return MOE_ERR_NULL;
+  if (!aligned16(out) || !aligned16(tmp_routed) || !aligned16(tmp_shared)) return MOE_ERR_ALIGN;
+  if (rows > 0) {
+    const size_t nb = (size_t)rows * cfg->hidden * 2;
+    const char* b[4] = {(const char*)x, (const char*)out, (const char*)tmp_routed, (const char*)tmp_shared};
+    for (int i = 0; i < 4; ++i)
+      for (int j = i + 1; j < 4; ++j)
+        if (b[i] < b[j] + nb && b[j] < b[i] + nb) return MOE_ERR_ALIAS;
+  }
+  // 1: the routed experts alone (the fused pass of a layer without a shared expert)
+  moe_config routed = *cfg;
+  routed.n_shared = 0;
+  rc = forward_checked(&routed, w, x, rows, nullptr, tmp_routed, ws, ws_bytes, stream);
+  if (rc) return rc;
+  // 2, 3: the shared expert's gate/up, then its down
+  Params p;
+  int dev = 0;
+  rc = fill(cfg, w, x, rows, ws, ws_bytes, p, kModeForward, dev);
+  if (rc == kNoRows) return MOE_OK;
+  if (rc) return rc;
+  p.out = tmp_shared;
+  rc = do_launch(p, kModeSharedUp, stream, dev);
+  if (rc) return rc;
+  rc = do_launch(p, kModeSharedDown, stream, dev);
+  if (rc) return rc;
+  // 4: the add
+  const hipError_t e = launch_add(tmp_routed, tmp_shared, out, (size_t)rows * cfg->hidden, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    g_last_hip = (int)e;
+    return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+int moe_forward_after(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
+                      const uint16_t* residual, uint16_t* out, void* ws, size_t ws_bytes,
+                      const uint32_t* x_ready, uint32_t x_ready_value, uint32_t max_polls, void* stream) {
+  if (rows > 0 && !x_ready) return MOE_ERR_NULL;
+  if (x_ready && ((uintptr_t)x_ready & 3u)) return MOE_ERR_ALIGN;
+  return forward_checked(cfg, w, x, rows, residual, out, ws, ws_bytes, stream, x_ready, x_ready_value, max_polls);
 }
 
 int moe_read_error(void* ws, void* stream, uint32_t* bits) {

@@ -20,7 +20,15 @@ constexpr int kMaxGroups = 64;            // router groups
 constexpr int kMaxSlice = 64;             // output rows per CU in down
 constexpr int kMinLds = 84 * 1024;        // LDS per workgroup: more than half a CU's, so one per CU
 
-enum Mode { kModeForward = 0, kModeRoute = 1, kModeGroups = 2 };
+enum Mode {
+  kModeForward = 0,
+  kModeRoute = 1,
+  kModeGroups = 2,
+  // the unfused layout's shared-expert launches: gate/up only (mid to the
+  // workspace), down only (from the workspace's mid to out, bf16)
+  kModeSharedUp = 3,
+  kModeSharedDown = 4,
+};
 
 // Activation loads per weight item (AL) by batch size: a job takes at most
 // 4 * AL columns (a group with more columns is split into column tiles, each
@@ -85,6 +93,11 @@ struct Params {
   double* scores;  // [T][E] score slots: two 64-bit words (tag, high half of s), (tag, low half)
   uint16_t* mid;   // [T][K+1][mid_ld] bf16
   uint64_t* timeline;  // optional phase stamps ([ncu][64]); NULL unless built with MOE_TIMELINE
+  // forward after an upstream producer: x is read only once *x_ready has
+  // reached x_ready_value (wrap-around compare); NULL: x is ready at launch
+  const uint32_t* x_ready;
+  uint32_t x_ready_value;
+  uint32_t x_spins;  // the wait's bound in polls
 };
 
 WsLayout ws_layout(int max_rows, int E, int K, int H, int I, int Is);
@@ -98,7 +111,11 @@ hipError_t launch(const Params& p, int mode, hipStream_t stream, int dev);
 // moe_forward / moe_forward_residual after their own argument checks:
 // validates, carves the workspace ws (ws_bytes) and launches.
 int forward_checked(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
-                    const uint16_t* residual, uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+                    const uint16_t* residual, uint16_t* out, void* ws, size_t ws_bytes, void* stream,
+                    const uint32_t* x_ready = nullptr, uint32_t x_ready_value = 0, uint32_t x_spins = 0);
+
+// out[i] = bf16_RNE(a[i] + b[i]) for i < n (bf16 in, fp32 sum), on stream.
+hipError_t launch_add(const uint16_t* a, const uint16_t* b, uint16_t* out, size_t n, hipStream_t stream);
 
 // Records the HIP error behind a MOE_ERR_HIP return (moe_last_hip_error).
 void set_last_hip(int e);

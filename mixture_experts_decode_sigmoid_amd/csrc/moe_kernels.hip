@@ -2024,14 +2024,17 @@ __device__ inline void sum_kphases(const Params& p, const Lds& L, const Sched& s
 
 // RES: a residual, when given, is added in fp32 after the chain, then
 // rounded once (the residual add of the unfused layout, folded in).
-template <bool RES>
+// SHONLY: the shared expert's product alone (the unfused layout's shared
+// down launch).
+template <bool RES, bool SHONLY = false>
 __device__ inline void combine(const Params& p, const Lds& L, const Sched& s) {
   for (int t = threadIdx.x; t < p.T * s.hc; t += kThreads) {
     const int r = t / s.hc, hl = t - r * s.hc;
     const size_t o = (size_t)r * p.H + s.h0 + hl;
     const uint32_t res = RES && p.residual ? p.residual[o] : 0u;  // issued ahead of the chain
     float acc = p.n_shared ? down_product(p, L, r, p.K, hl) : 0.f;
-    for (int k = 0; k < p.K; ++k) acc = fmaf(L.w[r * p.K + k], down_product(p, L, r, k, hl), acc);
+    if (!SHONLY)
+      for (int k = 0; k < p.K; ++k) acc = fmaf(L.w[r * p.K + k], down_product(p, L, r, k, hl), acc);
     if (RES && p.residual) acc += bf16_bits_to_f32(res);
     p.out[o] = (uint16_t)f32_to_bf16_rne(acc);
   }
@@ -2199,6 +2202,96 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
 }
 
 
+// The unfused layout's shared-expert launches ("Daily AI Hotspot
+// 2026-08-21", "Most Worth Your Attention Today": the shared expert's
+// gate/up and its down are launches of their own between the routed MoE
+// and the add), run by the same stream without routing: UP streams this
+// CU's shared gate/up jobs and leaves mid in the workspace (visible to the
+// next launch at the kernel boundary); otherwise the down jobs of the shared
+// group read that mid, and the shared product alone is rounded to bf16.
+template <int FMT, int AL, bool DCLAIM, bool UP>
+__device__ __forceinline__ void shared_only(char* smem) {
+  const Params& p = fresh_args();
+  const Lds L = lds_map(smem, p);
+  const int wave = wave_id(), nS = shared_jobs_here(p);
+  int jn = 0;
+  bool ok = true;
+  const Sched s = make_sched(p, 1);
+  if (wave == 0) {
+    if (UP) {
+      if (threadIdx.x == 0) L.misc[kMiscNU] = nS;
+    } else {
+      routed_tables<2>(p, L, s, nS);
+    }
+  }
+  if (threadIdx.x == 0) {
+    L.misc[0] = 1;
+    L.misc[kMiscReady] = 1;
+  }
+  __syncthreads();
+  if (UP) {
+    const int nkb = p.H / 128;
+    PhaseN ph = {};
+    ph.nw = nkb < kWaves ? nkb : kWaves;
+    RingN<ring_up<FMT, AL>()> R;
+    ring_open<FMT, 1, ring_up<FMT, AL>(), AL>(p, L, ph, R, 0, nS, ok);
+    ring_fill<FMT, 1, false, ring_up<FMT, AL>(), AL>(p, L, ph, R, nS, ok);
+    ring_run<FMT, 1, false, ring_up<FMT, AL>(), AL>(p, L, ph, R, 0, nS, jn, ok);
+    return;
+  }
+  const int nD = lds_ldi_uniform(L.misc + kMiscND);
+  zero_partials(L, (size_t)p.wpt * p.T * (p.K + 1) * p.pitch);
+  __syncthreads();
+  RingN<kRingDD> R;
+  if (!DCLAIM) {
+    const PhaseN ph = down_phase(s.h0, s.hc, s.nrt, wave % s.nrt_p, wave / s.nrt_p, 31 - __builtin_clz(s.kph));
+    const int kend = ph.nlive > 0 ? p.qcap + nD : p.qcap;
+    ring_open<FMT, 2, kRingDD, AL>(p, L, ph, R, p.qcap, kend, ok);
+    ring_fill<FMT, 2, false, kRingDD, AL>(p, L, ph, R, kend, ok);
+    ring_run<FMT, 2, false, kRingDD, AL>(p, L, ph, R, p.qcap, kend, jn, ok);
+  } else {
+    const PhaseN ph = down_phase(s.h0, s.hc, s.nrt, 0, 0, 31 - __builtin_clz(s.kph));
+    const int nunits = s.hc > 0 ? nD * s.nrt : 0;
+    ring_open<FMT, 3, kRingDD, AL>(p, L, ph, R, -1, nunits, ok);
+    ring_fill<FMT, 3, false, kRingDD, AL>(p, L, ph, R, nunits, ok);
+    ring_run<FMT, 3, false, kRingDD, AL>(p, L, ph, R, 0, nunits, jn, ok);
+  }
+  __syncthreads();
+  sum_kphases(p, L, s);
+  combine<false, true>(p, L, s);
+}
+
+// A forward after an upstream producer (moe_forward_after): each wave first
+// issues loads of weights that do not depend on x, its piece of this CU's
+// router row and of the first item of the CU's first shared-expert job, so
+// they reach the caches while the producer finishes; then it polls the
+// ready word (agent scope, bounded: on timeout the error bit is set and the
+// call runs on), then acquires at agent scope before any load of x.
+__device__ inline void wait_x_ready(const Params& p) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+  if ((int)blockIdx.x < p.E) {
+    const int ch = p.H / kWaves, ngrp = ch >> 3;
+    a = ld16(p.router_w + (size_t)blockIdx.x * p.H + (size_t)wave * ch + 8 * (lane < ngrp ? lane : ngrp - 1));
+  }
+  if (p.n_shared && (int)blockIdx.x < p.Is / 8 && wave < p.H / 128) {
+    const int row = lane & 15, t = blockIdx.x;
+    const int lrow = row < 8 ? 8 * t + row : p.Is + 8 * t + row - 8;
+    b = ld16(p.sh_wgu + (size_t)lrow * p.H + 128 * wave + 32 * (lane >> 4));
+  }
+  for (uint32_t spins = 0;;) {
+    const uint32_t v = __hip_atomic_load(p.x_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((int32_t)(v - p.x_ready_value) >= 0) break;
+    if (++spins > p.x_spins) {
+      if (lane == 0) set_err(p.err, kErrTimeout);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  asm volatile("" ::"v"(a), "v"(b));  // (the early loads are complete by now)
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
 // NARROW picks the stream by batch size (see stream_al): 2 for one
 // activation load per item, 3 for two (down jobs split over the waves by
 // K-phase), 4 above kKsplitRows rows (two loads, down jobs claimed whole).
@@ -2210,6 +2303,14 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   const int tid = threadIdx.x, wave = wave_id();
 
   MOE_STAMP(p, 0);
+  if (MODE == kModeSharedUp || MODE == kModeSharedDown) {
+    if (tid < 64) L.ctl[tid] = 0u;
+    stream_init(p, L, shared_jobs_here(p));
+    __syncthreads();
+    constexpr int AL = NARROW == 2 ? 1 : 2;
+    shared_only<FMT, AL, NARROW == 4, MODE == kModeSharedUp>(smem);
+    return;
+  }
   if (MODE == kModeForward) {
     // Every wave reads the epoch for itself and first needs it to tag its
     // scores, after the router loads have come in.  The stream's LDS words
@@ -2220,6 +2321,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
     if (tid < 64) L.ctl[tid] = 0u;
     stream_init(p, L, shared_jobs_here(p));
     __syncthreads();
+    if (p.x_ready) wait_x_ready(p);
     if (p.T < kWaves) {
       router_logits(p, L, ep, 1u);
       // the logit partials lie in wave 0's routing scratch (wave 0 reads
@@ -2325,18 +2427,33 @@ static hipError_t launch_one(const Params& p, hipStream_t stream, int dev) {
   return hipGetLastError();
 }
 
-template <int FMT>
+template <int MODE, int FMT>
 static hipError_t launch_forward(const Params& p, hipStream_t stream, int dev) {
-  if (p.T > kKsplitRows) return launch_one<kModeForward, FMT, 4>(p, stream, dev);  // (stream_al: 2)
-  return stream_al(p.T) == 1 ? launch_one<kModeForward, FMT, 2>(p, stream, dev)
-                             : launch_one<kModeForward, FMT, 3>(p, stream, dev);
+  if (p.T > kKsplitRows) return launch_one<MODE, FMT, 4>(p, stream, dev);  // (stream_al: 2)
+  return stream_al(p.T) == 1 ? launch_one<MODE, FMT, 2>(p, stream, dev) : launch_one<MODE, FMT, 3>(p, stream, dev);
 }
 
 hipError_t launch(const Params& p, int mode, hipStream_t stream, int dev) {
   if (mode == kModeForward)
-    return p.routed_fmt == 0 ? launch_forward<0>(p, stream, dev) : launch_forward<1>(p, stream, dev);
+    return p.routed_fmt == 0 ? launch_forward<kModeForward, 0>(p, stream, dev)
+                             : launch_forward<kModeForward, 1>(p, stream, dev);
+  // the shared expert is FP8 in every format
+  if (mode == kModeSharedUp) return launch_forward<kModeSharedUp, 0>(p, stream, dev);
+  if (mode == kModeSharedDown) return launch_forward<kModeSharedDown, 0>(p, stream, dev);
   if (mode == kModeRoute) return launch_one<kModeRoute, 0>(p, stream, dev);
   return launch_one<kModeGroups, 0>(p, stream, dev);
+}
+
+__global__ void add_bf16(const uint16_t* __restrict__ a, const uint16_t* __restrict__ b, uint16_t* __restrict__ out,
+                         size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    out[i] = (uint16_t)f32_to_bf16_rne(bf16_bits_to_f32(a[i]) + bf16_bits_to_f32(b[i]));
+}
+
+hipError_t launch_add(const uint16_t* a, const uint16_t* b, uint16_t* out, size_t n, hipStream_t stream) {
+  const size_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+  hipLaunchKernelGGL(add_bf16, dim3((unsigned)(blocks ? blocks : 1)), dim3(256), 0, stream, a, b, out, n);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -93,3 +93,30 @@ def test_launch_error_code_and_probe_argument_errors():
     assert L.moe_probe_stream_read(C.c_void_p(0x1008), 1 << 20, sink, 4, None) == moe.MOE_ERR_ALIGN
     assert L.moe_probe_stream_read(C.c_void_p(0x1000), 1000, sink, 4, None) == moe.MOE_ERR_ALIGN
     assert L.moe_probe_stream_read(C.c_void_p(0x1000), 1 << 20, sink, 0, None) == moe.MOE_ERR_SHAPE
+
+
+def test_forward_after_argument_errors():
+    L = moe.lib()
+    cfg = _cfg()
+    w = moe.MoeWeights(*([0x10000] * 10))
+    x, out, ws = C.c_void_p(0x1000), C.c_void_p(0x2000), C.c_void_p(0x4000)
+    # a NULL or misaligned ready word is rejected before any launch
+    assert L.moe_forward_after(C.byref(cfg), C.byref(w), x, 1, None, out, ws, 1 << 30, None, 1, 0, None) == moe.MOE_ERR_NULL
+    assert L.moe_forward_after(C.byref(cfg), C.byref(w), x, 1, None, out, ws, 1 << 30, C.c_void_p(0x3002), 1, 0,
+                               None) == moe.MOE_ERR_ALIGN
+    # rows == 0 is a no-op even without a word
+    assert L.moe_forward_after(C.byref(cfg), C.byref(w), x, 0, None, out, ws, 1 << 30, None, 1, 0, None) == moe.MOE_OK
+
+
+def test_forward_unfused_argument_errors():
+    L = moe.lib()
+    cfg = _cfg()
+    w = moe.MoeWeights(*([0x10000] * 10))
+    x, out, ws = C.c_void_p(0x1000), C.c_void_p(0x100000), C.c_void_p(0x4000)
+    tr, ts = C.c_void_p(0x200000), C.c_void_p(0x300000)
+    assert L.moe_forward_unfused(C.byref(cfg), C.byref(w), x, 1, out, None, ts, ws, 1 << 30, None) == moe.MOE_ERR_NULL
+    assert L.moe_forward_unfused(C.byref(cfg), C.byref(w), x, 1, out, out, ts, ws, 1 << 30, None) == moe.MOE_ERR_ALIAS
+    assert L.moe_forward_unfused(C.byref(cfg), C.byref(w), x, 1, out, C.c_void_p(0x200008), ts, ws, 1 << 30,
+                                 None) == moe.MOE_ERR_ALIGN
+    cfg.n_shared = 0
+    assert L.moe_forward_unfused(C.byref(cfg), C.byref(w), x, 1, out, tr, ts, ws, 1 << 30, None) == moe.MOE_ERR_SHAPE

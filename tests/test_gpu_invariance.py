@@ -319,3 +319,56 @@ def test_graph_replay_matches_eager(T):
         assert np.array_equal(fixtures.bits16(out), eager)
         assert np.array_equal(run_forward(layer, x), eager)
     assert layer.read_error() == 0
+
+
+@pytest.mark.parametrize("T", [1, 8, 37])
+def test_forward_after_ready_word(T):
+    """moe_forward_after with the ready word raised by a producer earlier on
+    the same stream (a copy of x, then a fill of the word) gives moe_forward's
+    output bit for bit; so does a counter that wrapped past the value, and a
+    residual is added as in moe_forward_residual."""
+    say(f"forward after ready word T={T}")
+    spec = fixtures.spec_with("tiny", **MID)
+    case = gpu_case(spec, T, 70 + T, rows="corr", requests=max(1, T // 4))
+    layer = _layer(spec, case, T)
+    ref = run_forward(layer, case["x"])
+    word = torch.zeros(1, dtype=torch.int32, device="cuda")
+    x2 = torch.empty_like(case["x"])
+    x2.copy_(case["x"])
+    word.fill_(5)
+    out = torch.empty_like(x2)
+    moe.moe_forward_after(layer.cfg, layer.w, x2, out, layer.ws, word, 5)
+    torch.cuda.synchronize()
+    assert layer.read_error() == 0
+    assert np.array_equal(fixtures.bits16(out), ref)
+    word.fill_(3)  # 0xFFFFFFF8 + 11 wraps to 3: reached
+    out2 = torch.empty_like(x2)
+    moe.moe_forward_after(layer.cfg, layer.w, x2, out2, layer.ws, word, 0xFFFFFFF8)
+    torch.cuda.synchronize()
+    assert layer.read_error() == 0
+    assert np.array_equal(fixtures.bits16(out2), ref)
+    res = torch.randn(T, spec["hidden"], generator=torch.Generator().manual_seed(T)).bfloat16().cuda()
+    want = fixtures.bits16(layer.forward(case["x"], residual=res))
+    out3 = torch.empty_like(x2)
+    moe.moe_forward_after(layer.cfg, layer.w, x2, out3, layer.ws, word, 3, residual=res)
+    torch.cuda.synchronize()
+    assert layer.read_error() == 0
+    assert np.array_equal(fixtures.bits16(out3), want)
+
+
+def test_forward_after_word_never_raised():
+    """A ready word the host never raises: every CU's bounded wait (64 polls
+    here) gives up, the timeout bit is set and the call ends; the next
+    ordinary call on a re-initialised workspace is unaffected."""
+    say("forward after: word never raised")
+    spec = fixtures.spec_with("tiny", **MID)
+    case = gpu_case(spec, 4, 79)
+    layer = _layer(spec, case, 4)
+    ref = run_forward(layer, case["x"])
+    word = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(case["x"])
+    moe.moe_forward_after(layer.cfg, layer.w, case["x"], out, layer.ws, word, 7, max_polls=64)
+    torch.cuda.synchronize()
+    assert layer.read_error() & moe.MOE_DEVERR_WAIT_TIMEOUT
+    moe.moe_workspace_init(layer.ws)
+    assert np.array_equal(run_forward(layer, case["x"]), ref)

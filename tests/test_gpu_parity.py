@@ -253,3 +253,43 @@ def test_residual_single_rounding_bits(name, over, T, seed, rows):
     r = np.abs(bf16_to_f64(got))
     ulp = np.where(p > 0, np.exp2(np.floor(np.log2(np.where(p > 0, p, 1.0))) - 7), 2.0 ** -133)
     assert np.all(r <= ulp / 2)
+
+
+# The unfused four-launch layout (routed MoE, shared gate/up, shared down,
+# add) of the same layer: within the tolerance of the oracle, and within one
+# bf16 rounding of the fused output (its routed and shared sums are rounded
+# to bf16 before the add).
+UNFUSED = [
+    ("tiny_t1", dict(), 1, 81, "iid"),
+    ("v3r_t8", V3R, 8, 82, "corr"),
+    ("multichunk_ragged_t9", dict(hidden=1152, inter=640, shared_inter=384, n_experts=24, top_k=5), 9, 83, "corr"),
+    ("v3r_t37", V3R, 37, 84, "iid"),
+    ("mxfp4_t16", dict(hidden=2048, inter=1536, shared_inter=512, n_experts=16, top_k=6, routed_fmt=1, bias_bf16=1),
+     16, 85, "corr"),
+]
+
+
+@pytest.mark.parametrize("name,over,T,seed,rows", UNFUSED, ids=[u[0] for u in UNFUSED])
+def test_unfused_layout(name, over, T, seed, rows):
+    say(f"unfused {name} T={T}")
+    spec = _spec(over)
+    case = gpu_case(spec, T, seed, rows=rows, requests=max(1, T // 4))
+    layer = moe.Layer(spec, case, max_rows=T)
+    fused = run_forward(layer, case["x"])
+    out = torch.empty_like(case["x"])
+    t_r, t_s = torch.empty_like(out), torch.empty_like(out)
+    moe.moe_forward_unfused(layer.cfg, layer.w, case["x"], out, t_r, t_s, layer.ws)
+    torch.cuda.synchronize()
+    assert layer.read_error() == 0
+    got = fixtures.bits16(out)
+    o64, _ = oracle_rows(spec, case, range(T))
+    rel, mx = parity(got, o64, list(range(T)))
+    say(f"  rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert rel <= REL_L2 and mx <= MAX_ABS
+    # the two paths differ only by the roundings of the two partial sums
+    f, u = bf16_to_f64(fused), bf16_to_f64(got)
+    assert np.max(np.abs(f - u)) <= 4 * 2.0 ** -8 * max(1.0, np.max(np.abs(f)))
+    # the routed part alone is the fused pass of the layer without a shared expert
+    spec_r = dict(spec, n_shared=0)
+    layer_r = moe.Layer(spec_r, case, max_rows=T)
+    assert np.array_equal(fixtures.bits16(t_r), run_forward(layer_r, case["x"]))
