@@ -34,7 +34,8 @@ class Cfg(C.Structure):
     _fields_ = [("hidden", C.c_int), ("inter", C.c_int), ("shared_inter", C.c_int),
                 ("n_experts", C.c_int), ("top_k", C.c_int), ("n_group", C.c_int),
                 ("topk_group", C.c_int), ("n_shared", C.c_int),
-                ("routed_scale", C.c_double), ("routed_fmt", C.c_int), ("bias_bf16", C.c_int)]
+                ("routed_scale", C.c_double), ("routed_fmt", C.c_int), ("bias_bf16", C.c_int),
+                ("expert_first", C.c_int), ("expert_count", C.c_int)]
 
 
 _lib = None
@@ -86,7 +87,8 @@ def make_cfg(spec) -> Cfg:
     return Cfg(int(spec["hidden"]), int(spec["inter"]), int(spec["shared_inter"]),
                int(spec["n_experts"]), int(spec["top_k"]), int(spec["n_group"]),
                int(spec["topk_group"]), int(spec["n_shared"]), float(spec["routed_scale"]),
-               int(spec["routed_fmt"]), int(spec["bias_bf16"]))
+               int(spec["routed_fmt"]), int(spec["bias_bf16"]),
+               int(spec.get("expert_first", 0)), int(spec.get("expert_count", 0)))
 
 
 def dec_bf16(v): return lib().oracle_dec_bf16(int(v))

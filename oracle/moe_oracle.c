@@ -127,6 +127,8 @@ static int cfg_ok(const oracle_cfg* c) {
   if (c->n_group > 1 && c->n_experts / c->n_group < 2) return 0;
   if (c->n_group > 1 && c->topk_group * (c->n_experts / c->n_group) < c->top_k) return 0;
   if (c->n_shared != 0 && c->n_shared != 1) return 0;
+  if (c->expert_first < 0 || c->expert_count < 0 || c->expert_first + c->expert_count > c->n_experts) return 0;
+  if (c->expert_count == 0 && c->expert_first != 0) return 0;
   if (c->n_shared && (c->shared_inter <= 0 || c->shared_inter % 128 || c->hidden % 128)) return 0;
   if (c->routed_fmt == ORACLE_FMT_FP8_B128) {
     if (c->hidden % 128 || c->inter % 128) return 0;
@@ -341,7 +343,11 @@ void oracle_expert_ffn(int fmt, int H, int Iexp,
 /* out[r,:] = y_shared(x_r) + sum_{p=0..K-1} w[r,p] * y_{ids[r,p]}(x_r), in
  * fp64 with the shared term first, then rounded once to bf16 (the hotspot
  * page: fp32-or-better accumulation, bf16 written once; the shared expert is
- * applied to every token with weight 1). */
+ * applied to every token with weight 1).
+ * Expert parallelism (the expert-parallel all-to-all backends the hotspot
+ * page mentions): with a range of held experts, the sum runs over the picks
+ * inside it only, in the same order; the full layer is the sum of the
+ * shares of a partition of the experts, the shared term counted in one. */
 int oracle_forward_rows(const oracle_cfg* cfg, const uint16_t* x, int T,
                         const int32_t* rows, int nrows,
                         const uint16_t* router_w, const void* bias,
@@ -377,8 +383,11 @@ int oracle_forward_rows(const oracle_cfg* cfg, const uint16_t* x, int T,
                         sh_w_down, sh_s_down, xr, y, NULL);
       for (int h = 0; h < H; ++h) acc[h] = y[h];
     }
+    const int e_lo = cfg->expert_first;
+    const int e_hi = cfg->expert_count ? cfg->expert_first + cfg->expert_count : cfg->n_experts;
     for (int p = 0; p < K; ++p) {
       const int e = ids[p];
+      if (e < e_lo || e >= e_hi) continue; /* another device's expert */
       if (!w_gate_up[e] || !s_gate_up[e] || !w_down[e] || !s_down[e]) { rc = -2; break; }
       oracle_expert_ffn(cfg->routed_fmt, H, I, w_gate_up[e], s_gate_up[e], w_down[e], s_down[e],
                         xr, y, NULL);

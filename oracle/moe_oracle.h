@@ -52,6 +52,12 @@ typedef struct {
   double routed_scale;
   int routed_fmt;    /* ORACLE_FMT_*; the shared expert is always FP8_B128 */
   int bias_bf16;     /* 0: bias is fp32[E]; 1: bias is bf16[E] */
+  /* Expert parallelism: the routed experts this evaluation holds are
+   * expert_first .. expert_first + expert_count - 1 (count 0: all E).  Rows
+   * are routed over all E experts; picks outside the range contribute
+   * nothing here (another device's share of the layer). */
+  int expert_first;
+  int expert_count;
 } oracle_cfg;
 
 /* ---- format decode (one code -> exact fp64 value) ---- */

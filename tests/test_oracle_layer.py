@@ -252,3 +252,56 @@ def test_residual_is_rounded_once(orc):
     want = np.array([_bf16.brute_rne(float(v), codes, vals) for v in err.ravel()], np.uint16).reshape(ob.shape)
     assert np.array_equal(ob, want)
     assert np.count_nonzero(ob & np.uint16(0x7FFF)) > 0.95 * ob.size
+
+
+# ---------------------------------------------------------------- expert parallelism
+def test_expert_range_all_is_the_layer(orc):
+    """Holding every expert (count E, or 0 meaning all) is the whole layer."""
+    spec, h = _tiny(T=3)
+    full64, fullb = orc.forward(spec, h)
+    for first, count in ((0, 16), (0, 0)):
+        o64, ob = orc.forward(dict(spec, expert_first=first, expert_count=count), h)
+        assert np.array_equal(o64, full64) and np.array_equal(ob, fullb)
+
+
+def test_expert_shards_sum_to_the_layer(orc):
+    """Four shards of four experts each, the shared expert in the first: the
+    fp64 shares add up to the whole layer (up to the order of the fp64
+    additions); a share is zero for a row none of whose picks it holds."""
+    spec, h = _tiny(T=6)
+    full64, _ = orc.forward(spec, h)
+    ids, _, _, _ = orc.route(spec, h["x"], h["router_w"], h["bias"])
+    total = np.zeros_like(full64)
+    for s in range(4):
+        sp = dict(spec, expert_first=4 * s, expert_count=4, n_shared=1 if s == 0 else 0)
+        o64, _ = orc.forward(sp, h)
+        total += o64
+        if s:
+            for r in range(6):
+                if not any(4 * s <= e < 4 * s + 4 for e in ids[r]):
+                    assert np.all(o64[r] == 0.0)
+    assert np.max(np.abs(total - full64)) <= 1e-12 * np.max(np.abs(full64))
+
+
+def test_expert_shard_without_local_picks_is_the_shared_expert(orc):
+    """A row none of whose picks lies in the held range gets exactly the
+    shared expert's output (the layer with routed_scale 0)."""
+    spec, h = _tiny(T=6)
+    ids, _, _, _ = orc.route(spec, h["x"], h["router_w"], h["bias"])
+    shared64, _ = orc.forward(dict(spec, routed_scale=0.0), h)
+    checked = 0
+    for s in range(4):
+        sp = dict(spec, expert_first=4 * s, expert_count=4)
+        o64, _ = orc.forward(sp, h)
+        for r in range(6):
+            if not any(4 * s <= e < 4 * s + 4 for e in ids[r]):
+                assert np.array_equal(o64[r], shared64[r])
+                checked += 1
+    assert checked > 0
+
+
+def test_expert_range_checked(orc):
+    spec, h = _tiny(T=1)
+    for first, count in ((-1, 4), (14, 4), (3, 0)):
+        with pytest.raises(ValueError):
+            orc.forward(dict(spec, expert_first=first, expert_count=count), h)
