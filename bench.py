@@ -38,8 +38,9 @@ N_COPIES = 4
 HEADLINE = "v3_t1"
 EXTRA = ("v3_t8", "v3_t64")
 # workloads with weights of their own: the tiny layer, the V4-style MXFP4
-# layer, and one GPU's share of the V3 layer under 8-way tensor parallelism
-EXTRA_OWN = ("tiny_t1", "v4_t16", "v3tp8_t1", "v3tp8_t8")
+# layer, and one GPU's share of the V3 layer under 8- and 4-way tensor
+# parallelism and under 8-way expert parallelism
+EXTRA_OWN = ("tiny_t1", "v4_t16", "v3tp8_t1", "v3tp8_t8", "v3tp4_t1", "v3tp4_t8", "v3ep8_t8", "v3ep8_t64")
 STREAM_BYTES = 4 << 30
 
 
@@ -92,6 +93,7 @@ def time_layer(spec, copies, x, steps, warmup, unfused=False):
     of the step."""
     import numpy as np
     import torch
+    import fixtures
     import mixture_experts_decode_sigmoid_amd as moe
     T = x.shape[0]
     layers = [moe.Layer(spec, dict(c, x=x), max_rows=T) for c in copies]
@@ -118,7 +120,7 @@ def time_layer(spec, copies, x, steps, warmup, unfused=False):
     if any(errs):
         raise RuntimeError(f"device error bits {errs}")
     ids, _ = layers[0].route(x)
-    distinct = len(set(ids.cpu().view(-1).tolist()))
+    distinct = fixtures.held_distinct(spec, ids.cpu().view(-1).tolist())
     return per, distinct
 
 

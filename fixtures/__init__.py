@@ -53,6 +53,16 @@ SPECS = {
     "v3tp8": dict(hidden=7168, inter=256, shared_inter=256, n_experts=256, top_k=8,
                   n_group=8, topk_group=4, n_shared=1, routed_scale=2.5,
                   routed_fmt=FMT_FP8_B128, bias_bf16=0),
+    # ... and under 4-way tensor parallelism (2048 / 4)
+    "v3tp4": dict(hidden=7168, inter=512, shared_inter=512, n_experts=256, top_k=8,
+                  n_group=8, topk_group=4, n_shared=1, routed_scale=2.5,
+                  routed_fmt=FMT_FP8_B128, bias_bf16=0),
+    # one GPU's share of the V3 layer under 8-way expert parallelism: routed
+    # experts 0..31 (the first routing group) and the shared expert; every
+    # row is routed over all 256 experts
+    "v3ep8": dict(hidden=7168, inter=2048, shared_inter=2048, n_experts=256, top_k=8,
+                  n_group=8, topk_group=4, n_shared=1, routed_scale=2.5,
+                  routed_fmt=FMT_FP8_B128, bias_bf16=0, expert_first=0, expert_count=32),
 }
 
 # The workloads: (spec, rows, row recipe, seed, requests).
@@ -64,6 +74,12 @@ WORKLOADS = {
     "v4_t16": ("v4", 16, "corr", 5, 4),
     "v3tp8_t1": ("v3tp8", 1, "iid", 6, 1),
     "v3tp8_t8": ("v3tp8", 8, "corr", 7, 2),
+    "v3tp4_t1": ("v3tp4", 1, "iid", 10, 1),
+    "v3tp4_t8": ("v3tp4", 8, "corr", 11, 2),
+    # 8 and 64 rows (8 data-parallel ranks of 8 rows each) at one
+    # expert-parallel device
+    "v3ep8_t8": ("v3ep8", 8, "corr", 8, 2),
+    "v3ep8_t64": ("v3ep8", 64, "iid", 9, 64),
 }
 
 
@@ -71,6 +87,19 @@ def spec_with(name: str, **over) -> dict:
     s = dict(SPECS[name])
     s.update(over)
     return s
+
+
+def held(spec: dict) -> tuple[int, int]:
+    """(first, count) of the routed experts a device holds: the spec's
+    expert range, or all E experts."""
+    c = int(spec.get("expert_count", 0))
+    return (int(spec.get("expert_first", 0)), c) if c else (0, int(spec["n_experts"]))
+
+
+def held_distinct(spec: dict, ids) -> int:
+    """Distinct held experts among the picks `ids` (any iterable of ints)."""
+    f, c = held(spec)
+    return len(set(int(e) for e in ids if f <= int(e) < f + c))
 
 
 def _gen(device, seed):
@@ -119,15 +148,18 @@ def _quant(w, fmt):
 
 
 def make_case(spec: dict, T: int, seed: int, device="cpu", rows: str = "iid",
-              requests: int = 1, expert_chunk: int = 16, experts: bool = True) -> dict:
+              requests: int = 1, experts: bool = True) -> dict:
     """Draws one seeded case.  Returns torch tensors on `device`:
     x [T,H] bf16, router_w [E,H] bf16, bias [E] fp32|bf16,
     w_gate_up [E,2I,H] u8 (or [E,2I,H/2] for MXFP4), s_gate_up,
     w_down [E,H,I] u8 (or [E,H,I/2]), s_down, and the shared expert's
     sh_w_gate_up [2I_s,H] u8, sh_s_gate_up, sh_w_down [H,I_s] u8, sh_s_down.
-    experts=False stops after the router weights, bias and activations."""
+    experts=False stops after the router weights, bias and activations.
+    With an expert range in the spec (expert_first, expert_count) the routed
+    tensors hold those experts only (same draws as the whole layer's)."""
     H, I, Is, E = spec["hidden"], spec["inter"], spec["shared_inter"], spec["n_experts"]
     fmt = spec["routed_fmt"]
+    ef, ec = held(spec)
     g = _gen(device, seed)
     dev = torch.device(device)
     rw = (torch.randn(E, H, generator=g, device=dev) / math.sqrt(H)).to(torch.bfloat16)
@@ -154,23 +186,24 @@ def make_case(spec: dict, T: int, seed: int, device="cpu", rows: str = "iid",
         case["sh_w_down"], case["sh_s_down"] = quant_fp8_b128(wsh)
         del wsh
     if fmt == FMT_FP8_B128:
-        wgu = torch.empty(E, 2 * I, H, dtype=torch.uint8, device=dev)
-        sgu = torch.empty(E, 2 * I // 128, H // 128, dtype=torch.float32, device=dev)
-        wd = torch.empty(E, H, I, dtype=torch.uint8, device=dev)
-        sd = torch.empty(E, H // 128, I // 128, dtype=torch.float32, device=dev)
+        wgu = torch.empty(ec, 2 * I, H, dtype=torch.uint8, device=dev)
+        sgu = torch.empty(ec, 2 * I // 128, H // 128, dtype=torch.float32, device=dev)
+        wd = torch.empty(ec, H, I, dtype=torch.uint8, device=dev)
+        sd = torch.empty(ec, H // 128, I // 128, dtype=torch.float32, device=dev)
     else:
-        wgu = torch.empty(E, 2 * I, H // 2, dtype=torch.uint8, device=dev)
-        sgu = torch.empty(E, 2 * I, H // 32, dtype=torch.uint8, device=dev)
-        wd = torch.empty(E, H, I // 2, dtype=torch.uint8, device=dev)
-        sd = torch.empty(E, H, I // 32, dtype=torch.uint8, device=dev)
-    for e0 in range(0, E, expert_chunk):
-        e1 = min(E, e0 + expert_chunk)
-        for e in range(e0, e1):
-            w = torch.randn(2 * I, H, generator=g, device=dev) * 0.02
-            wgu[e], sgu[e] = _quant(w, fmt)
-            w = torch.randn(H, I, generator=g, device=dev) * 0.02
-            wd[e], sd[e] = _quant(w, fmt)
-            del w
+        wgu = torch.empty(ec, 2 * I, H // 2, dtype=torch.uint8, device=dev)
+        sgu = torch.empty(ec, 2 * I, H // 32, dtype=torch.uint8, device=dev)
+        wd = torch.empty(ec, H, I // 2, dtype=torch.uint8, device=dev)
+        sd = torch.empty(ec, H, I // 32, dtype=torch.uint8, device=dev)
+    # experts past the held range need no draws
+    for e in range(ef + ec):
+        w = torch.randn(2 * I, H, generator=g, device=dev) * 0.02
+        if e >= ef:
+            wgu[e - ef], sgu[e - ef] = _quant(w, fmt)
+        w = torch.randn(H, I, generator=g, device=dev) * 0.02
+        if e >= ef:
+            wd[e - ef], sd[e - ef] = _quant(w, fmt)
+        del w
     case.update(w_gate_up=wgu, s_gate_up=sgu, w_down=wd, s_down=sd)
     return case
 
@@ -187,14 +220,21 @@ def bits16(t: torch.Tensor) -> np.ndarray:
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def host_case(case: dict, experts=None) -> dict:
+def host_case(case: dict, experts=None, spec=None) -> dict:
     """Host (numpy) copy for the oracle.  Only experts listed in `experts`
     are copied (others None), so a full-size case needs host memory only for
-    the experts a step uses."""
-    E = case["w_gate_up"].shape[0]
+    the experts a step uses.  With a spec that holds an expert range, the
+    lists are indexed by global expert (length E) and only held experts can
+    be copied."""
+    if spec is not None:
+        E = int(spec["n_experts"])
+        ef, ec = held(spec)
+    else:
+        E = case["w_gate_up"].shape[0]
+        ef, ec = 0, E
     if experts is None:
-        experts = range(E)
-    experts = set(int(e) for e in experts)
+        experts = range(ef, ef + ec)
+    experts = set(int(e) for e in experts if ef <= int(e) < ef + ec)
     out = dict(x=bits16(case["x"]), router_w=bits16(case["router_w"]))
     b = case["bias"]
     out["bias"] = bits16(b) if b.dtype == torch.bfloat16 else b.cpu().numpy()
@@ -202,7 +242,7 @@ def host_case(case: dict, experts=None) -> dict:
         if k in case:
             out[k] = case[k].cpu().numpy()
     for k in ("w_gate_up", "s_gate_up", "w_down", "s_down"):
-        out[k] = [case[k][e].cpu().numpy() if e in experts else None for e in range(E)]
+        out[k] = [case[k][e - ef].cpu().numpy() if e in experts else None for e in range(E)]
     return out
 
 

@@ -109,16 +109,29 @@ typedef struct {
   int shared_fmt;    /* moe_wfmt of the shared expert: MOE_FMT_FP8_B128 only */
   int bias_dtype;    /* moe_bias_dtype */
   int max_rows;      /* largest rows a call will pass; sizes the workspace; <= 64 */
+  /* A device's share under expert parallelism: the routed experts
+   * [expert_first, expert_first + expert_count) are held here.  Every row is
+   * still routed over all E experts with the weights normalised over all K
+   * picks; the output sums, in pick order, only the terms of the picks held
+   * here, plus the shared expert's when n_shared is 1 (set it on one device
+   * of the group only).  The devices' outputs add up to the layer.  The
+   * routed weight arrays then hold these experts only (E_w = expert_count).
+   * expert_count 0 (with expert_first 0) means all E experts (E_w = E).
+   * Reading of "Daily AI Hotspot 2026-08-21", section "Most Worth Your
+   * Attention Today", which names expert-parallel all-to-all backends for
+   * these layers without describing the split. */
+  int expert_first;
+  int expert_count;
 } moe_config;
 
 /* Weights (host struct of device pointers). */
 typedef struct {
   const uint16_t* router_w;   /* [E, H] bf16 */
   const void* bias;           /* [E] fp32 or bf16 (bias_dtype) */
-  const uint8_t* w_gate_up;   /* [E, 2I, H] FP8, or [E, 2I, H/2] MXFP4 */
-  const void* s_gate_up;      /* [E, 2I/128, H/128] fp32, or [E, 2I, H/32] E8M0 bytes */
-  const uint8_t* w_down;      /* [E, H, I] FP8, or [E, H, I/2] MXFP4 */
-  const void* s_down;         /* [E, H/128, I/128] fp32, or [E, H, I/32] E8M0 bytes */
+  const uint8_t* w_gate_up;   /* [E_w, 2I, H] FP8, or [E_w, 2I, H/2] MXFP4 (E_w: see expert_count) */
+  const void* s_gate_up;      /* [E_w, 2I/128, H/128] fp32, or [E_w, 2I, H/32] E8M0 bytes */
+  const uint8_t* w_down;      /* [E_w, H, I] FP8, or [E_w, H, I/2] MXFP4 */
+  const void* s_down;         /* [E_w, H/128, I/128] fp32, or [E_w, H, I/32] E8M0 bytes */
   const uint8_t* sh_w_gate_up;/* [2I_s, H] FP8 (n_shared == 1) */
   const float* sh_s_gate_up;  /* [2I_s/128, H/128] fp32 */
   const uint8_t* sh_w_down;   /* [H, I_s] FP8 */
@@ -147,7 +160,9 @@ int moe_route(const moe_config* cfg, const moe_weights* w, const uint16_t* x, in
  *   then expert[G] (-1 for the shared group), ncols[G], col_start[G],
  *   then cols[sum ncols] = row*16 + slot (slot K = the shared expert).
  * Groups: the shared expert first (if any), then routed experts in order of
- * first use over u = row*K + slot; a group's columns in ascending u. */
+ * first use over u = row*K + slot; a group's columns in ascending u.  With an
+ * expert range (expert_count > 0) only the experts held here form groups;
+ * expert[] keeps the global expert index. */
 int moe_groups(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
                int32_t* groups_out, void* ws, size_t ws_bytes, void* stream);
 
@@ -192,6 +207,18 @@ int moe_forward_residual(const moe_config* cfg, const moe_weights* w, const uint
  * Arguments and return codes are as for moe_forward. */
 int moe_forward_noalloc(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows,
                         uint16_t* out, void* stream);
+
+/* The layer for more rows than one call takes (prefill-sized batches): the
+ * fused pass over consecutive chunks of cfg->max_rows rows (the last one
+ * shorter), each a launch of its own on `stream`, with the one workspace.
+ * Each chunk groups its own rows' distinct experts, so the weights of an
+ * expert several chunks use are streamed once per chunk: the bytes moved
+ * grow with rows / max_rows (a grouped GEMM over the whole batch would stream
+ * every used expert once).  Every row's output is bit for bit what
+ * moe_forward gives it in any batch.  rows >= 0, any size; x and out are
+ * [rows, H] bf16 and must not overlap.  Otherwise as moe_forward. */
+int moe_forward_prefill(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows, uint16_t* out,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* The same layer in the unfused layout, for measuring what fusion gains on
  * this GPU: four launches, as before shared-expert fusion ("Daily AI

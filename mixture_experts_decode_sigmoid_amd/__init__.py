@@ -41,7 +41,7 @@ class MoeConfig(C.Structure):
                 ("n_experts", C.c_int), ("top_k", C.c_int), ("n_group", C.c_int),
                 ("topk_group", C.c_int), ("n_shared", C.c_int), ("routed_scale", C.c_float),
                 ("routed_fmt", C.c_int), ("shared_fmt", C.c_int), ("bias_dtype", C.c_int),
-                ("max_rows", C.c_int)]
+                ("max_rows", C.c_int), ("expert_first", C.c_int), ("expert_count", C.c_int)]
 
 
 class MoeWeights(C.Structure):
@@ -92,12 +92,14 @@ def lib() -> C.CDLL:
         L.moe_last_hip_error.argtypes = []
         L.moe_probe_stream_read.argtypes = [P, Z, P, I, P]
         L.moe_forward_noalloc.argtypes = [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P]
+        L.moe_forward_prefill.argtypes = [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, Z, P]
         L.moe_forward_unfused.argtypes = [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, P, P, Z, P]
         L.moe_forward_after.argtypes = [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, P, Z, P,
                                          C.c_uint32, C.c_uint32, P]
         for f in ("moe_workspace_size", "moe_workspace_init", "moe_route", "moe_groups",
                   "moe_forward", "moe_forward_residual", "moe_read_error", "moe_last_hip_error",
-                  "moe_probe_stream_read", "moe_forward_noalloc", "moe_forward_after", "moe_forward_unfused"):
+                  "moe_probe_stream_read", "moe_forward_noalloc", "moe_forward_after", "moe_forward_unfused",
+                  "moe_forward_prefill"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -105,7 +107,8 @@ def lib() -> C.CDLL:
 
 EXPORTS = ("moe_workspace_size", "moe_workspace_init", "moe_route", "moe_groups",
            "moe_forward", "moe_forward_residual", "moe_read_error", "moe_strerror", "moe_last_hip_error",
-           "moe_probe_stream_read", "moe_forward_noalloc", "moe_forward_after", "moe_forward_unfused")
+           "moe_probe_stream_read", "moe_forward_noalloc", "moe_forward_after", "moe_forward_unfused",
+           "moe_forward_prefill")
 
 
 def strerror(code: int) -> str:
@@ -133,7 +136,8 @@ def make_config(spec: dict, max_rows: int) -> MoeConfig:
                      int(spec["n_experts"]), int(spec["top_k"]), int(spec["n_group"]),
                      int(spec["topk_group"]), int(spec["n_shared"]), float(spec["routed_scale"]),
                      int(spec["routed_fmt"]), MOE_FMT_FP8_B128,
-                     MOE_BIAS_BF16 if spec["bias_bf16"] else MOE_BIAS_F32, int(max_rows))
+                     MOE_BIAS_BF16 if spec["bias_bf16"] else MOE_BIAS_F32, int(max_rows),
+                     int(spec.get("expert_first", 0)), int(spec.get("expert_count", 0)))
 
 
 def make_weights(case: dict) -> MoeWeights:
@@ -191,6 +195,12 @@ def moe_forward_noalloc(cfg, w, x, out, stream=None):
     workspace argument, nothing allocated)."""
     _check(lib().moe_forward_noalloc(C.byref(cfg), C.byref(w), _ptr(x), int(x.shape[0]), _ptr(out),
                                      _stream(stream)), "moe_forward_noalloc")
+
+
+def moe_forward_prefill(cfg, w, x, out, ws, stream=None):
+    """Any number of rows: the fused pass over chunks of cfg.max_rows rows."""
+    _check(lib().moe_forward_prefill(C.byref(cfg), C.byref(w), _ptr(x), int(x.shape[0]), _ptr(out), _ptr(ws),
+                                     ws.numel(), _stream(stream)), "moe_forward_prefill")
 
 
 def moe_forward_unfused(cfg, w, x, out, tmp_routed, tmp_shared, ws, stream=None):
@@ -265,8 +275,7 @@ class Layer:
         b = buf.cpu().tolist()
         G = b[0]
         ge, gn, gs = b[4:4 + G], b[4 + G:4 + 2 * G], b[4 + 2 * G:4 + 3 * G]
-        ncol = T * (K + (1 if self.spec["n_shared"] else 0))
-        cols = b[4 + 3 * G:4 + 3 * G + ncol]
+        cols = b[4 + 3 * G:4 + 3 * G + sum(gn)]
         return ge, gn, gs, cols
 
     def read_error(self, stream=None) -> int:

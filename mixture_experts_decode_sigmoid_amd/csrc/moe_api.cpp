@@ -68,6 +68,9 @@ int check_cfg(const moe_config* c) {
   }
   if (!(c->routed_scale == c->routed_scale)) return MOE_ERR_SHAPE;
   if (c->max_rows < 1 || c->max_rows > kMaxRows) return MOE_ERR_ROWS;
+  if (c->expert_count < 0 || c->expert_first < 0) return MOE_ERR_SHAPE;
+  if (c->expert_count == 0 ? c->expert_first != 0 : c->expert_first > c->n_experts - c->expert_count)
+    return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 
@@ -116,6 +119,8 @@ int fill(const moe_config* c, const moe_weights* w, const uint16_t* x, int rows,
   p.I = c->inter;
   p.Is = c->n_shared ? c->shared_inter : 0;
   p.E = c->n_experts;
+  p.ef = c->expert_first;
+  p.ec = c->expert_count ? c->expert_count : c->n_experts;
   p.K = c->top_k;
   p.ng = c->n_group;
   p.kg = c->topk_group;
@@ -257,6 +262,25 @@ int moe_forward_residual(const moe_config* cfg, const moe_weights* w, const uint
                          const uint16_t* residual, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
   if (rows > 0 && !residual) return MOE_ERR_NULL;
   return forward_checked(cfg, w, x, rows, residual, out, ws, ws_bytes, stream);
+}
+
+int moe_forward_prefill(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows, uint16_t* out,
+                        void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (rows < 0) return MOE_ERR_ROWS;
+  if (rows == 0) return MOE_OK;
+  if (!x || !out) return MOE_ERR_NULL;
+  const size_t nb = (size_t)rows * cfg->hidden * 2;
+  const char *xo = (const char*)x, *oo = (const char*)out;
+  if (xo < oo + nb && oo < xo + nb) return MOE_ERR_ALIAS;
+  for (int r0 = 0; r0 < rows; r0 += cfg->max_rows) {
+    const int n = rows - r0 < cfg->max_rows ? rows - r0 : cfg->max_rows;
+    const size_t off = (size_t)r0 * cfg->hidden;
+    rc = forward_checked(cfg, w, x + off, n, nullptr, out + off, ws, ws_bytes, stream);
+    if (rc) return rc;
+  }
+  return MOE_OK;
 }
 
 int moe_forward_unfused(const moe_config* cfg, const moe_weights* w, const uint16_t* x, int rows, uint16_t* out,

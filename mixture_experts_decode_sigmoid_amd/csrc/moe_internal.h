@@ -49,6 +49,7 @@ struct WsLayout {
 struct Params {
   // shape
   int H, I, Is, E, K, ng, kg, n_shared, T;
+  int ef, ec;       // routed experts held here: [ef, ef + ec) (ec = E: all); weights indexed e - ef
   int routed_fmt, bias_bf16;
   double routed_scale;
   int hs;          // output rows per CU in down

@@ -24,7 +24,8 @@
 //                       LDS.  Unit batches that lie past the step's groups
 //                       issue nothing (dead-batch skip).
 //   S5  combine         out[r][h] = shared + sum_p w[r][p] * P[r][p][h] in this
-//                       row-local order, rounded to bf16 once.
+//                       row-local order, rounded to bf16 once (under an expert
+//                       range, p over the picks whose expert is held here).
 //
 // Prior art: sgl-amd-mono-upstream PR #27 (Motivation, Modifications: every
 // CTA routes all rows, groups by ballot over the picks, deals 8-intermediate
@@ -895,15 +896,19 @@ __device__ __forceinline__ int use_rank(const Lds& L, int e, int r) {
   return r < 32 ? __popc(lo & ((1u << r) - 1u)) : __popc(lo) + __popc(hi & ((1u << (r - 32)) - 1u));
 }
 
+// Whether routed expert e is held here (the expert range of the config).
+__device__ __forceinline__ bool held(const Params& p, int e) { return (unsigned)(e - p.ef) < (unsigned)p.ec; }
+
 // The grouping of up to 64 uses by one wave (the narrow stream's wave 7),
-// one use per lane, no workgroup barriers.
+// one use per lane, no workgroup barriers.  Uses of experts not held here
+// form no group and get no column.
 __device__ inline void groups_one_wave(const Params& p, const Lds& L) {
   const int lane = threadIdx.x & 63;
   const int U = p.T * p.K;
   {
     {
-      const bool valid = lane < U;
-      const int e = valid ? L.ids[lane] : 0, r = lane / p.K;
+      const int e = lane < U ? L.ids[lane] : 0, r = lane / p.K;
+      const bool valid = lane < U && held(p, e);
       if (valid) {
         L.first[e] = 0xffffffffu;
         L.rmask[2 * e] = 0u;
@@ -964,6 +969,7 @@ __device__ inline void build_groups(const Params& p, const Lds& L) {
   __syncthreads();
   for (int u = tid; u < U; u += kThreads) {
     const int e = L.ids[u], r = u / p.K;
+    if (!held(p, e)) continue;
     atomicMin(&L.first[e], (uint32_t)u);
     atomicOr(&L.rmask[2 * e + (r >> 5)], 1u << (r & 31));
   }
@@ -972,7 +978,7 @@ __device__ inline void build_groups(const Params& p, const Lds& L) {
   int base = p.n_shared;
   for (int u0 = 0; u0 < U; u0 += kThreads) {
     const int u = u0 + tid;
-    const bool isf = u < U && L.first[L.ids[u]] == (uint32_t)u;
+    const bool isf = u < U && held(p, L.ids[u]) && L.first[L.ids[u]] == (uint32_t)u;
     const unsigned long long m = __ballot(isf);
     const int before = __popcll(m & ((1ull << lane) - 1ull));
     if (lane == 0) L.misc[8 + wave] = __popcll(m);
@@ -1011,6 +1017,7 @@ __device__ inline void build_groups(const Params& p, const Lds& L) {
     }
   for (int u = tid; u < U; u += kThreads) {
     const int e = L.ids[u], r = u / p.K, slot = u - r * p.K;
+    if (!held(p, e)) continue;
     const int g = L.egrp[e], c = L.gstart[g] + use_rank(L, e, r);
     L.cols[c] = r * 16 + slot;
     L.cgrp[c] = g;
@@ -1210,6 +1217,7 @@ __device__ inline JobDesc make_desc(const Params& p, bool up, bool sh, int e, in
   JobDesc d;
   const int iexp = sh ? p.Is : p.I;
   const int kdim = up ? p.H : iexp;
+  e -= p.ef;  // index into the routed weights held here
   d.fmt = sh ? 0 : p.routed_fmt;
   d.nkb = kdim / (d.fmt ? 256 : 128);  // K-blocks: 128 bytes of every row (128 FP8 or 256 MXFP4 values)
   d.ncols = ncols;
@@ -2034,7 +2042,8 @@ __device__ inline void combine(const Params& p, const Lds& L, const Sched& s) {
     const uint32_t res = RES && p.residual ? p.residual[o] : 0u;  // issued ahead of the chain
     float acc = p.n_shared ? down_product(p, L, r, p.K, hl) : 0.f;
     if (!SHONLY)
-      for (int k = 0; k < p.K; ++k) acc = fmaf(L.w[r * p.K + k], down_product(p, L, r, k, hl), acc);
+      for (int k = 0; k < p.K; ++k)
+        if (held(p, L.ids[r * p.K + k])) acc = fmaf(L.w[r * p.K + k], down_product(p, L, r, k, hl), acc);
     if (RES && p.residual) acc += bf16_bits_to_f32(res);
     p.out[o] = (uint16_t)f32_to_bf16_rne(acc);
   }

@@ -43,7 +43,7 @@ def oracle_rows(spec, case, rows, ids=None, nthreads=0):
     if ids is None:
         ids, _, _, _ = oracle_route(spec, case)
     used = sorted(set(int(e) for r in rows for e in ids[r]))
-    h = fixtures.host_case(case, experts=used)
+    h = fixtures.host_case(case, experts=used, spec=spec)
     o64, ob = oracle.forward(spec, h, rows=list(rows), nthreads=nthreads)
     return o64, ob
 

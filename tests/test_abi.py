@@ -49,6 +49,13 @@ def test_workspace_size_and_config_checks():
         (dict(routed_fmt=1, inter=1152), moe.MOE_ERR_SHAPE),
         (dict(routed_fmt=1, hidden=2048, inter=1280), None),
         (dict(bias_bf16=0, n_group=1, topk_group=1, top_k=8), None),
+        # expert range: [first, first + count) within the E experts; count 0 = all
+        (dict(expert_first=224, expert_count=32), None),
+        (dict(expert_first=0, expert_count=256), None),
+        (dict(expert_first=225, expert_count=32), moe.MOE_ERR_SHAPE),
+        (dict(expert_first=-1, expert_count=32), moe.MOE_ERR_SHAPE),
+        (dict(expert_first=0, expert_count=-1), moe.MOE_ERR_SHAPE),
+        (dict(expert_first=3, expert_count=0), moe.MOE_ERR_SHAPE),
     ]
     for over, code in bad:
         cfg = _cfg(**over)
@@ -120,3 +127,15 @@ def test_forward_unfused_argument_errors():
                                  None) == moe.MOE_ERR_ALIGN
     cfg.n_shared = 0
     assert L.moe_forward_unfused(C.byref(cfg), C.byref(w), x, 1, out, tr, ts, ws, 1 << 30, None) == moe.MOE_ERR_SHAPE
+
+
+def test_forward_prefill_argument_errors():
+    L = moe.lib()
+    cfg = _cfg()
+    w = moe.MoeWeights(*([0x10000] * 10))
+    x, ws = C.c_void_p(0x1000), C.c_void_p(0x4000)
+    assert L.moe_forward_prefill(C.byref(cfg), C.byref(w), x, 0, None, ws, 1 << 30, None) == moe.MOE_OK
+    assert L.moe_forward_prefill(C.byref(cfg), C.byref(w), x, -1, x, ws, 1 << 30, None) == moe.MOE_ERR_ROWS
+    assert L.moe_forward_prefill(C.byref(cfg), C.byref(w), x, 100, None, ws, 1 << 30, None) == moe.MOE_ERR_NULL
+    assert L.moe_forward_prefill(C.byref(cfg), C.byref(w), x, 100, C.c_void_p(0x1000 + 64), ws, 1 << 30,
+                                 None) == moe.MOE_ERR_ALIAS

@@ -372,3 +372,23 @@ def test_forward_after_word_never_raised():
     assert layer.read_error() & moe.MOE_DEVERR_WAIT_TIMEOUT
     moe.moe_workspace_init(layer.ws)
     assert np.array_equal(run_forward(layer, case["x"]), ref)
+
+
+def test_prefill_chunks_are_batch_invariant():
+    """moe_forward_prefill over 150 rows in chunks of 64 (64, 64, 22): every
+    row's output equals a one-row moe_forward call of it, bit for bit, and
+    equals the chunks run as separate calls."""
+    say("prefill chunks")
+    spec = fixtures.spec_with("tiny", **V3R)
+    case = gpu_case(spec, 150, 88, rows="corr", requests=30)
+    layer = _layer(spec, case, 64)
+    x = case["x"]
+    out = torch.empty_like(x)
+    moe.moe_forward_prefill(layer.cfg, layer.w, x, out, layer.ws)
+    torch.cuda.synchronize()
+    assert layer.read_error() == 0
+    got = fixtures.bits16(out)
+    for r0, n in ((0, 64), (64, 64), (128, 22)):
+        assert np.array_equal(got[r0:r0 + n], run_forward(layer, x[r0:r0 + n].contiguous()))
+    for r in (0, 63, 64, 127, 128, 149):
+        assert np.array_equal(got[r], run_forward(layer, x[r:r + 1].contiguous())[0]), r

@@ -118,6 +118,11 @@ FULL = [
     # the 8-way tensor-parallel share of the V3 layer (intermediate 256)
     ("v3tp8_t1", [0]),
     ("v3tp8_t8", [0, 4, 7]),
+    ("v3tp4_t1", [0]),
+    ("v3tp4_t8", [1, 6]),
+    # the 8-way expert-parallel share (experts 0..31 and the shared expert)
+    ("v3ep8_t8", list(range(8))),
+    ("v3ep8_t64", [0, 21, 42, 63]),
 ]
 
 
@@ -293,3 +298,72 @@ def test_unfused_layout(name, over, T, seed, rows):
     spec_r = dict(spec, n_shared=0)
     layer_r = moe.Layer(spec_r, case, max_rows=T)
     assert np.array_equal(fixtures.bits16(t_r), run_forward(layer_r, case["x"]))
+
+
+# One device's share under expert parallelism (the config's expert range):
+# every row routed over all experts, the output summing only the held
+# experts' terms, plus the shared expert's on the one device that holds it.
+# Each shard against the oracle's reading, rows with neither a held pick nor
+# the shared expert exactly zero, the grouping equal to the oracle's with
+# the other experts' groups taken out, and the shards' outputs adding up to
+# the whole layer's.
+EP = [
+    ("tiny_4x4", dict(), 4, 6, 91, "corr"),
+    ("v3r_8x32_t8", V3R, 8, 8, 92, "iid"),
+    ("v3r_8x32_t40", V3R, 8, 40, 93, "corr"),
+    ("mxfp4_2x8_t12", dict(hidden=2048, inter=512, shared_inter=256, n_experts=16, top_k=6,
+                           routed_fmt=1, bias_bf16=1), 2, 12, 94, "corr"),
+]
+
+
+def _shard(spec, case, s, n):
+    per = spec["n_experts"] // n
+    sp = dict(spec, expert_first=s * per, expert_count=per, n_shared=spec["n_shared"] if s == 0 else 0)
+    sub = dict(case)
+    for k in ("w_gate_up", "s_gate_up", "w_down", "s_down"):
+        sub[k] = case[k][s * per:(s + 1) * per].clone()
+    if s:
+        for k in ("sh_w_gate_up", "sh_s_gate_up", "sh_w_down", "sh_s_down"):
+            sub.pop(k, None)
+    return sp, sub
+
+
+@pytest.mark.parametrize("name,over,n,T,seed,rows", EP, ids=[e[0] for e in EP])
+def test_expert_shards(name, over, n, T, seed, rows):
+    import oracle
+    say(f"expert shards {name} n={n} T={T}")
+    spec = _spec(over)
+    case = gpu_case(spec, T, seed, rows=rows, requests=max(1, T // 4))
+    H = spec["hidden"]
+    full = bf16_to_f64(run_forward(moe.Layer(spec, case, max_rows=T), case["x"]))
+    ids_o, _, _, _ = oracle_route(spec, case)
+    ge_o, gn_o, gs_o, cols_o, _ = oracle.groups(spec, ids_o)
+    total = np.zeros((T, H))
+    for s in range(n):
+        sp, sub = _shard(spec, case, s, n)
+        f, c = fixtures.held(sp)
+        layer = moe.Layer(sp, sub, max_rows=T)
+        ids, _ = layer.route(case["x"])
+        torch.cuda.synchronize()
+        assert np.array_equal(ids.cpu().numpy(), ids_o)
+        out = run_forward(layer, case["x"])
+        live = [r for r in range(T) if sp["n_shared"] or any(f <= e < f + c for e in ids_o[r])]
+        dead = [r for r in range(T) if r not in live]
+        assert not np.any(out[dead]), (s, dead)
+        if live:
+            o64, _ = oracle_rows(sp, sub, live, ids=ids_o)
+            rel, mx = parity(out, o64, live)
+            say(f"  shard {s}: {len(live)} live rows rel_l2={rel:.3e} max_abs={mx:.3e}")
+            assert rel <= REL_L2 and mx <= MAX_ABS, (s, rel, mx)
+        # grouping: the oracle's groups of held experts (and the shared one),
+        # columns renumbered in the same order
+        keep = [g for g in range(len(ge_o)) if ge_o[g] < 0 and sp["n_shared"] or f <= ge_o[g] < f + c]
+        ge, gn, gs, cols = layer.groups(case["x"])
+        assert ge == [int(ge_o[g]) for g in keep]
+        assert gn == [int(gn_o[g]) for g in keep]
+        assert gs == [sum(gn[:g]) for g in range(len(gn))]
+        assert cols == [int(v) for g in keep for v in cols_o[gs_o[g]:gs_o[g] + gn_o[g]]]
+        total += bf16_to_f64(out)
+    rel = float(np.linalg.norm(total - full) / np.linalg.norm(full))
+    say(f"  shards sum vs layer rel_l2={rel:.3e}")
+    assert rel <= REL_L2 and float(np.max(np.abs(total - full))) <= MAX_ABS
