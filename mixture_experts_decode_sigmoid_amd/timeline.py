@@ -102,10 +102,11 @@ def run(workload: str, calls: int, copies: int = 4):
     # and by XCD (workgroup i runs on XCD i mod 8)
     print("  spread over CUs: p10 / p50 / p90 / max; then the median per XCD 0..7")
     for i in (11, 4, 12, 5, 6, 7):
-        if not valid[:, :, i].all():
+        if not valid[:, :, i].any():
             continue
-        q = np.median(np.percentile(us[:, :, i], [10, 50, 90, 100], axis=1), axis=1)
-        xcd = [np.median(us[:, x::8, i]) for x in range(8)]
+        v = np.where(valid[:, :, i], us[:, :, i], np.nan)
+        q = np.nanmedian(np.nanpercentile(v, [10, 50, 90, 100], axis=1), axis=1)
+        xcd = [np.nanmedian(v[:, x::8]) for x in range(8)]
         print(f"  {NAMES[i]:28s} " + " ".join(f"{v:7.2f}" for v in q) + "  |" +
               " ".join(f"{v:6.1f}" for v in xcd))
     return rows
