@@ -193,7 +193,7 @@ int moe_forward_residual(const moe_config* cfg, const moe_weights* w, const uint
  * layer as moe_forward (same kernel, same result bit for bit), with the
  * workspace held in a static device array of the library, one per GPU, of
  * 5 MiB (5,242,880 bytes), kept until the process ends.  Every configuration
- * moe_workspace_size accepts fits (the largest needs 4,985,088 bytes); one
+ * moe_workspace_size accepts fits (the largest needs 4,993,280 bytes); one
  * that did not would give MOE_ERR_WORKSPACE.  Nothing is allocated.
  *   - The first call on a device sets the array up (its address, and a
  *     clearing kernel on `stream` for the words that must start at zero); that

@@ -151,6 +151,7 @@ int fill(const moe_config* c, const moe_weights* w, const uint16_t* x, int rows,
   p.flags = (uint32_t*)(base + L.flags);
   p.err = (uint32_t*)(base + L.err);
   p.scores = (double*)(base + L.scores);
+  p.picks = (uint64_t*)(base + L.picks);
   p.mid = (uint16_t*)(base + L.mid);
 #ifdef MOE_TIMELINE
   p.timeline = (uint64_t*)(base + L.total);  // callers of a timeline build add 1024*16*8 bytes

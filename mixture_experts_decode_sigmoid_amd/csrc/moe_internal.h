@@ -42,7 +42,7 @@ constexpr int kKsplitRows = 16;
 
 // Workspace layout (byte offsets from the workspace base).
 struct WsLayout {
-  size_t flags, err, scores, mid, total;
+  size_t flags, err, scores, picks, mid, total;
   int mid_ld;  // bf16 elements per (row, slot) line of mid
 };
 
@@ -92,6 +92,7 @@ struct Params {
   uint32_t* flags;
   uint32_t* err;
   double* scores;  // [T][E] score slots: two 64-bit words (tag, high half of s), (tag, low half)
+  uint64_t* picks; // [T][K] routed picks above 8 rows: two 64-bit words (tag, expert), (tag, weight bits)
   uint16_t* mid;   // [T][K+1][mid_ld] bf16
   uint64_t* timeline;  // optional phase stamps ([ncu][64]); NULL unless built with MOE_TIMELINE
   // forward after an upstream producer: x is read only once *x_ready has

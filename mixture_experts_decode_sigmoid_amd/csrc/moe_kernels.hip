@@ -587,12 +587,13 @@ __device__ inline void router_logits(const Params& p, const Lds& L, uint32_t epo
 
 // The same logits with one wave per (row, expert), in the same summation
 // order as router_logits, so that a logit has the same bits whatever the
-// batch size (the two forms are chosen by batch size): the wave walks the 8
-// chunks of H/8 in order, lane l sums the 16-byte groups l and l+64 of a
-// chunk (8 elements each, in order), the lanes are summed by the same fixed
-// tree (wave_sum_d), and the chunk sums are added in chunk order.  The
-// loads of NC chunks are issued before their products are summed (all 8
-// with LATE).  Used from 8 rows up, where every wave has rows of its own.
+// batch size (the two forms are chosen by batch size): a dot's 8 chunks of
+// H/8 are added in chunk order, lane l sums the 16-byte groups l and l+64 of
+// a chunk (8 elements each, in order), and the lanes are summed by the same
+// fixed tree (wave_sum_d).  Used from 8 rows up, where every wave has rows of
+// its own (rows wave, wave+8, ..., at most 8).  The loop runs chunk by chunk
+// over all of the wave's rows: a router chunk is loaded and widened to fp64
+// once and serves every row (the products are the same exact fp64 values).
 // LATE: `v` is the epoch, a load still in flight, first read once the sums
 // are formed (tag = epoch + 1); otherwise `v` is the tag.
 template <bool LATE>
@@ -601,49 +602,70 @@ __device__ inline void router_logits_rows(const Params& p, uint32_t v) {
   if (wave >= kWaves) return;
   const int ch = p.H / kWaves, ngrp = ch >> 3;
   const int g0 = lane < ngrp ? lane : ngrp - 1, g1 = lane + 64 < ngrp ? lane + 64 : g0;
-  constexpr int NC = LATE ? kWaves : kWaves / 2;
+  const bool a0 = lane < ngrp, a1 = lane + 64 < ngrp;
+  const int nr = p.T > wave ? (p.T - 1 - wave) / kWaves + 1 : 0;  // this wave's rows (<= 8)
+  if (nr == 0) return;
+  constexpr int kRows = kMaxRows / kWaves;
   for (int e = blockIdx.x; e < p.E; e += p.ncu) {
     const uint16_t* wr = p.router_w + (size_t)e * p.H;
     // LATE: the bias bits are converted once the sums are formed
     const uint32_t braw = LATE ? load_bias_raw(p, e) : 0u;
     const double bias = LATE ? 0.0 : load_bias(p, e);
-    for (int r = wave; r < p.T; r += kWaves) {
-      const uint16_t* xr = p.x + (size_t)r * p.H;
-      double l = 0.0;
-      for (int c0 = 0; c0 < kWaves; c0 += NC) {
-        u32x4 xv[NC][2], wv[NC][2];
+    double l[kRows];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const size_t o = (size_t)(c0 + c) * ch;
-          xv[c][0] = ld16(xr + o + 8 * g0);
-          wv[c][0] = ld16(wr + o + 8 * g0);
-          xv[c][1] = ld16(xr + o + 8 * g1);
-          wv[c][1] = ld16(wr + o + 8 * g1);
+    for (int j = 0; j < kRows; ++j) l[j] = 0.0;
+#pragma unroll 1
+    for (int c = 0; c < kWaves; ++c) {
+      const size_t o = (size_t)c * ch;
+      u32x4 xv[kRows][2], wv[2];
+      wv[0] = ld16(wr + o + 8 * g0);
+      wv[1] = ld16(wr + o + 8 * g1);
+#pragma unroll
+      for (int j = 0; j < kRows; ++j) {
+        const int r = j < nr ? wave + kWaves * j : wave;
+        const uint16_t* xr = p.x + (size_t)r * p.H + o;
+        xv[j][0] = ld16(xr + 8 * g0);
+        xv[j][1] = ld16(xr + 8 * g1);
+      }
+      double wd[16];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          wd[8 * q + 2 * i] = (double)bf16_bits_to_f32(wv[q][i] & 0xffffu);
+          wd[8 * q + 2 * i + 1] = (double)bf16_bits_to_f32(wv[q][i] >> 16);
         }
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
+      for (int j = 0; j < kRows; ++j) {
+        if (j < nr) {
           double acc = 0.0;
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
-            if (q == 0 ? lane < ngrp : lane + 64 < ngrp) {
+            if (q == 0 ? a0 : a1) {
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                const uint32_t xa = xv[c][q][i], wa = wv[c][q][i];
-                acc = fma((double)bf16_bits_to_f32(xa & 0xffffu), (double)bf16_bits_to_f32(wa & 0xffffu), acc);
-                acc = fma((double)bf16_bits_to_f32(xa >> 16), (double)bf16_bits_to_f32(wa >> 16), acc);
+                const uint32_t xa = xv[j][q][i];
+                acc = fma((double)bf16_bits_to_f32(xa & 0xffffu), wd[8 * q + 2 * i], acc);
+                acc = fma((double)bf16_bits_to_f32(xa >> 16), wd[8 * q + 2 * i + 1], acc);
               }
             }
           }
-          l += wave_sum_d(acc);
+          l[j] += wave_sum_d(acc);
         }
       }
-      uint32_t ep = v, br = braw;
-      if (LATE) asm volatile("" : "+v"(ep), "+v"(br));
-      if (lane == 0) {
-        double s = 1.0 / (1.0 + exp(-l));
-        double b = s + (LATE ? bias_from_raw(p, br) : bias);
-        if (!isfinite(l) || !isfinite(b)) set_err(p.err, kErrScore);
-        publish_score(p, r, e, s, LATE ? ep + 1 : v);
+    }
+    uint32_t ep = v, br = braw;
+    if (LATE) asm volatile("" : "+v"(ep), "+v"(br));
+    if (lane == 0) {
+      const double bz = LATE ? bias_from_raw(p, br) : bias;
+#pragma unroll
+      for (int j = 0; j < kRows; ++j) {
+        if (j < nr) {
+          const double s = 1.0 / (1.0 + exp(-l[j]));
+          const double bb = s + bz;
+          if (!isfinite(l[j]) || !isfinite(bb)) set_err(p.err, kErrScore);
+          publish_score(p, wave + kWaves * j, e, s, LATE ? ep + 1 : v);
+        }
       }
     }
   }
@@ -677,16 +699,22 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
   double bias[4];  // loaded first: they do not depend on the scores
 #pragma unroll
   for (int i = 0; i < 4; ++i) bias[i] = 4 * lane + i < p.E ? load_bias(p, 4 * lane + i) : 0.0;
+  // a slot is loaded again only until both its words carry the tag, so the
+  // later rounds of the poll fetch only the slots still missing
+  bool got[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) got[i] = 4 * lane + i >= p.E;
   for (int spins = 0;;) {
     bool ready = true;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int e = 4 * lane + i, q = i * e4 + lane;  // q: expert e's slot in the row
-      if (e < p.E) {
+      const int q = i * e4 + lane;  // q: expert 4 * lane + i's slot in the row
+      if (!got[i]) {
         w0[i] = __hip_atomic_load(sc + 2 * q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         w1[i] = __hip_atomic_load(sc + 2 * q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ready = ready && (uint32_t)(w0[i] >> 32) == tag && (uint32_t)(w1[i] >> 32) == tag;
+        got[i] = (uint32_t)(w0[i] >> 32) == tag && (uint32_t)(w1[i] >> 32) == tag;
       }
+      ready = ready && got[i];
     }
     if (__all(ready)) break;
     if (++spins > kSpinLimit) {
@@ -899,6 +927,46 @@ __device__ __forceinline__ int use_rank(const Lds& L, int e, int r) {
 // Whether routed expert e is held here (the expert range of the config).
 __device__ __forceinline__ bool held(const Params& p, int e) { return (unsigned)(e - p.ef) < (unsigned)p.ec; }
 
+// Above 8 rows the rows are routed across CUs instead of every CU routing
+// every row (eight rows or more per wave, one after another): row r by
+// wave r / ncu of CU r mod ncu, which publishes the row's picks as tagged
+// words (like the score slots); then every thread of every CU polls the
+// picks of one use (row, slot) until both its words carry the call's tag.
+// The routing arithmetic is the same whichever CU runs it, so the picks
+// are the same bits as when every CU routes every row.
+__device__ inline void route_rows_spread(const Params& p, const Lds& L, uint32_t tag) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  typedef __attribute__((address_space(1))) uint64_t G64;
+  for (int r = (int)blockIdx.x + wave * p.ncu; r < p.T; r += kWaves * p.ncu) {
+    route_row(p, L, r, tag);
+    wave_sync();  // the row's ids and weights, written by single lanes
+    if (lane < p.K) {
+      const uint32_t id = (uint32_t)L.ids[r * p.K + lane];
+      const uint32_t wb = __float_as_uint(L.w[r * p.K + lane]);
+      G64* q = (G64*)p.picks + 2 * (r * p.K + lane);
+      __hip_atomic_store(q, ((uint64_t)tag << 32) | id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(q + 1, ((uint64_t)tag << 32) | wb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  const int U = p.T * p.K;
+  for (int u = threadIdx.x; u < U; u += kThreads) {
+    const G64* q = (const G64*)p.picks + 2 * u;
+    uint64_t a = 0, b = 0;
+    for (int spins = 0;;) {
+      a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((uint32_t)(a >> 32) == tag && (uint32_t)(b >> 32) == tag) break;
+      if (++spins > kSpinLimit) {
+        set_err(p.err, kErrTimeout);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    L.ids[u] = (int32_t)(uint32_t)a;
+    L.w[u] = __uint_as_float((uint32_t)b);
+  }
+}
+
 // The grouping of up to 64 uses by one wave (the narrow stream's wave 7),
 // one use per lane, no workgroup barriers.  Uses of experts not held here
 // form no group and get no column.
@@ -1031,14 +1099,14 @@ __device__ inline void build_groups(const Params& p, const Lds& L) {
 // routed up/gate tiles (16 weight rows, 8 gate + 8 up, over all of H), then
 // its 16-row down tiles of every used expert (over that expert's
 // intermediate size).  The 8 waves split every job along the reduction
-// axis: wave w owns the 128-element K-blocks w, w+8, w+16, ...  One such
-// K-block of one job is an item: the 16 rows' weights (FP8 32 bytes or
-// MXFP4 16 bytes per lane), the activations of the group's columns and the
-// block scale.  A wave loads its items straight from HBM into registers,
-// D items ahead of the one it multiplies; every item issues the same number
-// of loads, so the in-order wait for item n leaves items n+1..n+D-1 in
-// flight.  (An LDS ring fed by LDS-DMA reached a lower and less steady
-// share of HBM bandwidth.)
+// axis in K-phases: phase w holds the K-blocks w, w+8, w+16, ... (128 bytes
+// of every weight row: 128 FP8 or 256 MXFP4 values).  One K-block of one
+// job is an item: the 16 rows' weights (32 bytes per lane), the block
+// scale and the activations of the job's columns.  A wave loads its items
+// straight from HBM into registers, D items ahead of the one it
+// multiplies; every item issues the same number of loads, so the in-order
+// wait for item n leaves items n+1..n+D-1 in flight.  (An LDS ring fed by
+// LDS-DMA reached a lower and less steady share of HBM bandwidth.)
 
 
 // Wave-uniform loop state, re-asserted as uniform: the compiler's uniformity
@@ -1387,6 +1455,7 @@ struct PhaseN {
   int dnb;        // FP8 down: block rows between the tile's first and last live row (0 or 1)
   int rt;         // down: this wave's tile
   int nw;         // up/gate: waves with items (min(K-blocks, 8))
+  int nsc, nct;   // up/gate: chunks of the CU's shared-expert jobs, column tiles per shared pair
   int h0, hc, nrt;  // KIND 3: this CU's slice and its 16-row tiles
 };
 template <int KIND>
@@ -1552,10 +1621,27 @@ __device__ __forceinline__ uint32_t lds_inc_lane0(uint32_t* a) {
 // side; past the end once c / nw reaches the CU's job count (the wave then
 // claims no more).  Jobs from nS on wait for the routed tables (bounded).
 __device__ __forceinline__ int chunk_job(uint32_t c, int nw) { return nw == kWaves ? (int)(c >> 3) : (int)c / nw; }
+// Chunk c's job and K-phase.  The column-tile jobs of one shared-expert pair
+// (the same weight rows for different columns) are taken phase by phase,
+// all tiles' phase 0, then phase 1, ..., so a K-block's repeats follow each
+// other closely and come from the caches; every other job's chunks are
+// taken job by job.
+__device__ __forceinline__ void chunk_map(uint32_t c, const PhaseN& ph, int& q, int& kp) {
+  if ((int)c < ph.nsc && ph.nct > 1) {
+    const int per = ph.nct * ph.nw;
+    const int pi = (int)c / per, i = (int)c - pi * per;
+    kp = i / ph.nct;
+    q = pi * ph.nct + (i - kp * ph.nct);
+  } else {
+    q = chunk_job(c, ph.nw);
+    kp = (int)c - q * ph.nw;
+  }
+}
 template <int FMT, int AL>
 __device__ inline void fetch_next_up(const Params& p, const Lds& L, const PhaseN& ph, FetchN& f, int nS, bool& ok) {
   const uint32_t c = lds_inc_lane0(L.ccnt);
-  const int q = chunk_job(c, ph.nw), kp = (int)c - q * ph.nw;
+  int q, kp;
+  chunk_map(c, ph, q, kp);
   if (q >= nS && f.nu < 0) {
     lds_wait<1>(p, (const uint32_t*)L.misc + kMiscReady, 1u, ok);
     f.nu = ok ? lds_ldi_uniform(L.misc + kMiscNU) : 0;
@@ -1707,7 +1793,8 @@ __device__ inline bool eat_next_up(const Params& p, const Lds& L, const PhaseN& 
   const int lane = threadIdx.x & 63, lg = lane >> 4, col = lane_col<AL>(lane);
   const uint32_t c = (uint32_t)lds_ldi_uniform((const int32_t*)L.cfifo + wave_id() * 8 + (e.nch & 7));
   e.nch = e.nch + 1;
-  const int q = chunk_job(c, ph.nw), kp = (int)c - q * ph.nw;
+  int q, kp;
+  chunk_map(c, ph, q, kp);
   const JobDesc d = read_desc(L, q);
   e.q = q;
   e.left = ((d.nkb - 1 - kp) >> 3) + 1;
@@ -2030,6 +2117,8 @@ __device__ inline void sum_kphases(const Params& p, const Lds& L, const Sched& s
   __syncthreads();
 }
 
+// A pick whose expert is not held here (expert range) has no column: its
+// product stays at the zeroed partials, and its term adds exactly +0.
 // RES: a residual, when given, is added in fp32 after the chain, then
 // rounded once (the residual add of the unfused layout, folded in).
 // SHONLY: the shared expert's product alone (the unfused layout's shared
@@ -2042,8 +2131,7 @@ __device__ inline void combine(const Params& p, const Lds& L, const Sched& s) {
     const uint32_t res = RES && p.residual ? p.residual[o] : 0u;  // issued ahead of the chain
     float acc = p.n_shared ? down_product(p, L, r, p.K, hl) : 0.f;
     if (!SHONLY)
-      for (int k = 0; k < p.K; ++k)
-        if (held(p, L.ids[r * p.K + k])) acc = fmaf(L.w[r * p.K + k], down_product(p, L, r, k, hl), acc);
+      for (int k = 0; k < p.K; ++k) acc = fmaf(L.w[r * p.K + k], down_product(p, L, r, k, hl), acc);
     if (RES && p.residual) acc += bf16_bits_to_f32(res);
     p.out[o] = (uint16_t)f32_to_bf16_rne(acc);
   }
@@ -2100,6 +2188,8 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
     PhaseN ph = {};
     ph.nw = nkb < kWaves ? nkb : kWaves;
     const int nS = shared_jobs_here(p);
+    ph.nct = p.n_shared ? n_ctiles(p, p.T) : 1;
+    ph.nsc = nS * ph.nw;
     const bool early = p.T <= kWaves && p.T * p.K <= 64 && nS > 0;
     MOE_STAMP(p, 2);
     if (early) {
@@ -2133,7 +2223,11 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
       }
       if (r >= p.T) lds_wait<1>(p, (const uint32_t*)L.misc + kMiscPolled, (uint32_t)p.T, ok);
     } else {
-      for (int r = wave; r < p.T; r += kWaves) route_row(p, L, r, epoch + 1);
+      if (p.T > kWaves) {
+        route_rows_spread(p, L, epoch + 1);
+      } else {
+        for (int r = wave; r < p.T; r += kWaves) route_row(p, L, r, epoch + 1);
+      }
       __syncthreads();
       MOE_STAMP(p, 10);
       build_groups(p, L);
@@ -2242,6 +2336,8 @@ __device__ __forceinline__ void shared_only(char* smem) {
     const int nkb = p.H / 128;
     PhaseN ph = {};
     ph.nw = nkb < kWaves ? nkb : kWaves;
+    ph.nct = n_ctiles(p, p.T);
+    ph.nsc = nS * ph.nw;
     RingN<ring_up<FMT, AL>()> R;
     ring_open<FMT, 1, ring_up<FMT, AL>(), AL>(p, L, ph, R, 0, nS, ok);
     ring_fill<FMT, 1, false, ring_up<FMT, AL>(), AL>(p, L, ph, R, nS, ok);
@@ -2396,6 +2492,7 @@ WsLayout ws_layout(int max_rows, int E, int K, int H, int I, int Is) {
   w.flags = q; q = align_up(q + 4 * 1024, 256);
   w.err = q; q = align_up(q + 256, 256);
   w.scores = q; q = align_up(q + 16 * (size_t)max_rows * 4 * ((E + 3) / 4), 256);
+  w.picks = q; q = align_up(q + 16 * (size_t)max_rows * K, 256);
   w.mid_ld = (I > Is ? I : Is);
   w.mid = q; q = align_up(q + 2 * (size_t)max_rows * (K + 1) * w.mid_ld, 256);
   w.total = q;

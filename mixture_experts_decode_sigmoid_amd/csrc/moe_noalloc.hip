@@ -18,7 +18,7 @@
 #include <mutex>
 
 // Large enough for every configuration the library accepts: 64 rows, 256
-// experts, top-8 and intermediates up to 4096 need 4,985,088 bytes.
+// experts, top-8 and intermediates up to 4096 need 4,993,280 bytes.
 static constexpr size_t kScratchBytes = 5u << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 

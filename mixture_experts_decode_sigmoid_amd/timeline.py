@@ -98,6 +98,14 @@ def run(workload: str, calls: int, copies: int = 4):
         rows.append((med, f"waves: {name}", mx))
     for med, name, mx in sorted(rows):
         print(f"  {name:40s} {med:8.2f} {mx:8.2f}")
+    # per wave index: the median over CUs and calls of each per-wave stamp
+    print("  per wave 0..7 (median over CUs and calls)")
+    for k, name in WAVE_NAMES.items():
+        sl = [16 + 8 * k + w for w in range(8)]
+        if not valid[:, :, sl].any():
+            continue
+        vals = np.where(valid[:, :, sl], us[:, :, sl], np.nan)
+        print(f"  {name:28s} " + " ".join(f"{np.nanmedian(vals[:, :, w]):7.2f}" for w in range(8)))
     # spread over CUs of the phase ends (median over calls of each percentile),
     # and by XCD (workgroup i runs on XCD i mod 8)
     print("  spread over CUs: p10 / p50 / p90 / max; then the median per XCD 0..7")
