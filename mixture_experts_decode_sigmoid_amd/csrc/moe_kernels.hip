@@ -587,13 +587,12 @@ __device__ inline void router_logits(const Params& p, const Lds& L, uint32_t epo
 
 // The same logits with one wave per (row, expert), in the same summation
 // order as router_logits, so that a logit has the same bits whatever the
-// batch size (the two forms are chosen by batch size): a dot's 8 chunks of
-// H/8 are added in chunk order, lane l sums the 16-byte groups l and l+64 of
-// a chunk (8 elements each, in order), and the lanes are summed by the same
-// fixed tree (wave_sum_d).  Used from 8 rows up, where every wave has rows of
-// its own (rows wave, wave+8, ..., at most 8).  The loop runs chunk by chunk
-// over all of the wave's rows: a router chunk is loaded and widened to fp64
-// once and serves every row (the products are the same exact fp64 values).
+// batch size (the two forms are chosen by batch size): the wave walks the 8
+// chunks of H/8 in order, lane l sums the 16-byte groups l and l+64 of a
+// chunk (8 elements each, in order), the lanes are summed by the same fixed
+// tree (wave_sum_d), and the chunk sums are added in chunk order.  The
+// loads of NC chunks are issued before their products are summed (all 8
+// with LATE).  Used from 8 rows up, where every wave has rows of its own.
 // LATE: `v` is the epoch, a load still in flight, first read once the sums
 // are formed (tag = epoch + 1); otherwise `v` is the tag.
 template <bool LATE>
@@ -602,70 +601,49 @@ __device__ inline void router_logits_rows(const Params& p, uint32_t v) {
   if (wave >= kWaves) return;
   const int ch = p.H / kWaves, ngrp = ch >> 3;
   const int g0 = lane < ngrp ? lane : ngrp - 1, g1 = lane + 64 < ngrp ? lane + 64 : g0;
-  const bool a0 = lane < ngrp, a1 = lane + 64 < ngrp;
-  const int nr = p.T > wave ? (p.T - 1 - wave) / kWaves + 1 : 0;  // this wave's rows (<= 8)
-  if (nr == 0) return;
-  constexpr int kRows = kMaxRows / kWaves;
+  constexpr int NC = LATE ? kWaves : kWaves / 2;
   for (int e = blockIdx.x; e < p.E; e += p.ncu) {
     const uint16_t* wr = p.router_w + (size_t)e * p.H;
     // LATE: the bias bits are converted once the sums are formed
     const uint32_t braw = LATE ? load_bias_raw(p, e) : 0u;
     const double bias = LATE ? 0.0 : load_bias(p, e);
-    double l[kRows];
+    for (int r = wave; r < p.T; r += kWaves) {
+      const uint16_t* xr = p.x + (size_t)r * p.H;
+      double l = 0.0;
+      for (int c0 = 0; c0 < kWaves; c0 += NC) {
+        u32x4 xv[NC][2], wv[NC][2];
 #pragma unroll
-    for (int j = 0; j < kRows; ++j) l[j] = 0.0;
-#pragma unroll 1
-    for (int c = 0; c < kWaves; ++c) {
-      const size_t o = (size_t)c * ch;
-      u32x4 xv[kRows][2], wv[2];
-      wv[0] = ld16(wr + o + 8 * g0);
-      wv[1] = ld16(wr + o + 8 * g1);
-#pragma unroll
-      for (int j = 0; j < kRows; ++j) {
-        const int r = j < nr ? wave + kWaves * j : wave;
-        const uint16_t* xr = p.x + (size_t)r * p.H + o;
-        xv[j][0] = ld16(xr + 8 * g0);
-        xv[j][1] = ld16(xr + 8 * g1);
-      }
-      double wd[16];
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          wd[8 * q + 2 * i] = (double)bf16_bits_to_f32(wv[q][i] & 0xffffu);
-          wd[8 * q + 2 * i + 1] = (double)bf16_bits_to_f32(wv[q][i] >> 16);
+        for (int c = 0; c < NC; ++c) {
+          const size_t o = (size_t)(c0 + c) * ch;
+          xv[c][0] = ld16(xr + o + 8 * g0);
+          wv[c][0] = ld16(wr + o + 8 * g0);
+          xv[c][1] = ld16(xr + o + 8 * g1);
+          wv[c][1] = ld16(wr + o + 8 * g1);
         }
 #pragma unroll
-      for (int j = 0; j < kRows; ++j) {
-        if (j < nr) {
+        for (int c = 0; c < NC; ++c) {
           double acc = 0.0;
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
-            if (q == 0 ? a0 : a1) {
+            if (q == 0 ? lane < ngrp : lane + 64 < ngrp) {
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                const uint32_t xa = xv[j][q][i];
-                acc = fma((double)bf16_bits_to_f32(xa & 0xffffu), wd[8 * q + 2 * i], acc);
-                acc = fma((double)bf16_bits_to_f32(xa >> 16), wd[8 * q + 2 * i + 1], acc);
+                const uint32_t xa = xv[c][q][i], wa = wv[c][q][i];
+                acc = fma((double)bf16_bits_to_f32(xa & 0xffffu), (double)bf16_bits_to_f32(wa & 0xffffu), acc);
+                acc = fma((double)bf16_bits_to_f32(xa >> 16), (double)bf16_bits_to_f32(wa >> 16), acc);
               }
             }
           }
-          l[j] += wave_sum_d(acc);
+          l += wave_sum_d(acc);
         }
       }
-    }
-    uint32_t ep = v, br = braw;
-    if (LATE) asm volatile("" : "+v"(ep), "+v"(br));
-    if (lane == 0) {
-      const double bz = LATE ? bias_from_raw(p, br) : bias;
-#pragma unroll
-      for (int j = 0; j < kRows; ++j) {
-        if (j < nr) {
-          const double s = 1.0 / (1.0 + exp(-l[j]));
-          const double bb = s + bz;
-          if (!isfinite(l[j]) || !isfinite(bb)) set_err(p.err, kErrScore);
-          publish_score(p, wave + kWaves * j, e, s, LATE ? ep + 1 : v);
-        }
+      uint32_t ep = v, br = braw;
+      if (LATE) asm volatile("" : "+v"(ep), "+v"(br));
+      if (lane == 0) {
+        double s = 1.0 / (1.0 + exp(-l));
+        double b = s + (LATE ? bias_from_raw(p, br) : bias);
+        if (!isfinite(l) || !isfinite(b)) set_err(p.err, kErrScore);
+        publish_score(p, r, e, s, LATE ? ep + 1 : v);
       }
     }
   }
@@ -2407,6 +2385,9 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   const Lds L = lds_map(smem, p);
   const int tid = threadIdx.x, wave = wave_id();
 
+#ifdef MOE_TIMELINE
+  if (tid > 0 && tid < 64) MOE_TL(p, tid) = 0;  // stamps this call does not take stay zero
+#endif
   MOE_STAMP(p, 0);
   if (MODE == kModeSharedUp || MODE == kModeSharedDown) {
     if (tid < 64) L.ctl[tid] = 0u;
