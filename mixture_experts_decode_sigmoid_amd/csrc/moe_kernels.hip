@@ -1305,14 +1305,19 @@ __device__ inline JobDesc make_desc(const Params& p, bool up, bool sh, int e, in
 }
 
 // Up/gate (group, 8-intermediate tile) pair j of the step: the shared tiles,
-// then rt_tiles tiles per routed group.  Sets its group and tile.
+// then rt_tiles tiles per routed group.  Sets its group and tile.  A routed
+// group's tiles are rotated by 37 per group, so that a CU's pairs fall on
+// different row blocks of successive experts (unrotated, CU c reads row
+// block c of every expert, and the phase ends were spread by XCD, up to
+// 18 us apart at 64 rows; rotated: 64 rows 1379 -> 1348 us, 8 rows 234 ->
+// 232 us, same-box A/B).  Any rotation keeps the tiles a permutation.
 __device__ __forceinline__ void up_pair(const Params& p, const Sched& s, int j, int& g, int& tile) {
   if (j < s.sh_tiles) {
     g = 0;
     tile = j;
   } else {
     g = p.n_shared + (j - s.sh_tiles) / s.rt_tiles;
-    tile = (j - s.sh_tiles) % s.rt_tiles;
+    tile = ((j - s.sh_tiles) % s.rt_tiles + (g - p.n_shared + 1) * 37) % s.rt_tiles;
   }
 }
 
