@@ -1439,6 +1439,7 @@ struct PhaseN {
   int rt;         // down: this wave's tile
   int nw;         // up/gate: waves with items (min(K-blocks, 8))
   int nsc, nct;   // up/gate: chunks of the CU's shared-expert jobs, column tiles per shared pair
+  int js, jp;     // K-split down: the wave takes the down jobs j with j mod js == jp
   int h0, hc, nrt;  // KIND 3: this CU's slice and its 16-row tiles
 };
 template <int KIND>
@@ -1460,11 +1461,33 @@ __device__ __forceinline__ PhaseN down_phase(int h0, int hc, int nrt, int rt, in
   ph.split = (ph.hb / 128 + 1) * 128 - ph.hb;  // a 16-row tile spans at most two scale block rows
   ph.dnb = ph.nlive > 0 ? ((ph.hb + ph.nlive - 1) >> 7) - (ph.hb >> 7) : 0;
   ph.nw = 0;
+  ph.js = 1;
+  ph.jp = 0;
   ph.h0 = h0;
   ph.hc = hc;
   ph.nrt = nrt;
   return ph;
 }
+
+// The K-split down constants of wave w: tile w mod nrt_p of the CU's slice
+// and K-phase (w / nrt_p) of the kph phases.  When a down job has fewer
+// K-blocks than kph (a small intermediate size), the phases are cut to the
+// power of two kpe >= the most K-blocks a down job has, and the waves left
+// over take every (kph/kpe)-th job instead, so no wave idles.  Each phase
+// then holds at most one K-block, as it did with kph phases: the partials,
+// and their phase-order sum, are the same bits.
+__device__ __forceinline__ PhaseN ksplit_phase(const Params& p, const Sched& s, int w) {
+  const int nkb_rt = p.I / (p.routed_fmt ? 256 : 128), nkb_sh = p.n_shared ? p.Is / 128 : 0;
+  const int nkb = nkb_rt > nkb_sh ? nkb_rt : nkb_sh;
+  int kpe = 1;
+  while (kpe < nkb && kpe < s.kph) kpe <<= 1;
+  const int q = w / s.nrt_p;
+  PhaseN ph = down_phase(s.h0, s.hc, s.nrt, w % s.nrt_p, q % kpe, 31 - __builtin_clz(kpe));
+  ph.js = s.kph / kpe;
+  ph.jp = q / kpe;
+  return ph;
+}
+
 
 template <int KIND>
 __device__ __forceinline__ int job_items(const PhaseN& ph, int nkb) {
@@ -1574,6 +1597,7 @@ __device__ __forceinline__ void fetch_dead(const Params& p, FetchN& f) {
 template <int FMT, int KIND, int AL>
 __device__ inline void fetch_next_n(const Params& p, const Lds& L, const PhaseN& ph, FetchN& f, int kend) {
   for (; f.k < kend; ++f.k) {
+    if (KIND == 2 && ((f.k - p.qcap) & (ph.js - 1)) != ph.jp) continue;
     const JobDesc d = read_desc(L, f.k);
     const int n = job_items<KIND>(ph, d.nkb);
     if (n == 0) continue;
@@ -1750,6 +1774,7 @@ template <int FMT, int KIND, int AL>
 __device__ inline bool eat_next_n(const Params& p, const Lds& L, const PhaseN& ph, EatN& e, int kend) {
   const int lane = threadIdx.x & 63, lg = lane >> 4, col = lane_col<AL>(lane);
   for (; e.k < kend; ++e.k) {
+    if (KIND == 2 && ((e.k - p.qcap) & (ph.js - 1)) != ph.jp) continue;
     const JobDesc d = read_desc(L, e.k);
     const int n = job_items<KIND>(ph, d.nkb);
     if (n == 0) continue;
@@ -2247,7 +2272,7 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
     if (!DCLAIM) {
       // wave w takes tile w % nrt_p of this CU's slice and K-blocks
       // w / nrt_p + wpt*i of every down job
-      const PhaseN ph = down_phase(s.h0, s.hc, s.nrt, wave % s.nrt_p, wave / s.nrt_p, 31 - __builtin_clz(s.kph));
+      const PhaseN ph = ksplit_phase(p, s, wave);
       const int kend = ph.nlive > 0 ? p.qcap + nD : p.qcap;
       ring_open<FMT, 2, kRingDD, AL>(p, L, ph, R, p.qcap, kend, ok);
       ring_fill<FMT, 2, true, kRingDD, AL>(p, L, ph, R, kend, ok);
@@ -2332,7 +2357,7 @@ __device__ __forceinline__ void shared_only(char* smem) {
   __syncthreads();
   RingN<kRingDD> R;
   if (!DCLAIM) {
-    const PhaseN ph = down_phase(s.h0, s.hc, s.nrt, wave % s.nrt_p, wave / s.nrt_p, 31 - __builtin_clz(s.kph));
+    const PhaseN ph = ksplit_phase(p, s, wave);
     const int kend = ph.nlive > 0 ? p.qcap + nD : p.qcap;
     ring_open<FMT, 2, kRingDD, AL>(p, L, ph, R, p.qcap, kend, ok);
     ring_fill<FMT, 2, false, kRingDD, AL>(p, L, ph, R, kend, ok);
