@@ -6,7 +6,7 @@ The library built with MOE_TIMELINE (libmoe_timeline.so, beside libmoe.so)
 has thread 0 of every workgroup (and lane 0 of every wave for the per-wave
 stamps) write s_memrealtime (100 MHz) at phase boundaries into 64 slots per
 CU placed after the workspace.  This tool runs the workload with rotating
-weight copies, and for every stamp prints the median and maximum over CUs
+weight copies (--save keeps every stamp as a .npy array), and for every stamp prints the median and maximum over CUs
 (medians over calls) in microseconds from the earliest CU start of the call.
 """
 from __future__ import annotations
@@ -49,7 +49,7 @@ def build():
     return b.build(verbose=False, out=LIB_TL, defines=("MOE_TIMELINE",))
 
 
-def run(workload: str, calls: int, copies: int = 4):
+def run(workload: str, calls: int, copies: int = 4, save: str | None = None):
     import torch
     sys.path.insert(0, ROOT)
     import fixtures
@@ -79,6 +79,8 @@ def run(workload: str, calls: int, copies: int = 4):
     t0 = S[:, :, 0].min(axis=1)[:, None]      # earliest start per call
     us = (S - t0[:, :, None]) / 100.0         # 100 MHz ticks -> us
     valid = S > 0
+    if save:
+        np.save(save, np.where(valid, us, np.nan))
     print(f"{workload}: {calls} calls, {ncu} CUs; median / max over CUs, median over calls (us)")
     rows = []
     for i, name in NAMES.items():
@@ -125,10 +127,11 @@ def main():
     ap.add_argument("workload")
     ap.add_argument("--calls", type=int, default=30)
     ap.add_argument("--build", action="store_true")
+    ap.add_argument("--save", help="also write the stamps (calls x CUs x 64, us; NaN where unset) as .npy")
     a = ap.parse_args()
     if a.build:
         print(build())
-    run(a.workload, a.calls)
+    run(a.workload, a.calls, save=a.save)
 
 
 if __name__ == "__main__":
