@@ -39,6 +39,7 @@ __host__ __device__ inline int stream_al(int T) { return T <= 4 ? 1 : 2; }
 // Down jobs are split over waves by K-phase up to this many rows; above it
 // every wave claims whole down jobs (the K-phase partials would not fit LDS).
 constexpr int kKsplitRows = 16;
+constexpr int kSpreadRows = 8;          // from this many rows (up to 8) each row is routed by one CU
 
 // Workspace layout (byte offsets from the workspace base).
 struct WsLayout {

@@ -649,6 +649,10 @@ __device__ inline void router_logits_rows(const Params& p, uint32_t v) {
   }
 }
 
+// The row whose routing the timeline build stamps: row 0, or above 8 rows
+// (one row per routing CU) this CU's own row.
+__device__ __forceinline__ int tl_row(const Params& p) { return p.T > kWaves ? (int)blockIdx.x : 0; }
+
 // Two largest values (t1 >= t2) over an aligned lane group, one exchange
 // step: the larger of the two firsts, and the larger of the smaller first
 // and the two seconds.
@@ -701,7 +705,7 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
     }
     __builtin_amdgcn_s_sleep(1);
   }
-  if (r == 0) MOE_LSTAMP(p, 9);
+  if (r == tl_row(p)) MOE_LSTAMP(p, 9);
   if (lane == 0)  // rows whose scores are in (see narrow_forward)
     __hip_atomic_fetch_add((__attribute__((address_space(3))) uint32_t*)(L.misc + kMiscPolled), 1u,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -716,7 +720,7 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
     sv[i] = alive[i] ? s : 0.0;
     bv[i] = isnan(b) ? -INFINITY : b;
   }
-  if (r == 0) MOE_LSTAMP(p, 60);
+  if (r == tl_row(p)) MOE_LSTAMP(p, 60);
   if (p.ng > 1) {
     const int gsz = p.E / p.ng, lpg = gsz >> 2;
     if ((gsz & 3) == 0 && lpg <= 64 && (lpg & (lpg - 1)) == 0) {
@@ -777,7 +781,7 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
         if (alive[i]) alive[i] = L.rkept[wave * 64 + (4 * lane + i) / gsz] != 0;
     }
   }
-  if (r == 0) MOE_LSTAMP(p, 14);
+  if (r == tl_row(p)) MOE_LSTAMP(p, 14);
   // Top-k among the alive experts by (b desc, e asc), in two steps.
   // (1) Rounded to fp32, keys keep their order (ties aside), so the k-th
   // largest rounded key t is the rounding of the k-th largest exact key,
@@ -850,7 +854,7 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  if (r == 0) MOE_LSTAMP(p, 15);
+  if (r == tl_row(p)) MOE_LSTAMP(p, 15);
   // every lane forms the same sum in pick order; lane k writes weight k
   double ssum = 0.0;
   for (int k = 0; k < p.K; ++k) ssum += ps[k];
@@ -912,22 +916,28 @@ __device__ __forceinline__ bool held(const Params& p, int e) { return (unsigned)
 // picks of one use (row, slot) until both its words carry the call's tag.
 // The routing arithmetic is the same whichever CU runs it, so the picks
 // are the same bits as when every CU routes every row.
-__device__ inline void route_rows_spread(const Params& p, const Lds& L, uint32_t tag) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Routes row r with the calling wave and publishes its picks (lanes < K).
+__device__ inline void route_publish(const Params& p, const Lds& L, int r, uint32_t tag) {
+  const int lane = threadIdx.x & 63;
   typedef __attribute__((address_space(1))) uint64_t G64;
-  for (int r = (int)blockIdx.x + wave * p.ncu; r < p.T; r += kWaves * p.ncu) {
-    route_row(p, L, r, tag);
-    wave_sync();  // the row's ids and weights, written by single lanes
-    if (lane < p.K) {
-      const uint32_t id = (uint32_t)L.ids[r * p.K + lane];
-      const uint32_t wb = __float_as_uint(L.w[r * p.K + lane]);
-      G64* q = (G64*)p.picks + 2 * (r * p.K + lane);
-      __hip_atomic_store(q, ((uint64_t)tag << 32) | id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(q + 1, ((uint64_t)tag << 32) | wb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+  route_row(p, L, r, tag);
+  wave_sync();  // the row's ids and weights, written by single lanes
+  if (lane < p.K) {
+    const uint32_t id = (uint32_t)L.ids[r * p.K + lane];
+    const uint32_t wb = __float_as_uint(L.w[r * p.K + lane]);
+    G64* q = (G64*)p.picks + 2 * (r * p.K + lane);
+    __hip_atomic_store(q, ((uint64_t)tag << 32) | id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, ((uint64_t)tag << 32) | wb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  MOE_LSTAMP(p, 61);
+}
+
+// Reads the picks of uses u0, u0 + step, ... < T*K into L.ids / L.w,
+// polling each until both its words carry the call's tag.
+__device__ inline void read_picks(const Params& p, const Lds& L, uint32_t tag, int u0, int step) {
+  typedef __attribute__((address_space(1))) uint64_t G64;
   const int U = p.T * p.K;
-  for (int u = threadIdx.x; u < U; u += kThreads) {
+  for (int u = u0; u < U; u += step) {
     const G64* q = (const G64*)p.picks + 2 * u;
     uint64_t a = 0, b = 0;
     for (int spins = 0;;) {
@@ -943,6 +953,13 @@ __device__ inline void route_rows_spread(const Params& p, const Lds& L, uint32_t
     L.ids[u] = (int32_t)(uint32_t)a;
     L.w[u] = __uint_as_float((uint32_t)b);
   }
+}
+
+__device__ inline void route_rows_spread(const Params& p, const Lds& L, uint32_t tag) {
+  const int wave = threadIdx.x >> 6;
+  for (int r = (int)blockIdx.x + wave * p.ncu; r < p.T; r += kWaves * p.ncu) route_publish(p, L, r, tag);
+  read_picks(p, L, tag, (int)threadIdx.x, kThreads);
+  MOE_STAMP(p, 63);
 }
 
 // The grouping of up to 64 uses by one wave (the narrow stream's wave 7),
@@ -2199,8 +2216,37 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
     ph.nct = p.n_shared ? n_ctiles(p, p.T) : 1;
     ph.nsc = nS * ph.nw;
     const bool early = p.T <= kWaves && p.T * p.K <= 64 && nS > 0;
+    const bool spread = early && p.T >= kSpreadRows;
     MOE_STAMP(p, 2);
-    if (early) {
+    if (spread) {
+      // Each row is routed by wave 7 of one CU (row r: CU r mod ncu), which
+      // publishes its picks; wave 7 of every CU then reads every row's
+      // picks, groups the uses and writes the routed tables.  Waves 0..6
+      // start on the CU's shared-expert chunks at once, except on a CU that
+      // routes a row, where they wait until its scores are in.
+      int here = 0;
+      for (int r = (int)blockIdx.x; r < p.T; r += p.ncu) ++here;
+      if (wave == kWaves - 1) {
+        __builtin_amdgcn_s_setprio(3);
+        for (int r = (int)blockIdx.x; r < p.T; r += p.ncu) route_publish(p, L, r, epoch + 1);
+        read_picks(p, L, epoch + 1, threadIdx.x & 63, 64);
+        wave_sync();
+        MOE_LSTAMP(p, 10);
+        groups_one_wave(p, L);
+        wave_sync();
+        MOE_LSTAMP(p, 3);
+        const int G = lds_ldi_uniform(L.misc);
+        const Sched s = make_sched(p, G);
+        routed_tables<1>(p, L, s, nS);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the up/gate tables, before the flag
+        lds_st32(L.misc + kMiscReady, 1u);
+        routed_tables<2>(p, L, s, nS);
+        __builtin_amdgcn_s_setprio(0);
+        MOE_LSTAMP(p, 11);
+      } else if (here > 0) {
+        lds_wait<1>(p, (const uint32_t*)L.misc + kMiscPolled, (uint32_t)here, ok);
+      }
+    } else if (early) {
       // The top T waves route (row r by wave 7 - r; the scores of a batch
       // under 8 rows are published by wave 0), wave 7 then groups.  The
       // streaming waves start once every row's scores are in: their loads

@@ -26,10 +26,12 @@ NAMES = {
     0: "kernel start",
     1: "logits stored",
     2: "routing start",
-    9: "row 0 scores in (its routing wave)",
+    9: "row 0 scores in (its routing wave; above 8 rows: each routing CU's row)",
     60: "row 0 keys formed",
     14: "row 0 group stage done",
     15: "row 0 top-k done",
+    61: "above 8 rows: picks stored (routing CUs)",
+    63: "above 8 rows: thread 0 has its picks",
     10: "all rows routed",
     3: "groups built",
     11: "tables written",
