@@ -172,7 +172,7 @@ extern __shared__ __attribute__((aligned(16))) char moe_tl_smem[];
   } while (0)
 #define MOE_JSTAMP(p, jc)                                                                \
   do {                                                                                   \
-    if (threadIdx.x == 0 && (p).timeline && (jc) < 20)                                   \
+    if (threadIdx.x == 0 && (p).timeline && (jc) < 12)                                   \
       MOE_TL(p, 40 + (jc)) = __builtin_amdgcn_s_memrealtime();                           \
   } while (0)
 #define MOE_TVAL(p, i, v)                                                                \
@@ -804,6 +804,7 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
     }
     if (t == 0u) break;  // fewer alive experts than k (not reachable with validated shapes)
   }
+  if (r == tl_row(p)) MOE_LSTAMP(p, 56);
   // (2) The candidates go to LDS in expert order; each is ranked exactly
   // by (b desc, e asc) against all of them.
   double* cb = L.rcb + (size_t)wave * p.E;
@@ -824,6 +825,7 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  if (r == tl_row(p)) MOE_LSTAMP(p, 57);
   double* ps = L.rgs + (size_t)wave * 64;  // the winners' s in pick order
   if (nc <= 8) {
     // lane 8a + c compares candidate c with candidate a; a's rank is the
@@ -859,6 +861,7 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
   double ssum = 0.0;
   for (int k = 0; k < p.K; ++k) ssum += ps[k];
   if (lane < p.K) L.w[r * p.K + lane] = (float)(ps[lane] / ssum * p.routed_scale);
+  if (r == tl_row(p)) MOE_LSTAMP(p, 58);
 }
 
 // ------------------------------------------------------------------ S2 grouping
@@ -2270,6 +2273,7 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
         routed_tables<1>(p, L, s, nS);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the up/gate tables, before the flag
         lds_st32(L.misc + kMiscReady, 1u);
+        MOE_LSTAMP(p, 59);
         // the down tables are read after the phase barrier
         routed_tables<2>(p, L, s, nS);
         __builtin_amdgcn_s_setprio(0);

@@ -29,7 +29,11 @@ NAMES = {
     9: "row 0 scores in (its routing wave; above 8 rows: each routing CU's row)",
     60: "row 0 keys formed",
     14: "row 0 group stage done",
+    56: "row 0 top-k threshold found",
+    57: "row 0 top-k candidates in LDS",
     15: "row 0 top-k done",
+    58: "row 0 weights formed",
+    59: "routed up/gate tables ready",
     61: "above 8 rows: picks stored (routing CUs)",
     63: "above 8 rows: thread 0 has its picks",
     10: "all rows routed",
