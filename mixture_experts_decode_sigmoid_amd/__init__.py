@@ -7,6 +7,7 @@ CPU fallback: if libmoe.so is missing or cannot be loaded, every call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes as C
 import os
 
@@ -71,6 +72,41 @@ def use_library(path: str) -> None:
     _lib_path = path
 
 
+def load_library(path: str, strict: bool = True) -> C.CDLL:
+    """Loads the build of the library at `path` with its argument types set.
+    Several builds can be loaded side by side, each with its own kernels (the
+    A/B tool does so).  strict=False skips entry points a build lacks."""
+    L = C.CDLL(path)
+    P, I, Z = C.c_void_p, C.c_int, C.c_size_t
+    sig = {
+        "moe_workspace_size": [C.POINTER(MoeConfig), C.POINTER(C.c_size_t)],
+        "moe_workspace_init": [P, Z, P],
+        "moe_route": [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, P, Z, P],
+        "moe_groups": [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, Z, P],
+        "moe_forward": [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, Z, P],
+        "moe_forward_residual": [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, P, Z, P],
+        "moe_read_error": [P, P, C.POINTER(C.c_uint32)],
+        "moe_strerror": [I],
+        "moe_last_hip_error": [],
+        "moe_probe_stream_read": [P, Z, P, I, P],
+        "moe_forward_noalloc": [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P],
+        "moe_forward_prefill": [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, Z, P],
+        "moe_forward_unfused": [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, P, P, Z, P],
+        "moe_forward_after": [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, P, Z, P,
+                              C.c_uint32, C.c_uint32, P],
+    }
+    for name, args in sig.items():
+        try:
+            f = getattr(L, name)
+        except AttributeError:
+            if strict:
+                raise
+            continue
+        f.argtypes = args
+        f.restype = C.c_char_p if name == "moe_strerror" else C.c_int
+    return L
+
+
 def lib() -> C.CDLL:
     """The loaded libmoe.so (raises if it is missing: no fallback)."""
     global _lib
@@ -78,31 +114,20 @@ def lib() -> C.CDLL:
         if not os.path.exists(_lib_path):
             raise RuntimeError(f"{_lib_path} is missing: build it with "
                                "`python -m mixture_experts_decode_sigmoid_amd.build`")
-        L = C.CDLL(_lib_path)
-        P, I, Z = C.c_void_p, C.c_int, C.c_size_t
-        L.moe_workspace_size.argtypes = [C.POINTER(MoeConfig), C.POINTER(C.c_size_t)]
-        L.moe_workspace_init.argtypes = [P, Z, P]
-        L.moe_route.argtypes = [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, P, Z, P]
-        L.moe_groups.argtypes = [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, Z, P]
-        L.moe_forward.argtypes = [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, Z, P]
-        L.moe_forward_residual.argtypes = [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, P, Z, P]
-        L.moe_read_error.argtypes = [P, P, C.POINTER(C.c_uint32)]
-        L.moe_strerror.argtypes = [I]
-        L.moe_strerror.restype = C.c_char_p
-        L.moe_last_hip_error.argtypes = []
-        L.moe_probe_stream_read.argtypes = [P, Z, P, I, P]
-        L.moe_forward_noalloc.argtypes = [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P]
-        L.moe_forward_prefill.argtypes = [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, Z, P]
-        L.moe_forward_unfused.argtypes = [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, P, P, Z, P]
-        L.moe_forward_after.argtypes = [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, P, Z, P,
-                                         C.c_uint32, C.c_uint32, P]
-        for f in ("moe_workspace_size", "moe_workspace_init", "moe_route", "moe_groups",
-                  "moe_forward", "moe_forward_residual", "moe_read_error", "moe_last_hip_error",
-                  "moe_probe_stream_read", "moe_forward_noalloc", "moe_forward_after", "moe_forward_unfused",
-                  "moe_forward_prefill"):
-            getattr(L, f).restype = C.c_int
-        _lib = L
+        _lib = load_library(_lib_path)
     return _lib
+
+
+@contextlib.contextmanager
+def using(L: C.CDLL):
+    """Routes this module's calls to the loaded build L while the block runs."""
+    global _lib
+    prev = _lib
+    _lib = L
+    try:
+        yield L
+    finally:
+        _lib = prev
 
 
 EXPORTS = ("moe_workspace_size", "moe_workspace_init", "moe_route", "moe_groups",

@@ -590,9 +590,13 @@ __device__ inline void router_logits(const Params& p, const Lds& L, uint32_t epo
 // batch size (the two forms are chosen by batch size): the wave walks the 8
 // chunks of H/8 in order, lane l sums the 16-byte groups l and l+64 of a
 // chunk (8 elements each, in order), the lanes are summed by the same fixed
-// tree (wave_sum_d), and the chunk sums are added in chunk order.  The
-// loads of NC chunks are issued before their products are summed (all 8
-// with LATE).  Used from 8 rows up, where every wave has rows of its own.
+// tree (wave_sum_d), and the chunk sums are added in chunk order.  Used from
+// 8 rows up.  The T x E dots are cut into blocks of rb rows by eb experts,
+// one block per CU, with rb and eb near the square root of a CU's share:
+// every CU reads rb rows of x and eb router rows (not every row of x, which
+// at 64 rows made the logits bound by the L2's bandwidth).  Wave w takes the
+// block's dots w, w + 8, ... (row-fastest); when the block's row count
+// divides 8 a wave keeps one row, whose x it loads once.
 // LATE: `v` is the epoch, a load still in flight, first read once the sums
 // are formed (tag = epoch + 1); otherwise `v` is the tag.
 template <bool LATE>
@@ -601,50 +605,63 @@ __device__ inline void router_logits_rows(const Params& p, uint32_t v) {
   if (wave >= kWaves) return;
   const int ch = p.H / kWaves, ngrp = ch >> 3;
   const int g0 = lane < ngrp ? lane : ngrp - 1, g1 = lane + 64 < ngrp ? lane + 64 : g0;
-  constexpr int NC = LATE ? kWaves : kWaves / 2;
-  for (int e = blockIdx.x; e < p.E; e += p.ncu) {
+  int pr = 1;  // row blocks (a power of two); pe = ncu / pr expert blocks
+  while (pr < p.T && 2 * pr <= p.ncu && 4 * pr * pr * p.E <= p.T * p.ncu) pr *= 2;
+  while ((p.T + pr - 1) / pr > kWaves && 2 * pr <= p.ncu) pr *= 2;
+  const int pe = p.ncu / pr;
+  const int rb = (p.T + pr - 1) / pr, eb = (p.E + pe - 1) / pe;
+  const int c = (int)blockIdx.x;
+  if (c >= pr * pe) return;
+  const int r0 = (c / pe) * rb, e0 = (c % pe) * eb;
+  const int nr = p.T - r0 < rb ? p.T - r0 : rb, ne = p.E - e0 < eb ? p.E - e0 : eb;
+  if (nr <= 0 || ne <= 0) return;
+  u32x4 xv[kWaves][2];
+  int xrow = -1;
+  for (int d = wave; d < nr * ne; d += kWaves) {
+    const int r = r0 + d % nr, e = e0 + d / nr;
+    if (r != xrow) {
+      const uint16_t* xr = p.x + (size_t)r * p.H;
+#pragma unroll
+      for (int k = 0; k < kWaves; ++k) {
+        xv[k][0] = ld16(xr + (size_t)k * ch + 8 * g0);
+        xv[k][1] = ld16(xr + (size_t)k * ch + 8 * g1);
+      }
+      xrow = r;
+    }
     const uint16_t* wr = p.router_w + (size_t)e * p.H;
+    u32x4 wv[kWaves][2];
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+      wv[k][0] = ld16(wr + (size_t)k * ch + 8 * g0);
+      wv[k][1] = ld16(wr + (size_t)k * ch + 8 * g1);
+    }
     // LATE: the bias bits are converted once the sums are formed
     const uint32_t braw = LATE ? load_bias_raw(p, e) : 0u;
     const double bias = LATE ? 0.0 : load_bias(p, e);
-    for (int r = wave; r < p.T; r += kWaves) {
-      const uint16_t* xr = p.x + (size_t)r * p.H;
-      double l = 0.0;
-      for (int c0 = 0; c0 < kWaves; c0 += NC) {
-        u32x4 xv[NC][2], wv[NC][2];
+    double l = 0.0;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const size_t o = (size_t)(c0 + c) * ch;
-          xv[c][0] = ld16(xr + o + 8 * g0);
-          wv[c][0] = ld16(wr + o + 8 * g0);
-          xv[c][1] = ld16(xr + o + 8 * g1);
-          wv[c][1] = ld16(wr + o + 8 * g1);
-        }
+    for (int k = 0; k < kWaves; ++k) {
+      double acc = 0.0;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          double acc = 0.0;
+      for (int q = 0; q < 2; ++q) {
+        if (q == 0 ? lane < ngrp : lane + 64 < ngrp) {
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            if (q == 0 ? lane < ngrp : lane + 64 < ngrp) {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const uint32_t xa = xv[c][q][i], wa = wv[c][q][i];
-                acc = fma((double)bf16_bits_to_f32(xa & 0xffffu), (double)bf16_bits_to_f32(wa & 0xffffu), acc);
-                acc = fma((double)bf16_bits_to_f32(xa >> 16), (double)bf16_bits_to_f32(wa >> 16), acc);
-              }
-            }
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t xa = xv[k][q][i], wa = wv[k][q][i];
+            acc = fma((double)bf16_bits_to_f32(xa & 0xffffu), (double)bf16_bits_to_f32(wa & 0xffffu), acc);
+            acc = fma((double)bf16_bits_to_f32(xa >> 16), (double)bf16_bits_to_f32(wa >> 16), acc);
           }
-          l += wave_sum_d(acc);
         }
       }
-      uint32_t ep = v, br = braw;
-      if (LATE) asm volatile("" : "+v"(ep), "+v"(br));
-      if (lane == 0) {
-        double s = 1.0 / (1.0 + exp(-l));
-        double b = s + (LATE ? bias_from_raw(p, br) : bias);
-        if (!isfinite(l) || !isfinite(b)) set_err(p.err, kErrScore);
-        publish_score(p, r, e, s, LATE ? ep + 1 : v);
-      }
+      l += wave_sum_d(acc);
+    }
+    uint32_t ep = v, br = braw;
+    if (LATE) asm volatile("" : "+v"(ep), "+v"(br));
+    if (lane == 0) {
+      double s = 1.0 / (1.0 + exp(-l));
+      double b = s + (LATE ? bias_from_raw(p, br) : bias);
+      if (!isfinite(l) || !isfinite(b)) set_err(p.err, kErrScore);
+      publish_score(p, r, e, s, LATE ? ep + 1 : v);
     }
   }
 }
