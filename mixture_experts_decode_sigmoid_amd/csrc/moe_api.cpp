@@ -132,6 +132,17 @@ int fill(const moe_config* c, const moe_weights* w, const uint16_t* x, int rows,
   p.hs = hs;
   p.ncu = d.ncu;
   p.mid_ld = L.mid_ld;
+  // up to 8 rows every wave may route a row; above, a forward call routes
+  // row r on wave r / ncu of CU r mod ncu (or on wave 7, while the other
+  // waves stream), and the routing-only calls route on every wave of one CU
+  // with no stream running
+  if (rows <= kWaves || mode != kModeForward) {
+    p.rslots = kWaves;
+    p.rsover = rows > kWaves;
+  } else {
+    p.rslots = (rows + d.ncu - 1) / d.ncu;
+    p.rsover = 0;
+  }
   size_t lds = stream_geometry(p);
   if (lds > d.max_lds) return MOE_ERR_SHAPE;
   if (lds < (size_t)kMinLds) lds = kMinLds;

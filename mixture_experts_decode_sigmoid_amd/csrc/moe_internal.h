@@ -57,6 +57,8 @@ struct Params {
   int ncu;         // workgroups launched (= CUs)
   int mid_ld;
   int lds_bytes;   // dynamic LDS size
+  int rslots;      // routing scratch slots (one per wave that routes at once)
+  int rsover;      // 1: the routing scratch may share LDS with the stream partials (no stream runs while routing)
   // stream geometry (see lds_offsets)
   int nrt_p;       // 16-row down tiles of a CU's slice, rounded up to 1, 2 or 4
   int kph;         // K-phases of a down sum: waves per down tile (8 / nrt_p); every

@@ -278,15 +278,16 @@ __host__ __device__ inline LdsOffsets lds_offsets(const Params& p) {
   o.ctl = q; q = align_up(q + 4 * 64, 16);
   o.wst = q; q = align_up(q + 8 * kPuWin + 16 + 4 * kWaves * 8, 16);
   o.jd = q; q = align_up(q + kJobDescBytes * (size_t)(p.qcap + p.dcap), 16);
-  // routing scratch: rb, rgs, rkept, then the top-k candidates (b, s, e) per wave
+  // routing scratch: rb, rgs, rkept, then the top-k candidates (b, s, e),
+  // one slot per wave that routes at once
   o.rs = q;
-  const size_t rs = 8 * (size_t)kWaves * E + 8 * (size_t)kWaves * 64 + 4 * (size_t)kWaves * 64 +
-                    20 * (size_t)kWaves * E;
+  const size_t ns = (size_t)p.rslots;
+  const size_t rs = 8 * ns * E + 8 * ns * 64 + 4 * ns * 64 + 20 * ns * E;
   const size_t pu = 4 * (size_t)kPuWin * kWaves * p.pcols * 16;
   const size_t pd = 4 * (size_t)p.wpt * T * (K + 1) * p.pitch;
   const size_t need = pu > pd ? pu : pd;
   size_t end;
-  if (T <= kWaves) {
+  if (!p.rsover) {
     o.pbuf = align_up(q + rs, 16);
     end = o.pbuf + need;
   } else {
@@ -340,12 +341,13 @@ __device__ inline Lds lds_map(char* base, const Params& p) {
   L.ccnt = L.wgen + kPuWin;
   L.cfifo = L.ccnt + 4;
   L.pbuf = (float*)(base + o.pbuf);
+  const size_t ns = (size_t)p.rslots;
   L.rb = (double*)(base + o.rs);
-  L.rgs = L.rb + (size_t)kWaves * p.E;
-  L.rkept = (int32_t*)(L.rgs + (size_t)kWaves * 64);
-  L.rcb = (double*)(L.rkept + (size_t)kWaves * 64);
-  L.rcs = L.rcb + (size_t)kWaves * p.E;
-  L.rce = (int32_t*)(L.rcs + (size_t)kWaves * p.E);
+  L.rgs = L.rb + ns * p.E;
+  L.rkept = (int32_t*)(L.rgs + ns * 64);
+  L.rcb = (double*)(L.rkept + ns * 64);
+  L.rcs = L.rcb + ns * p.E;
+  L.rce = (int32_t*)(L.rcs + ns * p.E);
   return L;
 }
 
@@ -688,9 +690,10 @@ __device__ __forceinline__ void top2_step(double& t1, double& t2) {
 // two) is an aligned run of m lanes.
 // Polls row r's score slots (agent-scope loads) until every one carries
 // this call's tag (bounded: on timeout the error bit is set and routing
-// runs on).
-__device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t tag) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// runs on).  `slot`: the wave's part of the routing scratch (waves that
+// route at the same time use different slots).
+__device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t tag, int slot) {
+  const int lane = threadIdx.x & 63;
   typedef __attribute__((address_space(1))) uint64_t G64;
   const G64* sc = (const G64*)p.scores + score_slot(p, r, 0) * 2;  // the row's first slot
   const int e4 = slot_e4(p.E);
@@ -768,7 +771,7 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
 #pragma unroll
       for (int i = 0; i < 4; ++i) alive[i] = alive[i] && rank < p.kg;
     } else {
-      double* rb = L.rb + (size_t)wave * p.E;
+      double* rb = L.rb + (size_t)slot * p.E;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (alive[i]) rb[4 * lane + i] = bv[i];
@@ -781,21 +784,21 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
           if (v > t1) { t2 = t1; t1 = v; }
           else if (v > t2) { t2 = v; }
         }
-        L.rgs[wave * 64 + lane] = t1 + t2;
+        L.rgs[slot * 64 + lane] = t1 + t2;
       }
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       if (lane < p.ng) {
-        const double mine = L.rgs[wave * 64 + lane];
+        const double mine = L.rgs[slot * 64 + lane];
         int rank = 0;
-        for (int j = 0; j < p.ng; ++j) rank += key_before(L.rgs[wave * 64 + j], j, mine, lane) ? 1 : 0;
-        L.rkept[wave * 64 + lane] = rank < p.kg;
+        for (int j = 0; j < p.ng; ++j) rank += key_before(L.rgs[slot * 64 + j], j, mine, lane) ? 1 : 0;
+        L.rkept[slot * 64 + lane] = rank < p.kg;
       }
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (alive[i]) alive[i] = L.rkept[wave * 64 + (4 * lane + i) / gsz] != 0;
+        if (alive[i]) alive[i] = L.rkept[slot * 64 + (4 * lane + i) / gsz] != 0;
     }
   }
   if (r == tl_row(p)) MOE_LSTAMP(p, 14);
@@ -824,9 +827,9 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
   if (r == tl_row(p)) MOE_LSTAMP(p, 56);
   // (2) The candidates go to LDS in expert order; each is ranked exactly
   // by (b desc, e asc) against all of them.
-  double* cb = L.rcb + (size_t)wave * p.E;
-  double* cs = L.rcs + (size_t)wave * p.E;
-  int32_t* ce = L.rce + (size_t)wave * p.E;
+  double* cb = L.rcb + (size_t)slot * p.E;
+  double* cs = L.rcs + (size_t)slot * p.E;
+  int32_t* ce = L.rce + (size_t)slot * p.E;
   int nc = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -843,7 +846,7 @@ __device__ inline void route_row(const Params& p, const Lds& L, int r, uint32_t 
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   if (r == tl_row(p)) MOE_LSTAMP(p, 57);
-  double* ps = L.rgs + (size_t)wave * 64;  // the winners' s in pick order
+  double* ps = L.rgs + (size_t)slot * 64;  // the winners' s in pick order
   if (nc <= 8) {
     // lane 8a + c compares candidate c with candidate a; a's rank is the
     // count of its lane group's bits
@@ -936,11 +939,12 @@ __device__ __forceinline__ bool held(const Params& p, int e) { return (unsigned)
 // picks of one use (row, slot) until both its words carry the call's tag.
 // The routing arithmetic is the same whichever CU runs it, so the picks
 // are the same bits as when every CU routes every row.
-// Routes row r with the calling wave and publishes its picks (lanes < K).
-__device__ inline void route_publish(const Params& p, const Lds& L, int r, uint32_t tag) {
+// Routes row r with the calling wave (routing scratch `slot`) and publishes
+// its picks (lanes < K).
+__device__ inline void route_publish(const Params& p, const Lds& L, int r, uint32_t tag, int slot) {
   const int lane = threadIdx.x & 63;
   typedef __attribute__((address_space(1))) uint64_t G64;
-  route_row(p, L, r, tag);
+  route_row(p, L, r, tag, slot);
   wave_sync();  // the row's ids and weights, written by single lanes
   if (lane < p.K) {
     const uint32_t id = (uint32_t)L.ids[r * p.K + lane];
@@ -952,86 +956,137 @@ __device__ inline void route_publish(const Params& p, const Lds& L, int r, uint3
   MOE_LSTAMP(p, 61);
 }
 
-// Reads the picks of uses u0, u0 + step, ... < T*K into L.ids / L.w,
-// polling each until both its words carry the call's tag.
+// Reads the picks of uses u0, u0 + step, ... < T*K (at most PER per lane)
+// into L.ids / L.w, polling them together (one round trip per round, the
+// later rounds reloading only the uses still missing) until both words of
+// each carry the call's tag.
+template <int PER>
 __device__ inline void read_picks(const Params& p, const Lds& L, uint32_t tag, int u0, int step) {
   typedef __attribute__((address_space(1))) uint64_t G64;
+  constexpr int kPer = PER;
   const int U = p.T * p.K;
-  for (int u = u0; u < U; u += step) {
-    const G64* q = (const G64*)p.picks + 2 * u;
-    uint64_t a = 0, b = 0;
-    for (int spins = 0;;) {
-      a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if ((uint32_t)(a >> 32) == tag && (uint32_t)(b >> 32) == tag) break;
-      if (++spins > kSpinLimit) {
-        set_err(p.err, kErrTimeout);
-        break;
+  uint64_t a[kPer], b[kPer];
+  bool got[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    got[i] = u0 + i * step >= U;
+    a[i] = 0;
+    b[i] = 0;
+  }
+  for (int spins = 0;;) {
+    bool all = true;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (!got[i]) {
+        const G64* q = (const G64*)p.picks + 2 * (u0 + i * step);
+        a[i] = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        b[i] = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      __builtin_amdgcn_s_sleep(2);
     }
-    L.ids[u] = (int32_t)(uint32_t)a;
-    L.w[u] = __uint_as_float((uint32_t)b);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (!got[i]) got[i] = (uint32_t)(a[i] >> 32) == tag && (uint32_t)(b[i] >> 32) == tag;
+      all = all && got[i];
+    }
+    if (__all(all)) break;
+    if (++spins > kSpinLimit) {
+      set_err(p.err, kErrTimeout);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int u = u0 + i * step;
+    if (u < U) {
+      L.ids[u] = (int32_t)(uint32_t)a[i];
+      L.w[u] = __uint_as_float((uint32_t)b[i]);
+    }
   }
 }
 
 __device__ inline void route_rows_spread(const Params& p, const Lds& L, uint32_t tag) {
   const int wave = threadIdx.x >> 6;
-  for (int r = (int)blockIdx.x + wave * p.ncu; r < p.T; r += kWaves * p.ncu) route_publish(p, L, r, tag);
-  read_picks(p, L, tag, (int)threadIdx.x, kThreads);
+  for (int r = (int)blockIdx.x + wave * p.ncu; r < p.T; r += kWaves * p.ncu) route_publish(p, L, r, tag, wave);
+  read_picks<kMaxRows * kMaxTopK / kThreads>(p, L, tag, (int)threadIdx.x, kThreads);
   MOE_STAMP(p, 63);
 }
 
-// The grouping of up to 64 uses by one wave (the narrow stream's wave 7),
-// one use per lane, no workgroup barriers.  Uses of experts not held here
-// form no group and get no column.
+// The grouping by one wave (the narrow stream's wave 7) of up to 64 * PER
+// uses, lane l taking uses l + 64 i, no workgroup barriers; the PER passes
+// of each step are unrolled so that their LDS accesses overlap.  Uses of
+// experts not held here form no group and get no column.
+template <int PER>
 __device__ inline void groups_one_wave(const Params& p, const Lds& L) {
   const int lane = threadIdx.x & 63;
   const int U = p.T * p.K;
-  {
-    {
-      const int e = lane < U ? L.ids[lane] : 0, r = lane / p.K;
-      const bool valid = lane < U && held(p, e);
-      if (valid) {
-        L.first[e] = 0xffffffffu;
-        L.rmask[2 * e] = 0u;
-        L.rmask[2 * e + 1] = 0u;
-      }
-      wave_sync();
-      if (valid) {
-        atomicMin(&L.first[e], (uint32_t)lane);
-        atomicOr(&L.rmask[2 * e + (r >> 5)], 1u << (r & 31));
-      }
-      wave_sync();
-      const bool isf = valid && L.first[e] == (uint32_t)lane;
-      const unsigned long long m = __ballot(isf);
-      const int G = p.n_shared + __popcll(m);
-      if (isf) {
-        const int g = p.n_shared + __popcll(m & ((1ull << lane) - 1ull));
-        L.egrp[e] = g;
-        L.gexp[g] = e;
-        L.gcnt[g] = __popc(L.rmask[2 * e]) + __popc(L.rmask[2 * e + 1]);
-      }
-      if (lane == 0) {
-        L.misc[0] = G;
-        if (p.n_shared) {
-          L.gexp[0] = -1;
-          L.gcnt[0] = p.T;
-          L.gstart[0] = 0;
-        }
-      }
-      wave_sync();
-      scan_gstart(L, p.n_shared, G, p.n_shared ? p.T : 0);
-      wave_sync();
-      if (p.n_shared && lane < p.T) {
-        L.cols[lane] = lane * 16 + p.K;
-        L.cgrp[lane] = 0;
-      }
-      if (valid) {
-        const int g = L.egrp[e], c = L.gstart[g] + use_rank(L, e, r);
-        L.cols[c] = r * 16 + (lane - r * p.K);
-        L.cgrp[c] = g;
-      }
+  int ev[PER], rv[PER];
+  bool hv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int u = lane + 64 * i;
+    ev[i] = u < U ? L.ids[u] : 0;
+    rv[i] = u / p.K;
+    hv[i] = u < U && held(p, ev[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (hv[i]) {
+      L.first[ev[i]] = 0xffffffffu;
+      L.rmask[2 * ev[i]] = 0u;
+      L.rmask[2 * ev[i] + 1] = 0u;
+    }
+  }
+  wave_sync();
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (hv[i]) {
+      atomicMin(&L.first[ev[i]], (uint32_t)(lane + 64 * i));
+      atomicOr(&L.rmask[2 * ev[i] + (rv[i] >> 5)], 1u << (rv[i] & 31));
+    }
+  }
+  wave_sync();
+  // groups in order of first use
+  uint32_t fv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) fv[i] = hv[i] ? L.first[ev[i]] : 0u;
+  int G = p.n_shared;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const bool isf = hv[i] && fv[i] == (uint32_t)(lane + 64 * i);
+    const unsigned long long m = __ballot(isf);
+    if (isf) {
+      const int g = G + __popcll(m & ((1ull << lane) - 1ull));
+      const int e = ev[i];
+      L.egrp[e] = g;
+      L.gexp[g] = e;
+      L.gcnt[g] = __popc(L.rmask[2 * e]) + __popc(L.rmask[2 * e + 1]);
+    }
+    G += __popcll(m);
+  }
+  if (lane == 0) {
+    L.misc[0] = G;
+    if (p.n_shared) {
+      L.gexp[0] = -1;
+      L.gcnt[0] = p.T;
+      L.gstart[0] = 0;
+    }
+  }
+  wave_sync();
+  scan_gstart(L, p.n_shared, G, p.n_shared ? p.T : 0);
+  wave_sync();
+  if (p.n_shared)
+    for (int r = lane; r < p.T; r += 64) {
+      L.cols[r] = r * 16 + p.K;
+      L.cgrp[r] = 0;
+    }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (hv[i]) {
+      const int e = ev[i], r = rv[i];
+      const int g = L.egrp[e], c = L.gstart[g] + use_rank(L, e, r);
+      L.cols[c] = r * 16 + (lane + 64 * i - r * p.K);
+      L.cgrp[c] = g;
     }
   }
 }
@@ -1040,7 +1095,7 @@ __device__ inline void build_groups(const Params& p, const Lds& L) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int U = p.T * p.K;
   if (U <= 64) {
-    if (wave == 0) groups_one_wave(p, L);
+    if (wave == 0) groups_one_wave<1>(p, L);
     __syncthreads();
     return;
   }
@@ -2236,23 +2291,30 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
     ph.nct = p.n_shared ? n_ctiles(p, p.T) : 1;
     ph.nsc = nS * ph.nw;
     const bool early = p.T <= kWaves && p.T * p.K <= 64 && nS > 0;
-    const bool spread = early && p.T >= kSpreadRows;
+    const bool spread = nS > 0 && p.T >= kSpreadRows && (early || p.T > kWaves);
     MOE_STAMP(p, 2);
     if (spread) {
-      // Each row is routed by wave 7 of one CU (row r: CU r mod ncu), which
-      // publishes its picks; wave 7 of every CU then reads every row's
-      // picks, groups the uses and writes the routed tables.  Waves 0..6
-      // start on the CU's shared-expert chunks at once, except on a CU that
-      // routes a row, where they wait until its scores are in.
+      // From 8 rows up each row is routed by wave 7 of one CU (row r: CU
+      // r mod ncu), which publishes its picks; wave 7 of every CU then reads
+      // every row's picks, groups the uses and writes the routed tables.
+      // Waves 0..6 start on the CU's shared-expert chunks at once, except on
+      // a CU that routes a row, where they wait until its scores are in.
       int here = 0;
       for (int r = (int)blockIdx.x; r < p.T; r += p.ncu) ++here;
       if (wave == kWaves - 1) {
         __builtin_amdgcn_s_setprio(3);
-        for (int r = (int)blockIdx.x; r < p.T; r += p.ncu) route_publish(p, L, r, epoch + 1);
-        read_picks(p, L, epoch + 1, threadIdx.x & 63, 64);
-        wave_sync();
-        MOE_LSTAMP(p, 10);
-        groups_one_wave(p, L);
+        for (int r = (int)blockIdx.x; r < p.T; r += p.ncu) route_publish(p, L, r, epoch + 1, 0);
+        if (p.T * p.K <= 64) {
+          read_picks<1>(p, L, epoch + 1, threadIdx.x & 63, 64);
+          wave_sync();
+          MOE_LSTAMP(p, 10);
+          groups_one_wave<1>(p, L);
+        } else {
+          read_picks<kMaxRows * kMaxTopK / 64>(p, L, epoch + 1, threadIdx.x & 63, 64);
+          wave_sync();
+          MOE_LSTAMP(p, 10);
+          groups_one_wave<kMaxRows * kMaxTopK / 64>(p, L);
+        }
         wave_sync();
         MOE_LSTAMP(p, 3);
         const int G = lds_ldi_uniform(L.misc);
@@ -2275,14 +2337,14 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
       const int r = kWaves - 1 - wave;
       if (r < p.T) {
         __builtin_amdgcn_s_setprio(3);
-        route_row(p, L, r, epoch + 1);
+        route_row(p, L, r, epoch + 1, wave);
         if (r != 0) __builtin_amdgcn_s_setprio(0);
         lds_inc_lane0((uint32_t*)(L.misc + kMiscRouted));  // after this wave's ids / w writes (LDS order)
       }
       if (r == 0) {
         lds_wait<1>(p, (const uint32_t*)L.misc + kMiscRouted, (uint32_t)p.T, ok);
         MOE_LSTAMP(p, 10);
-        groups_one_wave(p, L);
+        groups_one_wave<1>(p, L);
         wave_sync();
         MOE_LSTAMP(p, 3);
         const int G = lds_ldi_uniform(L.misc);
@@ -2301,7 +2363,7 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
       if (p.T > kWaves) {
         route_rows_spread(p, L, epoch + 1);
       } else {
-        for (int r = wave; r < p.T; r += kWaves) route_row(p, L, r, epoch + 1);
+        for (int r = wave; r < p.T; r += kWaves) route_row(p, L, r, epoch + 1, wave);
       }
       __syncthreads();
       MOE_STAMP(p, 10);
@@ -2534,7 +2596,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
   MOE_STAMP(p, 1);
   if (blockIdx.x != 0) return;
   MOE_STAMP(p, 2);
-  for (int r = wave; r < p.T; r += kWaves) route_row(p, L, r, epoch + 1);
+  for (int r = wave; r < p.T; r += kWaves) route_row(p, L, r, epoch + 1, wave);
   __syncthreads();
   MOE_STAMP(p, 10);
   if (MODE == kModeRoute) {
