@@ -596,7 +596,8 @@ __device__ inline void router_logits(const Params& p, const Lds& L, uint32_t epo
 // 8 rows up.  The T x E dots are cut into blocks of rb rows by eb experts,
 // one block per CU, with rb and eb near the square root of a CU's share:
 // every CU reads rb rows of x and eb router rows (not every row of x, which
-// at 64 rows made the logits bound by the L2's bandwidth).  Wave w takes the
+// at 64 rows made the logits bound by the L2's bandwidth); at 8 rows the
+// block is one expert's column.  Wave w takes the
 // block's dots w, w + 8, ... (row-fastest); when the block's row count
 // divides 8 a wave keeps one row, whose x it loads once.
 // LATE: `v` is the epoch, a load still in flight, first read once the sums
@@ -607,8 +608,12 @@ __device__ inline void router_logits_rows(const Params& p, uint32_t v) {
   if (wave >= kWaves) return;
   const int ch = p.H / kWaves, ngrp = ch >> 3;
   const int g0 = lane < ngrp ? lane : ngrp - 1, g1 = lane + 64 < ngrp ? lane + 64 : g0;
-  int pr = 1;  // row blocks (a power of two); pe = ncu / pr expert blocks
-  while (pr < p.T && 2 * pr <= p.ncu && 4 * pr * pr * p.E <= p.T * p.ncu) pr *= 2;
+  // row blocks (a power of two; pe = ncu / pr expert blocks).  Up to 8
+  // rows one block row: CU c takes expert c and wave w row w, so the rows
+  // of the fast waves (the older wave of each SIMD) are complete early and
+  // their routing overlaps the wait for the others.
+  int pr = 1;
+  while (p.T > kWaves && pr < p.T && 2 * pr <= p.ncu && 4 * pr * pr * p.E <= p.T * p.ncu) pr *= 2;
   while ((p.T + pr - 1) / pr > kWaves && 2 * pr <= p.ncu) pr *= 2;
   const int pe = p.ncu / pr;
   const int rb = (p.T + pr - 1) / pr, eb = (p.E + pe - 1) / pe;
