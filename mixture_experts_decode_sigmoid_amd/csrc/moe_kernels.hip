@@ -2206,9 +2206,12 @@ __device__ __forceinline__ float down_product(const Params& p, const Lds& L, int
 
 // Each (row, slot, h) product is first summed over its K-phases (in order,
 // into the K-phase 0 copy) by one thread per product, so the row's chain
-// below reads one value per slot.  With one K-phase (claimed down jobs) the
-// products are checked only.  Whole workgroup; ends synchronised.
+// below reads one value per slot.  With one K-phase (claimed down jobs)
+// there is nothing to sum: the combine checks the products.  Whole
+// workgroup; ends synchronised.
+template <bool ONE>
 __device__ inline void sum_kphases(const Params& p, const Lds& L, const Sched& s) {
+  if (ONE) return;
   const size_t kstride = (size_t)p.T * (p.K + 1) * p.pitch;
   const int n = p.T * (p.K + 1) * s.hc;
   for (int t = threadIdx.x; t < n; t += kThreads) {
@@ -2228,15 +2231,37 @@ __device__ inline void sum_kphases(const Params& p, const Lds& L, const Sched& s
 // rounded once (the residual add of the unfused layout, folded in).
 // SHONLY: the shared expert's product alone (the unfused layout's shared
 // down launch).
-template <bool RES, bool SHONLY = false>
+// ONE: one K-phase (claimed down jobs, wpt = 1), so nothing was summed
+// before and the products are checked here; the picks' weights and
+// products are then read before the chain (K <= 8), their LDS reads in
+// flight together (a chain of dependent reads per row is the longer path
+// at 64 rows).
+template <bool RES, bool SHONLY = false, bool ONE = false>
 __device__ inline void combine(const Params& p, const Lds& L, const Sched& s) {
   for (int t = threadIdx.x; t < p.T * s.hc; t += kThreads) {
     const int r = t / s.hc, hl = t - r * s.hc;
     const size_t o = (size_t)r * p.H + s.h0 + hl;
     const uint32_t res = RES && p.residual ? p.residual[o] : 0u;  // issued ahead of the chain
     float acc = p.n_shared ? down_product(p, L, r, p.K, hl) : 0.f;
-    if (!SHONLY)
+    if (ONE) {
+      bool bad = !isfinite(acc);
+      if (!SHONLY) {
+        float wv[kMaxTopK], pv[kMaxTopK];
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k) {
+          wv[k] = k < p.K ? L.w[r * p.K + k] : 0.f;
+          pv[k] = k < p.K ? down_product(p, L, r, k, hl) : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k) {
+          if (k < p.K) acc = fmaf(wv[k], pv[k], acc);
+          bad = bad || !isfinite(pv[k]);
+        }
+      }
+      if (bad) set_err(p.err, kErrMid);
+    } else if (!SHONLY) {
       for (int k = 0; k < p.K; ++k) acc = fmaf(L.w[r * p.K + k], down_product(p, L, r, k, hl), acc);
+    }
     if (RES && p.residual) acc += bf16_bits_to_f32(res);
     p.out[o] = (uint16_t)f32_to_bf16_rne(acc);
   }
@@ -2436,8 +2461,8 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
     const Lds L = lds_map(smem, p);
     const Sched s = make_sched(p, G);
     __syncthreads();
-    sum_kphases(p, L, s);
-    combine<true>(p, L, s);
+    sum_kphases<DCLAIM>(p, L, s);
+    combine<true, false, DCLAIM>(p, L, s);
     MOE_STAMP(p, 7);
 #ifdef MOE_TIMELINE
     __syncthreads();
@@ -2504,8 +2529,8 @@ __device__ __forceinline__ void shared_only(char* smem) {
     ring_run<FMT, 3, false, kRingDD, AL>(p, L, ph, R, 0, nunits, jn, ok);
   }
   __syncthreads();
-  sum_kphases(p, L, s);
-  combine<false, true>(p, L, s);
+  sum_kphases<DCLAIM>(p, L, s);
+  combine<false, true, DCLAIM>(p, L, s);
 }
 
 // A forward after an upstream producer (moe_forward_after): each wave first
