@@ -2217,8 +2217,13 @@ __device__ inline void sum_kphases(const Params& p, const Lds& L, const Sched& s
   for (int t = threadIdx.x; t < n; t += kThreads) {
     const int rs = t / s.hc, hl = t - rs * s.hc;  // rs = row * (K+1) + slot
     float* q = L.pbuf + (size_t)rs * p.pitch + hl;
+    float c[kWaves];  // the copies read before the sum (wpt <= 8), in flight together
+#pragma unroll
+    for (int kp = 0; kp < kWaves; ++kp) c[kp] = kp < s.wpt ? q[kp * kstride] : 0.f;
     float v = 0.f;
-    for (int kp = 0; kp < p.wpt; ++kp) v += q[kp * kstride];
+#pragma unroll
+    for (int kp = 0; kp < kWaves; ++kp)
+      if (kp < s.wpt) v += c[kp];
     if (!isfinite(v)) set_err(p.err, kErrMid);
     q[0] = v;
   }
