@@ -28,6 +28,11 @@ SMALL = [
     ("mxfp4_small", dict(hidden=2048, inter=1536, shared_inter=512, n_experts=16, top_k=6,
                          routed_fmt=1, bias_bf16=1), 16, 16, "corr"),
     ("no_shared", dict(n_shared=0, hidden=512, inter=256, n_experts=12, top_k=3), 7, 17, "iid"),
+    # no shared expert above 8 rows: every routing wave publishes its rows'
+    # picks and every CU reads them before any streaming (nothing to stream
+    # meanwhile); 40 rows: the whole-workgroup grouping and claimed down jobs
+    ("no_shared_t12", dict(n_shared=0, hidden=512, inter=256, n_experts=12, top_k=3), 12, 26, "iid"),
+    ("no_shared_t40", dict(n_shared=0, hidden=512, inter=256, n_experts=24, top_k=4), 40, 27, "corr"),
     ("k_equals_e", dict(n_experts=8, top_k=8, hidden=256, inter=128), 3, 18, "iid"),
     # hidden > 16 * 256: a CU's down slice spans two 16-row tiles (the second ragged)
     ("two_down_tiles", dict(hidden=4352, inter=256, shared_inter=256, n_experts=16, top_k=4), 5, 19, "corr"),
