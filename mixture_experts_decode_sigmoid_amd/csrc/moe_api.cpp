@@ -322,6 +322,13 @@ int moe_forward_unfused(const moe_config* cfg, const moe_weights* w, const uint1
   if (rc == kNoRows) return MOE_OK;
   if (rc) return rc;
   p.out = tmp_shared;
+  // the shared-expert launches are FP8 instances: their tile size is the
+  // FP8 kernels' whatever the routed format
+  {
+    size_t lds = stream_geometry(p, true);
+    if (lds < (size_t)kMinLds) lds = kMinLds;
+    p.lds_bytes = (int)lds;
+  }
   rc = do_launch(p, kModeSharedUp, stream, dev);
   if (rc) return rc;
   rc = do_launch(p, kModeSharedDown, stream, dev);

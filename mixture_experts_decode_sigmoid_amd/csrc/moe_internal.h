@@ -36,6 +36,16 @@ enum Mode {
 // Measured on the DeepSeek-V3 layer at 12 and 16 rows (and the MXFP4 layer
 // at 16): two loads beat four by 12-16% and one by 5-7%.
 __host__ __device__ inline int stream_al(int T) { return T <= 4 ? 1 : 2; }
+// Intermediates per up/gate tile (ti).  An item is one 16-row MFMA tile (8
+// gate rows and their 8 up rows), except in a kernel with MXFP4 routed
+// experts and two activation loads per item: there an item is two tiles (16
+// gate rows, then their 16 up rows) on one activation operand, which halves
+// the activation bytes a CU reads per weight byte (an MXFP4 K-block carries
+// twice the activations of an FP8 one).  Each output element's arithmetic is
+// the same either way.  Measured (paired A/B): MXFP4 16 rows -11.7 us; FP8
+// 8 rows +1.0 and 64 rows +2.9 us, where each chunk then streams twice the
+// bytes and the waves' last chunks end further apart.
+__host__ __device__ inline int stream_ti(int T, int fmt) { return stream_al(T) == 2 && fmt != 0 ? 16 : 8; }
 // Down jobs are split over waves by K-phase up to this many rows; above it
 // every wave claims whole down jobs (the K-phase partials would not fit LDS).
 constexpr int kKsplitRows = 16;
@@ -69,6 +79,7 @@ struct Params {
   int pitch;       // floats per (row, slot) line of the down products (16 * tiles)
   int cpj;         // columns per job (4 * AL); groups with more are split
   int pcols;       // columns of an up/gate partial tile (min(T, cpj))
+  int ti, lti;     // intermediates per up/gate tile (stream_ti) and its log2
   int qcap;        // up/gate job entries of a CU (its share of the most jobs a batch can have)
   int dcap;        // down job entries (one per group and column tile, most a batch can have)
   // inputs
@@ -108,7 +119,9 @@ struct Params {
 WsLayout ws_layout(int max_rows, int E, int K, int H, int I, int Is);
 // Fills the stream geometry of p (T, K, E, I, Is, hs, ncu, n_shared set)
 // and returns the LDS bytes it needs.
-size_t stream_geometry(Params& p);
+// fp8_tiles: the tiles of an FP8-routed instance whatever p.routed_fmt is
+// (the unfused layout's shared-expert launches are FP8 instances).
+size_t stream_geometry(Params& p, bool fp8_tiles = false);
 // Launches the fused kernel instance for p and mode on device `dev` (the
 // current device).  Returns hipErrorCooperativeLaunchTooLarge when one
 // workgroup per CU with p's LDS size cannot be resident on this device.

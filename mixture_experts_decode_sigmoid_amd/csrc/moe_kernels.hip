@@ -237,9 +237,10 @@ constexpr int kMiscND = 6;      // down job entries (groups x column tiles), onc
 
 // Every wave keeps its partial tiles apart in LDS, and they are summed over
 // the waves in wave order:
-//   up/gate  Pu[win][w][col][16], win = local job mod kPuWin (w = 0..7, the
-//            job's K-phase; col < pcols, the job's column; 16 rows: 8 gate
-//            then 8 up), summed by the wave that ends the job's last chunk
+//   up/gate  Pu[win][w][col][2*ti], win = local job mod kPuWin (w = 0..7,
+//            the job's K-phase; col < pcols, the job's column; ti gate rows
+//            then ti up rows), summed by the wave that ends the job's last
+//            chunk
 //   down     Pd[kp][row][slot][pitch]  (kp = 0..wpt-1, the K-phase of the
 //            waves that share a 16-row down tile; h along the slice),
 //            summed in the combine; with wpt = 1 (above kKsplitRows rows)
@@ -283,7 +284,7 @@ __host__ __device__ inline LdsOffsets lds_offsets(const Params& p) {
   o.rs = q;
   const size_t ns = (size_t)p.rslots;
   const size_t rs = 8 * ns * E + 8 * ns * 64 + 4 * ns * 64 + 20 * ns * E;
-  const size_t pu = 4 * (size_t)kPuWin * kWaves * p.pcols * 16;
+  const size_t pu = 4 * (size_t)kPuWin * kWaves * p.pcols * 2 * p.ti;
   const size_t pd = 4 * (size_t)p.wpt * T * (K + 1) * p.pitch;
   const size_t need = pu > pd ? pu : pd;
   size_t end;
@@ -302,7 +303,7 @@ __host__ __device__ inline LdsOffsets lds_offsets(const Params& p) {
 // tiles of each group, and a group of c columns is ceil(c/cpj) jobs per tile;
 // over a batch the routed groups number at most min(E, T*K) with T*K
 // columns, so their column tiles number at most min(E, T*K) + T*K/cpj.
-size_t stream_geometry(Params& p) {
+size_t stream_geometry(Params& p, bool fp8_tiles) {
   const int nrt = (p.hs + 15) / 16;
   p.nrt_p = nrt <= 1 ? 1 : nrt <= 2 ? 2 : 4;
   p.kph = kWaves / p.nrt_p;
@@ -310,10 +311,12 @@ size_t stream_geometry(Params& p) {
   p.pitch = 16 * nrt;
   p.cpj = 4 * stream_al(p.T);
   p.pcols = p.T < p.cpj ? p.T : p.cpj;
+  p.ti = stream_ti(p.T, fp8_tiles ? 0 : p.routed_fmt);
+  p.lti = p.ti == 16 ? 4 : 3;
   const int tk = p.T * p.K;
   const int nct_sh = p.n_shared ? (p.T + p.cpj - 1) / p.cpj : 0;
   const int ct_routed = (p.E < tk ? p.E : tk) + (tk + p.cpj - 1) / p.cpj;
-  const int sh_tiles = p.n_shared ? p.Is / 8 : 0, rt_tiles = p.I / 8;
+  const int sh_tiles = p.n_shared ? p.Is >> p.lti : 0, rt_tiles = p.I >> p.lti;
   const int per_sh = (sh_tiles + p.ncu - 1) / p.ncu, per_rt = (rt_tiles + p.ncu - 1) / p.ncu;
   p.qcap = per_sh * nct_sh + per_rt * ct_routed;
   p.dcap = nct_sh + ct_routed;
@@ -1272,8 +1275,8 @@ __device__ inline uint32_t lds_wait(const Params& p, const uint32_t* a, uint32_t
 }
 
 struct Sched {
-  int sh_tiles;  // shared up/gate tiles (I_s / 8)
-  int rt_tiles;  // routed up/gate tiles per group (I / 8)
+  int sh_tiles;  // shared up/gate tiles (I_s / ti)
+  int rt_tiles;  // routed up/gate tiles per group (I / ti)
   int n_pairs;   // all (group, tile) pairs, known after routing
   int G;         // groups, known after routing
   int h0, hc;    // this CU's down rows
@@ -1321,8 +1324,9 @@ __device__ __forceinline__ void balance(const Lds& L, int jc) {
 struct JobDesc {
   uint64_t wb;        // weights of the job's row 0 (up/gate: gate row 8t; down: the expert's W_down)
   uint64_t sb;        // block scales of that row (FP8 up/gate: its 128-row block row; MXFP4: its row)
-  uint32_t tile;      // up/gate: the 8-intermediate tile
-  uint32_t jump;      // up/gate: rows between lane row 7 (gate) and lane row 8 (up), minus one
+  uint32_t tile;      // up/gate: the tile of ti intermediates
+  uint32_t jump;      // up/gate, ti = 8: rows between lane row 7 (gate) and lane row 8 (up), minus one;
+                      // ti = 16: rows from a gate row to its up row
   uint32_t shi;       // FP8 up/gate: scale bytes from the gate rows' block row to the up rows'; MXFP4: scale bytes per row
   int32_t nkb;        // K-blocks
   int32_t fmt;        // 0 FP8, 1 MXFP4
@@ -1353,7 +1357,7 @@ __device__ inline JobDesc read_desc(const Lds& L, int k) {
   return d;
 }
 
-// The descriptor of an up/gate job (tile `tile` of the expert's 8-row gate
+// The descriptor of an up/gate job (tile `tile` of the expert's ti-row gate
 // and up tiles) or of a down job (the expert's whole W_down).
 __device__ inline JobDesc make_desc(const Params& p, bool up, bool sh, int e, int tile, int ncols, int cbase) {
   const size_t H = p.H, I = p.I;
@@ -1366,7 +1370,8 @@ __device__ inline JobDesc make_desc(const Params& p, bool up, bool sh, int e, in
   d.ncols = ncols;
   d.cbase = cbase;
   d.spare = 0;
-  d.jump = up ? iexp - 8 : 0;
+  const int lti = p.lti;
+  d.jump = up ? (lti == 3 ? iexp - 8 : iexp) : 0;
   d.tile = (uint32_t)tile;
   const uint8_t* w;
   const uint8_t* S;
@@ -1380,8 +1385,8 @@ __device__ inline JobDesc make_desc(const Params& p, bool up, bool sh, int e, in
              : (const uint8_t*)p.sd + 4 * (size_t)e * (H / 128) * (I / 128);
     }
     if (up) {
-      const int nb_lo = (8 * tile) / 128, nb_hi = (iexp + 8 * tile) / 128;
-      w += (size_t)8 * tile * kdim;
+      const int nb_lo = (tile << lti) / 128, nb_hi = (iexp + (tile << lti)) / 128;
+      w += (size_t)(tile << lti) * kdim;
       S += 4 * (size_t)nb_lo * d.nkb;
       d.shi = 4u * (uint32_t)((nb_hi - nb_lo) * d.nkb);
     } else {
@@ -1392,8 +1397,8 @@ __device__ inline JobDesc make_desc(const Params& p, bool up, bool sh, int e, in
     w = up ? p.wgu + (size_t)e * 2 * I * (H / 2) : p.wd + (size_t)e * H * (I / 2);
     S = up ? (const uint8_t*)p.sgu + (size_t)e * 2 * I * (H / 32) : (const uint8_t*)p.sd + (size_t)e * H * (I / 32);
     if (up) {
-      w += (size_t)8 * tile * (kdim / 2);
-      S += (size_t)8 * tile * d.shi;
+      w += (size_t)(tile << lti) * (kdim / 2);
+      S += (size_t)(tile << lti) * d.shi;
     }
   }
   d.wb = (uint64_t)w;
@@ -1432,7 +1437,7 @@ __device__ __forceinline__ int n_ctiles(const Params& p, int c) { return (c + p.
 
 // This CU's shared-expert pairs (dealt c, c + ncu, ...) and their jobs.
 __device__ __forceinline__ int shared_pairs_here(const Params& p) {
-  const int sh_tiles = p.n_shared ? p.Is / 8 : 0;
+  const int sh_tiles = p.n_shared ? p.Is >> p.lti : 0;
   return (int)blockIdx.x < sh_tiles ? (sh_tiles - 1 - (int)blockIdx.x) / p.ncu + 1 : 0;
 }
 __device__ __forceinline__ int shared_jobs_here(const Params& p) { return shared_pairs_here(p) * n_ctiles(p, p.T); }
@@ -1607,7 +1612,15 @@ struct FetchN {
   const uint8_t* ab;             // activations: x or mid
   uint32_t wo, so, ao;           // this lane's offsets of the next item
   uint32_t h2;                   // MXFP4 items: the second half's activation offset (FP8 items: 0)
+  uint32_t wj, sj;               // two-tile items: bytes from a tile-A row's weights (MXFP4: scales) to its tile-B row's
 };
+
+// Weight tiles per item (see stream_ti): up/gate items of a kernel with
+// MXFP4 routed experts and two activation loads are two 16-row tiles (gate
+// rows, then their up rows) on one activation operand; every other item is
+// one tile.
+template <int FMT, int KIND, int AL>
+constexpr int item_wt() { return FMT != 0 && KIND == 1 && AL == 2 ? 2 : 1; }
 
 // One item: a K-block of a 16-row tile, 128 bytes of each row (FP8: 128
 // values, one fp32 block scale per 128-row block; MXFP4: 256 values, the
@@ -1615,8 +1628,8 @@ struct FetchN {
 // values (2*AL in a kernel with MXFP4 experts, whose FP8 items repeat the
 // first AL as the second).
 struct ItemN {
-  u32x4 w0, w1, B[8];
-  uint32_t s;
+  u32x4 w0, w1, w2, w3, B[8];  // w2, w3: a two-tile item's tile B
+  uint32_t s, s2;
 };
 
 // Column code (row*16 + slot) of this lane's column in a job (a lane past
@@ -1643,7 +1656,9 @@ __device__ __forceinline__ void fetch_from_desc(const Params& p, const PhaseN& p
                                                 int n, int code) {
   const int lane = threadIdx.x & 63, lg = lane >> 4, row = lane & 15;
   const int fmt = FMT == 0 ? 0 : d.fmt;
-  const uint32_t lrow = KIND == 1 ? (row < 8 ? row : row + d.jump) : ph.hb + (row < ph.nlive ? row : ph.nlive - 1);
+  constexpr int WT = item_wt<FMT, KIND, AL>();
+  const uint32_t lrow = KIND == 1 ? (WT == 2 ? row : row < 8 ? row : row + d.jump)
+                                  : ph.hb + (row < ph.nlive ? row : ph.nlive - 1);
   f.wb = (const uint8_t*)d.wb;
   // 128 bytes of each row per K-block, 32 per lane group
   f.wo = lmul(lrow, (uint32_t)(d.nkb * 128)) + (uint32_t)k0 * 128u + (uint32_t)lg * 32u;
@@ -1669,6 +1684,8 @@ __device__ __forceinline__ void fetch_from_desc(const Params& p, const PhaseN& p
   f.fmt = fmt;
   f.nstep = 1 << ph_lstep<KIND>(ph);
   f.left = n;
+  f.wj = WT == 2 ? d.jump * (uint32_t)(d.nkb * 128) : 0u;
+  f.sj = WT == 2 && fmt ? d.jump * d.shi : 0u;
 }
 
 // Past the last job: dead items load from the start of x (weights and
@@ -1687,6 +1704,8 @@ __device__ __forceinline__ void fetch_dead(const Params& p, FetchN& f) {
   f.fmt = 0;
   f.nstep = 0;
   f.left = 1 << 30;
+  f.wj = 0;
+  f.sj = 0;
 }
 
 // Down: moves the fetch side to the next job of [f.k, kend) with items for
@@ -1813,12 +1832,19 @@ __device__ __forceinline__ void fetch_next_any(const Params& p, const Lds& L, co
   else fetch_next_n<FMT, KIND, AL>(p, L, ph, f, kend);
 }
 
-template <int FMT>
+template <int FMT, int WT>
 __device__ __forceinline__ void fetch_weights_n(const FetchN& f, ItemN& it) {
   const uint8_t* w = f.wb + f.wo;
   it.w0 = ldg<u32x4>(w);
   it.w1 = ldg<u32x4>(w + 16);
+  if (WT == 2) {
+    it.w2 = ldg<u32x4>(w + f.wj);
+    it.w3 = ldg<u32x4>(w + f.wj + 16);
+  }
   it.s = ldg<uint32_t>(f.sb + f.so);
+  // an MXFP4 tile B has scales of its own (FP8: the up rows' block scale is
+  // lane 32's word of s); an FP8 item of such a kernel loads s again
+  if (WT == 2 && FMT != 0) it.s2 = ldg<uint32_t>(f.sb + f.so + f.sj);
 }
 // Activations: AL loads of 16 B per lane per 128 values, pieces j + G*i
 // (the load instructions, not the bytes, are what the vector memory path
@@ -1835,9 +1861,9 @@ __device__ __forceinline__ void fetch_acts_n(const uint8_t* ab, uint32_t ao, uin
     for (int i = 0; i < AL; ++i) it.B[AL + i] = ldg<u32x4>(a + h2 + 16 * (4 / AL) * i);
   }
 }
-template <int FMT, int AL>
+template <int FMT, int AL, int WT>
 __device__ __forceinline__ void fetch_item_n(const FetchN& f, ItemN& it) {
-  fetch_weights_n<FMT>(f, it);
+  fetch_weights_n<FMT, WT>(f, it);
   fetch_acts_n<FMT, AL>(f.ab, f.ao, f.h2, it);
 }
 
@@ -1905,7 +1931,8 @@ __device__ inline bool eat_next_up(const Params& p, const Lds& L, const PhaseN& 
   e.left = ((d.nkb - 1 - kp) >> 3) + 1;
   e.fmt = FMT == 0 ? 0 : d.fmt;
   e.pst = col < d.ncols && (lane & (4 / AL - 1)) == 0;
-  e.pidx = ((((uint32_t)q & (kPuWin - 1)) * kWaves + (uint32_t)kp) * (uint32_t)p.pcols + (uint32_t)col) * 16u +
+  e.pidx = ((((uint32_t)q & (kPuWin - 1)) * kWaves + (uint32_t)kp) * (uint32_t)p.pcols + (uint32_t)col) *
+               (16u * (uint32_t)item_wt<FMT, 1, AL>()) +
            4u * (uint32_t)lg;
   return true;
 }
@@ -1967,13 +1994,16 @@ __device__ inline bool dc_phase_end(const Params& p, const Lds& L, const PhaseN&
 // Up/gate job q is complete in partial window win (waves 0..nw-1 stored):
 // every (column, intermediate) is summed over the 8 waves in order (a wave
 // without items adds zero), gate and up, and its SwiGLU value goes to mid as
-// bf16.  One wave; lane = (column, pair of intermediates).
+// bf16.  One wave; lane = (column, pair of intermediates); a column's 8*WT
+// gate rows come first, then their up rows.
+template <int WT>
 __device__ inline void up_reduce_job(const Params& p, const Lds& L, int q, int win, int nw) {
   const JobDesc d = read_desc(L, q);
-  const int lane = threadIdx.x & 63, col = lane >> 2, i2 = 2 * (lane & 3);
+  constexpr int per = 4 * WT;  // pairs of intermediates per column
+  const int lane = threadIdx.x & 63, col = lane / per, i2 = 2 * (lane % per);
   if (col < d.ncols) {
-    const size_t wstride = (size_t)p.pcols * 16;
-    const float* pu = L.pbuf + ((size_t)win * kWaves * p.pcols + col) * 16 + i2;
+    const size_t wstride = (size_t)p.pcols * 16 * WT;
+    const float* pu = L.pbuf + ((size_t)win * kWaves * p.pcols + col) * 16 * WT + i2;
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f;
 #pragma unroll
@@ -1981,7 +2011,7 @@ __device__ inline void up_reduce_job(const Params& p, const Lds& L, int q, int w
       f32x2 gv = {0.f, 0.f}, uv = {0.f, 0.f};
       if (w < nw) {
         gv = lds_get<f32x2>(pu + w * wstride);
-        uv = lds_get<f32x2>(pu + w * wstride + 8);
+        uv = lds_get<f32x2>(pu + w * wstride + 8 * WT);
       }
       g0 += gv[0];
       g1 += gv[1];
@@ -1991,7 +2021,7 @@ __device__ inline void up_reduce_job(const Params& p, const Lds& L, int q, int w
     const float m0 = swiglu(g0, u0), m1 = swiglu(g1, u1);
     if (!isfinite(m0) || !isfinite(m1)) set_err(p.err, kErrMid);
     const int code = lds_get<int32_t>(L.cols + d.cbase + col);
-    st_agent<uint32_t>(p.mid + ((size_t)(code >> 4) * (p.K + 1) + (code & 15)) * p.mid_ld + 8 * d.tile + i2,
+    st_agent<uint32_t>(p.mid + ((size_t)(code >> 4) * (p.K + 1) + (code & 15)) * p.mid_ld + 8 * WT * d.tile + i2,
                        f32_to_bf16_rne(m0) | (f32_to_bf16_rne(m1) << 16));
   }
 }
@@ -1999,12 +2029,17 @@ __device__ inline void up_reduce_job(const Params& p, const Lds& L, int q, int w
 // The end of a chunk of up/gate job e.q: once the window's previous job is
 // summed, store the chunk's partial tile and arrive; the wave that ends the
 // job's last (nw-th) chunk sums the job and frees the window.
-__device__ inline void up_job_end(const Params& p, const Lds& L, const EatN& e, const f32x4& acc, int nw, bool& ok) {
+template <int WT>
+__device__ inline void up_job_end(const Params& p, const Lds& L, const EatN& e, const f32x4& acc, const f32x4& acc2,
+                                  int nw, bool& ok) {
   const int win = e.q & (kPuWin - 1);
   lds_wait<1>(p, L.wgen + win, (uint32_t)(e.q / kPuWin), ok);
-  if (e.pst) lds_st128(L.pbuf + e.pidx, __builtin_bit_cast(u32x4, acc));
+  if (e.pst) {
+    lds_st128(L.pbuf + e.pidx, __builtin_bit_cast(u32x4, acc));
+    if (WT == 2) lds_st128(L.pbuf + e.pidx + 16, __builtin_bit_cast(u32x4, acc2));
+  }
   if (lds_inc_lane0(L.wcnt + win) == (uint32_t)nw - 1) {
-    up_reduce_job(p, L, e.q, win, nw);
+    up_reduce_job<WT>(p, L, e.q, win, nw);
     lds_st32(L.wcnt + win, 0u);
     lds_st32(L.wgen + win, (uint32_t)(e.q / kPuWin + 1));
   }
@@ -2039,10 +2074,10 @@ __device__ __forceinline__ bf16x8 act_operand(const ItemN& it, int m) {
   return __builtin_bit_cast(bf16x8, b);
 }
 
-template <int F, int AL>
-__device__ __forceinline__ void eat_item_n(int split, int lg, const ItemN& it, f32x4& acc) {
+template <int F, int AL, int WT>
+__device__ __forceinline__ void eat_item_n(int split, int lg, const ItemN& it, f32x4& acc, f32x4& acc2) {
   bf16x8 A[4];
-  if (F == 0) {
+  if (F == 0 && WT == 1) {
     A[0] = e4m3x8_to_bf16(it.w0[0], it.w0[1]);
     A[1] = e4m3x8_to_bf16(it.w0[2], it.w0[3]);
     A[2] = e4m3x8_to_bf16(it.w1[0], it.w1[1]);
@@ -2054,7 +2089,34 @@ __device__ __forceinline__ void eat_item_n(int split, int lg, const ItemN& it, f
     for (int m = 0; m < 4; ++m) t = mfma16(A[m], act_operand<AL>(it, m), t);
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = fmaf(t[q], 4 * lg + q < split ? s_lo : s_hi, acc[q]);
-  } else {
+  } else if (F == 0) {
+    // two tiles on one activation operand: tile A the gate rows (block
+    // scale s_lo), tile B their up rows (s_hi)
+    bf16x8 Bm[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) Bm[m] = act_operand<AL>(it, m);
+    const float s_lo = __int_as_float(__builtin_amdgcn_readlane((int)it.s, 0));
+    const float s_hi = __int_as_float(__builtin_amdgcn_readlane((int)it.s, 32));
+    A[0] = e4m3x8_to_bf16(it.w0[0], it.w0[1]);
+    A[1] = e4m3x8_to_bf16(it.w0[2], it.w0[3]);
+    A[2] = e4m3x8_to_bf16(it.w1[0], it.w1[1]);
+    A[3] = e4m3x8_to_bf16(it.w1[2], it.w1[3]);
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) t = mfma16(A[m], Bm[m], t);
+    A[0] = e4m3x8_to_bf16(it.w2[0], it.w2[1]);
+    A[1] = e4m3x8_to_bf16(it.w2[2], it.w2[3]);
+    A[2] = e4m3x8_to_bf16(it.w3[0], it.w3[1]);
+    A[3] = e4m3x8_to_bf16(it.w3[2], it.w3[3]);
+    f32x4 t2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) t2 = mfma16(A[m], Bm[m], t2);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[q] = fmaf(t[q], s_lo, acc[q]);
+      acc2[q] = fmaf(t2[q], s_hi, acc2[q]);
+    }
+  } else if (WT == 1) {
     // 256 values: lane group lg holds values 64lg.. (w0: the first 32 with
     // scale byte 2lg, w1: the next 32 with byte 2lg+1); MFMA m takes
     // values 64lg + 8m.. of every lane group
@@ -2068,6 +2130,34 @@ __device__ __forceinline__ void eat_item_n(int split, int lg, const ItemN& it, f
     for (int m = 0; m < 4; ++m) A[m] = e2m1x8_to_bf16(it.w1[m], sc1);
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc = mfma16(A[m], act_operand<AL>(it, 4 + m), acc);
+  } else {
+    // the same for two tiles (tile B with its own scale bytes s2)
+    bf16x8 Bm[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) Bm[m] = act_operand<AL>(it, m);
+    const uint32_t sh = 16u * (uint32_t)(lg & 1);
+    {
+      const float sc0 = e8m0_to_f32((it.s >> sh) & 0xffu), sc1 = e8m0_to_f32((it.s >> (sh + 8)) & 0xffu);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) A[m] = e2m1x8_to_bf16(it.w0[m], sc0);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc = mfma16(A[m], Bm[m], acc);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) A[m] = e2m1x8_to_bf16(it.w1[m], sc1);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc = mfma16(A[m], Bm[4 + m], acc);
+    }
+    {
+      const float sc0 = e8m0_to_f32((it.s2 >> sh) & 0xffu), sc1 = e8m0_to_f32((it.s2 >> (sh + 8)) & 0xffu);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) A[m] = e2m1x8_to_bf16(it.w2[m], sc0);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc2 = mfma16(A[m], Bm[m], acc2);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) A[m] = e2m1x8_to_bf16(it.w3[m], sc1);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc2 = mfma16(A[m], Bm[4 + m], acc2);
+    }
   }
 }
 
@@ -2080,9 +2170,10 @@ __device__ __forceinline__ void eat_item_n(int split, int lg, const ItemN& it, f
 constexpr int kRingD = 5;   // up/gate (and the default)
 constexpr int kRingDD = 6;  // down: its second tile has fewer live rows, so items carry fewer bytes
 // up/gate ring depth by activation loads per item (FP8 with 2 loads: 7
-// measured best at 8 rows)
+// measured best at 8 rows; MXFP4 with 2, whose items are two weight tiles:
+// 3 measured best at 16 rows, against 4 and 5)
 template <int FMT, int AL>
-constexpr int ring_up() { return FMT == 0 && AL == 2 ? 7 : kRingD; }
+constexpr int ring_up() { return AL == 2 ? (FMT == 0 ? 7 : 3) : kRingD; }
 template <int D = kRingD>
 struct RingN {
   FetchN f;
@@ -2108,11 +2199,11 @@ __device__ __forceinline__ void ring_fill(const Params& p, const Lds& L, const P
 #pragma unroll
   for (int d = 0; d < D; ++d) {
     if (WONLY) {
-      fetch_weights_n<FMT>(R.f, R.r[d]);
+      fetch_weights_n<FMT, item_wt<FMT, KIND, AL>()>(R.f, R.r[d]);
       R.aop[d] = R.f.ao;
       R.h2p[d] = R.f.h2;
     } else {
-      fetch_item_n<FMT, AL>(R.f, R.r[d]);
+      fetch_item_n<FMT, AL, item_wt<FMT, KIND, AL>()>(R.f, R.r[d]);
     }
     fetch_adv_n<FMT>(R.f);
     if (R.f.left == 0) fetch_next_any<FMT, KIND, AL>(p, L, ph, R.f, kend, ok);
@@ -2141,7 +2232,9 @@ __device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const Ph
   if (any) {
     const int lg = (threadIdx.x & 63) >> 4;
     const int split_c = KIND == 3 ? 0 : ph_split<KIND>(ph);
+    constexpr int WT = item_wt<FMT, KIND, AL>();
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};  // a two-tile item's tile B
     f32x4 tot = {0.f, 0.f, 0.f, 0.f};  // KIND 3: the unit's sum over its K-phases
     // The loop is left only after a whole round of D slots: once the last
     // job has ended, the rest of the round multiplies dead items and
@@ -2153,9 +2246,9 @@ __device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const Ph
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         const int split = KIND == 3 ? e.split : split_c;
-        if (FMT == 0 || e.fmt == 0) eat_item_n<0, AL>(split, lg, R.r[d], acc);
-        else eat_item_n<1, AL>(split, lg, R.r[d], acc);
-        fetch_item_n<FMT, AL>(R.f, R.r[d]);
+        if (FMT == 0 || e.fmt == 0) eat_item_n<0, AL, WT>(split, lg, R.r[d], acc, acc2);
+        else eat_item_n<1, AL, WT>(split, lg, R.r[d], acc, acc2);
+        fetch_item_n<FMT, AL, WT>(R.f, R.r[d]);
         fetch_adv_n<FMT>(R.f);
         if (R.f.left == 0) fetch_next_any<FMT, KIND, AL>(p, L, ph, R.f, kend, ok);
         if (!done) {
@@ -2168,9 +2261,10 @@ __device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const Ph
               balance(L, ++jc);
             }
           } else if (e.left == 0) {
-            if (KIND == 1) up_job_end(p, L, e, acc, ph.nw, ok);
+            if (KIND == 1) up_job_end<WT>(p, L, e, acc, acc2, ph.nw, ok);
             else if (e.pst) lds_st128(L.pbuf + e.pidx, __builtin_bit_cast(u32x4, acc));
             acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            acc2 = f32x4{0.f, 0.f, 0.f, 0.f};
             MOE_JSTAMP(p, jc);
             balance(L, ++jc);
             done = KIND == 1 ? !eat_next_up<FMT, AL>(p, L, ph, e, R.f.nch)
@@ -2276,8 +2370,8 @@ __device__ inline void combine(const Params& p, const Lds& L, const Sched& s) {
 
 __device__ __forceinline__ Sched make_sched(const Params& p, int G) {
   Sched s;
-  s.sh_tiles = p.n_shared ? p.Is / 8 : 0;
-  s.rt_tiles = p.I / 8;
+  s.sh_tiles = p.n_shared ? p.Is >> p.lti : 0;
+  s.rt_tiles = p.I >> p.lti;
   s.G = G;
   s.n_pairs = s.sh_tiles + (G - p.n_shared) * s.rt_tiles;
   s.h0 = blockIdx.x * p.hs;
@@ -2551,9 +2645,9 @@ __device__ inline void wait_x_ready(const Params& p) {
     const int ch = p.H / kWaves, ngrp = ch >> 3;
     a = ld16(p.router_w + (size_t)blockIdx.x * p.H + (size_t)wave * ch + 8 * (lane < ngrp ? lane : ngrp - 1));
   }
-  if (p.n_shared && (int)blockIdx.x < p.Is / 8 && wave < p.H / 128) {
+  if (p.n_shared && (int)blockIdx.x < (p.Is >> p.lti) && wave < p.H / 128) {
     const int row = lane & 15, t = blockIdx.x;
-    const int lrow = row < 8 ? 8 * t + row : p.Is + 8 * t + row - 8;
+    const int lrow = p.lti == 4 ? 16 * t + row : row < 8 ? 8 * t + row : p.Is + 8 * t + row - 8;
     b = ld16(p.sh_wgu + (size_t)lrow * p.H + 128 * wave + 32 * (lane >> 4));
   }
   for (uint32_t spins = 0;;) {
