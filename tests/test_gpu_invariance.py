@@ -16,6 +16,9 @@ pytestmark = pytest.mark.gpu
 MID = dict(hidden=2048, inter=512, shared_inter=512, n_experts=64, top_k=6, n_group=8, topk_group=3)
 # hidden > 16 * 256: two 16-row down tiles per CU, split over the waves
 MID2 = dict(hidden=4352, inter=256, shared_inter=256, n_experts=32, top_k=4, n_group=4, topk_group=2)
+# MXFP4 routed experts: from 5 rows up the up/gate items are two 16-row tiles
+# on one activation operand, up to 4 rows one tile; the bits must not change
+MID3 = dict(hidden=2048, inter=512, shared_inter=512, n_experts=48, top_k=6, routed_fmt=1, bias_bf16=1)
 
 
 # DeepSeek-V3 routing geometry (256 experts in 8 groups of 32, keep 4,
@@ -28,10 +31,11 @@ def _layer(spec, case, T):
 
 
 @pytest.mark.parametrize("mid,T", [(1, 1), (1, 2), (1, 5), (1, 8), (1, 16), (1, 37), (1, 64),
-                                   (2, 1), (2, 9), (2, 16), (2, 17)])
+                                   (2, 1), (2, 9), (2, 16), (2, 17),
+                                   (3, 4), (3, 5), (3, 16), (3, 17), (3, 64)])
 def test_batch_invariance_mid(mid, T):
     say(f"batch invariance mid{mid} T={T}")
-    spec = fixtures.spec_with("tiny", **(MID if mid == 1 else MID2))
+    spec = fixtures.spec_with("tiny", **{1: MID, 2: MID2, 3: MID3}[mid])
     case = gpu_case(spec, 64, 21, rows="corr", requests=16)
     layer = _layer(spec, case, 64)
     full = run_forward(layer, case["x"])

@@ -47,6 +47,9 @@ SMALL = [
                       routed_fmt=1, bias_bf16=1), 3, 22, "corr"),
     ("mxfp4_t6", dict(hidden=2048, inter=1536, shared_inter=512, n_experts=16, top_k=6,
                       routed_fmt=1, bias_bf16=1), 6, 23, "corr"),
+    # MXFP4 above 16 rows: two-tile up/gate items with down units claimed whole
+    ("mxfp4_t37", dict(hidden=2048, inter=1536, shared_inter=512, n_experts=16, top_k=6,
+                       routed_fmt=1, bias_bf16=1), 37, 28, "iid"),
     ("four_rows_one_request", dict(hidden=1024, inter=512, shared_inter=256, n_experts=12, top_k=4), 4, 24, "corr"),
     ("two_down_tiles_t2", dict(hidden=4352, inter=256, shared_inter=256, n_experts=16, top_k=4), 2, 25, "corr"),
 ]
@@ -276,6 +279,10 @@ UNFUSED = [
     ("v3r_t37", V3R, 37, 84, "iid"),
     ("mxfp4_t16", dict(hidden=2048, inter=1536, shared_inter=512, n_experts=16, top_k=6, routed_fmt=1, bias_bf16=1),
      16, 85, "corr"),
+    # above 16 rows: the shared-expert launches are FP8 instances with FP8
+    # tiles while the routed pass has two-tile MXFP4 items
+    ("mxfp4_t24", dict(hidden=2048, inter=1536, shared_inter=512, n_experts=16, top_k=6, routed_fmt=1, bias_bf16=1),
+     24, 86, "iid"),
 ]
 
 
