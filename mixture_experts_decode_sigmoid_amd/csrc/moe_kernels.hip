@@ -1539,6 +1539,7 @@ struct PhaseN {
   int split;      // FP8: MFMA output rows (4*lg + q) below it take the first scale block row
   int dnb;        // FP8 down: block rows between the tile's first and last live row (0 or 1)
   int rt;         // down: this wave's tile
+  int hb2, nlive2, split2, dnb2;  // two-tile K-split down: tile B (tile rt + 1); nlive2 <= 0: none
   int nw;         // up/gate: waves with items (min(K-blocks, 8))
   int nsc, nct;   // up/gate: chunks of the CU's shared-expert jobs, column tiles per shared pair
   int js, jp;     // K-split down: the wave takes the down jobs j with j mod js == jp
@@ -1548,8 +1549,12 @@ template <int KIND>
 __device__ __forceinline__ int ph_k0(const PhaseN& ph) { return KIND == 1 ? wave_id() : ph.k0; }
 template <int KIND>
 __device__ __forceinline__ int ph_lstep(const PhaseN& ph) { return KIND == 1 ? 3 : ph.lstep; }
+template <int KIND, int WT>
+__device__ __forceinline__ int ph_split(const PhaseN& ph) { return KIND == 1 ? (WT == 2 ? 16 : 8) : ph.split; }
+// a two-tile item's tile B: up/gate, all up rows (the second scale word of
+// s2, which repeats s); down, its own rows
 template <int KIND>
-__device__ __forceinline__ int ph_split(const PhaseN& ph) { return KIND == 1 ? 8 : ph.split; }
+__device__ __forceinline__ int ph_split2(const PhaseN& ph) { return KIND == 1 ? 0 : ph.split2; }
 
 // The down constants of tile rt of the slice [h0, h0 + hc), K-blocks
 // k0 + (i << lstep).
@@ -1562,6 +1567,10 @@ __device__ __forceinline__ PhaseN down_phase(int h0, int hc, int nrt, int rt, in
   ph.nlive = hc - 16 * rt < 16 ? hc - 16 * rt : 16;
   ph.split = (ph.hb / 128 + 1) * 128 - ph.hb;  // a 16-row tile spans at most two scale block rows
   ph.dnb = ph.nlive > 0 ? ((ph.hb + ph.nlive - 1) >> 7) - (ph.hb >> 7) : 0;
+  ph.hb2 = ph.hb + 16;
+  ph.nlive2 = 0;
+  ph.split2 = 0;
+  ph.dnb2 = 0;
   ph.nw = 0;
   ph.js = 1;
   ph.jp = 0;
@@ -1578,15 +1587,34 @@ __device__ __forceinline__ PhaseN down_phase(int h0, int hc, int nrt, int rt, in
 // over take every (kph/kpe)-th job instead, so no wave idles.  Each phase
 // then holds at most one K-block, as it did with kph phases: the partials,
 // and their phase-order sum, are the same bits.
+//
+// WT = 2 (two-tile items): a wave takes tiles 2i and 2i+1 together (pair i =
+// w mod nrt_p/2) on one activation operand, and the two waves that would
+// have taken them in the same K-phase take alternate jobs instead.  Each
+// (tile, K-phase) partial is the same chain over the same K-blocks, so the
+// products keep their bits.  With one tile (nrt_p = 1) tile B is empty.
+template <int WT>
 __device__ __forceinline__ PhaseN ksplit_phase(const Params& p, const Sched& s, int w) {
   const int nkb_rt = p.I / (p.routed_fmt ? 256 : 128), nkb_sh = p.n_shared ? p.Is / 128 : 0;
   const int nkb = nkb_rt > nkb_sh ? nkb_rt : nkb_sh;
   int kpe = 1;
   while (kpe < nkb && kpe < s.kph) kpe <<= 1;
-  const int q = w / s.nrt_p;
-  PhaseN ph = down_phase(s.h0, s.hc, s.nrt, w % s.nrt_p, q % kpe, 31 - __builtin_clz(kpe));
-  ph.js = s.kph / kpe;
-  ph.jp = q / kpe;
+  if (WT == 1 || s.nrt_p == 1) {
+    const int q = w / s.nrt_p;
+    PhaseN ph = down_phase(s.h0, s.hc, s.nrt, w % s.nrt_p, q % kpe, 31 - __builtin_clz(kpe));
+    ph.js = s.kph / kpe;
+    ph.jp = q / kpe;
+    return ph;
+  }
+  const int npair = s.nrt_p >> 1, rest = w / npair, q = rest % s.kph;
+  PhaseN ph = down_phase(s.h0, s.hc, s.nrt, 2 * (w % npair), q % kpe, 31 - __builtin_clz(kpe));
+  const PhaseN b = down_phase(s.h0, s.hc, s.nrt, 2 * (w % npair) + 1, 0, 0);
+  ph.hb2 = b.hb;
+  ph.nlive2 = b.nlive;
+  ph.split2 = b.split;
+  ph.dnb2 = b.dnb;
+  ph.js = 2 * (s.kph / kpe);
+  ph.jp = q / kpe + (s.kph / kpe) * (rest / s.kph);
   return ph;
 }
 
@@ -1619,8 +1647,10 @@ struct FetchN {
 // MXFP4 routed experts and two activation loads are two 16-row tiles (gate
 // rows, then their up rows) on one activation operand; every other item is
 // one tile.
+// K-split down items are the CU's two 16-row down tiles of one K-phase
+// (see ksplit_phase).
 template <int FMT, int KIND, int AL>
-constexpr int item_wt() { return FMT != 0 && KIND == 1 && AL == 2 ? 2 : 1; }
+constexpr int item_wt() { return (AL == 2 && FMT != 0 && KIND == 1) || KIND == 2 ? 2 : 1; }
 
 // One item: a K-block of a 16-row tile, 128 bytes of each row (FP8: 128
 // values, one fp32 block scale per 128-row block; MXFP4: 256 values, the
@@ -1684,8 +1714,26 @@ __device__ __forceinline__ void fetch_from_desc(const Params& p, const PhaseN& p
   f.fmt = fmt;
   f.nstep = 1 << ph_lstep<KIND>(ph);
   f.left = n;
-  f.wj = WT == 2 ? d.jump * (uint32_t)(d.nkb * 128) : 0u;
-  f.sj = WT == 2 && fmt ? d.jump * d.shi : 0u;
+  if (WT == 2 && KIND == 1) {
+    f.wj = d.jump * (uint32_t)(d.nkb * 128);
+    f.sj = fmt ? d.jump * d.shi : 0u;
+  } else if (WT == 2) {
+    // down tile B's rows (its last live row repeated, or tile A's rows if
+    // it has none); both offsets are from tile A's and not negative
+    const uint32_t lrow2 = ph.nlive2 > 0 ? (uint32_t)(ph.hb2 + (row < ph.nlive2 ? row : ph.nlive2 - 1)) : lrow;
+    f.wj = lmul(lrow2 - lrow, (uint32_t)(d.nkb * 128));
+    if (fmt == 0) {
+      const uint32_t so2 = ph.nlive2 > 0 ? 4u * (uint32_t)(((ph.hb2 >> 7) - (ph.hb >> 7)) * d.nkb) +
+                                               (lane < 32 ? 0u : 4u * (uint32_t)(ph.dnb2 * d.nkb)) + 4u * (uint32_t)k0
+                                         : f.so;
+      f.sj = so2 - f.so;
+    } else {
+      f.sj = lmul(lrow2 - lrow, d.shi);
+    }
+  } else {
+    f.wj = 0u;
+    f.sj = 0u;
+  }
 }
 
 // Past the last job: dead items load from the start of x (weights and
@@ -1842,9 +1890,10 @@ __device__ __forceinline__ void fetch_weights_n(const FetchN& f, ItemN& it) {
     it.w3 = ldg<u32x4>(w + f.wj + 16);
   }
   it.s = ldg<uint32_t>(f.sb + f.so);
-  // an MXFP4 tile B has scales of its own (FP8: the up rows' block scale is
-  // lane 32's word of s); an FP8 item of such a kernel loads s again
-  if (WT == 2 && FMT != 0) it.s2 = ldg<uint32_t>(f.sb + f.so + f.sj);
+  // tile B's scales: an MXFP4 up/gate tile B's rows, a down tile B's rows;
+  // an FP8 up/gate item loads s again (the up rows' block scale is lane 32's
+  // word of s)
+  if (WT == 2) it.s2 = ldg<uint32_t>(f.sb + (uint32_t)(f.so + f.sj));
 }
 // Activations: AL loads of 16 B per lane per 128 values, pieces j + G*i
 // (the load instructions, not the bytes, are what the vector memory path
@@ -2074,8 +2123,10 @@ __device__ __forceinline__ bf16x8 act_operand(const ItemN& it, int m) {
   return __builtin_bit_cast(bf16x8, b);
 }
 
+// split / split2: MFMA output rows (4*lg + q) of tile A / tile B below it
+// take lane 0's scale word of s / s2, the others lane 32's (FP8).
 template <int F, int AL, int WT>
-__device__ __forceinline__ void eat_item_n(int split, int lg, const ItemN& it, f32x4& acc, f32x4& acc2) {
+__device__ __forceinline__ void eat_item_n(int split, int split2, int lg, const ItemN& it, f32x4& acc, f32x4& acc2) {
   bf16x8 A[4];
   if (F == 0 && WT == 1) {
     A[0] = e4m3x8_to_bf16(it.w0[0], it.w0[1]);
@@ -2090,13 +2141,16 @@ __device__ __forceinline__ void eat_item_n(int split, int lg, const ItemN& it, f
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = fmaf(t[q], 4 * lg + q < split ? s_lo : s_hi, acc[q]);
   } else if (F == 0) {
-    // two tiles on one activation operand: tile A the gate rows (block
-    // scale s_lo), tile B their up rows (s_hi)
+    // two tiles on one activation operand: up/gate, tile A the gate rows
+    // (lane 0's word of s) and tile B their up rows (lane 32's word of s2 =
+    // s); down, two 16-row tiles with scale words of their own
     bf16x8 Bm[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) Bm[m] = act_operand<AL>(it, m);
     const float s_lo = __int_as_float(__builtin_amdgcn_readlane((int)it.s, 0));
     const float s_hi = __int_as_float(__builtin_amdgcn_readlane((int)it.s, 32));
+    const float s2_lo = __int_as_float(__builtin_amdgcn_readlane((int)it.s2, 0));
+    const float s2_hi = __int_as_float(__builtin_amdgcn_readlane((int)it.s2, 32));
     A[0] = e4m3x8_to_bf16(it.w0[0], it.w0[1]);
     A[1] = e4m3x8_to_bf16(it.w0[2], it.w0[3]);
     A[2] = e4m3x8_to_bf16(it.w1[0], it.w1[1]);
@@ -2113,8 +2167,8 @@ __device__ __forceinline__ void eat_item_n(int split, int lg, const ItemN& it, f
     for (int m = 0; m < 4; ++m) t2 = mfma16(A[m], Bm[m], t2);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      acc[q] = fmaf(t[q], s_lo, acc[q]);
-      acc2[q] = fmaf(t2[q], s_hi, acc2[q]);
+      acc[q] = fmaf(t[q], 4 * lg + q < split ? s_lo : s_hi, acc[q]);
+      acc2[q] = fmaf(t2[q], 4 * lg + q < split2 ? s2_lo : s2_hi, acc2[q]);
     }
   } else if (WT == 1) {
     // 256 values: lane group lg holds values 64lg.. (w0: the first 32 with
@@ -2169,6 +2223,10 @@ __device__ __forceinline__ void eat_item_n(int split, int lg, const ItemN& it, f
 // zero where this wave has no items.
 constexpr int kRingD = 5;   // up/gate (and the default)
 constexpr int kRingDD = 6;  // down: its second tile has fewer live rows, so items carry fewer bytes
+// K-split down ring depth: its items are two tiles, twice the weights of a
+// claimed down item (3 measured best at 8 and 16 rows, against 4 and 5)
+template <int FMT, int AL>
+constexpr int ring_dn() { return 3; }
 // up/gate ring depth by activation loads per item (FP8 with 2 loads: 7
 // measured best at 8 rows; MXFP4 with 2, whose items are two weight tiles:
 // 3 measured best at 16 rows, against 4 and 5)
@@ -2231,8 +2289,9 @@ __device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const Ph
                                : eat_next_n<FMT, KIND, AL>(p, L, ph, e, kend);
   if (any) {
     const int lg = (threadIdx.x & 63) >> 4;
-    const int split_c = KIND == 3 ? 0 : ph_split<KIND>(ph);
     constexpr int WT = item_wt<FMT, KIND, AL>();
+    const int split_c = KIND == 3 ? 0 : ph_split<KIND, WT>(ph);
+    const int split2_c = KIND == 3 ? 0 : ph_split2<KIND>(ph);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};  // a two-tile item's tile B
     f32x4 tot = {0.f, 0.f, 0.f, 0.f};  // KIND 3: the unit's sum over its K-phases
@@ -2246,8 +2305,8 @@ __device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const Ph
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         const int split = KIND == 3 ? e.split : split_c;
-        if (FMT == 0 || e.fmt == 0) eat_item_n<0, AL, WT>(split, lg, R.r[d], acc, acc2);
-        else eat_item_n<1, AL, WT>(split, lg, R.r[d], acc, acc2);
+        if (FMT == 0 || e.fmt == 0) eat_item_n<0, AL, WT>(split, split2_c, lg, R.r[d], acc, acc2);
+        else eat_item_n<1, AL, WT>(split, split2_c, lg, R.r[d], acc, acc2);
         fetch_item_n<FMT, AL, WT>(R.f, R.r[d]);
         fetch_adv_n<FMT>(R.f);
         if (R.f.left == 0) fetch_next_any<FMT, KIND, AL>(p, L, ph, R.f, kend, ok);
@@ -2262,7 +2321,10 @@ __device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const Ph
             }
           } else if (e.left == 0) {
             if (KIND == 1) up_job_end<WT>(p, L, e, acc, acc2, ph.nw, ok);
-            else if (e.pst) lds_st128(L.pbuf + e.pidx, __builtin_bit_cast(u32x4, acc));
+            else if (e.pst) {
+              lds_st128(L.pbuf + e.pidx, __builtin_bit_cast(u32x4, acc));
+              if (WT == 2 && ph.nlive2 > 0) lds_st128(L.pbuf + e.pidx + 16, __builtin_bit_cast(u32x4, acc2));
+            }
             acc = f32x4{0.f, 0.f, 0.f, 0.f};
             acc2 = f32x4{0.f, 0.f, 0.f, 0.f};
             MOE_JSTAMP(p, jc);
@@ -2526,31 +2588,32 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
     zero_partials(L, (size_t)p.wpt * p.T * (p.K + 1) * p.pitch);
     // the first D items' weights do not depend on mid: issue them before the
     // wait, their activations after it
-    RingN<kRingDD> R;
+    constexpr int DD = DCLAIM ? kRingDD : ring_dn<FMT, AL>();
+    RingN<DD> R;
     if (!DCLAIM) {
       // wave w takes tile w % nrt_p of this CU's slice and K-blocks
-      // w / nrt_p + wpt*i of every down job
-      const PhaseN ph = ksplit_phase(p, s, wave);
+      // w / nrt_p + wpt*i of every down job (two-tile items: see ksplit_phase)
+      const PhaseN ph = ksplit_phase<item_wt<FMT, 2, AL>()>(p, s, wave);
       const int kend = ph.nlive > 0 ? p.qcap + nD : p.qcap;
-      ring_open<FMT, 2, kRingDD, AL>(p, L, ph, R, p.qcap, kend, ok);
-      ring_fill<FMT, 2, true, kRingDD, AL>(p, L, ph, R, kend, ok);
+      ring_open<FMT, 2, DD, AL>(p, L, ph, R, p.qcap, kend, ok);
+      ring_fill<FMT, 2, true, DD, AL>(p, L, ph, R, kend, ok);
       wait_all(p, epoch + 2);
       MOE_STAMP(p, 5);
       MOE_WSTAMP(p, 1);
-      ring_fill_acts<FMT, kRingDD, AL>(R);
-      ring_run<FMT, 2, true, kRingDD, AL>(p, L, ph, R, p.qcap, kend, jn, ok);
+      ring_fill_acts<FMT, DD, AL>(R);
+      ring_run<FMT, 2, true, DD, AL>(p, L, ph, R, p.qcap, kend, jn, ok);
     } else {
       // the waves claim (down job, 16-row tile) units and stream all their
       // K-blocks, K-phase by K-phase
       const PhaseN ph = down_phase(s.h0, s.hc, s.nrt, 0, 0, 31 - __builtin_clz(s.kph));
       const int nunits = s.hc > 0 ? nD * s.nrt : 0;
-      ring_open<FMT, 3, kRingDD, AL>(p, L, ph, R, -1, nunits, ok);
-      ring_fill<FMT, 3, true, kRingDD, AL>(p, L, ph, R, nunits, ok);
+      ring_open<FMT, 3, DD, AL>(p, L, ph, R, -1, nunits, ok);
+      ring_fill<FMT, 3, true, DD, AL>(p, L, ph, R, nunits, ok);
       wait_all(p, epoch + 2);
       MOE_STAMP(p, 5);
       MOE_WSTAMP(p, 1);
-      ring_fill_acts<FMT, kRingDD, AL>(R);
-      ring_run<FMT, 3, true, kRingDD, AL>(p, L, ph, R, 0, nunits, jn, ok);
+      ring_fill_acts<FMT, DD, AL>(R);
+      ring_run<FMT, 3, true, DD, AL>(p, L, ph, R, 0, nunits, jn, ok);
     }
     MOE_WSTAMP(p, 2);
     MOE_STAMP(p, 6);
@@ -2613,19 +2676,20 @@ __device__ __forceinline__ void shared_only(char* smem) {
   const int nD = lds_ldi_uniform(L.misc + kMiscND);
   zero_partials(L, (size_t)p.wpt * p.T * (p.K + 1) * p.pitch);
   __syncthreads();
-  RingN<kRingDD> R;
+  constexpr int DD = DCLAIM ? kRingDD : ring_dn<FMT, AL>();
+  RingN<DD> R;
   if (!DCLAIM) {
-    const PhaseN ph = ksplit_phase(p, s, wave);
+    const PhaseN ph = ksplit_phase<item_wt<FMT, 2, AL>()>(p, s, wave);
     const int kend = ph.nlive > 0 ? p.qcap + nD : p.qcap;
-    ring_open<FMT, 2, kRingDD, AL>(p, L, ph, R, p.qcap, kend, ok);
-    ring_fill<FMT, 2, false, kRingDD, AL>(p, L, ph, R, kend, ok);
-    ring_run<FMT, 2, false, kRingDD, AL>(p, L, ph, R, p.qcap, kend, jn, ok);
+    ring_open<FMT, 2, DD, AL>(p, L, ph, R, p.qcap, kend, ok);
+    ring_fill<FMT, 2, false, DD, AL>(p, L, ph, R, kend, ok);
+    ring_run<FMT, 2, false, DD, AL>(p, L, ph, R, p.qcap, kend, jn, ok);
   } else {
     const PhaseN ph = down_phase(s.h0, s.hc, s.nrt, 0, 0, 31 - __builtin_clz(s.kph));
     const int nunits = s.hc > 0 ? nD * s.nrt : 0;
-    ring_open<FMT, 3, kRingDD, AL>(p, L, ph, R, -1, nunits, ok);
-    ring_fill<FMT, 3, false, kRingDD, AL>(p, L, ph, R, nunits, ok);
-    ring_run<FMT, 3, false, kRingDD, AL>(p, L, ph, R, 0, nunits, jn, ok);
+    ring_open<FMT, 3, DD, AL>(p, L, ph, R, -1, nunits, ok);
+    ring_fill<FMT, 3, false, DD, AL>(p, L, ph, R, nunits, ok);
+    ring_run<FMT, 3, false, DD, AL>(p, L, ph, R, 0, nunits, jn, ok);
   }
   __syncthreads();
   sum_kphases<DCLAIM>(p, L, s);
