@@ -1580,6 +1580,18 @@ __device__ __forceinline__ PhaseN down_phase(int h0, int hc, int nrt, int rt, in
   return ph;
 }
 
+// Down constants of the unit of 16-row tiles 2*pr and 2*pr + 1 of the slice
+// (tile B empty past the slice's tiles).
+__device__ __forceinline__ PhaseN down_pair(int h0, int hc, int nrt, int pr, int k0, int lstep) {
+  PhaseN ph = down_phase(h0, hc, nrt, 2 * pr, k0, lstep);
+  const PhaseN b = down_phase(h0, hc, nrt, 2 * pr + 1, 0, 0);
+  ph.hb2 = b.hb;
+  ph.nlive2 = b.nlive;
+  ph.split2 = b.split;
+  ph.dnb2 = b.dnb;
+  return ph;
+}
+
 // The K-split down constants of wave w: tile w mod nrt_p of the CU's slice
 // and K-phase (w / nrt_p) of the kph phases.  When a down job has fewer
 // K-blocks than kph (a small intermediate size), the phases are cut to the
@@ -1647,10 +1659,10 @@ struct FetchN {
 // MXFP4 routed experts and two activation loads are two 16-row tiles (gate
 // rows, then their up rows) on one activation operand; every other item is
 // one tile.
-// K-split down items are the CU's two 16-row down tiles of one K-phase
-// (see ksplit_phase).
+// Down items are two 16-row down tiles of the CU's slice on one activation
+// operand (see ksplit_phase and fetch_next_dc).
 template <int FMT, int KIND, int AL>
-constexpr int item_wt() { return (AL == 2 && FMT != 0 && KIND == 1) || KIND == 2 ? 2 : 1; }
+constexpr int item_wt() { return (AL == 2 && FMT != 0 && KIND == 1) || KIND != 1 ? 2 : 1; }
 
 // One item: a K-block of a 16-row tile, 128 bytes of each row (FP8: 128
 // values, one fp32 block scale per 128-row block; MXFP4: 256 values, the
@@ -1835,7 +1847,8 @@ __device__ __forceinline__ int phase_items(int nkb, int kp, int lkph) {
 
 // Claimed down (KIND 3): moves the fetch side to the next K-phase with
 // items of the wave's unit, or claims this CU's next down unit u (down entry
-// u / nrt, 16-row tile u mod nrt of the slice) and hands u on to the
+// u / npu, tiles 2*pr and 2*pr + 1 of the slice for pr = u mod npu, npu =
+// the slice's pairs of 16-row tiles) and hands u on to the
 // multiplying side; past the end once u reaches nunits.  A unit's K-blocks
 // are fetched phase by phase (kp + kph*i for kp = 0, 1, ..), the order in
 // which its sum is formed (see dc_phase_end).
@@ -1848,9 +1861,9 @@ __device__ inline void fetch_next_dc(const Params& p, const Lds& L, const PhaseN
         const int n = phase_items(f.nkb, kp, ph.lstep);
         if (n > 0) {
           f.kp = kp;
-          const int ent = f.k / ph.nrt, rt = f.k - ent * ph.nrt;
+          const int npu = (ph.nrt + 1) >> 1, ent = f.k / npu, pr = f.k - ent * npu;
           const JobDesc d = read_desc(L, p.qcap + ent);
-          const PhaseN q = down_phase(ph.h0, ph.hc, ph.nrt, rt, kp, ph.lstep);
+          const PhaseN q = down_pair(ph.h0, ph.hc, ph.nrt, pr, kp, ph.lstep);
           fetch_from_desc<FMT, 2, AL>(p, q, f, d, kp, n, lane_code<AL>(L, d));
           return;
         }
@@ -1866,7 +1879,7 @@ __device__ inline void fetch_next_dc(const Params& p, const Lds& L, const PhaseN
     f.nch = f.nch + 1;
     f.k = (int)u;
     f.kp = -1;
-    f.nkb = read_desc(L, p.qcap + (int)u / ph.nrt).nkb;
+    f.nkb = read_desc(L, p.qcap + (int)u / ((ph.nrt + 1) >> 1)).nkb;
   }
 }
 
@@ -1937,6 +1950,8 @@ struct EatN {
   uint32_t pidx;   // this lane's partial (floats from L.pbuf); only stored when pst
   bool pst;        // this lane's column is one of the group's
   int split;       // KIND 3: the job's FP8 scale split (see PhaseN)
+  int split2;      // KIND 3: the same for the unit's tile B
+  bool pst2;       // KIND 3: the unit has a tile B
   int kp, nkb;     // KIND 3: the K-phase being multiplied, and the unit's K-blocks
 };
 
@@ -1988,15 +2003,16 @@ __device__ inline bool eat_next_up(const Params& p, const Lds& L, const PhaseN& 
 
 // Claimed down (KIND 3): moves the multiplying side to the next unit the
 // fetch side has claimed, at its first K-phase; false at the end.  The
-// unit's sum goes to Pd[0][row][slot] at its tile.
+// unit's sums go to Pd[0][row][slot] at its two tiles.
 template <int FMT, int AL>
 __device__ inline bool eat_next_dc(const Params& p, const Lds& L, const PhaseN& ph, EatN& e, int fnch) {
   if (e.nch >= fnch) return false;
   const int lane = threadIdx.x & 63, lg = lane >> 4, col = lane_col<AL>(lane);
   const uint32_t u = (uint32_t)lds_ldi_uniform((const int32_t*)L.cfifo + wave_id() * 8 + (e.nch & 7));
   e.nch = e.nch + 1;
-  const int ent = (int)u / ph.nrt, rt = (int)u - ent * ph.nrt;
+  const int npu = (ph.nrt + 1) >> 1, ent = (int)u / npu, pr = (int)u - ent * npu;
   const JobDesc d = read_desc(L, p.qcap + ent);
+  const PhaseN q = down_pair(ph.h0, ph.hc, ph.nrt, pr, 0, 0);
   e.nkb = d.nkb;
   e.kp = 0;
   e.left = phase_items(d.nkb, 0, ph.lstep);
@@ -2004,8 +2020,10 @@ __device__ inline bool eat_next_dc(const Params& p, const Lds& L, const PhaseN& 
   e.pst = col < d.ncols && (lane & (4 / AL - 1)) == 0;
   const int code = lane_code<AL>(L, d);
   e.pidx = lmul(lmul((uint32_t)(code >> 4), (uint32_t)(p.K + 1)) + (uint32_t)(code & 15), (uint32_t)p.pitch) +
-           16u * (uint32_t)rt + 4u * (uint32_t)lg;
-  e.split = down_phase(ph.h0, ph.hc, ph.nrt, rt, 0, 0).split;
+           32u * (uint32_t)pr + 4u * (uint32_t)lg;
+  e.split = q.split;
+  e.split2 = q.split2;
+  e.pst2 = e.pst && q.nlive2 > 0;
   return true;
 }
 
@@ -2016,13 +2034,18 @@ __device__ inline bool eat_next_dc(const Params& p, const Lds& L, const PhaseN& 
 // job's products get in the combine.  Moves to the next phase with items,
 // or at the unit's end stores the sum (unit_end) and starts the next unit;
 // false once no unit is left.
+// Both tiles of the unit (tile B: acc2, tot2) alike.
 template <int FMT, int AL>
 __device__ inline bool dc_phase_end(const Params& p, const Lds& L, const PhaseN& ph, EatN& e, f32x4& acc, f32x4& tot,
-                                    int fnch, bool& unit_end) {
+                                    f32x4& acc2, f32x4& tot2, int fnch, bool& unit_end) {
   const int kph = 1 << ph.lstep;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) tot[q] += acc[q];
+  for (int q = 0; q < 4; ++q) {
+    tot[q] += acc[q];
+    tot2[q] += acc2[q];
+  }
   acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  acc2 = f32x4{0.f, 0.f, 0.f, 0.f};
   unit_end = false;
   for (int kp = e.kp + 1; kp < kph; ++kp) {
     const int n = phase_items(e.nkb, kp, ph.lstep);
@@ -2032,11 +2055,16 @@ __device__ inline bool dc_phase_end(const Params& p, const Lds& L, const PhaseN&
       return true;
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) tot[q] += 0.f;
+    for (int q = 0; q < 4; ++q) {
+      tot[q] += 0.f;
+      tot2[q] += 0.f;
+    }
   }
   unit_end = true;
   if (e.pst) lds_st128(L.pbuf + e.pidx, __builtin_bit_cast(u32x4, tot));
+  if (e.pst2) lds_st128(L.pbuf + e.pidx + 16, __builtin_bit_cast(u32x4, tot2));
   tot = f32x4{0.f, 0.f, 0.f, 0.f};
+  tot2 = f32x4{0.f, 0.f, 0.f, 0.f};
   return eat_next_dc<FMT, AL>(p, L, ph, e, fnch);
 }
 
@@ -2222,11 +2250,13 @@ __device__ __forceinline__ void eat_item_n(int split, int split2, int lg, const 
 // refills until the last job has ended.  Partials go to LDS, which must be
 // zero where this wave has no items.
 constexpr int kRingD = 5;   // up/gate (and the default)
-constexpr int kRingDD = 6;  // down: its second tile has fewer live rows, so items carry fewer bytes
 // K-split down ring depth: its items are two tiles, twice the weights of a
 // claimed down item (3 measured best at 8 and 16 rows, against 4 and 5)
 template <int FMT, int AL>
 constexpr int ring_dn() { return 3; }
+// claimed down ring depth (items of two tiles; 4 measured best at 64 rows, against 3)
+template <int FMT, int AL>
+constexpr int ring_dc() { return 4; }
 // up/gate ring depth by activation loads per item (FP8 with 2 loads: 7
 // measured best at 8 rows; MXFP4 with 2, whose items are two weight tiles:
 // 3 measured best at 16 rows, against 4 and 5)
@@ -2295,6 +2325,7 @@ __device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const Ph
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};  // a two-tile item's tile B
     f32x4 tot = {0.f, 0.f, 0.f, 0.f};  // KIND 3: the unit's sum over its K-phases
+    f32x4 tot2 = {0.f, 0.f, 0.f, 0.f};  // KIND 3: the same for its tile B
     // The loop is left only after a whole round of D slots: once the last
     // job has ended, the rest of the round multiplies dead items and
     // refills with dead loads.  So every path to an item's wait has issued
@@ -2305,8 +2336,9 @@ __device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const Ph
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         const int split = KIND == 3 ? e.split : split_c;
-        if (FMT == 0 || e.fmt == 0) eat_item_n<0, AL, WT>(split, split2_c, lg, R.r[d], acc, acc2);
-        else eat_item_n<1, AL, WT>(split, split2_c, lg, R.r[d], acc, acc2);
+        const int split2 = KIND == 3 ? e.split2 : split2_c;
+        if (FMT == 0 || e.fmt == 0) eat_item_n<0, AL, WT>(split, split2, lg, R.r[d], acc, acc2);
+        else eat_item_n<1, AL, WT>(split, split2, lg, R.r[d], acc, acc2);
         fetch_item_n<FMT, AL, WT>(R.f, R.r[d]);
         fetch_adv_n<FMT>(R.f);
         if (R.f.left == 0) fetch_next_any<FMT, KIND, AL>(p, L, ph, R.f, kend, ok);
@@ -2314,7 +2346,7 @@ __device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const Ph
           e.left = uni(e.left) - 1;
           if (KIND == 3 && e.left == 0) {
             bool unit_end;
-            done = !dc_phase_end<FMT, AL>(p, L, ph, e, acc, tot, R.f.nch, unit_end);
+            done = !dc_phase_end<FMT, AL>(p, L, ph, e, acc, tot, acc2, tot2, R.f.nch, unit_end);
             if (unit_end) {
               MOE_JSTAMP(p, jc);
               balance(L, ++jc);
@@ -2588,7 +2620,7 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
     zero_partials(L, (size_t)p.wpt * p.T * (p.K + 1) * p.pitch);
     // the first D items' weights do not depend on mid: issue them before the
     // wait, their activations after it
-    constexpr int DD = DCLAIM ? kRingDD : ring_dn<FMT, AL>();
+    constexpr int DD = DCLAIM ? ring_dc<FMT, AL>() : ring_dn<FMT, AL>();
     RingN<DD> R;
     if (!DCLAIM) {
       // wave w takes tile w % nrt_p of this CU's slice and K-blocks
@@ -2603,10 +2635,10 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
       ring_fill_acts<FMT, DD, AL>(R);
       ring_run<FMT, 2, true, DD, AL>(p, L, ph, R, p.qcap, kend, jn, ok);
     } else {
-      // the waves claim (down job, 16-row tile) units and stream all their
-      // K-blocks, K-phase by K-phase
+      // the waves claim (down job, pair of 16-row tiles) units and stream
+      // all their K-blocks, K-phase by K-phase
       const PhaseN ph = down_phase(s.h0, s.hc, s.nrt, 0, 0, 31 - __builtin_clz(s.kph));
-      const int nunits = s.hc > 0 ? nD * s.nrt : 0;
+      const int nunits = s.hc > 0 ? nD * ((s.nrt + 1) >> 1) : 0;  // units: a job's pairs of 16-row tiles
       ring_open<FMT, 3, DD, AL>(p, L, ph, R, -1, nunits, ok);
       ring_fill<FMT, 3, true, DD, AL>(p, L, ph, R, nunits, ok);
       wait_all(p, epoch + 2);
@@ -2676,7 +2708,7 @@ __device__ __forceinline__ void shared_only(char* smem) {
   const int nD = lds_ldi_uniform(L.misc + kMiscND);
   zero_partials(L, (size_t)p.wpt * p.T * (p.K + 1) * p.pitch);
   __syncthreads();
-  constexpr int DD = DCLAIM ? kRingDD : ring_dn<FMT, AL>();
+  constexpr int DD = DCLAIM ? ring_dc<FMT, AL>() : ring_dn<FMT, AL>();
   RingN<DD> R;
   if (!DCLAIM) {
     const PhaseN ph = ksplit_phase<item_wt<FMT, 2, AL>()>(p, s, wave);
@@ -2686,7 +2718,7 @@ __device__ __forceinline__ void shared_only(char* smem) {
     ring_run<FMT, 2, false, DD, AL>(p, L, ph, R, p.qcap, kend, jn, ok);
   } else {
     const PhaseN ph = down_phase(s.h0, s.hc, s.nrt, 0, 0, 31 - __builtin_clz(s.kph));
-    const int nunits = s.hc > 0 ? nD * s.nrt : 0;
+    const int nunits = s.hc > 0 ? nD * ((s.nrt + 1) >> 1) : 0;  // units: a job's pairs of 16-row tiles
     ring_open<FMT, 3, DD, AL>(p, L, ph, R, -1, nunits, ok);
     ring_fill<FMT, 3, false, DD, AL>(p, L, ph, R, nunits, ok);
     ring_run<FMT, 3, false, DD, AL>(p, L, ph, R, 0, nunits, jn, ok);
