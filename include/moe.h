@@ -39,7 +39,13 @@
  *       MOE_FMT_MXFP4: OCP MX FP4 (E2M1), two elements per byte, element k in
  *         the low nibble when k is even; one E8M0 scale byte per 32
  *         consecutive k, scale grid [N][K/32]; element =
- *         e2m1(q) * 2^(s - 127).
+ *         e2m1(q) * 2^(s - 127).  The layer takes the scale bytes packed in
+ *         tiles (moe_pack_mxfp4_scales writes them from the [N][K/32] grid):
+ *         byte j of row n's K-block kb (K-blocks of 256 elements, bytes
+ *         kb*8 .. kb*8+7 of the row) sits at
+ *         ((n/16) * (K/256) + kb) * 128 + (n%16) * 8 + j, so the scales of
+ *         16 rows for one K-block are one 128-byte line (N a multiple of
+ *         16, K of 256).
  *     W_gate_up of an expert is [2*Iexp, H]: rows 0..Iexp-1 project to the
  *     gate, rows Iexp..2*Iexp-1 to the up half.  W_down is [H, Iexp].
  *   - A workspace belongs to one stream at a time: calls that overlap on the
@@ -129,9 +135,9 @@ typedef struct {
   const uint16_t* router_w;   /* [E, H] bf16 */
   const void* bias;           /* [E] fp32 or bf16 (bias_dtype) */
   const uint8_t* w_gate_up;   /* [E_w, 2I, H] FP8, or [E_w, 2I, H/2] MXFP4 (E_w: see expert_count) */
-  const void* s_gate_up;      /* [E_w, 2I/128, H/128] fp32, or [E_w, 2I, H/32] E8M0 bytes */
+  const void* s_gate_up;      /* [E_w, 2I/128, H/128] fp32, or E8M0 bytes of [E_w, 2I, H/32] packed in tiles */
   const uint8_t* w_down;      /* [E_w, H, I] FP8, or [E_w, H, I/2] MXFP4 */
-  const void* s_down;         /* [E_w, H/128, I/128] fp32, or [E_w, H, I/32] E8M0 bytes */
+  const void* s_down;         /* [E_w, H/128, I/128] fp32, or E8M0 bytes of [E_w, H, I/32] packed in tiles */
   const uint8_t* sh_w_gate_up;/* [2I_s, H] FP8 (n_shared == 1) */
   const float* sh_s_gate_up;  /* [2I_s/128, H/128] fp32 */
   const uint8_t* sh_w_down;   /* [H, I_s] FP8 */
@@ -264,6 +270,20 @@ int moe_forward_after(const moe_config* cfg, const moe_weights* w, const uint16_
 /* Waits for `stream`, then returns the workspace's device error bits in
  * *bits (host) and clears them. */
 int moe_read_error(void* ws, void* stream, uint32_t* bits);
+
+/* Packs MXFP4 E8M0 scale bytes from the [rows][k/32] grid (src, the layout
+ * of the OCP MX definition: one byte per 32 consecutive elements of a row)
+ * into the tiled layout the layer reads (dst; see "Weight formats"): the
+ * bytes of 16 consecutive rows for one K-block of 256 elements become one
+ * 128-byte line, so that one load of a 16-row weight tile touches one line
+ * of scales instead of 16.  rows: every row of the tensor (E_w * N for a
+ * stack of experts, N a multiple of 16), k: the row's elements (a multiple
+ * of 256).  src and dst are device buffers of rows * k / 32 bytes that must
+ * not overlap; asynchronous on `stream`.  Errors: MOE_ERR_NULL,
+ * MOE_ERR_ALIGN (a pointer not 16-byte aligned), MOE_ERR_SHAPE (rows not a
+ * positive multiple of 16, k not a positive multiple of 256),
+ * MOE_ERR_ALIAS, MOE_ERR_HIP (launch failure). */
+int moe_pack_mxfp4_scales(const uint8_t* src, uint8_t* dst, int rows, int k, void* stream);
 
 /* Measurement helper (not part of the layer): reads `bytes` (a multiple of
  * 16) of device memory at buf (16-byte aligned) once, as a plain streaming

@@ -89,6 +89,7 @@ def load_library(path: str, strict: bool = True) -> C.CDLL:
         "moe_strerror": [I],
         "moe_last_hip_error": [],
         "moe_probe_stream_read": [P, Z, P, I, P],
+        "moe_pack_mxfp4_scales": [P, P, I, I, P],
         "moe_forward_noalloc": [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P],
         "moe_forward_prefill": [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, Z, P],
         "moe_forward_unfused": [C.POINTER(MoeConfig), C.POINTER(MoeWeights), P, I, P, P, P, P, Z, P],
@@ -132,7 +133,7 @@ def using(L: C.CDLL):
 
 EXPORTS = ("moe_workspace_size", "moe_workspace_init", "moe_route", "moe_groups",
            "moe_forward", "moe_forward_residual", "moe_read_error", "moe_strerror", "moe_last_hip_error",
-           "moe_probe_stream_read", "moe_forward_noalloc", "moe_forward_after", "moe_forward_unfused",
+           "moe_probe_stream_read", "moe_pack_mxfp4_scales", "moe_forward_noalloc", "moe_forward_after", "moe_forward_unfused",
            "moe_forward_prefill")
 
 
@@ -171,6 +172,29 @@ def make_weights(case: dict) -> MoeWeights:
     return MoeWeights(_ptr(g("router_w")), _ptr(g("bias")), _ptr(g("w_gate_up")), _ptr(g("s_gate_up")),
                       _ptr(g("w_down")), _ptr(g("s_down")), _ptr(g("sh_w_gate_up")),
                       _ptr(g("sh_s_gate_up")), _ptr(g("sh_w_down")), _ptr(g("sh_s_down")))
+
+
+def moe_pack_mxfp4_scales(src: torch.Tensor, dst: torch.Tensor, rows: int, k: int, stream=None):
+    """E8M0 scale bytes of `rows` rows of k elements from the [rows][k/32]
+    grid (src) into the tiled layout the layer reads (dst, same size)."""
+    _check(lib().moe_pack_mxfp4_scales(_ptr(src), _ptr(dst), int(rows), int(k), _stream(stream)),
+           "moe_pack_mxfp4_scales")
+
+
+def packed_weights(spec: dict, case: dict) -> dict:
+    """The weight tensors the layer takes: case itself, or for MXFP4 routed
+    experts a copy of case whose scale bytes are packed into the tiled layout
+    (new device tensors; case keeps the [rows][k/32] grids)."""
+    if int(spec["routed_fmt"]) != MOE_FMT_MXFP4 or case.get("s_gate_up") is None:
+        return case
+    out = dict(case)
+    H, I = int(spec["hidden"]), int(spec["inter"])
+    for key, k in (("s_gate_up", H), ("s_down", I)):
+        src = case[key]
+        dst = torch.empty_like(src)
+        moe_pack_mxfp4_scales(src, dst, src.numel() // (k // 32), k)
+        out[key] = dst
+    return out
 
 
 def moe_workspace_size(cfg: MoeConfig) -> int:
@@ -270,7 +294,10 @@ class Layer:
         self.spec = spec
         self.case = case
         self.cfg = make_config(spec, max_rows)
-        self.w = make_weights(case)
+        # MXFP4 scales are packed once here (later changes to case's scale
+        # tensors do not reach the layer)
+        self.weights = packed_weights(spec, case)
+        self.w = make_weights(self.weights)
         self.ws_bytes = moe_workspace_size(self.cfg)
         self.ws = torch.empty(self.ws_bytes + ws_extra, dtype=torch.uint8, device=device)
         moe_workspace_init(self.ws)

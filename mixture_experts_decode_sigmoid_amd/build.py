@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["moe_kernels.hip", "moe_probe.hip", "moe_noalloc.hip", "moe_api.cpp"]
+SOURCES = ["moe_kernels.hip", "moe_probe.hip", "moe_pack.hip", "moe_noalloc.hip", "moe_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: no v_pk_*_f32 in the device code

@@ -1332,7 +1332,7 @@ struct JobDesc {
   int32_t fmt;        // 0 FP8, 1 MXFP4
   int32_t ncols;      // the group's columns
   int32_t cbase;      // its first column in the column table
-  int32_t spare;
+  int32_t srow;       // MXFP4: the expert row of lane row 0 in the tiled scale bytes (up/gate: the tile's first gate row)
 };
 static_assert(sizeof(JobDesc) == 48, "three 16-byte LDS reads");
 
@@ -1353,7 +1353,7 @@ __device__ inline JobDesc read_desc(const Lds& L, int k) {
   d.fmt = uni((int)c[0]);
   d.ncols = uni((int)c[1]);
   d.cbase = uni((int)c[2]);
-  d.spare = 0;
+  d.srow = uni((int)c[3]);
   return d;
 }
 
@@ -1369,7 +1369,7 @@ __device__ inline JobDesc make_desc(const Params& p, bool up, bool sh, int e, in
   d.nkb = kdim / (d.fmt ? 256 : 128);  // K-blocks: 128 bytes of every row (128 FP8 or 256 MXFP4 values)
   d.ncols = ncols;
   d.cbase = cbase;
-  d.spare = 0;
+  d.srow = 0;
   const int lti = p.lti;
   d.jump = up ? (lti == 3 ? iexp - 8 : iexp) : 0;
   d.tile = (uint32_t)tile;
@@ -1398,7 +1398,7 @@ __device__ inline JobDesc make_desc(const Params& p, bool up, bool sh, int e, in
     S = up ? (const uint8_t*)p.sgu + (size_t)e * 2 * I * (H / 32) : (const uint8_t*)p.sd + (size_t)e * H * (I / 32);
     if (up) {
       w += (size_t)(tile << lti) * (kdim / 2);
-      S += (size_t)(tile << lti) * d.shi;
+      d.srow = tile << lti;  // the scales are addressed by expert row (tiled layout)
     }
   }
   d.wb = (uint64_t)w;
@@ -1691,6 +1691,12 @@ __device__ __forceinline__ int lane_code(const Lds& L, const JobDesc& d) {
   return (int)lds_ld32(L.cols + d.cbase + (col < d.ncols ? col : d.ncols - 1));
 }
 
+// Byte offset of expert row n's K-block kb in tiled MXFP4 scale bytes (16
+// rows of one K-block are one 128-byte line; nkb K-blocks per row).
+__device__ __forceinline__ uint32_t mx_soff(uint32_t n, uint32_t nkb, uint32_t kb) {
+  return ((lmul(n >> 4, nkb) + kb) << 7) + ((n & 15u) << 3);
+}
+
 // Sets the fetch side to job descriptor d, whose first item is this wave's
 // K-block k0; `code` is this lane's column (row*16 + slot), n its items.
 template <int FMT, int KIND, int AL>
@@ -1716,7 +1722,7 @@ __device__ __forceinline__ void fetch_from_desc(const Params& p, const PhaseN& p
     // the K-block's 8 scale bytes of the row: lane group lg takes bytes
     // 2lg and 2lg+1, from the aligned word 4*(lg >> 1)
     f.sb = (const uint8_t*)d.sb;
-    f.so = lmul(lrow, d.shi) + 8u * (uint32_t)k0 + 4u * (uint32_t)(lg >> 1);
+    f.so = mx_soff((uint32_t)d.srow + lrow, (uint32_t)d.nkb, (uint32_t)k0) + 4u * (uint32_t)(lg >> 1);
   }
   // a lane's first piece: j = lane mod G; an MXFP4 K-block is 256 values,
   // 64 per lane group
@@ -1728,7 +1734,9 @@ __device__ __forceinline__ void fetch_from_desc(const Params& p, const PhaseN& p
   f.left = n;
   if (WT == 2 && KIND == 1) {
     f.wj = d.jump * (uint32_t)(d.nkb * 128);
-    f.sj = fmt ? d.jump * d.shi : 0u;
+    f.sj = fmt ? mx_soff((uint32_t)d.srow + lrow + d.jump, (uint32_t)d.nkb, 0u) -
+                     mx_soff((uint32_t)d.srow + lrow, (uint32_t)d.nkb, 0u)
+               : 0u;
   } else if (WT == 2) {
     // down tile B's rows (its last live row repeated, or tile A's rows if
     // it has none); both offsets are from tile A's and not negative
@@ -1740,7 +1748,7 @@ __device__ __forceinline__ void fetch_from_desc(const Params& p, const PhaseN& p
                                          : f.so;
       f.sj = so2 - f.so;
     } else {
-      f.sj = lmul(lrow2 - lrow, d.shi);
+      f.sj = mx_soff(lrow2, (uint32_t)d.nkb, 0u) - mx_soff(lrow, (uint32_t)d.nkb, 0u);
     }
   } else {
     f.wj = 0u;
@@ -1934,7 +1942,7 @@ __device__ __forceinline__ void fetch_adv_n(FetchN& f) {
   const uint32_t n = (uint32_t)uni(f.nstep);
   const bool mx = FMT != 0 && f.fmt != 0;
   f.wo += n * 128u;
-  f.so += (mx ? 8u : 4u) * n;
+  f.so += (mx ? 128u : 4u) * n;
   f.ao += (mx ? 512u : 256u) * n;
   f.left = uni(f.left) - 1;
   f.cnt = uni(f.cnt) + 1;

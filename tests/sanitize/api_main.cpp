@@ -72,6 +72,11 @@ int main(void) {
   EXPECT(moe_forward_prefill(&c, &w, (const uint16_t*)0x1000, 100, (uint16_t*)0x1040, (void*)0x4000, 1u << 30,
                              NULL) == MOE_ERR_ALIAS);
   EXPECT(moe_probe_stream_read(NULL, 1, NULL, 1, NULL) == MOE_ERR_NULL);
+  EXPECT(moe_pack_mxfp4_scales(NULL, (uint8_t*)0x1000, 16, 256, NULL) == MOE_ERR_NULL);
+  EXPECT(moe_pack_mxfp4_scales((const uint8_t*)0x1008, (uint8_t*)0x2000, 16, 256, NULL) == MOE_ERR_ALIGN);
+  EXPECT(moe_pack_mxfp4_scales((const uint8_t*)0x1000, (uint8_t*)0x2000, 15, 256, NULL) == MOE_ERR_SHAPE);
+  EXPECT(moe_pack_mxfp4_scales((const uint8_t*)0x1000, (uint8_t*)0x2000, 16, 128, NULL) == MOE_ERR_SHAPE);
+  EXPECT(moe_pack_mxfp4_scales((const uint8_t*)0x1000, (uint8_t*)0x1040, 16, 256, NULL) == MOE_ERR_ALIAS);
   for (int code = -2; code <= 12; ++code) EXPECT(moe_strerror(code) != NULL && moe_strerror(code)[0]);
   printf("ok\n");
   return 0;

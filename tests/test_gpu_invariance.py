@@ -160,9 +160,12 @@ def test_poisoned_unused_experts(fmt):
         else:
             case["s_gate_up"][e].fill_(0xFF)   # E8M0 NaN
             case["s_down"][e].fill_(0xFF)
-    out = run_forward(layer, case["x"])
+    # a layer built on the poisoned weights (MXFP4 scales are packed when a
+    # layer is built)
+    layer2 = _layer(spec, case, 8)
+    out = run_forward(layer2, case["x"])
     assert np.array_equal(out, ref)
-    assert layer.read_error() == 0
+    assert layer2.read_error() == 0
 
 
 def test_routing_exact_ties():
@@ -209,13 +212,13 @@ def test_error_word_on_nan_weight_code_in_a_used_expert(fmt, T):
         over.update(routed_fmt=1, bias_bf16=1, n_group=1, topk_group=1)
     spec = fixtures.spec_with("tiny", **over)
     case = gpu_case(spec, T, 27 + T)
-    layer = _layer(spec, case, T)
     ids, _, _, _ = oracle_route(spec, case)
     e = int(ids[0, 0])
     if fmt == 0:
         case["w_gate_up"][e, 3, 17] = 0x7F      # one weight of one gate row
     else:
         case["s_down"][e, 5, 2] = 0xFF          # one block scale of one down row
+    layer = _layer(spec, case, T)               # (MXFP4 scales are packed here)
     run_forward(layer, case["x"], check=False)
     bits = layer.read_error()
     assert bits & moe.MOE_DEVERR_NONFINITE_MID, bits

@@ -32,7 +32,7 @@ def test_oracle_under_sanitizers(tmp_path):
 
 def test_api_host_side_under_sanitizers(tmp_path):
     objdir = os.path.join(ROOT, "_build", "libmoe")
-    dev = [os.path.join(objdir, s + ".o") for s in ("moe_kernels.hip", "moe_probe.hip", "moe_noalloc.hip")]
+    dev = [os.path.join(objdir, s + ".o") for s in ("moe_kernels.hip", "moe_probe.hip", "moe_pack.hip", "moe_noalloc.hip")]
     if not all(os.path.exists(o) for o in dev) or not os.path.exists("/opt/rocm/lib/libamdhip64.so"):
         pytest.skip("needs the in-tree build's device objects and the HIP runtime")
     csrc = os.path.join(ROOT, "mixture_experts_decode_sigmoid_amd", "csrc")
