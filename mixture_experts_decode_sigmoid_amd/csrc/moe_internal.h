@@ -36,19 +36,23 @@ enum Mode {
 // Measured on the DeepSeek-V3 layer at 12 and 16 rows (and the MXFP4 layer
 // at 16): two loads beat four by 12-16% and one by 5-7%.
 __host__ __device__ inline int stream_al(int T) { return T <= 4 ? 1 : 2; }
-// Intermediates per up/gate tile (ti).  An item is one 16-row MFMA tile (8
-// gate rows and their 8 up rows), except in a kernel with MXFP4 routed
-// experts and two activation loads per item: there an item is two tiles (16
-// gate rows, then their 16 up rows) on one activation operand, which halves
-// the activation bytes a CU reads per weight byte (an MXFP4 K-block carries
-// twice the activations of an FP8 one).  Each output element's arithmetic is
-// the same either way.  Measured (paired A/B): MXFP4 16 rows -11.7 us; FP8
-// 8 rows +1.0 and 64 rows +2.9 us, where each chunk then streams twice the
-// bytes and the waves' last chunks end further apart.
-__host__ __device__ inline int stream_ti(int T, int fmt) { return stream_al(T) == 2 && fmt != 0 ? 16 : 8; }
 // Down jobs are split over waves by K-phase up to this many rows; above it
 // every wave claims whole down jobs (the K-phase partials would not fit LDS).
 constexpr int kKsplitRows = 16;
+// Intermediates per up/gate tile (ti).  An item is one 16-row MFMA tile (8
+// gate rows and their 8 up rows), except with two activation loads per item
+// in a kernel with MXFP4 routed experts, or above kKsplitRows rows: there an
+// item is two tiles (16 gate rows, then their 16 up rows) on one activation
+// operand, which halves the activation bytes a CU reads per weight byte.
+// Each output element's arithmetic is the same either way.  Measured
+// (paired A/B): MXFP4 16 rows -11.7 us; FP8 64 rows -19 to -25 us (ring
+// depth 6), while FP8 from 5 to 16 rows lost 0.5 to 2.6 us and the 8-way
+// expert-parallel share at 64 rows 15 us (a CU's jobs are then few, and its
+// last chunks end further apart), so stream_geometry keeps FP8 layers with
+// fewer than 32 (group, tile) pairs per CU at one tile.
+__host__ __device__ inline int stream_ti(int T, int fmt) {
+  return (stream_al(T) == 2 && fmt != 0) || T > kKsplitRows ? 16 : 8;
+}
 constexpr int kSpreadRows = 8;          // from this many rows (up to 8) each row is routed by one CU
 
 // Workspace layout (byte offsets from the workspace base).

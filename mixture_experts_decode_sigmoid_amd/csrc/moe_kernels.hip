@@ -312,6 +312,12 @@ size_t stream_geometry(Params& p, bool fp8_tiles) {
   p.cpj = 4 * stream_al(p.T);
   p.pcols = p.T < p.cpj ? p.T : p.cpj;
   p.ti = stream_ti(p.T, fp8_tiles ? 0 : p.routed_fmt);
+  if (p.ti == 16 && (fp8_tiles || p.routed_fmt == 0)) {
+    // FP8 two-tile items only where a CU has many (group, tile) pairs: with
+    // few (an expert range of 32 experts) the coarser jobs end unevenly
+    const int groups = (p.ec < p.T * p.K ? p.ec : p.T * p.K) + p.n_shared;
+    if ((long)groups * (p.I / 16) < 32L * p.ncu) p.ti = 8;
+  }
   p.lti = p.ti == 16 ? 4 : 3;
   const int tk = p.T * p.K;
   const int nct_sh = p.n_shared ? (p.T + p.cpj - 1) / p.cpj : 0;
@@ -1661,8 +1667,10 @@ struct FetchN {
 // one tile.
 // Down items are two 16-row down tiles of the CU's slice on one activation
 // operand (see ksplit_phase and fetch_next_dc).
-template <int FMT, int KIND, int AL>
-constexpr int item_wt() { return (AL == 2 && FMT != 0 && KIND == 1) || KIND != 1 ? 2 : 1; }
+// W2: the up/gate items of an FP8 kernel are two tiles too (above
+// kKsplitRows rows, see stream_ti).
+template <int FMT, int KIND, int AL, bool W2 = false>
+constexpr int item_wt() { return (AL == 2 && (FMT != 0 || W2) && KIND == 1) || KIND != 1 ? 2 : 1; }
 
 // One item: a K-block of a 16-row tile, 128 bytes of each row (FP8: 128
 // values, one fp32 block scale per 128-row block; MXFP4: 256 values, the
@@ -1699,12 +1707,12 @@ __device__ __forceinline__ uint32_t mx_soff(uint32_t n, uint32_t nkb, uint32_t k
 
 // Sets the fetch side to job descriptor d, whose first item is this wave's
 // K-block k0; `code` is this lane's column (row*16 + slot), n its items.
-template <int FMT, int KIND, int AL>
+template <int FMT, int KIND, int AL, bool W2 = false>
 __device__ __forceinline__ void fetch_from_desc(const Params& p, const PhaseN& ph, FetchN& f, const JobDesc& d, int k0,
                                                 int n, int code) {
   const int lane = threadIdx.x & 63, lg = lane >> 4, row = lane & 15;
   const int fmt = FMT == 0 ? 0 : d.fmt;
-  constexpr int WT = item_wt<FMT, KIND, AL>();
+  constexpr int WT = item_wt<FMT, KIND, AL, W2>();
   const uint32_t lrow = KIND == 1 ? (WT == 2 ? row : row < 8 ? row : row + d.jump)
                                   : ph.hb + (row < ph.nlive ? row : ph.nlive - 1);
   f.wb = (const uint8_t*)d.wb;
@@ -1828,7 +1836,7 @@ __device__ __forceinline__ void chunk_map(uint32_t c, const PhaseN& ph, int& q, 
     kp = (int)c - q * ph.nw;
   }
 }
-template <int FMT, int AL>
+template <int FMT, int AL, bool W2 = false>
 __device__ inline void fetch_next_up(const Params& p, const Lds& L, const PhaseN& ph, FetchN& f, int nS, bool& ok) {
   const uint32_t c = lds_inc_lane0(L.ccnt);
   int q, kp;
@@ -1841,7 +1849,7 @@ __device__ inline void fetch_next_up(const Params& p, const Lds& L, const PhaseN
     const JobDesc d = read_desc(L, q);
     lds_st32(L.cfifo + wave_id() * 8 + (f.nch & 7), c);
     f.nch = f.nch + 1;
-    fetch_from_desc<FMT, 1, AL>(p, ph, f, d, kp, ((d.nkb - 1 - kp) >> 3) + 1, lane_code<AL>(L, d));
+    fetch_from_desc<FMT, 1, AL, W2>(p, ph, f, d, kp, ((d.nkb - 1 - kp) >> 3) + 1, lane_code<AL>(L, d));
     return;
   }
   fetch_dead(p, f);
@@ -1893,10 +1901,10 @@ __device__ inline void fetch_next_dc(const Params& p, const Lds& L, const PhaseN
 
 // kend: up/gate, the CU's shared-expert job count; down (KIND 2), the end of
 // its job range; KIND 3, its unit count.
-template <int FMT, int KIND, int AL>
+template <int FMT, int KIND, int AL, bool W2 = false>
 __device__ __forceinline__ void fetch_next_any(const Params& p, const Lds& L, const PhaseN& ph, FetchN& f, int kend,
                                                bool& ok) {
-  if (KIND == 1) fetch_next_up<FMT, AL>(p, L, ph, f, kend, ok);
+  if (KIND == 1) fetch_next_up<FMT, AL, W2>(p, L, ph, f, kend, ok);
   else if (KIND == 3) fetch_next_dc<FMT, AL>(p, L, ph, f, kend);
   else fetch_next_n<FMT, KIND, AL>(p, L, ph, f, kend);
 }
@@ -1990,7 +1998,7 @@ __device__ inline bool eat_next_n(const Params& p, const Lds& L, const PhaseN& p
 // Up/gate: moves the multiplying side to the next chunk the fetch side has
 // set up (fnch: chunks it has claimed); false at the end.  The partial goes
 // to window q mod kPuWin, K-phase row kp, the lane's column.
-template <int FMT, int AL>
+template <int FMT, int AL, bool W2 = false>
 __device__ inline bool eat_next_up(const Params& p, const Lds& L, const PhaseN& ph, EatN& e, int fnch) {
   if (e.nch >= fnch) return false;
   const int lane = threadIdx.x & 63, lg = lane >> 4, col = lane_col<AL>(lane);
@@ -2004,7 +2012,7 @@ __device__ inline bool eat_next_up(const Params& p, const Lds& L, const PhaseN& 
   e.fmt = FMT == 0 ? 0 : d.fmt;
   e.pst = col < d.ncols && (lane & (4 / AL - 1)) == 0;
   e.pidx = ((((uint32_t)q & (kPuWin - 1)) * kWaves + (uint32_t)kp) * (uint32_t)p.pcols + (uint32_t)col) *
-               (16u * (uint32_t)item_wt<FMT, 1, AL>()) +
+               (16u * (uint32_t)item_wt<FMT, 1, AL, W2>()) +
            4u * (uint32_t)lg;
   return true;
 }
@@ -2268,8 +2276,8 @@ constexpr int ring_dc() { return 4; }
 // up/gate ring depth by activation loads per item (FP8 with 2 loads: 7
 // measured best at 8 rows; MXFP4 with 2, whose items are two weight tiles:
 // 3 measured best at 16 rows, against 4 and 5)
-template <int FMT, int AL>
-constexpr int ring_up() { return AL == 2 ? (FMT == 0 ? 7 : 3) : kRingD; }
+template <int FMT, int AL, bool W2 = false>
+constexpr int ring_up() { return AL == 2 ? (FMT == 0 ? (W2 ? 6 : 7) : 3) : kRingD; }
 template <int D = kRingD>
 struct RingN {
   FetchN f;
@@ -2277,7 +2285,7 @@ struct RingN {
   uint32_t aop[D], h2p[D];  // activation offsets of the filled items (split fill)
 };
 
-template <int FMT, int KIND, int D, int AL>
+template <int FMT, int KIND, int D, int AL, bool W2 = false>
 __device__ __forceinline__ void ring_open(const Params& p, const Lds& L, const PhaseN& ph, RingN<D>& R, int k, int kend,
                                           bool& ok) {
   R.f.k = k;
@@ -2285,24 +2293,24 @@ __device__ __forceinline__ void ring_open(const Params& p, const Lds& L, const P
   R.f.nu = -1;
   R.f.cnt = 0;
   R.f.ab = (const uint8_t*)(KIND == 1 ? arg_ptr(p.x) : arg_ptr(p.mid));
-  fetch_next_any<FMT, KIND, AL>(p, L, ph, R.f, kend, ok);
+  fetch_next_any<FMT, KIND, AL, W2>(p, L, ph, R.f, kend, ok);
 }
 
 // WONLY: weights and scales only (the activation offsets are kept).
-template <int FMT, int KIND, bool WONLY, int D, int AL>
+template <int FMT, int KIND, bool WONLY, int D, int AL, bool W2 = false>
 __device__ __forceinline__ void ring_fill(const Params& p, const Lds& L, const PhaseN& ph, RingN<D>& R, int kend,
                                           bool& ok) {
 #pragma unroll
   for (int d = 0; d < D; ++d) {
     if (WONLY) {
-      fetch_weights_n<FMT, item_wt<FMT, KIND, AL>()>(R.f, R.r[d]);
+      fetch_weights_n<FMT, item_wt<FMT, KIND, AL, W2>()>(R.f, R.r[d]);
       R.aop[d] = R.f.ao;
       R.h2p[d] = R.f.h2;
     } else {
-      fetch_item_n<FMT, AL, item_wt<FMT, KIND, AL>()>(R.f, R.r[d]);
+      fetch_item_n<FMT, AL, item_wt<FMT, KIND, AL, W2>()>(R.f, R.r[d]);
     }
     fetch_adv_n<FMT>(R.f);
-    if (R.f.left == 0) fetch_next_any<FMT, KIND, AL>(p, L, ph, R.f, kend, ok);
+    if (R.f.left == 0) fetch_next_any<FMT, KIND, AL, W2>(p, L, ph, R.f, kend, ok);
   }
 }
 
@@ -2316,18 +2324,18 @@ __device__ __forceinline__ void ring_fill_acts(RingN<D>& R) {
 // counted from the steady load order (a split fill issues them in another).
 // Up/gate (KIND 1): chunks are claimed from the CU's counter and chunk ends
 // go through the partial windows.
-template <int FMT, int KIND, bool PEEL, int D, int AL>
+template <int FMT, int KIND, bool PEEL, int D, int AL, bool W2 = false>
 __device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const PhaseN& ph, RingN<D>& R, int k, int kend,
                                          int& jc, bool& ok) {
   EatN e;
   e.k = k;
   e.nch = 0;
-  const bool any = KIND == 1   ? eat_next_up<FMT, AL>(p, L, ph, e, R.f.nch)
+  const bool any = KIND == 1   ? eat_next_up<FMT, AL, W2>(p, L, ph, e, R.f.nch)
                    : KIND == 3 ? eat_next_dc<FMT, AL>(p, L, ph, e, R.f.nch)
                                : eat_next_n<FMT, KIND, AL>(p, L, ph, e, kend);
   if (any) {
     const int lg = (threadIdx.x & 63) >> 4;
-    constexpr int WT = item_wt<FMT, KIND, AL>();
+    constexpr int WT = item_wt<FMT, KIND, AL, W2>();
     const int split_c = KIND == 3 ? 0 : ph_split<KIND, WT>(ph);
     const int split2_c = KIND == 3 ? 0 : ph_split2<KIND>(ph);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -2349,7 +2357,7 @@ __device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const Ph
         else eat_item_n<1, AL, WT>(split, split2, lg, R.r[d], acc, acc2);
         fetch_item_n<FMT, AL, WT>(R.f, R.r[d]);
         fetch_adv_n<FMT>(R.f);
-        if (R.f.left == 0) fetch_next_any<FMT, KIND, AL>(p, L, ph, R.f, kend, ok);
+        if (R.f.left == 0) fetch_next_any<FMT, KIND, AL, W2>(p, L, ph, R.f, kend, ok);
         if (!done) {
           e.left = uni(e.left) - 1;
           if (KIND == 3 && e.left == 0) {
@@ -2369,7 +2377,7 @@ __device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const Ph
             acc2 = f32x4{0.f, 0.f, 0.f, 0.f};
             MOE_JSTAMP(p, jc);
             balance(L, ++jc);
-            done = KIND == 1 ? !eat_next_up<FMT, AL>(p, L, ph, e, R.f.nch)
+            done = KIND == 1 ? !eat_next_up<FMT, AL, W2>(p, L, ph, e, R.f.nch)
                              : !eat_next_n<FMT, KIND, AL>(p, L, ph, e, kend);
           }
         }
@@ -2506,13 +2514,15 @@ __device__ __forceinline__ const Params& fresh_args() {
 // once it has grouped the uses and written the routed tables.
 // DCLAIM: down jobs claimed whole by the waves (above kKsplitRows rows),
 // else split over the waves by K-phase.
-template <int FMT, int AL, bool DCLAIM>
+// W2: FP8 up/gate items of two tiles (see stream_ti).
+template <int FMT, int AL, bool DCLAIM, bool W2>
 __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
   const int wave = wave_id();
   int jn = 0;  // jobs this wave has ended (for balance)
   bool ok = true;
   {
-    RingN<ring_up<FMT, AL>()> R;
+    constexpr int DU = ring_up<FMT, AL, W2>();
+    RingN<DU> R;
     const Params& p = fresh_args();
     const Lds L = lds_map(smem, p);
     const int nkb = p.H / 128;
@@ -2607,11 +2617,11 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
       __syncthreads();
       MOE_STAMP(p, 11);
     }
-    ring_open<FMT, 1, ring_up<FMT, AL>(), AL>(p, L, ph, R, 0, nS, ok);
+    ring_open<FMT, 1, DU, AL, W2>(p, L, ph, R, 0, nS, ok);
     MOE_STAMP(p, 62);
-    ring_fill<FMT, 1, false, ring_up<FMT, AL>(), AL>(p, L, ph, R, nS, ok);
+    ring_fill<FMT, 1, false, DU, AL, W2>(p, L, ph, R, nS, ok);
     MOE_STAMP(p, 13);
-    ring_run<FMT, 1, false, ring_up<FMT, AL>(), AL>(p, L, ph, R, 0, nS, jn, ok);
+    ring_run<FMT, 1, false, DU, AL, W2>(p, L, ph, R, 0, nS, jn, ok);
     MOE_WSTAMP(p, 0);
     MOE_TVAL(p, 8, jn);
   }
@@ -2681,7 +2691,7 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
 // CU's shared gate/up jobs and leaves mid in the workspace (visible to the
 // next launch at the kernel boundary); otherwise the down jobs of the shared
 // group read that mid, and the shared product alone is rounded to bf16.
-template <int FMT, int AL, bool DCLAIM, bool UP>
+template <int FMT, int AL, bool DCLAIM, bool UP, bool W2>
 __device__ __forceinline__ void shared_only(char* smem) {
   const Params& p = fresh_args();
   const Lds L = lds_map(smem, p);
@@ -2707,10 +2717,11 @@ __device__ __forceinline__ void shared_only(char* smem) {
     ph.nw = nkb < kWaves ? nkb : kWaves;
     ph.nct = n_ctiles(p, p.T);
     ph.nsc = nS * ph.nw;
-    RingN<ring_up<FMT, AL>()> R;
-    ring_open<FMT, 1, ring_up<FMT, AL>(), AL>(p, L, ph, R, 0, nS, ok);
-    ring_fill<FMT, 1, false, ring_up<FMT, AL>(), AL>(p, L, ph, R, nS, ok);
-    ring_run<FMT, 1, false, ring_up<FMT, AL>(), AL>(p, L, ph, R, 0, nS, jn, ok);
+    constexpr int DU = ring_up<FMT, AL, W2>();
+    RingN<DU> R;
+    ring_open<FMT, 1, DU, AL, W2>(p, L, ph, R, 0, nS, ok);
+    ring_fill<FMT, 1, false, DU, AL, W2>(p, L, ph, R, nS, ok);
+    ring_run<FMT, 1, false, DU, AL, W2>(p, L, ph, R, 0, nS, jn, ok);
     return;
   }
   const int nD = lds_ldi_uniform(L.misc + kMiscND);
@@ -2786,7 +2797,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
     stream_init(p, L, shared_jobs_here(p));
     __syncthreads();
     constexpr int AL = NARROW == 2 ? 1 : 2;
-    shared_only<FMT, AL, NARROW == 4, MODE == kModeSharedUp>(smem);
+    shared_only<FMT, AL, NARROW >= 4, MODE == kModeSharedUp, NARROW == 4>(smem);
     return;
   }
   if (MODE == kModeForward) {
@@ -2811,7 +2822,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_fused(Params p) {
     }
     MOE_STAMP(p, 1);
     constexpr int AL = NARROW == 2 ? 1 : 2;
-    narrow_forward<FMT, AL, NARROW == 4>(smem, __builtin_amdgcn_readfirstlane(ep));
+    narrow_forward<FMT, AL, NARROW >= 4, NARROW == 4>(smem, __builtin_amdgcn_readfirstlane(ep));
     return;
   }
 
@@ -2908,7 +2919,10 @@ static hipError_t launch_one(const Params& p, hipStream_t stream, int dev) {
 
 template <int MODE, int FMT>
 static hipError_t launch_forward(const Params& p, hipStream_t stream, int dev) {
-  if (p.T > kKsplitRows) return launch_one<MODE, FMT, 4>(p, stream, dev);  // (stream_al: 2)
+  // above kKsplitRows rows: two-tile up/gate items (4) or, for an FP8 layer
+  // whose tiles are 8 intermediates (stream_geometry), one-tile items (5)
+  if (p.T > kKsplitRows)
+    return FMT == 0 && p.ti == 8 ? launch_one<MODE, FMT, 5>(p, stream, dev) : launch_one<MODE, FMT, 4>(p, stream, dev);
   return stream_al(p.T) == 1 ? launch_one<MODE, FMT, 2>(p, stream, dev) : launch_one<MODE, FMT, 3>(p, stream, dev);
 }
 
