@@ -7,17 +7,17 @@
 //                       publishes each score in a slot tagged with the call's
 //                       epoch; then raises its flag (epoch + 1).
 //   S1  shared up/gate  the shared expert does not depend on routing, so its
-//                       8-intermediate tiles are streamed while the other CUs
-//                       finish S0.
+//                       tiles are streamed while the routing runs.
 //   S2  route + group   every CU polls the score slots of every row until
 //                       they carry the call's tag, routes every row itself
 //                       (no hand-off) and builds the step's group table in
 //                       LDS: distinct experts in order of first use, found by
 //                       ballot / prefix count, each with its using rows.
-//   S3  routed up/gate  jobs (group, 8-intermediate tile) dealt round-robin
-//                       over CUs; each job streams 16 weight rows (8 gate + 8
-//                       up) once and uses every row of the group as an MFMA
-//                       column; SwiGLU mid values go to the workspace.
+//   S3  routed up/gate  jobs (group, tile of 8 or 16 intermediates) dealt
+//                       round-robin over CUs; each job streams its gate and
+//                       up weight rows once and uses every row of the group
+//                       as an MFMA column; SwiGLU mid values go to the
+//                       workspace.
 //   S4  down            after a second flag barrier, CU c owns output rows
 //                       [c*hs, (c+1)*hs) and streams that slice of every used
 //                       expert's W_down once; per (row, slot) products stay in
@@ -1180,13 +1180,14 @@ __device__ inline void build_groups(const Params& p, const Lds& L) {
 // ------------------------------------------------------------------ weight stream
 //
 // Each CU walks a sequence of jobs: its shared-expert up/gate tiles, its
-// routed up/gate tiles (16 weight rows, 8 gate + 8 up, over all of H), then
-// its 16-row down tiles of every used expert (over that expert's
-// intermediate size).  The 8 waves split every job along the reduction
-// axis in K-phases: phase w holds the K-blocks w, w+8, w+16, ... (128 bytes
-// of every weight row: 128 FP8 or 256 MXFP4 values).  One K-block of one
-// job is an item: the 16 rows' weights (32 bytes per lane), the block
-// scale and the activations of the job's columns.  A wave loads its items
+// routed up/gate tiles (8 gate rows and their 8 up rows, or 16 and 16 in
+// two-tile items, over all of H), then its down rows of every used expert
+// (over that expert's intermediate size).  The 8 waves split every job
+// along the reduction axis in K-phases: phase w holds the K-blocks w, w+8,
+// w+16, ... (128 bytes of every weight row: 128 FP8 or 256 MXFP4 values).
+// One K-block of one job is an item: the weights of one or two 16-row MFMA
+// tiles (32 bytes per lane each), their block scales and the activations of
+// the job's columns, shared by the tiles.  A wave loads its items
 // straight from HBM into registers, D items ahead of the one it
 // multiplies; every item issues the same number of loads, so the in-order
 // wait for item n leaves items n+1..n+D-1 in flight.  (An LDS ring fed by
@@ -1412,7 +1413,7 @@ __device__ inline JobDesc make_desc(const Params& p, bool up, bool sh, int e, in
   return d;
 }
 
-// Up/gate (group, 8-intermediate tile) pair j of the step: the shared tiles,
+// Up/gate (group, tile) pair j of the step: the shared tiles,
 // then rt_tiles tiles per routed group.  Sets its group and tile.  A routed
 // group's tiles are rotated by 37 per group, so that a CU's pairs fall on
 // different row blocks of successive experts (unrotated, CU c reads row
@@ -1535,10 +1536,12 @@ __device__ inline void routed_tables(const Params& p, const Lds& L, const Sched&
 
 // Per-wave constants of a phase (KIND 1 up/gate, 2 down split by K-phase,
 // 3 down by claimed whole jobs).  Up/gate: every wave takes K-blocks w + 8i
-// of each job, rows 0..7 of a tile are gate rows and 8..15 up rows.  Down
-// (KIND 2): wave w takes tile rt = w % nrt_p of the CU's slice, rows hb..
-// (nlive live), and K-blocks w / nrt_p + wpt*i.  KIND 3: a claimed job's
-// tile and all its K-blocks (the constants are set per job).
+// of each job; in a one-tile item rows 0..7 are gate rows and 8..15 up rows,
+// in a two-tile item tile A holds 16 gate rows and tile B their up rows.
+// Down (KIND 2): wave w takes tile rt of the CU's slice, rows hb.. (nlive
+// live), and with two-tile items tile rt + 1 too (hb2, nlive2), and its
+// K-phase's K-blocks (see ksplit_phase).  KIND 3: a claimed unit's tiles and
+// all its K-blocks (the constants are set per unit).
 struct PhaseN {
   int k0, lstep;  // this wave's K-blocks: k0 + (i << lstep)
   int hb, nlive;  // down: first row of this wave's tile and its live rows
@@ -2641,8 +2644,8 @@ __device__ __forceinline__ void narrow_forward(char* smem, uint32_t epoch) {
     constexpr int DD = DCLAIM ? ring_dc<FMT, AL>() : ring_dn<FMT, AL>();
     RingN<DD> R;
     if (!DCLAIM) {
-      // wave w takes tile w % nrt_p of this CU's slice and K-blocks
-      // w / nrt_p + wpt*i of every down job (two-tile items: see ksplit_phase)
+      // each wave takes its tiles of this CU's slice in one K-phase of the
+      // down jobs it shares out with the other waves (see ksplit_phase)
       const PhaseN ph = ksplit_phase<item_wt<FMT, 2, AL>()>(p, s, wave);
       const int kend = ph.nlive > 0 ? p.qcap + nD : p.qcap;
       ring_open<FMT, 2, DD, AL>(p, L, ph, R, p.qcap, kend, ok);
