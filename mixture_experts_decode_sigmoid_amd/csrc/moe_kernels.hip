@@ -1718,6 +1718,14 @@ __device__ __forceinline__ void fetch_from_desc(const Params& p, const PhaseN& p
   constexpr int WT = item_wt<FMT, KIND, AL, W2>();
   const uint32_t lrow = KIND == 1 ? (WT == 2 ? row : row < 8 ? row : row + d.jump)
                                   : ph.hb + (row < ph.nlive ? row : ph.nlive - 1);
+  // down tile B's rows (its last live row repeated, or tile A's rows if
+  // it has none)
+  const uint32_t lrow2 = WT == 2 && KIND != 1 && ph.nlive2 > 0
+                             ? (uint32_t)(ph.hb2 + (row < ph.nlive2 ? row : ph.nlive2 - 1))
+                             : lrow;
+  // A kernel with MXFP4 experts loads a two-tile item's scales with one
+  // load (s): see eat_item_n.
+  constexpr bool M2 = FMT != 0 && WT == 2;
   f.wb = (const uint8_t*)d.wb;
   // 128 bytes of each row per K-block, 32 per lane group
   f.wo = lmul(lrow, (uint32_t)(d.nkb * 128)) + (uint32_t)k0 * 128u + (uint32_t)lg * 32u;
@@ -1725,10 +1733,23 @@ __device__ __forceinline__ void fetch_from_desc(const Params& p, const PhaseN& p
     if (KIND == 1) {
       f.sb = (const uint8_t*)d.sb;
       f.so = (lane < 32 ? 0u : d.shi) + 4u * (uint32_t)k0;
+    } else if (M2) {
+      // one block-scale word per lane quarter: tile A's first and second
+      // block row, then tile B's (tile A's again if tile B has no rows)
+      f.sb = (const uint8_t*)d.sb + 4 * (size_t)(ph.hb >> 7) * d.nkb;
+      const uint32_t b2 = ph.nlive2 > 0 ? 4u * (uint32_t)(((ph.hb2 >> 7) - (ph.hb >> 7)) * d.nkb) : 0u;
+      const uint32_t d2 = 4u * (uint32_t)((ph.nlive2 > 0 ? ph.dnb2 : ph.dnb) * d.nkb);
+      f.so = (lg == 0 ? 0u : lg == 1 ? 4u * (uint32_t)(ph.dnb * d.nkb) : lg == 2 ? b2 : b2 + d2) + 4u * (uint32_t)k0;
     } else {
       f.sb = (const uint8_t*)d.sb + 4 * (size_t)(ph.hb >> 7) * d.nkb;
       f.so = (lane < 32 ? 0u : 4u * (uint32_t)(ph.dnb * d.nkb)) + 4u * (uint32_t)k0;
     }
+  } else if (M2) {
+    // lane groups 0 and 1 take words 0 and 1 (bytes 0..7) of tile A's row,
+    // groups 2 and 3 those of tile B's row
+    f.sb = (const uint8_t*)d.sb;
+    const uint32_t na = (uint32_t)d.srow + lrow, nb = KIND == 1 ? na + d.jump : lrow2;
+    f.so = mx_soff(lg < 2 ? na : nb, (uint32_t)d.nkb, (uint32_t)k0) + 4u * (uint32_t)(lg & 1);
   } else {
     // the K-block's 8 scale bytes of the row: lane group lg takes bytes
     // 2lg and 2lg+1, from the aligned word 4*(lg >> 1)
@@ -1745,15 +1766,13 @@ __device__ __forceinline__ void fetch_from_desc(const Params& p, const PhaseN& p
   f.left = n;
   if (WT == 2 && KIND == 1) {
     f.wj = d.jump * (uint32_t)(d.nkb * 128);
-    f.sj = fmt ? mx_soff((uint32_t)d.srow + lrow + d.jump, (uint32_t)d.nkb, 0u) -
-                     mx_soff((uint32_t)d.srow + lrow, (uint32_t)d.nkb, 0u)
-               : 0u;
+    f.sj = 0u;  // (an FP8 kernel's up/gate s2 repeats s)
   } else if (WT == 2) {
-    // down tile B's rows (its last live row repeated, or tile A's rows if
-    // it has none); both offsets are from tile A's and not negative
-    const uint32_t lrow2 = ph.nlive2 > 0 ? (uint32_t)(ph.hb2 + (row < ph.nlive2 ? row : ph.nlive2 - 1)) : lrow;
+    // tile B's weights from tile A's: not negative
     f.wj = lmul(lrow2 - lrow, (uint32_t)(d.nkb * 128));
-    if (fmt == 0) {
+    if (M2) {
+      f.sj = 0u;
+    } else if (fmt == 0) {
       const uint32_t so2 = ph.nlive2 > 0 ? 4u * (uint32_t)(((ph.hb2 >> 7) - (ph.hb >> 7)) * d.nkb) +
                                                (lane < 32 ? 0u : 4u * (uint32_t)(ph.dnb2 * d.nkb)) + 4u * (uint32_t)k0
                                          : f.so;
@@ -1922,10 +1941,10 @@ __device__ __forceinline__ void fetch_weights_n(const FetchN& f, ItemN& it) {
     it.w3 = ldg<u32x4>(w + f.wj + 16);
   }
   it.s = ldg<uint32_t>(f.sb + f.so);
-  // tile B's scales: an MXFP4 up/gate tile B's rows, a down tile B's rows;
-  // an FP8 up/gate item loads s again (the up rows' block scale is lane 32's
-  // word of s)
-  if (WT == 2) it.s2 = ldg<uint32_t>(f.sb + (uint32_t)(f.so + f.sj));
+  // an FP8 kernel's tile B scales: a down tile B's block rows; an up/gate
+  // item loads s again (the up rows' block scale is lane 32's word of s).
+  // A kernel with MXFP4 experts has both tiles' scales in s.
+  if (WT == 2 && FMT == 0) it.s2 = ldg<uint32_t>(f.sb + (uint32_t)(f.so + f.sj));
 }
 // Activations: AL loads of 16 B per lane per 128 values, pieces j + G*i
 // (the load instructions, not the bytes, are what the vector memory path
@@ -2172,7 +2191,12 @@ __device__ __forceinline__ bf16x8 act_operand(const ItemN& it, int m) {
 
 // split / split2: MFMA output rows (4*lg + q) of tile A / tile B below it
 // take lane 0's scale word of s / s2, the others lane 32's (FP8).
-template <int F, int AL, int WT>
+// Q4 (two-tile items in a kernel with MXFP4 experts): an FP8 item holds
+// tile A's two block-scale words at lanes 0 and 16 of s and tile B's at
+// lanes 32 and 48; an MXFP4 item holds words 0 and 1 of each row's scale
+// bytes for tile A in lane groups 0 and 1 and for tile B in groups 2 and 3,
+// which two row-swap steps hand to the lanes that use them.
+template <int F, int AL, int WT, bool Q4 = false>
 __device__ __forceinline__ void eat_item_n(int split, int split2, int lg, const ItemN& it, f32x4& acc, f32x4& acc2) {
   bf16x8 A[4];
   if (F == 0 && WT == 1) {
@@ -2195,9 +2219,9 @@ __device__ __forceinline__ void eat_item_n(int split, int split2, int lg, const 
 #pragma unroll
     for (int m = 0; m < 4; ++m) Bm[m] = act_operand<AL>(it, m);
     const float s_lo = __int_as_float(__builtin_amdgcn_readlane((int)it.s, 0));
-    const float s_hi = __int_as_float(__builtin_amdgcn_readlane((int)it.s, 32));
-    const float s2_lo = __int_as_float(__builtin_amdgcn_readlane((int)it.s2, 0));
-    const float s2_hi = __int_as_float(__builtin_amdgcn_readlane((int)it.s2, 32));
+    const float s_hi = __int_as_float(__builtin_amdgcn_readlane((int)it.s, Q4 ? 16 : 32));
+    const float s2_lo = __int_as_float(__builtin_amdgcn_readlane((int)(Q4 ? it.s : it.s2), Q4 ? 32 : 0));
+    const float s2_hi = __int_as_float(__builtin_amdgcn_readlane((int)(Q4 ? it.s : it.s2), Q4 ? 48 : 32));
     A[0] = e4m3x8_to_bf16(it.w0[0], it.w0[1]);
     A[1] = e4m3x8_to_bf16(it.w0[2], it.w0[3]);
     A[2] = e4m3x8_to_bf16(it.w1[0], it.w1[1]);
@@ -2237,8 +2261,14 @@ __device__ __forceinline__ void eat_item_n(int split, int split2, int lg, const 
 #pragma unroll
     for (int m = 0; m < 8; ++m) Bm[m] = act_operand<AL>(it, m);
     const uint32_t sh = 16u * (uint32_t)(lg & 1);
+    // lane group g gets word g >> 1 of its row's bytes for each tile
+    // (row r of lane group g: lane 16g + r)
+    const auto x = __builtin_amdgcn_permlane32_swap(it.s, it.s, false, false);  // groups (0,1,0,1), (2,3,2,3)
+    const auto ta = __builtin_amdgcn_permlane16_swap(x[0], x[0], false, false);  // all groups 0, all 1
+    const auto tb = __builtin_amdgcn_permlane16_swap(x[1], x[1], false, false);  // all groups 2, all 3
+    const uint32_t sa = lg < 2 ? ta[0] : ta[1], sb = lg < 2 ? tb[0] : tb[1];
     {
-      const float sc0 = e8m0_to_f32((it.s >> sh) & 0xffu), sc1 = e8m0_to_f32((it.s >> (sh + 8)) & 0xffu);
+      const float sc0 = e8m0_to_f32((sa >> sh) & 0xffu), sc1 = e8m0_to_f32((sa >> (sh + 8)) & 0xffu);
 #pragma unroll
       for (int m = 0; m < 4; ++m) A[m] = e2m1x8_to_bf16(it.w0[m], sc0);
 #pragma unroll
@@ -2249,7 +2279,7 @@ __device__ __forceinline__ void eat_item_n(int split, int split2, int lg, const 
       for (int m = 0; m < 4; ++m) acc = mfma16(A[m], Bm[4 + m], acc);
     }
     {
-      const float sc0 = e8m0_to_f32((it.s2 >> sh) & 0xffu), sc1 = e8m0_to_f32((it.s2 >> (sh + 8)) & 0xffu);
+      const float sc0 = e8m0_to_f32((sb >> sh) & 0xffu), sc1 = e8m0_to_f32((sb >> (sh + 8)) & 0xffu);
 #pragma unroll
       for (int m = 0; m < 4; ++m) A[m] = e2m1x8_to_bf16(it.w2[m], sc0);
 #pragma unroll
@@ -2356,7 +2386,7 @@ __device__ __forceinline__ void ring_run(const Params& p, const Lds& L, const Ph
       for (int d = 0; d < D; ++d) {
         const int split = KIND == 3 ? e.split : split_c;
         const int split2 = KIND == 3 ? e.split2 : split2_c;
-        if (FMT == 0 || e.fmt == 0) eat_item_n<0, AL, WT>(split, split2, lg, R.r[d], acc, acc2);
+        if (FMT == 0 || e.fmt == 0) eat_item_n<0, AL, WT, FMT != 0>(split, split2, lg, R.r[d], acc, acc2);
         else eat_item_n<1, AL, WT>(split, split2, lg, R.r[d], acc, acc2);
         fetch_item_n<FMT, AL, WT>(R.f, R.r[d]);
         fetch_adv_n<FMT>(R.f);
