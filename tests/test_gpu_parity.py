@@ -3,8 +3,8 @@
 Small cases run the whole batch through the oracle; they are sized to span
 several weight chunks (1024-element K chunks, 16-row tiles) with ragged
 tails.  Full-size cases (DeepSeek-V3 shape at 1, 8 and 64 rows; the
-V4-style MXFP4 layer at 16 rows) are checked on sampled rows the oracle
-computes one by one.  Routing must match bit-exactly (ids and order),
+V4-style MXFP4 layer at 16 rows; the tensor- and expert-parallel shares) are
+checked on every row, with the oracle given only the experts the rows use.  Routing must match bit-exactly (ids and order),
 outputs within 2e-2 relative L2 and 1e-1 max-abs of the fp64 oracle."""
 import numpy as np
 import pytest
@@ -125,12 +125,12 @@ FULL = [
     ("v4_t16", list(range(16))),
     # the 8-way tensor-parallel share of the V3 layer (intermediate 256)
     ("v3tp8_t1", [0]),
-    ("v3tp8_t8", [0, 4, 7]),
+    ("v3tp8_t8", list(range(8))),
     ("v3tp4_t1", [0]),
-    ("v3tp4_t8", [1, 6]),
+    ("v3tp4_t8", list(range(8))),
     # the 8-way expert-parallel share (experts 0..31 and the shared expert)
     ("v3ep8_t8", list(range(8))),
-    ("v3ep8_t64", [0, 21, 42, 63]),
+    ("v3ep8_t64", list(range(64))),
 ]
 
 
@@ -149,7 +149,7 @@ def full_cases():
 
 
 @pytest.mark.parametrize("name,rows", FULL, ids=[f[0] for f in FULL])
-def test_full_size_sampled(full_cases, name, rows):
+def test_full_size_every_row(full_cases, name, rows):
     say(f"full {name} rows={rows}")
     spec, case = full_cases(name)
     T = case["x"].shape[0]
