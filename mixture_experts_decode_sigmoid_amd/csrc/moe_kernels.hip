@@ -2,27 +2,32 @@
 //
 // One persistent launch: one workgroup of 8 waves per CU, all resident.
 //
-//   S0  router logits   CU c computes l[r][e] for its experts e = c, c+ncu..
-//                       (fp64 sums of exact bf16 products) and sigmoid, and
-//                       publishes each score in a slot tagged with the call's
-//                       epoch; then raises its flag (epoch + 1).
+//   S0  router logits   l[r][e] for a block of (row, expert) dots per CU
+//                       (fp64 sums of exact bf16 products, one summation
+//                       order at every batch size) and sigmoid; each score
+//                       goes to a slot tagged with the call's epoch, so no
+//                       flag barrier is needed.
 //   S1  shared up/gate  the shared expert does not depend on routing, so its
 //                       tiles are streamed while the routing runs.
-//   S2  route + group   every CU polls the score slots of every row until
-//                       they carry the call's tag, routes every row itself
-//                       (no hand-off) and builds the step's group table in
-//                       LDS: distinct experts in order of first use, found by
-//                       ballot / prefix count, each with its using rows.
+//   S2  route + group   below 8 rows every CU polls the score slots of every
+//                       row until they carry the call's tag and routes every
+//                       row itself (no hand-off); from 8 rows each row is
+//                       routed by one CU, which publishes the row's picks as
+//                       tagged words that every CU polls.  Each CU then
+//                       builds the step's group table in LDS: distinct
+//                       experts in order of first use, found by ballot /
+//                       prefix count, each with its using rows.
 //   S3  routed up/gate  jobs (group, tile of 8 or 16 intermediates) dealt
 //                       round-robin over CUs; each job streams its gate and
 //                       up weight rows once and uses every row of the group
 //                       as an MFMA column; SwiGLU mid values go to the
 //                       workspace.
-//   S4  down            after a second flag barrier, CU c owns output rows
-//                       [c*hs, (c+1)*hs) and streams that slice of every used
-//                       expert's W_down once; per (row, slot) products stay in
-//                       LDS.  Unit batches that lie past the step's groups
-//                       issue nothing (dead-batch skip).
+//   S4  down            after the one flag barrier of the call (the
+//                       meeting), CU c owns output rows [c*hs, (c+1)*hs) and
+//                       streams that slice of every used expert's W_down
+//                       once; per (row, slot) products stay in LDS.  Unit
+//                       batches that lie past the step's groups issue
+//                       nothing (dead-batch skip).
 //   S5  combine         out[r][h] = shared + sum_p w[r][p] * P[r][p][h] in this
 //                       row-local order, rounded to bf16 once (under an expert
 //                       range, p over the picks whose expert is held here).
@@ -41,14 +46,14 @@
 // the same fixed-order reduction over the 8 waves' K ranges; the combine is
 // row-local.  Only which CU does the work depends on the batch.
 //
-// Cross-CU data (scores, mid) is stored at agent scope (written through to
-// the device's point of coherence), so raising a flag after it needs only
-// the workgroup's own store completion, not an L2 writeback; the one
-// exception is the wide stream's mid, stored plainly and published with an
-// agent-scope release fence.  Readers poll the flags (or, for scores, the
-// epoch tags in the slots themselves) and then acquire at agent scope.
-// Each CU owns one flag and raises it by one per phase; a call advances
-// every flag by two, so the workspace needs no reset.  Waits are bounded:
+// Cross-CU data (scores, picks, mid) is stored at agent scope (written
+// through to the device's point of coherence), so raising a flag after it
+// needs only the workgroup's own store completion, not an L2 writeback.
+// Readers poll the flags (or, for scores and picks, the epoch tags in the
+// words themselves) and then acquire at agent scope.  Each CU owns one
+// flag; a call advances every flag by two (the forward raises it straight
+// to epoch + 2 at the meeting, the routing-only calls to epoch + 1), so the
+// workspace needs no reset.  Waits are bounded:
 // on timeout an error bit is set and the kernel runs on.
 #include "moe_internal.h"
 
