@@ -1325,7 +1325,10 @@ __device__ __forceinline__ void balance(const Lds& L, int jc) {
 
 // ------------------------------------------------------------------ narrow stream
 //
-// Batches of at most 16 rows (one 16-column MFMA tile per group).  A wave's
+// Every batch size (the name is older than the wide batches): a group's
+// columns go to jobs of at most 4 * AL columns (a column spans 4 / AL of
+// the 16 MFMA columns), a group with more columns being several jobs.  A
+// wave's
 // items run through a D-deep register ring: each step multiplies the oldest
 // item, refills its slot with the item D later and counts; only a job
 // change on either side does more.  At a job end the wave stores its
@@ -2545,7 +2548,7 @@ __device__ __forceinline__ const Params& fresh_args() {
 }
 
 // The forward after the logits: routing and grouping, the up/gate stream
-// (its sums formed at job ends), the second flag barrier, the down stream,
+// (its sums formed at job ends), the meeting (the call's one flag barrier), the down stream,
 // the combine.  With at most as many rows as waves, the waves that route no
 // row start on this CU's shared-expert jobs once every row's scores are in,
 // the routing waves but wave 7 as soon as their row is routed, and wave 7
