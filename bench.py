@@ -42,6 +42,7 @@ EXTRA = ("v3_t8", "v3_t64")
 # parallelism and under 8-way expert parallelism
 EXTRA_OWN = ("tiny_t1", "v4_t16", "v3tp8_t1", "v3tp8_t8", "v3tp4_t1", "v3tp4_t8", "v3ep8_t8", "v3ep8_t64")
 STREAM_BYTES = 4 << 30
+PREFILL_ROWS, PREFILL_CHUNK = 256, 64
 
 
 def kernel_source_hash() -> str:
@@ -134,6 +135,47 @@ def time_layer(spec, copies, x, steps, warmup, unfused=False, marked=True):
     ids, _ = layers[0].route(x)
     distinct = fixtures.held_distinct(spec, ids.cpu().view(-1).tolist())
     return mean, per, distinct
+
+
+def time_prefill(spec, copies, x, steps, warmup, stream_gbs):
+    """Times moe_forward_prefill over all rows of x (chunks of PREFILL_CHUNK
+    rows, one fused launch each) rotating weight copies, between two HIP
+    events on the launch stream.  The algorithmic bytes are each chunk's own
+    (its distinct experts' weights once, plus the router), summed."""
+    import torch
+    import fixtures
+    import mixture_experts_decode_sigmoid_amd as moe
+    T = x.shape[0]
+    layers = [moe.Layer(spec, dict(c, x=x[:PREFILL_CHUNK]), max_rows=PREFILL_CHUNK) for c in copies]
+    out = torch.empty_like(x)
+
+    def call(l):
+        moe.moe_forward_prefill(l.cfg, l.w, x, out, l.ws)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        call(layers[i % len(layers)])
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(steps):
+        call(layers[i % len(layers)])
+    b.record(stream)
+    torch.cuda.synchronize()
+    mean = a.elapsed_time(b) * 1000.0 / steps
+    errs = [l.read_error() for l in layers]
+    if any(errs):
+        raise RuntimeError(f"device error bits {errs}")
+    b_alg, distinct = 0, []
+    for r0 in range(0, T, PREFILL_CHUNK):
+        ids, _ = layers[0].route(x[r0:r0 + PREFILL_CHUNK].contiguous())
+        d = fixtures.held_distinct(spec, ids.cpu().view(-1).tolist())
+        distinct.append(d)
+        b_alg += fixtures.algorithmic_bytes(spec, d)
+    gbs = b_alg / (mean * 1e-6) / 1e9
+    return dict(rows=T, chunk_rows=PREFILL_CHUNK, launches=len(distinct), distinct_experts_per_chunk=distinct,
+                us_per_call=round(mean, 2), us_per_row=round(mean / T, 2), algorithmic_bytes=b_alg,
+                gbs=round(gbs, 1), frac_of_peak=round(gbs / PEAK_HBM_GBS, 4),
+                frac_of_stream_read=round(gbs / stream_gbs, 4) if stream_gbs else None, steps=steps)
 
 
 def summary(mean, per, b_alg, stream_gbs):
@@ -334,6 +376,14 @@ def main():
                             fusion_gain_pct=round(100.0 * (u - f) / u, 2), rounds=3, statistic="best of 3 means")
             note(f"fusion A/B {name}: fused {f:.2f} us, unfused {u:.2f} us")
         extra["fusion_ab"] = ab
+
+        # the larger-T path: 256 independent rows through moe_forward_prefill
+        # (consecutive fused calls of 64 rows, each its own launch)
+        hd = fixtures.make_case(spec, PREFILL_ROWS, 5, device="cuda", rows="iid", requests=PREFILL_ROWS,
+                                experts=False)
+        cps = [dict(c, router_w=hd["router_w"], bias=hd["bias"]) for c in copies]
+        extra["v3_prefill_t256"] = time_prefill(spec, cps, hd["x"], max(10, args.steps // 20), 3, stream_gbs)
+        note(f"v3_prefill_t256: {extra['v3_prefill_t256']['us_per_call']} us")
 
         del copies
         torch.cuda.empty_cache()
